@@ -1,0 +1,248 @@
+/*
+ * flashloop.h — C ABI of the FlashLoop loop-attention hot path on MI355X (gfx950).
+ *
+ * What the library computes (FlashLoop: Fast and Memory-Efficient Looped
+ * Transformers via Lazy Updates; paperlayer.ai abstract page, "p1" below, with
+ * its sections; the flozi-tech guide, "guide"):
+ *   A looped model applies one shared block R times, H^(r) = F(H^(r-1)), and
+ *   keeps a separate (K^(r), V^(r)) for every loop (guide §1; p1 §3).  The
+ *   library implements the attention of that block across loops:
+ *     - the cross-loop KV cache: a quantized loop-1 base plus quantized
+ *       residuals against the reconstructed previous loop, stored for active
+ *       tokens only (p1 §4.3, §D.3)            -> fl_kv_resq
+ *     - loop-aware column selection: rank the candidate key columns by the
+ *       attention mass loop r-1 gave them over the rows loop r recomputes,
+ *       keep the top K, cache their mass (p1 §4.2, §D.2)   -> fl_colsel
+ *     - sparse loop-r attention: recompute the active rows (p1 §4.1, §D.1)
+ *       only against the selected columns and rescale the softmax by their
+ *       cached mass, reusing every other column's contribution (p1 §4.2;
+ *       guide §3: the rank-K correction of the paper's eq. 3) -> fl_loop_attn
+ *     - the decode step over the packed streams, with the selection fused in
+ *       (p1 App. G)                                -> fl_loop_decode
+ *
+ * Notation: loops r = 1..R; A_r = active rows of a sequence (A_1 = all rows,
+ * A_r ⊆ A_{r-1}, shared by every head and layer), n_r = |A_r|; S_r = selected
+ * columns of a (b, h) (S_1 = all), K_r = |S_r|, S_r ⊆ S_{r-1}; tau = fp32(1/sqrt(d)).
+ * With J_i = {j in S_r : j <= i} and P^(r-1) the probabilities loop r-1 left:
+ *   M^r_i = sum_{J_i} P^(r-1)_ij,     U^r_i = O^(r-1)_i - sum_{J_i} P^(r-1)_ij v~^(r-1)_j,
+ *   O^r_i = U^r_i + M^r_i * sum_{J_i} softmax_{J_i}(tau q^r_i . k~^r_j) v~^r_j,
+ *   lse^r_i = log sum_{J_i} exp(tau q^r_i . k~^r_j).
+ * k~, v~ are the reconstructions (rounded to bf16 for bf16 prefill inputs).
+ *
+ * Conventions for every call:
+ *   - All array arguments are device pointers to caller-owned memory, 16-byte
+ *     aligned.  The library allocates nothing and keeps no pointer after a call.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and do not synchronize.  They are reentrant and thread safe.
+ *   - Every argument is validated before anything is launched; on error the
+ *     call returns a nonzero fl_status, launches nothing and writes nothing;
+ *     fl_last_error() then describes the error (per thread).  No C++ exception
+ *     crosses this boundary.
+ *   - Device-data preconditions are documented, not checked: rows ascending
+ *     and nested, finite inputs, |x| < 8e6 (the fp16 scale range).
+ */
+#ifndef FLASHLOOP_H
+#define FLASHLOOP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FL_ABI_VERSION 1
+#define FL_MAX_LOOPS 16
+
+typedef enum fl_status {
+  FL_OK = 0,
+  FL_EINVAL = 1,        /* bad pointer, size, loop index or budget */
+  FL_EUNSUPPORTED = 2,  /* valid but not implemented: d, bits, dtype, size */
+  FL_EHIP = 3           /* a HIP launch or runtime call failed */
+} fl_status;
+
+typedef enum fl_dtype {
+  FL_F32 = 0,   /* float32 inputs; attention operands are the fp32 reconstructions */
+  FL_BF16 = 1   /* bfloat16 inputs; prefill operands rounded to bf16 (matrix cores) */
+} fl_dtype;
+
+/* A stream handle: a hipStream_t passed through as an opaque pointer. */
+typedef void* fl_stream;
+
+/*
+ * The packed cross-loop KV cache of L layers (p1 §4.3 and §D.3; p1 App. G:
+ * packed 4-bit storage, "anchor and residual KV streams").  Index r of every
+ * loop array is the loop number (index 0 is unused).
+ *
+ *   L, B, H, S, d, R   layers, sequences, heads, tokens, head dim (64 or 128),
+ *                      loops (1..FL_MAX_LOOPS)
+ *   n[r]               active rows per sequence at loop r (n[1] == S), the
+ *                      same for every sequence
+ *   bits[r]            residual code width of loop r: 4 or 2 (bits[1] == 8)
+ *   rows[r]            [B][n_r] int32, strictly ascending positions of A_r
+ *                      (rows[1] unused: every row)
+ *   slot[r]            [B][S] int32: index of position j in rows[r], or -1.
+ *                      Written by fl_kv_resq(r); read by the other calls.
+ *   base               [L][B][H][S] base records (fl_base_record_bytes(d) each)
+ *   res[r]             [L][B][H][n_r] residual records of loop r
+ *                      (fl_residual_record_bytes(d, bits[r]) each), in rows[r]
+ *                      order
+ *
+ * Base record of one (token, head), G = d/32 groups of 32 dims:
+ *   [0,d) K codes int8 | [d,2d) V codes int8 | K scales fp16 x G | V scales fp16 x G
+ *   | zero padding to a multiple of 16 bytes          (d = 128: 272 bytes)
+ *   x_hat = code * scale (exact in fp32); codes in [-127, 127].
+ * Residual record, b bits, C = d*b/8:
+ *   [0,C) K codes | [C,2C) V codes | K scales | K zeros | V scales | V zeros
+ *   (fp16 x G each) | padding to 16 bytes        (d = 128: 160 bytes at 4 bits, 96 at 2)
+ *   4-bit: element 2k in the low nibble of byte k, 2k+1 in the high nibble;
+ *   2-bit: element 4k+t in bits 2t..2t+1 of byte k.
+ *   delta_hat = fma(code, scale, zero) rounded once to fp32; x_hat^(r) =
+ *   x_hat^(r-1) + delta_hat in fp32.  Tokens outside A_r keep x_hat^(r-1).
+ */
+typedef struct fl_cache {
+  int L, B, H, S, d, R;
+  int n[FL_MAX_LOOPS + 1];
+  int bits[FL_MAX_LOOPS + 1];
+  const int32_t* rows[FL_MAX_LOOPS + 1];
+  int32_t* slot[FL_MAX_LOOPS + 1];
+  uint8_t* base;
+  uint8_t* res[FL_MAX_LOOPS + 1];
+} fl_cache;
+
+/* Per-row prefill state, position indexed (one layer: the cache's L must be 1).
+ *   O, U  [B][H][S][d] float32     output and reused part
+ *   M     [B][H][S] float32        cached mass of the selected columns
+ *   lse   [B][H][S] float32        log-sum-exp of the last recomputation
+ *                                  (-inf when a row had no column left) */
+typedef struct fl_state {
+  float* O;
+  float* U;
+  float* M;
+  float* lse;
+} fl_state;
+
+/* Decode state of one new token per (layer, sequence, head).
+ *   O, U    [L][B][H][d] float32
+ *   M, lse  [L][B][H] float32
+ *   logits  [L][B][H][S] float32: after loop 1 the logits of all S cached
+ *           tokens; after loop r >= 2 the logits of the K_r selected tokens,
+ *           compacted to the front in the order of sel
+ *   sel     [L][B][H][S] int32: after loop r >= 2 the K_r selected token
+ *           positions, ascending, at the front */
+typedef struct fl_dstate {
+  float* O;
+  float* U;
+  float* M;
+  float* lse;
+  float* logits;
+  int32_t* sel;
+} fl_dstate;
+
+/* ABI version of the loaded library (FL_ABI_VERSION). */
+int fl_abi_version(void);
+
+/* Text of the last error on the calling thread ("" if none).  The pointer
+ * stays valid until the next library call on the same thread. */
+const char* fl_last_error(void);
+
+/* Record sizes in bytes (see fl_cache); 0 for unsupported d or bits. */
+size_t fl_base_record_bytes(int d);
+size_t fl_residual_record_bytes(int d, int bits);
+
+/* Workspace sizes in bytes for the calls that take one.
+ *   which = FL_WS_COLSEL: fl_colsel at loop r with K_prev candidates
+ *   which = FL_WS_ATTN:   fl_loop_attn at loop r
+ *   which = FL_WS_DECODE: fl_loop_decode at loop r
+ * A call may be given a larger workspace; 0 means none is needed. */
+#define FL_WS_COLSEL 1
+#define FL_WS_ATTN 2
+#define FL_WS_DECODE 3
+size_t fl_workspace_bytes(int which, const fl_cache* cache, int r, int K_prev, int K_r);
+
+/*
+ * fl_kv_resq — quantize and pack loop r's keys and values (p1 §4.3 and §D.3;
+ * guide §3: residuals X^(r) - X_hat^(r-1) of the active tokens only).
+ *   r == 1: k, v are [L][B][H][S][d] (dtype); writes cache->base.
+ *           Per group of 32: s = fp16 rounded up of (max|x| / 127) (fp32
+ *           divide); code = clamp(rint(x / s), -127, 127), 0 when s == 0.
+ *   r >= 2: k, v are [L][B][H][n_r][d] in rows[r] order (the loop-r values of
+ *           the active rows); writes cache->res[r] and cache->slot[r].
+ *           delta = x - x_hat^(r-1) (fp32); z = fp16 rounded down of min(delta);
+ *           s = fp16 rounded up of ((max(delta) - z) / (2^b - 1));
+ *           code = clamp(rint((delta - z) / s), 0, 2^b - 1), 0 when s == 0.
+ *           Needs the streams of loops 1..r-1 (and slot[2..r-1]) in place.
+ * Codes, scales and zeros are bit-exact functions of the inputs.
+ */
+fl_status fl_kv_resq(const fl_cache* cache, int r, const void* k, const void* v, fl_dtype dtype,
+                     fl_stream stream);
+
+/*
+ * fl_colsel — loop-aware column selection for loop r >= 2 of one layer
+ * (p1 §4.2: top-K key columns ranked using the preceding loop, and later
+ * loops prune the selected set further; p1 §D.2: the selection caches key
+ * indices and their global mass).
+ *   q_prev   [B][H][n_{r-1}][d] (dtype): loop r-1 queries in rows[r-1] order
+ *   state    the fl_state left by loop r-1 (O, lse, M read; U, M written)
+ *   cand     [B][H][K_prev] int32 ascending: S_{r-1}; NULL means every
+ *            position (then K_prev must equal S)
+ *   K_r      budget, 1 <= K_r <= K_prev
+ *   mass_in  [B][H][K_prev] float32 or NULL: column masses to rank instead of
+ *            computing them (lets a caller reproduce a selection exactly)
+ *   mass_out [B][H][K_prev] float32 or NULL: receives the computed mass
+ *            c_j = sum_{i in A_r, i >= j} P^(r-1)_ij, in fp32, accumulated in
+ *            a fixed order (deterministic)
+ *   sel_out  [B][H][K_r] int32: S_r, the K_r candidates first under
+ *            (mass descending, position ascending), written ascending
+ *   ws       workspace of fl_workspace_bytes(FL_WS_COLSEL, ...) bytes
+ * When K_r == K_prev the selection is the candidate set itself; sel_out gets
+ * a copy and U, M are left as they are (they already hold M^r, U^r).
+ * Otherwise M^r and U^r of the rows in A_r are written into state.
+ * The mass pass runs when it is needed for the selection or mass_out is set.
+ */
+fl_status fl_colsel(const fl_cache* cache, int r, const void* q_prev, fl_dtype dtype, const fl_state* state,
+                    int K_prev, const int32_t* cand, int K_r, const float* mass_in, float* mass_out,
+                    int32_t* sel_out, void* ws, size_t ws_bytes, fl_stream stream);
+
+/*
+ * fl_loop_attn — loop-r attention of one layer (prefill), over the packed
+ * cache streams (p1 App. G: attention reads the packed anchor and residual
+ * streams; p1 §4.4: selected tokens and keys are gathered into compact tiles).
+ *   r == 1: q [B][H][S][d]; dense causal attention of every row:
+ *           O = softmax(tau q k~^T) v~, lse; sets M = 1 and U = 0.
+ *   r >= 2: q [B][H][n_r][d] in rows[r] order; sel [B][H][K_r] = S_r from
+ *           fl_colsel.  For i in A_r with J_i non-empty: O_i = U_i +
+ *           M_i * softmax_{J_i}(...) v~ and lse_i; rows with J_i empty get
+ *           lse_i = -inf and keep O_i.  Rows outside A_r are not touched.
+ * The cache must hold the streams of loops 1..r (fl_kv_resq(r) done).
+ */
+fl_status fl_loop_attn(const fl_cache* cache, int r, const void* q, fl_dtype dtype, int K_r,
+                       const int32_t* sel, const fl_state* state, void* ws, size_t ws_bytes,
+                       fl_stream stream);
+
+/*
+ * fl_loop_decode — loop r of one decode step for every (layer, sequence,
+ * head) of the cache (guide §1 and Cell 1: decode is bound by reading the
+ * cache; p1 App. G: packed streams read directly, fused sparse decode
+ * selection).  The new token attends all S cached tokens (its own K/V is
+ * already cached) and is active at every loop.  Operands are the fp32
+ * reconstructions.
+ *   q      [L][B][H][d] (dtype): the loop-r query of the new token
+ *   r == 1: O, lse, logits of all S tokens; M = 1, U = 0.
+ *   r >= 2: S_r = top K_r of the K_prev candidates (state.sel, or every
+ *           position when r == 2 and K_prev == S) ranked by their stored
+ *           loop r-1 logits (ties: lower position first); when K_r < K_prev,
+ *           M = sum_{S_r} P^(r-1)_j and U = O - sum_{S_r} P^(r-1)_j v^(r-1)_j
+ *           with P^(r-1)_j = M exp(logit_j - lse); then
+ *           O = U + M softmax_{S_r}(tau q.k^r) v^r, lse, and the new logits
+ *           and selection are compacted into state.logits / state.sel.
+ *   K_prev S when r == 2, else the K of the previous loop; 1 <= K_r <= K_prev.
+ */
+fl_status fl_loop_decode(const fl_cache* cache, int r, const void* q, fl_dtype dtype, int K_prev, int K_r,
+                         const fl_dstate* state, void* ws, size_t ws_bytes, fl_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHLOOP_H */

@@ -1,0 +1,92 @@
+"""Device buffers for the C ABI structs, allocated with torch (memory only)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from ._lib import FL_MAX_LOOPS, FlCache, FlDState, FlState, fl_base_record_bytes, fl_residual_record_bytes
+
+
+def _dev_i32(x, device):
+    return torch.as_tensor(np.ascontiguousarray(np.asarray(x, dtype=np.int32))).to(device)
+
+
+class CacheBuffers:
+    """A packed cross-loop cache of L layers and the FlCache struct pointing at it.
+
+    rows[r-1]: int32 [B][n_r] active positions of loop r (loop 1 ignored)."""
+
+    def __init__(self, L, B, H, S, d, R, n, bits, rows, device="cuda"):
+        assert R <= FL_MAX_LOOPS and len(n) == R and len(bits) == R
+        self.L, self.B, self.H, self.S, self.d, self.R = L, B, H, S, d, R
+        self.n, self.bits = list(n), list(bits)
+        self.base_rb = fl_base_record_bytes(d)
+        self.res_rb = [0] + [fl_residual_record_bytes(d, bits[r]) for r in range(1, R)]
+        self.base = torch.empty(L * B * H * S * self.base_rb, dtype=torch.uint8, device=device)
+        self.res = [None] + [torch.empty(L * B * H * n[r] * self.res_rb[r], dtype=torch.uint8, device=device)
+                             for r in range(1, R)]
+        self.rows = [None] + [_dev_i32(rows[r], device).reshape(B, n[r]) for r in range(1, R)]
+        self.slot = [None] + [torch.full((B, S), -1, dtype=torch.int32, device=device) for _ in range(1, R)]
+        self.fl = self._struct(0, L)
+
+    def _struct(self, layer, L):
+        c = FlCache()
+        c.L, c.B, c.H, c.S, c.d, c.R = L, self.B, self.H, self.S, self.d, self.R
+        per_base = self.B * self.H * self.S * self.base_rb
+        c.base = self.base.data_ptr() + layer * per_base
+        for r in range(1, self.R + 1):
+            c.n[r] = self.n[r - 1]
+            c.bits[r] = self.bits[r - 1]
+            if r >= 2:
+                c.rows[r] = self.rows[r - 1].data_ptr()
+                c.slot[r] = self.slot[r - 1].data_ptr()
+                per = self.B * self.H * self.n[r - 1] * self.res_rb[r - 1]
+                c.res[r] = self.res[r - 1].data_ptr() + layer * per
+        return c
+
+    def layer_view(self, layer: int) -> FlCache:
+        """The same cache restricted to one layer (L = 1)."""
+        return self._struct(layer, 1)
+
+    def replicate_layer0(self):
+        """Copy layer 0's records into every other layer."""
+        per_base = self.B * self.H * self.S * self.base_rb
+        b = self.base.view(self.L, per_base)
+        b[1:].copy_(b[0:1].expand(self.L - 1, per_base))
+        for r in range(1, self.R):
+            per = self.B * self.H * self.n[r] * self.res_rb[r]
+            x = self.res[r].view(self.L, per)
+            x[1:].copy_(x[0:1].expand(self.L - 1, per))
+
+    def base_records(self) -> torch.Tensor:
+        return self.base.view(self.L, self.B, self.H, self.S, self.base_rb)
+
+    def res_records(self, r: int) -> torch.Tensor:
+        return self.res[r - 1].view(self.L, self.B, self.H, self.n[r - 1], self.res_rb[r - 1])
+
+    def nbytes(self) -> int:
+        return self.base.numel() + sum(x.numel() for x in self.res[1:])
+
+
+class PrefillState:
+    def __init__(self, B, H, S, d, device="cuda"):
+        self.O = torch.zeros(B, H, S, d, dtype=torch.float32, device=device)
+        self.U = torch.zeros(B, H, S, d, dtype=torch.float32, device=device)
+        self.M = torch.ones(B, H, S, dtype=torch.float32, device=device)
+        self.lse = torch.zeros(B, H, S, dtype=torch.float32, device=device)
+        self.fl = FlState(self.O.data_ptr(), self.U.data_ptr(), self.M.data_ptr(), self.lse.data_ptr())
+
+    def snapshot(self):
+        return {k: getattr(self, k).clone() for k in ("O", "U", "M", "lse")}
+
+
+class DecodeState:
+    def __init__(self, L, B, H, S, d, device="cuda"):
+        self.O = torch.zeros(L, B, H, d, dtype=torch.float32, device=device)
+        self.U = torch.zeros(L, B, H, d, dtype=torch.float32, device=device)
+        self.M = torch.ones(L, B, H, dtype=torch.float32, device=device)
+        self.lse = torch.zeros(L, B, H, dtype=torch.float32, device=device)
+        self.logits = torch.zeros(L, B, H, S, dtype=torch.float32, device=device)
+        self.sel = torch.zeros(L, B, H, S, dtype=torch.int32, device=device)
+        self.fl = FlDState(self.O.data_ptr(), self.U.data_ptr(), self.M.data_ptr(), self.lse.data_ptr(),
+                           self.logits.data_ptr(), self.sel.data_ptr())

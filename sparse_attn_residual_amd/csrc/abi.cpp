@@ -1,0 +1,278 @@
+// C ABI of the FlashLoop hot path: argument validation, workspace sizing,
+// error reporting and kernel dispatch.  Declarations and the meaning of every
+// argument are in include/flashloop.h.  Nothing here allocates device memory;
+// every check happens before the first launch of a call.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+fl_status fail(fl_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+fl_status hip_fail(hipError_t e, const char* what) {
+  return fail(FL_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define FL_NEED_PTR(p, name)                                                                 \
+  do {                                                                                       \
+    if (!(p)) return fail(FL_EINVAL, "%s: %s is NULL", fn, name);                            \
+    if (!aligned16(p)) return fail(FL_EINVAL, "%s: %s is not 16-byte aligned", fn, name);    \
+  } while (0)
+
+// Validates the cache geometry and the streams needed by loop r; fills geo.
+fl_status check_cache(const char* fn, const fl_cache* c, int r, bool need_res_r, fl::CacheGeo* geo) {
+  if (!c) return fail(FL_EINVAL, "%s: cache is NULL", fn);
+  if (c->L < 1 || c->B < 1 || c->H < 1 || c->S < 1)
+    return fail(FL_EINVAL, "%s: L, B, H, S must be >= 1 (got %d, %d, %d, %d)", fn, c->L, c->B, c->H, c->S);
+  if (c->d != 64 && c->d != 128) return fail(FL_EUNSUPPORTED, "%s: head dim %d (supported: 64, 128)", fn, c->d);
+  if (c->R < 1 || c->R > FL_MAX_LOOPS) return fail(FL_EINVAL, "%s: R = %d outside [1, %d]", fn, c->R, FL_MAX_LOOPS);
+  if (r < 1 || r > c->R) return fail(FL_EINVAL, "%s: loop r = %d outside [1, R = %d]", fn, r, c->R);
+  if (c->n[1] != c->S) return fail(FL_EINVAL, "%s: n[1] = %d must equal S = %d", fn, c->n[1], c->S);
+  if ((long long)c->L * c->B * c->H * c->S > (1LL << 40)) return fail(FL_EUNSUPPORTED, "%s: cache too large", fn);
+  FL_NEED_PTR(c->base, "cache->base");
+  const int last = need_res_r ? r : r - 1;
+  for (int rr = 2; rr <= c->R; ++rr) {
+    if (c->n[rr] < 1 || c->n[rr] > c->n[rr - 1])
+      return fail(FL_EINVAL, "%s: n[%d] = %d must be in [1, n[%d] = %d] (nested sets)", fn, rr, c->n[rr], rr - 1,
+                  c->n[rr - 1]);
+    if (c->bits[rr] != 2 && c->bits[rr] != 4)
+      return fail(FL_EUNSUPPORTED, "%s: bits[%d] = %d (supported: 2, 4)", fn, rr, c->bits[rr]);
+  }
+  for (int rr = 2; rr <= r; ++rr) {
+    char name[32];
+    std::snprintf(name, sizeof name, "cache->rows[%d]", rr);
+    FL_NEED_PTR(c->rows[rr], name);
+    std::snprintf(name, sizeof name, "cache->slot[%d]", rr);
+    FL_NEED_PTR(c->slot[rr], name);
+    if (rr <= last) {
+      std::snprintf(name, sizeof name, "cache->res[%d]", rr);
+      FL_NEED_PTR(c->res[rr], name);
+    }
+  }
+  *geo = fl::CacheGeo{};
+  geo->L = c->L; geo->B = c->B; geo->H = c->H; geo->S = c->S; geo->d = c->d; geo->R = c->R;
+  geo->base = c->base;
+  geo->base_rb = fl::base_record_bytes(c->d);
+  for (int rr = 1; rr <= c->R; ++rr) {
+    geo->n[rr] = c->n[rr];
+    geo->bits[rr] = rr == 1 ? 8 : c->bits[rr];
+    geo->rows[rr] = c->rows[rr];
+    geo->slot[rr] = c->slot[rr];
+    geo->res[rr] = c->res[rr];
+    geo->res_rb[rr] = rr == 1 ? 0 : fl::residual_record_bytes(c->d, c->bits[rr]);
+  }
+  return FL_OK;
+}
+
+fl_status check_dtype(const char* fn, fl_dtype dt) {
+  if (dt != FL_F32 && dt != FL_BF16) return fail(FL_EUNSUPPORTED, "%s: dtype %d (supported: FL_F32, FL_BF16)", fn, (int)dt);
+  return FL_OK;
+}
+
+fl_status check_state(const char* fn, const fl_state* s) {
+  if (!s) return fail(FL_EINVAL, "%s: state is NULL", fn);
+  FL_NEED_PTR(s->O, "state->O");
+  FL_NEED_PTR(s->U, "state->U");
+  FL_NEED_PTR(s->M, "state->M");
+  FL_NEED_PTR(s->lse, "state->lse");
+  return FL_OK;
+}
+
+constexpr int kTopkMax = 65536;
+
+}  // namespace
+
+extern "C" {
+
+int fl_abi_version(void) { return FL_ABI_VERSION; }
+
+const char* fl_last_error(void) { return g_err.c_str(); }
+
+size_t fl_base_record_bytes(int d) { return (d == 64 || d == 128) ? (size_t)fl::base_record_bytes(d) : 0; }
+
+size_t fl_residual_record_bytes(int d, int bits) {
+  if ((d != 64 && d != 128) || (bits != 2 && bits != 4)) return 0;
+  return (size_t)fl::residual_record_bytes(d, bits);
+}
+
+size_t fl_workspace_bytes(int which, const fl_cache* cache, int r, int K_prev, int K_r) {
+  (void)r;
+  (void)K_r;
+  if (!cache || K_prev < 0) return 0;
+  if (which == FL_WS_COLSEL) return (size_t)cache->B * cache->H * (size_t)K_prev * sizeof(float);
+  return 0;
+}
+
+fl_status fl_kv_resq(const fl_cache* cache, int r, const void* k, const void* v, fl_dtype dtype, fl_stream stream) {
+  const char* fn = "fl_kv_resq";
+  g_err.clear();
+  fl::CacheGeo geo;
+  fl_status s = check_cache(fn, cache, r, true, &geo);
+  if (s != FL_OK) return s;
+  if ((s = check_dtype(fn, dtype)) != FL_OK) return s;
+  FL_NEED_PTR(k, "k");
+  FL_NEED_PTR(v, "v");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (r == 1) {
+    e = fl::launch_quant_base(geo, k, v, dtype, cache->base, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return FL_OK;
+  }
+  e = fl::launch_build_slot(geo, r, cache->slot[r], st);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  e = fl::launch_quant_res(geo, r, k, v, dtype, cache->res[r], st);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return FL_OK;
+}
+
+fl_status fl_colsel(const fl_cache* cache, int r, const void* q_prev, fl_dtype dtype, const fl_state* state,
+                    int K_prev, const int32_t* cand, int K_r, const float* mass_in, float* mass_out, int32_t* sel_out,
+                    void* ws, size_t ws_bytes, fl_stream stream) {
+  const char* fn = "fl_colsel";
+  g_err.clear();
+  fl::CacheGeo geo;
+  fl_status s = check_cache(fn, cache, r, false, &geo);
+  if (s != FL_OK) return s;
+  if (r < 2) return fail(FL_EINVAL, "%s: loop r = %d (selection exists for r >= 2)", fn, r);
+  if (cache->L != 1) return fail(FL_EINVAL, "%s: prefill state covers one layer (L = %d)", fn, cache->L);
+  if ((s = check_dtype(fn, dtype)) != FL_OK) return s;
+  if ((s = check_state(fn, state)) != FL_OK) return s;
+  FL_NEED_PTR(q_prev, "q_prev");
+  FL_NEED_PTR(sel_out, "sel_out");
+  if (K_prev < 1 || K_prev > cache->S) return fail(FL_EINVAL, "%s: K_prev = %d outside [1, S]", fn, K_prev);
+  if (!cand && K_prev != cache->S) return fail(FL_EINVAL, "%s: cand is NULL but K_prev = %d != S", fn, K_prev);
+  if (cand && !aligned16(cand)) return fail(FL_EINVAL, "%s: cand is not 16-byte aligned", fn);
+  if (K_r < 1 || K_r > K_prev) return fail(FL_EINVAL, "%s: K_r = %d outside [1, K_prev = %d]", fn, K_r, K_prev);
+  if (mass_in && !aligned16(mass_in)) return fail(FL_EINVAL, "%s: mass_in is not 16-byte aligned", fn);
+  if (mass_out && !aligned16(mass_out)) return fail(FL_EINVAL, "%s: mass_out is not 16-byte aligned", fn);
+  const bool prune = K_r < K_prev;
+  const bool need_mass = (prune && !mass_in) || mass_out;
+  float* mass = mass_out;
+  if (need_mass && !mass) {
+    const size_t need = fl_workspace_bytes(FL_WS_COLSEL, cache, r, K_prev, K_r);
+    if (!ws || ws_bytes < need)
+      return fail(FL_EINVAL, "%s: workspace of %zu bytes needed (got %zu)", fn, need, ws ? ws_bytes : (size_t)0);
+    if (!aligned16(ws)) return fail(FL_EINVAL, "%s: ws is not 16-byte aligned", fn);
+    mass = (float*)ws;
+  }
+  if (prune && K_prev > kTopkMax)
+    return fail(FL_EUNSUPPORTED, "%s: %d candidates (at most %d)", fn, K_prev, kTopkMax);
+  hipStream_t st = (hipStream_t)stream;
+  fl::AttnArgs a{};
+  a.c = geo;
+  a.r = r;
+  a.dt = dtype;
+  a.q = q_prev;
+  a.O = state->O; a.U = state->U; a.M = state->M; a.lse = state->lse;
+  hipError_t e;
+  if (need_mass) {
+    e = fl::launch_mass(a, cand, K_prev, mass, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+  }
+  const int P = cache->B * cache->H;
+  if (!prune) {
+    e = fl::launch_copy_sel(cand, P, K_prev, sel_out, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return FL_OK;
+  }
+  const float* keys = mass_in ? mass_in : mass;
+  e = fl::launch_topk(keys, K_prev, cand, K_prev, P, K_prev, K_r, sel_out, K_r, nullptr, 0, st);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  a.K = K_r;
+  a.sel = sel_out;
+  e = fl::launch_um(a, st);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return FL_OK;
+}
+
+fl_status fl_loop_attn(const fl_cache* cache, int r, const void* q, fl_dtype dtype, int K_r, const int32_t* sel,
+                       const fl_state* state, void* ws, size_t ws_bytes, fl_stream stream) {
+  (void)ws;
+  (void)ws_bytes;
+  const char* fn = "fl_loop_attn";
+  g_err.clear();
+  fl::CacheGeo geo;
+  fl_status s = check_cache(fn, cache, r, true, &geo);
+  if (s != FL_OK) return s;
+  if (cache->L != 1) return fail(FL_EINVAL, "%s: prefill state covers one layer (L = %d)", fn, cache->L);
+  if ((s = check_dtype(fn, dtype)) != FL_OK) return s;
+  if ((s = check_state(fn, state)) != FL_OK) return s;
+  FL_NEED_PTR(q, "q");
+  if (r >= 2) {
+    FL_NEED_PTR(sel, "sel");
+    if (K_r < 1 || K_r > cache->S) return fail(FL_EINVAL, "%s: K_r = %d outside [1, S]", fn, K_r);
+  }
+  fl::AttnArgs a{};
+  a.c = geo;
+  a.r = r;
+  a.dt = dtype;
+  a.q = q;
+  a.K = r >= 2 ? K_r : 0;
+  a.sel = r >= 2 ? sel : nullptr;
+  a.O = state->O; a.U = state->U; a.M = state->M; a.lse = state->lse;
+  hipError_t e = fl::launch_attn(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return FL_OK;
+}
+
+fl_status fl_loop_decode(const fl_cache* cache, int r, const void* q, fl_dtype dtype, int K_prev, int K_r,
+                         const fl_dstate* state, void* ws, size_t ws_bytes, fl_stream stream) {
+  (void)ws;
+  (void)ws_bytes;
+  const char* fn = "fl_loop_decode";
+  g_err.clear();
+  fl::CacheGeo geo;
+  fl_status s = check_cache(fn, cache, r, true, &geo);
+  if (s != FL_OK) return s;
+  if (cache->d != 128) return fail(FL_EUNSUPPORTED, "%s: head dim %d (decode supports 128)", fn, cache->d);
+  if ((s = check_dtype(fn, dtype)) != FL_OK) return s;
+  if (!state) return fail(FL_EINVAL, "%s: state is NULL", fn);
+  FL_NEED_PTR(state->O, "state->O");
+  FL_NEED_PTR(state->U, "state->U");
+  FL_NEED_PTR(state->M, "state->M");
+  FL_NEED_PTR(state->lse, "state->lse");
+  FL_NEED_PTR(state->logits, "state->logits");
+  FL_NEED_PTR(state->sel, "state->sel");
+  FL_NEED_PTR(q, "q");
+  if ((long long)cache->L * cache->B * cache->H > 0x7FFFFFFFLL)
+    return fail(FL_EUNSUPPORTED, "%s: too many (layer, sequence, head) triples", fn);
+  if (r >= 2) {
+    if (K_prev < 1 || K_prev > cache->S) return fail(FL_EINVAL, "%s: K_prev = %d outside [1, S]", fn, K_prev);
+    if (r == 2 && K_prev != cache->S) return fail(FL_EINVAL, "%s: at r = 2 K_prev must be S", fn);
+    if (K_r < 1 || K_r > K_prev) return fail(FL_EINVAL, "%s: K_r = %d outside [1, K_prev = %d]", fn, K_r, K_prev);
+    if (K_r < K_prev && K_prev > kTopkMax)
+      return fail(FL_EUNSUPPORTED, "%s: %d candidates (at most %d)", fn, K_prev, kTopkMax);
+  }
+  fl::DecodeArgs a{};
+  a.c = geo;
+  a.r = r;
+  a.dt = dtype;
+  a.q = q;
+  a.K_prev = K_prev;
+  a.K = K_r;
+  a.O = state->O; a.U = state->U; a.M = state->M; a.lse = state->lse;
+  a.logits = state->logits;
+  a.sel = state->sel;
+  hipError_t e = fl::launch_decode(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return FL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,164 @@
+// Device-side helpers shared by the FlashLoop kernels (gfx950, wave64).
+//
+// Record geometry and dequantization follow the packed cache layout declared
+// in include/flashloop.h (p1 §4.3 and App. G: a quantized anchor plus packed
+// low-bit residual streams read directly by the attention kernels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "flashloop.h"
+
+namespace fl {
+
+constexpr int kWave = 64;
+constexpr int kGroup = 32;  // quantization group (dims)
+
+// ---------------------------------------------------------------- geometry
+// Kernel-side copy of the cache description (passed by value).
+struct CacheGeo {
+  int L, B, H, S, d, R;
+  int n[FL_MAX_LOOPS + 1];
+  int bits[FL_MAX_LOOPS + 1];
+  int res_rb[FL_MAX_LOOPS + 1];  // residual record bytes per loop
+  int base_rb;                   // base record bytes
+  const int32_t* rows[FL_MAX_LOOPS + 1];
+  const int32_t* slot[FL_MAX_LOOPS + 1];
+  const uint8_t* base;
+  const uint8_t* res[FL_MAX_LOOPS + 1];
+};
+
+__host__ __device__ inline int pad16(int n) { return (n + 15) & ~15; }
+__host__ __device__ inline int base_record_bytes(int d) { return pad16(2 * d + 4 * (d / kGroup)); }
+__host__ __device__ inline int residual_record_bytes(int d, int bits) {
+  return pad16(2 * (d * bits / 8) + 8 * (d / kGroup));
+}
+
+// Address of the base record of token j of (layer l, seq b, head h).
+__device__ inline const uint8_t* base_rec(const CacheGeo& c, int l, int b, int h, int j) {
+  long long idx = (((long long)l * c.B + b) * c.H + h) * c.S + j;
+  return c.base + idx * c.base_rb;
+}
+// Address of the loop-r residual record number t (t = slot) of (l, b, h).
+__device__ inline const uint8_t* res_rec(const CacheGeo& c, int r, int l, int b, int h, int t) {
+  long long idx = (((long long)l * c.B + b) * c.H + h) * c.n[r] + t;
+  return c.res[r] + idx * c.res_rb[r];
+}
+
+// ---------------------------------------------------------------- numbers
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+// Round-to-nearest-even float -> bf16 bits (finite inputs).
+__device__ inline uint16_t f32_to_bf16(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ inline float round_bf16(float x) { return bf16_to_f32(f32_to_bf16(x)); }
+
+__device__ inline float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+__device__ inline uint16_t f2h_rn(float x) { return __half_as_ushort(__float2half_rn(x)); }
+
+// fp16 rounded toward +inf of a finite float within the fp16 range.
+__device__ inline uint16_t f2h_up(float y) {
+  uint16_t h = f2h_rn(y);
+  if (h2f(h) < y) {
+    if (h == 0x8000u) h = 0x0001u;           // -0 -> smallest positive subnormal
+    else if (h & 0x8000u) h = (uint16_t)(h - 1u);  // negative: magnitude shrinks
+    else h = (uint16_t)(h + 1u);
+  }
+  return h;
+}
+// fp16 rounded toward -inf of a finite float within the fp16 range.
+__device__ inline uint16_t f2h_down(float y) {
+  uint16_t h = f2h_rn(y);
+  if (h2f(h) > y) {
+    if (h == 0x0000u) h = 0x8001u;           // +0 -> smallest negative subnormal
+    else if (h & 0x8000u) h = (uint16_t)(h + 1u);  // negative: magnitude grows
+    else h = (uint16_t)(h - 1u);
+  }
+  return h;
+}
+
+// Loads of one input element (float or bf16 bits) as float.
+template <typename T> __device__ inline float load_elem(const T* p);
+template <> __device__ inline float load_elem<float>(const float* p) { return *p; }
+template <> __device__ inline float load_elem<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+
+// ---------------------------------------------------------------- dequant
+// Element e (0 <= e < d) of K (kv = 0) or V (kv = 1) of a base record.
+__device__ inline float base_elem(const uint8_t* rec, int d, int kv, int e) {
+  int8_t c = (int8_t)rec[kv * d + e];
+  const uint16_t* sc = (const uint16_t*)(rec + 2 * d) + kv * (d / kGroup);
+  return (float)c * h2f(sc[e / kGroup]);
+}
+// Dequantized residual element: fma(code, scale, zero), one rounding.
+__device__ inline float res_elem(const uint8_t* rec, int d, int bits, int kv, int e) {
+  int C = d * bits / 8;
+  int per = 8 / bits;
+  uint8_t byte = rec[kv * C + e / per];
+  int code = (byte >> (bits * (e % per))) & ((1 << bits) - 1);
+  const uint16_t* meta = (const uint16_t*)(rec + 2 * C);
+  int G = d / kGroup;
+  float s = h2f(meta[(2 * kv) * G + e / kGroup]);
+  float z = h2f(meta[(2 * kv + 1) * G + e / kGroup]);
+  return __builtin_fmaf((float)code, s, z);
+}
+
+// Reconstruction x_hat^(r) of element e of token j: the base plus the
+// residuals of loops 2..r in which j was active (sets are nested, so the
+// chain stops at the first loop where j is inactive).
+__device__ inline float chain_elem(const CacheGeo& c, int r, int l, int b, int h, int j, int kv, int e) {
+  float x = base_elem(base_rec(c, l, b, h, j), c.d, kv, e);
+  for (int rr = 2; rr <= r; ++rr) {
+    int t = c.slot[rr][(long long)b * c.S + j];
+    if (t < 0) break;
+    x = x + res_elem(res_rec(c, rr, l, b, h, t), c.d, c.bits[rr], kv, e);
+  }
+  return x;
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Exclusive prefix sum over a block of NT threads (NT a multiple of 64).
+// Returns the exclusive prefix of `v`; *total receives the block sum.
+template <int NT>
+__device__ inline int block_exclusive_scan(int v, int* smem /* >= NT/64 + 1 ints */, int* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) smem[wid] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int w = 0; w < NT / kWave; ++w) {
+      int t = smem[w];
+      smem[w] = acc;
+      acc += t;
+    }
+    smem[NT / kWave] = acc;
+  }
+  __syncthreads();
+  int res = smem[wid] + x - v;
+  *total = smem[NT / kWave];
+  __syncthreads();
+  return res;
+}
+
+}  // namespace fl

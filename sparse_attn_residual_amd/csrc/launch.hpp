@@ -1,0 +1,66 @@
+// Host-side launchers of the FlashLoop kernels, called by the C ABI layer
+// (abi.cpp) after it has validated every argument.  Each returns the HIP
+// status of its launches.
+#pragma once
+
+#include "common.hpp"
+
+namespace fl {
+
+// ---- fl_kv_resq
+hipError_t launch_quant_base(const CacheGeo& c, const void* k, const void* v, fl_dtype dt, uint8_t* base,
+                             hipStream_t st);
+hipError_t launch_build_slot(const CacheGeo& c, int r, int32_t* slot, hipStream_t st);
+hipError_t launch_quant_res(const CacheGeo& c, int r, const void* k, const void* v, fl_dtype dt, uint8_t* res,
+                            hipStream_t st);
+
+// ---- selection (top-K of keys per problem; ties to the lower position).
+// keys [P][key_stride] (first n valid), cand [P][cand_stride] or NULL (iota);
+// writes sel_out [P][sel_stride] ascending and, if keys_out is set, the keys
+// of the selected entries in the same order.  In place (keys_out == keys,
+// sel_out == cand) is allowed: every block reads its inputs before writing.
+hipError_t launch_topk(const float* keys, long long key_stride, const int32_t* cand, long long cand_stride,
+                       int P, int n, int K, int32_t* sel_out, long long sel_stride, float* keys_out,
+                       long long keys_out_stride, hipStream_t st);
+// sel[p][t] = cand ? cand[p][t] : t for t < K
+hipError_t launch_copy_sel(const int32_t* cand, int P, int K, int32_t* sel, hipStream_t st);
+
+// ---- prefill attention family (one layer: l = 0).
+struct AttnArgs {
+  CacheGeo c;
+  int r;                 // loop whose chain / state is used
+  fl_dtype dt;
+  const void* q;         // [B][H][nq][d], rows of loop r (r == 1: all S)
+  int K;                 // number of selected columns (r >= 2)
+  const int32_t* sel;    // [B][H][K] or NULL (dense loop 1)
+  float* O;
+  float* U;
+  float* M;
+  float* lse;
+};
+// Loop r attention (dense when r == 1, sparse otherwise).
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+// Cached mass and reused part for loop r: reads loop r-1 state, q_prev and
+// chains to r-1; rows A_r; columns sel (S_r).
+hipError_t launch_um(const AttnArgs& a, hipStream_t st);
+// Column mass of the candidates cand (NULL: all S) over rows A_r with loop
+// r-1's probabilities.
+hipError_t launch_mass(const AttnArgs& a, const int32_t* cand, int K_prev, float* mass, hipStream_t st);
+
+// ---- decode
+struct DecodeArgs {
+  CacheGeo c;
+  int r;
+  fl_dtype dt;
+  const void* q;     // [L][B][H][d]
+  int K_prev, K;
+  float* O;
+  float* U;
+  float* M;
+  float* lse;
+  float* logits;     // [L][B][H][S]
+  int32_t* sel;      // [L][B][H][S]
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+
+}  // namespace fl

@@ -1,0 +1,191 @@
+// fl_kv_resq kernels: the quantized loop-1 base and the low-bit residuals of
+// the active tokens against the reconstructed previous loop (p1 §4.3, §D.3;
+// guide §3).  HBM-bound: every thread owns one 32-dim group of one token's K
+// or V row, so a token's 2*G threads read its K and V rows contiguously.
+//
+// The operation sequence is fixed so that codes are bit-exact: fp32 max/min
+// and subtraction, IEEE fp32 division, round-half-even, clamp, directed fp16
+// rounding of scale (up) and zero (down); no fused multiply-add except the
+// single-rounding residual dequantization fma(code, scale, zero).  The file is
+// compiled with floating-point contraction off.
+#include "launch.hpp"
+
+namespace fl {
+
+template <typename T>
+__device__ inline void load_group(const T* src, float* x) {
+#pragma unroll
+  for (int i = 0; i < kGroup; ++i) x[i] = load_elem<T>(src + i);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_quant_base(const T* __restrict__ k, const T* __restrict__ v,
+                                                    uint8_t* __restrict__ base, long long ntok, int d, int rb) {
+  const int G = d / kGroup;
+  long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  long long tok = gid / (2 * G);
+  int sub = (int)(gid - tok * (2 * G));
+  if (tok >= ntok) return;
+  const int kv = sub >= G;
+  const int g = sub - kv * G;
+  const T* src = (kv ? v : k) + tok * d + g * kGroup;
+  float x[kGroup];
+  load_group<T>(src, x);
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kGroup; ++i) a = fmaxf(a, fabsf(x[i]));
+  const uint16_t sh = f2h_up(a / 127.0f);
+  const float s = h2f(sh);
+  uint32_t packed[kGroup / 4];
+#pragma unroll
+  for (int w = 0; w < kGroup / 4; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      int c = 0;
+      if (s != 0.0f) {
+        float q = rintf(x[4 * w + t] / s);
+        q = fminf(fmaxf(q, -127.0f), 127.0f);
+        c = (int)q;
+      }
+      word |= ((uint32_t)(uint8_t)(int8_t)c) << (8 * t);
+    }
+    packed[w] = word;
+  }
+  uint8_t* rec = base + tok * rb;
+  uint4* dst = (uint4*)(rec + kv * d + g * kGroup);
+  dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+  ((uint16_t*)(rec + 2 * d))[kv * G + g] = sh;
+  if (sub == 0) {
+    for (int p = 2 * d + 4 * G; p < rb; ++p) rec[p] = 0;  // deterministic padding
+  }
+}
+
+// One thread per (active row, group, K|V) of loop r >= 2.
+template <typename T>
+__global__ __launch_bounds__(256) void k_quant_res(CacheGeo c, int r, const T* __restrict__ k,
+                                                   const T* __restrict__ v, uint8_t* __restrict__ res) {
+  const int d = c.d, G = d / kGroup, nr = c.n[r], bits = c.bits[r];
+  long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  long long row = gid / (2 * G);  // over [L][B][H][n_r]
+  int sub = (int)(gid - row * (2 * G));
+  long long total = (long long)c.L * c.B * c.H * nr;
+  if (row >= total) return;
+  const int kv = sub >= G;
+  const int g = sub - kv * G;
+  const int t = (int)(row % nr);
+  long long lbh = row / nr;
+  const int h = (int)(lbh % c.H);
+  const int b = (int)((lbh / c.H) % c.B);
+  const int l = (int)(lbh / ((long long)c.H * c.B));
+  const int j = c.rows[r][(long long)b * nr + t];
+
+  float x[kGroup];
+  load_group<T>((kv ? v : k) + row * d + g * kGroup, x);
+  float delta[kGroup];
+  float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kGroup; ++i) {
+    const float prev = chain_elem(c, r - 1, l, b, h, j, kv, g * kGroup + i);
+    delta[i] = x[i] - prev;
+    lo = i == 0 ? delta[i] : fminf(lo, delta[i]);
+    hi = i == 0 ? delta[i] : fmaxf(hi, delta[i]);
+  }
+  const float levels = (float)((1 << bits) - 1);
+  const uint16_t zh = f2h_down(lo);
+  const float z = h2f(zh);
+  const float w = hi - z;
+  const uint16_t sh = f2h_up(w / levels);
+  const float s = h2f(sh);
+  int code[kGroup];
+#pragma unroll
+  for (int i = 0; i < kGroup; ++i) {
+    int cc = 0;
+    if (s != 0.0f) {
+      float q = rintf((delta[i] - z) / s);
+      q = fminf(fmaxf(q, 0.0f), levels);
+      cc = (int)q;
+    }
+    code[i] = cc;
+  }
+  const int C = d * bits / 8;
+  uint8_t* rec = res + row * c.res_rb[r];
+  if (bits == 4) {
+    uint32_t wds[4];
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int t8 = 0; t8 < 8; ++t8) word |= (uint32_t)code[8 * w4 + t8] << (4 * t8);
+      wds[w4] = word;
+    }
+    *(uint4*)(rec + kv * C + g * 16) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+  } else {
+    uint32_t wds[2];
+#pragma unroll
+    for (int w2 = 0; w2 < 2; ++w2) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int t16 = 0; t16 < 16; ++t16) word |= (uint32_t)code[16 * w2 + t16] << (2 * t16);
+      wds[w2] = word;
+    }
+    *(uint2*)(rec + kv * C + g * 8) = make_uint2(wds[0], wds[1]);
+  }
+  uint16_t* meta = (uint16_t*)(rec + 2 * C);
+  meta[(2 * kv) * G + g] = sh;
+  meta[(2 * kv + 1) * G + g] = zh;
+  if (sub == 0) {
+    for (int p = 2 * C + 8 * G; p < c.res_rb[r]; ++p) rec[p] = 0;
+  }
+}
+
+// slot[b][j] = index of j in rows[b][0..n) or -1 (binary search; rows ascending).
+__global__ void k_build_slot(const int32_t* __restrict__ rows, int n, int S, int B, int32_t* __restrict__ slot) {
+  long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long long)B * S) return;
+  int b = (int)(gid / S), j = (int)(gid % S);
+  const int32_t* rb = rows + (long long)b * n;
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if (rb[mid] < j) lo = mid + 1; else hi = mid;
+  }
+  slot[gid] = (lo < n && rb[lo] == j) ? lo : -1;
+}
+
+hipError_t launch_quant_base(const CacheGeo& c, const void* k, const void* v, fl_dtype dt, uint8_t* base,
+                             hipStream_t st) {
+  long long ntok = (long long)c.L * c.B * c.H * c.S;
+  long long threads = ntok * 2 * (c.d / kGroup);
+  dim3 grid((unsigned)((threads + 255) / 256));
+  if (dt == FL_BF16)
+    hipLaunchKernelGGL(k_quant_base<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)k, (const uint16_t*)v,
+                       base, ntok, c.d, c.base_rb);
+  else
+    hipLaunchKernelGGL(k_quant_base<float>, grid, dim3(256), 0, st, (const float*)k, (const float*)v, base, ntok,
+                       c.d, c.base_rb);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_slot(const CacheGeo& c, int r, int32_t* slot, hipStream_t st) {
+  long long n = (long long)c.B * c.S;
+  hipLaunchKernelGGL(k_build_slot, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, c.rows[r], c.n[r], c.S, c.B,
+                     slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_res(const CacheGeo& c, int r, const void* k, const void* v, fl_dtype dt, uint8_t* res,
+                            hipStream_t st) {
+  long long rowsn = (long long)c.L * c.B * c.H * c.n[r];
+  long long threads = rowsn * 2 * (c.d / kGroup);
+  dim3 grid((unsigned)((threads + 255) / 256));
+  if (dt == FL_BF16)
+    hipLaunchKernelGGL(k_quant_res<uint16_t>, grid, dim3(256), 0, st, c, r, (const uint16_t*)k, (const uint16_t*)v,
+                       res);
+  else
+    hipLaunchKernelGGL(k_quant_res<float>, grid, dim3(256), 0, st, c, r, (const float*)k, (const float*)v, res);
+  return hipGetLastError();
+}
+
+}  // namespace fl

@@ -1,0 +1,119 @@
+"""Shared driver of the GPU parity tests: runs the HIP path through the C ABI
+binding on seeded workloads and collects what the oracle is compared with.
+Inputs come from ``workloads`` only; no expected value comes from here."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import workloads
+
+DEV = "cuda"
+
+
+def tdtype(cfg):
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+def fl_dtype(cfg):
+    import sparse_attn_residual_amd as fl
+    return fl.FL_BF16 if cfg.dtype == "bf16" else fl.FL_F32
+
+
+def upload(x: np.ndarray, cfg) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV).to(tdtype(cfg)).contiguous()
+
+
+def rows_list(cfg, rows):
+    """rows[b][r] -> per-loop [B][n_r] arrays."""
+    return [np.stack([rows[b][r] for b in range(cfg.B)]) for r in range(cfg.R)]
+
+
+def run_prefill(cfg, rows, slices, *, mass_in=None, K_budget=None, mfma=None):
+    """All loops of one layer.  mass_in: optional {r: float32 [B][H][K_prev]}.
+    Returns dict with per-loop snapshots (index r-1), sel, mass and the cache."""
+    import sparse_attn_residual_amd as fl
+    K_budget = cfg.K if K_budget is None else K_budget
+    R, B, H, S, d = cfg.R, cfg.B, cfg.H, cfg.S, cfg.d
+    cache = fl.CacheBuffers(1, B, H, S, d, R, cfg.n, cfg.bits, rows_list(cfg, rows))
+    st = fl.PrefillState(B, H, S, d)
+    dt = fl_dtype(cfg)
+    qs = [upload(workloads.stack_loop(cfg, slices, r, "q"), cfg) for r in range(1, R + 1)]
+    out = dict(state=[], sel=[None], mass=[None], cache=cache, q=qs)
+    K_prev = S
+    sel_prev = None
+    for r in range(1, R + 1):
+        k = upload(workloads.stack_loop(cfg, slices, r, "k"), cfg)
+        v = upload(workloads.stack_loop(cfg, slices, r, "v"), cfg)
+        fl.fl_kv_resq(cache.fl, r, k, v, dt)
+        sel = None
+        K = 0
+        if r >= 2:
+            K = min(K_budget, K_prev)
+            sel = torch.empty(B, H, K, dtype=torch.int32, device=DEV)
+            mass = torch.empty(B, H, K_prev, dtype=torch.float32, device=DEV)
+            mi = None
+            if mass_in is not None and r in mass_in:
+                mi = torch.from_numpy(np.ascontiguousarray(mass_in[r], np.float32)).to(DEV)
+            fl.fl_colsel(cache.fl, r, qs[r - 2], dt, st.fl, K_prev, sel_prev, K, mi, mass, sel)
+            out["sel"].append(sel.cpu().numpy())
+            out["mass"].append(mass.cpu().numpy())
+        fl.fl_loop_attn(cache.fl, r, qs[r - 1], dt, K, sel, st.fl)
+        torch.cuda.synchronize()
+        out["state"].append({k2: v2.cpu().numpy() for k2, v2 in st.snapshot().items()})
+        if r >= 2:
+            sel_prev, K_prev = sel, K
+        del k, v
+    return out
+
+
+def near_tie_ok(sel_gpu, sel_orc, mass_orc, cand, eps):
+    """Selections may differ only between candidates whose masses are within
+    eps * max mass of each other."""
+    a, b = set(sel_gpu.tolist()), set(sel_orc.tolist())
+    if a == b:
+        return True, 0
+    pos = {int(j): t for t, j in enumerate(cand)}
+    only_g = [mass_orc[pos[j]] for j in a - b]
+    only_o = [mass_orc[pos[j]] for j in b - a]
+    gap = max(only_o) - min(only_g)
+    return gap <= eps * float(np.max(mass_orc)), len(a - b)
+
+
+def build_decode_cache(cfg, rows, slices, L=None):
+    """Quantize layer 0 through fl_kv_resq, then copy it to every layer."""
+    import sparse_attn_residual_amd as fl
+    L = cfg.L if L is None else L
+    cache = fl.CacheBuffers(L, cfg.B, cfg.H, cfg.S, cfg.d, cfg.R, cfg.n, cfg.bits, rows_list(cfg, rows))
+    view = cache.layer_view(0)
+    dt = fl_dtype(cfg)
+    for r in range(1, cfg.R + 1):
+        k = upload(workloads.stack_loop(cfg, slices, r, "k"), cfg)
+        v = upload(workloads.stack_loop(cfg, slices, r, "v"), cfg)
+        fl.fl_kv_resq(view, r, k, v, dt)
+        torch.cuda.synchronize()
+        del k, v
+    if L > 1:
+        cache.replicate_layer0()
+    return cache
+
+
+def run_decode(cfg, cache, queries, K_budget=None):
+    """queries[r-1]: float32 [L][B][H][d].  Returns per-loop snapshots."""
+    import sparse_attn_residual_amd as fl
+    K_budget = cfg.K if K_budget is None else K_budget
+    L = queries[0].shape[0]
+    st = fl.DecodeState(L, cfg.B, cfg.H, cfg.S, cfg.d)
+    dt = fl_dtype(cfg)
+    out = []
+    K_prev = cfg.S
+    for r in range(1, cfg.R + 1):
+        q = upload(queries[r - 1], cfg)
+        K = cfg.S if r == 1 else min(K_budget, K_prev)
+        fl.fl_loop_decode(cache.fl, r, q, dt, K_prev, K, st.fl)
+        torch.cuda.synchronize()
+        snap = dict(O=st.O.cpu().numpy(), U=st.U.cpu().numpy(), M=st.M.cpu().numpy(), lse=st.lse.cpu().numpy(),
+                    logits=st.logits[..., :K].cpu().numpy(), sel=st.sel[..., :K].cpu().numpy() if r > 1 else None)
+        out.append(snap)
+        K_prev = K
+    return out

@@ -1,0 +1,115 @@
+"""Host-side checks of the C ABI: exported symbols, struct layout, and the
+validation layer (every call below fails validation, so nothing launches)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashloop.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fl_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    import sparse_attn_residual_amd as fl
+    lib = ctypes.CDLL(fl.lib_path())
+    names = _declared()
+    assert {"fl_kv_resq", "fl_colsel", "fl_loop_attn", "fl_loop_decode"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layout_matches_c(tmp_path):
+    import sparse_attn_residual_amd as fl
+    prog = tmp_path / "layout.c"
+    prog.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "flashloop.h"\n'
+                    'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(fl_cache),'
+                    'offsetof(fl_cache,n), offsetof(fl_cache,rows), offsetof(fl_cache,slot),'
+                    'offsetof(fl_cache,base), offsetof(fl_cache,res), sizeof(fl_state), sizeof(fl_dstate));return 0;}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.dirname(HEADER), str(prog), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    C = fl.FlCache
+    want = [ctypes.sizeof(C), C.n.offset, C.rows.offset, C.slot.offset, C.base.offset, C.res.offset,
+            ctypes.sizeof(fl.FlState), ctypes.sizeof(fl.FlDState)]
+    assert got == want
+
+
+def _cache(**kw):
+    import sparse_attn_residual_amd as fl
+    c = fl.FlCache()
+    c.L, c.B, c.H, c.S, c.d, c.R = 1, 1, 2, 64, 64, 2
+    c.n[1], c.n[2] = 64, 32
+    c.bits[1], c.bits[2] = 8, 4
+    c.base = 0x10000
+    c.rows[2] = c.slot[2] = 0x20000
+    c.res[2] = 0x30000
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _status(fn, *args):
+    import sparse_attn_residual_amd as fl
+    lib = fl._lib._lib
+    return getattr(lib, fn)(*args), fl.fl_last_error()
+
+
+def test_validation_errors():
+    import sparse_attn_residual_amd as fl
+    EINVAL, EUNSUP = 1, 2
+    ok_ptr = 0x40000
+    st, msg = _status("fl_kv_resq", None, 1, ok_ptr, ok_ptr, fl.FL_F32, None)
+    assert st == EINVAL and "cache is NULL" in msg
+    st, msg = _status("fl_kv_resq", ctypes.byref(_cache(d=96)), 1, ok_ptr, ok_ptr, fl.FL_F32, None)
+    assert st == EUNSUP and "head dim" in msg
+    st, msg = _status("fl_kv_resq", ctypes.byref(_cache()), 3, ok_ptr, ok_ptr, fl.FL_F32, None)
+    assert st == EINVAL and "outside" in msg
+    bad = _cache()
+    bad.bits[2] = 3
+    st, msg = _status("fl_kv_resq", ctypes.byref(bad), 2, ok_ptr, ok_ptr, fl.FL_F32, None)
+    assert st == EUNSUP and "bits" in msg
+    st, msg = _status("fl_kv_resq", ctypes.byref(_cache()), 1, ok_ptr + 4, ok_ptr, fl.FL_F32, None)
+    assert st == EINVAL and "aligned" in msg
+    st, msg = _status("fl_kv_resq", ctypes.byref(_cache()), 1, ok_ptr, ok_ptr, 7, None)
+    assert st == EUNSUP and "dtype" in msg
+    nest = _cache()
+    nest.n[2] = 65
+    st, msg = _status("fl_kv_resq", ctypes.byref(nest), 1, ok_ptr, ok_ptr, fl.FL_F32, None)
+    assert st == EINVAL and "nested" in msg
+    s = fl.FlState(ok_ptr, ok_ptr, ok_ptr, ok_ptr)
+    st, msg = _status("fl_colsel", ctypes.byref(_cache()), 2, ok_ptr, fl.FL_F32, ctypes.byref(s), 64, None, 65,
+                      None, None, ok_ptr, None, 0, None)
+    assert st == EINVAL and "K_r" in msg
+    st, msg = _status("fl_colsel", ctypes.byref(_cache()), 2, ok_ptr, fl.FL_F32, ctypes.byref(s), 64, None, 10,
+                      None, None, ok_ptr, None, 0, None)
+    assert st == EINVAL and "workspace" in msg
+    st, msg = _status("fl_colsel", ctypes.byref(_cache()), 1, ok_ptr, fl.FL_F32, ctypes.byref(s), 64, None, 10,
+                      None, None, ok_ptr, None, 0, None)
+    assert st == EINVAL
+    st, msg = _status("fl_loop_attn", ctypes.byref(_cache()), 2, ok_ptr, fl.FL_F32, 10, None, ctypes.byref(s),
+                      None, 0, None)
+    assert st == EINVAL and "sel" in msg
+    ds = fl.FlDState(ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr)
+    st, msg = _status("fl_loop_decode", ctypes.byref(_cache()), 1, ok_ptr, fl.FL_F32, 64, 64, ctypes.byref(ds),
+                      None, 0, None)
+    assert st == EUNSUP and "decode" in msg   # head dim 64
+    c128 = _cache(d=128)
+    st, msg = _status("fl_loop_decode", ctypes.byref(c128), 2, ok_ptr, fl.FL_F32, 30, 10, ctypes.byref(ds),
+                      None, 0, None)
+    assert st == EINVAL and "K_prev" in msg
+    assert fl.fl_workspace_bytes(fl.FL_WS_COLSEL, _cache(), 2, 64, 10) == 1 * 2 * 64 * 4
+
+
+def test_binding_raises():
+    import sparse_attn_residual_amd as fl
+    with pytest.raises(fl.FlashLoopError) as ei:
+        fl.fl_kv_resq(_cache(d=96), 1, 0x40000, 0x40000, fl.FL_F32, stream=0)
+    assert ei.value.status == 2

@@ -1,0 +1,90 @@
+"""GPU parity of fl_loop_decode with the CPU oracle's decode step."""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import decode, prefill, quant
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _decode_case(cfg, tol, rel):
+    import tests.gpu_harness as gh
+    rows, slices = workloads.gen_batch(cfg)
+    cache = gh.build_decode_cache(cfg, rows, slices)
+    qs = workloads.decode_queries(cfg)
+    gpu = gh.run_decode(cfg, cache, qs)
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            s = slices[(b, h)]
+            _, krec = quant.quantize_chain(s.k, s.rows, list(cfg.bits))
+            _, vrec = quant.quantize_chain(s.v, s.rows, list(cfg.bits))
+            for l in range(cfg.L):
+                force = {r + 1: gpu[r]["sel"][l, b, h] for r in range(1, cfg.R)}
+                orc = decode.decode_slice(krec, vrec, [q[l, b, h] for q in qs], cfg.K, sel_force=force)
+                cand = np.arange(cfg.S)
+                for r in range(cfg.R):
+                    g = {k: gpu[r][k][l, b, h] for k in ("O", "U", "M", "lse")}
+                    o = orc[r]
+                    if r >= 1:
+                        key = orc[r - 1]["logits"]
+                        own = prefill.topk(key, cand, min(cfg.K, len(cand)))
+                        ok, nd = gh.near_tie_ok(gpu[r]["sel"][l, b, h], own, key - key.min(), cand, 1e-5 if not rel else 2e-3)
+                        assert ok, (l, b, h, r + 1, nd)
+                        cand = gpu[r]["sel"][l, b, h]
+                    lg = gpu[r]["logits"][l, b, h]
+                    assert np.max(np.abs(lg - o["logits"])) <= 1e-4 * max(1.0, np.max(np.abs(o["logits"])))
+                    if rel:
+                        err = np.linalg.norm(g["O"] - o["O"]) / np.linalg.norm(o["O"])
+                        assert err <= tol, (l, b, h, r + 1, err)
+                    else:
+                        assert np.max(np.abs(g["O"] - o["O"])) <= tol, (l, b, h, r + 1)
+                    assert abs(g["lse"] - o["lse"]) <= tol * max(1.0, abs(o["lse"]))
+                    assert abs(g["M"] - o["M"]) <= tol
+                    assert np.max(np.abs(g["U"] - o["U"])) <= tol * max(1.0, np.max(np.abs(o["O"])))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_small(dtype):
+    cfg = workloads.custom(name="decode-small", dtype=dtype, B=2, H=2, d=128, S=1000, R=4, act=(1, 0.3, 0.15, 0.08),
+                           col="0.10", bits=(8, 4, 4, 2), gamma=0.5, lognormal=0.5, L=2, decode=True, seed=1)
+    _say("decode", dtype, cfg)
+    _decode_case(cfg, 1e-5, rel=False)
+
+
+def test_decode_pruned_every_loop():
+    """Budgets that shrink every loop exercise the reuse update at r >= 3."""
+    import tests.gpu_harness as gh
+    cfg = workloads.custom(name="decode-prune", dtype="f32", B=1, H=2, d=128, S=777, R=4, act=(1, 0.5, 0.3, 0.2),
+                           col="0.3", bits=(8, 4, 2, 4), lognormal=0.5, L=1, decode=True, seed=2)
+    _say("decode prune", cfg)
+    rows, slices = workloads.gen_batch(cfg)
+    cache = gh.build_decode_cache(cfg, rows, slices)
+    qs = workloads.decode_queries(cfg)
+    budgets = [None, 233, 120, 61]
+    import sparse_attn_residual_amd as fl
+    import torch
+    st = fl.DecodeState(cfg.L, cfg.B, cfg.H, cfg.S, cfg.d)
+    K_prev = cfg.S
+    snaps = []
+    for r in range(1, cfg.R + 1):
+        K = cfg.S if r == 1 else budgets[r - 1]
+        fl.fl_loop_decode(cache.fl, r, gh.upload(qs[r - 1], cfg), fl.FL_F32, K_prev, K, st.fl)
+        torch.cuda.synchronize()
+        snaps.append(dict(O=st.O.cpu().numpy(), M=st.M.cpu().numpy(), sel=st.sel[..., :K].cpu().numpy()))
+        K_prev = K
+    for h in range(cfg.H):
+        s = slices[(0, h)]
+        _, krec = quant.quantize_chain(s.k, s.rows, list(cfg.bits))
+        _, vrec = quant.quantize_chain(s.v, s.rows, list(cfg.bits))
+        T = cfg.S
+        # the oracle with the same per-loop budgets
+        force = {r + 1: snaps[r]["sel"][0, 0, h] for r in range(1, cfg.R)}
+        orc = decode.decode_slice(krec, vrec, [q[0, 0, h] for q in qs], 10 ** 9, sel_force=force)
+        for r in range(cfg.R):
+            assert np.max(np.abs(snaps[r]["O"][0, 0, h] - orc[r]["O"])) <= 1e-5, (h, r + 1)
+            assert abs(snaps[r]["M"][0, 0, h] - orc[r]["M"]) <= 1e-5

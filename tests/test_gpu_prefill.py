@@ -1,0 +1,142 @@
+"""GPU parity of the prefill path (fl_kv_resq, fl_colsel, fl_loop_attn) with
+the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import prefill, records
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _oracle_slices(cfg, rows, slices, gpu, heads):
+    """Oracle per (b, h), teacher-forced with the GPU's selections."""
+    res = {}
+    for b in range(cfg.B):
+        for h in heads:
+            s = slices[(b, h)]
+            force = {r + 1: gpu["sel"][r][b, h] for r in range(1, cfg.R)}
+            res[(b, h)] = prefill.prefill_slice(s.rows, s.q, s.k, s.v, K_budget=cfg.K, bits=cfg.bits,
+                                                dtype=cfg.dtype, sel_force=force)
+    return res
+
+
+def _check_records(cfg, gpu, orc, heads):
+    cache = gpu["cache"]
+    base = cache.base_records().cpu().numpy()
+    for b in range(cfg.B):
+        for h in heads:
+            o = orc[(b, h)]
+            ks, vs = o["k_streams"], o["v_streams"]
+            want = records.pack_base(ks[0]["codes"], ks[0]["scale"], vs[0]["codes"], vs[0]["scale"])
+            assert np.array_equal(base[0, b, h], want), (b, h, "base")
+            for r in range(2, cfg.R + 1):
+                got = cache.res_records(r).cpu().numpy()[0, b, h]
+                k, v = ks[r - 1], vs[r - 1]
+                want = records.pack_residual(k["codes"], k["scale"], k["zero"], v["codes"], v["scale"], v["zero"],
+                                             cfg.bits[r - 1])
+                assert np.array_equal(got, want), (b, h, r)
+
+
+def _check_outputs(cfg, gpu, orc, heads, tol, rel):
+    for b in range(cfg.B):
+        for h in heads:
+            o = orc[(b, h)]
+            for r in range(cfg.R):
+                g = gpu["state"][r]
+                st = o["state"][r]
+                O = g["O"][b, h]
+                if rel:
+                    err = np.linalg.norm(O - st.O) / np.linalg.norm(st.O)
+                    assert err <= tol, (b, h, r + 1, "O", err)
+                    fin = np.isfinite(st.lse)
+                    assert np.array_equal(fin, np.isfinite(g["lse"][b, h]))
+                    assert np.max(np.abs(g["lse"][b, h][fin] - st.lse[fin])) <= 8 * tol * max(1, np.max(np.abs(st.lse[fin])))
+                    assert np.max(np.abs(g["M"][b, h] - st.M)) <= 4 * tol
+                else:
+                    assert np.max(np.abs(O - st.O)) <= tol, (b, h, r + 1, "O", np.max(np.abs(O - st.O)))
+                    fin = np.isfinite(st.lse)
+                    assert np.array_equal(fin, np.isfinite(g["lse"][b, h]))
+                    assert np.max(np.abs(g["lse"][b, h][fin] - st.lse[fin])) <= tol
+                    assert np.max(np.abs(g["M"][b, h] - st.M)) <= tol
+                if r >= 1:
+                    m_or = o["mass"][r]
+                    m_g = gpu["mass"][r][b, h]
+                    scale = np.max(m_or)
+                    assert np.max(np.abs(m_g - m_or)) <= (tol if not rel else 4 * tol) * max(scale, 1.0), (b, h, r + 1)
+
+
+@pytest.mark.parametrize("cfgid", [0])
+def test_prefill_fp32_parity(cfgid):
+    import tests.gpu_harness as gh
+    cfg = workloads.CONFIGS[cfgid]
+    _say("prefill parity", cfg.name)
+    rows, slices = workloads.gen_batch(cfg)
+    gpu = gh.run_prefill(cfg, rows, slices)
+    heads = list(range(cfg.H))
+    orc = _oracle_slices(cfg, rows, slices, gpu, heads)
+    _check_records(cfg, gpu, orc, heads)
+    # teacher forcing is only allowed over near ties
+    for b in range(cfg.B):
+        for h in heads:
+            s = slices[(b, h)]
+            cand = np.arange(cfg.S)
+            for r in range(1, cfg.R):
+                m = orc[(b, h)]["mass"][r]
+                own = prefill.topk(m, cand, min(cfg.K, len(cand)))
+                ok, ndiff = gh.near_tie_ok(gpu["sel"][r][b, h], own, m, cand, 1e-5)
+                assert ok, (b, h, r + 1, ndiff)
+                cand = gpu["sel"][r][b, h]
+    _check_outputs(cfg, gpu, orc, heads, 1e-5, rel=False)
+
+
+def test_topk_bitexact_with_mass_in():
+    """Given the same fp32 masses, the GPU selection equals the oracle's."""
+    import tests.gpu_harness as gh
+    cfg = workloads.custom(dtype="f32", B=2, H=3, d=64, S=700, R=2, act=(1, 0.4), col="0.13", bits=(8, 4))
+    _say("topk mass_in", cfg)
+    rows, slices = workloads.gen_batch(cfg)
+    rng = np.random.default_rng(0)
+    # masses with many exact ties (quantized values) exercise the tie rule
+    mass = (np.round(rng.random((cfg.B, cfg.H, cfg.S)) * 64) / 64).astype(np.float32)
+    gpu = gh.run_prefill(cfg, rows, slices, mass_in={2: mass})
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            want = prefill.topk(mass[b, h].astype(np.float64), np.arange(cfg.S), cfg.K)
+            assert np.array_equal(gpu["sel"][1][b, h], want), (b, h)
+
+
+@pytest.mark.parametrize("bits,d", [((8, 2, 4, 2), 64), ((8, 4, 2, 4, 2), 64)])
+def test_prefill_fp32_ragged(bits, d):
+    """Sizes that leave ragged tails everywhere, 2- and 4-bit residuals."""
+    import tests.gpu_harness as gh
+    R = len(bits)
+    act = tuple([1.0, 0.55, 0.4, 0.23, 0.11][:R])
+    cfg = workloads.custom(dtype="f32", B=2, H=2, d=d, S=333, R=R, act=act, col="0.17", bits=bits, lognormal=0.5,
+                           seed=3)
+    _say("prefill ragged", cfg)
+    rows, slices = workloads.gen_batch(cfg)
+    gpu = gh.run_prefill(cfg, rows, slices)
+    heads = list(range(cfg.H))
+    orc = _oracle_slices(cfg, rows, slices, gpu, heads)
+    _check_records(cfg, gpu, orc, heads)
+    _check_outputs(cfg, gpu, orc, heads, 1e-5, rel=False)
+
+
+def test_prefill_deterministic():
+    import tests.gpu_harness as gh
+    cfg = workloads.CONFIGS[0]
+    _say("determinism", cfg.name)
+    rows, slices = workloads.gen_batch(cfg)
+    a = gh.run_prefill(cfg, rows, slices)
+    b = gh.run_prefill(cfg, rows, slices)
+    for r in range(cfg.R):
+        for k in ("O", "U", "M", "lse"):
+            assert np.array_equal(a["state"][r][k], b["state"][r][k]), (r, k)
+    for r in range(1, cfg.R):
+        assert np.array_equal(a["sel"][r], b["sel"][r])
+        assert np.array_equal(a["mass"][r], b["mass"][r])
