@@ -42,6 +42,11 @@ class FlDState(ctypes.Structure):
 
 
 def _load():
+    # The library links libamdhip64.so.7 by SONAME.  torch ships its own HIP
+    # runtime under that SONAME; importing torch first makes the dynamic
+    # linker reuse it, so device memory and streams from torch and the
+    # library's launches share one runtime.
+    import torch  # noqa: F401
     path = lib_path()
     if not os.path.exists(path):
         raise ImportError(f"libflashloop.so not built ({path}); run __graft_entry__.build()")

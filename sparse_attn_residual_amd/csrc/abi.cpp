@@ -111,11 +111,26 @@ size_t fl_residual_record_bytes(int d, int bits) {
   return (size_t)fl::residual_record_bytes(d, bits);
 }
 
+namespace {
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+size_t tiles_bytes(const fl_cache* c, int K) {
+  if (c->d != 128 || K < 1) return 0;
+  fl::CacheGeo g{};
+  g.B = c->B;
+  g.H = c->H;
+  return fl::gather_bytes(g, K);
+}
+}  // namespace
+
 size_t fl_workspace_bytes(int which, const fl_cache* cache, int r, int K_prev, int K_r) {
-  (void)r;
-  (void)K_r;
-  if (!cache || K_prev < 0) return 0;
-  if (which == FL_WS_COLSEL) return (size_t)cache->B * cache->H * (size_t)K_prev * sizeof(float);
+  if (!cache || K_prev < 0 || K_r < 0 || r < 1) return 0;
+  if (which == FL_WS_COLSEL) {
+    // the mass pass of r >= 3 (or with explicit candidates) gathers the
+    // candidates' tiles; the cached-mass pass gathers the selected ones
+    const int kt = (r == 2 && K_prev == cache->S) ? K_r : K_prev;
+    return align256((size_t)cache->B * cache->H * (size_t)K_prev * sizeof(float)) + tiles_bytes(cache, kt);
+  }
+  if (which == FL_WS_ATTN) return r >= 2 ? tiles_bytes(cache, K_r) : 0;
   return 0;
 }
 
@@ -165,12 +180,19 @@ fl_status fl_colsel(const fl_cache* cache, int r, const void* q_prev, fl_dtype d
   const bool prune = K_r < K_prev;
   const bool need_mass = (prune && !mass_in) || mass_out;
   float* mass = mass_out;
-  if (need_mass && !mass) {
-    const size_t need = fl_workspace_bytes(FL_WS_COLSEL, cache, r, K_prev, K_r);
+  const size_t mass_ws = align256((size_t)cache->B * cache->H * (size_t)K_prev * sizeof(float));
+  // tiles gathered by the mass pass (all but r == 2 over every position) or the cached-mass pass
+  const int kt = (r == 2 && !cand) ? K_r : K_prev;
+  const size_t need = (need_mass && !mass_out ? mass_ws : 0) + ((prune || need_mass) ? tiles_bytes(cache, kt) : 0);
+  if (need > 0) {
     if (!ws || ws_bytes < need)
       return fail(FL_EINVAL, "%s: workspace of %zu bytes needed (got %zu)", fn, need, ws ? ws_bytes : (size_t)0);
     if (!aligned16(ws)) return fail(FL_EINVAL, "%s: ws is not 16-byte aligned", fn);
+  }
+  uint8_t* tiles_ws = (uint8_t*)ws;
+  if (need_mass && !mass_out) {
     mass = (float*)ws;
+    tiles_ws = (uint8_t*)ws + mass_ws;
   }
   if (prune && K_prev > kTopkMax)
     return fail(FL_EUNSUPPORTED, "%s: %d candidates (at most %d)", fn, K_prev, kTopkMax);
@@ -183,7 +205,7 @@ fl_status fl_colsel(const fl_cache* cache, int r, const void* q_prev, fl_dtype d
   a.O = state->O; a.U = state->U; a.M = state->M; a.lse = state->lse;
   hipError_t e;
   if (need_mass) {
-    e = fl::launch_mass(a, cand, K_prev, mass, st);
+    e = fl::launch_mass(a, cand, K_prev, mass, tiles_ws, st);
     if (e != hipSuccess) return hip_fail(e, fn);
   }
   const int P = cache->B * cache->H;
@@ -197,15 +219,13 @@ fl_status fl_colsel(const fl_cache* cache, int r, const void* q_prev, fl_dtype d
   if (e != hipSuccess) return hip_fail(e, fn);
   a.K = K_r;
   a.sel = sel_out;
-  e = fl::launch_um(a, st);
+  e = fl::launch_um(a, tiles_ws, st);
   if (e != hipSuccess) return hip_fail(e, fn);
   return FL_OK;
 }
 
 fl_status fl_loop_attn(const fl_cache* cache, int r, const void* q, fl_dtype dtype, int K_r, const int32_t* sel,
                        const fl_state* state, void* ws, size_t ws_bytes, fl_stream stream) {
-  (void)ws;
-  (void)ws_bytes;
   const char* fn = "fl_loop_attn";
   g_err.clear();
   fl::CacheGeo geo;
@@ -218,6 +238,10 @@ fl_status fl_loop_attn(const fl_cache* cache, int r, const void* q, fl_dtype dty
   if (r >= 2) {
     FL_NEED_PTR(sel, "sel");
     if (K_r < 1 || K_r > cache->S) return fail(FL_EINVAL, "%s: K_r = %d outside [1, S]", fn, K_r);
+    const size_t need = fl_workspace_bytes(FL_WS_ATTN, cache, r, K_r, K_r);
+    if (need > 0 && (!ws || ws_bytes < need))
+      return fail(FL_EINVAL, "%s: workspace of %zu bytes needed (got %zu)", fn, need, ws ? ws_bytes : (size_t)0);
+    if (need > 0 && !aligned16(ws)) return fail(FL_EINVAL, "%s: ws is not 16-byte aligned", fn);
   }
   fl::AttnArgs a{};
   a.c = geo;
@@ -227,7 +251,7 @@ fl_status fl_loop_attn(const fl_cache* cache, int r, const void* q, fl_dtype dty
   a.K = r >= 2 ? K_r : 0;
   a.sel = r >= 2 ? sel : nullptr;
   a.O = state->O; a.U = state->U; a.M = state->M; a.lse = state->lse;
-  hipError_t e = fl::launch_attn(a, (hipStream_t)stream);
+  hipError_t e = fl::launch_attn(a, (uint8_t*)ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, fn);
   return FL_OK;
 }

@@ -38,14 +38,18 @@ struct AttnArgs {
   float* M;
   float* lse;
 };
-// Loop r attention (dense when r == 1, sparse otherwise).
-hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+// Loop r attention (dense when r == 1, sparse otherwise).  ws: workspace of
+// gather_bytes(c, K) bytes for the gathered column tiles (sparse loops).
+hipError_t launch_attn(const AttnArgs& a, uint8_t* ws, hipStream_t st);
 // Cached mass and reused part for loop r: reads loop r-1 state, q_prev and
-// chains to r-1; rows A_r; columns sel (S_r).
-hipError_t launch_um(const AttnArgs& a, hipStream_t st);
+// chains to r-1; rows A_r; columns sel (S_r).  ws as for launch_attn.
+hipError_t launch_um(const AttnArgs& a, uint8_t* ws, hipStream_t st);
+// Bytes of the gathered tiles of K selected columns (head dim 128).
+size_t gather_bytes(const CacheGeo& c, int K);
 // Column mass of the candidates cand (NULL: all S) over rows A_r with loop
-// r-1's probabilities.
-hipError_t launch_mass(const AttnArgs& a, const int32_t* cand, int K_prev, float* mass, hipStream_t st);
+// r-1's probabilities.  ws: gather_bytes(c, K_prev) bytes when cand != NULL.
+hipError_t launch_mass(const AttnArgs& a, const int32_t* cand, int K_prev, float* mass, uint8_t* ws,
+                       hipStream_t st);
 
 // ---- decode
 struct DecodeArgs {

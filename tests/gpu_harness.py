@@ -55,10 +55,14 @@ def run_prefill(cfg, rows, slices, *, mass_in=None, K_budget=None, mfma=None):
             mi = None
             if mass_in is not None and r in mass_in:
                 mi = torch.from_numpy(np.ascontiguousarray(mass_in[r], np.float32)).to(DEV)
-            fl.fl_colsel(cache.fl, r, qs[r - 2], dt, st.fl, K_prev, sel_prev, K, mi, mass, sel)
+            nws = fl.fl_workspace_bytes(fl.FL_WS_COLSEL, cache.fl, r, K_prev, K)
+            ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=DEV)
+            fl.fl_colsel(cache.fl, r, qs[r - 2], dt, st.fl, K_prev, sel_prev, K, mi, mass, sel, ws, nws)
             out["sel"].append(sel.cpu().numpy())
             out["mass"].append(mass.cpu().numpy())
-        fl.fl_loop_attn(cache.fl, r, qs[r - 1], dt, K, sel, st.fl)
+        nws = fl.fl_workspace_bytes(fl.FL_WS_ATTN, cache.fl, r, K, K) if r >= 2 else 0
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=DEV)
+        fl.fl_loop_attn(cache.fl, r, qs[r - 1], dt, K, sel, st.fl, ws, nws)
         torch.cuda.synchronize()
         out["state"].append({k2: v2.cpu().numpy() for k2, v2 in st.snapshot().items()})
         if r >= 2:

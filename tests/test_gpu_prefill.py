@@ -140,3 +140,38 @@ def test_prefill_deterministic():
     for r in range(1, cfg.R):
         assert np.array_equal(a["sel"][r], b["sel"][r])
         assert np.array_equal(a["mass"][r], b["mass"][r])
+
+
+def _bf16_case(cfg, heads, sel_eps=2e-3):
+    import tests.gpu_harness as gh
+    rows, slices = workloads.gen_batch(cfg, heads=None)
+    gpu = gh.run_prefill(cfg, rows, slices)
+    orc = _oracle_slices(cfg, rows, slices, gpu, heads)
+    _check_records(cfg, gpu, orc, heads)
+    for b in range(cfg.B):
+        for h in heads:
+            cand = np.arange(cfg.S)
+            for r in range(1, cfg.R):
+                m = orc[(b, h)]["mass"][r]
+                own = prefill.topk(m, cand, min(cfg.K, len(cand)))
+                ok, ndiff = gh.near_tie_ok(gpu["sel"][r][b, h], own, m, cand, sel_eps)
+                assert ok, (b, h, r + 1, ndiff)
+                cand = gpu["sel"][r][b, h]
+    _check_outputs(cfg, gpu, orc, heads, 2e-3, rel=True)
+    return gpu, orc
+
+
+@pytest.mark.parametrize("S,bits,col", [(777, (8, 4, 4, 2), "0.10"), (1300, (8, 2, 4, 4), "0.33")])
+def test_prefill_bf16_mfma_small(S, bits, col):
+    cfg = workloads.custom(name="bf16-small", dtype="bf16", B=2, H=2, d=128, S=S, R=4, act=(1, 0.3, 0.15, 0.08),
+                           col=col, bits=bits, lognormal=0.5, seed=5)
+    _say("prefill bf16 mfma", cfg)
+    _bf16_case(cfg, heads=[0, 1])
+
+
+@pytest.mark.parametrize("cfgid,heads", [(1, [0, 11]), (4, [3])])
+def test_prefill_bf16_full_size(cfgid, heads):
+    """Full-size workloads (all heads on the GPU), oracle on sampled heads."""
+    cfg = workloads.CONFIGS[cfgid]
+    _say("prefill full size", cfg.name, heads)
+    _bf16_case(cfg, heads=heads)
