@@ -1,0 +1,306 @@
+"""Benchmark of the FlashLoop loop-attention hot path on one MI355X.
+
+One step = one pass of the whole prefill hot path over one layer of the
+32K-token, R = 4 workload (Ouro-2.6B shaped: 16 heads x 128 dims, bf16,
+nested active rows 100/30/15/8 %, top 10 % of columns, int8 base + 4/4/2-bit
+residuals): for every loop r, fl_kv_resq(r), then fl_colsel(r) (r >= 2), then
+fl_loop_attn(r).  Inputs (queries, keys and values of every loop) are
+resident in HBM before the timed region.  `value` is prefill tokens/s.
+
+The same run also times one decode step of the 48-layer packed cache
+(B = 16 sequences x 16 heads x 32K cached tokens, R = 4 launches of
+fl_loop_decode) and reports its packed-KV GB/s against the HBM roofline, and
+times the CPU oracle on a bounded sample of the prefill workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PREFILL_CFG = 2
+DECODE_CFG = 3
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def _upload(x, torch):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda").to(torch.bfloat16).contiguous()
+
+
+class Timer:
+    """HIP events on the stream the library launches on (torch's current)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def wrap(self, key, fn):
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        self.pairs.setdefault(key, []).append((e0, e1))
+
+    def reset(self):
+        self.pairs = {}
+
+    def mean_ms(self):
+        return {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in self.pairs.items()}
+
+
+def prefill_bench(args, torch, fl, workloads, acc):
+    cfg = workloads.CONFIGS[PREFILL_CFG]
+    t0 = time.time()
+    rows, slices = workloads.gen_batch(cfg)
+    log(f"generated {cfg.name} inputs in {time.time() - t0:.1f}s")
+    R, B, H, S, d = cfg.R, cfg.B, cfg.H, cfg.S, cfg.d
+    q = [_upload(workloads.stack_loop(cfg, slices, r, "q"), torch) for r in range(1, R + 1)]
+    k = [_upload(workloads.stack_loop(cfg, slices, r, "k"), torch) for r in range(1, R + 1)]
+    v = [_upload(workloads.stack_loop(cfg, slices, r, "v"), torch) for r in range(1, R + 1)]
+    del slices
+    rows_l = [np.stack([rows[b][r] for b in range(B)]) for r in range(R)]
+    cache = fl.CacheBuffers(1, B, H, S, d, R, cfg.n, cfg.bits, rows_l)
+    st = fl.PrefillState(B, H, S, d)
+    Ks = [S] + [min(cfg.K, S) for _ in range(1, R)]
+    for r in range(2, R + 1):
+        Ks[r - 1] = min(cfg.K, Ks[r - 2])
+    sel = [None] + [torch.empty(B, H, Ks[r], dtype=torch.int32, device="cuda") for r in range(1, R)]
+    ws_bytes = 16
+    for r in range(2, R + 1):
+        ws_bytes = max(ws_bytes, fl.fl_workspace_bytes(fl.FL_WS_COLSEL, cache.fl, r, Ks[r - 2], Ks[r - 1]),
+                       fl.fl_workspace_bytes(fl.FL_WS_ATTN, cache.fl, r, Ks[r - 1], Ks[r - 1]))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    dt = fl.FL_BF16
+    tm = Timer(torch)
+
+    def step(timed):
+        w = tm.wrap if timed else (lambda key, fn: fn())
+        for r in range(1, R + 1):
+            w(f"resq{r}", lambda r=r: fl.fl_kv_resq(cache.fl, r, k[r - 1], v[r - 1], dt))
+            if r >= 2:
+                cand = sel[r - 2] if r >= 3 else None
+                w(f"colsel{r}", lambda r=r, cand=cand: fl.fl_colsel(
+                    cache.fl, r, q[r - 2], dt, st.fl, Ks[r - 2], cand, Ks[r - 1], None, None, sel[r - 1], ws,
+                    ws_bytes))
+            w(f"attn{r}", lambda r=r: fl.fl_loop_attn(cache.fl, r, q[r - 1], dt, Ks[r - 1], sel[r - 1], st.fl, ws,
+                                                     ws_bytes))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    # timed region: barrier + synchronize on both sides (one process)
+    torch.cuda.synchronize()
+    tm.reset()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step(True)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    per = tm.mean_ms()
+    log(f"prefill: {ms_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}); per call (ms): "
+        + ", ".join(f"{kk}={vv:.3f}" for kk, vv in per.items()))
+
+    # algorithmic work from the index lists of the run
+    sels = [None] + [s.cpu().numpy() for s in sel[1:]]
+    masses_ran = [False] + [Ks[r] < Ks[r - 1] for r in range(1, R)]
+    work = acc.prefill_work(cfg, rows, sels, masses_ran)
+    dense_t = per["attn1"] * 1e-3
+    dense_tf = work["dense_flops"] / dense_t / 1e12
+    sparse_t = sum(per[f"attn{r}"] for r in range(2, R + 1)) * 1e-3
+    sparse_tf = work["sparse_flops"] / sparse_t / 1e12
+    total_tf = work["flops"] / (ms_step * 1e-3) / 1e12
+    return dict(cfg=cfg, ms_step=ms_step, per=per, work=work, dense_tf=dense_tf, sparse_tf=sparse_tf,
+                total_tf=total_tf, Ks=Ks)
+
+
+def decode_bench(args, torch, fl, workloads, acc):
+    cfg = workloads.CONFIGS[DECODE_CFG]
+    L, B, H, S, d, R = cfg.L, cfg.B, cfg.H, cfg.S, cfg.d, cfg.R
+    t0 = time.time()
+    rows = {b: workloads.active_rows(cfg, b) for b in range(B)}
+    rows_l = [np.stack([rows[b][r] for b in range(B)]) for r in range(R)]
+    cache = fl.CacheBuffers(L, B, H, S, d, R, cfg.n, cfg.bits, rows_l)
+    log(f"decode cache: {cache.nbytes() / 1e9:.1f} GB on device")
+    for b in range(B):
+        _, sl = workloads.gen_batch(cfg, batches=[b], with_q=False)
+        view = cache.seq_view(0, b)
+        for r in range(1, R + 1):
+            kk = _upload(workloads.stack_loop(cfg, sl, r, "k", batches=[b]), torch)
+            vv = _upload(workloads.stack_loop(cfg, sl, r, "v", batches=[b]), torch)
+            fl.fl_kv_resq(view, r, kk, vv, fl.FL_BF16)
+            torch.cuda.synchronize()
+            del kk, vv
+        del sl
+        log(f"decode cache: sequence {b + 1}/{B} quantized ({time.time() - t0:.0f}s)")
+    cache.replicate_layer0()
+    qs = [_upload(x, torch) for x in workloads.decode_queries(cfg)]
+    st = fl.DecodeState(L, B, H, S, d)
+    Ks = [S] + [min(cfg.K, S)] * (R - 1)
+    tm = Timer(torch)
+
+    def step(timed):
+        w = tm.wrap if timed else (lambda key, fn: fn())
+        for r in range(1, R + 1):
+            w(f"decode{r}", lambda r=r: fl.fl_loop_decode(cache.fl, r, qs[r - 1], fl.FL_BF16,
+                                                          Ks[r - 2] if r >= 2 else S, Ks[r - 1], st.fl))
+
+    for _ in range(max(1, args.warmup // 2)):
+        step(False)
+    torch.cuda.synchronize()
+    steps = max(2, args.steps // 2)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step(True)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    per = tm.mean_ms()
+    log(f"decode: {ms_step:.3f} ms/step; per loop (ms): " + ", ".join(f"{kk}={vv:.3f}" for kk, vv in per.items()))
+
+    # algorithmic packed bytes of the step, from the selections of the run
+    base_b = acc.base_record_bytes(d)
+    res_b = [0] + [acc.residual_record_bytes(d, cfg.bits[r]) for r in range(1, R)]
+    loop_bytes = [float(L * B * H * S * base_b)]
+    sel = st.sel[..., :Ks[-1]].long()  # S_2 = S_3 = S_4 with a constant budget
+    cum = torch.full((B, S), float(base_b), dtype=torch.float64, device="cuda")
+    for r in range(2, R + 1):
+        cum += (cache.slot[r - 1] >= 0).double() * res_b[r - 1]
+        per_j = torch.gather(cum.unsqueeze(0).unsqueeze(2).expand(L, B, H, S), 3, sel)
+        loop_bytes.append(float(per_j.sum().item()))
+    total = sum(loop_bytes)
+    logits_overhead = float(L * B * H * S * 4 * 2)
+    return dict(cfg=cfg, ms_step=ms_step, per=per, loop_bytes=loop_bytes, bytes=total,
+                gbs=total / (ms_step * 1e-3) / 1e9, dense_gbs=loop_bytes[0] / (per["decode1"] * 1e-3) / 1e9,
+                logits_overhead=logits_overhead, cache_bytes=cache.nbytes())
+
+
+def cpu_baseline(workloads):
+    """The oracle as it stands, on one head of the prefill workload."""
+    from oracle import prefill
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    cfg = workloads.CONFIGS[PREFILL_CFG]
+    rows, sl = workloads.gen_batch(cfg, heads=[0])
+    s = sl[(0, 0)]
+    t0 = time.perf_counter()
+    prefill.prefill_slice(s.rows, s.q, s.k, s.v, K_budget=cfg.K, bits=cfg.bits, dtype=cfg.dtype)
+    t = time.perf_counter() - t0
+    value = cfg.S / (t * cfg.H)   # one head is 1/H of a step
+    return dict(value=value, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"{cfg.name}: head 0 of {cfg.H}, all {cfg.R} loops in float64 ({t:.1f}s), "
+                       f"scaled to {cfg.H} heads")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: the hot path shards by heads and sequences with no exchange, and this "
+              f"build measures one GPU's share (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sparse_attn_residual_amd as fl
+    from sparse_attn_residual_amd import accounting as acc
+    import workloads
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    pf = prefill_bench(args, torch, fl, workloads, acc)
+    dec = None if args.no_decode else decode_bench(args, torch, fl, workloads, acc)
+    cpu = None if args.no_cpu else cpu_baseline(workloads)
+
+    cfg = pf["cfg"]
+    tokens_s = cfg.B * cfg.S / (pf["ms_step"] * 1e-3)
+    dense_flops = pf["work"]["dense_flops"]
+    out = {
+        "metric": "loop-attn prefill tokens/s @32K R=4; decode packed-KV GB/s vs HBM peak",
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pf["ms_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: one layer, B={cfg.B}, H={cfg.H}, d={cfg.d}, S={cfg.S}, R={cfg.R}, "
+                        f"active rows {cfg.n}, K={pf['Ks'][1]}, bits {list(cfg.bits)}",
+            "per_call_ms": {k: round(v, 4) for k, v in pf["per"].items()},
+            "prefill_flops": pf["work"]["flops"],
+            "mfma_frac_whole_step": pf["total_tf"] / acc.MI355X_BF16_TFLOPS,
+            "sparse_attn_tflops": pf["sparse_tf"],
+            "sparse_attn_mfma_frac": pf["sparse_tf"] / acc.MI355X_BF16_TFLOPS,
+        },
+        "roofline": {
+            "kernel": "k_attn_mfma (fl_loop_attn r=1, dense causal over the int8 base)",
+            "bound": "mfma",
+            "achieved": pf["dense_tf"],
+            "peak": acc.MI355X_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": pf["dense_tf"] / acc.MI355X_BF16_TFLOPS,
+            "traffic": None,
+            "flops_per_launch": dense_flops,
+            "avg_launch_ms": pf["per"]["attn1"],
+        },
+    }
+    if dec is not None:
+        dcfg = dec["cfg"]
+        out["decode"] = {
+            "workload": f"{dcfg.name}: L={dcfg.L} stacked layers, B={dcfg.B}, H={dcfg.H}, T={dcfg.S}, R={dcfg.R}, "
+                        f"K={min(dcfg.K, dcfg.S)}, bits {list(dcfg.bits)}",
+            "ms_per_step": dec["ms_step"],
+            "packed_kv_bytes_per_step": dec["bytes"],
+            "value": dec["gbs"],
+            "unit": "GB/s",
+            "per_loop_ms": {k: round(v, 4) for k, v in dec["per"].items()},
+            "loop_bytes": dec["loop_bytes"],
+            "logits_overhead_bytes": dec["logits_overhead"],
+            "roofline": {
+                "kernel": "k_decode_dense (fl_loop_decode r=1)",
+                "bound": "hbm",
+                "achieved": dec["dense_gbs"],
+                "peak": acc.MI355X_HBM_GBS,
+                "unit": "GB/s",
+                "frac": dec["dense_gbs"] / acc.MI355X_HBM_GBS,
+                "traffic": None,
+                "step_frac": dec["gbs"] / acc.MI355X_HBM_GBS,
+            },
+        }
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

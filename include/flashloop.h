@@ -30,8 +30,10 @@
  * k~, v~ are the reconstructions (rounded to bf16 for bf16 prefill inputs).
  *
  * Conventions for every call:
- *   - All array arguments are device pointers to caller-owned memory, 16-byte
- *     aligned.  The library allocates nothing and keeps no pointer after a call.
+ *   - All array arguments are device pointers to caller-owned memory.  Index
+ *     arrays (rows, slot, cand, sel), masses, M and lse must be 4-byte
+ *     aligned; every other array 16-byte aligned.  The library allocates
+ *     nothing and keeps no pointer after a call.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream) and do not synchronize.  They are reentrant and thread safe.
  *   - Every argument is validated before anything is launched; on error the

@@ -48,6 +48,18 @@ class CacheBuffers:
         """The same cache restricted to one layer (L = 1)."""
         return self._struct(layer, 1)
 
+    def seq_view(self, layer: int, b: int) -> FlCache:
+        """One layer and one sequence (L = B = 1): the records of (layer, b) are
+        contiguous in the [L][B][H][...] layout."""
+        c = self._struct(layer, 1)
+        c.B = 1
+        c.base += b * self.H * self.S * self.base_rb
+        for r in range(2, self.R + 1):
+            c.rows[r] += b * self.n[r - 1] * 4
+            c.slot[r] += b * self.S * 4
+            c.res[r] += b * self.H * self.n[r - 1] * self.res_rb[r - 1]
+        return c
+
     def replicate_layer0(self):
         """Copy layer 0's records into every other layer."""
         per_base = self.B * self.H * self.S * self.base_rb

@@ -28,11 +28,18 @@ fl_status hip_fail(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 #define FL_NEED_PTR(p, name)                                                                 \
   do {                                                                                       \
     if (!(p)) return fail(FL_EINVAL, "%s: %s is NULL", fn, name);                            \
     if (!aligned16(p)) return fail(FL_EINVAL, "%s: %s is not 16-byte aligned", fn, name);    \
+  } while (0)
+// index and mass arrays (int32 / float32 read element-wise): 4-byte alignment
+#define FL_NEED_PTR4(p, name)                                                                \
+  do {                                                                                       \
+    if (!(p)) return fail(FL_EINVAL, "%s: %s is NULL", fn, name);                            \
+    if (!aligned4(p)) return fail(FL_EINVAL, "%s: %s is not 4-byte aligned", fn, name);      \
   } while (0)
 
 // Validates the cache geometry and the streams needed by loop r; fills geo.
@@ -57,9 +64,9 @@ fl_status check_cache(const char* fn, const fl_cache* c, int r, bool need_res_r,
   for (int rr = 2; rr <= r; ++rr) {
     char name[32];
     std::snprintf(name, sizeof name, "cache->rows[%d]", rr);
-    FL_NEED_PTR(c->rows[rr], name);
+    FL_NEED_PTR4(c->rows[rr], name);
     std::snprintf(name, sizeof name, "cache->slot[%d]", rr);
-    FL_NEED_PTR(c->slot[rr], name);
+    FL_NEED_PTR4(c->slot[rr], name);
     if (rr <= last) {
       std::snprintf(name, sizeof name, "cache->res[%d]", rr);
       FL_NEED_PTR(c->res[rr], name);
@@ -89,8 +96,8 @@ fl_status check_state(const char* fn, const fl_state* s) {
   if (!s) return fail(FL_EINVAL, "%s: state is NULL", fn);
   FL_NEED_PTR(s->O, "state->O");
   FL_NEED_PTR(s->U, "state->U");
-  FL_NEED_PTR(s->M, "state->M");
-  FL_NEED_PTR(s->lse, "state->lse");
+  FL_NEED_PTR4(s->M, "state->M");
+  FL_NEED_PTR4(s->lse, "state->lse");
   return FL_OK;
 }
 
@@ -170,13 +177,13 @@ fl_status fl_colsel(const fl_cache* cache, int r, const void* q_prev, fl_dtype d
   if ((s = check_dtype(fn, dtype)) != FL_OK) return s;
   if ((s = check_state(fn, state)) != FL_OK) return s;
   FL_NEED_PTR(q_prev, "q_prev");
-  FL_NEED_PTR(sel_out, "sel_out");
+  FL_NEED_PTR4(sel_out, "sel_out");
   if (K_prev < 1 || K_prev > cache->S) return fail(FL_EINVAL, "%s: K_prev = %d outside [1, S]", fn, K_prev);
   if (!cand && K_prev != cache->S) return fail(FL_EINVAL, "%s: cand is NULL but K_prev = %d != S", fn, K_prev);
-  if (cand && !aligned16(cand)) return fail(FL_EINVAL, "%s: cand is not 16-byte aligned", fn);
+  if (cand && !aligned4(cand)) return fail(FL_EINVAL, "%s: cand is not 4-byte aligned", fn);
   if (K_r < 1 || K_r > K_prev) return fail(FL_EINVAL, "%s: K_r = %d outside [1, K_prev = %d]", fn, K_r, K_prev);
-  if (mass_in && !aligned16(mass_in)) return fail(FL_EINVAL, "%s: mass_in is not 16-byte aligned", fn);
-  if (mass_out && !aligned16(mass_out)) return fail(FL_EINVAL, "%s: mass_out is not 16-byte aligned", fn);
+  if (mass_in && !aligned4(mass_in)) return fail(FL_EINVAL, "%s: mass_in is not 4-byte aligned", fn);
+  if (mass_out && !aligned4(mass_out)) return fail(FL_EINVAL, "%s: mass_out is not 4-byte aligned", fn);
   const bool prune = K_r < K_prev;
   const bool need_mass = (prune && !mass_in) || mass_out;
   float* mass = mass_out;
@@ -236,7 +243,7 @@ fl_status fl_loop_attn(const fl_cache* cache, int r, const void* q, fl_dtype dty
   if ((s = check_state(fn, state)) != FL_OK) return s;
   FL_NEED_PTR(q, "q");
   if (r >= 2) {
-    FL_NEED_PTR(sel, "sel");
+    FL_NEED_PTR4(sel, "sel");
     if (K_r < 1 || K_r > cache->S) return fail(FL_EINVAL, "%s: K_r = %d outside [1, S]", fn, K_r);
     const size_t need = fl_workspace_bytes(FL_WS_ATTN, cache, r, K_r, K_r);
     if (need > 0 && (!ws || ws_bytes < need))
@@ -270,10 +277,10 @@ fl_status fl_loop_decode(const fl_cache* cache, int r, const void* q, fl_dtype d
   if (!state) return fail(FL_EINVAL, "%s: state is NULL", fn);
   FL_NEED_PTR(state->O, "state->O");
   FL_NEED_PTR(state->U, "state->U");
-  FL_NEED_PTR(state->M, "state->M");
-  FL_NEED_PTR(state->lse, "state->lse");
-  FL_NEED_PTR(state->logits, "state->logits");
-  FL_NEED_PTR(state->sel, "state->sel");
+  FL_NEED_PTR4(state->M, "state->M");
+  FL_NEED_PTR4(state->lse, "state->lse");
+  FL_NEED_PTR4(state->logits, "state->logits");
+  FL_NEED_PTR4(state->sel, "state->sel");
   FL_NEED_PTR(q, "q");
   if ((long long)cache->L * cache->B * cache->H > 0x7FFFFFFFLL)
     return fail(FL_EUNSUPPORTED, "%s: too many (layer, sequence, head) triples", fn);

@@ -156,27 +156,28 @@ def _lam(cfg: Config, tid, b, h):
     return _rng(cfg, tid, b, h).lognormal(0.0, cfg.lognormal, cfg.S).astype(np.float32)
 
 
-def gen_slice(cfg: Config, b: int, h: int, rows=None) -> Slice:
-    """All loop inputs of one (b, h) slice.  Loop-1 tensors cover every row."""
+def gen_slice(cfg: Config, b: int, h: int, rows=None, with_q: bool = True) -> Slice:
+    """All loop inputs of one (b, h) slice.  Loop-1 tensors cover every row.
+    with_q=False skips the queries (a decode cache needs keys and values only)."""
     if rows is None:
         rows = active_rows(cfg, b)
     lam_q = _lam(cfg, _T_LAM_Q, b, h)
     lam_k = _lam(cfg, _T_LAM_K, b, h)
     ones = np.ones(cfg.S, dtype=np.float32)
-    q = _chain(cfg, rows, _T_Q, _T_DQ, lam_q, b, h)
+    q = _chain(cfg, rows, _T_Q, _T_DQ, lam_q, b, h) if with_q else None
     k = _chain(cfg, rows, _T_K, _T_DK, lam_k, b, h)
     v = _chain(cfg, rows, _T_V, _T_DV, ones, b, h)
     return Slice(rows=rows, q=q, k=k, v=v)
 
 
-def gen_batch(cfg: Config, heads=None, batches=None, threads: int | None = None):
+def gen_batch(cfg: Config, heads=None, batches=None, threads: int | None = None, with_q: bool = True):
     """Slices for every (b, h) requested: returns (rows[b], {(b, h): Slice})."""
     heads = range(cfg.H) if heads is None else heads
     batches = range(cfg.B) if batches is None else batches
     rows = {b: active_rows(cfg, b) for b in batches}
     keys = [(b, h) for b in batches for h in heads]
     with ThreadPoolExecutor(max_workers=threads or min(16, len(keys))) as ex:
-        res = list(ex.map(lambda bh: gen_slice(cfg, bh[0], bh[1], rows[bh[0]]), keys))
+        res = list(ex.map(lambda bh: gen_slice(cfg, bh[0], bh[1], rows[bh[0]], with_q), keys))
     return rows, dict(zip(keys, res))
 
 
