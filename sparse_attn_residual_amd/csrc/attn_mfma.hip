@@ -36,9 +36,9 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kD = 128;
 constexpr int kBN = 64;        // key columns per tile
 constexpr int kKP = kD + 8;    // LDS pitch of the K tile (bf16 elements): 272 B
-constexpr int kVP = kBN + 8;   // LDS pitch of the V^T tile (fp16 elements): 144 B
-constexpr int kThreads = 256;
+constexpr int kVP = kBN + 4;   // LDS pitch of the V^T tile (fp16 elements): 136 B
 constexpr int kNoPos = 0x7fffffff;  // padding column: masked for every row
+constexpr float kRescale = 8.0f;    // lazy rescale threshold (log2 units): P <= 2^8
 
 struct __align__(16) Tile {
   __bf16 k[kBN * kKP];
@@ -52,41 +52,61 @@ constexpr int kTileKBytes = kBN * kD * 2;
 constexpr int kTileVBytes = kD * kBN * 2;
 constexpr int kTileBytes = kTileKBytes + kTileVBytes + kBN * 4;
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  const bf16x2_t v = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
 }
 // v~ = bf16(x) converted to fp16 (exact for every bf16 value above 2^-17 in
 // magnitude; smaller values round to the fp16 subnormal grid).
 __device__ inline _Float16 bf16_as_f16(float x) { return (_Float16)round_bf16(x); }
+__device__ inline void bf16x2_as_f16(float a, float b, _Float16& ha, _Float16& hb) {
+  const uint32_t w = pack_bf16x2(a, b);
+  ha = (_Float16)__uint_as_float(w << 16);
+  hb = (_Float16)__uint_as_float(w & 0xFFFF0000u);
+}
 
 // ------------------------------------------------------------- tile loaders
-// Loop-1 loader: columns j0..j0+63 of the int8 base of (b, h).
+// Loop-1 loader: columns j0..j0+63 of the int8 base of (b, h), NT threads.
+template <int NT>
 struct BaseRegs {
-  uint4 kc0, kc1;      // 32 K codes
-  uint16_t ks;         // K group scale
-  uint32_t vc[8];      // 4 V codes of 8 columns
-  uint16_t vs[8];      // their V group scales
+  static constexpr int KCH = kBN * kD / NT;        // K codes per thread (16 or 32)
+  static constexpr int VCOL = kBN * 32 / NT;       // V columns per thread (4 or 8)
+  uint32_t kc[KCH / 4];
+  uint16_t ks;
+  uint32_t vc[VCOL];
+  uint16_t vs[VCOL];
 };
 
-__device__ inline void fetch_base(const CacheGeo& c, int b, int h, int j0, BaseRegs& R) {
+template <int NT>
+__device__ inline void fetch_base(const uint8_t* recs, int rb, int S, int j0, BaseRegs<NT>& R) {
+  using BR = BaseRegs<NT>;
   const int t = threadIdx.x;
-  const int col = t >> 2, qd = t & 3;
+  constexpr int PER = kD / BR::KCH;  // threads per column for K
+  const int col = t / PER, part = t % PER;
   const int j = j0 + col;
-  if (j < c.S) {
-    const uint8_t* rec = base_rec(c, 0, b, h, j);
-    R.kc0 = *(const uint4*)(rec + qd * 32);
-    R.kc1 = *(const uint4*)(rec + qd * 32 + 16);
-    R.ks = ((const uint16_t*)(rec + 2 * kD))[qd];
+  if (j < S) {
+    const uint8_t* rec = recs + (uint32_t)j * rb;
+#pragma unroll
+    for (int w = 0; w < BR::KCH / 16; ++w) {
+      const uint4 v = *(const uint4*)(rec + part * BR::KCH + w * 16);
+      R.kc[4 * w] = v.x; R.kc[4 * w + 1] = v.y; R.kc[4 * w + 2] = v.z; R.kc[4 * w + 3] = v.w;
+    }
+    R.ks = ((const uint16_t*)(rec + 2 * kD))[part * BR::KCH / 32];
   } else {
-    R.kc0 = R.kc1 = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int w = 0; w < BR::KCH / 4; ++w) R.kc[w] = 0;
     R.ks = 0;
   }
   const int d4 = t & 31, jg = t >> 5;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int jj = j0 + jg * 8 + e;
-    if (jj < c.S) {
-      const uint8_t* rec = base_rec(c, 0, b, h, jj);
+  for (int e = 0; e < BR::VCOL; ++e) {
+    const int jj = j0 + jg * BR::VCOL + e;
+    if (jj < S) {
+      const uint8_t* rec = recs + (uint32_t)jj * rb;
       R.vc[e] = *(const uint32_t*)(rec + kD + d4 * 4);
       R.vs[e] = ((const uint16_t*)(rec + 2 * kD))[4 + (d4 >> 3)];
     } else {
@@ -96,72 +116,89 @@ __device__ inline void fetch_base(const CacheGeo& c, int b, int h, int j0, BaseR
   }
 }
 
-__device__ inline void store_base(const CacheGeo& c, int j0, const BaseRegs& R, Tile& T) {
+template <int NT>
+__device__ inline void store_base(int S, int j0, const BaseRegs<NT>& R, Tile& T) {
+  using BR = BaseRegs<NT>;
   const int t = threadIdx.x;
-  const int col = t >> 2, qd = t & 3;
+  constexpr int PER = kD / BR::KCH;
+  const int col = t / PER, part = t % PER;
   {
     const float s = h2f(R.ks);
-    const uint32_t w[8] = {R.kc0.x, R.kc0.y, R.kc0.z, R.kc0.w, R.kc1.x, R.kc1.y, R.kc1.z, R.kc1.w};
-    uint32_t o[16];
+    uint32_t o[BR::KCH / 2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float a0 = (float)(int8_t)(w[i]) * s;
-      const float a1 = (float)(int8_t)(w[i] >> 8) * s;
-      const float a2 = (float)(int8_t)(w[i] >> 16) * s;
-      const float a3 = (float)(int8_t)(w[i] >> 24) * s;
-      o[2 * i] = pack_bf16x2(a0, a1);
-      o[2 * i + 1] = pack_bf16x2(a2, a3);
+    for (int i = 0; i < BR::KCH / 4; ++i) {
+      const uint32_t w = R.kc[i];
+      o[2 * i] = pack_bf16x2((float)(int8_t)(w) * s, (float)(int8_t)(w >> 8) * s);
+      o[2 * i + 1] = pack_bf16x2((float)(int8_t)(w >> 16) * s, (float)(int8_t)(w >> 24) * s);
     }
-    uint4* dst = (uint4*)&T.k[col * kKP + qd * 32];
-    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-    dst[2] = make_uint4(o[8], o[9], o[10], o[11]);
-    dst[3] = make_uint4(o[12], o[13], o[14], o[15]);
+    uint4* dst = (uint4*)&T.k[col * kKP + part * BR::KCH];
+#pragma unroll
+    for (int i = 0; i < BR::KCH / 8; ++i) dst[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
   }
   {
     const int d4 = t & 31, jg = t >> 5;
-    f16x8_t out[4];
+    _Float16 out[4][BR::VCOL];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < BR::VCOL; ++e) {
       const float s = h2f(R.vs[e]);
-#pragma unroll
-      for (int dd = 0; dd < 4; ++dd) out[dd][e] = bf16_as_f16((float)(int8_t)(R.vc[e] >> (8 * dd)) * s);
+      const uint32_t w = R.vc[e];
+      bf16x2_as_f16((float)(int8_t)(w) * s, (float)(int8_t)(w >> 8) * s, out[0][e], out[1][e]);
+      bf16x2_as_f16((float)(int8_t)(w >> 16) * s, (float)(int8_t)(w >> 24) * s, out[2][e], out[3][e]);
     }
 #pragma unroll
-    for (int dd = 0; dd < 4; ++dd) *(f16x8_t*)&T.vt[(d4 * 4 + dd) * kVP + jg * 8] = out[dd];
+    for (int dd = 0; dd < 4; ++dd) {
+      _Float16* dst = &T.vt[(d4 * 4 + dd) * kVP + jg * BR::VCOL];
+      if constexpr (BR::VCOL == 4) {
+        *(f16x4_t*)dst = f16x4_t{out[dd][0], out[dd][1], out[dd][2], out[dd][3]};
+      } else {
+        *(f16x4_t*)dst = f16x4_t{out[dd][0], out[dd][1], out[dd][2], out[dd][3]};
+        *(f16x4_t*)(dst + 4) = f16x4_t{out[dd][4], out[dd][5], out[dd][6], out[dd][7]};
+      }
+    }
   }
-  if (t < kBN) T.pos[t] = (j0 + t < c.S) ? j0 + t : kNoPos;
+  if (t < kBN) T.pos[t] = (j0 + t < S) ? j0 + t : kNoPos;
 }
 
-// Compact-tile loader (sparse loops).
+// Compact-tile loader (sparse loops), NT threads.
+template <int NT>
 struct CompactRegs {
-  uint4 k[4];
-  uint4 v[4];
+  static constexpr int N16 = kTileKBytes / 16 / NT;  // uint4 per thread per half (4 or 2)
+  uint4 k[N16];
+  uint4 v[N16];
   int pos;
 };
 
-__device__ inline void fetch_compact(const uint8_t* tile, CompactRegs& R) {
+template <int NT>
+__device__ inline void fetch_compact(const uint8_t* tile, CompactRegs<NT>& R) {
+  using CR = CompactRegs<NT>;
   const int t = threadIdx.x;
-  const uint4* ks = (const uint4*)(tile + t * 64);
-  const uint4* vs = (const uint4*)(tile + kTileKBytes + t * 64);
+  const uint4* ks = (const uint4*)(tile + t * CR::N16 * 16);
+  const uint4* vs = (const uint4*)(tile + kTileKBytes + t * CR::N16 * 16);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < CR::N16; ++i) {
     R.k[i] = ks[i];
     R.v[i] = vs[i];
   }
   R.pos = t < kBN ? ((const int*)(tile + kTileKBytes + kTileVBytes))[t] : 0;
 }
 
-__device__ inline void store_compact(const CompactRegs& R, Tile& T) {
+template <int NT>
+__device__ inline void store_compact(const CompactRegs<NT>& R, Tile& T) {
+  using CR = CompactRegs<NT>;
   const int t = threadIdx.x;
-  const int col = t >> 2, qd = t & 3;
-  uint4* kd = (uint4*)&T.k[col * kKP + qd * 32];
-  const int d = t >> 1, half = t & 1;
-  uint4* vd = (uint4*)&T.vt[d * kVP + half * 32];
+  // K: byte offset t*N16*16 in a [64][128] bf16 tile
+  const int kb = t * CR::N16 * 8;  // element offset
+  uint4* kd = (uint4*)&T.k[(kb / kD) * kKP + kb % kD];
+  // V^T: element offset in a [128][64] fp16 tile
+  const int vb = t * CR::N16 * 8;
+  _Float16* vd = &T.vt[(vb / kBN) * kVP + vb % kBN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < CR::N16; ++i) {
     kd[i] = R.k[i];
-    vd[i] = R.v[i];
+    // rows of V^T are 136 B apart in LDS: store in 8-byte halves
+    const uint4 w = R.v[i];
+    *(uint2*)(vd + 8 * i) = make_uint2(w.x, w.y);
+    *(uint2*)(vd + 8 * i + 4) = make_uint2(w.z, w.w);
   }
   if (t < kBN) T.pos[t] = R.pos;
 }
@@ -177,9 +214,11 @@ struct MfmaArgs {
   float c2;               // tau * log2(e)
 };
 
-template <int RB, int MODE, bool BASE>
-__global__ __launch_bounds__(kThreads) void k_attn_mfma(MfmaArgs m) {
-  constexpr int BM = 4 * 32 * RB;
+// NW waves of 32 query rows each; BM = 32 * NW rows per block.
+template <int NW, int MODE, bool BASE>
+__global__ __launch_bounds__(64 * NW) void k_attn_mfma(MfmaArgs m) {
+  constexpr int NT = 64 * NW;
+  constexpr int BM = 32 * NW;
   __shared__ Tile tiles[2];
   __shared__ int sh_ntiles;
   const AttnArgs& a = m.a;
@@ -197,51 +236,43 @@ __global__ __launch_bounds__(kThreads) void k_attn_mfma(MfmaArgs m) {
   const int blk = m.nblk - 1 - (u - bh * m.nblk);
   const int b = bh / c.H, h = bh - b * c.H;
 
-  // rows of this block: loop-1 rows are positions; sparse rows are indices
-  // into rows[r] (ATTN) and rows[r] again for UM (queries of loop r-1).
   const int r = a.r;
-  const int nrows = (r == 1 && MODE == kModeAttn) ? c.S : c.n[r];
+  const bool dense = r == 1 && MODE == kModeAttn;
+  const int nrows = dense ? c.S : c.n[r];
   const int row0 = blk * BM;
   const long long bhS = (long long)bh * c.S;
 
-  // ---- per-lane rows, queries and row state
-  int ipos[RB];
-  bf16x8_t qf[RB][8];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int t = row0 + wv * 32 * RB + rb * 32 + l32;
-    int i = -1;
+  // ---- the lane's row, its queries (B operand of S^T = K Q^T)
+  int ipos = -1;
+  bf16x8_t qf[8];
+  {
+    const int t = row0 + wv * 32 + l32;
     long long qrow = 0;
     if (t < nrows) {
-      if (r == 1 && MODE == kModeAttn) {
-        i = t;
-        qrow = (long long)bh * c.S + t;
+      if (dense) {
+        ipos = t;
+        qrow = bhS + t;
       } else {
-        i = c.rows[r][(long long)b * c.n[r] + t];
+        ipos = c.rows[r][(long long)b * c.n[r] + t];
         if (MODE == kModeAttn) {
           qrow = (long long)bh * c.n[r] + t;
         } else {
           const int rp = r - 1;
-          const int qi = rp == 1 ? i : c.slot[rp][(long long)b * c.S + i];
+          const int qi = rp == 1 ? ipos : c.slot[rp][(long long)b * c.S + ipos];
           const int np = rp == 1 ? c.S : c.n[rp];
-          if (qi < 0) i = -1;  // not nested (precondition): leave the row alone
+          if (qi < 0) ipos = -1;  // not nested (precondition): leave the row alone
           qrow = (long long)bh * np + (qi < 0 ? 0 : qi);
         }
       }
     }
-    ipos[rb] = i;
     const bf16x8_t* qp = (const bf16x8_t*)((const uint16_t*)a.q + qrow * kD);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      if (i >= 0) qf[rb][ks] = qp[ks * 2 + hf];
-      else qf[rb][ks] = bf16x8_t{};
-    }
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = ipos >= 0 ? qp[ks * 2 + hf] : bf16x8_t{};
   }
-  // smallest and largest row position of the block (rows ascending)
   int blk_min, blk_max;
   {
     const int t0 = row0, t1 = min(row0 + BM, nrows) - 1;
-    if (r == 1 && MODE == kModeAttn) {
+    if (dense) {
       blk_min = t0;
       blk_max = t1;
     } else {
@@ -249,15 +280,14 @@ __global__ __launch_bounds__(kThreads) void k_attn_mfma(MfmaArgs m) {
       blk_max = c.rows[r][(long long)b * c.n[r] + t1];
     }
   }
-  // number of key tiles that hold a column <= blk_max
   const uint8_t* ctiles = BASE ? nullptr : m.tiles + (long long)bh * m.ntiles_total * kTileBytes;
+  const uint8_t* recs = BASE ? base_rec(c, 0, b, h, 0) : nullptr;
   if (threadIdx.x == 0) {
     int nt;
     if (BASE) {
       nt = (min(blk_max, c.S - 1) + kBN) / kBN;
     } else {
-      // first tile whose first column lies beyond blk_max
-      int lo = 0, hi = m.ntiles_total;
+      int lo = 0, hi = m.ntiles_total;  // first tile whose first column lies beyond blk_max
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
         const int p0 = ((const int*)(ctiles + (long long)mid * kTileBytes + kTileKBytes + kTileVBytes))[0];
@@ -268,37 +298,32 @@ __global__ __launch_bounds__(kThreads) void k_attn_mfma(MfmaArgs m) {
     sh_ntiles = nt;
   }
 
-  float mrow[RB], lrow[RB], off[RB];
-  f32x16_t o[RB][4];
+  // row state: mref = reference max (log2 units), lsum = partial row sum
+  float mref = -INFINITY, lsum = 0.0f;
+  f32x16_t o[4];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    mrow[rb] = -INFINITY;
-    lrow[rb] = 0.0f;
-    off[rb] = 0.0f;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[rb][db] = f32x16_t{};
-    if (MODE == kModeUM) {
-      // loop r-1 statistics of the row: P = M * 2^(x - lse*log2e)
-      float Mp = 0.0f, lp = 0.0f;
-      if (ipos[rb] >= 0) {
-        Mp = a.M[bhS + ipos[rb]];
-        lp = a.lse[bhS + ipos[rb]];
-      }
-      off[rb] = (Mp > 0.0f) ? lp * 1.4426950408889634f : INFINITY;
+  for (int db = 0; db < 4; ++db) o[db] = f32x16_t{};
+  if (MODE == kModeUM) {
+    // loop r-1 statistics of the row: P = M * 2^(x - lse*log2e)
+    float Mp = 0.0f, lp = 0.0f;
+    if (ipos >= 0) {
+      Mp = a.M[bhS + ipos];
+      lp = a.lse[bhS + ipos];
     }
+    mref = (Mp > 0.0f) ? lp * 1.4426950408889634f : INFINITY;
   }
   __syncthreads();
   const int ntiles = sh_ntiles;
 
-  BaseRegs breg;
-  CompactRegs creg;
+  BaseRegs<NT> breg;
+  CompactRegs<NT> creg;
   if (ntiles > 0) {
     if (BASE) {
-      fetch_base(c, b, h, 0, breg);
-      store_base(c, 0, breg, tiles[0]);
+      fetch_base<NT>(recs, c.base_rb, c.S, 0, breg);
+      store_base<NT>(c.S, 0, breg, tiles[0]);
     } else {
-      fetch_compact(ctiles, creg);
-      store_compact(creg, tiles[0]);
+      fetch_compact<NT>(ctiles, creg);
+      store_compact<NT>(creg, tiles[0]);
     }
   }
   __syncthreads();
@@ -307,73 +332,62 @@ __global__ __launch_bounds__(kThreads) void k_attn_mfma(MfmaArgs m) {
     const Tile& T = tiles[tt & 1];
     const bool more = tt + 1 < ntiles;
     if (more) {
-      if (BASE) fetch_base(c, b, h, (tt + 1) * kBN, breg);
-      else fetch_compact(ctiles + (long long)(tt + 1) * kTileBytes, creg);
+      if (BASE) fetch_base<NT>(recs, c.base_rb, c.S, (tt + 1) * kBN, breg);
+      else fetch_compact<NT>(ctiles + (long long)(tt + 1) * kTileBytes, creg);
     }
     // ---- S^T = K Q^T for the 64 columns of the tile
-    f32x16_t s[RB][2];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) s[rb][0] = s[rb][1] = f32x16_t{};
+    f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-        const bf16x8_t kf = *(const bf16x8_t*)&T.k[(jb * 32 + l32) * kKP + ks * 16 + hf * 8];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          s[rb][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[rb][ks], s[rb][jb], 0, 0, 0);
-      }
+      const bf16x8_t k0 = *(const bf16x8_t*)&T.k[l32 * kKP + ks * 16 + hf * 8];
+      const bf16x8_t k1 = *(const bf16x8_t*)&T.k[(32 + l32) * kKP + ks * 16 + hf * 8];
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
     }
     // ---- softmax of the lane's row over the tile's columns
-    const int tmax = T.pos[kBN - 1];
-    f16x8_t pf[RB][4];
+    float x[32];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int i = ipos[rb];
-      float x[32];
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) x[jb * 16 + v] = s[rb][jb][v] * m.c2;
-      }
-      if (tmax > blk_min || i < 0) {
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int col = jb * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
-            if (T.pos[col] > i) x[jb * 16 + v] = -INFINITY;
-          }
-        }
-      }
-      float base;
-      if (MODE == kModeAttn) {
-        float mt = x[0];
-#pragma unroll
-        for (int v = 1; v < 32; ++v) mt = fmaxf(mt, x[v]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float mn = fmaxf(mrow[rb], mt);
-        base = mn == -INFINITY ? 0.0f : mn;
-        const float alpha = __builtin_amdgcn_exp2f(mrow[rb] - base);
-        mrow[rb] = mn;
-        lrow[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[rb][db] *= alpha;
-      } else {
-        base = off[rb];
-      }
-      float ls = 0.0f;
-#pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(x[k2 * 8 + e] - base);
-          ls += p;
-          pf[rb][k2][e] = (_Float16)p;
-        }
-      }
-      lrow[rb] += ls;
+    for (int v = 0; v < 16; ++v) {
+      x[v] = s0[v];
+      x[16 + v] = s1[v];
     }
+    if (T.pos[kBN - 1] > blk_min || ipos < 0) {
+#pragma unroll
+      for (int v = 0; v < 32; ++v) {
+        const int col = (v >> 4) * 32 + 8 * ((v & 15) >> 2) + 4 * hf + (v & 3);
+        if (T.pos[col] > ipos) x[v] = -INFINITY;
+      }
+    }
+    if (MODE == kModeAttn) {
+      float mt = x[0];
+#pragma unroll
+      for (int v = 1; v < 32; ++v) mt = fmaxf(mt, x[v]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * m.c2;
+      // rescale only when the row max outgrows the reference by 2^8 (or the
+      // reference is unset); otherwise P stays below 2^8 and fp16 holds it
+      const bool need = mt > mref + kRescale;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float mn = need ? mt : mref;
+        const float alpha = need ? __builtin_amdgcn_exp2f(mref - mn) : 1.0f;
+        mref = mn;
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      }
+    }
+    const float base = (MODE == kModeAttn && mref == -INFINITY) ? 0.0f : mref;
+    f16x8_t pf[4];
+    float ls = 0.0f;
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[k2 * 8 + e], m.c2, -base));
+        ls += p;
+        pf[k2][e] = (_Float16)p;
+      }
+    }
+    lsum += ls;
     // ---- O^T += V^T P^T
 #pragma unroll
     for (int k2 = 0; k2 < 4; ++k2) {
@@ -384,79 +398,74 @@ __global__ __launch_bounds__(kThreads) void k_attn_mfma(MfmaArgs m) {
         const f16x4_t lo4 = *(const f16x4_t*)vp;
         const f16x4_t hi4 = *(const f16x4_t*)(vp + 8);
         const f16x8_t vf = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[rb][k2], o[rb][db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[k2], o[db], 0, 0, 0);
       }
     }
     if (more) {
-      if (BASE) store_base(c, (tt + 1) * kBN, breg, tiles[(tt + 1) & 1]);
-      else store_compact(creg, tiles[(tt + 1) & 1]);
+      if (BASE) store_base<NT>(c.S, (tt + 1) * kBN, breg, tiles[(tt + 1) & 1]);
+      else store_compact<NT>(creg, tiles[(tt + 1) & 1]);
     }
     __syncthreads();
   }
 
   // ---- epilogue: each lane writes 64 of its row's 128 dims
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int i = ipos[rb];
-    const float lt = lrow[rb] + __shfl_xor(lrow[rb], 32, 64);
-    if (i < 0) continue;
-    const long long rowp = (bhS + i) * kD;
-    if (MODE == kModeAttn) {
-      if (r == 1) {
-        const float inv = 1.0f / lt;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            const int dcol = db * 32 + qq * 8 + hf * 4;
-            f32x4_t ov = {o[rb][db][qq * 4] * inv, o[rb][db][qq * 4 + 1] * inv, o[rb][db][qq * 4 + 2] * inv,
-                          o[rb][db][qq * 4 + 3] * inv};
-            *(f32x4_t*)&a.O[rowp + dcol] = ov;
-            *(f32x4_t*)&a.U[rowp + dcol] = f32x4_t{};
-          }
-        }
-        if (hf == 0) {
-          a.lse[bhS + i] = (mrow[rb] + __log2f(lt)) * 0.6931471805599453f;
-          a.M[bhS + i] = 1.0f;
-        }
-      } else if (lt > 0.0f) {
-        const float Mi = a.M[bhS + i];
-        const float sc = Mi / lt;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            const int dcol = db * 32 + qq * 8 + hf * 4;
-            const f32x4_t uv = *(const f32x4_t*)&a.U[rowp + dcol];
-            f32x4_t ov;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ov[e] = uv[e] + sc * o[rb][db][qq * 4 + e];
-            *(f32x4_t*)&a.O[rowp + dcol] = ov;
-          }
-        }
-        if (hf == 0) a.lse[bhS + i] = (mrow[rb] + __log2f(lt)) * 0.6931471805599453f;
-      } else if (hf == 0) {
-        a.lse[bhS + i] = -INFINITY;
-      }
-    } else {
-      const float Mp = a.M[bhS + i];
-      const float Mu = Mp > 0.0f ? Mp : 0.0f;
+  const float lt = lsum + __shfl_xor(lsum, 32, 64);
+  if (ipos < 0) return;
+  const int i = ipos;
+  const long long rowp = (bhS + i) * kD;
+  if (MODE == kModeAttn) {
+    if (r == 1) {
+      const float inv = 1.0f / lt;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           const int dcol = db * 32 + qq * 8 + hf * 4;
-          const f32x4_t ov = *(const f32x4_t*)&a.O[rowp + dcol];
-          f32x4_t uv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) uv[e] = ov[e] - Mu * o[rb][db][qq * 4 + e];
-          *(f32x4_t*)&a.U[rowp + dcol] = uv;
+          f32x4_t ov = {o[db][qq * 4] * inv, o[db][qq * 4 + 1] * inv, o[db][qq * 4 + 2] * inv,
+                        o[db][qq * 4 + 3] * inv};
+          *(f32x4_t*)&a.O[rowp + dcol] = ov;
+          *(f32x4_t*)&a.U[rowp + dcol] = f32x4_t{};
         }
       }
-      if (hf == 0) a.M[bhS + i] = Mu * lt;
+      if (hf == 0) {
+        a.lse[bhS + i] = (mref + __log2f(lt)) * 0.6931471805599453f;
+        a.M[bhS + i] = 1.0f;
+      }
+    } else if (lt > 0.0f) {
+      const float Mi = a.M[bhS + i];
+      const float sc = Mi / lt;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int dcol = db * 32 + qq * 8 + hf * 4;
+          const f32x4_t uv = *(const f32x4_t*)&a.U[rowp + dcol];
+          f32x4_t ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = uv[e] + sc * o[db][qq * 4 + e];
+          *(f32x4_t*)&a.O[rowp + dcol] = ov;
+        }
+      }
+      if (hf == 0) a.lse[bhS + i] = (mref + __log2f(lt)) * 0.6931471805599453f;
+    } else if (hf == 0) {
+      a.lse[bhS + i] = -INFINITY;
     }
+  } else {
+    const float Mp = a.M[bhS + i];
+    const float Mu = Mp > 0.0f ? Mp : 0.0f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int dcol = db * 32 + qq * 8 + hf * 4;
+        const f32x4_t ov = *(const f32x4_t*)&a.O[rowp + dcol];
+        f32x4_t uv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) uv[e] = ov[e] - Mu * o[db][qq * 4 + e];
+        *(f32x4_t*)&a.U[rowp + dcol] = uv;
+      }
+    }
+    if (hf == 0) a.M[bhS + i] = Mu * lt;
   }
 }
 
@@ -510,6 +519,7 @@ __global__ __launch_bounds__(256) void k_gather_cols(CacheGeo c, int rc, const i
 // streams the active rows' loop r-1 queries through LDS in tiles of 64 rows,
 // double buffered.  Column sums accumulate in a fixed order: deterministic.
 constexpr int kMassRows = 64;
+constexpr int kThreads = 256;
 
 struct __align__(16) RowTile {
   __bf16 q[kMassRows * kKP];
@@ -727,14 +737,25 @@ hipError_t launch_gather(const CacheGeo& c, int rc, const int32_t* sel, int K, u
   return hipGetLastError();
 }
 
-template <int RB, int MODE, bool BASE>
+template <int NW, int MODE, bool BASE>
 static hipError_t launch_one(const MfmaArgs& m, hipStream_t st) {
   const int nunits = m.a.c.B * m.a.c.H * m.nblk;
-  hipLaunchKernelGGL((k_attn_mfma<RB, MODE, BASE>), dim3(nunits), dim3(kThreads), 0, st, m);
+  hipLaunchKernelGGL((k_attn_mfma<NW, MODE, BASE>), dim3(nunits), dim3(64 * NW), 0, st, m);
   return hipGetLastError();
 }
 
 static float c2_of(int d) { return (float)(1.4426950408889634 / __builtin_sqrt((double)d)); }
+
+// Sparse-row launch: 8-wave blocks when they still fill the chip twice.
+template <int MODE>
+static hipError_t launch_rows(MfmaArgs& m, int n, hipStream_t st) {
+  if ((long long)m.a.c.B * m.a.c.H * ((n + 255) / 256) >= 512) {
+    m.nblk = (n + 255) / 256;
+    return launch_one<8, MODE, false>(m, st);
+  }
+  m.nblk = (n + 127) / 128;
+  return launch_one<4, MODE, false>(m, st);
+}
 
 // Loop-r attention: r == 1 dense over the base; r >= 2 over gathered tiles
 // (ws: gather_bytes(c, K) bytes).
@@ -744,19 +765,13 @@ hipError_t launch_attn_mfma(const AttnArgs& a, uint8_t* ws, hipStream_t st) {
   m.c2 = c2_of(a.c.d);
   if (a.r == 1) {
     m.nblk = (a.c.S + 255) / 256;
-    return launch_one<2, kModeAttn, true>(m, st);
+    return launch_one<8, kModeAttn, true>(m, st);
   }
   hipError_t e = launch_gather(a.c, a.r, a.sel, a.K, ws, st);
   if (e != hipSuccess) return e;
   m.tiles = ws;
   m.ntiles_total = (a.K + kBN - 1) / kBN;
-  const int n = a.c.n[a.r];
-  if ((long long)a.c.B * a.c.H * ((n + 255) / 256) >= 512) {
-    m.nblk = (n + 255) / 256;
-    return launch_one<2, kModeAttn, false>(m, st);
-  }
-  m.nblk = (n + 127) / 128;
-  return launch_one<1, kModeAttn, false>(m, st);
+  return launch_rows<kModeAttn>(m, a.c.n[a.r], st);
 }
 
 // Cached mass and reused part of loop r over S_r = a.sel (chain r-1).
@@ -768,15 +783,8 @@ hipError_t launch_um_mfma(const AttnArgs& a, uint8_t* ws, hipStream_t st) {
   if (e != hipSuccess) return e;
   m.tiles = ws;
   m.ntiles_total = (a.K + kBN - 1) / kBN;
-  const int n = a.c.n[a.r];
-  if ((long long)a.c.B * a.c.H * ((n + 255) / 256) >= 512) {
-    m.nblk = (n + 255) / 256;
-    return launch_one<2, kModeUM, false>(m, st);
-  }
-  m.nblk = (n + 127) / 128;
-  return launch_one<1, kModeUM, false>(m, st);
+  return launch_rows<kModeUM>(m, a.c.n[a.r], st);
 }
-
 
 // Column mass of the candidates (r == 2 with cand == NULL reads the base
 // directly; otherwise the candidates' chains r-1 are gathered into ws first).
