@@ -79,7 +79,7 @@ def prefill_bench(args, torch, fl, workloads, acc):
     for r in range(2, R + 1):
         Ks[r - 1] = min(cfg.K, Ks[r - 2])
     sel = [None] + [torch.empty(B, H, Ks[r], dtype=torch.int32, device="cuda") for r in range(1, R)]
-    ws_bytes = 16
+    ws_bytes = fl.fl_workspace_bytes(fl.FL_WS_ATTN, cache.fl, 1, S, S)
     for r in range(2, R + 1):
         ws_bytes = max(ws_bytes, fl.fl_workspace_bytes(fl.FL_WS_COLSEL, cache.fl, r, Ks[r - 2], Ks[r - 1]),
                        fl.fl_workspace_bytes(fl.FL_WS_ATTN, cache.fl, r, Ks[r - 1], Ks[r - 1]))

@@ -137,7 +137,7 @@ size_t fl_workspace_bytes(int which, const fl_cache* cache, int r, int K_prev, i
     const int kt = (r == 2 && K_prev == cache->S) ? K_r : K_prev;
     return align256((size_t)cache->B * cache->H * (size_t)K_prev * sizeof(float)) + tiles_bytes(cache, kt);
   }
-  if (which == FL_WS_ATTN) return r >= 2 ? tiles_bytes(cache, K_r) : 0;
+  if (which == FL_WS_ATTN) return tiles_bytes(cache, r == 1 ? cache->S : K_r);
   return 0;
 }
 
@@ -245,7 +245,9 @@ fl_status fl_loop_attn(const fl_cache* cache, int r, const void* q, fl_dtype dty
   if (r >= 2) {
     FL_NEED_PTR4(sel, "sel");
     if (K_r < 1 || K_r > cache->S) return fail(FL_EINVAL, "%s: K_r = %d outside [1, S]", fn, K_r);
-    const size_t need = fl_workspace_bytes(FL_WS_ATTN, cache, r, K_r, K_r);
+  }
+  {
+    const size_t need = dtype == FL_BF16 ? fl_workspace_bytes(FL_WS_ATTN, cache, r, K_r, K_r) : 0;
     if (need > 0 && (!ws || ws_bytes < need))
       return fail(FL_EINVAL, "%s: workspace of %zu bytes needed (got %zu)", fn, need, ws ? ws_bytes : (size_t)0);
     if (need > 0 && !aligned16(ws)) return fail(FL_EINVAL, "%s: ws is not 16-byte aligned", fn);

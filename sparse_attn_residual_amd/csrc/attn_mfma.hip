@@ -20,9 +20,14 @@
 //    v_mfma_f32_32x32x16_f16: P in [0, 1] needs significand, not range, and
 //    bf16 rounding alone would spend the whole error budget; the bf16 value
 //    v~ converts to fp16 exactly;
-//  * loop 1 dequantizes the int8 base records into the LDS tiles inside the
-//    kernel; sparse loops read the compact tiles gathered by k_gather_cols
-//    (p1 §4.4: selected tokens and keys gathered into compact buffers).
+//  * every record a loop attends is dequantized once per loop by
+//    k_build_tiles into 64-column tile images laid out exactly like the LDS
+//    tiles (p1 §4.4: selected tokens and keys gathered into compact
+//    buffers); the attention kernel copies them into a three-deep LDS ring
+//    with direct global->LDS loads and overlaps the QK^T of the next tile
+//    with the softmax of the current one.  Dequantizing inside the
+//    attention kernel instead would repeat the work for every row block and
+//    the vector ALUs are already the busier unit on gfx950.
 #include "launch.hpp"
 
 namespace fl {
@@ -34,173 +39,117 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;
-constexpr int kBN = 64;        // key columns per tile
-constexpr int kKP = kD + 8;    // LDS pitch of the K tile (bf16 elements): 272 B
-constexpr int kVP = kBN + 4;   // LDS pitch of the V^T tile (fp16 elements): 136 B
+constexpr int kBN = 64;             // key columns per tile
 constexpr int kNoPos = 0x7fffffff;  // padding column: masked for every row
 constexpr float kRescale = 8.0f;    // lazy rescale threshold (log2 units): P <= 2^8
 
-struct __align__(16) Tile {
-  __bf16 k[kBN * kKP];
-  _Float16 vt[kD * kVP];
-  int pos[kBN];
-};
-
-// Compact gathered tiles (k_gather_cols): per (b, h, tile): K [64][128] bf16,
-// then V^T [128][64] fp16, then positions [64] int32.
-constexpr int kTileKBytes = kBN * kD * 2;
-constexpr int kTileVBytes = kD * kBN * 2;
-constexpr int kTileBytes = kTileKBytes + kTileVBytes + kBN * 4;
+// Tile image: the exact LDS layout of one 64-column tile, built once per loop
+// in HBM and copied into LDS by direct global->LDS loads.
+//   K   [64][kKP]  bf16  (row = column of the tile, 272-byte rows)
+//   V^T [128][kVP] fp16  (row = head dim, 136-byte rows)
+//   pos [64]       int32 (position of each column, kNoPos for padding)
+constexpr int kKP = kD + 8;
+constexpr int kVP = kBN + 4;
+constexpr int kImgV = kBN * kKP * 2;          // 17408
+constexpr int kImgPos = kImgV + kD * kVP * 2;  // 34816
+constexpr int kImgBytes = 35 * 1024;           // 35840: 35 chunks of 1 KB
+constexpr int kImgChunks = kImgBytes / 1024;
+constexpr int kRing = 3;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 // Two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
   const bf16x2_t v = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
   return __builtin_bit_cast(uint32_t, v);
 }
-// v~ = bf16(x) converted to fp16 (exact for every bf16 value above 2^-17 in
-// magnitude; smaller values round to the fp16 subnormal grid).
+// v~ = bf16(x), stored as fp16 (exact for every bf16 value above 2^-17 in
+// magnitude; smaller ones round to the fp16 subnormal grid).
 __device__ inline _Float16 bf16_as_f16(float x) { return (_Float16)round_bf16(x); }
-__device__ inline void bf16x2_as_f16(float a, float b, _Float16& ha, _Float16& hb) {
-  const uint32_t w = pack_bf16x2(a, b);
-  ha = (_Float16)__uint_as_float(w << 16);
-  hb = (_Float16)__uint_as_float(w & 0xFFFF0000u);
-}
 
-// ------------------------------------------------------------- tile loaders
-// Loop-1 loader: columns j0..j0+63 of the int8 base of (b, h), NT threads.
-template <int NT>
-struct BaseRegs {
-  static constexpr int KCH = kBN * kD / NT;        // K codes per thread (16 or 32)
-  static constexpr int VCOL = kBN * 32 / NT;       // V columns per thread (4 or 8)
-  uint32_t kc[KCH / 4];
-  uint16_t ks;
-  uint32_t vc[VCOL];
-  uint16_t vs[VCOL];
-};
-
-template <int NT>
-__device__ inline void fetch_base(const uint8_t* recs, int rb, int S, int j0, BaseRegs<NT>& R) {
-  using BR = BaseRegs<NT>;
-  const int t = threadIdx.x;
-  constexpr int PER = kD / BR::KCH;  // threads per column for K
-  const int col = t / PER, part = t % PER;
-  const int j = j0 + col;
-  if (j < S) {
-    const uint8_t* rec = recs + (uint32_t)j * rb;
+// ------------------------------------------------------------- tile images
+// 32 consecutive dims [g*32, g*32+32) of K (kv = 0) or V (kv = 1) of token j
+// reconstructed at loop rc: the base plus the residuals of the loops <= rc
+// in which j was active, added in fp32 in loop order.
+__device__ inline void chain32(const CacheGeo& c, int rc, int b, int h, int j, int kv, int g, float* x) {
+  const uint8_t* rec = base_rec(c, 0, b, h, j);
+  const uint4 w0 = *(const uint4*)(rec + kv * kD + g * 32);
+  const uint4 w1 = *(const uint4*)(rec + kv * kD + g * 32 + 16);
+  const float s = h2f(((const uint16_t*)(rec + 2 * kD))[kv * 4 + g]);
+  const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-    for (int w = 0; w < BR::KCH / 16; ++w) {
-      const uint4 v = *(const uint4*)(rec + part * BR::KCH + w * 16);
-      R.kc[4 * w] = v.x; R.kc[4 * w + 1] = v.y; R.kc[4 * w + 2] = v.z; R.kc[4 * w + 3] = v.w;
-    }
-    R.ks = ((const uint16_t*)(rec + 2 * kD))[part * BR::KCH / 32];
-  } else {
+  for (int e = 0; e < 32; ++e) x[e] = (float)(int8_t)(w[e >> 2] >> (8 * (e & 3))) * s;
+  for (int rr = 2; rr <= rc; ++rr) {
+    const int t = c.slot[rr][(long long)b * c.S + j];
+    if (t < 0) break;
+    const uint8_t* rrec = res_rec(c, rr, 0, b, h, t);
+    const int bits = c.bits[rr];
+    const int C = kD * bits / 8;
+    const uint16_t* meta = (const uint16_t*)(rrec + 2 * C);
+    const float rs = h2f(meta[(2 * kv) * 4 + g]);
+    const float rz = h2f(meta[(2 * kv + 1) * 4 + g]);
+    if (bits == 4) {
+      const uint4 pw = *(const uint4*)(rrec + kv * C + g * 16);
+      const uint32_t ws[4] = {pw.x, pw.y, pw.z, pw.w};
 #pragma unroll
-    for (int w = 0; w < BR::KCH / 4; ++w) R.kc[w] = 0;
-    R.ks = 0;
-  }
-  const int d4 = t & 31, jg = t >> 5;
-#pragma unroll
-  for (int e = 0; e < BR::VCOL; ++e) {
-    const int jj = j0 + jg * BR::VCOL + e;
-    if (jj < S) {
-      const uint8_t* rec = recs + (uint32_t)jj * rb;
-      R.vc[e] = *(const uint32_t*)(rec + kD + d4 * 4);
-      R.vs[e] = ((const uint16_t*)(rec + 2 * kD))[4 + (d4 >> 3)];
+      for (int e = 0; e < 32; ++e) x[e] = x[e] + __builtin_fmaf((float)((ws[e >> 3] >> (4 * (e & 7))) & 15), rs, rz);
     } else {
-      R.vc[e] = 0;
-      R.vs[e] = 0;
+      const uint2 pw = *(const uint2*)(rrec + kv * C + g * 8);
+      const uint32_t ws[2] = {pw.x, pw.y};
+#pragma unroll
+      for (int e = 0; e < 32; ++e) x[e] = x[e] + __builtin_fmaf((float)((ws[e >> 4] >> (2 * (e & 15))) & 3), rs, rz);
     }
   }
 }
 
-template <int NT>
-__device__ inline void store_base(int S, int j0, const BaseRegs<NT>& R, Tile& T) {
-  using BR = BaseRegs<NT>;
+// One block of 256 threads per tile: columns sel[tile*64 .. +64) (sel NULL:
+// positions tile*64 ..), reconstructed at loop rc, staged in LDS in the image
+// layout and written out with 16-byte stores.  Every packed record a loop
+// attends is dequantized exactly once here (p1 §4.4: selected keys gathered
+// into compact buffers; p1 App. G: the packed streams are read directly).
+__global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const int32_t* __restrict__ sel, int K,
+                                                     int ntiles, uint8_t* __restrict__ out) {
+  __shared__ __align__(16) uint8_t img[kImgBytes];
+  const int bh = blockIdx.x / ntiles;
+  const int tile = blockIdx.x - bh * ntiles;
+  const int b = bh / c.H, h = bh - b * c.H;
   const int t = threadIdx.x;
-  constexpr int PER = kD / BR::KCH;
-  const int col = t / PER, part = t % PER;
+  const int col = t >> 2, g = t & 3;
+  const int idx = tile * kBN + col;
+  const int j = idx < K ? (sel ? sel[(long long)bh * K + idx] : idx) : -1;
+  float x[32];
+  // K rows (bf16)
+  if (j >= 0) chain32(c, rc, b, h, j, 0, g, x);
+  else {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) x[e] = 0.0f;
+  }
   {
-    const float s = h2f(R.ks);
-    uint32_t o[BR::KCH / 2];
+    uint4* dst = (uint4*)(img + (col * kKP + g * 32) * 2);
 #pragma unroll
-    for (int i = 0; i < BR::KCH / 4; ++i) {
-      const uint32_t w = R.kc[i];
-      o[2 * i] = pack_bf16x2((float)(int8_t)(w) * s, (float)(int8_t)(w >> 8) * s);
-      o[2 * i + 1] = pack_bf16x2((float)(int8_t)(w >> 16) * s, (float)(int8_t)(w >> 24) * s);
-    }
-    uint4* dst = (uint4*)&T.k[col * kKP + part * BR::KCH];
+    for (int i = 0; i < 4; ++i)
+      dst[i] = make_uint4(pack_bf16x2(x[8 * i], x[8 * i + 1]), pack_bf16x2(x[8 * i + 2], x[8 * i + 3]),
+                          pack_bf16x2(x[8 * i + 4], x[8 * i + 5]), pack_bf16x2(x[8 * i + 6], x[8 * i + 7]));
+  }
+  // V^T rows (bf16 value in fp16)
+  if (j >= 0) chain32(c, rc, b, h, j, 1, g, x);
+  else {
 #pragma unroll
-    for (int i = 0; i < BR::KCH / 8; ++i) dst[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+    for (int e = 0; e < 32; ++e) x[e] = 0.0f;
   }
   {
-    const int d4 = t & 31, jg = t >> 5;
-    _Float16 out[4][BR::VCOL];
+    _Float16* vt = (_Float16*)(img + kImgV);
 #pragma unroll
-    for (int e = 0; e < BR::VCOL; ++e) {
-      const float s = h2f(R.vs[e]);
-      const uint32_t w = R.vc[e];
-      bf16x2_as_f16((float)(int8_t)(w) * s, (float)(int8_t)(w >> 8) * s, out[0][e], out[1][e]);
-      bf16x2_as_f16((float)(int8_t)(w >> 16) * s, (float)(int8_t)(w >> 24) * s, out[2][e], out[3][e]);
-    }
-#pragma unroll
-    for (int dd = 0; dd < 4; ++dd) {
-      _Float16* dst = &T.vt[(d4 * 4 + dd) * kVP + jg * BR::VCOL];
-      if constexpr (BR::VCOL == 4) {
-        *(f16x4_t*)dst = f16x4_t{out[dd][0], out[dd][1], out[dd][2], out[dd][3]};
-      } else {
-        *(f16x4_t*)dst = f16x4_t{out[dd][0], out[dd][1], out[dd][2], out[dd][3]};
-        *(f16x4_t*)(dst + 4) = f16x4_t{out[dd][4], out[dd][5], out[dd][6], out[dd][7]};
-      }
-    }
+    for (int e = 0; e < 32; ++e) vt[(g * 32 + e) * kVP + col] = bf16_as_f16(x[e]);
   }
-  if (t < kBN) T.pos[t] = (j0 + t < S) ? j0 + t : kNoPos;
-}
-
-// Compact-tile loader (sparse loops), NT threads.
-template <int NT>
-struct CompactRegs {
-  static constexpr int N16 = kTileKBytes / 16 / NT;  // uint4 per thread per half (4 or 2)
-  uint4 k[N16];
-  uint4 v[N16];
-  int pos;
-};
-
-template <int NT>
-__device__ inline void fetch_compact(const uint8_t* tile, CompactRegs<NT>& R) {
-  using CR = CompactRegs<NT>;
-  const int t = threadIdx.x;
-  const uint4* ks = (const uint4*)(tile + t * CR::N16 * 16);
-  const uint4* vs = (const uint4*)(tile + kTileKBytes + t * CR::N16 * 16);
-#pragma unroll
-  for (int i = 0; i < CR::N16; ++i) {
-    R.k[i] = ks[i];
-    R.v[i] = vs[i];
-  }
-  R.pos = t < kBN ? ((const int*)(tile + kTileKBytes + kTileVBytes))[t] : 0;
-}
-
-template <int NT>
-__device__ inline void store_compact(const CompactRegs<NT>& R, Tile& T) {
-  using CR = CompactRegs<NT>;
-  const int t = threadIdx.x;
-  // K: byte offset t*N16*16 in a [64][128] bf16 tile
-  const int kb = t * CR::N16 * 8;  // element offset
-  uint4* kd = (uint4*)&T.k[(kb / kD) * kKP + kb % kD];
-  // V^T: element offset in a [128][64] fp16 tile
-  const int vb = t * CR::N16 * 8;
-  _Float16* vd = &T.vt[(vb / kBN) * kVP + vb % kBN];
-#pragma unroll
-  for (int i = 0; i < CR::N16; ++i) {
-    kd[i] = R.k[i];
-    // rows of V^T are 136 B apart in LDS: store in 8-byte halves
-    const uint4 w = R.v[i];
-    *(uint2*)(vd + 8 * i) = make_uint2(w.x, w.y);
-    *(uint2*)(vd + 8 * i + 4) = make_uint2(w.z, w.w);
-  }
-  if (t < kBN) T.pos[t] = R.pos;
+  if (g == 0) ((int*)(img + kImgPos))[col] = j >= 0 ? j : kNoPos;
+  __syncthreads();
+  uint4* dst = (uint4*)(out + ((long long)bh * ntiles + tile) * kImgBytes);
+  const uint4* src = (const uint4*)img;
+  for (int i = t; i < kImgBytes / 16; i += 256) dst[i] = src[i];
 }
 
 // ------------------------------------------------------------- main kernel
@@ -208,23 +157,142 @@ enum { kModeAttn = 0, kModeUM = 1 };
 
 struct MfmaArgs {
   AttnArgs a;
-  const uint8_t* tiles;   // compact tiles [B][H][ntiles] (sparse loaders)
-  int ntiles_total;       // tiles per (b, h) in `tiles`
+  const uint8_t* tiles;   // tile images [B][H][ntiles_total]
+  int ntiles_total;       // tiles per (b, h)
   int nblk;               // row blocks per (b, h)
   float c2;               // tau * log2(e)
 };
 
-// NW waves of 32 query rows each; BM = 32 * NW rows per block.
-template <int NW, int MODE, bool BASE>
-__global__ __launch_bounds__(64 * NW) void k_attn_mfma(MfmaArgs m) {
-  constexpr int NT = 64 * NW;
-  constexpr int BM = 32 * NW;
-  __shared__ Tile tiles[2];
+template <int NW>
+__device__ inline void dma_tile(const uint8_t* img, uint8_t* lds) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int ch = wv; ch < kImgChunks; ch += NW)
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(img + ch * 1024 + lane * 16), (lds_void_t*)(lds + ch * 1024), 16,
+                                     0, 0);
+}
+
+// S^T = K Q^T for one tile: the lane's row against the tile's 64 columns.
+__device__ inline void qk_tile(const uint8_t* T, const bf16x8_t* qf, int l32, int hf, f32x16_t& s0, f32x16_t& s1) {
+  const __bf16* kt = (const __bf16*)T;
+#ifdef FLV_QK4
+  f32x16_t a0 = f32x16_t{}, a1 = f32x16_t{}, b0 = f32x16_t{}, b1 = f32x16_t{};
+#pragma unroll
+  for (int ks = 0; ks < 8; ks += 2) {
+    const bf16x8_t k0 = *(const bf16x8_t*)&kt[l32 * kKP + ks * 16 + hf * 8];
+    const bf16x8_t k1 = *(const bf16x8_t*)&kt[(32 + l32) * kKP + ks * 16 + hf * 8];
+    const bf16x8_t k2 = *(const bf16x8_t*)&kt[l32 * kKP + ks * 16 + 16 + hf * 8];
+    const bf16x8_t k3 = *(const bf16x8_t*)&kt[(32 + l32) * kKP + ks * 16 + 16 + hf * 8];
+    a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], a0, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], a1, 0, 0, 0);
+    b0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k2, qf[ks + 1], b0, 0, 0, 0);
+    b1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k3, qf[ks + 1], b1, 0, 0, 0);
+  }
+  s0 = a0 + b0;
+  s1 = a1 + b1;
+#else
+  s0 = f32x16_t{};
+  s1 = f32x16_t{};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const bf16x8_t k0 = *(const bf16x8_t*)&kt[l32 * kKP + ks * 16 + hf * 8];
+    const bf16x8_t k1 = *(const bf16x8_t*)&kt[(32 + l32) * kKP + ks * 16 + hf * 8];
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
+  }
+#endif
+}
+
+// Softmax step of one tile for the lane's row ("ALU phase"): causal mask,
+// running max with lazy rescale (ATTN) or fixed loop r-1 statistics (UM),
+// P = 2^(x*c2 - base) rounded to fp16, partial row sum.
+template <int MODE>
+__device__ inline void softmax_tile(const uint8_t* T, f32x16_t s0, f32x16_t s1, int ipos, int blk_min, int hf, float c2,
+                                    float& mref, float& lsum, f32x16_t* o, f16x8_t* pf) {
+  const int* tpos = (const int*)(T + kImgPos);
+  float x[32];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    x[v] = s0[v];
+    x[16 + v] = s1[v];
+  }
+  if (tpos[kBN - 1] > blk_min || ipos < 0) {
+#pragma unroll
+    for (int v = 0; v < 32; ++v) {
+      const int col = (v >> 4) * 32 + 8 * ((v & 15) >> 2) + 4 * hf + (v & 3);
+      if (tpos[col] > ipos) x[v] = -INFINITY;
+    }
+  }
+  if (MODE == kModeAttn) {
+    float mt = x[0];
+#pragma unroll
+    for (int v = 1; v < 32; ++v) mt = fmaxf(mt, x[v]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * c2;
+    // rescale only when the row max outgrows the reference by 2^8 (or the
+    // reference is unset); otherwise P stays below 2^8 and fp16 holds it
+    const bool need = mt > mref + kRescale;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float mn = need ? mt : mref;
+      const float alpha = need ? __builtin_amdgcn_exp2f(mref - mn) : 1.0f;
+      mref = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+    }
+  }
+  const float base = (MODE == kModeAttn && mref == -INFINITY) ? 0.0f : mref;
+  float ls = 0.0f;
+#pragma unroll
+  for (int k2 = 0; k2 < 4; ++k2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[k2 * 8 + e], c2, -base));
+      ls += p;
+      pf[k2][e] = (_Float16)p;
+    }
+  }
+  lsum += ls;
+}
+
+// O^T += V^T P^T for one tile ("GEMM phase", second half).
+__device__ inline void pv_tile(const uint8_t* T, const f16x8_t* pf, int l32, int hf, f32x16_t* o) {
+  const _Float16* vt = (const _Float16*)(T + kImgV);
+#pragma unroll
+  for (int k2 = 0; k2 < 4; ++k2) {
+    const int c0 = k2 * 16 + hf * 4;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const _Float16* vp = &vt[(db * 32 + l32) * kVP + c0];
+      const f16x4_t lo4 = *(const f16x4_t*)vp;
+      const f16x4_t hi4 = *(const f16x4_t*)(vp + 8);
+      const f16x8_t vf = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[k2], o[db], 0, 0, 0);
+    }
+  }
+}
+
+__device__ inline void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// 8 waves of 32 query rows (BM = 256) in two groups of four.  Wave w and
+// wave w+4 share a SIMD; group 1 runs one phase behind group 0, so while one
+// group multiplies on the matrix cores (GEMM phase: S of tile t+1 and
+// O += P V of tile t) the other forms the probabilities of its tile on the
+// vector ALUs (ALU phase).  Block barriers separate the phases; tile images
+// arrive by direct global->LDS loads issued two phases before first use, so
+// the loop itself writes no LDS.
+template <int MODE>
+__global__ __launch_bounds__(512) void k_attn_mfma(MfmaArgs m) {
+  constexpr int BM = 256;
+  extern __shared__ __align__(16) uint8_t lds[];   // kRing tile images
   __shared__ int sh_ntiles;
   const AttnArgs& a = m.a;
   const CacheGeo& c = a.c;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
+  const int grp = wv >> 2;        // phase group
   const int hf = lane >> 5;       // half of the wave
   const int l32 = lane & 31;
 
@@ -234,15 +302,16 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(MfmaArgs m) {
   if ((nunits & 7) == 0) u = (u & 7) * (nunits >> 3) + (u >> 3);
   const int bh = u / m.nblk;
   const int blk = m.nblk - 1 - (u - bh * m.nblk);
-  const int b = bh / c.H, h = bh - b * c.H;
+  const int b = bh / c.H;
 
   const int r = a.r;
   const bool dense = r == 1 && MODE == kModeAttn;
   const int nrows = dense ? c.S : c.n[r];
   const int row0 = blk * BM;
   const long long bhS = (long long)bh * c.S;
+  const uint8_t* imgs = m.tiles + (long long)bh * m.ntiles_total * kImgBytes;
 
-  // ---- the lane's row, its queries (B operand of S^T = K Q^T)
+  // ---- the lane's row and its queries (B operand of S^T = K Q^T)
   int ipos = -1;
   bf16x8_t qf[8];
   {
@@ -280,22 +349,14 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(MfmaArgs m) {
       blk_max = c.rows[r][(long long)b * c.n[r] + t1];
     }
   }
-  const uint8_t* ctiles = BASE ? nullptr : m.tiles + (long long)bh * m.ntiles_total * kTileBytes;
-  const uint8_t* recs = BASE ? base_rec(c, 0, b, h, 0) : nullptr;
   if (threadIdx.x == 0) {
-    int nt;
-    if (BASE) {
-      nt = (min(blk_max, c.S - 1) + kBN) / kBN;
-    } else {
-      int lo = 0, hi = m.ntiles_total;  // first tile whose first column lies beyond blk_max
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        const int p0 = ((const int*)(ctiles + (long long)mid * kTileBytes + kTileKBytes + kTileVBytes))[0];
-        if (p0 <= blk_max) lo = mid + 1; else hi = mid;
-      }
-      nt = lo;
+    int lo = 0, hi = m.ntiles_total;  // first tile whose first column lies beyond blk_max
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      const int p0 = *(const int*)(imgs + (long long)mid * kImgBytes + kImgPos);
+      if (p0 <= blk_max) lo = mid + 1; else hi = mid;
     }
-    sh_ntiles = nt;
+    sh_ntiles = lo;
   }
 
   // row state: mref = reference max (log2 units), lsum = partial row sum
@@ -313,99 +374,40 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(MfmaArgs m) {
     mref = (Mp > 0.0f) ? lp * 1.4426950408889634f : INFINITY;
   }
   __syncthreads();
-  const int ntiles = sh_ntiles;
+  const int nt = sh_ntiles;
 
-  BaseRegs<NT> breg;
-  CompactRegs<NT> creg;
-  if (ntiles > 0) {
-    if (BASE) {
-      fetch_base<NT>(recs, c.base_rb, c.S, 0, breg);
-      store_base<NT>(c.S, 0, breg, tiles[0]);
-    } else {
-      fetch_compact<NT>(ctiles, creg);
-      store_compact<NT>(creg, tiles[0]);
-    }
-  }
+  // ---- prologue: tiles 0 and 1 into the ring, S of tile 0 (both groups)
+  if (nt > 0) dma_tile<8>(imgs, lds);
+  if (nt > 1) dma_tile<8>(imgs + kImgBytes, lds + kImgBytes);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
+  if (nt > 0) qk_tile(lds, qf, l32, hf, s0, s1);
+  f16x8_t pf[4];
 
-  for (int tt = 0; tt < ntiles; ++tt) {
-    const Tile& T = tiles[tt & 1];
-    const bool more = tt + 1 < ntiles;
-    if (more) {
-      if (BASE) fetch_base<NT>(recs, c.base_rb, c.S, (tt + 1) * kBN, breg);
-      else fetch_compact<NT>(ctiles + (long long)(tt + 1) * kTileBytes, creg);
+  for (int p = 0; p <= 2 * nt; ++p) {
+    // tile k+2 goes into the slot tile k-1 left, two phases before first use
+    if (p & 1) {
+      const int k = (p >> 1) + 2;
+      if (k < nt) dma_tile<8>(imgs + (long long)k * kImgBytes, lds + (k % kRing) * kImgBytes);
     }
-    // ---- S^T = K Q^T for the 64 columns of the tile
-    f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8_t k0 = *(const bf16x8_t*)&T.k[l32 * kKP + ks * 16 + hf * 8];
-      const bf16x8_t k1 = *(const bf16x8_t*)&T.k[(32 + l32) * kKP + ks * 16 + hf * 8];
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
-    }
-    // ---- softmax of the lane's row over the tile's columns
-    float x[32];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      x[v] = s0[v];
-      x[16 + v] = s1[v];
-    }
-    if (T.pos[kBN - 1] > blk_min || ipos < 0) {
-#pragma unroll
-      for (int v = 0; v < 32; ++v) {
-        const int col = (v >> 4) * 32 + 8 * ((v & 15) >> 2) + 4 * hf + (v & 3);
-        if (T.pos[col] > ipos) x[v] = -INFINITY;
+    const int q = p - grp;
+    if (q >= 0 && q < 2 * nt) {
+      const int t = q >> 1;
+      const uint8_t* T = lds + (t % kRing) * kImgBytes;
+      if ((q & 1) == 0) {
+#ifdef FLV_NO_SOFTMAX
+        if (t == 0) softmax_tile<MODE>(T, s0, s1, ipos, blk_min, hf, m.c2, mref, lsum, o, pf);
+#else
+        softmax_tile<MODE>(T, s0, s1, ipos, blk_min, hf, m.c2, mref, lsum, o, pf);
+#endif
+      } else {
+        if (t + 1 < nt) qk_tile(lds + ((t + 1) % kRing) * kImgBytes, qf, l32, hf, s0, s1);
+        pv_tile(T, pf, l32, hf, o);
       }
     }
-    if (MODE == kModeAttn) {
-      float mt = x[0];
-#pragma unroll
-      for (int v = 1; v < 32; ++v) mt = fmaxf(mt, x[v]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * m.c2;
-      // rescale only when the row max outgrows the reference by 2^8 (or the
-      // reference is unset); otherwise P stays below 2^8 and fp16 holds it
-      const bool need = mt > mref + kRescale;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float mn = need ? mt : mref;
-        const float alpha = need ? __builtin_amdgcn_exp2f(mref - mn) : 1.0f;
-        mref = mn;
-        lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[db] *= alpha;
-      }
-    }
-    const float base = (MODE == kModeAttn && mref == -INFINITY) ? 0.0f : mref;
-    f16x8_t pf[4];
-    float ls = 0.0f;
-#pragma unroll
-    for (int k2 = 0; k2 < 4; ++k2) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[k2 * 8 + e], m.c2, -base));
-        ls += p;
-        pf[k2][e] = (_Float16)p;
-      }
-    }
-    lsum += ls;
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int k2 = 0; k2 < 4; ++k2) {
-      const int c0 = k2 * 16 + hf * 4;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const _Float16* vp = &T.vt[(db * 32 + l32) * kVP + c0];
-        const f16x4_t lo4 = *(const f16x4_t*)vp;
-        const f16x4_t hi4 = *(const f16x4_t*)(vp + 8);
-        const f16x8_t vf = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[k2], o[db], 0, 0, 0);
-      }
-    }
-    if (more) {
-      if (BASE) store_base<NT>(c.S, (tt + 1) * kBN, breg, tiles[(tt + 1) & 1]);
-      else store_compact<NT>(creg, tiles[(tt + 1) & 1]);
-    }
-    __syncthreads();
+    if (!(p & 1)) __builtin_amdgcn_s_waitcnt(0);  // this wave's tile loads are in LDS
+    phase_barrier();
   }
 
   // ---- epilogue: each lane writes 64 of its row's 128 dims
@@ -466,47 +468,6 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(MfmaArgs m) {
       }
     }
     if (hf == 0) a.M[bhS + i] = Mu * lt;
-  }
-}
-
-// ------------------------------------------------------------- gather
-// Compact tiles of the selected columns' reconstructions at loop `rc`:
-// K~ (bf16, row-major) and V~ (bf16 value stored as fp16, transposed).
-// One thread per (column, 32-dim group, K|V).
-__global__ __launch_bounds__(256) void k_gather_cols(CacheGeo c, int rc, const int32_t* __restrict__ sel, int K,
-                                                     int ntiles, uint8_t* __restrict__ out) {
-  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const int per_bh = ntiles * kBN * 8;
-  if (gid >= (long long)c.B * c.H * per_bh) return;
-  const int bh = (int)(gid / per_bh);
-  const int rem = (int)(gid - (long long)bh * per_bh);
-  const int colg = rem >> 3;  // column slot in [0, ntiles*64)
-  const int sub = rem & 7;
-  const int kv = sub >> 2, g = sub & 3;
-  const int b = bh / c.H, h = bh - b * c.H;
-  const int tile = colg / kBN, col = colg - tile * kBN;
-  uint8_t* tp = out + ((long long)bh * ntiles + tile) * kTileBytes;
-  const int j = colg < K ? (sel ? sel[(long long)bh * K + colg] : colg) : -1;  // sel NULL: every position
-  if (sub == 0) ((int*)(tp + kTileKBytes + kTileVBytes))[col] = j >= 0 ? j : kNoPos;
-  float x[32];
-  if (j >= 0) {
-#pragma unroll 4
-    for (int e = 0; e < 32; ++e) x[e] = chain_elem(c, rc, 0, b, h, j, kv, g * 32 + e);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 32; ++e) x[e] = 0.0f;
-  }
-  if (kv == 0) {
-    uint32_t w[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) w[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
-    uint4* dst = (uint4*)(tp + (col * kD + g * 32) * 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
-  } else {
-    _Float16* vt = (_Float16*)(tp + kTileKBytes);
-#pragma unroll
-    for (int e = 0; e < 32; ++e) vt[(g * 32 + e) * kBN + col] = bf16_as_f16(x[e]);
   }
 }
 
@@ -641,9 +602,9 @@ __global__ __launch_bounds__(kThreads) void k_mass_mfma(MassArgs m) {
   } else {
     const int tile = cidx / kBN, col = cidx - tile * kBN;
     if (cidx < m.K_prev) {
-      const uint8_t* tp = m.tiles + ((long long)bh * m.ntiles_total + tile) * kTileBytes;
-      jpos = ((const int*)(tp + kTileKBytes + kTileVBytes))[col];
-      const bf16x8_t* kr = (const bf16x8_t*)(tp + col * kD * 2);
+      const uint8_t* tp = m.tiles + ((long long)bh * m.ntiles_total + tile) * kImgBytes;
+      jpos = ((const int*)(tp + kImgPos))[col];
+      const bf16x8_t* kr = (const bf16x8_t*)(tp + col * kKP * 2);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) kf[ks] = kr[ks * 2 + hf];
     } else {
@@ -660,8 +621,8 @@ __global__ __launch_bounds__(kThreads) void k_mass_mfma(MassArgs m) {
     } else {
       const int ci = cb * 128;
       const int tile = ci / kBN;
-      const uint8_t* tp = m.tiles + ((long long)bh * m.ntiles_total + tile) * kTileBytes;
-      jmin = ((const int*)(tp + kTileKBytes + kTileVBytes))[ci - tile * kBN];
+      const uint8_t* tp = m.tiles + ((long long)bh * m.ntiles_total + tile) * kImgBytes;
+      jmin = ((const int*)(tp + kImgPos))[ci - tile * kBN];
     }
     const int32_t* rows = c.rows[a.r] + (long long)b * nr;
     int lo = 0, hi = nr;
@@ -726,52 +687,51 @@ __global__ __launch_bounds__(kThreads) void k_mass_mfma(MassArgs m) {
 // ------------------------------------------------------------- host side
 size_t gather_bytes(const CacheGeo& c, int K) {
   const int nt = (K + kBN - 1) / kBN;
-  return (size_t)c.B * c.H * nt * kTileBytes;
+  return (size_t)c.B * c.H * nt * kImgBytes;
 }
 
+// Tile images of K columns (sel NULL: positions 0..K-1) at loop rc.
 hipError_t launch_gather(const CacheGeo& c, int rc, const int32_t* sel, int K, uint8_t* out, hipStream_t st) {
   const int nt = (K + kBN - 1) / kBN;
-  const long long threads = (long long)c.B * c.H * nt * kBN * 8;
-  hipLaunchKernelGGL(k_gather_cols, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, c, rc, sel, K, nt,
-                     out);
+  hipLaunchKernelGGL(k_build_tiles, dim3((unsigned)(c.B * c.H * nt)), dim3(256), 0, st, c, rc, sel, K, nt, out);
   return hipGetLastError();
 }
 
-template <int NW, int MODE, bool BASE>
+template <int MODE>
 static hipError_t launch_one(const MfmaArgs& m, hipStream_t st) {
+  constexpr size_t lds = (size_t)kRing * kImgBytes;
+  static bool attr = false;  // the attribute is per kernel; setting it twice is harmless
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_attn_mfma<MODE>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
   const int nunits = m.a.c.B * m.a.c.H * m.nblk;
-  hipLaunchKernelGGL((k_attn_mfma<NW, MODE, BASE>), dim3(nunits), dim3(64 * NW), 0, st, m);
+  hipLaunchKernelGGL((k_attn_mfma<MODE>), dim3(nunits), dim3(512), lds, st, m);
   return hipGetLastError();
 }
 
 static float c2_of(int d) { return (float)(1.4426950408889634 / __builtin_sqrt((double)d)); }
 
-// Sparse-row launch: 8-wave blocks when they still fill the chip twice.
 template <int MODE>
 static hipError_t launch_rows(MfmaArgs& m, int n, hipStream_t st) {
-  if ((long long)m.a.c.B * m.a.c.H * ((n + 255) / 256) >= 512) {
-    m.nblk = (n + 255) / 256;
-    return launch_one<8, MODE, false>(m, st);
-  }
-  m.nblk = (n + 127) / 128;
-  return launch_one<4, MODE, false>(m, st);
+  m.nblk = (n + 255) / 256;
+  return launch_one<MODE>(m, st);
 }
 
-// Loop-r attention: r == 1 dense over the base; r >= 2 over gathered tiles
-// (ws: gather_bytes(c, K) bytes).
+// Loop-r attention: r == 1 dense over every position, r >= 2 over S_r.
+// ws: gather_bytes(c, K) bytes (K = S at r == 1).
 hipError_t launch_attn_mfma(const AttnArgs& a, uint8_t* ws, hipStream_t st) {
   MfmaArgs m{};
   m.a = a;
   m.c2 = c2_of(a.c.d);
-  if (a.r == 1) {
-    m.nblk = (a.c.S + 255) / 256;
-    return launch_one<8, kModeAttn, true>(m, st);
-  }
-  hipError_t e = launch_gather(a.c, a.r, a.sel, a.K, ws, st);
+  const int K = a.r == 1 ? a.c.S : a.K;
+  hipError_t e = launch_gather(a.c, a.r, a.r == 1 ? nullptr : a.sel, K, ws, st);
   if (e != hipSuccess) return e;
   m.tiles = ws;
-  m.ntiles_total = (a.K + kBN - 1) / kBN;
-  return launch_rows<kModeAttn>(m, a.c.n[a.r], st);
+  m.ntiles_total = (K + kBN - 1) / kBN;
+  return launch_rows<kModeAttn>(m, a.r == 1 ? a.c.S : a.c.n[a.r], st);
 }
 
 // Cached mass and reused part of loop r over S_r = a.sel (chain r-1).

@@ -60,7 +60,7 @@ def run_prefill(cfg, rows, slices, *, mass_in=None, K_budget=None, mfma=None):
             fl.fl_colsel(cache.fl, r, qs[r - 2], dt, st.fl, K_prev, sel_prev, K, mi, mass, sel, ws, nws)
             out["sel"].append(sel.cpu().numpy())
             out["mass"].append(mass.cpu().numpy())
-        nws = fl.fl_workspace_bytes(fl.FL_WS_ATTN, cache.fl, r, K, K) if r >= 2 else 0
+        nws = fl.fl_workspace_bytes(fl.FL_WS_ATTN, cache.fl, r, K, K)
         ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=DEV)
         fl.fl_loop_attn(cache.fl, r, qs[r - 1], dt, K, sel, st.fl, ws, nws)
         torch.cuda.synchronize()
