@@ -174,22 +174,6 @@ __device__ inline void dma_tile(const uint8_t* img, uint8_t* lds) {
 // S^T = K Q^T for one tile: the lane's row against the tile's 64 columns.
 __device__ inline void qk_tile(const uint8_t* T, const bf16x8_t* qf, int l32, int hf, f32x16_t& s0, f32x16_t& s1) {
   const __bf16* kt = (const __bf16*)T;
-#ifdef FLV_QK4
-  f32x16_t a0 = f32x16_t{}, a1 = f32x16_t{}, b0 = f32x16_t{}, b1 = f32x16_t{};
-#pragma unroll
-  for (int ks = 0; ks < 8; ks += 2) {
-    const bf16x8_t k0 = *(const bf16x8_t*)&kt[l32 * kKP + ks * 16 + hf * 8];
-    const bf16x8_t k1 = *(const bf16x8_t*)&kt[(32 + l32) * kKP + ks * 16 + hf * 8];
-    const bf16x8_t k2 = *(const bf16x8_t*)&kt[l32 * kKP + ks * 16 + 16 + hf * 8];
-    const bf16x8_t k3 = *(const bf16x8_t*)&kt[(32 + l32) * kKP + ks * 16 + 16 + hf * 8];
-    a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], a0, 0, 0, 0);
-    a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], a1, 0, 0, 0);
-    b0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k2, qf[ks + 1], b0, 0, 0, 0);
-    b1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k3, qf[ks + 1], b1, 0, 0, 0);
-  }
-  s0 = a0 + b0;
-  s1 = a1 + b1;
-#else
   s0 = f32x16_t{};
   s1 = f32x16_t{};
 #pragma unroll
@@ -199,17 +183,15 @@ __device__ inline void qk_tile(const uint8_t* T, const bf16x8_t* qf, int l32, in
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
   }
-#endif
 }
 
-// Softmax step of one tile for the lane's row ("ALU phase"): causal mask,
-// running max with lazy rescale (ATTN) or fixed loop r-1 statistics (UM),
-// P = 2^(x*c2 - base) rounded to fp16, partial row sum.
+// Softmax of one tile for the lane's row, first part: causal mask, running
+// max with lazy rescale (ATTN) or fixed loop r-1 statistics (UM).  Leaves the
+// masked scores in x and returns the exponent base.
 template <int MODE>
-__device__ inline void softmax_tile(const uint8_t* T, f32x16_t s0, f32x16_t s1, int ipos, int blk_min, int hf, float c2,
-                                    float& mref, float& lsum, f32x16_t* o, f16x8_t* pf) {
+__device__ inline float softmax_stats(const uint8_t* T, f32x16_t s0, f32x16_t s1, int ipos, int blk_min, int hf,
+                                      float c2, float& mref, float& lsum, f32x16_t* o, float* x) {
   const int* tpos = (const int*)(T + kImgPos);
-  float x[32];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     x[v] = s0[v];
@@ -239,7 +221,11 @@ __device__ inline void softmax_tile(const uint8_t* T, f32x16_t s0, f32x16_t s1, 
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
     }
   }
-  const float base = (MODE == kModeAttn && mref == -INFINITY) ? 0.0f : mref;
+  return (MODE == kModeAttn && mref == -INFINITY) ? 0.0f : mref;
+}
+
+// Second part: P = 2^(x*c2 - base) rounded to fp16 and the partial row sum.
+__device__ inline void softmax_probs(const float* x, float base, float c2, float& lsum, f16x8_t* pf) {
   float ls = 0.0f;
 #pragma unroll
   for (int k2 = 0; k2 < 4; ++k2) {
@@ -270,29 +256,20 @@ __device__ inline void pv_tile(const uint8_t* T, const f16x8_t* pf, int l32, int
   }
 }
 
-__device__ inline void phase_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// 8 waves of 32 query rows (BM = 256) in two groups of four.  Wave w and
-// wave w+4 share a SIMD; group 1 runs one phase behind group 0, so while one
-// group multiplies on the matrix cores (GEMM phase: S of tile t+1 and
-// O += P V of tile t) the other forms the probabilities of its tile on the
-// vector ALUs (ALU phase).  Block barriers separate the phases; tile images
-// arrive by direct global->LDS loads issued two phases before first use, so
-// the loop itself writes no LDS.
-template <int MODE>
-__global__ __launch_bounds__(512) void k_attn_mfma(MfmaArgs m) {
-  constexpr int BM = 256;
+// NW waves of 32 query rows each (BM = 32 * NW).  Per 64-column tile: the
+// next tile's S^T = K Q^T is issued on the matrix cores while this tile's
+// probabilities are formed on the vector ALUs, then O^T += V^T P^T.  Tile
+// images arrive by direct global->LDS loads issued two tiles ahead into a
+// three-deep ring, so the loop itself writes no LDS.
+template <int NW, int MODE>
+__global__ __launch_bounds__(64 * NW) void k_attn_mfma(MfmaArgs m) {
+  constexpr int BM = 32 * NW;
   extern __shared__ __align__(16) uint8_t lds[];   // kRing tile images
   __shared__ int sh_ntiles;
   const AttnArgs& a = m.a;
   const CacheGeo& c = a.c;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  const int grp = wv >> 2;        // phase group
   const int hf = lane >> 5;       // half of the wave
   const int l32 = lane & 31;
 
@@ -376,38 +353,37 @@ __global__ __launch_bounds__(512) void k_attn_mfma(MfmaArgs m) {
   __syncthreads();
   const int nt = sh_ntiles;
 
-  // ---- prologue: tiles 0 and 1 into the ring, S of tile 0 (both groups)
-  if (nt > 0) dma_tile<8>(imgs, lds);
-  if (nt > 1) dma_tile<8>(imgs + kImgBytes, lds + kImgBytes);
+  // ---- prologue: tiles 0 and 1 into the ring, S of tile 0
+  if (nt > 0) dma_tile<NW>(imgs, lds);
+  if (nt > 1) dma_tile<NW>(imgs + kImgBytes, lds + kImgBytes);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
   if (nt > 0) qk_tile(lds, qf, l32, hf, s0, s1);
-  f16x8_t pf[4];
 
-  for (int p = 0; p <= 2 * nt; ++p) {
-    // tile k+2 goes into the slot tile k-1 left, two phases before first use
-    if (p & 1) {
-      const int k = (p >> 1) + 2;
-      if (k < nt) dma_tile<8>(imgs + (long long)k * kImgBytes, lds + (k % kRing) * kImgBytes);
+  for (int tt = 0; tt < nt; ++tt) {
+    const uint8_t* T = lds + (tt % kRing) * kImgBytes;
+    const uint8_t* Tn = lds + ((tt + 1) % kRing) * kImgBytes;
+    // tile tt+2 goes into the slot tile tt-1 left (all waves passed it)
+    if (tt + 2 < nt) dma_tile<NW>(imgs + (long long)(tt + 2) * kImgBytes, lds + ((tt + 2) % kRing) * kImgBytes);
+    float x[32];
+    const float base = softmax_stats<MODE>(T, s0, s1, ipos, blk_min, hf, m.c2, mref, lsum, o, x);
+    // S of the next tile on the matrix cores while these probabilities
+    // are formed on the vector ALUs (stale data past the last tile: unused)
+    f32x16_t n0, n1;
+    qk_tile(Tn, qf, l32, hf, n0, n1);
+    f16x8_t pf[4];
+    softmax_probs(x, base, m.c2, lsum, pf);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // five VALU
     }
-    const int q = p - grp;
-    if (q >= 0 && q < 2 * nt) {
-      const int t = q >> 1;
-      const uint8_t* T = lds + (t % kRing) * kImgBytes;
-      if ((q & 1) == 0) {
-#ifdef FLV_NO_SOFTMAX
-        if (t == 0) softmax_tile<MODE>(T, s0, s1, ipos, blk_min, hf, m.c2, mref, lsum, o, pf);
-#else
-        softmax_tile<MODE>(T, s0, s1, ipos, blk_min, hf, m.c2, mref, lsum, o, pf);
-#endif
-      } else {
-        if (t + 1 < nt) qk_tile(lds + ((t + 1) % kRing) * kImgBytes, qf, l32, hf, s0, s1);
-        pv_tile(T, pf, l32, hf, o);
-      }
-    }
-    if (!(p & 1)) __builtin_amdgcn_s_waitcnt(0);  // this wave's tile loads are in LDS
-    phase_barrier();
+    pv_tile(T, pf, l32, hf, o);
+    s0 = n0;
+    s1 = n1;
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of tile tt+2 are in LDS
+    __syncthreads();
   }
 
   // ---- epilogue: each lane writes 64 of its row's 128 dims
@@ -697,27 +673,32 @@ hipError_t launch_gather(const CacheGeo& c, int rc, const int32_t* sel, int K, u
   return hipGetLastError();
 }
 
-template <int MODE>
+template <int NW, int MODE>
 static hipError_t launch_one(const MfmaArgs& m, hipStream_t st) {
   constexpr size_t lds = (size_t)kRing * kImgBytes;
   static bool attr = false;  // the attribute is per kernel; setting it twice is harmless
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_attn_mfma<MODE>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
+    hipError_t e = hipFuncSetAttribute((const void*)k_attn_mfma<NW, MODE>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr = true;
   }
   const int nunits = m.a.c.B * m.a.c.H * m.nblk;
-  hipLaunchKernelGGL((k_attn_mfma<MODE>), dim3(nunits), dim3(512), lds, st, m);
+  hipLaunchKernelGGL((k_attn_mfma<NW, MODE>), dim3(nunits), dim3(64 * NW), lds, st, m);
   return hipGetLastError();
 }
 
 static float c2_of(int d) { return (float)(1.4426950408889634 / __builtin_sqrt((double)d)); }
 
+// Row blocks of 256 when they still fill the chip twice, else 128.
 template <int MODE>
 static hipError_t launch_rows(MfmaArgs& m, int n, hipStream_t st) {
-  m.nblk = (n + 255) / 256;
-  return launch_one<MODE>(m, st);
+  if ((long long)m.a.c.B * m.a.c.H * ((n + 255) / 256) >= 512) {
+    m.nblk = (n + 255) / 256;
+    return launch_one<8, MODE>(m, st);
+  }
+  m.nblk = (n + 127) / 128;
+  return launch_one<4, MODE>(m, st);
 }
 
 // Loop-r attention: r == 1 dense over every position, r >= 2 over S_r.
