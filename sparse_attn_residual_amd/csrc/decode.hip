@@ -116,62 +116,120 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_dense(DecodeArgs a, floa
   }
 }
 
-// x_hat^(r) of the 16 dims [sub*16, sub*16+16) of K (kv = 0) or V (kv = 1) of
-// token j, and optionally x_hat^(r-1) of the same dims.
-__device__ inline void chain16(const CacheGeo& c, int r, int l, int b, int h, int j, int kv, int sub, float* x,
-                               float* xprev) {
-  const int d = 128, G = d / kGroup;
+constexpr int kMaxFastLoops = 5;  // loops whose slot lookups are issued together
+
+// The 16 dims [sub*16, sub*16+16) of K and V of token j reconstructed at
+// loop r (and V at loop r-1 when vprev is set): the base plus the residuals
+// of loops 2..r in which j was active.  Every slot lookup and record load of
+// the token is issued before any of them is used.
+template <bool PREV>
+__device__ inline void token16(const CacheGeo& c, int r, int l, int b, int h, int j, int sub, float* kx, float* vx,
+                               float* vprev) {
+  constexpr int d = 128, G = 4;
   const uint8_t* rec = base_rec(c, l, b, h, j);
-  const uint4 w = *(const uint4*)(rec + kv * d + sub * 16);
-  const float s = h2f(((const uint16_t*)(rec + 2 * d))[kv * G + (sub >> 1)]);
-  unpack_i8x16(w, x);
+  const uint4 kw = *(const uint4*)(rec + sub * 16);
+  const uint4 vw = *(const uint4*)(rec + d + sub * 16);
+  const uint16_t* sc = (const uint16_t*)(rec + 2 * d);
+  const uint16_t ksh = sc[sub >> 1], vsh = sc[G + (sub >> 1)];
+  int slot[kMaxFastLoops - 1];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) x[e] = x[e] * s;
-  for (int rr = 2; rr <= r; ++rr) {
-    const int t = c.slot[rr][(long long)b * c.S + j];
-    if (t < 0) break;
-    if (rr == r && xprev) {
+  for (int k = 0; k < kMaxFastLoops - 1; ++k) slot[k] = (k + 2 <= r) ? c.slot[k + 2][(long long)b * c.S + j] : -1;
+  uint2 kr[kMaxFastLoops - 1], vr[kMaxFastLoops - 1];
+  uint32_t meta[kMaxFastLoops - 1][2];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) xprev[e] = x[e];
+  for (int k = 0; k < kMaxFastLoops - 1; ++k) {
+    kr[k] = vr[k] = make_uint2(0, 0);
+    meta[k][0] = meta[k][1] = 0;
+    if (slot[k] >= 0) {
+      const int rr = k + 2, bits = c.bits[rr], C = d * bits / 8;
+      const uint8_t* rrec = res_rec(c, rr, l, b, h, slot[k]);
+      if (bits == 4) {
+        kr[k] = *(const uint2*)(rrec + sub * 8);
+        vr[k] = *(const uint2*)(rrec + C + sub * 8);
+      } else {
+        kr[k].x = *(const uint32_t*)(rrec + sub * 4);
+        vr[k].x = *(const uint32_t*)(rrec + C + sub * 4);
+      }
+      const uint16_t* mt = (const uint16_t*)(rrec + 2 * C);
+      const int g = sub >> 1;
+      meta[k][0] = (uint32_t)mt[g] | ((uint32_t)mt[G + g] << 16);          // K scale, zero
+      meta[k][1] = (uint32_t)mt[2 * G + g] | ((uint32_t)mt[3 * G + g] << 16);  // V scale, zero
     }
-    const uint8_t* rrec = res_rec(c, rr, l, b, h, t);
-    const int bits = c.bits[rr];
-    const int C = d * bits / 8;
-    const uint16_t* meta = (const uint16_t*)(rrec + 2 * C);
-    const float rs = h2f(meta[(2 * kv) * G + (sub >> 1)]);
-    const float rz = h2f(meta[(2 * kv + 1) * G + (sub >> 1)]);
+  }
+  {
+    const float ks = h2f(ksh), vs = h2f(vsh);
+    const uint32_t kws[4] = {kw.x, kw.y, kw.z, kw.w}, vws[4] = {vw.x, vw.y, vw.z, vw.w};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      kx[e] = (float)(int8_t)(kws[e >> 2] >> (8 * (e & 3))) * ks;
+      vx[e] = (float)(int8_t)(vws[e >> 2] >> (8 * (e & 3))) * vs;
+    }
+  }
+  if (PREV) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) vprev[e] = vx[e];
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxFastLoops - 1; ++k) {
+    if (slot[k] < 0) continue;
+    const int bits = c.bits[k + 2];
+    const float krs = h2f((uint16_t)meta[k][0]), krz = h2f((uint16_t)(meta[k][0] >> 16));
+    const float vrs = h2f((uint16_t)meta[k][1]), vrz = h2f((uint16_t)(meta[k][1] >> 16));
+    if (PREV && k + 2 == r) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) vprev[e] = vx[e];
+    }
     if (bits == 4) {
-      const uint2 pw = *(const uint2*)(rrec + kv * C + sub * 8);
-      const uint32_t ws[2] = {pw.x, pw.y};
+      const uint32_t kq[2] = {kr[k].x, kr[k].y}, vq[2] = {vr[k].x, vr[k].y};
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int code = (ws[e >> 3] >> (4 * (e & 7))) & 15;
-        x[e] = x[e] + __builtin_fmaf((float)code, rs, rz);
+        kx[e] = kx[e] + __builtin_fmaf((float)((kq[e >> 3] >> (4 * (e & 7))) & 15), krs, krz);
+        vx[e] = vx[e] + __builtin_fmaf((float)((vq[e >> 3] >> (4 * (e & 7))) & 15), vrs, vrz);
       }
     } else {
-      const uint32_t pw = *(const uint32_t*)(rrec + kv * C + sub * 4);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int code = (pw >> (2 * e)) & 3;
-        x[e] = x[e] + __builtin_fmaf((float)code, rs, rz);
+        kx[e] = kx[e] + __builtin_fmaf((float)((kr[k].x >> (2 * e)) & 3), krs, krz);
+        vx[e] = vx[e] + __builtin_fmaf((float)((vr[k].x >> (2 * e)) & 3), vrs, vrz);
       }
     }
   }
-  if (xprev) {
-    // when the chain stopped before loop r, x_hat^(r-1) == x_hat^(r)
-    const int tr = r >= 2 ? c.slot[r][(long long)b * c.S + j] : -1;
-    if (tr < 0) {
+  // loops beyond the batched range, one lookup at a time
+  bool active_r = r >= 2 && r <= kMaxFastLoops && slot[r - 2] >= 0;
+  for (int rr = kMaxFastLoops + 1; rr <= r && slot[kMaxFastLoops - 2] >= 0; ++rr) {
+    const int t = c.slot[rr][(long long)b * c.S + j];
+    if (t < 0) break;
+    if (PREV && rr == r) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) xprev[e] = x[e];
+      for (int e = 0; e < 16; ++e) vprev[e] = vx[e];
+      active_r = true;
     }
+    const int bits = c.bits[rr], C = d * bits / 8, g = sub >> 1;
+    const uint8_t* rrec = res_rec(c, rr, l, b, h, t);
+    const uint16_t* mt = (const uint16_t*)(rrec + 2 * C);
+    const float krs = h2f(mt[g]), krz = h2f(mt[G + g]), vrs = h2f(mt[2 * G + g]), vrz = h2f(mt[3 * G + g]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int kc = bits == 4 ? (rrec[sub * 8 + (e >> 1)] >> (4 * (e & 1))) & 15
+                               : (rrec[sub * 4 + (e >> 2)] >> (2 * (e & 3))) & 3;
+      const int vc = bits == 4 ? (rrec[C + sub * 8 + (e >> 1)] >> (4 * (e & 1))) & 15
+                               : (rrec[C + sub * 4 + (e >> 2)] >> (2 * (e & 3))) & 3;
+      kx[e] = kx[e] + __builtin_fmaf((float)kc, krs, krz);
+      vx[e] = vx[e] + __builtin_fmaf((float)vc, vrs, vrz);
+    }
+  }
+  // a token inactive at loop r has x_hat^(r-1) == x_hat^(r)
+  if (PREV && !active_r) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) vprev[e] = vx[e];
   }
 }
 
 // Loop r >= 2 over the K selected tokens (sel/logits compacted at the front).
-template <typename T>
-__global__ __launch_bounds__(kDecThreads) void k_decode_sparse(DecodeArgs a, float tau, int pruned) {
+template <typename T, bool PRUNED>
+__global__ __launch_bounds__(kDecThreads) void k_decode_sparse(DecodeArgs a, float tau) {
   __shared__ GroupState gs;
-  __shared__ float csum[kDecGroups][128];
+  __shared__ float csum[PRUNED ? kDecGroups : 1][128];
   __shared__ float psum[kDecGroups];
   const CacheGeo& c = a.c;
   const long long lbh = blockIdx.x;
@@ -196,20 +254,20 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_sparse(DecodeArgs a, flo
   float* logit = a.logits + lbh * c.S;
   for (int t = gid; t < a.K; t += kDecGroups) {
     const int j = sel[t];
+    const float old = PRUNED ? logit[t] : 0.0f;
     float kx[16], vx[16], vp[16];
-    chain16(c, r, l, b, h, j, 0, sub, kx, nullptr);
-    chain16(c, r, l, b, h, j, 1, sub, vx, pruned ? vp : nullptr);
-    if (pruned) {
-      const float pj = Mprev * __expf(logit[t] - lprev);
-      P += pj;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) C[e] = __builtin_fmaf(pj, vp[e], C[e]);
-    }
+    token16<PRUNED>(c, r, l, b, h, j, sub, kx, vx, vp);
     float part = 0.0f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) part = __builtin_fmaf(q[e], kx[e], part);
     const float s = tau * group8_sum(part);
-    if (sub == 0) logit[t] = s;  // every lane of the group has read logit[t] above
+    if (sub == 0) logit[t] = s;  // every lane of the group read the old logit above
+    if (PRUNED) {
+      const float pj = Mprev * __expf(old - lprev);
+      P += pj;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) C[e] = __builtin_fmaf(pj, vp[e], C[e]);
+    }
     const float mn = fmaxf(m, s);
     const float alpha = __expf(m - mn);
     const float p = __expf(s - mn);
@@ -226,12 +284,12 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_sparse(DecodeArgs a, flo
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     gs.acc[gid][sub * 16 + e] = acc[e];
-    csum[gid][sub * 16 + e] = C[e];
+    if (PRUNED) csum[gid][sub * 16 + e] = C[e];
   }
   __syncthreads();
   if (threadIdx.x < d) {
     float Mr = Mprev, Ud = a.U[lbh * d + threadIdx.x];
-    if (pruned) {
+    if (PRUNED) {
       float ps = 0.0f, cs = 0.0f;
       for (int g = 0; g < kDecGroups; ++g) {
         ps += psum[g];
@@ -278,8 +336,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
     e = launch_copy_sel(nullptr, (int)P, a.c.S, a.sel, st);
     if (e != hipSuccess) return e;
   }
-  if (bf) hipLaunchKernelGGL(k_decode_sparse<uint16_t>, dim3((unsigned)P), dim3(kDecThreads), 0, st, a, tau, pruned);
-  else hipLaunchKernelGGL(k_decode_sparse<float>, dim3((unsigned)P), dim3(kDecThreads), 0, st, a, tau, pruned);
+  if (pruned) {
+    if (bf) hipLaunchKernelGGL((k_decode_sparse<uint16_t, true>), dim3((unsigned)P), dim3(kDecThreads), 0, st, a, tau);
+    else hipLaunchKernelGGL((k_decode_sparse<float, true>), dim3((unsigned)P), dim3(kDecThreads), 0, st, a, tau);
+  } else {
+    if (bf) hipLaunchKernelGGL((k_decode_sparse<uint16_t, false>), dim3((unsigned)P), dim3(kDecThreads), 0, st, a, tau);
+    else hipLaunchKernelGGL((k_decode_sparse<float, false>), dim3((unsigned)P), dim3(kDecThreads), 0, st, a, tau);
+  }
   return hipGetLastError();
 }
 
