@@ -222,16 +222,26 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only copy 1 GiB device to device three times (scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: the hot path shards by heads and sequences with no exchange, and this "
               f"build measures one GPU's share (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calib_copy:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_read": 1 << 30, "calib_copy_bytes_written": 1 << 30, "copies": 3}))
+        return
     import sparse_attn_residual_amd as fl
     from sparse_attn_residual_amd import accounting as acc
     import workloads
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
 
     pf = prefill_bench(args, torch, fl, workloads, acc)
     dec = None if args.no_decode else decode_bench(args, torch, fl, workloads, acc)

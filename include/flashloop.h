@@ -16,7 +16,7 @@
  *     - sparse loop-r attention: recompute the active rows (p1 §4.1, §D.1)
  *       only against the selected columns and rescale the softmax by their
  *       cached mass, reusing every other column's contribution (p1 §4.2;
- *       guide §3: the rank-K correction of the paper's eq. 3) -> fl_loop_attn
+ *       guide §3: a low-rank fix of the previous output, eq. 3) -> fl_loop_attn
  *     - the decode step over the packed streams, with the selection fused in
  *       (p1 App. G)                                -> fl_loop_decode
  *
@@ -73,7 +73,7 @@ typedef void* fl_stream;
 
 /*
  * The packed cross-loop KV cache of L layers (p1 §4.3 and §D.3; p1 App. G:
- * packed 4-bit storage, "anchor and residual KV streams").  Index r of every
+ * the engine keeps the base and the residuals as packed streams).  Index r of every
  * loop array is the loop number (index 0 is unused).
  *
  *   L, B, H, S, d, R   layers, sequences, heads, tokens, head dim (64 or 128),
@@ -181,9 +181,9 @@ fl_status fl_kv_resq(const fl_cache* cache, int r, const void* k, const void* v,
 
 /*
  * fl_colsel — loop-aware column selection for loop r >= 2 of one layer
- * (p1 §4.2: top-K key columns ranked using the preceding loop, and later
- * loops prune the selected set further; p1 §D.2: the selection caches key
- * indices and their global mass).
+ * (p1 §4.2: the previous loop's attention picks the top-K key columns, and a
+ * later loop may keep a subset of them; p1 §D.2: the chosen positions are
+ * kept together with their share of the full distribution).
  *   q_prev   [B][H][n_{r-1}][d] (dtype): loop r-1 queries in rows[r-1] order
  *   state    the fl_state left by loop r-1 (O, lse, M read; U, M written)
  *   cand     [B][H][K_prev] int32 ascending: S_{r-1}; NULL means every
@@ -208,8 +208,8 @@ fl_status fl_colsel(const fl_cache* cache, int r, const void* q_prev, fl_dtype d
 
 /*
  * fl_loop_attn — loop-r attention of one layer (prefill), over the packed
- * cache streams (p1 App. G: attention reads the packed anchor and residual
- * streams; p1 §4.4: selected tokens and keys are gathered into compact tiles).
+ * cache streams (p1 App. G: attention works from the packed streams; p1 §4.4:
+ * the chosen tokens and keys are gathered into dense tiles).
  *   r == 1: q [B][H][S][d]; dense causal attention of every row:
  *           O = softmax(tau q k~^T) v~, lse; sets M = 1 and U = 0.
  *   r >= 2: q [B][H][n_r][d] in rows[r] order; sel [B][H][K_r] = S_r from

@@ -2,15 +2,15 @@
 
 Follows the FlashLoop pages step by step, in float64:
   * loop 1 is dense causal attention of every row over the reconstructed
-    base (the workload definition: loop 1 is dense exact attention; p1 §D.1:
-    sparse loops come after dense early loops);
+    base (the workload definition; p1 §D.1 makes the first loops dense and
+    the later ones sparse);
   * loop r >= 2 recomputes only the active rows A_r (p1 §4.1, §D.1), only
     against the top-K key columns ranked by loop r-1's attention statistics
     (p1 §4.2 and §D.2; guide §3), and rescales the softmax over those columns
-    by their cached loop r-1 mass, reusing the contribution of every other
-    column from loop r-1's output (p1 §4.2: rescale by the cached
-    full-attention mass; guide §3: a rank-K correction of the previous output,
-    the paper's eq. 3, whose formula the pages do not print).
+    by the share of loop r-1's distribution those columns held, keeping every
+    other column's contribution from loop r-1's output (p1 §4.2; guide §3
+    describes the update as a low-rank fix of the previous output, the
+    paper's eq. 3, whose formula the pages do not print).
 
 Reading of the unprinted eq. 3 (the design doc lists every reading): with
 J_i = {j in S_r : j <= i} and P^(r-1) the probabilities that loop r-1 left,

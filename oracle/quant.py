@@ -1,10 +1,10 @@
 """Quantizers of the cross-loop KV cache (p1 §4.3 and §D.3; guide §3).
 
 The pages store a quantized loop-1 base and, for every later loop, quantized
-residuals of the active tokens against the *reconstructed* previous loop
-(p1 §4.3: residual updates relative to each preceding reconstructed loop;
-guide §3: the stored residual is X^(r) - X_hat^(r-1), active tokens only).
-Inactive tokens reuse their K/V state and store nothing (p1 §4.3).
+residuals of the active tokens taken against the *reconstructed* previous
+loop (p1 §4.3; guide §3 writes the stored residual as X^(r) - X_hat^(r-1),
+for active tokens only).  A token that is not active keeps its previous K/V
+and stores nothing (p1 §4.3).
 
 Storage format (the workload definitions fix it; the paper's own INT4/g64
 setting of p1 App. E is a different format): groups of 32 consecutive

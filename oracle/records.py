@@ -1,7 +1,7 @@
 """Byte layout of the packed cache records, written from its specification.
 
-The pages store "physically packed low-bit streams" that attention kernels read
-directly (p1 App. G: packed 4-bit KV storage; anchor and residual KV streams).
+The pages keep the cache as packed low-bit streams that the attention kernels
+read without first expanding them (p1 App. G).
 The record layout below is this implementation's own; the oracle writes and
 reads it from the specification only (it never calls the library's code).
 

@@ -5,8 +5,8 @@
 // first loop); loop r >= 2 recomputes the active rows only against the
 // selected columns and rescales by the cached mass (p1 §4.1, §4.2, §D.2;
 // guide §3); the cached mass M and reused part U come from loop r-1's
-// probabilities over the selected columns (p1 §D.2: cached key indices and
-// their global mass).
+// probabilities over the selected columns (p1 §D.2: the selection keeps the
+// chosen key positions together with their share of the full distribution).
 //
 // Design (gfx950, wave64):
 //  * a 256-thread block owns BM = 4 waves x 32*RB query rows; a wave keeps
@@ -22,8 +22,8 @@
 //    v~ converts to fp16 exactly;
 //  * every record a loop attends is dequantized once per loop by
 //    k_build_tiles into 64-column tile images laid out exactly like the LDS
-//    tiles (p1 §4.4: selected tokens and keys gathered into compact
-//    buffers); the attention kernel copies them into a three-deep LDS ring
+//    tiles (p1 §4.4: the engine gathers the chosen tokens and keys into
+//    dense buffers); the attention kernel copies them into a three-deep LDS ring
 //    with direct global->LDS loads and overlaps the QK^T of the next tile
 //    with the softmax of the current one.  Dequantizing inside the
 //    attention kernel instead would repeat the work for every row block and
@@ -108,8 +108,8 @@ __device__ inline void chain32(const CacheGeo& c, int rc, int b, int h, int j, i
 // One block of 256 threads per tile: columns sel[tile*64 .. +64) (sel NULL:
 // positions tile*64 ..), reconstructed at loop rc, staged in LDS in the image
 // layout and written out with 16-byte stores.  Every packed record a loop
-// attends is dequantized exactly once here (p1 §4.4: selected keys gathered
-// into compact buffers; p1 App. G: the packed streams are read directly).
+// attends is dequantized exactly once here (p1 §4.4: chosen keys gathered into
+// dense buffers; p1 App. G: attention works from the packed streams).
 __global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const int32_t* __restrict__ sel, int K,
                                                      int ntiles, uint8_t* __restrict__ out) {
   __shared__ __align__(16) uint8_t img[kImgBytes];

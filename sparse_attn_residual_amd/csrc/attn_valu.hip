@@ -9,7 +9,7 @@
 //   cached mass M and reused part U (p1 §4.2 and §D.2; guide §3, eq. 3),
 //   sparse loop-r update of the active rows (p1 §4.1, §4.2),
 //   column mass of the candidates over the rows loop r recomputes (p1 §4.2:
-//   columns ranked using the preceding loop's attention statistics).
+//   the previous loop's attention decides which columns matter).
 #include "launch.hpp"
 
 namespace fl {

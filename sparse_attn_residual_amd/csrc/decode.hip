@@ -1,7 +1,7 @@
 // fl_loop_decode kernels: one new token per (layer, sequence, head) attends
 // its whole cached context at every loop (guide §1 and Cell 1: decode is
-// bound by the bytes of the cache it reads; p1 App. G: attention reads the
-// packed anchor and residual streams directly, selection fused in).
+// bound by the bytes of the cache it reads; p1 App. G: attention works from
+// the packed base and residual streams, with the selection fused in).
 //
 // Work split: one 256-thread block per (layer, b, h).  Eight lanes share one
 // token record (16 dims each), so a wavefront streams eight consecutive
