@@ -58,6 +58,7 @@ constexpr int kRing = 3;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
@@ -171,6 +172,31 @@ __device__ inline void dma_tile(const uint8_t* img, uint8_t* lds) {
                                      0, 0);
 }
 
+// Workgroup barrier for the tile ring: the wave's LDS reads have returned
+// (lgkmcnt 0) and the compiler may not move memory operations across it, but
+// unlike __syncthreads it does not drain the wave's in-flight tile copies.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// the wave are outstanding (expcnt and lgkmcnt left unconstrained).
+constexpr int vm_wait_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// Wait until the wave's copies of every tile but the one issued last have
+// landed: the wave issued ceil or floor of kImgChunks / NW chunk loads for
+// that tile, and they may stay in flight.
+template <int NW>
+__device__ inline void wait_all_but_last_tile() {
+  constexpr int hi = (kImgChunks + NW - 1) / NW, lo = kImgChunks / NW;
+  const int wv = threadIdx.x >> 6;
+  if (wv < kImgChunks - lo * NW || hi == lo)
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(hi));
+  else
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(lo));
+}
+
 // S^T = K Q^T for one tile: the lane's row against the tile's 64 columns.
 __device__ inline void qk_tile(const uint8_t* T, const bf16x8_t* qf, int l32, int hf, f32x16_t& s0, f32x16_t& s1) {
   const __bf16* kt = (const __bf16*)T;
@@ -224,19 +250,28 @@ __device__ inline float softmax_stats(const uint8_t* T, f32x16_t s0, f32x16_t s1
   return (MODE == kModeAttn && mref == -INFINITY) ? 0.0f : mref;
 }
 
-// Second part: P = 2^(x*c2 - base) rounded to fp16 and the partial row sum.
+// Second part: P = 2^(x*c2 - base) rounded to fp16, and the partial row sum
+// of exactly those fp16 weights (pairs summed into fp32 by v_dot2 with 1s,
+// in two chains).
 __device__ inline void softmax_probs(const float* x, float base, float c2, float& lsum, f16x8_t* pf) {
-  float ls = 0.0f;
+  const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+  float ls0 = 0.0f, ls1 = 0.0f;
 #pragma unroll
   for (int k2 = 0; k2 < 4; ++k2) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[k2 * 8 + e], c2, -base));
-      ls += p;
-      pf[k2][e] = (_Float16)p;
+    for (int e = 0; e < 8; e += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[k2 * 8 + e], c2, -base));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[k2 * 8 + e + 1], c2, -base));
+      const f16x2_t h = {(_Float16)p0, (_Float16)p1};
+      pf[k2][e] = h[0];
+      pf[k2][e + 1] = h[1];
+      if (e & 2)
+        ls1 = __builtin_amdgcn_fdot2(h, one2, ls1, false);
+      else
+        ls0 = __builtin_amdgcn_fdot2(h, one2, ls0, false);
     }
   }
-  lsum += ls;
+  lsum += ls0 + ls1;
 }
 
 // O^T += V^T P^T for one tile ("GEMM phase", second half).
@@ -253,6 +288,71 @@ __device__ inline void pv_tile(const uint8_t* T, const f16x8_t* pf, int l32, int
       const f16x8_t vf = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[k2], o[db], 0, 0, 0);
     }
+  }
+}
+
+// Output of one row (64 of its 128 dims per lane): loop 1 writes O, U = 0,
+// M = 1 and lse; a sparse loop patches O = U + M * acc / l and lse (or
+// lse = -inf when no column was left); the cached-mass pass writes
+// U = O - M_prev * acc and M = M_prev * l.
+template <int MODE>
+__device__ inline void write_row(const AttnArgs& a, int r, long long bhS, int i, int hf, float mref, float lt,
+                                 const f32x16_t* o) {
+  if (i < 0) return;
+  const long long rowp = (bhS + i) * kD;
+  if (MODE == kModeAttn) {
+    if (r == 1) {
+      const float inv = 1.0f / lt;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int dcol = db * 32 + qq * 8 + hf * 4;
+          f32x4_t ov = {o[db][qq * 4] * inv, o[db][qq * 4 + 1] * inv, o[db][qq * 4 + 2] * inv,
+                        o[db][qq * 4 + 3] * inv};
+          *(f32x4_t*)&a.O[rowp + dcol] = ov;
+          *(f32x4_t*)&a.U[rowp + dcol] = f32x4_t{};
+        }
+      }
+      if (hf == 0) {
+        a.lse[bhS + i] = (mref + __log2f(lt)) * 0.6931471805599453f;
+        a.M[bhS + i] = 1.0f;
+      }
+    } else if (lt > 0.0f) {
+      const float Mi = a.M[bhS + i];
+      const float sc = Mi / lt;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int dcol = db * 32 + qq * 8 + hf * 4;
+          const f32x4_t uv = *(const f32x4_t*)&a.U[rowp + dcol];
+          f32x4_t ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = uv[e] + sc * o[db][qq * 4 + e];
+          *(f32x4_t*)&a.O[rowp + dcol] = ov;
+        }
+      }
+      if (hf == 0) a.lse[bhS + i] = (mref + __log2f(lt)) * 0.6931471805599453f;
+    } else if (hf == 0) {
+      a.lse[bhS + i] = -INFINITY;
+    }
+  } else {
+    const float Mp = a.M[bhS + i];
+    const float Mu = Mp > 0.0f ? Mp : 0.0f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int dcol = db * 32 + qq * 8 + hf * 4;
+        const f32x4_t ov = *(const f32x4_t*)&a.O[rowp + dcol];
+        f32x4_t uv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) uv[e] = ov[e] - Mu * o[db][qq * 4 + e];
+        *(f32x4_t*)&a.U[rowp + dcol] = uv;
+      }
+    }
+    if (hf == 0) a.M[bhS + i] = Mu * lt;
   }
 }
 
@@ -382,69 +482,17 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(MfmaArgs m) {
     pv_tile(T, pf, l32, hf, o);
     s0 = n0;
     s1 = n1;
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of tile tt+2 are in LDS
-    __syncthreads();
+    // tile tt+1 must be in LDS for every wave; tile tt+2 may stay in flight
+    if (tt + 2 < nt)
+      wait_all_but_last_tile<NW>();
+    else
+      __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
   }
 
   // ---- epilogue: each lane writes 64 of its row's 128 dims
   const float lt = lsum + __shfl_xor(lsum, 32, 64);
-  if (ipos < 0) return;
-  const int i = ipos;
-  const long long rowp = (bhS + i) * kD;
-  if (MODE == kModeAttn) {
-    if (r == 1) {
-      const float inv = 1.0f / lt;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int dcol = db * 32 + qq * 8 + hf * 4;
-          f32x4_t ov = {o[db][qq * 4] * inv, o[db][qq * 4 + 1] * inv, o[db][qq * 4 + 2] * inv,
-                        o[db][qq * 4 + 3] * inv};
-          *(f32x4_t*)&a.O[rowp + dcol] = ov;
-          *(f32x4_t*)&a.U[rowp + dcol] = f32x4_t{};
-        }
-      }
-      if (hf == 0) {
-        a.lse[bhS + i] = (mref + __log2f(lt)) * 0.6931471805599453f;
-        a.M[bhS + i] = 1.0f;
-      }
-    } else if (lt > 0.0f) {
-      const float Mi = a.M[bhS + i];
-      const float sc = Mi / lt;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int dcol = db * 32 + qq * 8 + hf * 4;
-          const f32x4_t uv = *(const f32x4_t*)&a.U[rowp + dcol];
-          f32x4_t ov;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ov[e] = uv[e] + sc * o[db][qq * 4 + e];
-          *(f32x4_t*)&a.O[rowp + dcol] = ov;
-        }
-      }
-      if (hf == 0) a.lse[bhS + i] = (mref + __log2f(lt)) * 0.6931471805599453f;
-    } else if (hf == 0) {
-      a.lse[bhS + i] = -INFINITY;
-    }
-  } else {
-    const float Mp = a.M[bhS + i];
-    const float Mu = Mp > 0.0f ? Mp : 0.0f;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int dcol = db * 32 + qq * 8 + hf * 4;
-        const f32x4_t ov = *(const f32x4_t*)&a.O[rowp + dcol];
-        f32x4_t uv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) uv[e] = ov[e] - Mu * o[db][qq * 4 + e];
-        *(f32x4_t*)&a.U[rowp + dcol] = uv;
-      }
-    }
-    if (hf == 0) a.M[bhS + i] = Mu * lt;
-  }
+  write_row<MODE>(a, r, bhS, ipos, hf, mref, lt, o);
 }
 
 // ------------------------------------------------------------- column mass

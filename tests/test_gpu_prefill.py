@@ -175,3 +175,12 @@ def test_prefill_bf16_full_size(cfgid, heads):
     cfg = workloads.CONFIGS[cfgid]
     _say("prefill full size", cfg.name, heads)
     _bf16_case(cfg, heads=heads)
+
+
+def test_prefill_bf16_mfma_wide():
+    """Enough heads that the 64-rows-per-wave kernel runs, with ragged row
+    blocks in the dense loop and in loop 2."""
+    cfg = workloads.custom(name="bf16-wide", dtype="bf16", B=2, H=40, d=128, S=1000, R=4, act=(1, 0.9, 0.6, 0.3),
+                           col="0.25", bits=(8, 4, 2, 4), lognormal=0.5, seed=7)
+    _say("prefill bf16 wide", cfg)
+    _bf16_case(cfg, heads=[0, 21, 39])
