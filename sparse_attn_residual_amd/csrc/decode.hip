@@ -116,49 +116,63 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_dense(DecodeArgs a, floa
   }
 }
 
-constexpr int kMaxFastLoops = 5;  // loops whose slot lookups are issued together
+constexpr int kMaxFastLoops = 5;  // loops whose slot lookups are batched
+constexpr int kNF = kMaxFastLoops - 1;
 
-// The 16 dims [sub*16, sub*16+16) of K and V of token j reconstructed at
-// loop r (and V at loop r-1 when vprev is set): the base plus the residuals
-// of loops 2..r in which j was active.  Every slot lookup and record load of
-// the token is issued before any of them is used.
-template <bool PREV>
-__device__ inline void token16(const CacheGeo& c, int r, int l, int b, int h, int j, int sub, float* kx, float* vx,
-                               float* vprev) {
+// Raw loads of the 16 dims [sub*16, sub*16+16) of one token: base codes and
+// scales, and for loops 2..kMaxFastLoops the residual codes and meta of the
+// loops the token was active in (slot >= 0).  Split from the decoding so
+// that the loads of several tokens can be in flight together.
+template <int NR>
+struct TokLoads {
+  uint4 kw, vw;
+  uint32_t sc;                 // K scale | V scale << 16
+  uint2 kr[NR], vr[NR];
+  uint32_t meta[NR][2];        // K scale | zero << 16, V scale | zero << 16
+};
+
+// NR: residual loops 2..NR+1 whose loads are batched (NR = min(r, 5) - 1).
+template <int NR>
+__device__ inline void tok_load(const CacheGeo& c, int l, int b, int h, int j, const int* slot, int sub,
+                                TokLoads<NR>& t) {
   constexpr int d = 128, G = 4;
   const uint8_t* rec = base_rec(c, l, b, h, j);
-  const uint4 kw = *(const uint4*)(rec + sub * 16);
-  const uint4 vw = *(const uint4*)(rec + d + sub * 16);
+  t.kw = *(const uint4*)(rec + sub * 16);
+  t.vw = *(const uint4*)(rec + d + sub * 16);
   const uint16_t* sc = (const uint16_t*)(rec + 2 * d);
-  const uint16_t ksh = sc[sub >> 1], vsh = sc[G + (sub >> 1)];
-  int slot[kMaxFastLoops - 1];
+  t.sc = (uint32_t)sc[sub >> 1] | ((uint32_t)sc[G + (sub >> 1)] << 16);
 #pragma unroll
-  for (int k = 0; k < kMaxFastLoops - 1; ++k) slot[k] = (k + 2 <= r) ? c.slot[k + 2][(long long)b * c.S + j] : -1;
-  uint2 kr[kMaxFastLoops - 1], vr[kMaxFastLoops - 1];
-  uint32_t meta[kMaxFastLoops - 1][2];
-#pragma unroll
-  for (int k = 0; k < kMaxFastLoops - 1; ++k) {
-    kr[k] = vr[k] = make_uint2(0, 0);
-    meta[k][0] = meta[k][1] = 0;
+  for (int k = 0; k < NR; ++k) {
+    t.kr[k] = t.vr[k] = make_uint2(0, 0);
+    t.meta[k][0] = t.meta[k][1] = 0;
     if (slot[k] >= 0) {
       const int rr = k + 2, bits = c.bits[rr], C = d * bits / 8;
       const uint8_t* rrec = res_rec(c, rr, l, b, h, slot[k]);
       if (bits == 4) {
-        kr[k] = *(const uint2*)(rrec + sub * 8);
-        vr[k] = *(const uint2*)(rrec + C + sub * 8);
+        t.kr[k] = *(const uint2*)(rrec + sub * 8);
+        t.vr[k] = *(const uint2*)(rrec + C + sub * 8);
       } else {
-        kr[k].x = *(const uint32_t*)(rrec + sub * 4);
-        vr[k].x = *(const uint32_t*)(rrec + C + sub * 4);
+        t.kr[k].x = *(const uint32_t*)(rrec + sub * 4);
+        t.vr[k].x = *(const uint32_t*)(rrec + C + sub * 4);
       }
       const uint16_t* mt = (const uint16_t*)(rrec + 2 * C);
       const int g = sub >> 1;
-      meta[k][0] = (uint32_t)mt[g] | ((uint32_t)mt[G + g] << 16);          // K scale, zero
-      meta[k][1] = (uint32_t)mt[2 * G + g] | ((uint32_t)mt[3 * G + g] << 16);  // V scale, zero
+      t.meta[k][0] = (uint32_t)mt[g] | ((uint32_t)mt[G + g] << 16);
+      t.meta[k][1] = (uint32_t)mt[2 * G + g] | ((uint32_t)mt[3 * G + g] << 16);
     }
   }
+}
+
+// K and V of the token reconstructed at loop r (and V at loop r-1 when PREV
+// is set) from its loads: base, plus the residuals of loops 2..r in which it
+// was active; loops beyond kMaxFastLoops are looked up here one at a time.
+template <bool PREV, int NR>
+__device__ inline void tok_decode(const CacheGeo& c, int r, int l, int b, int h, int j, const int* slot, int sub,
+                                  const TokLoads<NR>& t, float* kx, float* vx, float* vprev) {
+  constexpr int d = 128, G = 4;
   {
-    const float ks = h2f(ksh), vs = h2f(vsh);
-    const uint32_t kws[4] = {kw.x, kw.y, kw.z, kw.w}, vws[4] = {vw.x, vw.y, vw.z, vw.w};
+    const float ks = h2f((uint16_t)t.sc), vs = h2f((uint16_t)(t.sc >> 16));
+    const uint32_t kws[4] = {t.kw.x, t.kw.y, t.kw.z, t.kw.w}, vws[4] = {t.vw.x, t.vw.y, t.vw.z, t.vw.w};
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       kx[e] = (float)(int8_t)(kws[e >> 2] >> (8 * (e & 3))) * ks;
@@ -170,17 +184,17 @@ __device__ inline void token16(const CacheGeo& c, int r, int l, int b, int h, in
     for (int e = 0; e < 16; ++e) vprev[e] = vx[e];
   }
 #pragma unroll
-  for (int k = 0; k < kMaxFastLoops - 1; ++k) {
+  for (int k = 0; k < NR; ++k) {
     if (slot[k] < 0) continue;
     const int bits = c.bits[k + 2];
-    const float krs = h2f((uint16_t)meta[k][0]), krz = h2f((uint16_t)(meta[k][0] >> 16));
-    const float vrs = h2f((uint16_t)meta[k][1]), vrz = h2f((uint16_t)(meta[k][1] >> 16));
+    const float krs = h2f((uint16_t)t.meta[k][0]), krz = h2f((uint16_t)(t.meta[k][0] >> 16));
+    const float vrs = h2f((uint16_t)t.meta[k][1]), vrz = h2f((uint16_t)(t.meta[k][1] >> 16));
     if (PREV && k + 2 == r) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) vprev[e] = vx[e];
     }
     if (bits == 4) {
-      const uint32_t kq[2] = {kr[k].x, kr[k].y}, vq[2] = {vr[k].x, vr[k].y};
+      const uint32_t kq[2] = {t.kr[k].x, t.kr[k].y}, vq[2] = {t.vr[k].x, t.vr[k].y};
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         kx[e] = kx[e] + __builtin_fmaf((float)((kq[e >> 3] >> (4 * (e & 7))) & 15), krs, krz);
@@ -189,23 +203,22 @@ __device__ inline void token16(const CacheGeo& c, int r, int l, int b, int h, in
     } else {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        kx[e] = kx[e] + __builtin_fmaf((float)((kr[k].x >> (2 * e)) & 3), krs, krz);
-        vx[e] = vx[e] + __builtin_fmaf((float)((vr[k].x >> (2 * e)) & 3), vrs, vrz);
+        kx[e] = kx[e] + __builtin_fmaf((float)((t.kr[k].x >> (2 * e)) & 3), krs, krz);
+        vx[e] = vx[e] + __builtin_fmaf((float)((t.vr[k].x >> (2 * e)) & 3), vrs, vrz);
       }
     }
   }
-  // loops beyond the batched range, one lookup at a time
-  bool active_r = r >= 2 && r <= kMaxFastLoops && slot[r - 2] >= 0;
-  for (int rr = kMaxFastLoops + 1; rr <= r && slot[kMaxFastLoops - 2] >= 0; ++rr) {
-    const int t = c.slot[rr][(long long)b * c.S + j];
-    if (t < 0) break;
+  bool active_r = r >= 2 && r <= NR + 1 && slot[r - 2] >= 0;
+  for (int rr = kMaxFastLoops + 1; NR == kNF && rr <= r && slot[kNF - 1] >= 0; ++rr) {
+    const int ts = c.slot[rr][(long long)b * c.S + j];
+    if (ts < 0) break;
     if (PREV && rr == r) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) vprev[e] = vx[e];
       active_r = true;
     }
     const int bits = c.bits[rr], C = d * bits / 8, g = sub >> 1;
-    const uint8_t* rrec = res_rec(c, rr, l, b, h, t);
+    const uint8_t* rrec = res_rec(c, rr, l, b, h, ts);
     const uint16_t* mt = (const uint16_t*)(rrec + 2 * C);
     const float krs = h2f(mt[g]), krz = h2f(mt[G + g]), vrs = h2f(mt[2 * G + g]), vrz = h2f(mt[3 * G + g]);
 #pragma unroll
@@ -225,8 +238,52 @@ __device__ inline void token16(const CacheGeo& c, int r, int l, int b, int h, in
   }
 }
 
+// Index stage of a chunk of 64 selected tokens: lane L takes token
+// t = t0 + L and loads its position, its slot in loops 2..kMaxFastLoops and
+// (pruned loops) its previous logit.
+template <bool PRUNED, int NR>
+__device__ inline void chunk_index(const DecodeArgs& a, int b, int t0, int lane, const int32_t* sel,
+                                   const float* logit, int& j, int* slot, float& old) {
+  const CacheGeo& c = a.c;
+  const int t = t0 + lane;
+  j = t < a.K ? sel[t] : -1;
+  old = (PRUNED && t < a.K) ? logit[t] : 0.0f;
+#pragma unroll
+  for (int k = 0; k < NR; ++k) slot[k] = j >= 0 ? c.slot[k + 2][(long long)b * c.S + j] : -1;
+}
+
+// One token's contribution to the group's online softmax (and, pruned, to
+// the cached-mass sums C and P of the previous loop's weights).
+template <bool PRUNED>
+__device__ inline void tok_accumulate(const float* q, const float* kx, const float* vx, const float* vp, float tau,
+                                      float old, float Mprev, float lprev, bool valid, int sub, float* lg, float& m,
+                                      float& lsum, float* acc, float* C, float& P) {
+  float part = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) part = __builtin_fmaf(q[e], kx[e], part);
+  const float s = tau * group8_sum(part);
+  if (!valid) return;
+  if (sub == 0) *lg = s;
+  if (PRUNED) {
+    const float pj = Mprev * __expf(old - lprev);
+    P += pj;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) C[e] = __builtin_fmaf(pj, vp[e], C[e]);
+  }
+  const float mn = fmaxf(m, s);
+  const float alpha = __expf(m - mn);
+  const float p = __expf(s - mn);
+  lsum = lsum * alpha + p;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = __builtin_fmaf(p, vx[e], acc[e] * alpha);
+  m = mn;
+}
+
 // Loop r >= 2 over the K selected tokens (sel/logits compacted at the front).
-template <typename T, bool PRUNED>
+// Each wave walks chunks of 64 selected tokens: the index stage of the next
+// chunk (positions, slots, old logits; one token per lane) is in flight while
+// the current chunk's records are read, two tokens per 8-lane group at a time.
+template <typename T, bool PRUNED, int NR>
 __global__ __launch_bounds__(kDecThreads) void k_decode_sparse(DecodeArgs a, float tau) {
   __shared__ GroupState gs;
   __shared__ float csum[PRUNED ? kDecGroups : 1][128];
@@ -243,6 +300,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_sparse(DecodeArgs a, flo
   const int sub = lane & 7;
   const int grp = lane >> 3;
   const int gid = wv * 8 + grp;
+  constexpr int kWaves = kDecThreads / kWave;
   float q[16];
   load_q16<T>((const T*)a.q + lbh * d, sub, q);
   const float Mprev = a.M[lbh];
@@ -252,29 +310,72 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_sparse(DecodeArgs a, flo
   for (int e = 0; e < 16; ++e) acc[e] = C[e] = 0.0f;
   const int32_t* sel = a.sel + lbh * c.S;
   float* logit = a.logits + lbh * c.S;
-  for (int t = gid; t < a.K; t += kDecGroups) {
-    const int j = sel[t];
-    const float old = PRUNED ? logit[t] : 0.0f;
-    float kx[16], vx[16], vp[16];
-    token16<PRUNED>(c, r, l, b, h, j, sub, kx, vx, vp);
-    float part = 0.0f;
+  const int nch = (a.K + 63) / 64;
+
+  int jn = -1, sn[NR];
+  float on = 0.0f;
+  if (wv < nch) chunk_index<PRUNED, NR>(a, b, wv * 64, lane, sel, logit, jn, sn, on);
+  for (int ch = wv; ch < nch; ch += kWaves) {
+    const int jc = jn;
+    int sc[NR];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) part = __builtin_fmaf(q[e], kx[e], part);
-    const float s = tau * group8_sum(part);
-    if (sub == 0) logit[t] = s;  // every lane of the group read the old logit above
-    if (PRUNED) {
-      const float pj = Mprev * __expf(old - lprev);
-      P += pj;
+    for (int k = 0; k < NR; ++k) sc[k] = sn[k];
+    const float oc = on;
+    if (ch + kWaves < nch) chunk_index<PRUNED, NR>(a, b, (ch + kWaves) * 64, lane, sel, logit, jn, sn, on);
+    const int t0 = ch * 64;
+    const int nv = min(64, a.K - t0);  // valid tokens of the chunk (a prefix)
+    // Order the chunk's tokens by how many residual loops they carry (slots
+    // are nested: active at loop k+2 implies active at every earlier loop),
+    // most first, invalid tokens last, so that the eight tokens a wave step
+    // reads share their residual work and the wave skips loops none of them
+    // has.  src: lane (= token of the chunk) taken at sorted position L.
+    int src_of_pos;
+    {
+      int nres = jc >= 0 ? 0 : -1;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) C[e] = __builtin_fmaf(pj, vp[e], C[e]);
+      for (int k = 0; k < NR; ++k) nres += (sc[k] >= 0) ? 1 : 0;
+      const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+      int pos = 0, base = 0;
+#pragma unroll
+      for (int v = NR; v >= -1; --v) {
+        const uint64_t mv = __ballot(nres == v);
+        if (nres == v) pos = base + __popcll(mv & below);
+        base += __popcll(mv);
+      }
+      src_of_pos = __builtin_amdgcn_ds_permute(pos * 4, lane);
     }
-    const float mn = fmaxf(m, s);
-    const float alpha = __expf(m - mn);
-    const float p = __expf(s - mn);
-    lsum = lsum * alpha + p;
+#pragma unroll 1
+    for (int it = 0; it * 8 < nv; it += 2) {  // wave-uniform trip count
+      // sorted positions it*8+grp and (it+1)*8+grp; invalid ones read token 0
+      int j2[2], s2[2][NR], tt[2];
+      float o2[2];
+      bool v2[2];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = __builtin_fmaf(p, vx[e], acc[e] * alpha);
-    m = mn;
+      for (int u = 0; u < 2; ++u) {
+        const int src = __shfl(src_of_pos, (it + u) * 8 + grp, kWave);
+        tt[u] = t0 + src;
+        j2[u] = __shfl(jc, src, kWave);
+#pragma unroll
+        for (int k = 0; k < NR; ++k) s2[u][k] = __shfl(sc[k], src, kWave);
+        o2[u] = __shfl(oc, src, kWave);
+        v2[u] = j2[u] >= 0;
+        if (!v2[u]) {
+          j2[u] = 0;
+#pragma unroll
+          for (int k = 0; k < NR; ++k) s2[u][k] = -1;
+        }
+      }
+      TokLoads<NR> t2[2];
+      tok_load(c, l, b, h, j2[0], s2[0], sub, t2[0]);
+      tok_load(c, l, b, h, j2[1], s2[1], sub, t2[1]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float kx[16], vx[16], vp[16];
+        tok_decode<PRUNED>(c, r, l, b, h, j2[u], s2[u], sub, t2[u], kx, vx, vp);
+        tok_accumulate<PRUNED>(q, kx, vx, vp, tau, o2[u], Mprev, lprev, v2[u], sub, logit + tt[u], m, lsum, acc,
+                               C, P);
+      }
+    }
   }
   if (sub == 0) {
     gs.m[gid] = m;
@@ -336,12 +437,25 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
     e = launch_copy_sel(nullptr, (int)P, a.c.S, a.sel, st);
     if (e != hipSuccess) return e;
   }
-  if (pruned) {
-    if (bf) hipLaunchKernelGGL((k_decode_sparse<uint16_t, true>), dim3((unsigned)P), dim3(kDecThreads), 0, st, a, tau);
-    else hipLaunchKernelGGL((k_decode_sparse<float, true>), dim3((unsigned)P), dim3(kDecThreads), 0, st, a, tau);
-  } else {
-    if (bf) hipLaunchKernelGGL((k_decode_sparse<uint16_t, false>), dim3((unsigned)P), dim3(kDecThreads), 0, st, a, tau);
-    else hipLaunchKernelGGL((k_decode_sparse<float, false>), dim3((unsigned)P), dim3(kDecThreads), 0, st, a, tau);
+  const int nr = (a.r < kMaxFastLoops ? a.r : kMaxFastLoops) - 1;
+  switch (nr * 4 + pruned * 2 + (bf ? 1 : 0)) {
+#define FL_DEC_CASE(NR, PR, BF, T)                                                                          \
+  case NR * 4 + PR * 2 + BF:                                                                                \
+    hipLaunchKernelGGL((k_decode_sparse<T, PR, NR>), dim3((unsigned)P), dim3(kDecThreads), 0, st, a, tau); \
+    break;
+#define FL_DEC_NR(NR)                 \
+  FL_DEC_CASE(NR, 0, 0, float)        \
+  FL_DEC_CASE(NR, 0, 1, uint16_t)     \
+  FL_DEC_CASE(NR, 1, 0, float)        \
+  FL_DEC_CASE(NR, 1, 1, uint16_t)
+    FL_DEC_NR(1)
+    FL_DEC_NR(2)
+    FL_DEC_NR(3)
+    FL_DEC_NR(4)
+#undef FL_DEC_NR
+#undef FL_DEC_CASE
+    default:
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -88,3 +88,23 @@ def test_decode_pruned_every_loop():
         for r in range(cfg.R):
             assert np.max(np.abs(snaps[r]["O"][0, 0, h] - orc[r]["O"])) <= 1e-5, (h, r + 1)
             assert abs(snaps[r]["M"][0, 0, h] - orc[r]["M"]) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_deep_loops(dtype):
+    """Seven loops: residual loops past the batched slot lookups, and a
+    selection spanning many 64-token chunks with a ragged last one."""
+    cfg = workloads.custom(name="decode-deep", dtype=dtype, B=1, H=2, d=128, S=1500, R=7,
+                           act=(1, 0.6, 0.45, 0.3, 0.2, 0.12, 0.07), col="0.47", bits=(8, 4, 2, 4, 2, 4, 2),
+                           gamma=0.5, lognormal=0.5, L=1, decode=True, seed=4)
+    _say("decode deep", dtype, cfg)
+    _decode_case(cfg, 1e-5 if dtype == "f32" else 2e-3, rel=dtype != "f32")
+
+
+def test_decode_full_shape():
+    """The 48-layer decode workload's per-head shape (T = 32768, K = 3276,
+    R = 4, bits 8/4/4/2) on two heads of one layer and sequence."""
+    import dataclasses
+    cfg = dataclasses.replace(workloads.CONFIGS[3], name="decode-full-shape", B=1, H=2, L=1)
+    _say("decode full shape", cfg)
+    _decode_case(cfg, 2e-3, rel=True)
