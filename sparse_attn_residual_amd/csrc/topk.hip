@@ -81,14 +81,19 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const float* kp = keys + (long long)p * key_stride;
 
+  // Loads are unconditional (clamped index) so that all of them are issued
+  // before the first is waited for; out-of-range items are masked after.
   uint32_t u[ITEMS];
   int32_t idx[CAND ? ITEMS : 1];
+  float raw[ITEMS];
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
-    const int e = i * kTopkThreads + tid;
-    u[i] = e < n ? order_key(kp[e]) : 0u;
-    if (CAND) idx[i] = e < n ? cand[(long long)p * cand_stride + e] : 0;
+    const int e = min(i * kTopkThreads + tid, n - 1);
+    raw[i] = kp[e];
+    if (CAND) idx[i] = cand[(long long)p * cand_stride + e];
   }
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) u[i] = i * kTopkThreads + tid < n ? order_key(raw[i]) : 0u;
   __syncthreads();  // every read of keys/cand precedes any write (in-place use)
 
   uint32_t prefix = 0, mask = 0;
@@ -108,7 +113,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
           const uint64_t pm = __ballot(part);
           if (pm == 0) break;
           const int leader = __ffsll((long long)pm) - 1;
-          const uint32_t ld = __shfl(dg, leader, kWave);
+          const uint32_t ld = (uint32_t)__builtin_amdgcn_readlane((int)dg, leader);
           const uint64_t same = __ballot(part && dg == ld);
           if (lane == leader) atomicAdd(&hist[ld], (uint32_t)__popcll(same));
           if (dg == ld) part = false;
@@ -191,6 +196,7 @@ hipError_t launch_copy_sel(const int32_t* cand, int P, int K, int32_t* sel, hipS
 hipError_t launch_topk(const float* keys, long long key_stride, const int32_t* cand, long long cand_stride, int P,
                        int n, int K, int32_t* sel_out, long long sel_stride, float* keys_out,
                        long long keys_out_stride, hipStream_t st) {
+  if (n < 1 || K < 1 || K > n) return hipErrorInvalidValue;
   const int items = (n + kTopkThreads - 1) / kTopkThreads;
   dim3 grid(P), block(kTopkThreads);
 #define FL_TOPK(IT)                                                                                             \
