@@ -14,13 +14,6 @@ namespace fl {
 constexpr int kDecThreads = 256;
 constexpr int kDecGroups = kDecThreads / 8;  // 8 lanes per token
 
-__device__ inline float group8_sum(float v) {
-  v += __shfl_xor(v, 1, kWave);
-  v += __shfl_xor(v, 2, kWave);
-  v += __shfl_xor(v, 4, kWave);
-  return v;
-}
-
 template <typename T>
 __device__ inline void load_q16(const T* q, int sub, float* x) {
 #pragma unroll
@@ -44,7 +37,21 @@ struct GroupState {
   float acc[kDecGroups][128];
 };
 
-// Loop 1: dense over all S cached tokens, d == 128.
+// Sum over the 8 lanes of a group with DPP moves (no LDS round trip):
+// xor 1 and xor 2 within quads, then the mirrored half-row pairs quad 0 of
+// the group with quad 1.
+__device__ inline float group8_sum_dpp(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  return v;
+}
+
+constexpr float kDecRescale = 16.0f;  // lazy rescale threshold (natural log units)
+
+// Loop 1: dense over all S cached tokens, d == 128.  The group's softmax
+// keeps a reference maximum that only moves when a score exceeds it by more
+// than kDecRescale, so the accumulators are rescaled rarely.
 template <typename T>
 __global__ __launch_bounds__(kDecThreads) void k_decode_dense(DecodeArgs a, float tau) {
   __shared__ GroupState gs;
@@ -59,6 +66,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_dense(DecodeArgs a, floa
   const int sub = lane & 7;        // 16-dim slice of the record
   const int grp = lane >> 3;       // token within the wave's step
   const int gid = wv * 8 + grp;    // group id in the block
+  const int g = sub >> 1;          // quantization group of the slice
   float q[16];
   load_q16<T>((const T*)a.q + lbh * d, sub, q);
   float m = -INFINITY, lsum = 0.0f, acc[16];
@@ -66,30 +74,34 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_dense(DecodeArgs a, floa
   for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
   const uint8_t* recs = base_rec(c, l, b, h, 0);
   float* logit = a.logits + lbh * c.S;
-  const int G = d / kGroup;
-  for (int j = wv * 8 + grp; j < c.S; j += kDecThreads / 8) {
+  const uint16_t* scl = (const uint16_t*)(recs + 2 * d);
+  for (int j = gid; j < c.S; j += kDecGroups) {
     const uint8_t* rec = recs + (long long)j * c.base_rb;
     const uint4 kw = *(const uint4*)(rec + sub * 16);
     const uint4 vw = *(const uint4*)(rec + d + sub * 16);
-    const uint16_t* sc = (const uint16_t*)(rec + 2 * d);
-    const float ks = h2f(sc[sub >> 1]);
-    const float vs = h2f(sc[G + (sub >> 1)]);
+    const uint16_t* sc = (const uint16_t*)((const uint8_t*)scl + (long long)j * c.base_rb);
+    const float ks = h2f(sc[g]);
+    const float vs = h2f(sc[4 + g]);
     float cv[16];
     unpack_i8x16(kw, cv);
     float part = 0.0f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) part = __builtin_fmaf(q[e], cv[e], part);
-    const float s = tau * group8_sum(part * ks);
+    const float s = tau * group8_sum_dpp(part * ks);
     if (sub == 0) logit[j] = s;
-    const float mn = fmaxf(m, s);
-    const float alpha = __expf(m - mn);
-    const float p = __expf(s - mn);
-    lsum = lsum * alpha + p;
+    if (s > m + kDecRescale) {
+      const float alpha = __expf(m - s);  // 0 on the group's first token
+      lsum *= alpha;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] *= alpha;
+      m = s;
+    }
+    const float p = __expf(s - m);
+    lsum += p;
     const float pv = p * vs;
     unpack_i8x16(vw, cv);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = __builtin_fmaf(pv, cv[e], acc[e] * alpha);
-    m = mn;
+    for (int e = 0; e < 16; ++e) acc[e] = __builtin_fmaf(pv, cv[e], acc[e]);
   }
   if (sub == 0) {
     gs.m[gid] = m;
@@ -100,12 +112,12 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_dense(DecodeArgs a, floa
   __syncthreads();
   if (threadIdx.x < d) {
     float mx = -INFINITY;
-    for (int g = 0; g < kDecGroups; ++g) mx = fmaxf(mx, gs.m[g]);
+    for (int gg = 0; gg < kDecGroups; ++gg) mx = fmaxf(mx, gs.m[gg]);
     float L = 0.0f, A = 0.0f;
-    for (int g = 0; g < kDecGroups; ++g) {
-      const float f = gs.m[g] == -INFINITY ? 0.0f : __expf(gs.m[g] - mx);
-      L += gs.l[g] * f;
-      A += gs.acc[g][threadIdx.x] * f;
+    for (int gg = 0; gg < kDecGroups; ++gg) {
+      const float f = gs.m[gg] == -INFINITY ? 0.0f : __expf(gs.m[gg] - mx);
+      L += gs.l[gg] * f;
+      A += gs.acc[gg][threadIdx.x] * f;
     }
     a.O[lbh * d + threadIdx.x] = A / L;
     a.U[lbh * d + threadIdx.x] = 0.0f;
@@ -261,7 +273,7 @@ __device__ inline void tok_accumulate(const float* q, const float* kx, const flo
   float part = 0.0f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) part = __builtin_fmaf(q[e], kx[e], part);
-  const float s = tau * group8_sum(part);
+  const float s = tau * group8_sum_dpp(part);
   if (!valid) return;
   if (sub == 0) *lg = s;
   if (PRUNED) {
@@ -270,13 +282,17 @@ __device__ inline void tok_accumulate(const float* q, const float* kx, const flo
 #pragma unroll
     for (int e = 0; e < 16; ++e) C[e] = __builtin_fmaf(pj, vp[e], C[e]);
   }
-  const float mn = fmaxf(m, s);
-  const float alpha = __expf(m - mn);
-  const float p = __expf(s - mn);
-  lsum = lsum * alpha + p;
+  if (s > m + kDecRescale) {  // lazy rescale, as in the dense loop
+    const float alpha = __expf(m - s);
+    lsum *= alpha;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = __builtin_fmaf(p, vx[e], acc[e] * alpha);
-  m = mn;
+    for (int e = 0; e < 16; ++e) acc[e] *= alpha;
+    m = s;
+  }
+  const float p = __expf(s - m);
+  lsum += p;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = __builtin_fmaf(p, vx[e], acc[e]);
 }
 
 // Loop r >= 2 over the K selected tokens (sel/logits compacted at the front).
