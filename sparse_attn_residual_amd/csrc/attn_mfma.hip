@@ -46,13 +46,15 @@ constexpr float kRescale = 8.0f;    // lazy rescale threshold (log2 units): P <=
 // Tile image: the exact LDS layout of one 64-column tile, built once per loop
 // in HBM and copied into LDS by direct global->LDS loads.
 //   K   [64][kKP]  bf16  (row = column of the tile, 272-byte rows)
-//   V^T [128][kVP] fp16  (row = head dim, 136-byte rows)
+//   V^T [128][kVP] fp16  (row = head dim, 144-byte rows; within each 16
+//                        columns, the 8 a lane multiplies are stored
+//                        contiguously: see vt_col)
 //   pos [64]       int32 (position of each column, kNoPos for padding)
 constexpr int kKP = kD + 8;
-constexpr int kVP = kBN + 4;
+constexpr int kVP = kBN + 8;
 constexpr int kImgV = kBN * kKP * 2;          // 17408
-constexpr int kImgPos = kImgV + kD * kVP * 2;  // 34816
-constexpr int kImgBytes = 35 * 1024;           // 35840: 35 chunks of 1 KB
+constexpr int kImgPos = kImgV + kD * kVP * 2;  // 35840
+constexpr int kImgBytes = 36 * 1024;           // 36864: 36 chunks of 1 KB (36096 used)
 constexpr int kImgChunks = kImgBytes / 1024;
 constexpr int kRing = 3;
 
@@ -111,6 +113,16 @@ __device__ inline void chain32(const CacheGeo& c, int rc, int b, int h, int j, i
 // layout and written out with 16-byte stores.  Every packed record a loop
 // attends is dequantized exactly once here (p1 §4.4: chosen keys gathered into
 // dense buffers; p1 App. G: attention works from the packed streams).
+// Column slot of tile column x in the V^T image.  In the S^T = K Q^T
+// accumulator a lane of half hf holds, per 16 columns, columns 4hf..4hf+3
+// and 8+4hf..8+4hf+3; storing those eight next to each other lets the PV
+// product read its B fragment with one 16-byte LDS load.
+__host__ __device__ constexpr int vt_col(int x) {
+  return (x & ~15) + ((x >> 2) & 1) * 8 + ((x >> 3) & 1) * 4 + (x & 3);
+}
+static_assert(vt_col(0) == 0 && vt_col(4) == 8 && vt_col(8) == 4 && vt_col(12) == 12 && vt_col(21) == 25,
+              "V^T column slots");
+
 __global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const int32_t* __restrict__ sel, int K,
                                                      int ntiles, uint8_t* __restrict__ out) {
   __shared__ __align__(16) uint8_t img[kImgBytes];
@@ -143,8 +155,9 @@ __global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const i
   }
   {
     _Float16* vt = (_Float16*)(img + kImgV);
+    const int vc = vt_col(col);
 #pragma unroll
-    for (int e = 0; e < 32; ++e) vt[(g * 32 + e) * kVP + col] = bf16_as_f16(x[e]);
+    for (int e = 0; e < 32; ++e) vt[(g * 32 + e) * kVP + vc] = bf16_as_f16(x[e]);
   }
   if (g == 0) ((int*)(img + kImgPos))[col] = j >= 0 ? j : kNoPos;
   __syncthreads();
@@ -279,13 +292,9 @@ __device__ inline void pv_tile(const uint8_t* T, const f16x8_t* pf, int l32, int
   const _Float16* vt = (const _Float16*)(T + kImgV);
 #pragma unroll
   for (int k2 = 0; k2 < 4; ++k2) {
-    const int c0 = k2 * 16 + hf * 4;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const _Float16* vp = &vt[(db * 32 + l32) * kVP + c0];
-      const f16x4_t lo4 = *(const f16x4_t*)vp;
-      const f16x4_t hi4 = *(const f16x4_t*)(vp + 8);
-      const f16x8_t vf = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      const f16x8_t vf = *(const f16x8_t*)&vt[(db * 32 + l32) * kVP + k2 * 16 + hf * 8];
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[k2], o[db], 0, 0, 0);
     }
   }
