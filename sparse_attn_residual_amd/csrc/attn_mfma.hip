@@ -42,6 +42,7 @@ constexpr int kD = 128;
 constexpr int kBN = 64;             // key columns per tile
 constexpr int kNoPos = 0x7fffffff;  // padding column: masked for every row
 constexpr float kRescale = 8.0f;    // lazy rescale threshold (log2 units): P <= 2^8
+constexpr float kRescaleP = 256.0f;  // 2^kRescale
 
 // Tile image: the exact LDS layout of one 64-column tile, built once per loop
 // in HBM and copied into LDS by direct global->LDS loads.
@@ -224,12 +225,10 @@ __device__ inline void qk_tile(const uint8_t* T, const bf16x8_t* qf, int l32, in
   }
 }
 
-// Softmax of one tile for the lane's row, first part: causal mask, running
-// max with lazy rescale (ATTN) or fixed loop r-1 statistics (UM).  Leaves the
-// masked scores in x and returns the exponent base.
-template <int MODE>
-__device__ inline float softmax_stats(const uint8_t* T, f32x16_t s0, f32x16_t s1, int ipos, int blk_min, int hf,
-                                      float c2, float& mref, float& lsum, f32x16_t* o, float* x) {
+// Softmax of one tile for the lane's row, first part: the causal mask.
+// Copies the scores into x with -inf where the column lies after the row.
+__device__ inline void softmax_mask(const uint8_t* T, f32x16_t s0, f32x16_t s1, int ipos, int blk_min, int hf,
+                                    float* x) {
   const int* tpos = (const int*)(T + kImgPos);
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
@@ -243,30 +242,32 @@ __device__ inline float softmax_stats(const uint8_t* T, f32x16_t s0, f32x16_t s1
       if (tpos[col] > ipos) x[v] = -INFINITY;
     }
   }
-  if (MODE == kModeAttn) {
-    float mt = x[0];
-#pragma unroll
-    for (int v = 1; v < 32; ++v) mt = fmaxf(mt, x[v]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * c2;
-    // rescale only when the row max outgrows the reference by 2^8 (or the
-    // reference is unset); otherwise P stays below 2^8 and fp16 holds it
-    const bool need = mt > mref + kRescale;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float mn = need ? mt : mref;
-      const float alpha = need ? __builtin_amdgcn_exp2f(mref - mn) : 1.0f;
-      mref = mn;
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= alpha;
-    }
-  }
-  return (MODE == kModeAttn && mref == -INFINITY) ? 0.0f : mref;
 }
 
-// Second part: P = 2^(x*c2 - base) rounded to fp16, and the partial row sum
+// Lazy rescale: the reference max mref (log2 units) moves to the row max of
+// the tile only when that max exceeds it by more than kRescale (or it is
+// unset); the row sum and accumulators are rescaled then.  Otherwise every
+// weight 2^(x*c2 - mref) stays below 2^kRescale and fp16 holds it.
+__device__ inline void softmax_rescale(const float* x, float c2, float& mref, float& lsum, f32x16_t* o) {
+  float mt = x[0];
+#pragma unroll
+  for (int v = 1; v < 32; ++v) mt = fmaxf(mt, x[v]);
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * c2;
+  const bool need = mt > mref + kRescale;
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    const float mn = need ? mt : mref;
+    const float alpha = need ? __builtin_amdgcn_exp2f(mref - mn) : 1.0f;
+    mref = mn;
+    lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] *= alpha;
+  }
+}
+
+// Second part: P = 2^(x*c2 - base) rounded to fp16; returns the lane's sum
 // of exactly those fp16 weights (pairs summed into fp32 by v_dot2 with 1s,
 // in two chains).
-__device__ inline void softmax_probs(const float* x, float base, float c2, float& lsum, f16x8_t* pf) {
+__device__ inline float softmax_probs(const float* x, float base, float c2, f16x8_t* pf) {
   const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
   float ls0 = 0.0f, ls1 = 0.0f;
 #pragma unroll
@@ -284,7 +285,7 @@ __device__ inline void softmax_probs(const float* x, float base, float c2, float
         ls0 = __builtin_amdgcn_fdot2(h, one2, ls0, false);
     }
   }
-  lsum += ls0 + ls1;
+  return ls0 + ls1;
 }
 
 // O^T += V^T P^T for one tile ("GEMM phase", second half).
@@ -476,18 +477,30 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(MfmaArgs m) {
     // tile tt+2 goes into the slot tile tt-1 left (all waves passed it)
     if (tt + 2 < nt) dma_tile<NW>(imgs + (long long)(tt + 2) * kImgBytes, lds + ((tt + 2) % kRing) * kImgBytes);
     float x[32];
-    const float base = softmax_stats<MODE>(T, s0, s1, ipos, blk_min, hf, m.c2, mref, lsum, o, x);
+    softmax_mask(T, s0, s1, ipos, blk_min, hf, x);
     // S of the next tile on the matrix cores while these probabilities
     // are formed on the vector ALUs (stale data past the last tile: unused)
     f32x16_t n0, n1;
     qk_tile(Tn, qf, l32, hf, n0, n1);
+    // Weights against the current reference (UM: the fixed loop r-1
+    // statistics).  ATTN: only if a lane's sum exceeds 2^kRescale (so some
+    // weight might) or a valid row has no reference yet is the tile max
+    // taken, the lazy rescale applied and the weights formed again.
     f16x8_t pf[4];
-    softmax_probs(x, base, m.c2, lsum, pf);
+    float ls = softmax_probs(x, (MODE == kModeAttn && mref == -INFINITY) ? 0.0f : mref, m.c2, pf);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // five VALU
     }
+    if (MODE == kModeAttn) {
+      const bool bad = (ipos >= 0 && mref == -INFINITY) || !(ls <= kRescaleP);
+      if (__builtin_amdgcn_ballot_w64(bad)) {
+        softmax_rescale(x, m.c2, mref, lsum, o);
+        ls = softmax_probs(x, mref == -INFINITY ? 0.0f : mref, m.c2, pf);
+      }
+    }
+    lsum += ls;
     pv_tile(T, pf, l32, hf, o);
     s0 = n0;
     s1 = n1;
@@ -507,7 +520,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(MfmaArgs m) {
 // ------------------------------------------------------------- column mass
 // c_j = sum_{i in A_r, i >= j} P^(r-1)_ij for the candidate columns (p1 §4.2
 // and §D.2: columns ranked by the preceding loop's attention statistics over
-// the rows loop r recomputes), with P^(r-1)_ij = M_i 2^(x_ij - lse_i log2 e).
+// the rows loop r recomputes), with P^(r-1)_ij = M_i 2^(x_ij - lse_i log2 e),
+// evaluated as 2^(x_ij - (lse_i log2 e - log2 M_i)).
 // A block owns 128 candidate columns (32 per wave, their K fragments held in
 // registers as the B operand of S = Q K^T, so each lane owns one column) and
 // streams the active rows' loop r-1 queries through LDS in tiles of 64 rows,
@@ -517,9 +531,8 @@ constexpr int kThreads = 256;
 
 struct __align__(16) RowTile {
   __bf16 q[kMassRows * kKP];
-  float off[kMassRows];   // lse * log2(e), +inf when the row had no column left
-  float M[kMassRows];
-  int pos[kMassRows];
+  float off[kMassRows];   // lse * log2(e) - log2(M): P = 2^(x - off); +inf: the row adds nothing
+  int pos[kMassRows];     // row position (-1 past the last active row)
 };
 
 struct MassArgs {
@@ -535,7 +548,7 @@ struct MassArgs {
 
 struct RowRegs {
   uint4 q[4];
-  float off, M;
+  float off;
   int pos;
 };
 
@@ -561,7 +574,6 @@ __device__ inline void fetch_rows(const CacheGeo& c, const AttnArgs& a, int b, i
   }
   R.pos = -1;
   R.off = INFINITY;
-  R.M = 0.0f;
   if (t < kMassRows) {
     const int tr2 = t0 + t;
     if (tr2 < nr) {
@@ -569,11 +581,8 @@ __device__ inline void fetch_rows(const CacheGeo& c, const AttnArgs& a, int b, i
       const int q2 = rp == 1 ? i2 : c.slot[rp][(long long)b * c.S + i2];
       const long long p = (long long)bh * c.S + i2;
       const float Mp = a.M[p];
-      if (q2 >= 0 && Mp > 0.0f) {
-        R.pos = i2;
-        R.M = Mp;
-        R.off = a.lse[p] * 1.4426950408889634f;
-      }
+      R.pos = i2;
+      if (q2 >= 0 && Mp > 0.0f) R.off = a.lse[p] * 1.4426950408889634f - __log2f(Mp);
     }
   }
 }
@@ -587,14 +596,13 @@ __device__ inline void store_rows(const RowRegs& R, RowTile& T) {
   if (t < kMassRows) {
     T.pos[t] = R.pos;
     T.off[t] = R.off;
-    T.M[t] = R.M;
   }
 }
 
 template <bool BASE>
 __global__ __launch_bounds__(kThreads) void k_mass_mfma(MassArgs m) {
   __shared__ RowTile rt[2];
-  __shared__ int sh_t0;
+  __shared__ int sh_t0, sh_jmax;
   const AttnArgs& a = m.a;
   const CacheGeo& c = a.c;
   const int lane = threadIdx.x & 63;
@@ -664,12 +672,20 @@ __global__ __launch_bounds__(kThreads) void k_mass_mfma(MassArgs m) {
       if (rows[mid] < jmin) lo = mid + 1; else hi = mid;
     }
     sh_t0 = lo;
+    // largest column position of the block (columns ascend)
+    if (BASE) {
+      sh_jmax = min(cb * 128 + 127, c.S - 1);
+    } else {
+      const int cl = min(cb * 128 + 127, m.K_prev - 1);
+      const int tile = cl / kBN;
+      const uint8_t* tp = m.tiles + ((long long)bh * m.ntiles_total + tile) * kImgBytes;
+      sh_jmax = ((const int*)(tp + kImgPos))[cl - tile * kBN];
+    }
   }
   __syncthreads();
   const int t0 = sh_t0;
   const int ntl = (nr - t0 + kMassRows - 1) / kMassRows;
-  // the block's largest column position (tiles beyond it need no mask)
-  int jmax_l = jpos == kNoPos ? -1 : jpos;
+  const int jmax = sh_jmax;
   float acc = 0.0f;
   RowRegs rr;
   if (ntl > 0) {
@@ -691,28 +707,41 @@ __global__ __launch_bounds__(kThreads) void k_mass_mfma(MassArgs m) {
         s[ib] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf[ks], s[ib], 0, 0, 0);
       }
     }
+    // rows are ascending: once the tile's first row lies at or after the
+    // block's last column, every row of it sees every column (no mask)
+    if (T.pos[0] >= jmax) {
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
+      for (int ib = 0; ib < 2; ++ib) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int rbase = ib * 32 + 8 * g + 4 * hf;
-        const float4 offv = *(const float4*)&T.off[rbase];
-        const float4 Mv = *(const float4*)&T.M[rbase];
-        const int4 pv = *(const int4*)&T.pos[rbase];
-        const float offs[4] = {offv.x, offv.y, offv.z, offv.w};
-        const float Ms[4] = {Mv.x, Mv.y, Mv.z, Mv.w};
-        const int ps[4] = {pv.x, pv.y, pv.z, pv.w};
+        for (int g = 0; g < 4; ++g) {
+          const float4 offv = *(const float4*)&T.off[ib * 32 + 8 * g + 4 * hf];
+          const float offs[4] = {offv.x, offv.y, offv.z, offv.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = Ms[e] * __builtin_amdgcn_exp2f(__builtin_fmaf(s[ib][4 * g + e], m.c2, -offs[e]));
-          acc += (ps[e] >= jpos) ? p : 0.0f;
+          for (int e = 0; e < 4; ++e)
+            acc += __builtin_amdgcn_exp2f(__builtin_fmaf(s[ib][4 * g + e], m.c2, -offs[e]));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int rbase = ib * 32 + 8 * g + 4 * hf;
+          const float4 offv = *(const float4*)&T.off[rbase];
+          const int4 pv = *(const int4*)&T.pos[rbase];
+          const float offs[4] = {offv.x, offv.y, offv.z, offv.w};
+          const int ps[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[ib][4 * g + e], m.c2, -offs[e]));
+            acc += (ps[e] >= jpos) ? p : 0.0f;
+          }
         }
       }
     }
     if (more) store_rows(rr, rt[(tt + 1) & 1]);
     __syncthreads();
   }
-  (void)jmax_l;
   acc += __shfl_xor(acc, 32, 64);
   if (hf == 0 && jpos != kNoPos) m.mass[(long long)bh * m.K_prev + cidx] = acc;
 }
