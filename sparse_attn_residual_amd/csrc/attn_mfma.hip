@@ -57,7 +57,8 @@ constexpr int kImgV = kBN * kKP * 2;          // 17408
 constexpr int kImgPos = kImgV + kD * kVP * 2;  // 35840
 constexpr int kImgBytes = 36 * 1024;           // 36864: 36 chunks of 1 KB (36096 used)
 constexpr int kImgChunks = kImgBytes / 1024;
-constexpr int kRing = 3;
+constexpr int kRing = 4;               // tile images resident in LDS
+constexpr int kAhead = kRing - 1;      // tiles copied ahead of the one in use
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -198,17 +199,24 @@ __device__ inline void lds_barrier() {
 // the wave are outstanding (expcnt and lgkmcnt left unconstrained).
 constexpr int vm_wait_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
-// Wait until the wave's copies of every tile but the one issued last have
-// landed: the wave issued ceil or floor of kImgChunks / NW chunk loads for
-// that tile, and they may stay in flight.
-template <int NW>
-__device__ inline void wait_all_but_last_tile() {
+// Wait until the wave's copies of every tile but the last `keep` issued
+// have landed (in-order completion): the wave issues ceil or floor of
+// kImgChunks / NW chunk loads per tile.
+template <int NW, int K>
+__device__ inline void wait_keep() {
   constexpr int hi = (kImgChunks + NW - 1) / NW, lo = kImgChunks / NW;
   const int wv = threadIdx.x >> 6;
   if (wv < kImgChunks - lo * NW || hi == lo)
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm(hi));
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(K * hi));
   else
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm(lo));
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(K * lo));
+}
+template <int NW>
+__device__ inline void wait_tiles_but(int keep) {
+  static_assert(kAhead <= 3, "wait_tiles_but covers up to two tiles in flight");
+  if (keep >= 2) wait_keep<NW, 2>();
+  else if (keep == 1) wait_keep<NW, 1>();
+  else __builtin_amdgcn_s_waitcnt(0);
 }
 
 // S^T = K Q^T for one tile: the lane's row against the tile's 64 columns.
@@ -463,9 +471,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(MfmaArgs m) {
   __syncthreads();
   const int nt = sh_ntiles;
 
-  // ---- prologue: tiles 0 and 1 into the ring, S of tile 0
-  if (nt > 0) dma_tile<NW>(imgs, lds);
-  if (nt > 1) dma_tile<NW>(imgs + kImgBytes, lds + kImgBytes);
+  // ---- prologue: the first kAhead tiles into the ring, S of tile 0
+  for (int k = 0; k < kAhead && k < nt; ++k) dma_tile<NW>(imgs + (long long)k * kImgBytes, lds + k * kImgBytes);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
@@ -474,8 +481,9 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(MfmaArgs m) {
   for (int tt = 0; tt < nt; ++tt) {
     const uint8_t* T = lds + (tt % kRing) * kImgBytes;
     const uint8_t* Tn = lds + ((tt + 1) % kRing) * kImgBytes;
-    // tile tt+2 goes into the slot tile tt-1 left (all waves passed it)
-    if (tt + 2 < nt) dma_tile<NW>(imgs + (long long)(tt + 2) * kImgBytes, lds + ((tt + 2) % kRing) * kImgBytes);
+    // tile tt+kAhead goes into the slot tile tt-1 left (all waves passed it)
+    if (tt + kAhead < nt)
+      dma_tile<NW>(imgs + (long long)(tt + kAhead) * kImgBytes, lds + ((tt + kAhead) % kRing) * kImgBytes);
     float x[32];
     softmax_mask(T, s0, s1, ipos, blk_min, hf, x);
     // S of the next tile on the matrix cores while these probabilities
@@ -504,11 +512,9 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(MfmaArgs m) {
     pv_tile(T, pf, l32, hf, o);
     s0 = n0;
     s1 = n1;
-    // tile tt+1 must be in LDS for every wave; tile tt+2 may stay in flight
-    if (tt + 2 < nt)
-      wait_all_but_last_tile<NW>();
-    else
-      __builtin_amdgcn_s_waitcnt(0);
+    // tile tt+1 must be in LDS for every wave; the loop's copies of the
+    // tiles after it (up to tt+kAhead) may stay in flight
+    wait_tiles_but<NW>(min(tt + kAhead, nt - 1) - (tt + 1));
     lds_barrier();
   }
 
