@@ -32,7 +32,7 @@ __device__ inline float key_value(uint32_t u) {
 // flagged candidate in candidate order is then
 //   rowoff[i] + wtab[w][i] + popcount(ballot_i & lanes below).
 template <int ITEMS>
-__device__ inline void row_counts(uint64_t bits, int (*wtab)[ITEMS], int* rowoff) {
+__device__ inline void row_counts(uint64_t bits, int (*wtab)[64], int* rowoff) {
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
@@ -62,18 +62,121 @@ __device__ inline void row_counts(uint64_t bits, int (*wtab)[ITEMS], int* rowoff
   __syncthreads();
 }
 
-template <int ITEMS, bool CAND>
+constexpr int kBins = 2048;     // value bins of the first stage
+constexpr int kCandCap = 2048;  // keys of the threshold bin resolved exactly (2 per thread)
+
+struct TopkShared {
+  uint32_t hist[kBins];         // value bins; the first 256 also serve as digit histogram
+  uint32_t cu[kCandCap];        // keys of the threshold bin
+  int wtab[kTopkWaves][64];
+  int rowoff[64];
+  int wsum[kTopkWaves];
+  uint32_t wmin[kTopkWaves], wmax[kTopkWaves];
+  uint32_t digit;
+  int rem, bstar, cnt, ncand, bad;
+};
+
+// Block-wide inclusive prefix sum of one value per thread.
+__device__ inline int block_incl_scan(int x, int* wsum) {
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) wsum[wv] = x;
+  __syncthreads();
+  for (int w = 0; w < wv; ++w) x += wsum[w];
+  __syncthreads();
+  return x;
+}
+
+// Radix select over NI keys per thread (bit i of vmask: key i valid): the
+// K-th largest key T and how many keys equal to T are among the K largest.
+// Four 8-bit passes with an LDS digit histogram and a parallel digit search.
+template <int NI>
+__device__ inline void radix_find(const uint32_t* v, uint64_t vmask, int K, TopkShared& sh, uint32_t& T, int& rem) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  uint32_t prefix = 0, mask = 0;
+  rem = K;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    if (tid < 256) sh.hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      bool part = ((vmask >> i) & 1) && (v[i] & mask) == prefix;
+      const uint32_t dg = (v[i] >> shift) & 255u;
+      if (pass == 0) {
+        // keys of one problem share their leading digit: aggregate per wave
+        for (int it = 0; it < 4; ++it) {
+          const uint64_t pm = __ballot(part);
+          if (pm == 0) break;
+          const int leader = __ffsll((long long)pm) - 1;
+          const uint32_t ld = (uint32_t)__builtin_amdgcn_readlane((int)dg, leader);
+          const uint64_t same = __ballot(part && dg == ld);
+          if (lane == leader) atomicAdd(&sh.hist[ld], (uint32_t)__popcll(same));
+          if (dg == ld) part = false;
+        }
+      }
+      if (part) atomicAdd(&sh.hist[dg], 1u);
+    }
+    __syncthreads();
+    // digit of the rem-th largest: inclusive scan of the histogram from the
+    // top by the first four waves (tid < 256 covers whole waves)
+    int c = 0, x = 0;
+    if (tid < 256) {
+      c = (int)sh.hist[255 - tid];
+      x = c;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
+      }
+      if (lane == kWave - 1) sh.wsum[wv] = x;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      for (int w = 0; w < wv; ++w) x += sh.wsum[w];
+      const int excl = x - c;
+      if (excl < rem && x >= rem) {
+        sh.digit = (uint32_t)(255 - tid);
+        sh.rem = rem - excl;
+      }
+    }
+    __syncthreads();
+    prefix |= sh.digit << shift;
+    mask |= 255u << shift;
+    rem = sh.rem;
+    __syncthreads();
+  }
+  T = prefix;
+}
+
+// Value bin of key u in [lo, hi]: monotone non-decreasing in the key, so a
+// key in a higher bin is larger than every key in a lower one.
+__device__ inline int value_bin(uint32_t u, float lo, float scale) {
+  const int bn = (int)((key_value(u) - lo) * scale);
+  return bn < kBins - 1 ? bn : kBins - 1;
+}
+
+// One 1024-thread block per problem.  Stage 1 (BINNED, when the keys are
+// finite and not all equal): a histogram of the keys over kBins equal-width
+// value bins spanning [min, max] finds the bin holding the K-th largest key
+// with one atomic per key; its keys (at most kCandCap) are gathered into LDS
+// and a radix select among them gives the exact threshold.  Otherwise, or
+// when that bin is too full, a radix select over all keys does.  The output
+// stage takes every key above the threshold and the first keys equal to it
+// in candidate order, ranked with wave ballots: ascending, unique.
+template <int ITEMS, bool CAND, bool BINNED>
 __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__ keys, long long key_stride,
                                                        const int32_t* cand, long long cand_stride, int n, int K,
                                                        int32_t* sel_out, long long sel_stride, float* keys_out,
                                                        long long keys_out_stride) {
   static_assert(ITEMS <= 64, "bitmasks hold 64 rows");
-  __shared__ uint32_t hist[256];
-  __shared__ int wtab[kTopkWaves][ITEMS];
-  __shared__ int rowoff[ITEMS];
-  __shared__ int wsum[4];
-  __shared__ uint32_t sh_digit;
-  __shared__ int sh_rem;
+  __shared__ TopkShared sh;
   const int p = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -85,95 +188,131 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
   // before the first is waited for; out-of-range items are masked after.
   uint32_t u[ITEMS];
   int32_t idx[CAND ? ITEMS : 1];
-  float raw[ITEMS];
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const int e = min(i * kTopkThreads + tid, n - 1);
-    raw[i] = kp[e];
-    if (CAND) idx[i] = cand[(long long)p * cand_stride + e];
-  }
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) u[i] = i * kTopkThreads + tid < n ? order_key(raw[i]) : 0u;
-  __syncthreads();  // every read of keys/cand precedes any write (in-place use)
-
-  uint32_t prefix = 0, mask = 0;
-  int rem = K;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
+  uint64_t vmask = 0;
+  bool finite = true;
+  {
+    float raw[ITEMS];
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
-      const int e = i * kTopkThreads + tid;
-      bool part = e < n && (u[i] & mask) == prefix;
-      const uint32_t dg = (u[i] >> shift) & 255u;
-      if (pass == 0) {
-        // keys of one problem share their leading digit: aggregate per wave
-        for (int it = 0; it < 4; ++it) {
-          const uint64_t pm = __ballot(part);
-          if (pm == 0) break;
-          const int leader = __ffsll((long long)pm) - 1;
-          const uint32_t ld = (uint32_t)__builtin_amdgcn_readlane((int)dg, leader);
-          const uint64_t same = __ballot(part && dg == ld);
-          if (lane == leader) atomicAdd(&hist[ld], (uint32_t)__popcll(same));
-          if (dg == ld) part = false;
-        }
-      }
-      if (part) atomicAdd(&hist[dg], 1u);
+      const int e = min(i * kTopkThreads + tid, n - 1);
+      raw[i] = kp[e];
+      if (CAND) idx[i] = cand[(long long)p * cand_stride + e];
     }
-    __syncthreads();
-    // digit of the rem-th largest: inclusive scan of the histogram from the
-    // top by the first four waves (tid < 256 covers whole waves)
-    int v = 0, x = 0;
-    if (tid < 256) {
-      v = (int)hist[255 - tid];
-      x = v;
 #pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(x, o, kWave);
-        if (lane >= o) x += y;
-      }
-      if (lane == kWave - 1) wsum[wv] = x;
-    }
-    __syncthreads();
-    if (tid < 256) {
-      for (int w = 0; w < wv; ++w) x += wsum[w];
-      const int excl = x - v;
-      if (excl < rem && x >= rem) {
-        sh_digit = (uint32_t)(255 - tid);
-        sh_rem = rem - excl;
+    for (int i = 0; i < ITEMS; ++i) {
+      const bool valid = i * kTopkThreads + tid < n;
+      u[i] = valid ? order_key(raw[i]) : 0u;
+      if (valid) {
+        vmask |= 1ull << i;
+        finite = finite && __builtin_isfinite(raw[i]);
       }
     }
-    __syncthreads();
-    prefix |= sh_digit << shift;
-    mask |= 255u << shift;
-    rem = sh_rem;
-    __syncthreads();
   }
-  const uint32_t T = prefix;
+  if (tid == 0) sh.bad = 0;
+  __syncthreads();  // every read of keys/cand precedes any write (in-place use)
+
+  uint32_t T;
+  int rem;
+  bool done = false;
+  if (BINNED) {
+    // ---- range of the keys
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      if ((vmask >> i) & 1) {
+        mn = min(mn, u[i]);
+        mx = max(mx, u[i]);
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+      mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+    }
+    if (lane == 0) {
+      sh.wmin[wv] = mn;
+      sh.wmax[wv] = mx;
+    }
+    if (__ballot(!finite) && lane == 0) atomicOr(&sh.bad, 1);
+    for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
+    __syncthreads();
+    mn = sh.wmin[0];
+    mx = sh.wmax[0];
+    for (int w = 1; w < kTopkWaves; ++w) {
+      mn = min(mn, sh.wmin[w]);
+      mx = max(mx, sh.wmax[w]);
+    }
+    const float lo = key_value(mn), hi = key_value(mx);
+    const float scale = (float)kBins / (hi - lo);
+    if (mn == mx && !sh.bad) {
+      // all keys equal: the first K in candidate order
+      T = mn;
+      rem = K;
+      done = true;
+    } else if (!sh.bad && scale < INFINITY) {
+      // ---- stage 1: value histogram
+#pragma unroll
+      for (int i = 0; i < ITEMS; ++i)
+        if ((vmask >> i) & 1) atomicAdd(&sh.hist[value_bin(u[i], lo, scale)], 1u);
+      __syncthreads();
+      // bins from the top: thread t covers bins kBins-1-2t and kBins-2-2t
+      const int b0 = kBins - 1 - 2 * tid, b1 = b0 - 1;
+      const int c0 = (int)sh.hist[b0], c1 = (int)sh.hist[b1];
+      const int incl = block_incl_scan(c0 + c1, sh.wsum);
+      const int excl = incl - c0 - c1;  // keys in bins above b0
+      if (excl < K && excl + c0 >= K) {
+        sh.bstar = b0;
+        sh.rem = K - excl;
+        sh.cnt = c0;
+      } else if (excl + c0 < K && incl >= K) {
+        sh.bstar = b1;
+        sh.rem = K - excl - c0;
+        sh.cnt = c1;
+      }
+      if (tid == 0) sh.ncand = 0;
+      __syncthreads();
+      if (sh.cnt <= kCandCap) {
+        // ---- gather the threshold bin's keys into LDS
+        const int bs = sh.bstar;
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i)
+          if (((vmask >> i) & 1) && value_bin(u[i], lo, scale) == bs) sh.cu[atomicAdd(&sh.ncand, 1)] = u[i];
+        __syncthreads();
+        const int nc = sh.ncand;
+        const uint32_t cv[2] = {tid < nc ? sh.cu[tid] : 0u, tid + kTopkThreads < nc ? sh.cu[tid + kTopkThreads] : 0u};
+        const uint64_t cm = (tid < nc ? 1ull : 0ull) | (tid + kTopkThreads < nc ? 2ull : 0ull);
+        const int remb = sh.rem;
+        __syncthreads();
+        radix_find<2>(cv, cm, remb, sh, T, rem);
+        done = true;
+      }
+    }
+  }
+  if (!done) radix_find<ITEMS>(u, vmask, K, sh, T, rem);
+
   // keys equal to T: the first `rem` of them in candidate order are taken
   uint64_t eq = 0, take = 0;
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
-    const bool valid = i * kTopkThreads + tid < n;
+    const bool valid = (vmask >> i) & 1;
     if (valid && u[i] == T) eq |= 1ull << i;
     if (valid && u[i] > T) take |= 1ull << i;
   }
-  row_counts<ITEMS>(eq, wtab, rowoff);
+  row_counts<ITEMS>(eq, sh.wtab, sh.rowoff);
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     const uint64_t m = __ballot((eq >> i) & 1);
-    const int rk = rowoff[i] + wtab[wv][i] + __popcll(m & below);
+    const int rk = sh.rowoff[i] + sh.wtab[wv][i] + __popcll(m & below);
     if (((eq >> i) & 1) && rk < rem) take |= 1ull << i;
   }
   __syncthreads();
-  row_counts<ITEMS>(take, wtab, rowoff);
+  row_counts<ITEMS>(take, sh.wtab, sh.rowoff);
   int32_t* so = sel_out + (long long)p * sel_stride;
   float* ko = keys_out ? keys_out + (long long)p * keys_out_stride : nullptr;
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     const uint64_t m = __ballot((take >> i) & 1);
-    const int rk = rowoff[i] + wtab[wv][i] + __popcll(m & below);
+    const int rk = sh.rowoff[i] + sh.wtab[wv][i] + __popcll(m & below);
     if (((take >> i) & 1) && rk < K) {
       so[rk] = CAND ? idx[i] : i * kTopkThreads + tid;
       if (ko) ko[rk] = key_value(u[i]);
@@ -199,21 +338,22 @@ hipError_t launch_topk(const float* keys, long long key_stride, const int32_t* c
   if (n < 1 || K < 1 || K > n) return hipErrorInvalidValue;
   const int items = (n + kTopkThreads - 1) / kTopkThreads;
   dim3 grid(P), block(kTopkThreads);
-#define FL_TOPK(IT)                                                                                             \
+#define FL_TOPK(IT, BIN)                                                                                        \
   do {                                                                                                          \
     if (cand)                                                                                                   \
-      hipLaunchKernelGGL((k_topk<IT, true>), grid, block, 0, st, keys, key_stride, cand, cand_stride, n, K,     \
+      hipLaunchKernelGGL((k_topk<IT, true, BIN>), grid, block, 0, st, keys, key_stride, cand, cand_stride, n, K, \
                          sel_out, sel_stride, keys_out, keys_out_stride);                                       \
     else                                                                                                        \
-      hipLaunchKernelGGL((k_topk<IT, false>), grid, block, 0, st, keys, key_stride, cand, cand_stride, n, K,    \
-                         sel_out, sel_stride, keys_out, keys_out_stride);                                       \
+      hipLaunchKernelGGL((k_topk<IT, false, BIN>), grid, block, 0, st, keys, key_stride, cand, cand_stride, n,   \
+                         K, sel_out, sel_stride, keys_out, keys_out_stride);                                    \
   } while (0)
-  if (items <= 1) FL_TOPK(1);
-  else if (items <= 4) FL_TOPK(4);
-  else if (items <= 8) FL_TOPK(8);
-  else if (items <= 16) FL_TOPK(16);
-  else if (items <= 32) FL_TOPK(32);
-  else if (items <= 64) FL_TOPK(64);
+  // small problems: radix select directly; larger: value bins first
+  if (items <= 1) FL_TOPK(1, false);
+  else if (items <= 4) FL_TOPK(4, false);
+  else if (items <= 8) FL_TOPK(8, true);
+  else if (items <= 16) FL_TOPK(16, true);
+  else if (items <= 32) FL_TOPK(32, true);
+  else if (items <= 64) FL_TOPK(64, true);
   else return hipErrorInvalidValue;
 #undef FL_TOPK
   return hipGetLastError();

@@ -184,3 +184,38 @@ def test_prefill_bf16_mfma_wide():
                            col="0.25", bits=(8, 4, 2, 4), lognormal=0.5, seed=7)
     _say("prefill bf16 wide", cfg)
     _bf16_case(cfg, heads=[0, 21, 39])
+
+
+def _keys(pattern, shape, rng):
+    x = rng.standard_normal(shape)
+    if pattern == "ties8":
+        x = np.round(x * 8) / 8
+    elif pattern == "binary":
+        x = (rng.random(shape) < 0.5).astype(np.float64)
+    elif pattern == "equal":
+        x = np.full(shape, 0.5)
+    elif pattern == "lognormal-wide":
+        x = np.exp(5.0 * x)
+    elif pattern == "inf":
+        x[..., ::97] = np.inf
+        x[..., 5::89] = -np.inf
+    elif pattern == "signed-zero":
+        x = np.where(rng.random(shape) < 0.6, np.where(rng.random(shape) < 0.5, -0.0, 0.0), x)
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("S,col", [(9000, "0.10"), (32768, "0.10"), (32768, "0.0001")])
+@pytest.mark.parametrize("pattern", ["normal", "ties8", "binary", "equal", "lognormal-wide", "inf", "signed-zero"])
+def test_topk_key_patterns(S, col, pattern):
+    """Selections from given keys equal the oracle's exactly: the value-binned
+    first stage, its exact resolution of the threshold bin, and the radix
+    fallback (non-finite keys, one over-full bin, all keys equal)."""
+    import tests.gpu_harness as gh
+    cfg = workloads.custom(dtype="f32", B=1, H=2, d=64, S=S, R=2, act=(1, 0.3), col=col, bits=(8, 4), seed=11)
+    _say("topk keys", pattern, S, cfg.K)
+    rows, slices = workloads.gen_batch(cfg)
+    mass = _keys(pattern, (cfg.B, cfg.H, cfg.S), np.random.default_rng(S + len(pattern)))
+    gpu = gh.run_prefill(cfg, rows, slices, mass_in={2: mass})
+    for h in range(cfg.H):
+        want = prefill.topk(mass[0, h].astype(np.float64), np.arange(cfg.S), cfg.K)
+        assert np.array_equal(gpu["sel"][1][0, h], want), (pattern, h)
