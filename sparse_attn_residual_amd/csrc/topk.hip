@@ -155,22 +155,54 @@ __device__ inline void radix_find(const uint32_t* v, uint64_t vmask, int K, Topk
   T = prefix;
 }
 
-// Value bin of key u in [lo, hi]: monotone non-decreasing in the key, so a
-// key in a higher bin is larger than every key in a lower one.
-__device__ inline int value_bin(uint32_t u, float lo, float scale) {
-  const int bn = (int)((key_value(u) - lo) * scale);
-  return bn < kBins - 1 ? bn : kBins - 1;
+// Block-wide min and max of one pair per thread.
+__device__ inline void block_minmax(uint32_t& mn, uint32_t& mx, TopkShared& sh) {
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+  }
+  if (lane == 0) {
+    sh.wmin[wv] = mn;
+    sh.wmax[wv] = mx;
+  }
+  __syncthreads();
+  mn = sh.wmin[0];
+  mx = sh.wmax[0];
+  for (int w = 1; w < kTopkWaves; ++w) {
+    mn = min(mn, sh.wmin[w]);
+    mx = max(mx, sh.wmax[w]);
+  }
+  __syncthreads();
 }
 
-// One 1024-thread block per problem.  Stage 1 (BINNED, when the keys are
-// finite and not all equal): a histogram of the keys over kBins equal-width
-// value bins spanning [min, max] finds the bin holding the K-th largest key
-// with one atomic per key; its keys (at most kCandCap) are gathered into LDS
-// and a radix select among them gives the exact threshold.  Otherwise, or
-// when that bin is too full, a radix select over all keys does.  The output
-// stage takes every key above the threshold and the first keys equal to it
-// in candidate order, ranked with wave ballots: ascending, unique.
-template <int ITEMS, bool CAND, bool BINNED>
+// Bin of key u at one level of the search over the key range [lo, hi]
+// (order-preserving keys).  The first level uses kBins equal-width value
+// bins of the float keys (flo, fscale) when the range is finite; later
+// levels take the next 11 bits of u - lo below its leading bit (shift).
+// Both are monotone non-decreasing in the key: a key in a higher bin is
+// larger than every key in a lower one.
+__device__ inline int level_bin(uint32_t u, uint32_t lo, bool by_value, float flo, float fscale, int shift) {
+  if (by_value) {
+    const int bn = (int)((key_value(u) - flo) * fscale);
+    return bn < kBins - 1 ? bn : kBins - 1;
+  }
+  return (int)((u - lo) >> shift);
+}
+
+// One 1024-thread block per problem.  The threshold (the K-th largest key T
+// and how many keys equal to T are among the K largest) is found by
+// histogram levels over a shrinking key range: each level bins the keys in
+// the range into kBins bins (one LDS atomic per key) and finds the bin
+// holding the rank sought.  If that bin holds at most kCandCap keys they are
+// gathered into LDS and a radix select among them gives T exactly;
+// otherwise the range shrinks to that bin's keys (at most four levels: the
+// first by value, then 11 bits of the order-preserving key at a time), and
+// a range of one value is T itself.  The output stage takes every key above
+// T and the first keys equal to T in candidate order, ranked with wave
+// ballots: ascending, unique.  Keys must not be NaN.
+template <int ITEMS, bool CAND>
 __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__ keys, long long key_stride,
                                                        const int32_t* cand, long long cand_stride, int n, int K,
                                                        int32_t* sel_out, long long sel_stride, float* keys_out,
@@ -186,10 +218,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
 
   // Loads are unconditional (clamped index) so that all of them are issued
   // before the first is waited for; out-of-range items are masked after.
+  // u = 0 marks an item past n (no finite or infinite key maps to 0)
   uint32_t u[ITEMS];
   int32_t idx[CAND ? ITEMS : 1];
-  uint64_t vmask = 0;
-  bool finite = true;
   {
     float raw[ITEMS];
 #pragma unroll
@@ -199,104 +230,95 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
       if (CAND) idx[i] = cand[(long long)p * cand_stride + e];
     }
 #pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      const bool valid = i * kTopkThreads + tid < n;
-      u[i] = valid ? order_key(raw[i]) : 0u;
-      if (valid) {
-        vmask |= 1ull << i;
-        finite = finite && __builtin_isfinite(raw[i]);
-      }
-    }
+    for (int i = 0; i < ITEMS; ++i) u[i] = i * kTopkThreads + tid < n ? order_key(raw[i]) : 0u;
   }
-  if (tid == 0) sh.bad = 0;
   __syncthreads();  // every read of keys/cand precedes any write (in-place use)
 
-  uint32_t T;
-  int rem;
-  bool done = false;
-  if (BINNED) {
-    // ---- range of the keys
-    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  // ---- range of the keys
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      if ((vmask >> i) & 1) {
-        mn = min(mn, u[i]);
-        mx = max(mx, u[i]);
-      }
+  for (int i = 0; i < ITEMS; ++i) {
+    lo = min(lo, u[i] ? u[i] : 0xFFFFFFFFu);
+    hi = max(hi, u[i]);
+  }
+  block_minmax(lo, hi, sh);
+
+  uint32_t T = lo;
+  int rem = K;       // rank sought among the keys in [lo, hi]
+  for (int level = 0; level < 5; ++level) {
+    if (lo == hi) {  // every key left is T
+      T = lo;
+      break;
     }
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
-      mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
-    }
-    if (lane == 0) {
-      sh.wmin[wv] = mn;
-      sh.wmax[wv] = mx;
-    }
-    if (__ballot(!finite) && lane == 0) atomicOr(&sh.bad, 1);
+    const float flo = key_value(lo), fhi = key_value(hi);
+    const float fscale = (float)kBins / (fhi - flo);
+    const bool by_value = level == 0 && fscale < INFINITY && fscale > 0.0f;
+    const int shift = max(0, 32 - __clz((int)(hi - lo)) - 11);
     for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
+    if (tid == 0) sh.ncand = 0;
     __syncthreads();
-    mn = sh.wmin[0];
-    mx = sh.wmax[0];
-    for (int w = 1; w < kTopkWaves; ++w) {
-      mn = min(mn, sh.wmin[w]);
-      mx = max(mx, sh.wmax[w]);
+    const uint32_t span = hi - lo;  // keys in range: u - lo <= span (lo >= 1 excludes u = 0)
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i)
+      if (u[i] - lo <= span) atomicAdd(&sh.hist[level_bin(u[i], lo, by_value, flo, fscale, shift)], 1u);
+    __syncthreads();
+    // bins from the top: thread t covers bins kBins-1-2t and kBins-2-2t
+    const int b0 = kBins - 1 - 2 * tid, b1 = b0 - 1;
+    const int c0 = (int)sh.hist[b0], c1 = (int)sh.hist[b1];
+    const int incl = block_incl_scan(c0 + c1, sh.wsum);
+    const int excl = incl - c0 - c1;  // keys in bins above b0
+    if (excl < rem && excl + c0 >= rem) {
+      sh.bstar = b0;
+      sh.rem = rem - excl;
+      sh.cnt = c0;
+    } else if (excl + c0 < rem && incl >= rem) {
+      sh.bstar = b1;
+      sh.rem = rem - excl - c0;
+      sh.cnt = c1;
     }
-    const float lo = key_value(mn), hi = key_value(mx);
-    const float scale = (float)kBins / (hi - lo);
-    if (mn == mx && !sh.bad) {
-      // all keys equal: the first K in candidate order
-      T = mn;
-      rem = K;
-      done = true;
-    } else if (!sh.bad && scale < INFINITY) {
-      // ---- stage 1: value histogram
+    __syncthreads();
+    const int bs = sh.bstar, cnt = sh.cnt;
+    rem = sh.rem;
+    // recompute the bins below rather than keep all of them live across the
+    // scan (the copies hide the equality from the compiler)
+    uint32_t lo2 = lo;
+    float flo2 = flo, fscale2 = fscale;
+    asm volatile("" : "+v"(lo2), "+v"(flo2), "+v"(fscale2));
+    if (cnt <= kCandCap) {
+      // ---- the bin's keys into LDS, exact select among them
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i)
-        if ((vmask >> i) & 1) atomicAdd(&sh.hist[value_bin(u[i], lo, scale)], 1u);
+        if (u[i] - lo2 <= span && level_bin(u[i], lo2, by_value, flo2, fscale2, shift) == bs)
+          sh.cu[atomicAdd(&sh.ncand, 1)] = u[i];
       __syncthreads();
-      // bins from the top: thread t covers bins kBins-1-2t and kBins-2-2t
-      const int b0 = kBins - 1 - 2 * tid, b1 = b0 - 1;
-      const int c0 = (int)sh.hist[b0], c1 = (int)sh.hist[b1];
-      const int incl = block_incl_scan(c0 + c1, sh.wsum);
-      const int excl = incl - c0 - c1;  // keys in bins above b0
-      if (excl < K && excl + c0 >= K) {
-        sh.bstar = b0;
-        sh.rem = K - excl;
-        sh.cnt = c0;
-      } else if (excl + c0 < K && incl >= K) {
-        sh.bstar = b1;
-        sh.rem = K - excl - c0;
-        sh.cnt = c1;
-      }
-      if (tid == 0) sh.ncand = 0;
+      const int nc = sh.ncand;
+      const uint32_t cv[2] = {tid < nc ? sh.cu[tid] : 0u, tid + kTopkThreads < nc ? sh.cu[tid + kTopkThreads] : 0u};
+      const uint64_t cm = (tid < nc ? 1ull : 0ull) | (tid + kTopkThreads < nc ? 2ull : 0ull);
+      const int rb = rem;
       __syncthreads();
-      if (sh.cnt <= kCandCap) {
-        // ---- gather the threshold bin's keys into LDS
-        const int bs = sh.bstar;
+      radix_find<2>(cv, cm, rb, sh, T, rem);
+      break;
+    }
+    // ---- narrow the range to the bin's keys
+    uint32_t nlo = 0xFFFFFFFFu, nhi = 0u;
 #pragma unroll
-        for (int i = 0; i < ITEMS; ++i)
-          if (((vmask >> i) & 1) && value_bin(u[i], lo, scale) == bs) sh.cu[atomicAdd(&sh.ncand, 1)] = u[i];
-        __syncthreads();
-        const int nc = sh.ncand;
-        const uint32_t cv[2] = {tid < nc ? sh.cu[tid] : 0u, tid + kTopkThreads < nc ? sh.cu[tid + kTopkThreads] : 0u};
-        const uint64_t cm = (tid < nc ? 1ull : 0ull) | (tid + kTopkThreads < nc ? 2ull : 0ull);
-        const int remb = sh.rem;
-        __syncthreads();
-        radix_find<2>(cv, cm, remb, sh, T, rem);
-        done = true;
+    for (int i = 0; i < ITEMS; ++i) {
+      if (u[i] - lo2 <= span && level_bin(u[i], lo2, by_value, flo2, fscale2, shift) == bs) {
+        nlo = min(nlo, u[i]);
+        nhi = max(nhi, u[i]);
       }
     }
+    block_minmax(nlo, nhi, sh);
+    lo = nlo;
+    hi = nhi;
   }
-  if (!done) radix_find<ITEMS>(u, vmask, K, sh, T, rem);
 
   // keys equal to T: the first `rem` of them in candidate order are taken
   uint64_t eq = 0, take = 0;
 #pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const bool valid = (vmask >> i) & 1;
-    if (valid && u[i] == T) eq |= 1ull << i;
-    if (valid && u[i] > T) take |= 1ull << i;
+  for (int i = 0; i < ITEMS; ++i) {  // T >= 1: items past n never match
+    if (u[i] == T) eq |= 1ull << i;
+    if (u[i] > T) take |= 1ull << i;
   }
   row_counts<ITEMS>(eq, sh.wtab, sh.rowoff);
 #pragma unroll
@@ -338,22 +360,21 @@ hipError_t launch_topk(const float* keys, long long key_stride, const int32_t* c
   if (n < 1 || K < 1 || K > n) return hipErrorInvalidValue;
   const int items = (n + kTopkThreads - 1) / kTopkThreads;
   dim3 grid(P), block(kTopkThreads);
-#define FL_TOPK(IT, BIN)                                                                                        \
+#define FL_TOPK(IT)                                                                                             \
   do {                                                                                                          \
     if (cand)                                                                                                   \
-      hipLaunchKernelGGL((k_topk<IT, true, BIN>), grid, block, 0, st, keys, key_stride, cand, cand_stride, n, K, \
+      hipLaunchKernelGGL((k_topk<IT, true>), grid, block, 0, st, keys, key_stride, cand, cand_stride, n, K,     \
                          sel_out, sel_stride, keys_out, keys_out_stride);                                       \
     else                                                                                                        \
-      hipLaunchKernelGGL((k_topk<IT, false, BIN>), grid, block, 0, st, keys, key_stride, cand, cand_stride, n,   \
-                         K, sel_out, sel_stride, keys_out, keys_out_stride);                                    \
+      hipLaunchKernelGGL((k_topk<IT, false>), grid, block, 0, st, keys, key_stride, cand, cand_stride, n, K,    \
+                         sel_out, sel_stride, keys_out, keys_out_stride);                                       \
   } while (0)
-  // small problems: radix select directly; larger: value bins first
-  if (items <= 1) FL_TOPK(1, false);
-  else if (items <= 4) FL_TOPK(4, false);
-  else if (items <= 8) FL_TOPK(8, true);
-  else if (items <= 16) FL_TOPK(16, true);
-  else if (items <= 32) FL_TOPK(32, true);
-  else if (items <= 64) FL_TOPK(64, true);
+  if (items <= 1) FL_TOPK(1);
+  else if (items <= 4) FL_TOPK(4);
+  else if (items <= 8) FL_TOPK(8);
+  else if (items <= 16) FL_TOPK(16);
+  else if (items <= 32) FL_TOPK(32);
+  else if (items <= 64) FL_TOPK(64);
   else return hipErrorInvalidValue;
 #undef FL_TOPK
   return hipGetLastError();
