@@ -3,12 +3,14 @@
 //
 // One 1024-thread block per problem.  Keys are mapped to order-preserving
 // uint32 values and held in registers, loaded coalesced: thread t holds the
-// candidates i*1024 + t.  Four 8-bit radix passes (LDS histogram, parallel
-// digit search) find the K-th largest key T and how many keys equal to T are
-// needed; the selection is every key above T plus the first `need` keys equal
-// to T in candidate order.  Ranks in candidate order come from wave ballots
-// and a small per-row table, so the output is ascending and the result is
-// unique.  No floating-point atomics; deterministic.
+// candidates i*1024 + t.  The K-th largest key T, and how many keys equal
+// to T are needed, come from histogram levels over a shrinking key range
+// (2048 bins, one LDS atomic per key) that end in an exact radix select
+// among the at most 2048 keys of one bin.  The selection is every key above
+// T plus the first `need` keys equal to T in candidate order.  Ranks in
+// candidate order come from wave ballots and a small per-row table, so the
+// output is ascending and the result is unique.  No floating-point atomics;
+// deterministic.
 #include "launch.hpp"
 
 namespace fl {
