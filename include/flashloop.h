@@ -199,6 +199,8 @@ fl_status fl_kv_resq(const fl_cache* cache, int r, const void* k, const void* v,
  *   ws       workspace of fl_workspace_bytes(FL_WS_COLSEL, ...) bytes
  * When K_r == K_prev the selection is the candidate set itself; sel_out gets
  * a copy and U, M are left as they are (they already hold M^r, U^r).
+ * A selection that prunes (K_r < K_prev) takes at most 32768 candidates
+ * (K_prev <= 32768; FL_EUNSUPPORTED beyond); keys must not be NaN.
  * Otherwise M^r and U^r of the rows in A_r are written into state.
  * The mass pass runs when it is needed for the selection or mass_out is set.
  */
@@ -239,6 +241,8 @@ fl_status fl_loop_attn(const fl_cache* cache, int r, const void* q, fl_dtype dty
  *           O = U + M softmax_{S_r}(tau q.k^r) v^r, lse, and the new logits
  *           and selection are compacted into state.logits / state.sel.
  *   K_prev S when r == 2, else the K of the previous loop; 1 <= K_r <= K_prev.
+ *   A loop that prunes (K_r < K_prev) takes at most 32768 candidates
+ *   (FL_EUNSUPPORTED beyond).
  */
 fl_status fl_loop_decode(const fl_cache* cache, int r, const void* q, fl_dtype dtype, int K_prev, int K_r,
                          const fl_dstate* state, void* ws, size_t ws_bytes, fl_stream stream);

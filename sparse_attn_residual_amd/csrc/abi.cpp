@@ -101,7 +101,7 @@ fl_status check_state(const char* fn, const fl_state* s) {
   return FL_OK;
 }
 
-constexpr int kTopkMax = 65536;
+constexpr int kTopkMax = 32768;  // keys per selection problem (32 per thread)
 
 }  // namespace
 

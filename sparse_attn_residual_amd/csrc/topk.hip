@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
                                                        const int32_t* cand, long long cand_stride, int n, int K,
                                                        int32_t* sel_out, long long sel_stride, float* keys_out,
                                                        long long keys_out_stride) {
-  static_assert(ITEMS <= 64, "bitmasks hold 64 rows");
+  static_assert(ITEMS <= 32, "at most 32768 keys per problem");
   __shared__ TopkShared sh;
   const int p = blockIdx.x;
   const int tid = threadIdx.x;
@@ -220,16 +220,18 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
 
   // Loads are unconditional (clamped index) so that all of them are issued
   // before the first is waited for; out-of-range items are masked after.
-  // u = 0 marks an item past n (no finite or infinite key maps to 0)
+  // u = 0 marks an item past n (no finite or infinite key maps to 0).
+  // Candidate positions wait in LDS (dynamic, ITEMS * 1024 ints) for the
+  // output stage, which keeps them out of registers.
+  extern __shared__ int32_t sh_idx[];
   uint32_t u[ITEMS];
-  int32_t idx[CAND ? ITEMS : 1];
   {
     float raw[ITEMS];
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
       const int e = min(i * kTopkThreads + tid, n - 1);
       raw[i] = kp[e];
-      if (CAND) idx[i] = cand[(long long)p * cand_stride + e];
+      if (CAND) sh_idx[i * kTopkThreads + tid] = cand[(long long)p * cand_stride + e];
     }
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) u[i] = i * kTopkThreads + tid < n ? order_key(raw[i]) : 0u;
@@ -333,12 +335,16 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
   row_counts<ITEMS>(take, sh.wtab, sh.rowoff);
   int32_t* so = sel_out + (long long)p * sel_stride;
   float* ko = keys_out ? keys_out + (long long)p * keys_out_stride : nullptr;
+  // candidate positions are recomputed here from a copy of tid: otherwise the
+  // compiler keeps all ITEMS of them from the loads and spills them
+  int tid2 = tid;
+  asm volatile("" : "+v"(tid2));
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     const uint64_t m = __ballot((take >> i) & 1);
     const int rk = sh.rowoff[i] + sh.wtab[wv][i] + __popcll(m & below);
     if (((take >> i) & 1) && rk < K) {
-      so[rk] = CAND ? idx[i] : i * kTopkThreads + tid;
+      so[rk] = CAND ? sh_idx[i * kTopkThreads + tid2] : i * kTopkThreads + tid2;
       if (ko) ko[rk] = key_value(u[i]);
     }
   }
@@ -364,19 +370,27 @@ hipError_t launch_topk(const float* keys, long long key_stride, const int32_t* c
   dim3 grid(P), block(kTopkThreads);
 #define FL_TOPK(IT)                                                                                             \
   do {                                                                                                          \
-    if (cand)                                                                                                   \
-      hipLaunchKernelGGL((k_topk<IT, true>), grid, block, 0, st, keys, key_stride, cand, cand_stride, n, K,     \
+    if (cand) {                                                                                                 \
+      const int lds = (IT) * kTopkThreads * (int)sizeof(int32_t);                                               \
+      static bool attr = false;                                                                                 \
+      if (!attr) {                                                                                              \
+        hipError_t e = hipFuncSetAttribute((const void*)k_topk<IT, true>,                                       \
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);                    \
+        if (e != hipSuccess) return e;                                                                          \
+        attr = true;                                                                                            \
+      }                                                                                                         \
+      hipLaunchKernelGGL((k_topk<IT, true>), grid, block, lds, st, keys, key_stride, cand, cand_stride, n, K,   \
                          sel_out, sel_stride, keys_out, keys_out_stride);                                       \
-    else                                                                                                        \
+    } else {                                                                                                    \
       hipLaunchKernelGGL((k_topk<IT, false>), grid, block, 0, st, keys, key_stride, cand, cand_stride, n, K,    \
                          sel_out, sel_stride, keys_out, keys_out_stride);                                       \
+    }                                                                                                           \
   } while (0)
   if (items <= 1) FL_TOPK(1);
   else if (items <= 4) FL_TOPK(4);
   else if (items <= 8) FL_TOPK(8);
   else if (items <= 16) FL_TOPK(16);
   else if (items <= 32) FL_TOPK(32);
-  else if (items <= 64) FL_TOPK(64);
   else return hipErrorInvalidValue;
 #undef FL_TOPK
   return hipGetLastError();

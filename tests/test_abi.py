@@ -106,6 +106,12 @@ def test_validation_errors():
                       None, 0, None)
     assert st == EINVAL and "K_prev" in msg
     assert fl.fl_workspace_bytes(fl.FL_WS_COLSEL, _cache(), 2, 64, 10) == 1 * 2 * 64 * 4
+    # a pruning selection takes at most 32768 candidates
+    big = _cache(S=40000)
+    big.n[1], big.n[2] = 40000, 20000
+    st, msg = _status("fl_colsel", ctypes.byref(big), 2, ok_ptr, fl.FL_F32, ctypes.byref(s), 40000, None, 10,
+                      None, None, ok_ptr, ok_ptr, 1 << 40, None)
+    assert st == EUNSUP and "candidates" in msg
 
 
 def test_binding_raises():
