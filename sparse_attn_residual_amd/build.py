@@ -36,6 +36,38 @@ def source_digest() -> str:
     return h.hexdigest()
 
 
+def resource_usage() -> dict:
+    """Per-kernel register, scratch and occupancy figures reported by the
+    compiler for every kernel source (device compile only)."""
+    import re
+    from concurrent.futures import ThreadPoolExecutor
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+    def one(src):
+        cmd = [hipcc, *[f for f in FLAGS if f != "-shared"], "-I", os.path.join(ROOT, "include"), "-x", "hip",
+               "--cuda-device-only", "-c", src, "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc failed:\n" + res.stderr)
+        out, cur = {}, None
+        for line in res.stderr.splitlines():
+            m = re.search(r"Function Name: (\S+)", line)
+            if m:
+                cur = out.setdefault(m.group(1), {})
+                continue
+            m = re.search(r"remark: ([A-Za-z ]+?)(?: \[[^]]*\])?: (\d+)", line)
+            if m and cur is not None:
+                cur[m.group(1).strip()] = int(m.group(2))
+        return out
+
+    srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+    usage = {}
+    with ThreadPoolExecutor(max_workers=min(4, len(srcs))) as ex:
+        for part in ex.map(one, srcs):
+            usage.update(part)
+    return usage
+
+
 def build_library(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
