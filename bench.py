@@ -30,6 +30,28 @@ if ROOT not in sys.path:
 
 PREFILL_CFG = 2
 DECODE_CFG = 3
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "bench_prefill_s32768_decode_t32768_l48_hbm_traffic.md")
+
+
+def measured_traffic(key):
+    """HBM bytes (read + written) per launch of one kernel, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE profile scaled by its copy calibration;
+    None when the kernel sources changed since that profile was taken."""
+    import re
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(\{.*\})\n```", text)
+    if not m:
+        return None
+    prof = json.loads(m.group(1))
+    from sparse_attn_residual_amd.build import source_digest
+    if prof.get("source_sha256") != source_digest():
+        return None
+    k = prof.get("kernels", {}).get(key)
+    return None if k is None else k["read_bytes"] + k["write_bytes"]
 
 
 def log(*a):
@@ -279,7 +301,8 @@ def main():
             "peak": acc.MI355X_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": pf["dense_tf"] / acc.MI355X_BF16_TFLOPS,
-            "traffic": None,
+            "traffic": measured_traffic("attn1"),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "flops_per_launch": dense_flops,
             "avg_launch_ms": pf["per"]["attn1"],
         },
@@ -303,7 +326,8 @@ def main():
                 "peak": acc.MI355X_HBM_GBS,
                 "unit": "GB/s",
                 "frac": dec["dense_gbs"] / acc.MI355X_HBM_GBS,
-                "traffic": None,
+                "traffic": measured_traffic("decode1"),
+                "algorithmic_bytes": dec["loop_bytes"][0],
                 "step_frac": dec["gbs"] / acc.MI355X_HBM_GBS,
             },
         }

@@ -49,12 +49,34 @@ __device__ inline float group8_sum_dpp(float v) {
 
 constexpr float kDecRescale = 16.0f;  // lazy rescale threshold (natural log units)
 
-// Loop 1: dense over all S cached tokens, d == 128.  The group's softmax
-// keeps a reference maximum that only moves when a score exceeds it by more
-// than kDecRescale, so the accumulators are rescaled rarely.
-template <typename T>
-__global__ __launch_bounds__(kDecThreads) void k_decode_dense(DecodeArgs a, float tau) {
-  __shared__ GroupState gs;
+// Online-softmax state of one 8-lane group (per lane: 16 dims of acc)
+// merged with the group whose lanes are `o` apart (o = 8, 16, 32: the groups
+// of one wavefront, lane by lane over the same dims).
+__device__ inline void merge_groups(float& m, float& l, float* acc, int o) {
+  const float m2 = __shfl_xor(m, o, kWave);
+  const float l2 = __shfl_xor(l, o, kWave);
+  const float mx = fmaxf(m, m2);
+  const float f1 = m == -INFINITY ? 0.0f : __expf(m - mx);
+  const float f2 = m2 == -INFINITY ? 0.0f : __expf(m2 - mx);
+  l = l * f1 + l2 * f2;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = acc[e] * f1 + __shfl_xor(acc[e], o, kWave) * f2;
+  m = mx;
+}
+
+constexpr int kDenseThreads = 512;  // one block per (layer, sequence, head)
+
+// Loop 1: dense over all S cached tokens, d == 128.  A block of NT threads
+// (NT/8 groups of 8 lanes, one token per group per step) walks its slab of
+// S records; the block's waves cover consecutive tokens, so few slabs (and
+// pages) are read at once on the chip.  The group's softmax keeps a
+// reference maximum that only moves when a score exceeds it by more than
+// kDecRescale, so the accumulators are rescaled rarely.  Group states merge
+// within each wavefront by lane shuffles, then across wavefronts in LDS.
+template <typename T, int NT>
+__global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
+  constexpr int NG = NT / 8, NW = NT / kWave;
+  __shared__ float wm[NW], wl[NW], wacc[NW][128];
   const CacheGeo& c = a.c;
   const long long lbh = blockIdx.x;
   const int h = (int)(lbh % c.H);
@@ -75,7 +97,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_dense(DecodeArgs a, floa
   const uint8_t* recs = base_rec(c, l, b, h, 0);
   float* logit = a.logits + lbh * c.S;
   const uint16_t* scl = (const uint16_t*)(recs + 2 * d);
-  for (int j = gid; j < c.S; j += kDecGroups) {
+  for (int j = gid; j < c.S; j += NG) {
     const uint8_t* rec = recs + (long long)j * c.base_rb;
     const uint4 kw = *(const uint4*)(rec + sub * 16);
     const uint4 vw = *(const uint4*)(rec + d + sub * 16);
@@ -103,21 +125,26 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_dense(DecodeArgs a, floa
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = __builtin_fmaf(pv, cv[e], acc[e]);
   }
-  if (sub == 0) {
-    gs.m[gid] = m;
-    gs.l[gid] = lsum;
-  }
+  merge_groups(m, lsum, acc, 8);
+  merge_groups(m, lsum, acc, 16);
+  merge_groups(m, lsum, acc, 32);
+  if (grp == 0) {
+    if (sub == 0) {
+      wm[wv] = m;
+      wl[wv] = lsum;
+    }
 #pragma unroll
-  for (int e = 0; e < 16; ++e) gs.acc[gid][sub * 16 + e] = acc[e];
+    for (int e = 0; e < 16; ++e) wacc[wv][sub * 16 + e] = acc[e];
+  }
   __syncthreads();
   if (threadIdx.x < d) {
     float mx = -INFINITY;
-    for (int gg = 0; gg < kDecGroups; ++gg) mx = fmaxf(mx, gs.m[gg]);
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, wm[w]);
     float L = 0.0f, A = 0.0f;
-    for (int gg = 0; gg < kDecGroups; ++gg) {
-      const float f = gs.m[gg] == -INFINITY ? 0.0f : __expf(gs.m[gg] - mx);
-      L += gs.l[gg] * f;
-      A += gs.acc[gg][threadIdx.x] * f;
+    for (int w = 0; w < NW; ++w) {
+      const float f = wm[w] == -INFINITY ? 0.0f : __expf(wm[w] - mx);
+      L += wl[w] * f;
+      A += wacc[w][threadIdx.x] * f;
     }
     a.O[lbh * d + threadIdx.x] = A / L;
     a.U[lbh * d + threadIdx.x] = 0.0f;
@@ -437,8 +464,12 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   const long long P = (long long)a.c.L * a.c.B * a.c.H;
   const bool bf = a.dt == FL_BF16;
   if (a.r == 1) {
-    if (bf) hipLaunchKernelGGL(k_decode_dense<uint16_t>, dim3((unsigned)P), dim3(kDecThreads), 0, st, a, tau);
-    else hipLaunchKernelGGL(k_decode_dense<float>, dim3((unsigned)P), dim3(kDecThreads), 0, st, a, tau);
+    if (bf)
+      hipLaunchKernelGGL((k_decode_dense<uint16_t, kDenseThreads>), dim3((unsigned)P), dim3(kDenseThreads), 0, st,
+                         a, tau);
+    else
+      hipLaunchKernelGGL((k_decode_dense<float, kDenseThreads>), dim3((unsigned)P), dim3(kDenseThreads), 0, st, a,
+                         tau);
     return hipGetLastError();
   }
   const int pruned = a.K < a.K_prev;
