@@ -558,38 +558,51 @@ struct RowRegs {
   int pos;
 };
 
-__device__ inline void fetch_rows(const CacheGeo& c, const AttnArgs& a, int b, int bh, int t0, RowRegs& R) {
+// Row indices of one 64-row tile, loaded a tile before the row data they
+// address so that no load waits on another inside one tile's time: the
+// position of the thread's query row in q_prev (-1: none) and, for threads
+// < 64, the position of the tile's row t and its slot at loop r-1.
+struct RowIdx {
+  int qi;
+  int i2, q2;
+};
+
+__device__ inline void fetch_idx(const CacheGeo& c, const AttnArgs& a, int b, int t0, RowIdx& X) {
   const int t = threadIdx.x;
-  const int row = t >> 2, qd = t & 3;
   const int r = a.r, rp = r - 1;
   const int nr = c.n[r];
-  const int np = rp == 1 ? c.S : c.n[rp];
-  int tr = t0 + row;
-  int qi = -1, i = -1;
+  const int tr = t0 + (t >> 2);
+  X.qi = -1;
   if (tr < nr) {
-    i = c.rows[r][(long long)b * nr + tr];
-    qi = rp == 1 ? i : c.slot[rp][(long long)b * c.S + i];
+    const int i = c.rows[r][(long long)b * nr + tr];
+    X.qi = rp == 1 ? i : c.slot[rp][(long long)b * c.S + i];
   }
-  if (qi >= 0) {
-    const uint4* src = (const uint4*)((const uint16_t*)a.q + ((long long)bh * np + qi) * kD + qd * 32);
+  X.i2 = -1;
+  X.q2 = -1;
+  if (t < kMassRows && t0 + t < nr) {
+    X.i2 = c.rows[r][(long long)b * nr + t0 + t];
+    X.q2 = rp == 1 ? X.i2 : c.slot[rp][(long long)b * c.S + X.i2];
+  }
+}
+
+__device__ inline void fetch_rows(const CacheGeo& c, const AttnArgs& a, int bh, const RowIdx& X, RowRegs& R) {
+  const int qd = threadIdx.x & 3;
+  const int rp = a.r - 1;
+  const int np = rp == 1 ? c.S : c.n[rp];
+  if (X.qi >= 0) {
+    const uint4* src = (const uint4*)((const uint16_t*)a.q + ((long long)bh * np + X.qi) * kD + qd * 32);
 #pragma unroll
     for (int k = 0; k < 4; ++k) R.q[k] = src[k];
   } else {
 #pragma unroll
     for (int k = 0; k < 4; ++k) R.q[k] = make_uint4(0, 0, 0, 0);
   }
-  R.pos = -1;
+  R.pos = X.i2;
   R.off = INFINITY;
-  if (t < kMassRows) {
-    const int tr2 = t0 + t;
-    if (tr2 < nr) {
-      const int i2 = c.rows[r][(long long)b * nr + tr2];
-      const int q2 = rp == 1 ? i2 : c.slot[rp][(long long)b * c.S + i2];
-      const long long p = (long long)bh * c.S + i2;
-      const float Mp = a.M[p];
-      R.pos = i2;
-      if (q2 >= 0 && Mp > 0.0f) R.off = a.lse[p] * 1.4426950408889634f - __log2f(Mp);
-    }
+  if (X.i2 >= 0) {
+    const long long p = (long long)bh * c.S + X.i2;
+    const float Mp = a.M[p];
+    if (X.q2 >= 0 && Mp > 0.0f) R.off = a.lse[p] * 1.4426950408889634f - __log2f(Mp);
   }
 }
 
@@ -694,15 +707,20 @@ __global__ __launch_bounds__(kThreads) void k_mass_mfma(MassArgs m) {
   const int jmax = sh_jmax;
   float acc = 0.0f;
   RowRegs rr;
+  RowIdx xn;  // indices of tile tt+1
   if (ntl > 0) {
-    fetch_rows(c, a, b, bh, t0, rr);
+    RowIdx x0;
+    fetch_idx(c, a, b, t0, x0);
+    fetch_rows(c, a, bh, x0, rr);
     store_rows(rr, rt[0]);
+    if (ntl > 1) fetch_idx(c, a, b, t0 + kMassRows, xn);
   }
   __syncthreads();
   for (int tt = 0; tt < ntl; ++tt) {
     const RowTile& T = rt[tt & 1];
     const bool more = tt + 1 < ntl;
-    if (more) fetch_rows(c, a, b, bh, t0 + (tt + 1) * kMassRows, rr);
+    if (more) fetch_rows(c, a, bh, xn, rr);
+    if (tt + 2 < ntl) fetch_idx(c, a, b, t0 + (tt + 2) * kMassRows, xn);
     f32x16_t s[2];
     s[0] = s[1] = f32x16_t{};
 #pragma unroll
