@@ -169,17 +169,18 @@ def test_prefill_bf16_mfma_small(S, bits, col):
     _bf16_case(cfg, heads=[0, 1])
 
 
-@pytest.mark.parametrize("cfgid,heads", [(1, [0, 11]), (4, [3])])
+@pytest.mark.parametrize("cfgid,heads", [(1, [0, 11]), (2, [0, 15]), (4, [3])])
 def test_prefill_bf16_full_size(cfgid, heads):
-    """Full-size workloads (all heads on the GPU), oracle on sampled heads."""
+    """Full-size workloads (all heads on the GPU, the launch configuration the
+    benchmark times for the 32K one), oracle on sampled heads."""
     cfg = workloads.CONFIGS[cfgid]
     _say("prefill full size", cfg.name, heads)
     _bf16_case(cfg, heads=heads)
 
 
 def test_prefill_bf16_mfma_wide():
-    """Enough heads that the 64-rows-per-wave kernel runs, with ragged row
-    blocks in the dense loop and in loop 2."""
+    """Enough heads that the eight-wave (256-row block) kernel runs, with
+    ragged row blocks in the dense loop and in loop 2."""
     cfg = workloads.custom(name="bf16-wide", dtype="bf16", B=2, H=40, d=128, S=1000, R=4, act=(1, 0.9, 0.6, 0.3),
                            col="0.25", bits=(8, 4, 2, 4), lognormal=0.5, seed=7)
     _say("prefill bf16 wide", cfg)
