@@ -57,12 +57,10 @@ constexpr int kImgV = kBN * kKP * 2;          // 17408
 constexpr int kImgPos = kImgV + kD * kVP * 2;  // 35840
 constexpr int kImgBytes = 36 * 1024;           // 36864: 36 chunks of 1 KB (36096 used)
 constexpr int kImgChunks = kImgBytes / 1024;
-// Tile ring of the attention kernel: PIPE (the QK^T of the next tile runs
-// under this tile's softmax) keeps four images resident and copies three
-// ahead; the lighter form keeps two (one copied ahead) so that two blocks
-// fit on a CU.
-template <bool PIPE> constexpr int ring_of() { return PIPE ? 4 : 2; }
-template <bool PIPE> constexpr int ahead_of() { return ring_of<PIPE>() - 1; }
+// Tile ring of the attention kernel: two images resident, the next one
+// copied while this one is used (72 KB of LDS).
+constexpr int kRing = 2;
+constexpr int kAhead = kRing - 1;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -217,7 +215,6 @@ __device__ inline void wait_keep() {
 }
 template <int NW>
 __device__ inline void wait_tiles_but(int keep) {
-  // covers up to two tiles in flight (ring of four, three ahead)
   if (keep >= 2) wait_keep<NW, 2>();
   else if (keep == 1) wait_keep<NW, 1>();
   else __builtin_amdgcn_s_waitcnt(0);
@@ -378,14 +375,14 @@ __device__ inline void write_row(const AttnArgs& a, int r, long long bhS, int i,
   }
 }
 
-// NW waves of 32 query rows each (BM = 32 * NW).  Per 64-column tile: the
-// next tile's S^T = K Q^T is issued on the matrix cores while this tile's
-// probabilities are formed on the vector ALUs, then O^T += V^T P^T.  Tile
-// images arrive by direct global->LDS loads issued two tiles ahead into a
-// three-deep ring, so the loop itself writes no LDS.
-template <int NW, int MODE, bool PIPE>
-__global__ __launch_bounds__(64 * NW, PIPE ? 1 : 2) void k_attn_mfma(MfmaArgs m) {
-  constexpr int kRing = ring_of<PIPE>(), kAhead = ahead_of<PIPE>();
+// NW waves of 32 query rows each (BM = 32 * NW).  Per 64-column tile:
+// S^T = K Q^T on the matrix cores, the probabilities on the vector ALUs,
+// then O^T += V^T P^T.  Several waves per SIMD (twelve waves per block, or
+// two blocks of four) let one wave's vector work run under another's matrix
+// work.  Tile images arrive by direct global->LDS loads issued one tile
+// ahead into a two-image ring, so the loop itself writes no LDS.
+template <int NW, int MODE>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_mfma(MfmaArgs m) {
   constexpr int BM = 32 * NW;
   extern __shared__ __align__(16) uint8_t lds[];   // kRing tile images
   __shared__ int sh_ntiles;
@@ -476,40 +473,26 @@ __global__ __launch_bounds__(64 * NW, PIPE ? 1 : 2) void k_attn_mfma(MfmaArgs m)
   __syncthreads();
   const int nt = sh_ntiles;
 
-  // ---- prologue: the first kAhead tiles into the ring (PIPE: S of tile 0)
+  // ---- prologue: the first kAhead tiles into the ring
   for (int k = 0; k < kAhead && k < nt; ++k) dma_tile<NW>(imgs + (long long)k * kImgBytes, lds + k * kImgBytes);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
-  if (PIPE && nt > 0) qk_tile(lds, qf, l32, hf, s0, s1);
 
   for (int tt = 0; tt < nt; ++tt) {
     const uint8_t* T = lds + (tt % kRing) * kImgBytes;
-    const uint8_t* Tn = lds + ((tt + 1) % kRing) * kImgBytes;
     // tile tt+kAhead goes into the slot tile tt-1 left (all waves passed it)
     if (tt + kAhead < nt)
       dma_tile<NW>(imgs + (long long)(tt + kAhead) * kImgBytes, lds + ((tt + kAhead) % kRing) * kImgBytes);
-    if (!PIPE) qk_tile(T, qf, l32, hf, s0, s1);
+    f32x16_t s0, s1;
+    qk_tile(T, qf, l32, hf, s0, s1);
     float x[32];
     softmax_mask(T, s0, s1, ipos, blk_min, hf, x);
-    // PIPE: S of the next tile on the matrix cores while these
-    // probabilities are formed on the vector ALUs (stale data past the last
-    // tile: unused)
-    f32x16_t n0, n1;
-    if (PIPE) qk_tile(Tn, qf, l32, hf, n0, n1);
     // Weights against the current reference (UM: the fixed loop r-1
     // statistics).  ATTN: only if a lane's sum exceeds 2^kRescale (so some
     // weight might) or a valid row has no reference yet is the tile max
     // taken, the lazy rescale applied and the weights formed again.
     f16x8_t pf[4];
     float ls = softmax_probs(x, (MODE == kModeAttn && mref == -INFINITY) ? 0.0f : mref, m.c2, pf);
-    if (PIPE) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // five VALU
-      }
-    }
     if (MODE == kModeAttn) {
       const bool bad = (ipos >= 0 && mref == -INFINITY) || !(ls <= kRescaleP);
       if (__builtin_amdgcn_ballot_w64(bad)) {
@@ -519,12 +502,7 @@ __global__ __launch_bounds__(64 * NW, PIPE ? 1 : 2) void k_attn_mfma(MfmaArgs m)
     }
     lsum += ls;
     pv_tile(T, pf, l32, hf, o);
-    if (PIPE) {
-      s0 = n0;
-      s1 = n1;
-    }
-    // tile tt+1 must be in LDS for every wave; the loop's copies of the
-    // tiles after it (up to tt+kAhead) may stay in flight
+    // tile tt+1 must be in LDS for every wave
     wait_tiles_but<NW>(min(tt + kAhead, nt - 1) - (tt + 1));
     lds_barrier();
   }
@@ -794,36 +772,36 @@ hipError_t launch_gather(const CacheGeo& c, int rc, const int32_t* sel, int K, u
   return hipGetLastError();
 }
 
-template <int NW, int MODE, bool PIPE>
+template <int NW, int MODE>
 static hipError_t launch_one(const MfmaArgs& m, hipStream_t st) {
-  constexpr size_t lds = (size_t)ring_of<PIPE>() * kImgBytes;
+  constexpr size_t lds = (size_t)kRing * kImgBytes;
   static bool attr = false;  // the attribute is per kernel; setting it twice is harmless
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_attn_mfma<NW, MODE, PIPE>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_attn_mfma<NW, MODE>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr = true;
   }
   const int nunits = m.a.c.B * m.a.c.H * m.nblk;
-  hipLaunchKernelGGL((k_attn_mfma<NW, MODE, PIPE>), dim3(nunits), dim3(64 * NW), lds, st, m);
+  hipLaunchKernelGGL((k_attn_mfma<NW, MODE>), dim3(nunits), dim3(64 * NW), lds, st, m);
   return hipGetLastError();
 }
 
-constexpr int kPipeBlocks = 1024;
+constexpr int kWideBlocks = 1024;
 
 static float c2_of(int d) { return (float)(1.4426950408889634 / __builtin_sqrt((double)d)); }
 
-// Row blocks of 256 rows (eight waves, one block per CU, pipelined) when
-// there are enough of them to fill the chip four times over; otherwise 128-row blocks
-// of four waves with a two-image ring, two blocks per CU.
+// 384-row blocks of twelve waves (three per SIMD, one block per CU) when
+// 256-row blocks would fill the chip four times over; otherwise 128-row
+// blocks of four waves, two blocks per CU.
 template <int MODE>
 static hipError_t launch_rows(MfmaArgs& m, int n, hipStream_t st) {
-  if ((long long)m.a.c.B * m.a.c.H * ((n + 255) / 256) >= kPipeBlocks) {
-    m.nblk = (n + 255) / 256;
-    return launch_one<8, MODE, true>(m, st);
+  if ((long long)m.a.c.B * m.a.c.H * ((n + 255) / 256) >= kWideBlocks) {
+    m.nblk = (n + 383) / 384;
+    return launch_one<12, MODE>(m, st);
   }
   m.nblk = (n + 127) / 128;
-  return launch_one<4, MODE, false>(m, st);
+  return launch_one<4, MODE>(m, st);
 }
 
 // Loop-r attention: r == 1 dense over every position, r >= 2 over S_r.

@@ -179,12 +179,13 @@ def test_prefill_bf16_full_size(cfgid, heads):
 
 
 def test_prefill_bf16_mfma_wide():
-    """Enough heads that the eight-wave (256-row block) kernel runs, with
-    ragged row blocks in the dense loop and in loop 2."""
-    cfg = workloads.custom(name="bf16-wide", dtype="bf16", B=2, H=40, d=128, S=1000, R=4, act=(1, 0.9, 0.6, 0.3),
+    """Enough heads that the twelve-wave (384-row block) kernel runs in the
+    dense loop and in loop 2, with ragged row blocks; loops 3 and 4 take the
+    four-wave kernel."""
+    cfg = workloads.custom(name="bf16-wide", dtype="bf16", B=4, H=64, d=128, S=1000, R=4, act=(1, 0.9, 0.6, 0.3),
                            col="0.25", bits=(8, 4, 2, 4), lognormal=0.5, seed=7)
     _say("prefill bf16 wide", cfg)
-    _bf16_case(cfg, heads=[0, 21, 39])
+    _bf16_case(cfg, heads=[0, 37, 63])
 
 
 def _keys(pattern, shape, rng):
