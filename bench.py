@@ -217,6 +217,30 @@ def decode_bench(args, torch, fl, workloads, acc):
                 logits_overhead=logits_overhead, cache_bytes=cache.nbytes())
 
 
+def measured_peaks(torch):
+    """Achievable rate of the vendor library's bf16 GEMM on this GPU (torch
+    .matmul -> hipBLASLt, 16384^3), measured in the same run; the MFMA
+    roofline reports its fraction next to the vendor peak."""
+    n = 16384
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(2):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm = 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    log(f"measured peak: library bf16 GEMM {gemm:.0f} TFLOP/s")
+    return dict(bf16_gemm_tflops=gemm)
+
+
 def cpu_baseline(workloads):
     """The oracle as it stands, on one head of the prefill workload."""
     from oracle import prefill
@@ -265,6 +289,7 @@ def main():
     from sparse_attn_residual_amd import accounting as acc
     import workloads
 
+    peaks = measured_peaks(torch)
     pf = prefill_bench(args, torch, fl, workloads, acc)
     dec = None if args.no_decode else decode_bench(args, torch, fl, workloads, acc)
     cpu = None if args.no_cpu else cpu_baseline(workloads)
@@ -301,6 +326,9 @@ def main():
             "peak": acc.MI355X_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": pf["dense_tf"] / acc.MI355X_BF16_TFLOPS,
+            "measured_peak": peaks["bf16_gemm_tflops"],
+            "measured_peak_kind": "hipBLASLt bf16 GEMM 16384^3 via torch.matmul, same run",
+            "frac_of_measured": pf["dense_tf"] / peaks["bf16_gemm_tflops"],
             "traffic": measured_traffic("attn1"),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "flops_per_launch": dense_flops,
