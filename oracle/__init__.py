@@ -19,6 +19,8 @@ Modules
              part, sparse loop-r update; whole-slice driver
   decode     one decode step per loop over a packed cache
   brute      full-matrix bookkeeping form of the loop recurrences (tiny sizes)
+  active     the next loop's active-token set (relative hidden-state change,
+             top-k, nested)
   accounting byte and FLOP accounting (cache sizes, decode bytes)
 
 Pins (see tests/test_oracle_*.py): brute-force code search, the half-step
