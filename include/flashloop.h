@@ -247,6 +247,28 @@ fl_status fl_loop_attn(const fl_cache* cache, int r, const void* q, fl_dtype dty
 fl_status fl_loop_decode(const fl_cache* cache, int r, const void* q, fl_dtype dtype, int K_prev, int K_r,
                          const fl_dstate* state, void* ws, size_t ws_bytes, fl_stream stream);
 
+/*
+ * fl_select_active — the next loop's active-token set (p1 §4.1 and §D.1:
+ * after the dense early loops, later loops recompute only nested active-token
+ * sets of budget k(r), and tokens outside them reuse their hidden and KV
+ * states; the guide's §3 summary: the tokens updated by the previous loop are
+ * ranked by their normalized hidden-state change and the top k kept).
+ *   h_prev, h_cur [B][S][D] (dtype): hidden states of every position before
+ *            and after the loop just run (rows outside rows_prev are not read)
+ *   rows_prev [B][n_prev] int32 ascending: the active set of that loop; NULL
+ *            means every position (then n_prev must equal S)
+ *   k        budget, 1 <= k <= n_prev; a pruning call (k < n_prev) takes at
+ *            most 32768 candidates (FL_EUNSUPPORTED beyond)
+ *   rows_out [B][k] int32: the k candidates of largest change (ties: lower
+ *            position first), written ascending — the next rows[r] of fl_cache
+ *   score_out [B][n_prev] float32: the change of every candidate, in
+ *            rows_prev order: ||h_cur - h_prev||_2 / ||h_prev||_2 accumulated in
+ *            fp32 (0 for an unmoved token, +inf for a move from a zero state)
+ * D must be a positive multiple of 8; h_prev and h_cur 16-byte aligned.
+ */
+fl_status fl_select_active(int B, int S, int D, const void* h_prev, const void* h_cur, fl_dtype dtype, int n_prev,
+                           const int32_t* rows_prev, int k, int32_t* rows_out, float* score_out, fl_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -71,6 +71,8 @@ def _load():
     lib.fl_loop_attn.restype = I
     lib.fl_loop_decode.argtypes = [cp, I, P, I, I, I, ctypes.POINTER(FlDState), P, S, P]
     lib.fl_loop_decode.restype = I
+    lib.fl_select_active.argtypes = [I, I, I, P, P, I, I, P, I, P, P, P]
+    lib.fl_select_active.restype = I
     return lib
 
 
@@ -140,3 +142,10 @@ def fl_loop_decode(cache: FlCache, r: int, q, dtype: int, K_prev: int, K_r: int,
                    ws_bytes: int = 0, stream=None) -> None:
     _check("fl_loop_decode", _lib.fl_loop_decode(ctypes.byref(cache), r, _ptr(q), dtype, K_prev, K_r,
                                                  ctypes.byref(state), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def fl_select_active(B: int, S: int, D: int, h_prev, h_cur, dtype: int, n_prev: int, rows_prev, k: int, rows_out,
+                     score_out, stream=None) -> None:
+    _check("fl_select_active", _lib.fl_select_active(B, S, D, _ptr(h_prev), _ptr(h_cur), dtype, n_prev,
+                                                     _ptr(rows_prev), k, _ptr(rows_out), _ptr(score_out),
+                                                     _stream(stream)))

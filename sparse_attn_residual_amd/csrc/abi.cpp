@@ -308,4 +308,29 @@ fl_status fl_loop_decode(const fl_cache* cache, int r, const void* q, fl_dtype d
   return FL_OK;
 }
 
+fl_status fl_select_active(int B, int S, int D, const void* h_prev, const void* h_cur, fl_dtype dtype, int n_prev,
+                           const int32_t* rows_prev, int k, int32_t* rows_out, float* score_out, fl_stream stream) {
+  const char* fn = "fl_select_active";
+  g_err.clear();
+  if (B < 1 || S < 1) return fail(FL_EINVAL, "%s: B, S must be >= 1 (got %d, %d)", fn, B, S);
+  if (D < 8 || D % 8 != 0) return fail(FL_EUNSUPPORTED, "%s: hidden size %d (a positive multiple of 8)", fn, D);
+  fl_status s = check_dtype(fn, dtype);
+  if (s != FL_OK) return s;
+  FL_NEED_PTR(h_prev, "h_prev");
+  FL_NEED_PTR(h_cur, "h_cur");
+  FL_NEED_PTR4(rows_out, "rows_out");
+  FL_NEED_PTR4(score_out, "score_out");
+  if (n_prev < 1 || n_prev > S) return fail(FL_EINVAL, "%s: n_prev = %d outside [1, S = %d]", fn, n_prev, S);
+  if (!rows_prev && n_prev != S) return fail(FL_EINVAL, "%s: rows_prev is NULL but n_prev = %d != S", fn, n_prev);
+  if (rows_prev && !aligned4(rows_prev)) return fail(FL_EINVAL, "%s: rows_prev is not 4-byte aligned", fn);
+  if (k < 1 || k > n_prev) return fail(FL_EINVAL, "%s: k = %d outside [1, n_prev = %d]", fn, k, n_prev);
+  if (k < n_prev && n_prev > kTopkMax)
+    return fail(FL_EUNSUPPORTED, "%s: %d candidates (at most %d)", fn, n_prev, kTopkMax);
+  if ((long long)B * S * D > (1LL << 40)) return fail(FL_EUNSUPPORTED, "%s: hidden states too large", fn);
+  hipError_t e = fl::launch_active(B, S, D, h_prev, h_cur, dtype, rows_prev, n_prev, k, rows_out, score_out,
+                                   (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return FL_OK;
+}
+
 }  // extern "C"

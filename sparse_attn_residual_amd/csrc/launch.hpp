@@ -51,6 +51,13 @@ size_t gather_bytes(const CacheGeo& c, int K);
 hipError_t launch_mass(const AttnArgs& a, const int32_t* cand, int K_prev, float* mass, uint8_t* ws,
                        hipStream_t st);
 
+// ---- next active set: scores [B][n_prev] (relative hidden-state change of
+// the candidates rows_prev, NULL: positions 0..n_prev-1), then the top k of
+// each sequence into rows_out [B][k], ascending.
+hipError_t launch_active(int B, int S, int D, const void* h_prev, const void* h_cur, fl_dtype dt,
+                         const int32_t* rows_prev, int n_prev, int k, int32_t* rows_out, float* score,
+                         hipStream_t st);
+
 // ---- decode
 struct DecodeArgs {
   CacheGeo c;

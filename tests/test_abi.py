@@ -21,7 +21,7 @@ def test_library_exports_every_declared_symbol():
     import sparse_attn_residual_amd as fl
     lib = ctypes.CDLL(fl.lib_path())
     names = _declared()
-    assert {"fl_kv_resq", "fl_colsel", "fl_loop_attn", "fl_loop_decode"} <= set(names)
+    assert {"fl_kv_resq", "fl_colsel", "fl_loop_attn", "fl_loop_decode", "fl_select_active"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -111,6 +111,19 @@ def test_validation_errors():
     big.n[1], big.n[2] = 40000, 20000
     st, msg = _status("fl_colsel", ctypes.byref(big), 2, ok_ptr, fl.FL_F32, ctypes.byref(s), 40000, None, 10,
                       None, None, ok_ptr, ok_ptr, 1 << 40, None)
+    assert st == EUNSUP and "candidates" in msg
+    # active-set selection
+    st, msg = _status("fl_select_active", 1, 64, 12, ok_ptr, ok_ptr, fl.FL_F32, 64, None, 10, ok_ptr, ok_ptr, None)
+    assert st == EUNSUP and "hidden size" in msg
+    st, msg = _status("fl_select_active", 1, 64, 16, ok_ptr, ok_ptr, fl.FL_F32, 32, None, 10, ok_ptr, ok_ptr, None)
+    assert st == EINVAL and "rows_prev is NULL" in msg
+    st, msg = _status("fl_select_active", 1, 64, 16, ok_ptr, ok_ptr, fl.FL_F32, 64, None, 65, ok_ptr, ok_ptr, None)
+    assert st == EINVAL and "k = 65" in msg
+    st, msg = _status("fl_select_active", 1, 64, 16, ok_ptr + 4, ok_ptr, fl.FL_F32, 64, None, 10, ok_ptr, ok_ptr,
+                      None)
+    assert st == EINVAL and "h_prev" in msg
+    st, msg = _status("fl_select_active", 1, 40000, 16, ok_ptr, ok_ptr, fl.FL_F32, 40000, None, 10, ok_ptr, ok_ptr,
+                      None)
     assert st == EUNSUP and "candidates" in msg
 
 

@@ -39,6 +39,7 @@ _T_LAM_Q, _T_LAM_K = 4, 5
 _T_ROWS = 6
 _T_DQ, _T_DK, _T_DV = 10, 30, 50   # + loop index r
 _T_DEC_Q, _T_DEC_LAM, _T_DEC_DQ = 70, 71, 80
+_T_HID, _T_HID_EPS, _T_HID_DIR = 90, 91, 92   # + loop index r for the last two
 
 
 def frac_count(f: str | float, n: int) -> int:
@@ -217,3 +218,24 @@ def custom(name="custom", dtype="f32", B=1, H=1, d=64, S=64, R=4, act=(1.0, 0.5,
            bits=(8, 4, 4, 4), gamma=0.5, lognormal=None, seed=0, L=1, decode=False) -> Config:
     """A small ad-hoc configuration (tests: ragged tails, edge cases)."""
     return Config(name, dtype, B, H, d, S, R, tuple(act), str(col), tuple(bits), gamma, lognormal, L, decode, seed)
+
+
+def gen_hidden(cfg: Config, b: int, D: int, r: int, moving) -> tuple[np.ndarray, np.ndarray]:
+    """Synthetic hidden states of sequence b before and after loop r-1,
+    [S, D] float32 rounded to the config dtype.  Tokens in `moving` (the
+    active set of loop r-1) move by a relative step of lognormal size (median
+    2 %, sigma 0.8) in a random direction; the others keep their state, as
+    inactive tokens reuse theirs.  Row magnitudes are lognormal (sigma 0.5)."""
+    S = cfg.S
+    rng = _rng(cfg, _T_HID, b)
+    h = rng.standard_normal((S, D)).astype(np.float32)
+    h *= np.exp(0.5 * rng.standard_normal((S, 1))).astype(np.float32)
+    h_prev = cast(h, cfg.dtype)
+    moving = np.asarray(moving, np.int64)
+    eps = 0.02 * np.exp(0.8 * _rng(cfg, _T_HID_EPS + 100 * r, b).standard_normal(moving.size))
+    u = _rng(cfg, _T_HID_DIR + 100 * r, b).standard_normal((moving.size, D))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    step = (eps * np.linalg.norm(h_prev[moving].astype(np.float64), axis=1))[:, None] * u
+    h_cur = h_prev.copy()
+    h_cur[moving] = cast((h_prev[moving] + step).astype(np.float32), cfg.dtype)
+    return h_prev, h_cur
