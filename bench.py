@@ -217,6 +217,44 @@ def decode_bench(args, torch, fl, workloads, acc):
                 logits_overhead=logits_overhead, cache_bytes=cache.nbytes())
 
 
+def select_bench(args, torch, fl, workloads, acc):
+    """Next active sets of the 32K workload (hidden size H*d = 2048, bf16):
+    one fl_select_active call per loop 2..R, each ranking the previous active
+    set.  Algorithmic bytes: both hidden states of every candidate."""
+    cfg = workloads.CONFIGS[PREFILL_CFG]
+    S, D = cfg.S, cfg.H * cfg.d
+    rows = workloads.active_rows(cfg, 0)
+    hp, hcs = None, []
+    for r in range(2, cfg.R + 1):
+        h_prev, h_cur = workloads.gen_hidden(cfg, 0, D, r, rows[r - 2])
+        if hp is None:
+            hp = _upload(h_prev, torch)
+        hcs.append(_upload(h_cur, torch))
+        del h_prev, h_cur
+    cands = [None] + [torch.from_numpy(rows[r - 2]).cuda() for r in range(3, cfg.R + 1)]
+    outs = [torch.empty(1, cfg.n[r - 1], dtype=torch.int32, device="cuda") for r in range(2, cfg.R + 1)]
+    scores = [torch.empty(1, cfg.n[r - 2], dtype=torch.float32, device="cuda") for r in range(2, cfg.R + 1)]
+    tm = Timer(torch)
+
+    def step(timed):
+        w = tm.wrap if timed else (lambda key, fn: fn())
+        for i, r in enumerate(range(2, cfg.R + 1)):
+            w(f"select{r}", lambda i=i, r=r: fl.fl_select_active(1, S, D, hp, hcs[i], fl.FL_BF16, cfg.n[r - 2],
+                                                                  cands[i], cfg.n[r - 1], outs[i], scores[i]))
+
+    for _ in range(max(1, args.warmup)):
+        step(False)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    per = tm.mean_ms()
+    loop_bytes = {f"select{r}": 2.0 * cfg.n[r - 2] * D * 2 for r in range(2, cfg.R + 1)}
+    gbs = {k: loop_bytes[k] / (per[k] * 1e-3) / 1e9 for k in per}
+    log("select: per loop (ms): " + ", ".join(f"{k}={v:.3f}" for k, v in per.items()))
+    return dict(per=per, bytes=loop_bytes, gbs=gbs, D=D)
+
+
 def measured_peaks(torch):
     """Achievable rate of the vendor library's bf16 GEMM on this GPU (torch
     .matmul -> hipBLASLt, 16384^3), measured in the same run; the MFMA
@@ -291,6 +329,7 @@ def main():
 
     peaks = measured_peaks(torch)
     pf = prefill_bench(args, torch, fl, workloads, acc)
+    sel = select_bench(args, torch, fl, workloads, acc)
     dec = None if args.no_decode else decode_bench(args, torch, fl, workloads, acc)
     cpu = None if args.no_cpu else cpu_baseline(workloads)
 
@@ -333,6 +372,20 @@ def main():
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "flops_per_launch": dense_flops,
             "avg_launch_ms": pf["per"]["attn1"],
+        },
+    }
+    out["select"] = {
+        "workload": f"{cfg.name}: next active sets of loops 2..{cfg.R}, hidden size {sel['D']}, bf16 "
+                    f"(fl_select_active, candidates {cfg.n[:-1]} -> {cfg.n[1:]})",
+        "per_loop_ms": {k: round(v, 4) for k, v in sel["per"].items()},
+        "roofline": {
+            "kernel": "k_active_score + k_topk (fl_select_active, loop 2)",
+            "bound": "hbm",
+            "achieved": sel["gbs"]["select2"],
+            "peak": acc.MI355X_HBM_GBS,
+            "unit": "GB/s",
+            "frac": sel["gbs"]["select2"] / acc.MI355X_HBM_GBS,
+            "algorithmic_bytes": sel["bytes"]["select2"],
         },
     }
     if dec is not None:
