@@ -97,9 +97,20 @@ def prefill_bench(args, torch, fl, workloads, acc):
     rows_l = [np.stack([rows[b][r] for b in range(B)]) for r in range(R)]
     cache = fl.CacheBuffers(1, B, H, S, d, R, cfg.n, cfg.bits, rows_l)
     st = fl.PrefillState(B, H, S, d)
-    Ks = [S] + [min(cfg.K, S) for _ in range(1, R)]
+    res = measure_prefill(args, torch, fl, acc, cfg, rows, q, k, v, cache, st, [cfg.K] * (R - 1))
+    # nested pruning: the budget halves at every loop after the second
+    res["pruned"] = measure_prefill(args, torch, fl, acc, cfg, rows, q, k, v, cache, st,
+                                    [cfg.K >> (r - 2) for r in range(2, R + 1)])
+    return res
+
+
+def measure_prefill(args, torch, fl, acc, cfg, rows, q, k, v, cache, st, budgets):
+    """Time args.steps prefill steps of one layer with column budgets
+    budgets[r-2] for loops r >= 2 (each clipped to the previous loop's)."""
+    R, B, H, S = cfg.R, cfg.B, cfg.H, cfg.S
+    Ks = [S]
     for r in range(2, R + 1):
-        Ks[r - 1] = min(cfg.K, Ks[r - 2])
+        Ks.append(min(budgets[r - 2], Ks[r - 2]))
     sel = [None] + [torch.empty(B, H, Ks[r], dtype=torch.int32, device="cuda") for r in range(1, R)]
     ws_bytes = fl.fl_workspace_bytes(fl.FL_WS_ATTN, cache.fl, 1, S, S)
     for r in range(2, R + 1):
@@ -138,7 +149,7 @@ def prefill_bench(args, torch, fl, workloads, acc):
     wall = time.perf_counter() - wall0
     ms_step = e0.elapsed_time(e1) / args.steps
     per = tm.mean_ms()
-    log(f"prefill: {ms_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}); per call (ms): "
+    log(f"prefill K={Ks[1:]}: {ms_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}); per call (ms): "
         + ", ".join(f"{kk}={vv:.3f}" for kk, vv in per.items()))
 
     # algorithmic work from the index lists of the run
@@ -357,6 +368,12 @@ def main():
             "mfma_frac_whole_step": pf["total_tf"] / acc.MI355X_BF16_TFLOPS,
             "sparse_attn_tflops": pf["sparse_tf"],
             "sparse_attn_mfma_frac": pf["sparse_tf"] / acc.MI355X_BF16_TFLOPS,
+            "pruned_schedule": {
+                "K": pf["pruned"]["Ks"][1:],
+                "ms_per_step": pf["pruned"]["ms_step"],
+                "tokens_per_s": cfg.B * cfg.S / (pf["pruned"]["ms_step"] * 1e-3),
+                "per_call_ms": {k: round(v, 4) for k, v in pf["pruned"]["per"].items()},
+            },
         },
         "roofline": {
             "kernel": "k_attn_mfma (fl_loop_attn r=1, dense causal over the int8 base)",

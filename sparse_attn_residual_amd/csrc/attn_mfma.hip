@@ -78,40 +78,6 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 __device__ inline _Float16 bf16_as_f16(float x) { return (_Float16)round_bf16(x); }
 
 // ------------------------------------------------------------- tile images
-// 32 consecutive dims [g*32, g*32+32) of K (kv = 0) or V (kv = 1) of token j
-// reconstructed at loop rc: the base plus the residuals of the loops <= rc
-// in which j was active, added in fp32 in loop order.
-__device__ inline void chain32(const CacheGeo& c, int rc, int b, int h, int j, int kv, int g, float* x) {
-  const uint8_t* rec = base_rec(c, 0, b, h, j);
-  const uint4 w0 = *(const uint4*)(rec + kv * kD + g * 32);
-  const uint4 w1 = *(const uint4*)(rec + kv * kD + g * 32 + 16);
-  const float s = h2f(((const uint16_t*)(rec + 2 * kD))[kv * 4 + g]);
-  const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-  for (int e = 0; e < 32; ++e) x[e] = (float)(int8_t)(w[e >> 2] >> (8 * (e & 3))) * s;
-  for (int rr = 2; rr <= rc; ++rr) {
-    const int t = c.slot[rr][(long long)b * c.S + j];
-    if (t < 0) break;
-    const uint8_t* rrec = res_rec(c, rr, 0, b, h, t);
-    const int bits = c.bits[rr];
-    const int C = kD * bits / 8;
-    const uint16_t* meta = (const uint16_t*)(rrec + 2 * C);
-    const float rs = h2f(meta[(2 * kv) * 4 + g]);
-    const float rz = h2f(meta[(2 * kv + 1) * 4 + g]);
-    if (bits == 4) {
-      const uint4 pw = *(const uint4*)(rrec + kv * C + g * 16);
-      const uint32_t ws[4] = {pw.x, pw.y, pw.z, pw.w};
-#pragma unroll
-      for (int e = 0; e < 32; ++e) x[e] = x[e] + __builtin_fmaf((float)((ws[e >> 3] >> (4 * (e & 7))) & 15), rs, rz);
-    } else {
-      const uint2 pw = *(const uint2*)(rrec + kv * C + g * 8);
-      const uint32_t ws[2] = {pw.x, pw.y};
-#pragma unroll
-      for (int e = 0; e < 32; ++e) x[e] = x[e] + __builtin_fmaf((float)((ws[e >> 4] >> (2 * (e & 15))) & 3), rs, rz);
-    }
-  }
-}
-
 // One block of 256 threads per tile: columns sel[tile*64 .. +64) (sel NULL:
 // positions tile*64 ..), reconstructed at loop rc, staged in LDS in the image
 // layout and written out with 16-byte stores.  Every packed record a loop
@@ -139,7 +105,7 @@ __global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const i
   const int j = idx < K ? (sel ? sel[(long long)bh * K + idx] : idx) : -1;
   float x[32];
   // K rows (bf16)
-  if (j >= 0) chain32(c, rc, b, h, j, 0, g, x);
+  if (j >= 0) chain_group(c, rc, 0, b, h, j, 0, g, x);
   else {
 #pragma unroll
     for (int e = 0; e < 32; ++e) x[e] = 0.0f;
@@ -152,7 +118,7 @@ __global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const i
                           pack_bf16x2(x[8 * i + 4], x[8 * i + 5]), pack_bf16x2(x[8 * i + 6], x[8 * i + 7]));
   }
   // V^T rows (bf16 value in fp16)
-  if (j >= 0) chain32(c, rc, b, h, j, 1, g, x);
+  if (j >= 0) chain_group(c, rc, 0, b, h, j, 1, g, x);
   else {
 #pragma unroll
     for (int e = 0; e < 32; ++e) x[e] = 0.0f;

@@ -119,6 +119,71 @@ __device__ inline float chain_elem(const CacheGeo& c, int r, int l, int b, int h
   return x;
 }
 
+// The same reconstruction for the 32 dims [32g, 32g+32) of one group, with
+// the records read by vector loads: the operations and their order are those
+// of chain_elem, so the values are the same.
+__device__ inline void chain_group(const CacheGeo& c, int r, int l, int b, int h, int j, int kv, int g, float* x) {
+  const int d = c.d, G = d / kGroup;
+  const uint8_t* rec = base_rec(c, l, b, h, j);
+  const uint4 w0 = *(const uint4*)(rec + kv * d + g * kGroup);
+  const uint4 w1 = *(const uint4*)(rec + kv * d + g * kGroup + 16);
+  const float s = h2f(((const uint16_t*)(rec + 2 * d))[kv * G + g]);
+  const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+  for (int e = 0; e < kGroup; ++e) x[e] = (float)(int8_t)(w[e >> 2] >> (8 * (e & 3))) * s;
+  for (int rr = 2; rr <= r; ++rr) {
+    const int t = c.slot[rr][(long long)b * c.S + j];
+    if (t < 0) break;
+    const uint8_t* q = res_rec(c, rr, l, b, h, t);
+    const int bits = c.bits[rr];
+    const int C = d * bits / 8;
+    const uint16_t* meta = (const uint16_t*)(q + 2 * C);
+    const float rs = h2f(meta[(2 * kv) * G + g]);
+    const float rz = h2f(meta[(2 * kv + 1) * G + g]);
+    if (bits == 4) {
+      const uint4 pw = *(const uint4*)(q + kv * C + g * 16);
+      const uint32_t ws[4] = {pw.x, pw.y, pw.z, pw.w};
+#pragma unroll
+      for (int e = 0; e < kGroup; ++e)
+        x[e] = x[e] + __builtin_fmaf((float)((ws[e >> 3] >> (4 * (e & 7))) & 15), rs, rz);
+    } else {
+      const uint2 pw = *(const uint2*)(q + kv * C + g * 8);
+      const uint32_t ws[2] = {pw.x, pw.y};
+#pragma unroll
+      for (int e = 0; e < kGroup; ++e)
+        x[e] = x[e] + __builtin_fmaf((float)((ws[e >> 4] >> (2 * (e & 15))) & 3), rs, rz);
+    }
+  }
+}
+
+// The 32 input elements [src, src + 32) of one group as floats, read with
+// 16-byte loads (src 16-byte aligned).
+template <typename T> __device__ inline void load_group16(const T* src, float* x);
+template <> __device__ inline void load_group16<uint16_t>(const uint16_t* src, float* x) {
+  const uint4* p = (const uint4*)src;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 w = p[i];
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[8 * i + 2 * k] = __uint_as_float(ws[k] << 16);
+      x[8 * i + 2 * k + 1] = __uint_as_float(ws[k] & 0xffff0000u);
+    }
+  }
+}
+template <> __device__ inline void load_group16<float>(const float* src, float* x) {
+  const float4* p = (const float4*)src;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 w = p[i];
+    x[4 * i] = w.x;
+    x[4 * i + 1] = w.y;
+    x[4 * i + 2] = w.z;
+    x[4 * i + 3] = w.w;
+  }
+}
+
 // ---------------------------------------------------------------- reductions
 __device__ inline float wave_sum(float v) {
 #pragma unroll

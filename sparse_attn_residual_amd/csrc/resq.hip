@@ -13,12 +13,6 @@
 namespace fl {
 
 template <typename T>
-__device__ inline void load_group(const T* src, float* x) {
-#pragma unroll
-  for (int i = 0; i < kGroup; ++i) x[i] = load_elem<T>(src + i);
-}
-
-template <typename T>
 __global__ __launch_bounds__(256) void k_quant_base(const T* __restrict__ k, const T* __restrict__ v,
                                                     uint8_t* __restrict__ base, long long ntok, int d, int rb) {
   const int G = d / kGroup;
@@ -30,7 +24,7 @@ __global__ __launch_bounds__(256) void k_quant_base(const T* __restrict__ k, con
   const int g = sub - kv * G;
   const T* src = (kv ? v : k) + tok * d + g * kGroup;
   float x[kGroup];
-  load_group<T>(src, x);
+  load_group16<T>(src, x);
   float a = 0.0f;
 #pragma unroll
   for (int i = 0; i < kGroup; ++i) a = fmaxf(a, fabsf(x[i]));
@@ -81,14 +75,14 @@ __global__ __launch_bounds__(256) void k_quant_res(CacheGeo c, int r, const T* _
   const int l = (int)(lbh / ((long long)c.H * c.B));
   const int j = c.rows[r][(long long)b * nr + t];
 
-  float x[kGroup];
-  load_group<T>((kv ? v : k) + row * d + g * kGroup, x);
+  float x[kGroup], prev[kGroup];
+  load_group16<T>((kv ? v : k) + row * d + g * kGroup, x);
+  chain_group(c, r - 1, l, b, h, j, kv, g, prev);
   float delta[kGroup];
   float lo = 0.0f, hi = 0.0f;
 #pragma unroll
   for (int i = 0; i < kGroup; ++i) {
-    const float prev = chain_elem(c, r - 1, l, b, h, j, kv, g * kGroup + i);
-    delta[i] = x[i] - prev;
+    delta[i] = x[i] - prev[i];
     lo = i == 0 ? delta[i] : fminf(lo, delta[i]);
     hi = i == 0 ? delta[i] : fmaxf(hi, delta[i]);
   }

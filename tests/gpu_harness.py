@@ -31,6 +31,7 @@ def rows_list(cfg, rows):
 
 def run_prefill(cfg, rows, slices, *, mass_in=None, K_budget=None, mfma=None):
     """All loops of one layer.  mass_in: optional {r: float32 [B][H][K_prev]}.
+    K_budget: one budget for every loop, or a list (loop r uses K_budget[r-2]).
     Returns dict with per-loop snapshots (index r-1), sel, mass and the cache."""
     import sparse_attn_residual_amd as fl
     K_budget = cfg.K if K_budget is None else K_budget
@@ -49,7 +50,7 @@ def run_prefill(cfg, rows, slices, *, mass_in=None, K_budget=None, mfma=None):
         sel = None
         K = 0
         if r >= 2:
-            K = min(K_budget, K_prev)
+            K = min(K_budget[r - 2] if isinstance(K_budget, (list, tuple)) else K_budget, K_prev)
             sel = torch.empty(B, H, K, dtype=torch.int32, device=DEV)
             mass = torch.empty(B, H, K_prev, dtype=torch.float32, device=DEV)
             mi = None
