@@ -156,7 +156,9 @@ size_t fl_residual_record_bytes(int d, int bits);
  *   which = FL_WS_COLSEL: fl_colsel at loop r with K_prev candidates
  *   which = FL_WS_ATTN:   fl_loop_attn at loop r
  *   which = FL_WS_DECODE: fl_loop_decode at loop r
- * A call may be given a larger workspace; 0 means none is needed. */
+ * A call may be given a larger workspace; 0 means none is needed.  For
+ * FL_WS_COLSEL at r == 2 with K_prev == S the size assumes cand == NULL (the
+ * mass pass reads the base records directly). */
 #define FL_WS_COLSEL 1
 #define FL_WS_ATTN 2
 #define FL_WS_DECODE 3

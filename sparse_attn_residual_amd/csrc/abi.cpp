@@ -2,6 +2,7 @@
 // error reporting and kernel dispatch.  Declarations and the meaning of every
 // argument are in include/flashloop.h.  Nothing here allocates device memory;
 // every check happens before the first launch of a call.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -127,15 +128,23 @@ size_t tiles_bytes(const fl_cache* c, int K) {
   g.H = c->H;
   return fl::gather_bytes(g, K);
 }
+// The mass pass: the candidates' tiles unless it reads the base (r == 2 over
+// every position), then the row images of A_r.
+size_t mass_pass_bytes(const fl_cache* c, int r, bool base, int K_prev) {
+  if (c->d != 128) return 0;
+  return (base ? 0 : tiles_bytes(c, K_prev)) + fl::row_img_bytes(c->B, c->H, c->n[r]);
+}
 }  // namespace
 
 size_t fl_workspace_bytes(int which, const fl_cache* cache, int r, int K_prev, int K_r) {
   if (!cache || K_prev < 0 || K_r < 0 || r < 1) return 0;
   if (which == FL_WS_COLSEL) {
-    // the mass pass of r >= 3 (or with explicit candidates) gathers the
-    // candidates' tiles; the cached-mass pass gathers the selected ones
-    const int kt = (r == 2 && K_prev == cache->S) ? K_r : K_prev;
-    return align256((size_t)cache->B * cache->H * (size_t)K_prev * sizeof(float)) + tiles_bytes(cache, kt);
+    // masses, then (in turn) what the mass pass reads and the tiles of the
+    // selected columns the cached-mass pass gathers
+    if (r > cache->R || r < 2) return 0;
+    const bool base = r == 2 && K_prev == cache->S;
+    return align256((size_t)cache->B * cache->H * (size_t)K_prev * sizeof(float)) +
+           std::max(tiles_bytes(cache, K_r), mass_pass_bytes(cache, r, base, K_prev));
   }
   if (which == FL_WS_ATTN) return tiles_bytes(cache, r == 1 ? cache->S : K_r);
   return 0;
@@ -188,9 +197,11 @@ fl_status fl_colsel(const fl_cache* cache, int r, const void* q_prev, fl_dtype d
   const bool need_mass = (prune && !mass_in) || mass_out;
   float* mass = mass_out;
   const size_t mass_ws = align256((size_t)cache->B * cache->H * (size_t)K_prev * sizeof(float));
-  // tiles gathered by the mass pass (all but r == 2 over every position) or the cached-mass pass
-  const int kt = (r == 2 && !cand) ? K_r : K_prev;
-  const size_t need = (need_mass && !mass_out ? mass_ws : 0) + ((prune || need_mass) ? tiles_bytes(cache, kt) : 0);
+  // what the mass pass reads, then (reusing the space) the tiles of the
+  // selected columns the cached-mass pass gathers
+  const size_t pass_ws = std::max(prune ? tiles_bytes(cache, K_r) : 0,
+                                  need_mass ? mass_pass_bytes(cache, r, r == 2 && !cand, K_prev) : 0);
+  const size_t need = (need_mass && !mass_out ? mass_ws : 0) + pass_ws;
   if (need > 0) {
     if (!ws || ws_bytes < need)
       return fail(FL_EINVAL, "%s: workspace of %zu bytes needed (got %zu)", fn, need, ws ? ws_bytes : (size_t)0);

@@ -147,12 +147,18 @@ struct MfmaArgs {
   float c2;               // tau * log2(e)
 };
 
-template <int NW>
-__device__ inline void dma_tile(const uint8_t* img, uint8_t* lds) {
+// Direct global->LDS copy of one image of CH 1 KB chunks, the chunks spread
+// over the block's NW waves (16 bytes per lane and chunk).
+template <int NW, int CH>
+__device__ inline void dma_img(const uint8_t* img, uint8_t* lds) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int ch = wv; ch < kImgChunks; ch += NW)
+  for (int ch = wv; ch < CH; ch += NW)
     __builtin_amdgcn_global_load_lds((gbl_void_t*)(img + ch * 1024 + lane * 16), (lds_void_t*)(lds + ch * 1024), 16,
                                      0, 0);
+}
+template <int NW>
+__device__ inline void dma_tile(const uint8_t* img, uint8_t* lds) {
+  dma_img<NW, kImgChunks>(img, lds);
 }
 
 // Workgroup barrier for the tile ring: the wave's LDS reads have returned
@@ -167,23 +173,28 @@ __device__ inline void lds_barrier() {
 // the wave are outstanding (expcnt and lgkmcnt left unconstrained).
 constexpr int vm_wait_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
-// Wait until the wave's copies of every tile but the last `keep` issued
+// Wait until the wave's copies of every image but the last `keep` issued
 // have landed (in-order completion): the wave issues ceil or floor of
-// kImgChunks / NW chunk loads per tile.
-template <int NW, int K>
+// CH / NW chunk loads per image and no other vector-memory operation in the
+// loops that use these waits.
+template <int NW, int CH, int K>
 __device__ inline void wait_keep() {
-  constexpr int hi = (kImgChunks + NW - 1) / NW, lo = kImgChunks / NW;
+  constexpr int hi = (CH + NW - 1) / NW, lo = CH / NW;
   const int wv = threadIdx.x >> 6;
-  if (wv < kImgChunks - lo * NW || hi == lo)
+  if (wv < CH - lo * NW || hi == lo)
     __builtin_amdgcn_s_waitcnt(vm_wait_imm(K * hi));
   else
     __builtin_amdgcn_s_waitcnt(vm_wait_imm(K * lo));
 }
+template <int NW, int CH>
+__device__ inline void wait_imgs_but(int keep) {
+  if (keep >= 2) wait_keep<NW, CH, 2>();
+  else if (keep == 1) wait_keep<NW, CH, 1>();
+  else __builtin_amdgcn_s_waitcnt(0);
+}
 template <int NW>
 __device__ inline void wait_tiles_but(int keep) {
-  if (keep >= 2) wait_keep<NW, 2>();
-  else if (keep == 1) wait_keep<NW, 1>();
-  else __builtin_amdgcn_s_waitcnt(0);
+  wait_imgs_but<NW, kImgChunks>(keep);
 }
 
 // S^T = K Q^T for one tile: the lane's row against the tile's 64 columns.
@@ -483,99 +494,87 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_mfma(MfmaArgs
 // and §D.2: columns ranked by the preceding loop's attention statistics over
 // the rows loop r recomputes), with P^(r-1)_ij = M_i 2^(x_ij - lse_i log2 e),
 // evaluated as 2^(x_ij - (lse_i log2 e - log2 M_i)).
-// A block owns 128 candidate columns (32 per wave, their K fragments held in
-// registers as the B operand of S = Q K^T, so each lane owns one column) and
-// streams the active rows' loop r-1 queries through LDS in tiles of 64 rows,
-// double buffered.  Column sums accumulate in a fixed order: deterministic.
+// Column-stationary: a block of NW waves owns 32 * NW candidate columns (a
+// lane owns one column; its K fragments stay in registers as the B operand of
+// S = Q K^T).  The rows of A_r are first laid out once per call as 64-row
+// images (k_build_rows: queries of loop r-1, the exponent offset and the
+// position of each row) that every column block then streams through an LDS
+// ring by direct global->LDS loads, as the attention kernel streams its
+// column tiles.  Column sums accumulate in a fixed order: deterministic.
 constexpr int kMassRows = 64;
-constexpr int kThreads = 256;
+// Row image: q [64][kKP] bf16 | off [64] f32 | pos [64] int32, 18 KB.
+//   off = lse * log2(e) - log2(M), P = 2^(x - off); +inf: the row adds nothing
+//   pos = row position, -1 past the last active row
+constexpr int kRowOffAt = kMassRows * kKP * 2;         // 17408
+constexpr int kRowPosAt = kRowOffAt + kMassRows * 4;   // 17664
+constexpr int kRowBytes = 18 * 1024;
+constexpr int kRowChunks = kRowBytes / 1024;
+constexpr int kMassNW = 8;      // waves per block: 256 columns
+constexpr int kMassRing = 3;    // row images resident in LDS (54 KB)
+constexpr int kMassAhead = kMassRing - 1;
 
-struct __align__(16) RowTile {
-  __bf16 q[kMassRows * kKP];
-  float off[kMassRows];   // lse * log2(e) - log2(M): P = 2^(x - off); +inf: the row adds nothing
-  int pos[kMassRows];     // row position (-1 past the last active row)
-};
+size_t row_img_bytes(int B, int H, int n) {
+  return (size_t)B * H * ((n + kMassRows - 1) / kMassRows) * kRowBytes;
+}
+
+// One block of 256 threads per row image: four threads per row, 32 dims each.
+__global__ __launch_bounds__(256) void k_build_rows(AttnArgs a, int ntr, uint8_t* __restrict__ out) {
+  const CacheGeo& c = a.c;
+  const int bh = blockIdx.x / ntr;
+  const int tile = blockIdx.x - bh * ntr;
+  const int b = bh / c.H;
+  const int t = threadIdx.x;
+  const int row = t >> 2, qd = t & 3;
+  const int r = a.r, rp = r - 1;
+  const int nr = c.n[r];
+  const int np = rp == 1 ? c.S : c.n[rp];
+  const int tr = tile * kMassRows + row;
+  int i = -1, qi = -1;
+  if (tr < nr) {
+    i = c.rows[r][(long long)b * nr + tr];
+    qi = rp == 1 ? i : c.slot[rp][(long long)b * c.S + i];
+  }
+  uint4 q4[4];
+  if (qi >= 0) {
+    const uint4* src = (const uint4*)((const uint16_t*)a.q + ((long long)bh * np + qi) * kD + qd * 32);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q4[k] = src[k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q4[k] = make_uint4(0, 0, 0, 0);
+  }
+  uint8_t* img = out + ((long long)bh * ntr + tile) * kRowBytes;
+  uint4* dst = (uint4*)(img + (row * kKP + qd * 32) * 2);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) dst[k] = q4[k];
+  if (qd == 0) {
+    float off = INFINITY;
+    if (qi >= 0) {
+      const long long p = (long long)bh * c.S + i;
+      const float Mp = a.M[p];
+      if (Mp > 0.0f) off = a.lse[p] * 1.4426950408889634f - __log2f(Mp);
+    }
+    ((float*)(img + kRowOffAt))[row] = off;
+    ((int*)(img + kRowPosAt))[row] = i;
+  }
+}
 
 struct MassArgs {
   AttnArgs a;
-  const int32_t* cand;    // NULL: every position (r == 2 over the base)
   int K_prev;
   float* mass;
-  const uint8_t* tiles;   // compact tiles of the candidates (cand != NULL)
+  const uint8_t* tiles;   // compact tiles of the candidates (not read when BASE)
   int ntiles_total;
+  const uint8_t* rows;    // row images [B*H][ntr]
+  int ntr;
   int ncb;                // column blocks per (b, h)
   float c2;
 };
 
-struct RowRegs {
-  uint4 q[4];
-  float off;
-  int pos;
-};
-
-// Row indices of one 64-row tile, loaded a tile before the row data they
-// address so that no load waits on another inside one tile's time: the
-// position of the thread's query row in q_prev (-1: none) and, for threads
-// < 64, the position of the tile's row t and its slot at loop r-1.
-struct RowIdx {
-  int qi;
-  int i2, q2;
-};
-
-__device__ inline void fetch_idx(const CacheGeo& c, const AttnArgs& a, int b, int t0, RowIdx& X) {
-  const int t = threadIdx.x;
-  const int r = a.r, rp = r - 1;
-  const int nr = c.n[r];
-  const int tr = t0 + (t >> 2);
-  X.qi = -1;
-  if (tr < nr) {
-    const int i = c.rows[r][(long long)b * nr + tr];
-    X.qi = rp == 1 ? i : c.slot[rp][(long long)b * c.S + i];
-  }
-  X.i2 = -1;
-  X.q2 = -1;
-  if (t < kMassRows && t0 + t < nr) {
-    X.i2 = c.rows[r][(long long)b * nr + t0 + t];
-    X.q2 = rp == 1 ? X.i2 : c.slot[rp][(long long)b * c.S + X.i2];
-  }
-}
-
-__device__ inline void fetch_rows(const CacheGeo& c, const AttnArgs& a, int bh, const RowIdx& X, RowRegs& R) {
-  const int qd = threadIdx.x & 3;
-  const int rp = a.r - 1;
-  const int np = rp == 1 ? c.S : c.n[rp];
-  if (X.qi >= 0) {
-    const uint4* src = (const uint4*)((const uint16_t*)a.q + ((long long)bh * np + X.qi) * kD + qd * 32);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) R.q[k] = src[k];
-  } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) R.q[k] = make_uint4(0, 0, 0, 0);
-  }
-  R.pos = X.i2;
-  R.off = INFINITY;
-  if (X.i2 >= 0) {
-    const long long p = (long long)bh * c.S + X.i2;
-    const float Mp = a.M[p];
-    if (X.q2 >= 0 && Mp > 0.0f) R.off = a.lse[p] * 1.4426950408889634f - __log2f(Mp);
-  }
-}
-
-__device__ inline void store_rows(const RowRegs& R, RowTile& T) {
-  const int t = threadIdx.x;
-  const int row = t >> 2, qd = t & 3;
-  uint4* dst = (uint4*)&T.q[row * kKP + qd * 32];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) dst[k] = R.q[k];
-  if (t < kMassRows) {
-    T.pos[t] = R.pos;
-    T.off[t] = R.off;
-  }
-}
-
-template <bool BASE>
-__global__ __launch_bounds__(kThreads) void k_mass_mfma(MassArgs m) {
-  __shared__ RowTile rt[2];
+template <bool BASE, int NW>
+__global__ __launch_bounds__(64 * NW) void k_mass_mfma(MassArgs m) {
+  constexpr int W = 32 * NW;
+  extern __shared__ __align__(16) uint8_t lds[];  // kMassRing row images
   __shared__ int sh_t0, sh_jmax;
   const AttnArgs& a = m.a;
   const CacheGeo& c = a.c;
@@ -591,7 +590,7 @@ __global__ __launch_bounds__(kThreads) void k_mass_mfma(MassArgs m) {
   const int b = bh / c.H, h = bh - b * c.H;
 
   // ---- this lane's candidate column: position jpos, candidate index cidx
-  const int cidx = cb * 128 + wv * 32 + l32;
+  const int cidx = cb * W + wv * 32 + l32;
   int jpos = kNoPos;
   bf16x8_t kf[8];
   if (BASE) {
@@ -627,17 +626,20 @@ __global__ __launch_bounds__(kThreads) void k_mass_mfma(MassArgs m) {
       for (int ks = 0; ks < 8; ++ks) kf[ks] = bf16x8_t{};
     }
   }
-  // smallest column position of the block: rows below it see none of them
+  // smallest and largest column position of the block (columns ascend): rows
+  // below the smallest see none of them, rows at or past the largest all
   const int nr = c.n[a.r];
   if (threadIdx.x == 0) {
     int jmin;
     if (BASE) {
-      jmin = cb * 128;
+      jmin = cb * W;
+      sh_jmax = min(cb * W + W - 1, c.S - 1);
     } else {
-      const int ci = cb * 128;
-      const int tile = ci / kBN;
-      const uint8_t* tp = m.tiles + ((long long)bh * m.ntiles_total + tile) * kImgBytes;
-      jmin = ((const int*)(tp + kImgPos))[ci - tile * kBN];
+      const int ci = cb * W, cl = min(cb * W + W - 1, m.K_prev - 1);
+      const uint8_t* t0p = m.tiles + ((long long)bh * m.ntiles_total + ci / kBN) * kImgBytes;
+      const uint8_t* t1p = m.tiles + ((long long)bh * m.ntiles_total + cl / kBN) * kImgBytes;
+      jmin = ((const int*)(t0p + kImgPos))[ci % kBN];
+      sh_jmax = ((const int*)(t1p + kImgPos))[cl % kBN];
     }
     const int32_t* rows = c.rows[a.r] + (long long)b * nr;
     int lo = 0, hi = nr;
@@ -646,54 +648,46 @@ __global__ __launch_bounds__(kThreads) void k_mass_mfma(MassArgs m) {
       if (rows[mid] < jmin) lo = mid + 1; else hi = mid;
     }
     sh_t0 = lo;
-    // largest column position of the block (columns ascend)
-    if (BASE) {
-      sh_jmax = min(cb * 128 + 127, c.S - 1);
-    } else {
-      const int cl = min(cb * 128 + 127, m.K_prev - 1);
-      const int tile = cl / kBN;
-      const uint8_t* tp = m.tiles + ((long long)bh * m.ntiles_total + tile) * kImgBytes;
-      sh_jmax = ((const int*)(tp + kImgPos))[cl - tile * kBN];
-    }
   }
   __syncthreads();
-  const int t0 = sh_t0;
-  const int ntl = (nr - t0 + kMassRows - 1) / kMassRows;
+  const int tile0 = sh_t0 / kMassRows;
+  const int ntl = sh_t0 < nr ? m.ntr - tile0 : 0;
   const int jmax = sh_jmax;
-  float acc = 0.0f;
-  RowRegs rr;
-  RowIdx xn;  // indices of tile tt+1
-  if (ntl > 0) {
-    RowIdx x0;
-    fetch_idx(c, a, b, t0, x0);
-    fetch_rows(c, a, bh, x0, rr);
-    store_rows(rr, rt[0]);
-    if (ntl > 1) fetch_idx(c, a, b, t0 + kMassRows, xn);
-  }
+  const uint8_t* rimg = m.rows + ((long long)bh * m.ntr + tile0) * kRowBytes;
+
+  for (int k = 0; k < kMassAhead && k < ntl; ++k)
+    dma_img<NW, kRowChunks>(rimg + (long long)k * kRowBytes, lds + k * kRowBytes);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+
+  float acc = 0.0f;
   for (int tt = 0; tt < ntl; ++tt) {
-    const RowTile& T = rt[tt & 1];
-    const bool more = tt + 1 < ntl;
-    if (more) fetch_rows(c, a, bh, xn, rr);
-    if (tt + 2 < ntl) fetch_idx(c, a, b, t0 + (tt + 2) * kMassRows, xn);
+    const uint8_t* T = lds + (tt % kMassRing) * kRowBytes;
+    // image tt+kMassAhead goes into the slot image tt-1 left (all waves passed it)
+    if (tt + kMassAhead < ntl)
+      dma_img<NW, kRowChunks>(rimg + (long long)(tt + kMassAhead) * kRowBytes,
+                              lds + ((tt + kMassAhead) % kMassRing) * kRowBytes);
+    const __bf16* tq = (const __bf16*)T;
+    const float* toff = (const float*)(T + kRowOffAt);
+    const int* tpos = (const int*)(T + kRowPosAt);
     f32x16_t s[2];
     s[0] = s[1] = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib) {
-        const bf16x8_t qf = *(const bf16x8_t*)&T.q[(ib * 32 + l32) * kKP + ks * 16 + hf * 8];
+        const bf16x8_t qf = *(const bf16x8_t*)&tq[(ib * 32 + l32) * kKP + ks * 16 + hf * 8];
         s[ib] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf[ks], s[ib], 0, 0, 0);
       }
     }
-    // rows are ascending: once the tile's first row lies at or after the
-    // block's last column, every row of it sees every column (no mask)
-    if (T.pos[0] >= jmax) {
+    // rows ascend: once the image's first row lies at or after the block's
+    // last column, every row of it sees every column (no mask)
+    if (tpos[0] >= jmax) {
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const float4 offv = *(const float4*)&T.off[ib * 32 + 8 * g + 4 * hf];
+          const float4 offv = *(const float4*)&toff[ib * 32 + 8 * g + 4 * hf];
           const float offs[4] = {offv.x, offv.y, offv.z, offv.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -706,8 +700,8 @@ __global__ __launch_bounds__(kThreads) void k_mass_mfma(MassArgs m) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int rbase = ib * 32 + 8 * g + 4 * hf;
-          const float4 offv = *(const float4*)&T.off[rbase];
-          const int4 pv = *(const int4*)&T.pos[rbase];
+          const float4 offv = *(const float4*)&toff[rbase];
+          const int4 pv = *(const int4*)&tpos[rbase];
           const float offs[4] = {offv.x, offv.y, offv.z, offv.w};
           const int ps[4] = {pv.x, pv.y, pv.z, pv.w};
 #pragma unroll
@@ -718,8 +712,9 @@ __global__ __launch_bounds__(kThreads) void k_mass_mfma(MassArgs m) {
         }
       }
     }
-    if (more) store_rows(rr, rt[(tt + 1) & 1]);
-    __syncthreads();
+    // image tt+1 must be in LDS for every wave
+    wait_imgs_but<NW, kRowChunks>(min(tt + kMassAhead, ntl - 1) - (tt + 1));
+    lds_barrier();
   }
   acc += __shfl_xor(acc, 32, 64);
   if (hf == 0 && jpos != kNoPos) m.mass[(long long)bh * m.K_prev + cidx] = acc;
@@ -798,26 +793,48 @@ hipError_t launch_um_mfma(const AttnArgs& a, uint8_t* ws, hipStream_t st) {
 
 // Column mass of the candidates (r == 2 with cand == NULL reads the base
 // directly; otherwise the candidates' chains r-1 are gathered into ws first).
+// ws: [candidate tiles: gather_bytes(c, K_prev), only when gathered]
+//     [row images: row_img_bytes(B, H, n_r)]
+template <bool BASE>
+static hipError_t launch_mass_one(const MassArgs& m, hipStream_t st) {
+  constexpr size_t lds = (size_t)kMassRing * kRowBytes;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_mass_mfma<BASE, kMassNW>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int nunits = m.a.c.B * m.a.c.H * m.ncb;
+  hipLaunchKernelGGL((k_mass_mfma<BASE, kMassNW>), dim3(nunits), dim3(64 * kMassNW), lds, st, m);
+  return hipGetLastError();
+}
+
 hipError_t launch_mass_mfma(const AttnArgs& a, const int32_t* cand, int K_prev, float* mass, uint8_t* ws,
                             hipStream_t st) {
   MassArgs m{};
   m.a = a;
-  m.cand = cand;
   m.K_prev = K_prev;
   m.mass = mass;
   m.c2 = c2_of(a.c.d);
-  m.ncb = (K_prev + 127) / 128;
-  const int nunits = a.c.B * a.c.H * m.ncb;
-  if (!cand && a.r == 2) {  // loop-1 chain = the base records themselves
-    hipLaunchKernelGGL(k_mass_mfma<true>, dim3(nunits), dim3(kThreads), 0, st, m);
-    return hipGetLastError();
+  m.ncb = (K_prev + 32 * kMassNW - 1) / (32 * kMassNW);
+  const bool base = !cand && a.r == 2;  // loop-1 chain = the base records themselves
+  uint8_t* rows = ws;
+  if (!base) {
+    hipError_t e = launch_gather(a.c, a.r - 1, cand, K_prev, ws, st);
+    if (e != hipSuccess) return e;
+    m.tiles = ws;
+    m.ntiles_total = (K_prev + kBN - 1) / kBN;
+    rows = ws + gather_bytes(a.c, K_prev);
   }
-  hipError_t e = launch_gather(a.c, a.r - 1, cand, K_prev, ws, st);
-  if (e != hipSuccess) return e;
-  m.tiles = ws;
-  m.ntiles_total = (K_prev + kBN - 1) / kBN;
-  hipLaunchKernelGGL(k_mass_mfma<false>, dim3(nunits), dim3(kThreads), 0, st, m);
-  return hipGetLastError();
+  m.ntr = (a.c.n[a.r] + kMassRows - 1) / kMassRows;
+  m.rows = rows;
+  if (m.ntr > 0) {
+    hipLaunchKernelGGL(k_build_rows, dim3((unsigned)(a.c.B * a.c.H * m.ntr)), dim3(256), 0, st, a, m.ntr, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return base ? launch_mass_one<true>(m, st) : launch_mass_one<false>(m, st);
 }
 
 }  // namespace fl

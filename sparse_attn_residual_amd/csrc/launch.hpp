@@ -46,8 +46,12 @@ hipError_t launch_attn(const AttnArgs& a, uint8_t* ws, hipStream_t st);
 hipError_t launch_um(const AttnArgs& a, uint8_t* ws, hipStream_t st);
 // Bytes of the gathered tiles of K selected columns (head dim 128).
 size_t gather_bytes(const CacheGeo& c, int K);
+// Bytes of the 64-row images of n rows per (b, h) that the mass pass streams.
+size_t row_img_bytes(int B, int H, int n);
 // Column mass of the candidates cand (NULL: all S) over rows A_r with loop
-// r-1's probabilities.  ws: gather_bytes(c, K_prev) bytes when cand != NULL.
+// r-1's probabilities.  ws (head dim 128, bf16): gather_bytes(c, K_prev)
+// bytes when the candidates are gathered (cand != NULL or r > 2), then
+// row_img_bytes(B, H, n_r).
 hipError_t launch_mass(const AttnArgs& a, const int32_t* cand, int K_prev, float* mass, uint8_t* ws,
                        hipStream_t st);
 
