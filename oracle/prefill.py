@@ -12,7 +12,7 @@ Follows the FlashLoop pages step by step, in float64:
     describes the update as a low-rank fix of the previous output, the
     paper's eq. 3, whose formula the pages do not print).
 
-Reading of the unprinted eq. 3 (the design doc lists every reading): with
+Reading of the unprinted eq. 3: with
 J_i = {j in S_r : j <= i} and P^(r-1) the probabilities that loop r-1 left,
   M^r_i = sum_{J_i} P^(r-1)_ij                         (cached mass)
   U^r_i = O^(r-1)_i - sum_{J_i} P^(r-1)_ij v~^(r-1)_j  (reused part)
@@ -140,6 +140,67 @@ def sparse_update(rows_r, sel, qfull, kt, vt, st: LoopState, tau):
         st.lse[ri[~has]] = -np.inf
 
 
+def selected_log_mass(rows_r, sel, qfull_prev, kt_prev, tau):
+    """L^r_i = log sum_{J_i} exp(tau q^(r-1)_i . k~^(r-1)_j), the loop r-1
+    logits of the selected columns as one log-sum-exp (-inf when J_i is
+    empty).  Only the exact mixed-logit combine uses it."""
+    L = np.full(rows_r.shape[0], -np.inf)
+    for i0 in range(0, rows_r.shape[0], ROW_BLOCK):
+        ri = rows_r[i0:i0 + ROW_BLOCK]
+        s = tau * (qfull_prev[ri] @ kt_prev[sel].T)
+        s[sel[None, :] > ri[:, None]] = -np.inf
+        m = s.max(axis=1)
+        has = np.isfinite(m)
+        L[i0:i0 + ROW_BLOCK][has] = m[has] + np.log(np.exp(s[has] - m[has][:, None]).sum(axis=1))
+    return L
+
+
+def sparse_update_mixed(rows_r, sel, qfull, kt, vt, st: LoopState, Lsel, tau):
+    """Exact mixed-logit combine, the ablation of the mass-rescaled one: a
+    single softmax over loop r's logits on J_i and the logits loop r-1's
+    distribution held everywhere else (p1 §4.2 names the renormalization this
+    avoids; the pages do not print it).  With Z_i the normalizer of loop r-1's
+    distribution over all columns, Z_i = exp(L^r_i) / M^r_i, and
+    b_i = log sum_{J_i} exp(tau q^r_i . k~^r_j), A_i = softmax_{J_i}(...) v~^r:
+      O^r_i = (U^r_i Z_i + e^{b_i} A_i) / ((1 - M^r_i) Z_i + e^{b_i})
+            = (U^r_i + M^r_i rho_i A_i) / (1 - M^r_i + M^r_i rho_i),  rho_i = e^{b_i - L^r_i}.
+    The state keeps O = U + M A with M = M^r rho / D, U = U^r / D (D the
+    denominator) and lse = b, so loop r's probabilities P^r = M e^{x - lse}
+    on J_i are those of the combined softmax.  Rows whose J_i is empty keep O
+    (lse = -inf); rows with M^r_i = 0 combine as in the mass-rescaled rule."""
+    for i0 in range(0, rows_r.shape[0], ROW_BLOCK):
+        ri = rows_r[i0:i0 + ROW_BLOCK]
+        Li = Lsel[i0:i0 + ROW_BLOCK]
+        s = tau * (qfull[ri] @ kt[sel].T)
+        s[sel[None, :] > ri[:, None]] = -np.inf
+        m = s.max(axis=1, keepdims=True)
+        has = np.isfinite(m[:, 0])
+        e = np.zeros_like(s)
+        e[has] = np.exp(s[has] - m[has])
+        l = e.sum(axis=1, keepdims=True)
+        b = np.full(ri.shape[0], -np.inf)
+        b[has] = (m[has] + np.log(l[has]))[:, 0]
+        for t in np.nonzero(has)[0]:
+            i = ri[t]
+            A = (e[t] / l[t, 0]) @ vt[sel]
+            Mi = st.M[i]
+            if Mi > 0 and np.isfinite(Li[t]):
+                g = np.log(Mi) + b[t] - Li[t]          # log(M rho)
+                if g > 0:
+                    D = (1.0 - Mi) * np.exp(-g) + 1.0
+                    st.O[i] = (st.U[i] * np.exp(-g) + A) / D
+                    st.U[i] = st.U[i] * np.exp(-g) / D
+                    st.M[i] = 1.0 / D
+                else:
+                    D = 1.0 - Mi + np.exp(g)
+                    st.O[i] = (st.U[i] + np.exp(g) * A) / D
+                    st.U[i] = st.U[i] / D
+                    st.M[i] = np.exp(g) / D
+            else:
+                st.O[i] = st.U[i] + Mi * A
+        st.lse[ri] = b
+
+
 def _full_rows(S, rows, x):
     """Scatter a compact per-loop tensor to position-indexed rows (others 0)."""
     out = np.zeros((S, x.shape[1]))
@@ -159,13 +220,14 @@ def identity_chain(x: list, rows: list):
 
 
 def prefill_slice(rows, q, k, v, *, K_budget, bits, dtype, sel_force=None, stop_after=None,
-                  quantize=True):
+                  quantize=True, combine="mass"):
     """Run every loop of one (b, h) slice.
 
     rows[r-1], q[r-1], k[r-1], v[r-1]: loop-r active rows and compact inputs
     (loop 1 covers every row).  sel_force: optional {r: sel} that replaces the
     oracle's own selection at loop r (teacher forcing after near ties).
-    Returns a dict of per-loop results (index r-1)."""
+    combine: "mass" (the method's mass-rescaled update) or "mixed" (the exact
+    mixed-logit ablation).  Returns a dict of per-loop results (index r-1)."""
     R = len(q)
     S, d = k[0].shape
     tau = softmax_scale(d)
@@ -195,8 +257,14 @@ def prefill_slice(rows, q, k, v, *, K_budget, bits, dtype, sel_force=None, stop_
             sel = np.asarray(sel_force[r + 1], dtype=np.int32)
         else:
             sel = topk(mass, cand, K)
-        cached_mass_and_reuse(rr, sel.astype(np.int64), qf[r - 1], kt[r - 1], vt[r - 1], st, tau)
-        sparse_update(rr, sel.astype(np.int64), qf[r], kt[r], vt[r], st, tau)
+        sl = sel.astype(np.int64)
+        Lsel = selected_log_mass(rr, sl, qf[r - 1], kt[r - 1], tau) if combine == "mixed" else None
+        cached_mass_and_reuse(rr, sl, qf[r - 1], kt[r - 1], vt[r - 1], st, tau)
+        if combine == "mixed":
+            sparse_update_mixed(rr, sl, qf[r], kt[r], vt[r], st, Lsel, tau)
+            out.setdefault("lsel", [None] * R)[r] = Lsel
+        else:
+            sparse_update(rr, sl, qf[r], kt[r], vt[r], st, tau)
         out["state"].append(st.copy())
         out["sel"].append(sel)
         out["mass"].append(mass)

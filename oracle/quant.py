@@ -13,7 +13,7 @@ dimensions of one (token, head) row;
   * residual: b-bit asymmetric codes in [0, 2^b - 1] (b = 4 or 2), one fp16
     scale and one fp16 zero (a float offset) per group.
 
-Readings where the pages are silent (all listed in the design doc):
+Readings where the pages are silent:
   * scale = fp16 rounded *up* of (range / levels), zero = fp16 rounded *down*
     of the group minimum, so every element stays within half a step;
   * codes: fp32 divide (IEEE, round to nearest even), round half to even,
