@@ -116,12 +116,27 @@ typedef struct fl_cache {
  *   O, U  [B][H][S][d] float32     output and reused part
  *   M     [B][H][S] float32        cached mass of the selected columns
  *   lse   [B][H][S] float32        log-sum-exp of the last recomputation
- *                                  (-inf when a row had no column left) */
+ *                                  (-inf when a row had no column left)
+ *   lsel  [B][H][S] float32 or NULL.  NULL: the method's mass-rescaled
+ *         combine (above).  Non-NULL selects the exact mixed-logit combine,
+ *         an ablation (p1 §4.2 names the renormalization the method avoids):
+ *         fl_colsel's cached-mass pass also stores
+ *           L^r_i = log sum_{J_i} exp(tau q^(r-1)_i . k~^(r-1)_j)
+ *         and fl_loop_attn forms one softmax over loop r's logits on J_i and
+ *         the logits loop r-1's distribution held elsewhere:
+ *           O^r_i = (U^r_i + M^r_i rho_i A_i) / (1 - M^r_i + M^r_i rho_i),
+ *           rho_i = exp(lse^r_i - L^r_i), A_i = softmax_{J_i}(...) v~^r,
+ *         then keeps O = U + M A with M = M^r rho / D, U = U^r / D (D the
+ *         denominator), so loop r's probabilities M e^{x - lse} on J_i are
+ *         those of the combined softmax.  Rows with M^r_i = 0 combine as in
+ *         the mass-rescaled rule.  Both calls of a loop must use the same
+ *         setting.  Decode always uses the mass-rescaled combine. */
 typedef struct fl_state {
   float* O;
   float* U;
   float* M;
   float* lse;
+  float* lsel;
 } fl_state;
 
 /* Decode state of one new token per (layer, sequence, head).
@@ -200,7 +215,8 @@ fl_status fl_kv_resq(const fl_cache* cache, int r, const void* k, const void* v,
  *            (mass descending, position ascending), written ascending
  *   ws       workspace of fl_workspace_bytes(FL_WS_COLSEL, ...) bytes
  * When K_r == K_prev the selection is the candidate set itself; sel_out gets
- * a copy and U, M are left as they are (they already hold M^r, U^r).
+ * a copy and U, M are left as they are (they already hold M^r, U^r); with
+ * state->lsel set, lsel receives a copy of lse (which then holds L^r).
  * A selection that prunes (K_r < K_prev) takes at most 32768 candidates
  * (K_prev <= 32768; FL_EUNSUPPORTED beyond); keys must not be NaN.
  * Otherwise M^r and U^r of the rows in A_r are written into state.

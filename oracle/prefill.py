@@ -167,7 +167,10 @@ def sparse_update_mixed(rows_r, sel, qfull, kt, vt, st: LoopState, Lsel, tau):
     The state keeps O = U + M A with M = M^r rho / D, U = U^r / D (D the
     denominator) and lse = b, so loop r's probabilities P^r = M e^{x - lse}
     on J_i are those of the combined softmax.  Rows whose J_i is empty keep O
-    (lse = -inf); rows with M^r_i = 0 combine as in the mass-rescaled rule."""
+    (lse = -inf); rows with M^r_i = 0 combine as in the mass-rescaled rule.
+    Returns D per row of rows_r (1 where the mass-rescaled rule applies): the
+    reused part enters O divided by it, so errors in U^r grow by 1/D."""
+    denom = np.ones(rows_r.shape[0])
     for i0 in range(0, rows_r.shape[0], ROW_BLOCK):
         ri = rows_r[i0:i0 + ROW_BLOCK]
         Li = Lsel[i0:i0 + ROW_BLOCK]
@@ -186,6 +189,7 @@ def sparse_update_mixed(rows_r, sel, qfull, kt, vt, st: LoopState, Lsel, tau):
             Mi = st.M[i]
             if Mi > 0 and np.isfinite(Li[t]):
                 g = np.log(Mi) + b[t] - Li[t]          # log(M rho)
+                denom[i0 + t] = 1.0 - Mi + np.exp(g)
                 if g > 0:
                     D = (1.0 - Mi) * np.exp(-g) + 1.0
                     st.O[i] = (st.U[i] * np.exp(-g) + A) / D
@@ -199,6 +203,7 @@ def sparse_update_mixed(rows_r, sel, qfull, kt, vt, st: LoopState, Lsel, tau):
             else:
                 st.O[i] = st.U[i] + Mi * A
         st.lse[ri] = b
+    return denom
 
 
 def _full_rows(S, rows, x):
@@ -261,8 +266,9 @@ def prefill_slice(rows, q, k, v, *, K_budget, bits, dtype, sel_force=None, stop_
         Lsel = selected_log_mass(rr, sl, qf[r - 1], kt[r - 1], tau) if combine == "mixed" else None
         cached_mass_and_reuse(rr, sl, qf[r - 1], kt[r - 1], vt[r - 1], st, tau)
         if combine == "mixed":
-            sparse_update_mixed(rr, sl, qf[r], kt[r], vt[r], st, Lsel, tau)
+            D = sparse_update_mixed(rr, sl, qf[r], kt[r], vt[r], st, Lsel, tau)
             out.setdefault("lsel", [None] * R)[r] = Lsel
+            out.setdefault("denom", [None] * R)[r] = D
         else:
             sparse_update(rr, sl, qf[r], kt[r], vt[r], st, tau)
         out["state"].append(st.copy())

@@ -33,7 +33,8 @@ class FlCache(ctypes.Structure):
 
 
 class FlState(ctypes.Structure):
-    _fields_ = [("O", ctypes.c_void_p), ("U", ctypes.c_void_p), ("M", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
+    _fields_ = [("O", ctypes.c_void_p), ("U", ctypes.c_void_p), ("M", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("lsel", ctypes.c_void_p)]
 
 
 class FlDState(ctypes.Structure):

@@ -81,15 +81,21 @@ class CacheBuffers:
 
 
 class PrefillState:
-    def __init__(self, B, H, S, d, device="cuda"):
+    """mixed=True adds the lsel buffer, which selects the exact mixed-logit
+    combine (an ablation of the mass-rescaled one)."""
+
+    def __init__(self, B, H, S, d, device="cuda", mixed=False):
         self.O = torch.zeros(B, H, S, d, dtype=torch.float32, device=device)
         self.U = torch.zeros(B, H, S, d, dtype=torch.float32, device=device)
         self.M = torch.ones(B, H, S, dtype=torch.float32, device=device)
         self.lse = torch.zeros(B, H, S, dtype=torch.float32, device=device)
-        self.fl = FlState(self.O.data_ptr(), self.U.data_ptr(), self.M.data_ptr(), self.lse.data_ptr())
+        self.lsel = torch.full((B, H, S), float("-inf"), dtype=torch.float32, device=device) if mixed else None
+        self.fl = FlState(self.O.data_ptr(), self.U.data_ptr(), self.M.data_ptr(), self.lse.data_ptr(),
+                          self.lsel.data_ptr() if mixed else None)
 
     def snapshot(self):
-        return {k: getattr(self, k).clone() for k in ("O", "U", "M", "lse")}
+        keys = ("O", "U", "M", "lse") + (("lsel",) if self.lsel is not None else ())
+        return {k: getattr(self, k).clone() for k in keys}
 
 
 class DecodeState:

@@ -99,6 +99,7 @@ fl_status check_state(const char* fn, const fl_state* s) {
   FL_NEED_PTR(s->U, "state->U");
   FL_NEED_PTR4(s->M, "state->M");
   FL_NEED_PTR4(s->lse, "state->lse");
+  if (s->lsel && !aligned4(s->lsel)) return fail(FL_EINVAL, "%s: state->lsel is not 4-byte aligned", fn);
   return FL_OK;
 }
 
@@ -221,6 +222,7 @@ fl_status fl_colsel(const fl_cache* cache, int r, const void* q_prev, fl_dtype d
   a.dt = dtype;
   a.q = q_prev;
   a.O = state->O; a.U = state->U; a.M = state->M; a.lse = state->lse;
+  a.lsel = state->lsel;
   hipError_t e;
   if (need_mass) {
     e = fl::launch_mass(a, cand, K_prev, mass, tiles_ws, st);
@@ -230,6 +232,11 @@ fl_status fl_colsel(const fl_cache* cache, int r, const void* q_prev, fl_dtype d
   if (!prune) {
     e = fl::launch_copy_sel(cand, P, K_prev, sel_out, st);
     if (e != hipSuccess) return hip_fail(e, fn);
+    // same columns as loop r-1: their loop r-1 log-sum-exp is loop r-1's lse
+    if (state->lsel) {
+      e = hipMemcpyAsync(state->lsel, state->lse, (size_t)P * cache->S * sizeof(float), hipMemcpyDeviceToDevice, st);
+      if (e != hipSuccess) return hip_fail(e, fn);
+    }
     return FL_OK;
   }
   const float* keys = mass_in ? mass_in : mass;
@@ -271,6 +278,7 @@ fl_status fl_loop_attn(const fl_cache* cache, int r, const void* q, fl_dtype dty
   a.K = r >= 2 ? K_r : 0;
   a.sel = r >= 2 ? sel : nullptr;
   a.O = state->O; a.U = state->U; a.M = state->M; a.lse = state->lse;
+  a.lsel = state->lsel;
   hipError_t e = fl::launch_attn(a, (uint8_t*)ws, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, fn);
   return FL_OK;

@@ -314,6 +314,31 @@ __device__ inline void write_row(const AttnArgs& a, int r, long long bhS, int i,
         a.lse[bhS + i] = (mref + __log2f(lt)) * 0.6931471805599453f;
         a.M[bhS + i] = 1.0f;
       }
+    } else if (lt > 0.0f && a.lsel) {
+      const float b2 = (mref + __log2f(lt)) * 0.6931471805599453f;
+      float cu, ca;
+      mixed_coeffs(a.M[bhS + i], b2, a.lsel[bhS + i], cu, ca);
+      const float sc = ca / lt;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int dcol = db * 32 + qq * 8 + hf * 4;
+          const f32x4_t uv = *(const f32x4_t*)&a.U[rowp + dcol];
+          f32x4_t ov, un;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            un[e] = cu * uv[e];
+            ov[e] = un[e] + sc * o[db][qq * 4 + e];
+          }
+          *(f32x4_t*)&a.O[rowp + dcol] = ov;
+          *(f32x4_t*)&a.U[rowp + dcol] = un;
+        }
+      }
+      if (hf == 0) {
+        a.lse[bhS + i] = b2;
+        a.M[bhS + i] = ca;
+      }
     } else if (lt > 0.0f) {
       const float Mi = a.M[bhS + i];
       const float sc = Mi / lt;
@@ -348,7 +373,11 @@ __device__ inline void write_row(const AttnArgs& a, int r, long long bhS, int i,
         *(f32x4_t*)&a.U[rowp + dcol] = uv;
       }
     }
-    if (hf == 0) a.M[bhS + i] = Mu * lt;
+    if (hf == 0) {
+      a.M[bhS + i] = Mu * lt;
+      // loop r-1 log-sum-exp over J_i (the mixed-logit combine reads it)
+      if (a.lsel) a.lsel[bhS + i] = lt > 0.0f ? (mref + __log2f(lt)) * 0.6931471805599453f : -INFINITY;
+    }
   }
 }
 

@@ -86,6 +86,21 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a, float tau) {
       a.lse[pos] = m + logf(l);
       a.M[pos] = 1.0f;
     }
+  } else if (l > 0.0f && a.lsel) {
+    const float b2 = m + logf(l);
+    float cu, ca;
+    mixed_coeffs(a.M[pos], b2, a.lsel[pos], cu, ca);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const long long o = pos * d + lane * E + e;
+      const float u = cu * a.U[o];
+      a.O[o] = u + ca * (acc[e] / l);
+      a.U[o] = u;
+    }
+    if (lane == 0) {
+      a.lse[pos] = b2;
+      a.M[pos] = ca;
+    }
   } else if (l > 0.0f) {
     const float Mi = a.M[pos];
 #pragma unroll
@@ -126,7 +141,7 @@ __global__ __launch_bounds__(256) void k_um_valu(AttnArgs a, float tau) {
   load_row<T, E>((const T*)a.q + (((long long)b * c.H + h) * nprev + qi) * d, lane, q);
   const long long pos = ((long long)b * c.H + h) * c.S + i;
   const float Mp = a.M[pos], lp = a.lse[pos];
-  float sum = 0.0f, C[E];
+  float sum = 0.0f, ez = 0.0f, C[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) C[e] = 0.0f;
   if (Mp > 0.0f) {
@@ -137,8 +152,10 @@ __global__ __launch_bounds__(256) void k_um_valu(AttnArgs a, float tau) {
       float kk[E], vv[E];
       load_kv<E>(c, r - 1, b, h, j, lane, bf16, kk, vv);
       const float s = tau * dot_lanes<E>(q, kk);
-      const float P = Mp * expf(s - lp);
+      const float x = expf(s - lp);
+      const float P = Mp * x;
       sum += P;
+      ez += x;
 #pragma unroll
       for (int e = 0; e < E; ++e) C[e] = __builtin_fmaf(P, vv[e], C[e]);
     }
@@ -148,7 +165,11 @@ __global__ __launch_bounds__(256) void k_um_valu(AttnArgs a, float tau) {
     const long long o = pos * d + lane * E + e;
     a.U[o] = a.O[o] - C[e];
   }
-  if (lane == 0) a.M[pos] = sum;
+  if (lane == 0) {
+    a.M[pos] = sum;
+    // loop r-1 log-sum-exp over J_i (the mixed-logit combine reads it)
+    if (a.lsel) a.lsel[pos] = ez > 0.0f ? lp + logf(ez) : -INFINITY;
+  }
 }
 
 // Column mass of the candidates, one wave per candidate column.

@@ -184,6 +184,30 @@ template <> __device__ inline void load_group16<float>(const float* src, float* 
   }
 }
 
+// Coefficients of the mixed-logit row update O = cu U + ca A (A the softmax
+// of loop r over J_i, b its log-sum-exp, M the cached mass, L the loop r-1
+// log-sum-exp over J_i): one softmax over the new logits on J_i and the old
+// ones elsewhere, cu = 1 / D, ca = M rho / D with rho = e^{b - L} and
+// D = 1 - M + M rho, formed without overflow.  Rows with M = 0 or L = -inf
+// keep the mass-rescaled coefficients (cu = 1, ca = M).
+__device__ inline void mixed_coeffs(float M, float b, float L, float& cu, float& ca) {
+  cu = 1.0f;
+  ca = M;
+  if (!(M > 0.0f) || !(L > -INFINITY)) return;
+  const float g = logf(M) + (b - L);  // log(M rho)
+  if (g > 0.0f) {
+    const float e = expf(-g);
+    const float D = (1.0f - M) * e + 1.0f;
+    cu = e / D;
+    ca = 1.0f / D;
+  } else {
+    const float e = expf(g);
+    const float D = (1.0f - M) + e;
+    cu = 1.0f / D;
+    ca = e / D;
+  }
+}
+
 // ---------------------------------------------------------------- reductions
 __device__ inline float wave_sum(float v) {
 #pragma unroll

@@ -37,6 +37,7 @@ struct AttnArgs {
   float* U;
   float* M;
   float* lse;
+  float* lsel;           // NULL: mass-rescaled combine; else the mixed-logit ablation
 };
 // Loop r attention (dense when r == 1, sparse otherwise).  ws: workspace of
 // gather_bytes(c, K) bytes for the gathered column tiles (sparse loops).

@@ -29,15 +29,16 @@ def rows_list(cfg, rows):
     return [np.stack([rows[b][r] for b in range(cfg.B)]) for r in range(cfg.R)]
 
 
-def run_prefill(cfg, rows, slices, *, mass_in=None, K_budget=None, mfma=None):
+def run_prefill(cfg, rows, slices, *, mass_in=None, K_budget=None, mfma=None, mixed=False):
     """All loops of one layer.  mass_in: optional {r: float32 [B][H][K_prev]}.
     K_budget: one budget for every loop, or a list (loop r uses K_budget[r-2]).
+    mixed: the exact mixed-logit combine (the state carries lsel).
     Returns dict with per-loop snapshots (index r-1), sel, mass and the cache."""
     import sparse_attn_residual_amd as fl
     K_budget = cfg.K if K_budget is None else K_budget
     R, B, H, S, d = cfg.R, cfg.B, cfg.H, cfg.S, cfg.d
     cache = fl.CacheBuffers(1, B, H, S, d, R, cfg.n, cfg.bits, rows_list(cfg, rows))
-    st = fl.PrefillState(B, H, S, d)
+    st = fl.PrefillState(B, H, S, d, mixed=mixed)
     dt = fl_dtype(cfg)
     qs = [upload(workloads.stack_loop(cfg, slices, r, "q"), cfg) for r in range(1, R + 1)]
     out = dict(state=[], sel=[None], mass=[None], cache=cache, q=qs)

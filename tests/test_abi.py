@@ -91,6 +91,10 @@ def test_validation_errors():
     st, msg = _status("fl_colsel", ctypes.byref(_cache()), 2, ok_ptr, fl.FL_F32, ctypes.byref(s), 64, None, 10,
                       None, None, ok_ptr, None, 0, None)
     assert st == EINVAL and "workspace" in msg
+    bad = fl.FlState(ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr + 2)
+    st, msg = _status("fl_loop_attn", ctypes.byref(_cache()), 2, ok_ptr, fl.FL_F32, 10, ok_ptr, ctypes.byref(bad),
+                      None, 0, None)
+    assert st == EINVAL and "lsel" in msg
     st, msg = _status("fl_colsel", ctypes.byref(_cache()), 1, ok_ptr, fl.FL_F32, ctypes.byref(s), 64, None, 10,
                       None, None, ok_ptr, None, 0, None)
     assert st == EINVAL

@@ -13,7 +13,7 @@ def _say(*a):
     print("[case]", *a, flush=True)
 
 
-def _oracle_slices(cfg, rows, slices, gpu, heads):
+def _oracle_slices(cfg, rows, slices, gpu, heads, combine="mass"):
     """Oracle per (b, h), teacher-forced with the GPU's selections."""
     res = {}
     for b in range(cfg.B):
@@ -21,7 +21,7 @@ def _oracle_slices(cfg, rows, slices, gpu, heads):
             s = slices[(b, h)]
             force = {r + 1: gpu["sel"][r][b, h] for r in range(1, cfg.R)}
             res[(b, h)] = prefill.prefill_slice(s.rows, s.q, s.k, s.v, K_budget=cfg.K, bits=cfg.bits,
-                                                dtype=cfg.dtype, sel_force=force)
+                                                dtype=cfg.dtype, sel_force=force, combine=combine)
     return res
 
 
@@ -142,14 +142,14 @@ def test_prefill_deterministic():
         assert np.array_equal(a["mass"][r], b["mass"][r])
 
 
-def _bf16_case(cfg, heads, sel_eps=2e-3, budgets=None, tol=2e-3, rel=True):
+def _bf16_case(cfg, heads, sel_eps=2e-3, budgets=None, tol=2e-3, rel=True, combine="mass", check=True):
     """budgets: optional per-loop K (loop r uses budgets[r-2]); the oracle is
     teacher-forced with the GPU's selections, which must match its own up to
     near ties of the masses."""
     import tests.gpu_harness as gh
     rows, slices = workloads.gen_batch(cfg, heads=None)
-    gpu = gh.run_prefill(cfg, rows, slices, K_budget=list(budgets) if budgets else None)
-    orc = _oracle_slices(cfg, rows, slices, gpu, heads)
+    gpu = gh.run_prefill(cfg, rows, slices, K_budget=list(budgets) if budgets else None, mixed=combine == "mixed")
+    orc = _oracle_slices(cfg, rows, slices, gpu, heads, combine=combine)
     _check_records(cfg, gpu, orc, heads)
     for b in range(cfg.B):
         for h in heads:
@@ -161,7 +161,8 @@ def _bf16_case(cfg, heads, sel_eps=2e-3, budgets=None, tol=2e-3, rel=True):
                 ok, ndiff = gh.near_tie_ok(gpu["sel"][r][b, h], own, m, cand, sel_eps)
                 assert ok, (b, h, r + 1, ndiff)
                 cand = gpu["sel"][r][b, h]
-    _check_outputs(cfg, gpu, orc, heads, tol, rel=rel)
+    if check:
+        _check_outputs(cfg, gpu, orc, heads, tol, rel=rel)
     return gpu, orc
 
 
@@ -267,3 +268,53 @@ def test_prefill_dense_second_loop():
         assert np.max(np.abs(g["M"][0, h][act] - 1.0)) <= 1e-5
         U, O = g["U"][0, h][act], g["O"][0, h][act]
         assert np.linalg.norm(U) <= 2e-3 * np.linalg.norm(O), np.linalg.norm(U) / np.linalg.norm(O)
+
+
+@pytest.mark.parametrize("dtype,d,budgets", [("f32", 64, (680, 350, 140)), ("f32", 64, (680, 680, 300)),
+                                             ("bf16", 128, (680, 350, 140)), ("bf16", 128, (680, 680, 300))])
+def test_prefill_mixed_combine(dtype, d, budgets):
+    """The exact mixed-logit combine (ablation): O, lse, M, U and the loop
+    r-1 log-sum-exp over the selected columns, against the oracle's mixed
+    rule; pruning loops and an unpruned loop (lsel copied from lse)."""
+    cfg = workloads.custom(name="prefill-mixed", dtype=dtype, B=2, H=3, d=d, S=1700, R=4, act=(1, 0.5, 0.3, 0.15),
+                           col="0.40", bits=(8, 4, 2, 4), lognormal=0.5 if dtype == "bf16" else None, seed=21)
+    _say("prefill mixed combine", dtype, budgets, cfg)
+    f32 = dtype == "f32"
+    tol = 1e-5 if f32 else 2e-3
+    gpu, orc = _bf16_case(cfg, heads=[0, 2], sel_eps=1e-5 if f32 else 2e-3, budgets=list(budgets), tol=tol,
+                          rel=not f32, combine="mixed", check=f32)
+    rows = {b: workloads.active_rows(cfg, b) for b in range(cfg.B)}
+    for b in range(cfg.B):
+        for h in (0, 2):
+            o = orc[(b, h)]
+            w = np.ones(cfg.S)
+            for r in range(1, cfg.R):
+                g = gpu["state"][r]
+                st = o["state"][r]
+                U = g["U"][b, h]
+                rr = rows[b][r]
+                if f32:
+                    assert np.max(np.abs(U - st.U)) <= tol, (b, h, r + 1, "U")
+                else:
+                    # The reused part U^r is formed by a cancellation (O^(r-1)
+                    # minus the selected columns' share) with the bf16/fp16
+                    # operands' error, which the mass-rescaled rule passes on
+                    # unscaled; the mixed rule divides it by D_i (the oracle's
+                    # denominator), and loop r inherits loop r-1's error through
+                    # O^(r-1), so rows are compared with weights
+                    # prod_{t <= r} max(1, 1/D^t_i).
+                    w[rr] *= np.maximum(1.0, 1.0 / o["denom"][r])
+                    for key, ref in (("O", st.O), ("U", st.U)):
+                        e = np.linalg.norm((g[key][b, h] - ref) / w[:, None])
+                        assert e <= tol * np.linalg.norm(st.O), (b, h, r + 1, key, e / np.linalg.norm(st.O))
+                    assert np.max(np.abs(g["M"][b, h] - st.M) / w) <= 4 * tol, (b, h, r + 1, "M")
+                    fin = np.isfinite(st.lse)
+                    assert np.array_equal(fin, np.isfinite(g["lse"][b, h]))
+                    assert np.max(np.abs(g["lse"][b, h][fin] - st.lse[fin])) <= \
+                        8 * tol * max(1, np.max(np.abs(st.lse[fin])))
+                want, got = o["lsel"][r], g["lsel"][b, h][rr]
+                fin = np.isfinite(want)
+                assert np.array_equal(fin, np.isfinite(got)), (b, h, r + 1)
+                err = np.max(np.abs(got[fin] - want[fin])) if fin.any() else 0.0
+                assert err <= (tol if f32 else 8 * tol) * max(1.0, np.max(np.abs(want[fin]), initial=0.0)), \
+                    (b, h, r + 1, "lsel", err)
