@@ -76,8 +76,13 @@ typedef void* fl_stream;
  * the engine keeps the base and the residuals as packed streams).  Index r of every
  * loop array is the loop number (index 0 is unused).
  *
- *   L, B, H, S, d, R   layers, sequences, heads, tokens, head dim (64 or 128),
- *                      loops (1..FL_MAX_LOOPS)
+ *   L, B, H, S, d, R   layers, sequences, query heads, tokens, head dim (64
+ *                      or 128), loops (1..FL_MAX_LOOPS)
+ *   Hkv                key/value heads (0: H).  H must be a multiple of it;
+ *                      query head h reads KV head h / (H / Hkv) (grouped-query
+ *                      attention, a serving variant the pages leave open).
+ *                      Queries, states, masses and selections are per query
+ *                      head; the streams below are per KV head.
  *   n[r]               active rows per sequence at loop r (n[1] == S), the
  *                      same for every sequence
  *   bits[r]            residual code width of loop r: 4 or 2 (bits[1] == 8)
@@ -85,8 +90,8 @@ typedef void* fl_stream;
  *                      (rows[1] unused: every row)
  *   slot[r]            [B][S] int32: index of position j in rows[r], or -1.
  *                      Written by fl_kv_resq(r); read by the other calls.
- *   base               [L][B][H][S] base records (fl_base_record_bytes(d) each)
- *   res[r]             [L][B][H][n_r] residual records of loop r
+ *   base               [L][B][Hkv][S] base records (fl_base_record_bytes(d) each)
+ *   res[r]             [L][B][Hkv][n_r] residual records of loop r
  *                      (fl_residual_record_bytes(d, bits[r]) each), in rows[r]
  *                      order
  *
@@ -110,6 +115,7 @@ typedef struct fl_cache {
   int32_t* slot[FL_MAX_LOOPS + 1];
   uint8_t* base;
   uint8_t* res[FL_MAX_LOOPS + 1];
+  int Hkv;
 } fl_cache;
 
 /* Per-row prefill state, position indexed (one layer: the cache's L must be 1).
@@ -182,10 +188,10 @@ size_t fl_workspace_bytes(int which, const fl_cache* cache, int r, int K_prev, i
 /*
  * fl_kv_resq — quantize and pack loop r's keys and values (p1 §4.3 and §D.3;
  * guide §3: residuals X^(r) - X_hat^(r-1) of the active tokens only).
- *   r == 1: k, v are [L][B][H][S][d] (dtype); writes cache->base.
+ *   r == 1: k, v are [L][B][Hkv][S][d] (dtype); writes cache->base.
  *           Per group of 32: s = fp16 rounded up of (max|x| / 127) (fp32
  *           divide); code = clamp(rint(x / s), -127, 127), 0 when s == 0.
- *   r >= 2: k, v are [L][B][H][n_r][d] in rows[r] order (the loop-r values of
+ *   r >= 2: k, v are [L][B][Hkv][n_r][d] in rows[r] order (the loop-r values of
  *           the active rows); writes cache->res[r] and cache->slot[r].
  *           delta = x - x_hat^(r-1) (fp32); z = fp16 rounded down of min(delta);
  *           s = fp16 rounded up of ((max(delta) - z) / (2^b - 1));

@@ -29,6 +29,7 @@ class FlCache(ctypes.Structure):
         ("n", ctypes.c_int * _N), ("bits", ctypes.c_int * _N),
         ("rows", ctypes.c_void_p * _N), ("slot", ctypes.c_void_p * _N),
         ("base", ctypes.c_void_p), ("res", ctypes.c_void_p * _N),
+        ("Hkv", ctypes.c_int),
     ]
 
 

@@ -14,16 +14,18 @@ def _dev_i32(x, device):
 class CacheBuffers:
     """A packed cross-loop cache of L layers and the FlCache struct pointing at it.
 
-    rows[r-1]: int32 [B][n_r] active positions of loop r (loop 1 ignored)."""
+    rows[r-1]: int32 [B][n_r] active positions of loop r (loop 1 ignored).
+    Hkv: key/value heads (None: H); the streams are [L][B][Hkv][...]."""
 
-    def __init__(self, L, B, H, S, d, R, n, bits, rows, device="cuda"):
+    def __init__(self, L, B, H, S, d, R, n, bits, rows, device="cuda", Hkv=None):
         assert R <= FL_MAX_LOOPS and len(n) == R and len(bits) == R
         self.L, self.B, self.H, self.S, self.d, self.R = L, B, H, S, d, R
+        self.Hkv = H if Hkv is None else Hkv   # heads of the streams
         self.n, self.bits = list(n), list(bits)
         self.base_rb = fl_base_record_bytes(d)
         self.res_rb = [0] + [fl_residual_record_bytes(d, bits[r]) for r in range(1, R)]
-        self.base = torch.empty(L * B * H * S * self.base_rb, dtype=torch.uint8, device=device)
-        self.res = [None] + [torch.empty(L * B * H * n[r] * self.res_rb[r], dtype=torch.uint8, device=device)
+        self.base = torch.empty(L * B * self.Hkv * S * self.base_rb, dtype=torch.uint8, device=device)
+        self.res = [None] + [torch.empty(L * B * self.Hkv * n[r] * self.res_rb[r], dtype=torch.uint8, device=device)
                              for r in range(1, R)]
         self.rows = [None] + [_dev_i32(rows[r], device).reshape(B, n[r]) for r in range(1, R)]
         self.slot = [None] + [torch.full((B, S), -1, dtype=torch.int32, device=device) for _ in range(1, R)]
@@ -32,7 +34,8 @@ class CacheBuffers:
     def _struct(self, layer, L):
         c = FlCache()
         c.L, c.B, c.H, c.S, c.d, c.R = L, self.B, self.H, self.S, self.d, self.R
-        per_base = self.B * self.H * self.S * self.base_rb
+        c.Hkv = self.Hkv
+        per_base = self.B * self.Hkv * self.S * self.base_rb
         c.base = self.base.data_ptr() + layer * per_base
         for r in range(1, self.R + 1):
             c.n[r] = self.n[r - 1]
@@ -40,7 +43,7 @@ class CacheBuffers:
             if r >= 2:
                 c.rows[r] = self.rows[r - 1].data_ptr()
                 c.slot[r] = self.slot[r - 1].data_ptr()
-                per = self.B * self.H * self.n[r - 1] * self.res_rb[r - 1]
+                per = self.B * self.Hkv * self.n[r - 1] * self.res_rb[r - 1]
                 c.res[r] = self.res[r - 1].data_ptr() + layer * per
         return c
 
@@ -50,31 +53,31 @@ class CacheBuffers:
 
     def seq_view(self, layer: int, b: int) -> FlCache:
         """One layer and one sequence (L = B = 1): the records of (layer, b) are
-        contiguous in the [L][B][H][...] layout."""
+        contiguous in the [L][B][Hkv][...] layout."""
         c = self._struct(layer, 1)
         c.B = 1
-        c.base += b * self.H * self.S * self.base_rb
+        c.base += b * self.Hkv * self.S * self.base_rb
         for r in range(2, self.R + 1):
             c.rows[r] += b * self.n[r - 1] * 4
             c.slot[r] += b * self.S * 4
-            c.res[r] += b * self.H * self.n[r - 1] * self.res_rb[r - 1]
+            c.res[r] += b * self.Hkv * self.n[r - 1] * self.res_rb[r - 1]
         return c
 
     def replicate_layer0(self):
         """Copy layer 0's records into every other layer."""
-        per_base = self.B * self.H * self.S * self.base_rb
+        per_base = self.B * self.Hkv * self.S * self.base_rb
         b = self.base.view(self.L, per_base)
         b[1:].copy_(b[0:1].expand(self.L - 1, per_base))
         for r in range(1, self.R):
-            per = self.B * self.H * self.n[r] * self.res_rb[r]
+            per = self.B * self.Hkv * self.n[r] * self.res_rb[r]
             x = self.res[r].view(self.L, per)
             x[1:].copy_(x[0:1].expand(self.L - 1, per))
 
     def base_records(self) -> torch.Tensor:
-        return self.base.view(self.L, self.B, self.H, self.S, self.base_rb)
+        return self.base.view(self.L, self.B, self.Hkv, self.S, self.base_rb)
 
     def res_records(self, r: int) -> torch.Tensor:
-        return self.res[r - 1].view(self.L, self.B, self.H, self.n[r - 1], self.res_rb[r - 1])
+        return self.res[r - 1].view(self.L, self.B, self.Hkv, self.n[r - 1], self.res_rb[r - 1])
 
     def nbytes(self) -> int:
         return self.base.numel() + sum(x.numel() for x in self.res[1:])

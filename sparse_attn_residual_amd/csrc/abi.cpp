@@ -52,6 +52,9 @@ fl_status check_cache(const char* fn, const fl_cache* c, int r, bool need_res_r,
   if (c->R < 1 || c->R > FL_MAX_LOOPS) return fail(FL_EINVAL, "%s: R = %d outside [1, %d]", fn, c->R, FL_MAX_LOOPS);
   if (r < 1 || r > c->R) return fail(FL_EINVAL, "%s: loop r = %d outside [1, R = %d]", fn, r, c->R);
   if (c->n[1] != c->S) return fail(FL_EINVAL, "%s: n[1] = %d must equal S = %d", fn, c->n[1], c->S);
+  const int hkv = c->Hkv == 0 ? c->H : c->Hkv;
+  if (hkv < 1 || c->H % hkv != 0)
+    return fail(FL_EINVAL, "%s: Hkv = %d must divide H = %d", fn, c->Hkv, c->H);
   if ((long long)c->L * c->B * c->H * c->S > (1LL << 40)) return fail(FL_EUNSUPPORTED, "%s: cache too large", fn);
   FL_NEED_PTR(c->base, "cache->base");
   const int last = need_res_r ? r : r - 1;
@@ -75,6 +78,8 @@ fl_status check_cache(const char* fn, const fl_cache* c, int r, bool need_res_r,
   }
   *geo = fl::CacheGeo{};
   geo->L = c->L; geo->B = c->B; geo->H = c->H; geo->S = c->S; geo->d = c->d; geo->R = c->R;
+  geo->Hkv = hkv;
+  geo->G = c->H / hkv;
   geo->base = c->base;
   geo->base_rb = fl::base_record_bytes(c->d);
   for (int rr = 1; rr <= c->R; ++rr) {

@@ -96,16 +96,20 @@ static_assert(vt_col(0) == 0 && vt_col(4) == 8 && vt_col(8) == 4 && vt_col(12) =
 __global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const int32_t* __restrict__ sel, int K,
                                                      int ntiles, uint8_t* __restrict__ out) {
   __shared__ __align__(16) uint8_t img[kImgBytes];
+  // sel NULL: the tiles of positions 0..K-1 are the same for every query
+  // head of a KV head, so they are built once per (b, KV head)
   const int bh = blockIdx.x / ntiles;
   const int tile = blockIdx.x - bh * ntiles;
-  const int b = bh / c.H, h = bh - b * c.H;
+  const int nh = sel ? c.H : c.Hkv;
+  const int b = bh / nh;
+  const int hk = sel ? kv_head(c, bh - b * nh) : bh - b * nh;
   const int t = threadIdx.x;
   const int col = t >> 2, g = t & 3;
   const int idx = tile * kBN + col;
   const int j = idx < K ? (sel ? sel[(long long)bh * K + idx] : idx) : -1;
   float x[32];
   // K rows (bf16)
-  if (j >= 0) chain_group(c, rc, 0, b, h, j, 0, g, x);
+  if (j >= 0) chain_group(c, rc, 0, b, hk, j, 0, g, x);
   else {
 #pragma unroll
     for (int e = 0; e < 32; ++e) x[e] = 0.0f;
@@ -118,7 +122,7 @@ __global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const i
                           pack_bf16x2(x[8 * i + 4], x[8 * i + 5]), pack_bf16x2(x[8 * i + 6], x[8 * i + 7]));
   }
   // V^T rows (bf16 value in fp16)
-  if (j >= 0) chain_group(c, rc, 0, b, h, j, 1, g, x);
+  if (j >= 0) chain_group(c, rc, 0, b, hk, j, 1, g, x);
   else {
 #pragma unroll
     for (int e = 0; e < 32; ++e) x[e] = 0.0f;
@@ -412,7 +416,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_mfma(MfmaArgs
   const int nrows = dense ? c.S : c.n[r];
   const int row0 = blk * BM;
   const long long bhS = (long long)bh * c.S;
-  const uint8_t* imgs = m.tiles + (long long)bh * m.ntiles_total * kImgBytes;
+  // loop 1 reads the tiles of its KV head (built once per KV head)
+  const long long tbh = dense ? (long long)b * c.Hkv + kv_head(c, bh - b * c.H) : bh;
+  const uint8_t* imgs = m.tiles + tbh * m.ntiles_total * kImgBytes;
 
   // ---- the lane's row and its queries (B operand of S^T = K Q^T)
   int ipos = -1;
@@ -594,6 +600,7 @@ struct MassArgs {
   float* mass;
   const uint8_t* tiles;   // compact tiles of the candidates (not read when BASE)
   int ntiles_total;
+  int tiles_kv;           // tiles built per (b, KV head): no candidate list
   const uint8_t* rows;    // row images [B*H][ntr]
   int ntr;
   int ncb;                // column blocks per (b, h)
@@ -617,6 +624,8 @@ __global__ __launch_bounds__(64 * NW) void k_mass_mfma(MassArgs m) {
   const int bh = u / m.ncb;
   const int cb = u - bh * m.ncb;
   const int b = bh / c.H, h = bh - b * c.H;
+  // candidate tiles built without a candidate list are per (b, KV head)
+  const long long tbh = m.tiles_kv ? (long long)b * c.Hkv + kv_head(c, h) : bh;
 
   // ---- this lane's candidate column: position jpos, candidate index cidx
   const int cidx = cb * W + wv * 32 + l32;
@@ -625,7 +634,7 @@ __global__ __launch_bounds__(64 * NW) void k_mass_mfma(MassArgs m) {
   if (BASE) {
     if (cidx < c.S) {
       jpos = cidx;
-      const uint8_t* rec = base_rec(c, 0, b, h, cidx);
+      const uint8_t* rec = base_rec(c, 0, b, kv_head(c, h), cidx);
       const uint16_t* sc = (const uint16_t*)(rec + 2 * kD);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
@@ -645,7 +654,7 @@ __global__ __launch_bounds__(64 * NW) void k_mass_mfma(MassArgs m) {
   } else {
     const int tile = cidx / kBN, col = cidx - tile * kBN;
     if (cidx < m.K_prev) {
-      const uint8_t* tp = m.tiles + ((long long)bh * m.ntiles_total + tile) * kImgBytes;
+      const uint8_t* tp = m.tiles + ((long long)tbh * m.ntiles_total + tile) * kImgBytes;
       jpos = ((const int*)(tp + kImgPos))[col];
       const bf16x8_t* kr = (const bf16x8_t*)(tp + col * kKP * 2);
 #pragma unroll
@@ -665,8 +674,8 @@ __global__ __launch_bounds__(64 * NW) void k_mass_mfma(MassArgs m) {
       sh_jmax = min(cb * W + W - 1, c.S - 1);
     } else {
       const int ci = cb * W, cl = min(cb * W + W - 1, m.K_prev - 1);
-      const uint8_t* t0p = m.tiles + ((long long)bh * m.ntiles_total + ci / kBN) * kImgBytes;
-      const uint8_t* t1p = m.tiles + ((long long)bh * m.ntiles_total + cl / kBN) * kImgBytes;
+      const uint8_t* t0p = m.tiles + ((long long)tbh * m.ntiles_total + ci / kBN) * kImgBytes;
+      const uint8_t* t1p = m.tiles + ((long long)tbh * m.ntiles_total + cl / kBN) * kImgBytes;
       jmin = ((const int*)(t0p + kImgPos))[ci % kBN];
       sh_jmax = ((const int*)(t1p + kImgPos))[cl % kBN];
     }
@@ -758,7 +767,8 @@ size_t gather_bytes(const CacheGeo& c, int K) {
 // Tile images of K columns (sel NULL: positions 0..K-1) at loop rc.
 hipError_t launch_gather(const CacheGeo& c, int rc, const int32_t* sel, int K, uint8_t* out, hipStream_t st) {
   const int nt = (K + kBN - 1) / kBN;
-  hipLaunchKernelGGL(k_build_tiles, dim3((unsigned)(c.B * c.H * nt)), dim3(256), 0, st, c, rc, sel, K, nt, out);
+  const int nh = sel ? c.H : c.Hkv;
+  hipLaunchKernelGGL(k_build_tiles, dim3((unsigned)(c.B * nh * nt)), dim3(256), 0, st, c, rc, sel, K, nt, out);
   return hipGetLastError();
 }
 
@@ -854,6 +864,7 @@ hipError_t launch_mass_mfma(const AttnArgs& a, const int32_t* cand, int K_prev, 
     if (e != hipSuccess) return e;
     m.tiles = ws;
     m.ntiles_total = (K_prev + kBN - 1) / kBN;
+    m.tiles_kv = cand == nullptr;
     rows = ws + gather_bytes(a.c, K_prev);
   }
   m.ntr = (a.c.n[a.r] + kMassRows - 1) / kMassRows;

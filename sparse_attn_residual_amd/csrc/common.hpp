@@ -20,6 +20,8 @@ constexpr int kGroup = 32;  // quantization group (dims)
 // Kernel-side copy of the cache description (passed by value).
 struct CacheGeo {
   int L, B, H, S, d, R;
+  int Hkv;                       // key/value heads (the streams are per KV head)
+  int G;                         // query heads per KV head, H / Hkv
   int n[FL_MAX_LOOPS + 1];
   int bits[FL_MAX_LOOPS + 1];
   int res_rb[FL_MAX_LOOPS + 1];  // residual record bytes per loop
@@ -36,14 +38,16 @@ __host__ __device__ inline int residual_record_bytes(int d, int bits) {
   return pad16(2 * (d * bits / 8) + 8 * (d / kGroup));
 }
 
-// Address of the base record of token j of (layer l, seq b, head h).
-__device__ inline const uint8_t* base_rec(const CacheGeo& c, int l, int b, int h, int j) {
-  long long idx = (((long long)l * c.B + b) * c.H + h) * c.S + j;
+// KV head that query head h reads (grouped-query attention; G = 1: h).
+__device__ inline int kv_head(const CacheGeo& c, int h) { return h / c.G; }
+// Address of the base record of token j of (layer l, seq b, KV head hk).
+__device__ inline const uint8_t* base_rec(const CacheGeo& c, int l, int b, int hk, int j) {
+  long long idx = (((long long)l * c.B + b) * c.Hkv + hk) * c.S + j;
   return c.base + idx * c.base_rb;
 }
-// Address of the loop-r residual record number t (t = slot) of (l, b, h).
-__device__ inline const uint8_t* res_rec(const CacheGeo& c, int r, int l, int b, int h, int t) {
-  long long idx = (((long long)l * c.B + b) * c.H + h) * c.n[r] + t;
+// Address of the loop-r residual record number t (t = slot) of (l, b, hk).
+__device__ inline const uint8_t* res_rec(const CacheGeo& c, int r, int l, int b, int hk, int t) {
+  long long idx = (((long long)l * c.B + b) * c.Hkv + hk) * c.n[r] + t;
   return c.res[r] + idx * c.res_rb[r];
 }
 
@@ -109,12 +113,12 @@ __device__ inline float res_elem(const uint8_t* rec, int d, int bits, int kv, in
 // Reconstruction x_hat^(r) of element e of token j: the base plus the
 // residuals of loops 2..r in which j was active (sets are nested, so the
 // chain stops at the first loop where j is inactive).
-__device__ inline float chain_elem(const CacheGeo& c, int r, int l, int b, int h, int j, int kv, int e) {
-  float x = base_elem(base_rec(c, l, b, h, j), c.d, kv, e);
+__device__ inline float chain_elem(const CacheGeo& c, int r, int l, int b, int hk, int j, int kv, int e) {
+  float x = base_elem(base_rec(c, l, b, hk, j), c.d, kv, e);
   for (int rr = 2; rr <= r; ++rr) {
     int t = c.slot[rr][(long long)b * c.S + j];
     if (t < 0) break;
-    x = x + res_elem(res_rec(c, rr, l, b, h, t), c.d, c.bits[rr], kv, e);
+    x = x + res_elem(res_rec(c, rr, l, b, hk, t), c.d, c.bits[rr], kv, e);
   }
   return x;
 }
@@ -122,9 +126,9 @@ __device__ inline float chain_elem(const CacheGeo& c, int r, int l, int b, int h
 // The same reconstruction for the 32 dims [32g, 32g+32) of one group, with
 // the records read by vector loads: the operations and their order are those
 // of chain_elem, so the values are the same.
-__device__ inline void chain_group(const CacheGeo& c, int r, int l, int b, int h, int j, int kv, int g, float* x) {
+__device__ inline void chain_group(const CacheGeo& c, int r, int l, int b, int hk, int j, int kv, int g, float* x) {
   const int d = c.d, G = d / kGroup;
-  const uint8_t* rec = base_rec(c, l, b, h, j);
+  const uint8_t* rec = base_rec(c, l, b, hk, j);
   const uint4 w0 = *(const uint4*)(rec + kv * d + g * kGroup);
   const uint4 w1 = *(const uint4*)(rec + kv * d + g * kGroup + 16);
   const float s = h2f(((const uint16_t*)(rec + 2 * d))[kv * G + g]);
@@ -134,7 +138,7 @@ __device__ inline void chain_group(const CacheGeo& c, int r, int l, int b, int h
   for (int rr = 2; rr <= r; ++rr) {
     const int t = c.slot[rr][(long long)b * c.S + j];
     if (t < 0) break;
-    const uint8_t* q = res_rec(c, rr, l, b, h, t);
+    const uint8_t* q = res_rec(c, rr, l, b, hk, t);
     const int bits = c.bits[rr];
     const int C = d * bits / 8;
     const uint16_t* meta = (const uint16_t*)(q + 2 * C);

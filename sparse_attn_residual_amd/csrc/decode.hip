@@ -94,7 +94,7 @@ __global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
   float m = -INFINITY, lsum = 0.0f, acc[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
-  const uint8_t* recs = base_rec(c, l, b, h, 0);
+  const uint8_t* recs = base_rec(c, l, b, kv_head(c, h), 0);
   float* logit = a.logits + lbh * c.S;
   const uint16_t* scl = (const uint16_t*)(recs + 2 * d);
   for (int j = gid; j < c.S; j += NG) {
@@ -175,7 +175,7 @@ template <int NR>
 __device__ inline void tok_load(const CacheGeo& c, int l, int b, int h, int j, const int* slot, int sub,
                                 TokLoads<NR>& t) {
   constexpr int d = 128, G = 4;
-  const uint8_t* rec = base_rec(c, l, b, h, j);
+  const uint8_t* rec = base_rec(c, l, b, kv_head(c, h), j);
   t.kw = *(const uint4*)(rec + sub * 16);
   t.vw = *(const uint4*)(rec + d + sub * 16);
   const uint16_t* sc = (const uint16_t*)(rec + 2 * d);
@@ -186,7 +186,7 @@ __device__ inline void tok_load(const CacheGeo& c, int l, int b, int h, int j, c
     t.meta[k][0] = t.meta[k][1] = 0;
     if (slot[k] >= 0) {
       const int rr = k + 2, bits = c.bits[rr], C = d * bits / 8;
-      const uint8_t* rrec = res_rec(c, rr, l, b, h, slot[k]);
+      const uint8_t* rrec = res_rec(c, rr, l, b, kv_head(c, h), slot[k]);
       if (bits == 4) {
         t.kr[k] = *(const uint2*)(rrec + sub * 8);
         t.vr[k] = *(const uint2*)(rrec + C + sub * 8);
@@ -257,7 +257,7 @@ __device__ inline void tok_decode(const CacheGeo& c, int r, int l, int b, int h,
       active_r = true;
     }
     const int bits = c.bits[rr], C = d * bits / 8, g = sub >> 1;
-    const uint8_t* rrec = res_rec(c, rr, l, b, h, ts);
+    const uint8_t* rrec = res_rec(c, rr, l, b, kv_head(c, h), ts);
     const uint16_t* mt = (const uint16_t*)(rrec + 2 * C);
     const float krs = h2f(mt[g]), krz = h2f(mt[G + g]), vrs = h2f(mt[2 * G + g]), vrz = h2f(mt[3 * G + g]);
 #pragma unroll

@@ -64,20 +64,20 @@ __global__ __launch_bounds__(256) void k_quant_res(CacheGeo c, int r, const T* _
   long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   long long row = gid / (2 * G);  // over [L][B][H][n_r]
   int sub = (int)(gid - row * (2 * G));
-  long long total = (long long)c.L * c.B * c.H * nr;
+  long long total = (long long)c.L * c.B * c.Hkv * nr;  // rows of every KV head
   if (row >= total) return;
   const int kv = sub >= G;
   const int g = sub - kv * G;
   const int t = (int)(row % nr);
   long long lbh = row / nr;
-  const int h = (int)(lbh % c.H);
-  const int b = (int)((lbh / c.H) % c.B);
-  const int l = (int)(lbh / ((long long)c.H * c.B));
+  const int hk = (int)(lbh % c.Hkv);
+  const int b = (int)((lbh / c.Hkv) % c.B);
+  const int l = (int)(lbh / ((long long)c.Hkv * c.B));
   const int j = c.rows[r][(long long)b * nr + t];
 
   float x[kGroup], prev[kGroup];
   load_group16<T>((kv ? v : k) + row * d + g * kGroup, x);
-  chain_group(c, r - 1, l, b, h, j, kv, g, prev);
+  chain_group(c, r - 1, l, b, hk, j, kv, g, prev);
   float delta[kGroup];
   float lo = 0.0f, hi = 0.0f;
 #pragma unroll
@@ -150,7 +150,7 @@ __global__ void k_build_slot(const int32_t* __restrict__ rows, int n, int S, int
 
 hipError_t launch_quant_base(const CacheGeo& c, const void* k, const void* v, fl_dtype dt, uint8_t* base,
                              hipStream_t st) {
-  long long ntok = (long long)c.L * c.B * c.H * c.S;
+  long long ntok = (long long)c.L * c.B * c.Hkv * c.S;
   long long threads = ntok * 2 * (c.d / kGroup);
   dim3 grid((unsigned)((threads + 255) / 256));
   if (dt == FL_BF16)
@@ -171,7 +171,7 @@ hipError_t launch_build_slot(const CacheGeo& c, int r, int32_t* slot, hipStream_
 
 hipError_t launch_quant_res(const CacheGeo& c, int r, const void* k, const void* v, fl_dtype dt, uint8_t* res,
                             hipStream_t st) {
-  long long rowsn = (long long)c.L * c.B * c.H * c.n[r];
+  long long rowsn = (long long)c.L * c.B * c.Hkv * c.n[r];
   long long threads = rowsn * 2 * (c.d / kGroup);
   dim3 grid((unsigned)((threads + 255) / 256));
   if (dt == FL_BF16)

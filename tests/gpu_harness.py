@@ -37,7 +37,7 @@ def run_prefill(cfg, rows, slices, *, mass_in=None, K_budget=None, mfma=None, mi
     import sparse_attn_residual_amd as fl
     K_budget = cfg.K if K_budget is None else K_budget
     R, B, H, S, d = cfg.R, cfg.B, cfg.H, cfg.S, cfg.d
-    cache = fl.CacheBuffers(1, B, H, S, d, R, cfg.n, cfg.bits, rows_list(cfg, rows))
+    cache = fl.CacheBuffers(1, B, H, S, d, R, cfg.n, cfg.bits, rows_list(cfg, rows), Hkv=cfg.kv_heads)
     st = fl.PrefillState(B, H, S, d, mixed=mixed)
     dt = fl_dtype(cfg)
     qs = [upload(workloads.stack_loop(cfg, slices, r, "q"), cfg) for r in range(1, R + 1)]
@@ -90,7 +90,8 @@ def build_decode_cache(cfg, rows, slices, L=None):
     """Quantize layer 0 through fl_kv_resq, then copy it to every layer."""
     import sparse_attn_residual_amd as fl
     L = cfg.L if L is None else L
-    cache = fl.CacheBuffers(L, cfg.B, cfg.H, cfg.S, cfg.d, cfg.R, cfg.n, cfg.bits, rows_list(cfg, rows))
+    cache = fl.CacheBuffers(L, cfg.B, cfg.H, cfg.S, cfg.d, cfg.R, cfg.n, cfg.bits, rows_list(cfg, rows),
+                            Hkv=cfg.kv_heads)
     view = cache.layer_view(0)
     dt = fl_dtype(cfg)
     for r in range(1, cfg.R + 1):

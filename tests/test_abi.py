@@ -84,6 +84,9 @@ def test_validation_errors():
     nest.n[2] = 65
     st, msg = _status("fl_kv_resq", ctypes.byref(nest), 1, ok_ptr, ok_ptr, fl.FL_F32, None)
     assert st == EINVAL and "nested" in msg
+    # key/value heads must divide the query heads
+    st, msg = _status("fl_kv_resq", ctypes.byref(_cache(Hkv=3)), 1, ok_ptr, ok_ptr, fl.FL_F32, None)
+    assert st == EINVAL and "Hkv" in msg
     s = fl.FlState(ok_ptr, ok_ptr, ok_ptr, ok_ptr)
     st, msg = _status("fl_colsel", ctypes.byref(_cache()), 2, ok_ptr, fl.FL_F32, ctypes.byref(s), 64, None, 65,
                       None, None, ok_ptr, None, 0, None)

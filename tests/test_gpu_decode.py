@@ -108,3 +108,13 @@ def test_decode_full_shape():
     cfg = dataclasses.replace(workloads.CONFIGS[3], name="decode-full-shape", B=1, H=2, L=1)
     _say("decode full shape", cfg)
     _decode_case(cfg, 2e-3, rel=True)
+
+
+@pytest.mark.parametrize("dtype,H,Hkv", [("f32", 4, 2), ("bf16", 6, 2)])
+def test_decode_gqa(dtype, H, Hkv):
+    """Grouped-query attention: each query head reads its KV head's packed
+    records and selects its own columns."""
+    cfg = workloads.custom(name="decode-gqa", dtype=dtype, B=2, H=H, d=128, S=900, R=4, act=(1, 0.3, 0.15, 0.08),
+                           col="0.10", bits=(8, 4, 4, 2), gamma=0.5, lognormal=0.5, L=2, decode=True, seed=6, Hkv=Hkv)
+    _say("decode gqa", dtype, cfg)
+    _decode_case(cfg, 1e-5 if dtype == "f32" else 2e-3, rel=dtype != "f32")

@@ -31,11 +31,12 @@ def _check_records(cfg, gpu, orc, heads):
     for b in range(cfg.B):
         for h in heads:
             o = orc[(b, h)]
+            hk = h // cfg.G   # the streams are per KV head
             ks, vs = o["k_streams"], o["v_streams"]
             want = records.pack_base(ks[0]["codes"], ks[0]["scale"], vs[0]["codes"], vs[0]["scale"])
-            assert np.array_equal(base[0, b, h], want), (b, h, "base")
+            assert np.array_equal(base[0, b, hk], want), (b, h, "base")
             for r in range(2, cfg.R + 1):
-                got = cache.res_records(r).cpu().numpy()[0, b, h]
+                got = cache.res_records(r).cpu().numpy()[0, b, hk]
                 k, v = ks[r - 1], vs[r - 1]
                 want = records.pack_residual(k["codes"], k["scale"], k["zero"], v["codes"], v["scale"], v["zero"],
                                              cfg.bits[r - 1])
@@ -318,3 +319,17 @@ def test_prefill_mixed_combine(dtype, d, budgets):
                 err = np.max(np.abs(got[fin] - want[fin])) if fin.any() else 0.0
                 assert err <= (tol if f32 else 8 * tol) * max(1.0, np.max(np.abs(want[fin]), initial=0.0)), \
                     (b, h, r + 1, "lsel", err)
+
+
+@pytest.mark.parametrize("dtype,d,H,Hkv", [("f32", 64, 4, 2), ("bf16", 128, 6, 2), ("bf16", 128, 4, 1)])
+def test_prefill_gqa(dtype, d, H, Hkv):
+    """Grouped-query attention: H query heads read Hkv key/value heads; the
+    streams are per KV head, loop 1's tiles are built once per KV head, every
+    other step is per query head (pruning budgets)."""
+    f32 = dtype == "f32"
+    cfg = workloads.custom(name="prefill-gqa", dtype=dtype, B=2, H=H, d=d, S=1300, R=4, act=(1, 0.5, 0.3, 0.15),
+                           col="0.30", bits=(8, 4, 2, 4), lognormal=None if f32 else 0.5, seed=31, Hkv=Hkv)
+    _say("prefill gqa", cfg)
+    heads = sorted({0, min(H // Hkv, H - 1), H - 1})
+    _bf16_case(cfg, heads=heads, sel_eps=1e-5 if f32 else 2e-3, budgets=[390, 200, 90], tol=1e-5 if f32 else 2e-3,
+               rel=not f32)

@@ -65,6 +65,16 @@ class Config:
     L: int = 1                 # stacked layers (decode only)
     decode: bool = False
     seed: int = 0
+    Hkv: int = 0               # key/value heads (0: H); query head h reads KV head h // (H // Hkv)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H if self.Hkv == 0 else self.Hkv
+
+    @property
+    def G(self) -> int:
+        """Query heads per KV head."""
+        return self.H // self.kv_heads
 
     @property
     def n(self) -> list[int]:
@@ -162,12 +172,13 @@ def gen_slice(cfg: Config, b: int, h: int, rows=None, with_q: bool = True) -> Sl
     with_q=False skips the queries (a decode cache needs keys and values only)."""
     if rows is None:
         rows = active_rows(cfg, b)
+    hk = h // cfg.G   # keys and values come from the query head's KV head
     lam_q = _lam(cfg, _T_LAM_Q, b, h)
-    lam_k = _lam(cfg, _T_LAM_K, b, h)
+    lam_k = _lam(cfg, _T_LAM_K, b, hk)
     ones = np.ones(cfg.S, dtype=np.float32)
     q = _chain(cfg, rows, _T_Q, _T_DQ, lam_q, b, h) if with_q else None
-    k = _chain(cfg, rows, _T_K, _T_DK, lam_k, b, h)
-    v = _chain(cfg, rows, _T_V, _T_DV, ones, b, h)
+    k = _chain(cfg, rows, _T_K, _T_DK, lam_k, b, hk)
+    v = _chain(cfg, rows, _T_V, _T_DV, ones, b, hk)
     return Slice(rows=rows, q=q, k=k, v=v)
 
 
@@ -183,9 +194,12 @@ def gen_batch(cfg: Config, heads=None, batches=None, threads: int | None = None,
 
 
 def stack_loop(cfg: Config, slices: dict, r: int, what: str, batches=None, heads=None) -> np.ndarray:
-    """[B][H][n_r][d] float32 tensor of loop r (1-based) for q/k/v."""
+    """[B][H][n_r][d] float32 tensor of loop r (1-based) for q; for k/v the
+    heads default to the KV heads ([B][Hkv][n_r][d], taken from the first
+    query head of each group)."""
     batches = range(cfg.B) if batches is None else batches
-    heads = range(cfg.H) if heads is None else heads
+    if heads is None:
+        heads = range(cfg.H) if what == "q" else range(0, cfg.H, cfg.G)
     return np.stack([np.stack([getattr(slices[(b, h)], what)[r - 1] for h in heads]) for b in batches])
 
 
@@ -215,9 +229,10 @@ def decode_queries(cfg: Config, layers=None, batches=None, heads=None) -> list[n
 
 
 def custom(name="custom", dtype="f32", B=1, H=1, d=64, S=64, R=4, act=(1.0, 0.5, 0.25, 0.125), col="0.25",
-           bits=(8, 4, 4, 4), gamma=0.5, lognormal=None, seed=0, L=1, decode=False) -> Config:
+           bits=(8, 4, 4, 4), gamma=0.5, lognormal=None, seed=0, L=1, decode=False, Hkv=0) -> Config:
     """A small ad-hoc configuration (tests: ragged tails, edge cases)."""
-    return Config(name, dtype, B, H, d, S, R, tuple(act), str(col), tuple(bits), gamma, lognormal, L, decode, seed)
+    return Config(name, dtype, B, H, d, S, R, tuple(act), str(col), tuple(bits), gamma, lognormal, L, decode, seed,
+                  Hkv)
 
 
 def gen_hidden(cfg: Config, b: int, D: int, r: int, moving) -> tuple[np.ndarray, np.ndarray]:
