@@ -84,8 +84,8 @@ class Timer:
         return {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in self.pairs.items()}
 
 
-def prefill_bench(args, torch, fl, workloads, acc):
-    cfg = workloads.CONFIGS[PREFILL_CFG]
+def prefill_bench(args, torch, fl, workloads, acc, cfg=None, pruned=True):
+    cfg = workloads.CONFIGS[PREFILL_CFG] if cfg is None else cfg
     t0 = time.time()
     rows, slices = workloads.gen_batch(cfg)
     log(f"generated {cfg.name} inputs in {time.time() - t0:.1f}s")
@@ -95,12 +95,13 @@ def prefill_bench(args, torch, fl, workloads, acc):
     v = [_upload(workloads.stack_loop(cfg, slices, r, "v"), torch) for r in range(1, R + 1)]
     del slices
     rows_l = [np.stack([rows[b][r] for b in range(B)]) for r in range(R)]
-    cache = fl.CacheBuffers(1, B, H, S, d, R, cfg.n, cfg.bits, rows_l)
+    cache = fl.CacheBuffers(1, B, H, S, d, R, cfg.n, cfg.bits, rows_l, Hkv=cfg.kv_heads)
     st = fl.PrefillState(B, H, S, d)
     res = measure_prefill(args, torch, fl, acc, cfg, rows, q, k, v, cache, st, [cfg.K] * (R - 1))
-    # nested pruning: the budget halves at every loop after the second
-    res["pruned"] = measure_prefill(args, torch, fl, acc, cfg, rows, q, k, v, cache, st,
-                                    [cfg.K >> (r - 2) for r in range(2, R + 1)])
+    if pruned:
+        # nested pruning: the budget halves at every loop after the second
+        res["pruned"] = measure_prefill(args, torch, fl, acc, cfg, rows, q, k, v, cache, st,
+                                        [cfg.K >> (r - 2) for r in range(2, R + 1)])
     return res
 
 
@@ -165,13 +166,14 @@ def measure_prefill(args, torch, fl, acc, cfg, rows, q, k, v, cache, st, budgets
                 total_tf=total_tf, Ks=Ks)
 
 
-def decode_bench(args, torch, fl, workloads, acc):
-    cfg = workloads.CONFIGS[DECODE_CFG]
+def decode_bench(args, torch, fl, workloads, acc, cfg=None):
+    cfg = workloads.CONFIGS[DECODE_CFG] if cfg is None else cfg
     L, B, H, S, d, R = cfg.L, cfg.B, cfg.H, cfg.S, cfg.d, cfg.R
+    Hkv = cfg.kv_heads
     t0 = time.time()
     rows = {b: workloads.active_rows(cfg, b) for b in range(B)}
     rows_l = [np.stack([rows[b][r] for b in range(B)]) for r in range(R)]
-    cache = fl.CacheBuffers(L, B, H, S, d, R, cfg.n, cfg.bits, rows_l)
+    cache = fl.CacheBuffers(L, B, H, S, d, R, cfg.n, cfg.bits, rows_l, Hkv=Hkv)
     log(f"decode cache: {cache.nbytes() / 1e9:.1f} GB on device")
     for b in range(B):
         _, sl = workloads.gen_batch(cfg, batches=[b], with_q=False)
@@ -212,9 +214,10 @@ def decode_bench(args, torch, fl, workloads, acc):
     log(f"decode: {ms_step:.3f} ms/step; per loop (ms): " + ", ".join(f"{kk}={vv:.3f}" for kk, vv in per.items()))
 
     # algorithmic packed bytes of the step, from the selections of the run
+    # (the dense loop reads every record of every KV head once)
     base_b = acc.base_record_bytes(d)
     res_b = [0] + [acc.residual_record_bytes(d, cfg.bits[r]) for r in range(1, R)]
-    loop_bytes = [float(L * B * H * S * base_b)]
+    loop_bytes = [float(L * B * Hkv * S * base_b)]
     sel = st.sel[..., :Ks[-1]].long()  # S_2 = S_3 = S_4 with a constant budget
     cum = torch.full((B, S), float(base_b), dtype=torch.float64, device="cuda")
     for r in range(2, R + 1):
@@ -358,6 +361,13 @@ def main():
     pf = prefill_bench(args, torch, fl, workloads, acc)
     sel = select_bench(args, torch, fl, workloads, acc)
     dec = None if args.no_decode else decode_bench(args, torch, fl, workloads, acc)
+    torch.cuda.empty_cache()
+    # grouped-query attention (4 query heads per KV head) on the same shapes
+    gqa_pf = prefill_bench(args, torch, fl, workloads, acc, cfg=workloads.CONFIGS[PREFILL_CFG].with_(Hkv=4),
+                           pruned=False)
+    gqa_dec = None if args.no_decode else decode_bench(args, torch, fl, workloads, acc,
+                                                       cfg=workloads.CONFIGS[DECODE_CFG].with_(Hkv=4))
+    torch.cuda.empty_cache()
     cpu = None if args.no_cpu else cpu_baseline(workloads)
 
     cfg = pf["cfg"]
@@ -448,6 +458,20 @@ def main():
                 "step_frac": dec["gbs"] / acc.MI355X_HBM_GBS,
             },
         }
+    out["gqa"] = {
+        "workload": f"the two workloads above with Hkv = 4 key/value heads for H = {cfg.H} query heads",
+        "prefill_ms_per_step": gqa_pf["ms_step"],
+        "prefill_tokens_per_s": cfg.B * cfg.S / (gqa_pf["ms_step"] * 1e-3),
+        "prefill_per_call_ms": {k: round(v, 4) for k, v in gqa_pf["per"].items()},
+    }
+    if gqa_dec is not None:
+        out["gqa"].update({
+            "decode_ms_per_step": gqa_dec["ms_step"],
+            "decode_per_loop_ms": {k: round(v, 4) for k, v in gqa_dec["per"].items()},
+            "decode_dense_unique_gbs": gqa_dec["dense_gbs"],
+            "decode_dense_note": "loop 1 reads each KV head's records once for its 4 query heads; GB/s counts "
+                                 "those unique bytes (the kernel is vector-ALU bound at this ratio)",
+        })
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

@@ -64,24 +64,31 @@ __device__ inline void merge_groups(float& m, float& l, float* acc, int o) {
   m = mx;
 }
 
-constexpr int kDenseThreads = 512;  // one block per (layer, sequence, head)
+constexpr int kDenseThreads = 512;  // one block per (layer, sequence, query-head group)
 
 // Loop 1: dense over all S cached tokens, d == 128.  A block of NT threads
-// (NT/8 groups of 8 lanes, one token per group per step) walks its slab of
-// S records; the block's waves cover consecutive tokens, so few slabs (and
-// pages) are read at once on the chip.  The group's softmax keeps a
-// reference maximum that only moves when a score exceeds it by more than
-// kDecRescale, so the accumulators are rescaled rarely.  Group states merge
-// within each wavefront by lane shuffles, then across wavefronts in LDS.
-template <typename T, int NT>
+// (NT/8 groups of 8 lanes, one token per group per step) walks the slab of S
+// records of one KV head for GQ of the query heads that read it (grouped-query
+// attention: each record is fetched once for all GQ heads; GQ = 1 otherwise).
+// The block's waves cover consecutive tokens, so few slabs (and pages) are
+// read at once on the chip.  Each group's softmax keeps a reference maximum
+// per head that only moves when a score exceeds it by more than kDecRescale,
+// so the accumulators are rescaled rarely.  Group states merge within each
+// wavefront by lane shuffles, then across wavefronts in LDS.  Every head's
+// arithmetic is the same whatever GQ is.
+template <typename T, int NT, int GQ>
 __global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
   constexpr int NG = NT / 8, NW = NT / kWave;
-  __shared__ float wm[NW], wl[NW], wacc[NW][128];
+  static_assert(GQ * 128 <= NT, "one thread per output dim of every head");
+  __shared__ float wm[GQ][NW], wl[GQ][NW], wacc[GQ][NW][128];
   const CacheGeo& c = a.c;
-  const long long lbh = blockIdx.x;
-  const int h = (int)(lbh % c.H);
-  const int b = (int)((lbh / c.H) % c.B);
-  const int l = (int)(lbh / ((long long)c.H * c.B));
+  const int HB = c.H / GQ;                 // query-head groups per sequence
+  const long long blk = blockIdx.x;        // over [L][B][HB]
+  const int hb = (int)(blk % HB);
+  const int b = (int)((blk / HB) % c.B);
+  const int l = (int)(blk / ((long long)HB * c.B));
+  const int h0 = hb * GQ;                  // GQ divides H / Hkv: one KV head
+  const long long lbh0 = ((long long)l * c.B + b) * c.H + h0;
   const int d = 128;
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
@@ -89,13 +96,17 @@ __global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
   const int grp = lane >> 3;       // token within the wave's step
   const int gid = wv * 8 + grp;    // group id in the block
   const int g = sub >> 1;          // quantization group of the slice
-  float q[16];
-  load_q16<T>((const T*)a.q + lbh * d, sub, q);
-  float m = -INFINITY, lsum = 0.0f, acc[16];
+  float q[GQ][16], m[GQ], lsum[GQ], acc[GQ][16];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
-  const uint8_t* recs = base_rec(c, l, b, kv_head(c, h), 0);
-  float* logit = a.logits + lbh * c.S;
+  for (int u = 0; u < GQ; ++u) {
+    load_q16<T>((const T*)a.q + (lbh0 + u) * d, sub, q[u]);
+    m[u] = -INFINITY;
+    lsum[u] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[u][e] = 0.0f;
+  }
+  const uint8_t* recs = base_rec(c, l, b, kv_head(c, h0), 0);
+  float* logit = a.logits + lbh0 * c.S;
   const uint16_t* scl = (const uint16_t*)(recs + 2 * d);
   for (int j = gid; j < c.S; j += NG) {
     const uint8_t* rec = recs + (long long)j * c.base_rb;
@@ -106,53 +117,78 @@ __global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
     const float vs = h2f(sc[4 + g]);
     float cv[16];
     unpack_i8x16(kw, cv);
-    float part = 0.0f;
+    float p[GQ];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) part = __builtin_fmaf(q[e], cv[e], part);
-    const float s = tau * group8_sum_dpp(part * ks);
-    if (sub == 0) logit[j] = s;
-    if (s > m + kDecRescale) {
-      const float alpha = __expf(m - s);  // 0 on the group's first token
-      lsum *= alpha;
+    for (int u = 0; u < GQ; ++u) {
+      float part = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] *= alpha;
-      m = s;
+      for (int e = 0; e < 16; ++e) part = __builtin_fmaf(q[u][e], cv[e], part);
+      const float s = tau * group8_sum_dpp(part * ks);
+      if (sub == 0) logit[(long long)u * c.S + j] = s;
+      if (s > m[u] + kDecRescale) {
+        const float alpha = __expf(m[u] - s);  // 0 on the group's first token
+        lsum[u] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[u][e] *= alpha;
+        m[u] = s;
+      }
+      p[u] = __expf(s - m[u]);
+      lsum[u] += p[u];
     }
-    const float p = __expf(s - m);
-    lsum += p;
-    const float pv = p * vs;
     unpack_i8x16(vw, cv);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = __builtin_fmaf(pv, cv[e], acc[e]);
-  }
-  merge_groups(m, lsum, acc, 8);
-  merge_groups(m, lsum, acc, 16);
-  merge_groups(m, lsum, acc, 32);
-  if (grp == 0) {
-    if (sub == 0) {
-      wm[wv] = m;
-      wl[wv] = lsum;
-    }
+    for (int u = 0; u < GQ; ++u) {
+      const float pv = p[u] * vs;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) wacc[wv][sub * 16 + e] = acc[e];
+      for (int e = 0; e < 16; ++e) acc[u][e] = __builtin_fmaf(pv, cv[e], acc[u][e]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < GQ; ++u) {
+    merge_groups(m[u], lsum[u], acc[u], 8);
+    merge_groups(m[u], lsum[u], acc[u], 16);
+    merge_groups(m[u], lsum[u], acc[u], 32);
+    if (grp == 0) {
+      if (sub == 0) {
+        wm[u][wv] = m[u];
+        wl[u][wv] = lsum[u];
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) wacc[u][wv][sub * 16 + e] = acc[u][e];
+    }
   }
   __syncthreads();
-  if (threadIdx.x < d) {
+  if (threadIdx.x < GQ * d) {
+    const int u = threadIdx.x / d, t = threadIdx.x - u * d;
     float mx = -INFINITY;
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, wm[w]);
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, wm[u][w]);
     float L = 0.0f, A = 0.0f;
     for (int w = 0; w < NW; ++w) {
-      const float f = wm[w] == -INFINITY ? 0.0f : __expf(wm[w] - mx);
-      L += wl[w] * f;
-      A += wacc[w][threadIdx.x] * f;
+      const float f = wm[u][w] == -INFINITY ? 0.0f : __expf(wm[u][w] - mx);
+      L += wl[u][w] * f;
+      A += wacc[u][w][t] * f;
     }
-    a.O[lbh * d + threadIdx.x] = A / L;
-    a.U[lbh * d + threadIdx.x] = 0.0f;
-    if (threadIdx.x == 0) {
+    const long long lbh = lbh0 + u;
+    a.O[lbh * d + t] = A / L;
+    a.U[lbh * d + t] = 0.0f;
+    if (t == 0) {
       a.lse[lbh] = mx + __logf(L);
       a.M[lbh] = 1.0f;
     }
   }
+}
+
+template <typename T>
+static void launch_dense(const DecodeArgs& a, float tau, hipStream_t st) {
+  // query heads per block: the largest of 4, 2, 1 dividing the group size
+  const int gq = a.c.G % 4 == 0 ? 4 : a.c.G % 2 == 0 ? 2 : 1;
+  const unsigned nblk = (unsigned)((long long)a.c.L * a.c.B * (a.c.H / gq));
+  if (gq == 4)
+    hipLaunchKernelGGL((k_decode_dense<T, kDenseThreads, 4>), dim3(nblk), dim3(kDenseThreads), 0, st, a, tau);
+  else if (gq == 2)
+    hipLaunchKernelGGL((k_decode_dense<T, kDenseThreads, 2>), dim3(nblk), dim3(kDenseThreads), 0, st, a, tau);
+  else
+    hipLaunchKernelGGL((k_decode_dense<T, kDenseThreads, 1>), dim3(nblk), dim3(kDenseThreads), 0, st, a, tau);
 }
 
 constexpr int kMaxFastLoops = 5;  // loops whose slot lookups are batched
@@ -465,11 +501,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   const bool bf = a.dt == FL_BF16;
   if (a.r == 1) {
     if (bf)
-      hipLaunchKernelGGL((k_decode_dense<uint16_t, kDenseThreads>), dim3((unsigned)P), dim3(kDenseThreads), 0, st,
-                         a, tau);
+      launch_dense<uint16_t>(a, tau, st);
     else
-      hipLaunchKernelGGL((k_decode_dense<float, kDenseThreads>), dim3((unsigned)P), dim3(kDenseThreads), 0, st, a,
-                         tau);
+      launch_dense<float>(a, tau, st);
     return hipGetLastError();
   }
   const int pruned = a.K < a.K_prev;

@@ -110,7 +110,7 @@ def test_decode_full_shape():
     _decode_case(cfg, 2e-3, rel=True)
 
 
-@pytest.mark.parametrize("dtype,H,Hkv", [("f32", 4, 2), ("bf16", 6, 2)])
+@pytest.mark.parametrize("dtype,H,Hkv", [("f32", 4, 2), ("bf16", 6, 2), ("bf16", 8, 2), ("f32", 8, 1)])
 def test_decode_gqa(dtype, H, Hkv):
     """Grouped-query attention: each query head reads its KV head's packed
     records and selects its own columns."""
