@@ -94,8 +94,11 @@ def prefill_bench(args, torch, fl, workloads, acc, cfg=None, pruned=True):
     k = [_upload(workloads.stack_loop(cfg, slices, r, "k"), torch) for r in range(1, R + 1)]
     v = [_upload(workloads.stack_loop(cfg, slices, r, "v"), torch) for r in range(1, R + 1)]
     del slices
-    rows_l = [np.stack([rows[b][r] for b in range(B)]) for r in range(R)]
-    cache = fl.CacheBuffers(1, B, H, S, d, R, cfg.n, cfg.bits, rows_l, Hkv=cfg.kv_heads)
+    # per-sequence rows padded to the capacity with their last row (ragged batches)
+    rows_l = [np.stack([np.concatenate([rows[b][r], np.full(cfg.n[r] - len(rows[b][r]), rows[b][r][-1], np.int32)])
+                        for b in range(B)]) for r in range(R)]
+    counts = [np.array([cfg.counts(b)[r] for b in range(B)], np.int32) for r in range(R)] if cfg.ragged else None
+    cache = fl.CacheBuffers(1, B, H, S, d, R, cfg.n, cfg.bits, rows_l, Hkv=cfg.kv_heads, counts=counts)
     st = fl.PrefillState(B, H, S, d)
     res = measure_prefill(args, torch, fl, acc, cfg, rows, q, k, v, cache, st, [cfg.K] * (R - 1))
     if pruned:
@@ -368,6 +371,9 @@ def main():
     gqa_dec = None if args.no_decode else decode_bench(args, torch, fl, workloads, acc,
                                                        cfg=workloads.CONFIGS[DECODE_CFG].with_(Hkv=4))
     torch.cuda.empty_cache()
+    # a ragged batch: two 32K sequences, the second keeping half as many active rows
+    rag_cfg = workloads.CONFIGS[PREFILL_CFG].with_(B=2, ragged=("1", "0.5"))
+    rag_pf = prefill_bench(args, torch, fl, workloads, acc, cfg=rag_cfg, pruned=False)
     cpu = None if args.no_cpu else cpu_baseline(workloads)
 
     cfg = pf["cfg"]
@@ -472,6 +478,12 @@ def main():
             "decode_dense_note": "loop 1 reads each KV head's records once for its 4 query heads; GB/s counts "
                                  "those unique bytes (the kernel is vector-ALU bound at this ratio)",
         })
+    out["ragged"] = {
+        "workload": f"{rag_cfg.name} with B = 2: active rows per loop {rag_cfg.counts(0)} and {rag_cfg.counts(1)}",
+        "prefill_ms_per_step": rag_pf["ms_step"],
+        "prefill_tokens_per_s": rag_cfg.B * rag_cfg.S / (rag_pf["ms_step"] * 1e-3),
+        "prefill_per_call_ms": {k: round(v, 4) for k, v in rag_pf["per"].items()},
+    }
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

@@ -83,8 +83,14 @@ typedef void* fl_stream;
  *                      attention, a serving variant the pages leave open).
  *                      Queries, states, masses and selections are per query
  *                      head; the streams below are per KV head.
- *   n[r]               active rows per sequence at loop r (n[1] == S), the
- *                      same for every sequence
+ *   n[r]               active rows per sequence at loop r (n[1] == S); with
+ *                      cnt[r] set, the capacity per sequence: the stride of
+ *                      rows[r], of the loop-r streams and of loop-r queries
+ *   cnt[r]             NULL, or [B] int32 device array: |A_r| of each sequence
+ *                      (ragged batches, a serving variant).  Each count must
+ *                      lie in [1, n[r]] and in [cnt[r+1][b], cnt[r-1][b]]
+ *                      (nested sets; not checked: device memory); rows past a
+ *                      sequence's count are neither read nor written.
  *   bits[r]            residual code width of loop r: 4 or 2 (bits[1] == 8)
  *   rows[r]            [B][n_r] int32, strictly ascending positions of A_r
  *                      (rows[1] unused: every row)
@@ -116,6 +122,7 @@ typedef struct fl_cache {
   uint8_t* base;
   uint8_t* res[FL_MAX_LOOPS + 1];
   int Hkv;
+  const int32_t* cnt[FL_MAX_LOOPS + 1];
 } fl_cache;
 
 /* Per-row prefill state, position indexed (one layer: the cache's L must be 1).

@@ -30,6 +30,7 @@ class FlCache(ctypes.Structure):
         ("rows", ctypes.c_void_p * _N), ("slot", ctypes.c_void_p * _N),
         ("base", ctypes.c_void_p), ("res", ctypes.c_void_p * _N),
         ("Hkv", ctypes.c_int),
+        ("cnt", ctypes.c_void_p * _N),
     ]
 
 

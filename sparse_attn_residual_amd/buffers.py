@@ -15,9 +15,11 @@ class CacheBuffers:
     """A packed cross-loop cache of L layers and the FlCache struct pointing at it.
 
     rows[r-1]: int32 [B][n_r] active positions of loop r (loop 1 ignored).
-    Hkv: key/value heads (None: H); the streams are [L][B][Hkv][...]."""
+    Hkv: key/value heads (None: H); the streams are [L][B][Hkv][...].
+    counts: optional per-loop [B] int32 |A_r| of each sequence (ragged batch;
+    n is then the capacity and rows[r-1][b] holds counts[r-1][b] positions)."""
 
-    def __init__(self, L, B, H, S, d, R, n, bits, rows, device="cuda", Hkv=None):
+    def __init__(self, L, B, H, S, d, R, n, bits, rows, device="cuda", Hkv=None, counts=None):
         assert R <= FL_MAX_LOOPS and len(n) == R and len(bits) == R
         self.L, self.B, self.H, self.S, self.d, self.R = L, B, H, S, d, R
         self.Hkv = H if Hkv is None else Hkv   # heads of the streams
@@ -29,6 +31,8 @@ class CacheBuffers:
                              for r in range(1, R)]
         self.rows = [None] + [_dev_i32(rows[r], device).reshape(B, n[r]) for r in range(1, R)]
         self.slot = [None] + [torch.full((B, S), -1, dtype=torch.int32, device=device) for _ in range(1, R)]
+        self.cnt = [None] * R if counts is None else \
+            [None] + [_dev_i32(counts[r], device).reshape(B) for r in range(1, R)]
         self.fl = self._struct(0, L)
 
     def _struct(self, layer, L):
@@ -43,6 +47,8 @@ class CacheBuffers:
             if r >= 2:
                 c.rows[r] = self.rows[r - 1].data_ptr()
                 c.slot[r] = self.slot[r - 1].data_ptr()
+                if self.cnt[r - 1] is not None:
+                    c.cnt[r] = self.cnt[r - 1].data_ptr()
                 per = self.B * self.Hkv * self.n[r - 1] * self.res_rb[r - 1]
                 c.res[r] = self.res[r - 1].data_ptr() + layer * per
         return c
@@ -60,6 +66,8 @@ class CacheBuffers:
         for r in range(2, self.R + 1):
             c.rows[r] += b * self.n[r - 1] * 4
             c.slot[r] += b * self.S * 4
+            if c.cnt[r]:
+                c.cnt[r] += b * 4
             c.res[r] += b * self.Hkv * self.n[r - 1] * self.res_rb[r - 1]
         return c
 

@@ -71,6 +71,7 @@ fl_status check_cache(const char* fn, const fl_cache* c, int r, bool need_res_r,
     FL_NEED_PTR4(c->rows[rr], name);
     std::snprintf(name, sizeof name, "cache->slot[%d]", rr);
     FL_NEED_PTR4(c->slot[rr], name);
+    if (c->cnt[rr] && !aligned4(c->cnt[rr])) return fail(FL_EINVAL, "%s: cache->cnt[%d] is not 4-byte aligned", fn, rr);
     if (rr <= last) {
       std::snprintf(name, sizeof name, "cache->res[%d]", rr);
       FL_NEED_PTR(c->res[rr], name);
@@ -87,6 +88,7 @@ fl_status check_cache(const char* fn, const fl_cache* c, int r, bool need_res_r,
     geo->bits[rr] = rr == 1 ? 8 : c->bits[rr];
     geo->rows[rr] = c->rows[rr];
     geo->slot[rr] = c->slot[rr];
+    geo->cnt[rr] = rr == 1 ? nullptr : c->cnt[rr];
     geo->res[rr] = c->res[rr];
     geo->res_rb[rr] = rr == 1 ? 0 : fl::residual_record_bytes(c->d, c->bits[rr]);
   }

@@ -413,8 +413,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_mfma(MfmaArgs
 
   const int r = a.r;
   const bool dense = r == 1 && MODE == kModeAttn;
-  const int nrows = dense ? c.S : c.n[r];
+  const int nrows = dense ? c.S : count_of(c, r, b);
   const int row0 = blk * BM;
+  if (row0 >= nrows) return;  // past this sequence's rows (ragged counts): the whole block
   const long long bhS = (long long)bh * c.S;
   // loop 1 reads the tiles of its KV head (built once per KV head)
   const long long tbh = dense ? (long long)b * c.Hkv + kv_head(c, bh - b * c.H) : bh;
@@ -561,11 +562,11 @@ __global__ __launch_bounds__(256) void k_build_rows(AttnArgs a, int ntr, uint8_t
   const int t = threadIdx.x;
   const int row = t >> 2, qd = t & 3;
   const int r = a.r, rp = r - 1;
-  const int nr = c.n[r];
+  const int nr = c.n[r];  // stride of rows[r]
   const int np = rp == 1 ? c.S : c.n[rp];
   const int tr = tile * kMassRows + row;
   int i = -1, qi = -1;
-  if (tr < nr) {
+  if (tr < count_of(c, r, b)) {
     i = c.rows[r][(long long)b * nr + tr];
     qi = rp == 1 ? i : c.slot[rp][(long long)b * c.S + i];
   }
@@ -666,7 +667,7 @@ __global__ __launch_bounds__(64 * NW) void k_mass_mfma(MassArgs m) {
   }
   // smallest and largest column position of the block (columns ascend): rows
   // below the smallest see none of them, rows at or past the largest all
-  const int nr = c.n[a.r];
+  const int nr = count_of(c, a.r, b);
   if (threadIdx.x == 0) {
     int jmin;
     if (BASE) {
@@ -679,7 +680,7 @@ __global__ __launch_bounds__(64 * NW) void k_mass_mfma(MassArgs m) {
       jmin = ((const int*)(t0p + kImgPos))[ci % kBN];
       sh_jmax = ((const int*)(t1p + kImgPos))[cl % kBN];
     }
-    const int32_t* rows = c.rows[a.r] + (long long)b * nr;
+    const int32_t* rows = c.rows[a.r] + (long long)b * c.n[a.r];
     int lo = 0, hi = nr;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
@@ -689,7 +690,7 @@ __global__ __launch_bounds__(64 * NW) void k_mass_mfma(MassArgs m) {
   }
   __syncthreads();
   const int tile0 = sh_t0 / kMassRows;
-  const int ntl = sh_t0 < nr ? m.ntr - tile0 : 0;
+  const int ntl = sh_t0 < nr ? (nr + kMassRows - 1) / kMassRows - tile0 : 0;
   const int jmax = sh_jmax;
   const uint8_t* rimg = m.rows + ((long long)bh * m.ntr + tile0) * kRowBytes;
 

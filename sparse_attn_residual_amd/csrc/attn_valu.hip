@@ -51,6 +51,7 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a, float tau) {
   const int t = (int)(w % nq);
   const int h = (int)((w / nq) % c.H);
   const int b = (int)(w / ((long long)nq * c.H));
+  if (t >= count_of(c, r, b)) return;  // past this sequence's rows (ragged counts)
   const int d = c.d;
   const bool bf16 = a.dt == FL_BF16;
   const int i = r == 1 ? t : c.rows[r][(long long)b * nq + t];
@@ -131,6 +132,7 @@ __global__ __launch_bounds__(256) void k_um_valu(AttnArgs a, float tau) {
   const int t = (int)(w % nr);
   const int h = (int)((w / nr) % c.H);
   const int b = (int)(w / ((long long)nr * c.H));
+  if (t >= count_of(c, r, b)) return;  // past this sequence's rows (ragged counts)
   const int d = c.d;
   const bool bf16 = a.dt == FL_BF16;
   const int i = c.rows[r][(long long)b * nr + t];
@@ -189,9 +191,9 @@ __global__ __launch_bounds__(256) void k_mass_valu(AttnArgs a, const int32_t* ca
   const int j = cand ? cand[w] : tt;
   float kk[E], vv[E];
   load_kv<E>(c, r - 1, b, h, j, lane, bf16, kk, vv);
-  const int nr = c.n[r];
+  const int nr = count_of(c, r, b);
   const int nprev = r - 1 == 1 ? c.S : c.n[r - 1];
-  const int32_t* rows = c.rows[r] + (long long)b * nr;
+  const int32_t* rows = c.rows[r] + (long long)b * c.n[r];
   int lo = 0, hi = nr;  // first row >= j
   while (lo < hi) {
     int mid = (lo + hi) >> 1;

@@ -28,6 +28,7 @@ struct CacheGeo {
   int base_rb;                   // base record bytes
   const int32_t* rows[FL_MAX_LOOPS + 1];
   const int32_t* slot[FL_MAX_LOOPS + 1];
+  const int32_t* cnt[FL_MAX_LOOPS + 1];  // per-sequence |A_r| (NULL: n[r] for every sequence)
   const uint8_t* base;
   const uint8_t* res[FL_MAX_LOOPS + 1];
 };
@@ -38,6 +39,11 @@ __host__ __device__ inline int residual_record_bytes(int d, int bits) {
   return pad16(2 * (d * bits / 8) + 8 * (d / kGroup));
 }
 
+// Rows of A_r in sequence b: n[r] is the capacity and stride of rows[r] and
+// of the loop-r streams, cnt[r][b] the count when sequences differ.
+__device__ inline int count_of(const CacheGeo& c, int r, int b) {
+  return r == 1 ? c.S : (c.cnt[r] ? c.cnt[r][b] : c.n[r]);
+}
 // KV head that query head h reads (grouped-query attention; G = 1: h).
 __device__ inline int kv_head(const CacheGeo& c, int h) { return h / c.G; }
 // Address of the base record of token j of (layer l, seq b, KV head hk).

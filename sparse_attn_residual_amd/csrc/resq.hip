@@ -73,6 +73,7 @@ __global__ __launch_bounds__(256) void k_quant_res(CacheGeo c, int r, const T* _
   const int hk = (int)(lbh % c.Hkv);
   const int b = (int)((lbh / c.Hkv) % c.B);
   const int l = (int)(lbh / ((long long)c.Hkv * c.B));
+  if (t >= count_of(c, r, b)) return;  // past this sequence's rows (ragged counts)
   const int j = c.rows[r][(long long)b * nr + t];
 
   float x[kGroup], prev[kGroup];
@@ -134,18 +135,21 @@ __global__ __launch_bounds__(256) void k_quant_res(CacheGeo c, int r, const T* _
   }
 }
 
-// slot[b][j] = index of j in rows[b][0..n) or -1 (binary search; rows ascending).
-__global__ void k_build_slot(const int32_t* __restrict__ rows, int n, int S, int B, int32_t* __restrict__ slot) {
+// slot[b][j] = index of j in rows[b][0..cnt_b) or -1 (binary search; rows
+// ascending; rows of sequence b start at b * n; cnt NULL: cnt_b = n).
+__global__ void k_build_slot(const int32_t* __restrict__ rows, int n, const int32_t* __restrict__ cnt, int S, int B,
+                             int32_t* __restrict__ slot) {
   long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (long long)B * S) return;
   int b = (int)(gid / S), j = (int)(gid % S);
   const int32_t* rb = rows + (long long)b * n;
-  int lo = 0, hi = n;
+  const int cb = cnt ? cnt[b] : n;
+  int lo = 0, hi = cb;
   while (lo < hi) {
     int mid = (lo + hi) >> 1;
     if (rb[mid] < j) lo = mid + 1; else hi = mid;
   }
-  slot[gid] = (lo < n && rb[lo] == j) ? lo : -1;
+  slot[gid] = (lo < cb && rb[lo] == j) ? lo : -1;
 }
 
 hipError_t launch_quant_base(const CacheGeo& c, const void* k, const void* v, fl_dtype dt, uint8_t* base,
@@ -164,8 +168,8 @@ hipError_t launch_quant_base(const CacheGeo& c, const void* k, const void* v, fl
 
 hipError_t launch_build_slot(const CacheGeo& c, int r, int32_t* slot, hipStream_t st) {
   long long n = (long long)c.B * c.S;
-  hipLaunchKernelGGL(k_build_slot, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, c.rows[r], c.n[r], c.S, c.B,
-                     slot);
+  hipLaunchKernelGGL(k_build_slot, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, c.rows[r], c.n[r], c.cnt[r],
+                     c.S, c.B, slot);
   return hipGetLastError();
 }
 

@@ -25,8 +25,21 @@ def upload(x: np.ndarray, cfg) -> torch.Tensor:
 
 
 def rows_list(cfg, rows):
-    """rows[b][r] -> per-loop [B][n_r] arrays."""
-    return [np.stack([rows[b][r] for b in range(cfg.B)]) for r in range(cfg.R)]
+    """rows[b][r] -> per-loop [B][n_r] arrays (ragged sequences padded to the
+    capacity with their last row; the kernels read only the counted ones)."""
+    out = []
+    for r in range(cfg.R):
+        n = cfg.n[r]
+        out.append(np.stack([np.concatenate([rows[b][r], np.full(n - len(rows[b][r]), rows[b][r][-1], np.int32)])
+                             for b in range(cfg.B)]))
+    return out
+
+
+def counts_list(cfg):
+    """Per-loop [B] counts for a ragged batch, else None."""
+    if not cfg.ragged:
+        return None
+    return [np.array([cfg.counts(b)[r] for b in range(cfg.B)], np.int32) for r in range(cfg.R)]
 
 
 def run_prefill(cfg, rows, slices, *, mass_in=None, K_budget=None, mfma=None, mixed=False):
@@ -37,7 +50,8 @@ def run_prefill(cfg, rows, slices, *, mass_in=None, K_budget=None, mfma=None, mi
     import sparse_attn_residual_amd as fl
     K_budget = cfg.K if K_budget is None else K_budget
     R, B, H, S, d = cfg.R, cfg.B, cfg.H, cfg.S, cfg.d
-    cache = fl.CacheBuffers(1, B, H, S, d, R, cfg.n, cfg.bits, rows_list(cfg, rows), Hkv=cfg.kv_heads)
+    cache = fl.CacheBuffers(1, B, H, S, d, R, cfg.n, cfg.bits, rows_list(cfg, rows), Hkv=cfg.kv_heads,
+                            counts=counts_list(cfg))
     st = fl.PrefillState(B, H, S, d, mixed=mixed)
     dt = fl_dtype(cfg)
     qs = [upload(workloads.stack_loop(cfg, slices, r, "q"), cfg) for r in range(1, R + 1)]
@@ -91,7 +105,7 @@ def build_decode_cache(cfg, rows, slices, L=None):
     import sparse_attn_residual_amd as fl
     L = cfg.L if L is None else L
     cache = fl.CacheBuffers(L, cfg.B, cfg.H, cfg.S, cfg.d, cfg.R, cfg.n, cfg.bits, rows_list(cfg, rows),
-                            Hkv=cfg.kv_heads)
+                            Hkv=cfg.kv_heads, counts=counts_list(cfg))
     view = cache.layer_view(0)
     dt = fl_dtype(cfg)
     for r in range(1, cfg.R + 1):

@@ -84,6 +84,11 @@ def test_validation_errors():
     nest.n[2] = 65
     st, msg = _status("fl_kv_resq", ctypes.byref(nest), 1, ok_ptr, ok_ptr, fl.FL_F32, None)
     assert st == EINVAL and "nested" in msg
+    # a per-sequence count array must be 4-byte aligned
+    rc = _cache()
+    rc.cnt[2] = ok_ptr + 2
+    st, msg = _status("fl_kv_resq", ctypes.byref(rc), 2, ok_ptr, ok_ptr, fl.FL_F32, None)
+    assert st == EINVAL and "cnt" in msg
     # key/value heads must divide the query heads
     st, msg = _status("fl_kv_resq", ctypes.byref(_cache(Hkv=3)), 1, ok_ptr, ok_ptr, fl.FL_F32, None)
     assert st == EINVAL and "Hkv" in msg

@@ -118,3 +118,14 @@ def test_decode_gqa(dtype, H, Hkv):
                            col="0.10", bits=(8, 4, 4, 2), gamma=0.5, lognormal=0.5, L=2, decode=True, seed=6, Hkv=Hkv)
     _say("decode gqa", dtype, cfg)
     _decode_case(cfg, 1e-5 if dtype == "f32" else 2e-3, rel=dtype != "f32")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_ragged_counts(dtype):
+    """Sequences with different active-row counts share one cache (n_r is the
+    capacity, per-sequence counts bound the residual streams)."""
+    cfg = workloads.custom(name="decode-ragged", dtype=dtype, B=3, H=2, d=128, S=800, R=4, act=(1, 0.4, 0.2, 0.1),
+                           col="0.10", bits=(8, 4, 2, 4), gamma=0.5, lognormal=0.5, L=1, decode=True, seed=8,
+                           ragged=(0.3, 1, 0.65))
+    _say("decode ragged", dtype, cfg)
+    _decode_case(cfg, 1e-5 if dtype == "f32" else 2e-3, rel=dtype != "f32")

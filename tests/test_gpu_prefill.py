@@ -40,6 +40,7 @@ def _check_records(cfg, gpu, orc, heads):
                 k, v = ks[r - 1], vs[r - 1]
                 want = records.pack_residual(k["codes"], k["scale"], k["zero"], v["codes"], v["scale"], v["zero"],
                                              cfg.bits[r - 1])
+                got = got[:want.shape[0]]   # a ragged sequence fills the first |A_r| records
                 assert np.array_equal(got, want), (b, h, r)
 
 
@@ -332,4 +333,17 @@ def test_prefill_gqa(dtype, d, H, Hkv):
     _say("prefill gqa", cfg)
     heads = sorted({0, min(H // Hkv, H - 1), H - 1})
     _bf16_case(cfg, heads=heads, sel_eps=1e-5 if f32 else 2e-3, budgets=[390, 200, 90], tol=1e-5 if f32 else 2e-3,
+               rel=not f32)
+
+
+@pytest.mark.parametrize("dtype,d,ragged", [("f32", 64, (1, 0.55, 0.3)), ("bf16", 128, (0.4, 1, 0.7))])
+def test_prefill_ragged_counts(dtype, d, ragged):
+    """A batch whose sequences keep different numbers of active rows (a
+    per-sequence count array; n_r is the capacity): records, selections and
+    outputs per sequence against the oracle; pruning budgets."""
+    f32 = dtype == "f32"
+    cfg = workloads.custom(name="prefill-ragged", dtype=dtype, B=3, H=2, d=d, S=1100, R=4, act=(1, 0.5, 0.3, 0.15),
+                           col="0.30", bits=(8, 4, 2, 4), lognormal=None if f32 else 0.5, seed=41, ragged=ragged)
+    _say("prefill ragged", cfg, [cfg.counts(b) for b in range(cfg.B)])
+    _bf16_case(cfg, heads=[0, 1], sel_eps=1e-5 if f32 else 2e-3, budgets=[330, 170, 80], tol=1e-5 if f32 else 2e-3,
                rel=not f32)

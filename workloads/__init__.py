@@ -66,6 +66,7 @@ class Config:
     decode: bool = False
     seed: int = 0
     Hkv: int = 0               # key/value heads (0: H); query head h reads KV head h // (H // Hkv)
+    ragged: tuple = ()         # per-sequence factors m_b: |A_r| of sequence b = max(1, floor(m_b * n_r)), r >= 2
 
     @property
     def kv_heads(self) -> int:
@@ -85,6 +86,13 @@ class Config:
     def K(self) -> int:
         """Column budget per head for the sparse loops."""
         return frac_count(self.col, self.S)
+
+    def counts(self, b: int) -> list[int]:
+        """|A_r| of sequence b for r = 1..R (n when the batch is not ragged)."""
+        if not self.ragged:
+            return self.n
+        m = Fraction(str(self.ragged[b]))
+        return [self.S if r == 0 else max(1, math.floor(m * self.n[r])) for r in range(self.R)]
 
     def with_(self, **kw) -> "Config":
         d = dict(self.__dict__)
@@ -128,9 +136,10 @@ def active_rows(cfg: Config, b: int) -> list[np.ndarray]:
     """Nested active sets A_1 ⊇ A_2 ⊇ ... for sequence b (int32, ascending)."""
     rng = _rng(cfg, _T_ROWS, b)
     rows = [np.arange(cfg.S, dtype=np.int32)]
+    cnt = cfg.counts(b)
     for r in range(1, cfg.R):
         prev = rows[-1]
-        pick = rng.choice(prev.shape[0], cfg.n[r], replace=False)
+        pick = rng.choice(prev.shape[0], cnt[r], replace=False)
         rows.append(np.sort(prev[pick]).astype(np.int32))
     return rows
 
@@ -200,7 +209,13 @@ def stack_loop(cfg: Config, slices: dict, r: int, what: str, batches=None, heads
     batches = range(cfg.B) if batches is None else batches
     if heads is None:
         heads = range(cfg.H) if what == "q" else range(0, cfg.H, cfg.G)
-    return np.stack([np.stack([getattr(slices[(b, h)], what)[r - 1] for h in heads]) for b in batches])
+    n = cfg.S if r == 1 else cfg.n[r - 1]   # capacity: ragged sequences are zero-padded
+    out = np.zeros((len(batches), len(heads), n, cfg.d), np.float32)
+    for bi, b in enumerate(batches):
+        for hi, h in enumerate(heads):
+            x = getattr(slices[(b, h)], what)[r - 1]
+            out[bi, hi, :x.shape[0]] = x
+    return out
 
 
 def decode_queries(cfg: Config, layers=None, batches=None, heads=None) -> list[np.ndarray]:
@@ -229,10 +244,10 @@ def decode_queries(cfg: Config, layers=None, batches=None, heads=None) -> list[n
 
 
 def custom(name="custom", dtype="f32", B=1, H=1, d=64, S=64, R=4, act=(1.0, 0.5, 0.25, 0.125), col="0.25",
-           bits=(8, 4, 4, 4), gamma=0.5, lognormal=None, seed=0, L=1, decode=False, Hkv=0) -> Config:
+           bits=(8, 4, 4, 4), gamma=0.5, lognormal=None, seed=0, L=1, decode=False, Hkv=0, ragged=()) -> Config:
     """A small ad-hoc configuration (tests: ragged tails, edge cases)."""
     return Config(name, dtype, B, H, d, S, R, tuple(act), str(col), tuple(bits), gamma, lognormal, L, decode, seed,
-                  Hkv)
+                  Hkv, tuple(str(x) for x in ragged))
 
 
 def gen_hidden(cfg: Config, b: int, D: int, r: int, moving) -> tuple[np.ndarray, np.ndarray]:
