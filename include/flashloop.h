@@ -91,6 +91,9 @@ typedef void* fl_stream;
  *                      lie in [1, n[r]] and in [cnt[r+1][b], cnt[r-1][b]]
  *                      (nested sets; not checked: device memory); rows past a
  *                      sequence's count are neither read nor written.
+ *                      fl_kv_append writes them.
+ *   T                  tokens a decode step attends, positions [0, T) (0: S);
+ *                      S is then the capacity in positions.
  *   bits[r]            residual code width of loop r: 4 or 2 (bits[1] == 8)
  *   rows[r]            [B][n_r] int32, strictly ascending positions of A_r
  *                      (rows[1] unused: every row)
@@ -122,7 +125,8 @@ typedef struct fl_cache {
   uint8_t* base;
   uint8_t* res[FL_MAX_LOOPS + 1];
   int Hkv;
-  const int32_t* cnt[FL_MAX_LOOPS + 1];
+  int32_t* cnt[FL_MAX_LOOPS + 1];
+  int T;
 } fl_cache;
 
 /* Per-row prefill state, position indexed (one layer: the cache's L must be 1).
@@ -208,6 +212,25 @@ size_t fl_workspace_bytes(int which, const fl_cache* cache, int r, int K_prev, i
  */
 fl_status fl_kv_resq(const fl_cache* cache, int r, const void* k, const void* v, fl_dtype dtype,
                      fl_stream stream);
+
+/*
+ * fl_kv_append — decode: write one new token's loop-r keys and values into the
+ * cache (p1 §4.3; the token being decoded is active in every loop and attends
+ * itself, so its records must be in place before fl_loop_decode(r)).
+ *   k, v   [L][B][Hkv][d] (dtype): the token's loop-r values
+ *   pos    its position, the same in every sequence, 0 <= pos < S
+ *   r == 1: writes the base records of pos.
+ *   r >= 2: needs cache->cnt[r]; in every sequence b whose count
+ *           t = cnt[r][b] is below n[r], pos becomes row t (rows[r][b][t] =
+ *           pos, slot[r][b][pos] = t), record t of res[r] receives the
+ *           residual against x_hat^(r-1) of pos, and cnt[r][b] becomes t + 1.
+ *           A sequence at capacity is left unchanged.  pos must exceed the
+ *           sequence's active rows, and loops 1..r-1 of pos must be in place.
+ * The records are those fl_kv_resq writes for the same token (same codes).
+ * Raise cache->T past pos (host side) before decoding it.
+ */
+fl_status fl_kv_append(const fl_cache* cache, int r, int pos, const void* k, const void* v, fl_dtype dtype,
+                       fl_stream stream);
 
 /*
  * fl_colsel — loop-aware column selection for loop r >= 2 of one layer

@@ -31,6 +31,7 @@ class FlCache(ctypes.Structure):
         ("base", ctypes.c_void_p), ("res", ctypes.c_void_p * _N),
         ("Hkv", ctypes.c_int),
         ("cnt", ctypes.c_void_p * _N),
+        ("T", ctypes.c_int),
     ]
 
 
@@ -68,6 +69,8 @@ def _load():
     lib.fl_workspace_bytes.restype = S
     lib.fl_kv_resq.argtypes = [cp, I, P, P, I, P]
     lib.fl_kv_resq.restype = I
+    lib.fl_kv_append.argtypes = [cp, I, I, P, P, I, P]
+    lib.fl_kv_append.restype = I
     lib.fl_colsel.argtypes = [cp, I, P, I, ctypes.POINTER(FlState), I, P, I, P, P, P, P, S, P]
     lib.fl_colsel.restype = I
     lib.fl_loop_attn.argtypes = [cp, I, P, I, I, P, ctypes.POINTER(FlState), P, S, P]
@@ -126,6 +129,10 @@ def fl_workspace_bytes(which: int, cache: FlCache, r: int, K_prev: int, K_r: int
 
 def fl_kv_resq(cache: FlCache, r: int, k, v, dtype: int, stream=None) -> None:
     _check("fl_kv_resq", _lib.fl_kv_resq(ctypes.byref(cache), r, _ptr(k), _ptr(v), dtype, _stream(stream)))
+
+
+def fl_kv_append(cache: FlCache, r: int, pos: int, k, v, dtype: int, stream=None) -> None:
+    _check("fl_kv_append", _lib.fl_kv_append(ctypes.byref(cache), r, pos, _ptr(k), _ptr(v), dtype, _stream(stream)))
 
 
 def fl_colsel(cache: FlCache, r: int, q_prev, dtype: int, state: FlState, K_prev: int, cand, K_r: int,

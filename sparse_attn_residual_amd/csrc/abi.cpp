@@ -53,6 +53,7 @@ fl_status check_cache(const char* fn, const fl_cache* c, int r, bool need_res_r,
   if (r < 1 || r > c->R) return fail(FL_EINVAL, "%s: loop r = %d outside [1, R = %d]", fn, r, c->R);
   if (c->n[1] != c->S) return fail(FL_EINVAL, "%s: n[1] = %d must equal S = %d", fn, c->n[1], c->S);
   const int hkv = c->Hkv == 0 ? c->H : c->Hkv;
+  if (c->T < 0 || c->T > c->S) return fail(FL_EINVAL, "%s: T = %d outside [0, S = %d]", fn, c->T, c->S);
   if (hkv < 1 || c->H % hkv != 0)
     return fail(FL_EINVAL, "%s: Hkv = %d must divide H = %d", fn, c->Hkv, c->H);
   if ((long long)c->L * c->B * c->H * c->S > (1LL << 40)) return fail(FL_EUNSUPPORTED, "%s: cache too large", fn);
@@ -81,6 +82,7 @@ fl_status check_cache(const char* fn, const fl_cache* c, int r, bool need_res_r,
   geo->L = c->L; geo->B = c->B; geo->H = c->H; geo->S = c->S; geo->d = c->d; geo->R = c->R;
   geo->Hkv = hkv;
   geo->G = c->H / hkv;
+  geo->T = c->T == 0 ? c->S : c->T;
   geo->base = c->base;
   geo->base_rb = fl::base_record_bytes(c->d);
   for (int rr = 1; rr <= c->R; ++rr) {
@@ -177,6 +179,27 @@ fl_status fl_kv_resq(const fl_cache* cache, int r, const void* k, const void* v,
   e = fl::launch_build_slot(geo, r, cache->slot[r], st);
   if (e != hipSuccess) return hip_fail(e, fn);
   e = fl::launch_quant_res(geo, r, k, v, dtype, cache->res[r], st);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return FL_OK;
+}
+
+fl_status fl_kv_append(const fl_cache* cache, int r, int pos, const void* k, const void* v, fl_dtype dtype,
+                       fl_stream stream) {
+  const char* fn = "fl_kv_append";
+  g_err.clear();
+  fl::CacheGeo geo;
+  fl_status s = check_cache(fn, cache, r, true, &geo);
+  if (s != FL_OK) return s;
+  if ((s = check_dtype(fn, dtype)) != FL_OK) return s;
+  FL_NEED_PTR(k, "k");
+  FL_NEED_PTR(v, "v");
+  if (pos < 0 || pos >= cache->S) return fail(FL_EINVAL, "%s: pos = %d outside [0, S = %d)", fn, pos, cache->S);
+  if (r >= 2 && !cache->cnt[r])
+    return fail(FL_EINVAL, "%s: appending a row at loop %d needs the per-sequence counts cache->cnt[%d]", fn, r, r);
+  hipError_t e = fl::launch_append(geo, r, pos, k, v, dtype, cache->base, cache->res[r],
+                                   r >= 2 ? const_cast<int32_t*>(cache->rows[r]) : nullptr,
+                                   r >= 2 ? cache->slot[r] : nullptr, r >= 2 ? cache->cnt[r] : nullptr,
+                                   (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, fn);
   return FL_OK;
 }
@@ -313,8 +336,8 @@ fl_status fl_loop_decode(const fl_cache* cache, int r, const void* q, fl_dtype d
   if ((long long)cache->L * cache->B * cache->H > 0x7FFFFFFFLL)
     return fail(FL_EUNSUPPORTED, "%s: too many (layer, sequence, head) triples", fn);
   if (r >= 2) {
-    if (K_prev < 1 || K_prev > cache->S) return fail(FL_EINVAL, "%s: K_prev = %d outside [1, S]", fn, K_prev);
-    if (r == 2 && K_prev != cache->S) return fail(FL_EINVAL, "%s: at r = 2 K_prev must be S", fn);
+    if (K_prev < 1 || K_prev > geo.T) return fail(FL_EINVAL, "%s: K_prev = %d outside [1, T = %d]", fn, K_prev, geo.T);
+    if (r == 2 && K_prev != geo.T) return fail(FL_EINVAL, "%s: at r = 2 K_prev must be T = %d", fn, geo.T);
     if (K_r < 1 || K_r > K_prev) return fail(FL_EINVAL, "%s: K_r = %d outside [1, K_prev = %d]", fn, K_r, K_prev);
     if (K_r < K_prev && K_prev > kTopkMax)
       return fail(FL_EUNSUPPORTED, "%s: %d candidates (at most %d)", fn, K_prev, kTopkMax);

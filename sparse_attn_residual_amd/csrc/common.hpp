@@ -21,6 +21,7 @@ constexpr int kGroup = 32;  // quantization group (dims)
 struct CacheGeo {
   int L, B, H, S, d, R;
   int Hkv;                       // key/value heads (the streams are per KV head)
+  int T;                         // tokens a decode step attends: positions [0, T)
   int G;                         // query heads per KV head, H / Hkv
   int n[FL_MAX_LOOPS + 1];
   int bits[FL_MAX_LOOPS + 1];

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
   const uint8_t* recs = base_rec(c, l, b, kv_head(c, h0), 0);
   float* logit = a.logits + lbh0 * c.S;
   const uint16_t* scl = (const uint16_t*)(recs + 2 * d);
-  for (int j = gid; j < c.S; j += NG) {
+  for (int j = gid; j < c.T; j += NG) {
     const uint8_t* rec = recs + (long long)j * c.base_rb;
     const uint4 kw = *(const uint4*)(rec + sub * 16);
     const uint4 vw = *(const uint4*)(rec + d + sub * 16);
@@ -509,13 +509,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   const int pruned = a.K < a.K_prev;
   hipError_t e;
   if (pruned) {
-    const int32_t* cand = (a.r == 2 && a.K_prev == a.c.S) ? nullptr : a.sel;
+    const int32_t* cand = (a.r == 2 && a.K_prev == a.c.T) ? nullptr : a.sel;
     e = launch_topk(a.logits, a.c.S, cand, a.c.S, (int)P, a.K_prev, a.K, a.sel, a.c.S, a.logits, a.c.S, st);
     if (e != hipSuccess) return e;
   } else if (a.r == 2) {
-    // every position stays selected: sel = 0..S-1 (rows of stride S); the
+    // every position stays selected: sel = 0..T-1 (rows of stride S); the
     // loop-1 logits are already in place
-    e = launch_copy_sel(nullptr, (int)P, a.c.S, a.sel, st);
+    e = launch_copy_sel(nullptr, (int)P, a.c.T, a.sel, st, a.c.S);
     if (e != hipSuccess) return e;
   }
   const int nr = (a.r < kMaxFastLoops ? a.r : kMaxFastLoops) - 1;

@@ -11,6 +11,10 @@ namespace fl {
 hipError_t launch_quant_base(const CacheGeo& c, const void* k, const void* v, fl_dtype dt, uint8_t* base,
                              hipStream_t st);
 hipError_t launch_build_slot(const CacheGeo& c, int r, int32_t* slot, hipStream_t st);
+// One new token at position pos, loop r, from k, v [L][B][Hkv][d]: r == 1 the
+// base records; r >= 2 row cnt[r][b] of every sequence, then the counts.
+hipError_t launch_append(const CacheGeo& c, int r, int pos, const void* k, const void* v, fl_dtype dt,
+                         uint8_t* base, uint8_t* res, int32_t* rows, int32_t* slot, int32_t* cnt, hipStream_t st);
 hipError_t launch_quant_res(const CacheGeo& c, int r, const void* k, const void* v, fl_dtype dt, uint8_t* res,
                             hipStream_t st);
 
@@ -23,7 +27,7 @@ hipError_t launch_topk(const float* keys, long long key_stride, const int32_t* c
                        int P, int n, int K, int32_t* sel_out, long long sel_stride, float* keys_out,
                        long long keys_out_stride, hipStream_t st);
 // sel[p][t] = cand ? cand[p][t] : t for t < K
-hipError_t launch_copy_sel(const int32_t* cand, int P, int K, int32_t* sel, hipStream_t st);
+hipError_t launch_copy_sel(const int32_t* cand, int P, int K, int32_t* sel, hipStream_t st, long long sel_stride = 0);
 
 // ---- prefill attention family (one layer: l = 0).
 struct AttnArgs {

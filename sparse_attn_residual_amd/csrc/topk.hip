@@ -350,15 +350,18 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
   }
 }
 
-__global__ void k_copy_sel(const int32_t* __restrict__ cand, int P, int K, int32_t* __restrict__ sel) {
+__global__ void k_copy_sel(const int32_t* __restrict__ cand, int P, int K, int32_t* __restrict__ sel,
+                           long long sel_stride) {
   long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (long long)P * K) return;
-  sel[gid] = cand ? cand[gid] : (int32_t)(gid % K);
+  const long long p = gid / K, i = gid - p * K;
+  sel[p * sel_stride + i] = cand ? cand[gid] : (int32_t)i;
 }
 
-hipError_t launch_copy_sel(const int32_t* cand, int P, int K, int32_t* sel, hipStream_t st) {
+hipError_t launch_copy_sel(const int32_t* cand, int P, int K, int32_t* sel, hipStream_t st, long long sel_stride) {
   long long n = (long long)P * K;
-  hipLaunchKernelGGL(k_copy_sel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, cand, P, K, sel);
+  hipLaunchKernelGGL(k_copy_sel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, cand, P, K, sel,
+                     sel_stride > 0 ? sel_stride : K);
   return hipGetLastError();
 }
 

@@ -119,19 +119,23 @@ def build_decode_cache(cfg, rows, slices, L=None):
     return cache
 
 
-def run_decode(cfg, cache, queries, K_budget=None):
-    """queries[r-1]: float32 [L][B][H][d].  Returns per-loop snapshots."""
+def run_decode(cfg, cache, queries, K_budget=None, T=None):
+    """queries[r-1]: float32 [L][B][H][d].  T: tokens attended (the cache's
+    first T positions; None: all S).  Returns per-loop snapshots."""
     import sparse_attn_residual_amd as fl
     K_budget = cfg.K if K_budget is None else K_budget
+    T = cfg.S if T is None else T
     L = queries[0].shape[0]
     st = fl.DecodeState(L, cfg.B, cfg.H, cfg.S, cfg.d)
     dt = fl_dtype(cfg)
     out = []
-    K_prev = cfg.S
+    K_prev = T
+    c = cache.fl
+    c.T = T
     for r in range(1, cfg.R + 1):
         q = upload(queries[r - 1], cfg)
-        K = cfg.S if r == 1 else min(K_budget, K_prev)
-        fl.fl_loop_decode(cache.fl, r, q, dt, K_prev, K, st.fl)
+        K = T if r == 1 else min(K_budget, K_prev)
+        fl.fl_loop_decode(c, r, q, dt, K_prev, K, st.fl)
         torch.cuda.synchronize()
         snap = dict(O=st.O.cpu().numpy(), U=st.U.cpu().numpy(), M=st.M.cpu().numpy(), lse=st.lse.cpu().numpy(),
                     logits=st.logits[..., :K].cpu().numpy(), sel=st.sel[..., :K].cpu().numpy() if r > 1 else None)

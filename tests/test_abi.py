@@ -84,6 +84,13 @@ def test_validation_errors():
     nest.n[2] = 65
     st, msg = _status("fl_kv_resq", ctypes.byref(nest), 1, ok_ptr, ok_ptr, fl.FL_F32, None)
     assert st == EINVAL and "nested" in msg
+    # appending: the position must lie in the cache, a residual row needs counts
+    st, msg = _status("fl_kv_append", ctypes.byref(_cache()), 1, 64, ok_ptr, ok_ptr, fl.FL_F32, None)
+    assert st == EINVAL and "pos" in msg
+    st, msg = _status("fl_kv_append", ctypes.byref(_cache()), 2, 63, ok_ptr, ok_ptr, fl.FL_F32, None)
+    assert st == EINVAL and "cnt" in msg
+    st, msg = _status("fl_kv_append", ctypes.byref(_cache(T=65)), 1, 3, ok_ptr, ok_ptr, fl.FL_F32, None)
+    assert st == EINVAL and "T =" in msg
     # a per-sequence count array must be 4-byte aligned
     rc = _cache()
     rc.cnt[2] = ok_ptr + 2

@@ -129,3 +129,126 @@ def test_decode_ragged_counts(dtype):
                            ragged=(0.3, 1, 0.65))
     _say("decode ragged", dtype, cfg)
     _decode_case(cfg, 1e-5 if dtype == "f32" else 2e-3, rel=dtype != "f32")
+
+
+def _check_decode(cfg, gpu, slices, qs, T, tol, rel, K_budget=None):
+    """Decode outputs of every (layer, b, h) against the oracle over the first
+    T cached tokens, teacher-forced with the GPU's selections, which must
+    match the oracle's own up to near ties of the logits."""
+    import tests.gpu_harness as gh
+    K_budget = cfg.K if K_budget is None else K_budget
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            s = slices[(b, h)]
+            _, krec = quant.quantize_chain(s.k, s.rows, list(cfg.bits))
+            _, vrec = quant.quantize_chain(s.v, s.rows, list(cfg.bits))
+            krec, vrec = [x[:T] for x in krec], [x[:T] for x in vrec]
+            for l in range(cfg.L):
+                force = {r + 1: gpu[r]["sel"][l, b, h] for r in range(1, cfg.R)}
+                orc = decode.decode_slice(krec, vrec, [q[l, b, h] for q in qs], K_budget, sel_force=force)
+                cand = np.arange(T)
+                for r in range(cfg.R):
+                    if r >= 1:
+                        key = orc[r - 1]["logits"]
+                        own = prefill.topk(key, cand, min(K_budget, len(cand)))
+                        ok, nd = gh.near_tie_ok(gpu[r]["sel"][l, b, h], own, key - key.min(), cand,
+                                                1e-5 if not rel else 2e-3)
+                        assert ok, (l, b, h, r + 1, nd)
+                        cand = gpu[r]["sel"][l, b, h]
+                    O, o = gpu[r]["O"][l, b, h], orc[r]["O"]
+                    err = np.linalg.norm(O - o) / np.linalg.norm(o) if rel else np.max(np.abs(O - o))
+                    assert err <= tol, (l, b, h, r + 1, err)
+                    assert abs(gpu[r]["lse"][l, b, h] - orc[r]["lse"]) <= tol * max(1.0, abs(orc[r]["lse"]))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_partial_context(dtype):
+    """A cache with room for S positions decoding over its first T < S
+    (fl_cache.T): the dense loop, the top-K and the sparse loops see only
+    positions below T."""
+    import tests.gpu_harness as gh
+    cfg = workloads.custom(name="decode-partial", dtype=dtype, B=2, H=2, d=128, S=700, R=4, act=(1, 0.4, 0.2, 0.1),
+                           col="0.10", bits=(8, 4, 2, 4), gamma=0.5, lognormal=0.5, L=1, decode=True, seed=14)
+    T = 513
+    _say("decode partial context", dtype, T, cfg)
+    rows, slices = workloads.gen_batch(cfg)
+    cache = gh.build_decode_cache(cfg, rows, slices)
+    qs = workloads.decode_queries(cfg)
+    gpu = gh.run_decode(cfg, cache, qs, T=T)
+    _check_decode(cfg, gpu, slices, qs, T, 1e-5 if dtype == "f32" else 2e-3, rel=dtype != "f32")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_append(dtype):
+    """The token being decoded, appended loop by loop with fl_kv_append to a
+    cache of the earlier tokens, gives byte for byte the cache fl_kv_resq
+    builds for all tokens (base, residual records, rows, slots, counts), and
+    decoding over it matches the oracle.  Grouped heads, two layers."""
+    import torch
+    import sparse_attn_residual_amd as fl
+    import tests.gpu_harness as gh
+    cfg = workloads.custom(name="decode-append", dtype=dtype, B=2, H=4, d=128, S=640, R=4, act=(1, 0.4, 0.2, 0.1),
+                           col="0.10", bits=(8, 4, 2, 4), gamma=0.5, lognormal=0.5, L=2, decode=True, seed=12, Hkv=2)
+    S, R, B, L = cfg.S, cfg.R, cfg.B, cfg.L
+    _say("decode append", dtype, cfg)
+    last = np.array([S - 1], np.int32)
+    rows_full = {b: [np.union1d(x, last).astype(np.int32) for x in workloads.active_rows(cfg, b)] for b in range(B)}
+    slices = {(b, h): workloads.gen_slice(cfg, b, h, rows_full[b]) for b in range(B) for h in range(cfg.H)}
+    cnt_full = [np.array([len(rows_full[b][r]) for b in range(B)], np.int32) for r in range(R)]
+    cap = [int(c.max()) for c in cnt_full]
+
+    def padded(rws):
+        return [np.stack([np.concatenate([rws[b][r], np.full(cap[r] - len(rws[b][r]), rws[b][r][-1], np.int32)])
+                          for b in range(B)]) for r in range(R)]
+
+    def stack(r, what):
+        out = np.zeros((B, cfg.kv_heads, cap[r - 1] if r > 1 else S, cfg.d), np.float32)
+        for b in range(B):
+            for hk in range(cfg.kv_heads):
+                x = getattr(slices[(b, hk * cfg.G)], what)[r - 1]
+                out[b, hk, :x.shape[0]] = x
+        return out
+
+    def build(rws, counts, drop_last):
+        cache = fl.CacheBuffers(L, B, cfg.H, S, cfg.d, R, cap, cfg.bits, padded(rws), Hkv=cfg.kv_heads, counts=counts)
+        for layer in range(L):
+            view = cache.layer_view(layer)
+            for r in range(1, R + 1):
+                k, v = stack(r, "k"), stack(r, "v")
+                if drop_last and r == 1:
+                    k[:, :, S - 1] = 0.0
+                    v[:, :, S - 1] = 0.0
+                fl.fl_kv_resq(view, r, gh.upload(k, cfg), gh.upload(v, cfg), gh.fl_dtype(cfg))
+        torch.cuda.synchronize()
+        return cache
+
+    full = build(rows_full, cnt_full, False)
+    rows_pre = {b: [rows_full[b][0]] + [x[:-1] for x in rows_full[b][1:]] for b in range(B)}
+    cnt_pre = [cnt_full[0]] + [c - 1 for c in cnt_full[1:]]
+    app = build(rows_pre, cnt_pre, True)
+    for r in range(1, R + 1):
+        x = {w: np.zeros((L, B, cfg.kv_heads, cfg.d), np.float32) for w in ("k", "v")}
+        for w in ("k", "v"):
+            st = stack(r, w)
+            for b in range(B):
+                t = S - 1 if r == 1 else cnt_full[r - 1][b] - 1
+                x[w][:, b] = st[b, :, t][None]
+        fl.fl_kv_append(app.fl, r, S - 1, gh.upload(x["k"], cfg), gh.upload(x["v"], cfg), gh.fl_dtype(cfg))
+    torch.cuda.synchronize()
+    assert np.array_equal(app.base.cpu().numpy(), full.base.cpu().numpy())
+    for r in range(2, R + 1):
+        assert np.array_equal(app.cnt[r - 1].cpu().numpy(), full.cnt[r - 1].cpu().numpy()), r
+        ra, rf = app.res_records(r).cpu().numpy(), full.res_records(r).cpu().numpy()
+        sa, sf = app.rows[r - 1].cpu().numpy(), full.rows[r - 1].cpu().numpy()
+        for b in range(B):
+            c = cnt_full[r - 1][b]
+            assert np.array_equal(ra[:, b, :, :c], rf[:, b, :, :c]), (r, b)
+            assert np.array_equal(sa[b, :c], sf[b, :c]), (r, b)
+        assert np.array_equal(app.slot[r - 1].cpu().numpy(), full.slot[r - 1].cpu().numpy()), r
+    qs = workloads.decode_queries(cfg)
+    ga = gh.run_decode(cfg, app, qs)
+    gf = gh.run_decode(cfg, full, qs)
+    for r in range(R):
+        for key in ("O", "lse", "M"):
+            assert np.array_equal(ga[r][key], gf[r][key]), (r + 1, key)
+    _check_decode(cfg, ga, slices, qs, S, 1e-5 if dtype == "f32" else 2e-3, rel=dtype != "f32")
