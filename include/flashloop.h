@@ -94,6 +94,27 @@ typedef void* fl_stream;
  *                      fl_kv_append writes them.
  *   T                  tokens a decode step attends, positions [0, T) (0: S);
  *                      S is then the capacity in positions.
+ *   fmt                FL_FMT_WORKLOAD (the records below) or FL_FMT_PAPER
+ *                      (the paper's own format, head dim 128; see below).
+ *
+ * FL_FMT_PAPER (p1 App. E: INT4 asymmetric group-wise quantization, group
+ * 64, for the base and every residual; post-RoPE keys per channel, values
+ * per token; the 64 most recent tokens in BF16).  Sq = max(0, S - 64)
+ * positions are quantized, [Sq, S) is the tail.  Each (layer, sequence, KV
+ * head) owns, per loop, one stream of fl_stream_bytes(cache, r) bytes:
+ *   m entries of 144 bytes (loop 1: m = Sq positions; loop r: m = n[r], the
+ *   compact rows): K codes 64 B | V codes 64 B (4-bit, dim 2i in the low
+ *   nibble of byte i) | V scale, zero fp16 of dims 0-63, then of 64-127 | 8
+ *   zero bytes;
+ *   ceil(m / 64) key blocks of 512 bytes: fp16 scales of channels 0..127,
+ *   then their fp16 zeros, for entries [64 k, 64 k + 64) (a key group is one
+ *   channel over 64 consecutive entries; loop r >= 2: the active rows below
+ *   Sq, which come first in rows[r]);
+ *   64 tail slots of 512 bytes: K then V of position Sq + slot in bf16 (the
+ *   loop's own values of an active tail token).
+ * Per group: z = fp16 rounded down of the minimum, s = fp16 rounded up of
+ * ((max - z) / 15), c = clamp(rint((x - z) / s), 0, 15) (0 when s == 0),
+ * x_hat = fma(c, s, z); loop 1 quantizes x, loop r >= 2 x^(r) - x_hat^(r-1).
  *   bits[r]            residual code width of loop r: 4 or 2 (bits[1] == 8)
  *   rows[r]            [B][n_r] int32, strictly ascending positions of A_r
  *                      (rows[1] unused: every row)
@@ -127,6 +148,7 @@ typedef struct fl_cache {
   int Hkv;
   int32_t* cnt[FL_MAX_LOOPS + 1];
   int T;
+  int fmt;
 } fl_cache;
 
 /* Per-row prefill state, position indexed (one layer: the cache's L must be 1).
@@ -183,6 +205,14 @@ const char* fl_last_error(void);
 /* Record sizes in bytes (see fl_cache); 0 for unsupported d or bits. */
 size_t fl_base_record_bytes(int d);
 size_t fl_residual_record_bytes(int d, int bits);
+
+#define FL_FMT_WORKLOAD 0
+#define FL_FMT_PAPER 1
+
+/* Bytes of one (layer, sequence, KV head) stream of loop r (r == 1: the base
+ * records of all S positions; r >= 2: n[r] residual records), in the cache's
+ * format; 0 for an invalid cache or r. */
+size_t fl_stream_bytes(const fl_cache* cache, int r);
 
 /* Workspace sizes in bytes for the calls that take one.
  *   which = FL_WS_COLSEL: fl_colsel at loop r with K_prev candidates

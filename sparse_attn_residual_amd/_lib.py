@@ -7,6 +7,7 @@ import os
 FL_MAX_LOOPS = 16
 FL_F32, FL_BF16 = 0, 1
 FL_WS_COLSEL, FL_WS_ATTN, FL_WS_DECODE = 1, 2, 3
+FL_FMT_WORKLOAD, FL_FMT_PAPER = 0, 1
 _N = FL_MAX_LOOPS + 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,6 +33,7 @@ class FlCache(ctypes.Structure):
         ("Hkv", ctypes.c_int),
         ("cnt", ctypes.c_void_p * _N),
         ("T", ctypes.c_int),
+        ("fmt", ctypes.c_int),
     ]
 
 
@@ -69,6 +71,8 @@ def _load():
     lib.fl_workspace_bytes.restype = S
     lib.fl_kv_resq.argtypes = [cp, I, P, P, I, P]
     lib.fl_kv_resq.restype = I
+    lib.fl_stream_bytes.argtypes = [cp, I]
+    lib.fl_stream_bytes.restype = S
     lib.fl_kv_append.argtypes = [cp, I, I, P, P, I, P]
     lib.fl_kv_append.restype = I
     lib.fl_colsel.argtypes = [cp, I, P, I, ctypes.POINTER(FlState), I, P, I, P, P, P, P, S, P]
@@ -129,6 +133,10 @@ def fl_workspace_bytes(which: int, cache: FlCache, r: int, K_prev: int, K_r: int
 
 def fl_kv_resq(cache: FlCache, r: int, k, v, dtype: int, stream=None) -> None:
     _check("fl_kv_resq", _lib.fl_kv_resq(ctypes.byref(cache), r, _ptr(k), _ptr(v), dtype, _stream(stream)))
+
+
+def fl_stream_bytes(cache: FlCache, r: int) -> int:
+    return _lib.fl_stream_bytes(ctypes.byref(cache), r)
 
 
 def fl_kv_append(cache: FlCache, r: int, pos: int, k, v, dtype: int, stream=None) -> None:

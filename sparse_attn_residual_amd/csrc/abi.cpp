@@ -54,6 +54,10 @@ fl_status check_cache(const char* fn, const fl_cache* c, int r, bool need_res_r,
   if (c->n[1] != c->S) return fail(FL_EINVAL, "%s: n[1] = %d must equal S = %d", fn, c->n[1], c->S);
   const int hkv = c->Hkv == 0 ? c->H : c->Hkv;
   if (c->T < 0 || c->T > c->S) return fail(FL_EINVAL, "%s: T = %d outside [0, S = %d]", fn, c->T, c->S);
+  if (c->fmt != FL_FMT_WORKLOAD && c->fmt != FL_FMT_PAPER)
+    return fail(FL_EUNSUPPORTED, "%s: cache format %d (supported: FL_FMT_WORKLOAD, FL_FMT_PAPER)", fn, c->fmt);
+  if (c->fmt == FL_FMT_PAPER && c->d != 128)
+    return fail(FL_EUNSUPPORTED, "%s: the paper format needs head dim 128 (got %d)", fn, c->d);
   if (hkv < 1 || c->H % hkv != 0)
     return fail(FL_EINVAL, "%s: Hkv = %d must divide H = %d", fn, c->Hkv, c->H);
   if ((long long)c->L * c->B * c->H * c->S > (1LL << 40)) return fail(FL_EUNSUPPORTED, "%s: cache too large", fn);
@@ -83,6 +87,8 @@ fl_status check_cache(const char* fn, const fl_cache* c, int r, bool need_res_r,
   geo->Hkv = hkv;
   geo->G = c->H / hkv;
   geo->T = c->T == 0 ? c->S : c->T;
+  geo->fmt = c->fmt;
+  geo->Sq = c->S > fl::kPTailN ? c->S - fl::kPTailN : 0;
   geo->base = c->base;
   geo->base_rb = fl::base_record_bytes(c->d);
   for (int rr = 1; rr <= c->R; ++rr) {
@@ -93,7 +99,10 @@ fl_status check_cache(const char* fn, const fl_cache* c, int r, bool need_res_r,
     geo->cnt[rr] = rr == 1 ? nullptr : c->cnt[rr];
     geo->res[rr] = c->res[rr];
     geo->res_rb[rr] = rr == 1 ? 0 : fl::residual_record_bytes(c->d, c->bits[rr]);
+    geo->pm[rr] = rr == 1 ? geo->Sq : c->n[rr];
+    geo->pbytes[rr] = fl::paper_stream_bytes(geo->pm[rr]);
   }
+  geo->res[1] = c->base;  // loop 1's stream of the paper format
   return FL_OK;
 }
 
@@ -124,6 +133,18 @@ const char* fl_last_error(void) { return g_err.c_str(); }
 
 size_t fl_base_record_bytes(int d) { return (d == 64 || d == 128) ? (size_t)fl::base_record_bytes(d) : 0; }
 
+size_t fl_stream_bytes(const fl_cache* c, int r) {
+  if (!c || r < 1 || r > c->R || r > FL_MAX_LOOPS || (c->d != 64 && c->d != 128)) return 0;
+  if (c->fmt == FL_FMT_PAPER) {
+    if (c->d != 128) return 0;
+    const int Sq = c->S > fl::kPTailN ? c->S - fl::kPTailN : 0;
+    return (size_t)fl::paper_stream_bytes(r == 1 ? Sq : c->n[r]);
+  }
+  if (r == 1) return (size_t)c->S * fl::base_record_bytes(c->d);
+  if (c->bits[r] != 2 && c->bits[r] != 4) return 0;
+  return (size_t)c->n[r] * fl::residual_record_bytes(c->d, c->bits[r]);
+}
+
 size_t fl_residual_record_bytes(int d, int bits) {
   if ((d != 64 && d != 128) || (bits != 2 && bits != 4)) return 0;
   return (size_t)fl::residual_record_bytes(d, bits);
@@ -152,7 +173,7 @@ size_t fl_workspace_bytes(int which, const fl_cache* cache, int r, int K_prev, i
     // masses, then (in turn) what the mass pass reads and the tiles of the
     // selected columns the cached-mass pass gathers
     if (r > cache->R || r < 2) return 0;
-    const bool base = r == 2 && K_prev == cache->S;
+    const bool base = r == 2 && K_prev == cache->S && cache->fmt == FL_FMT_WORKLOAD;
     return align256((size_t)cache->B * cache->H * (size_t)K_prev * sizeof(float)) +
            std::max(tiles_bytes(cache, K_r), mass_pass_bytes(cache, r, base, K_prev));
   }
@@ -172,13 +193,15 @@ fl_status fl_kv_resq(const fl_cache* cache, int r, const void* k, const void* v,
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (r == 1) {
-    e = fl::launch_quant_base(geo, k, v, dtype, cache->base, st);
+    e = geo.fmt == FL_FMT_PAPER ? fl::launch_paper_quant(geo, 1, k, v, dtype, cache->base, st)
+                                : fl::launch_quant_base(geo, k, v, dtype, cache->base, st);
     if (e != hipSuccess) return hip_fail(e, fn);
     return FL_OK;
   }
   e = fl::launch_build_slot(geo, r, cache->slot[r], st);
   if (e != hipSuccess) return hip_fail(e, fn);
-  e = fl::launch_quant_res(geo, r, k, v, dtype, cache->res[r], st);
+  e = geo.fmt == FL_FMT_PAPER ? fl::launch_paper_quant(geo, r, k, v, dtype, cache->res[r], st)
+                              : fl::launch_quant_res(geo, r, k, v, dtype, cache->res[r], st);
   if (e != hipSuccess) return hip_fail(e, fn);
   return FL_OK;
 }
@@ -194,6 +217,8 @@ fl_status fl_kv_append(const fl_cache* cache, int r, int pos, const void* k, con
   FL_NEED_PTR(k, "k");
   FL_NEED_PTR(v, "v");
   if (pos < 0 || pos >= cache->S) return fail(FL_EINVAL, "%s: pos = %d outside [0, S = %d)", fn, pos, cache->S);
+  if (geo.fmt == FL_FMT_PAPER)
+    return fail(FL_EUNSUPPORTED, "%s: appending to the paper format (its key groups span 64 tokens)", fn);
   if (r >= 2 && !cache->cnt[r])
     return fail(FL_EINVAL, "%s: appending a row at loop %d needs the per-sequence counts cache->cnt[%d]", fn, r, r);
   hipError_t e = fl::launch_append(geo, r, pos, k, v, dtype, cache->base, cache->res[r],
@@ -231,7 +256,8 @@ fl_status fl_colsel(const fl_cache* cache, int r, const void* q_prev, fl_dtype d
   // what the mass pass reads, then (reusing the space) the tiles of the
   // selected columns the cached-mass pass gathers
   const size_t pass_ws = std::max(prune ? tiles_bytes(cache, K_r) : 0,
-                                  need_mass ? mass_pass_bytes(cache, r, r == 2 && !cand, K_prev) : 0);
+                                  need_mass ? mass_pass_bytes(cache, r, r == 2 && !cand && geo.fmt == FL_FMT_WORKLOAD,
+                                                              K_prev) : 0);
   const size_t need = (need_mass && !mass_out ? mass_ws : 0) + pass_ws;
   if (need > 0) {
     if (!ws || ws_bytes < need)

@@ -109,8 +109,14 @@ __global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const i
   const int j = idx < K ? (sel ? sel[(long long)bh * K + idx] : idx) : -1;
   float x[32];
   // K rows (bf16)
-  if (j >= 0) chain_group(c, rc, 0, b, hk, j, 0, g, x);
-  else {
+  if (j >= 0) {
+    if (c.fmt == kFmtPaper) {
+      paper_chain16(c, rc, 0, b, hk, j, 0, g * 32, x);
+      paper_chain16(c, rc, 0, b, hk, j, 0, g * 32 + 16, x + 16);
+    } else {
+      chain_group(c, rc, 0, b, hk, j, 0, g, x);
+    }
+  } else {
 #pragma unroll
     for (int e = 0; e < 32; ++e) x[e] = 0.0f;
   }
@@ -122,8 +128,14 @@ __global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const i
                           pack_bf16x2(x[8 * i + 4], x[8 * i + 5]), pack_bf16x2(x[8 * i + 6], x[8 * i + 7]));
   }
   // V^T rows (bf16 value in fp16)
-  if (j >= 0) chain_group(c, rc, 0, b, hk, j, 1, g, x);
-  else {
+  if (j >= 0) {
+    if (c.fmt == kFmtPaper) {
+      paper_chain16(c, rc, 0, b, hk, j, 1, g * 32, x);
+      paper_chain16(c, rc, 0, b, hk, j, 1, g * 32 + 16, x + 16);
+    } else {
+      chain_group(c, rc, 0, b, hk, j, 1, g, x);
+    }
+  } else {
 #pragma unroll
     for (int e = 0; e < 32; ++e) x[e] = 0.0f;
   }
@@ -858,7 +870,8 @@ hipError_t launch_mass_mfma(const AttnArgs& a, const int32_t* cand, int K_prev, 
   m.mass = mass;
   m.c2 = c2_of(a.c.d);
   m.ncb = (K_prev + 32 * kMassNW - 1) / (32 * kMassNW);
-  const bool base = !cand && a.r == 2;  // loop-1 chain = the base records themselves
+  // loop-1 chain = the base records themselves (workload format)
+  const bool base = !cand && a.r == 2 && a.c.fmt != kFmtPaper;
   uint8_t* rows = ws;
   if (!base) {
     hipError_t e = launch_gather(a.c, a.r - 1, cand, K_prev, ws, st);

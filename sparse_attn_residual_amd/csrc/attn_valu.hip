@@ -24,8 +24,11 @@ template <int E>
 __device__ inline void load_kv(const CacheGeo& c, int r, int b, int h, int j, int lane, bool bf16, float* k, float* v) {
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    float kk = chain_elem(c, r, 0, b, kv_head(c, h), j, 0, lane * E + e);
-    float vv = chain_elem(c, r, 0, b, kv_head(c, h), j, 1, lane * E + e);
+    const bool paper = c.fmt == kFmtPaper;
+    float kk = paper ? paper_elem(c, r, 0, b, kv_head(c, h), j, 0, lane * E + e)
+                     : chain_elem(c, r, 0, b, kv_head(c, h), j, 0, lane * E + e);
+    float vv = paper ? paper_elem(c, r, 0, b, kv_head(c, h), j, 1, lane * E + e)
+                     : chain_elem(c, r, 0, b, kv_head(c, h), j, 1, lane * E + e);
     k[e] = bf16 ? round_bf16(kk) : kk;
     v[e] = bf16 ? round_bf16(vv) : vv;
   }

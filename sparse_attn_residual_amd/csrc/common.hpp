@@ -22,6 +22,13 @@ struct CacheGeo {
   int L, B, H, S, d, R;
   int Hkv;                       // key/value heads (the streams are per KV head)
   int T;                         // tokens a decode step attends: positions [0, T)
+  int fmt;                       // FL_FMT_WORKLOAD or FL_FMT_PAPER (record layout below)
+  int Sq;                        // paper format: quantized positions [0, Sq), the tail [Sq, S)
+  // paper format, per loop: entries of a stream (loop 1: Sq) and its bytes;
+  // res[1] points at the base.  Kept as arrays so that a loop index selects
+  // them without choosing between fields.
+  int pm[FL_MAX_LOOPS + 1];
+  long long pbytes[FL_MAX_LOOPS + 1];
   int G;                         // query heads per KV head, H / Hkv
   int n[FL_MAX_LOOPS + 1];
   int bits[FL_MAX_LOOPS + 1];
@@ -42,18 +49,24 @@ __host__ __device__ inline int residual_record_bytes(int d, int bits) {
 
 // Rows of A_r in sequence b: n[r] is the capacity and stride of rows[r] and
 // of the loop-r streams, cnt[r][b] the count when sequences differ.
-__device__ inline int count_of(const CacheGeo& c, int r, int b) {
-  return r == 1 ? c.S : (c.cnt[r] ? c.cnt[r][b] : c.n[r]);
+__device__ __forceinline__ int count_of(const CacheGeo& c, int r, int b) {
+  // n[1] == S and cnt[1] == NULL.  The capacity is taken as a wave-uniform
+  // value first, so the compiler does not turn the choice into one load
+  // through a pointer into the by-value geometry argument (which would copy
+  // the whole argument to scratch).
+  const int n = __builtin_amdgcn_readfirstlane(c.n[r]);
+  const int32_t* cnt = c.cnt[r];
+  return cnt ? cnt[b] : n;
 }
 // KV head that query head h reads (grouped-query attention; G = 1: h).
-__device__ inline int kv_head(const CacheGeo& c, int h) { return h / c.G; }
+__device__ __forceinline__ int kv_head(const CacheGeo& c, int h) { return h / c.G; }
 // Address of the base record of token j of (layer l, seq b, KV head hk).
-__device__ inline const uint8_t* base_rec(const CacheGeo& c, int l, int b, int hk, int j) {
+__device__ __forceinline__ const uint8_t* base_rec(const CacheGeo& c, int l, int b, int hk, int j) {
   long long idx = (((long long)l * c.B + b) * c.Hkv + hk) * c.S + j;
   return c.base + idx * c.base_rb;
 }
 // Address of the loop-r residual record number t (t = slot) of (l, b, hk).
-__device__ inline const uint8_t* res_rec(const CacheGeo& c, int r, int l, int b, int hk, int t) {
+__device__ __forceinline__ const uint8_t* res_rec(const CacheGeo& c, int r, int l, int b, int hk, int t) {
   long long idx = (((long long)l * c.B + b) * c.Hkv + hk) * c.n[r] + t;
   return c.res[r] + idx * c.res_rb[r];
 }
@@ -120,7 +133,7 @@ __device__ inline float res_elem(const uint8_t* rec, int d, int bits, int kv, in
 // Reconstruction x_hat^(r) of element e of token j: the base plus the
 // residuals of loops 2..r in which j was active (sets are nested, so the
 // chain stops at the first loop where j is inactive).
-__device__ inline float chain_elem(const CacheGeo& c, int r, int l, int b, int hk, int j, int kv, int e) {
+__device__ __forceinline__ float chain_elem(const CacheGeo& c, int r, int l, int b, int hk, int j, int kv, int e) {
   float x = base_elem(base_rec(c, l, b, hk, j), c.d, kv, e);
   for (int rr = 2; rr <= r; ++rr) {
     int t = c.slot[rr][(long long)b * c.S + j];
@@ -133,7 +146,7 @@ __device__ inline float chain_elem(const CacheGeo& c, int r, int l, int b, int h
 // The same reconstruction for the 32 dims [32g, 32g+32) of one group, with
 // the records read by vector loads: the operations and their order are those
 // of chain_elem, so the values are the same.
-__device__ inline void chain_group(const CacheGeo& c, int r, int l, int b, int hk, int j, int kv, int g, float* x) {
+__device__ __forceinline__ void chain_group(const CacheGeo& c, int r, int l, int b, int hk, int j, int kv, int g, float* x) {
   const int d = c.d, G = d / kGroup;
   const uint8_t* rec = base_rec(c, l, b, hk, j);
   const uint4 w0 = *(const uint4*)(rec + kv * d + g * kGroup);
@@ -164,6 +177,123 @@ __device__ inline void chain_group(const CacheGeo& c, int r, int l, int b, int h
       for (int e = 0; e < kGroup; ++e)
         x[e] = x[e] + __builtin_fmaf((float)((ws[e >> 4] >> (2 * (e & 15))) & 3), rs, rz);
     }
+  }
+}
+
+// ---------------------------------------------------------------- the paper's format
+// (FL_FMT_PAPER, head dim 128).  Every (layer, sequence, KV head) owns one
+// stream per loop: m entries (loop 1: the positions [0, Sq); loop r: the
+// capacity n[r] of its compact rows) of kPRec bytes
+//   K codes 64 B | V codes 64 B (4-bit, dim 2i in the low nibble of byte i) |
+//   V scale, zero (fp16) of dims 0-63, then of dims 64-127 | zero padding,
+// then ceil(m / 64) key blocks of kPKMeta bytes (fp16 scale of channels
+// 0..127, then their fp16 zeros) for entries [64 blk, 64 blk + 64), then 64
+// tail slots of kPTail bytes (K then V, bf16) for positions Sq + slot.
+constexpr int kFmtPaper = FL_FMT_PAPER;
+constexpr int kPRec = 144, kPKMeta = 512, kPTail = 512, kPGroup = 64, kPTailN = 64;
+__host__ __device__ inline long long paper_stream_bytes(int m) {
+  return (long long)m * kPRec + (long long)((m + kPGroup - 1) / kPGroup) * kPKMeta + (long long)kPTailN * kPTail;
+}
+__device__ __forceinline__ const uint8_t* paper_stream(const CacheGeo& c, int r, int l, int b, int hk) {
+  const long long lbh = ((long long)l * c.B + b) * c.Hkv + hk;
+  return c.res[r] + lbh * c.pbytes[r];
+}
+__host__ __device__ __forceinline__ int paper_entries(const CacheGeo& c, int r) { return c.pm[r]; }
+
+// Dequantized dims [e0, e0 + 16) (e0 a multiple of 16) of K (kv = 0) or V of
+// entry t of a paper-format stream with m entries: fma(code, scale, zero).
+__device__ __forceinline__ void paper_deq16(const uint8_t* st, int m, int t, int kv, int e0, float* x) {
+  const uint8_t* rec = st + (long long)t * kPRec;
+  const uint2 w = *(const uint2*)(rec + kv * 64 + e0 / 2);
+  const uint32_t ws[2] = {w.x, w.y};
+  if (kv == 0) {
+    const uint16_t* meta = (const uint16_t*)(st + (long long)m * kPRec + (long long)(t / kPGroup) * kPKMeta);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float code = (float)((ws[e >> 3] >> (4 * (e & 7))) & 15);
+      x[e] = __builtin_fmaf(code, h2f(meta[e0 + e]), h2f(meta[128 + e0 + e]));
+    }
+  } else {
+    const uint16_t* vm = (const uint16_t*)(rec + 128 + (e0 / 64) * 4);
+    const float s = h2f(vm[0]), z = h2f(vm[1]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) x[e] = __builtin_fmaf((float)((ws[e >> 3] >> (4 * (e & 7))) & 15), s, z);
+  }
+}
+
+// One element of paper_chain16 (the quantizers' previous-loop values).
+__device__ __forceinline__ float paper_deq1(const uint8_t* st, int m, int t, int kv, int e) {
+  const uint8_t* rec = st + (long long)t * kPRec;
+  const float code = (float)((rec[kv * 64 + e / 2] >> (4 * (e & 1))) & 15);
+  if (kv == 0) {
+    const uint16_t* meta = (const uint16_t*)(st + (long long)m * kPRec + (long long)(t / kPGroup) * kPKMeta);
+    return __builtin_fmaf(code, h2f(meta[e]), h2f(meta[128 + e]));
+  }
+  const uint16_t* vm = (const uint16_t*)(rec + 128 + (e / 64) * 4);
+  return __builtin_fmaf(code, h2f(vm[0]), h2f(vm[1]));
+}
+__device__ __forceinline__ const uint16_t* paper_tail(const CacheGeo& c, int r, int l, int b, int hk, int j, int kv) {
+  const int m = paper_entries(c, r);
+  return (const uint16_t*)(paper_stream(c, r, l, b, hk) + (long long)m * kPRec +
+                           (long long)((m + kPGroup - 1) / kPGroup) * kPKMeta + (long long)(j - c.Sq) * kPTail +
+                           kv * 256);
+}
+__device__ __forceinline__ float paper_elem(const CacheGeo& c, int r, int l, int b, int hk, int j, int kv, int e) {
+  if (j >= c.Sq) {
+    int rr = 1;
+    for (int q = 2; q <= r; ++q) {
+      if (c.slot[q][(long long)b * c.S + j] < 0) break;
+      rr = q;
+    }
+    return bf16_to_f32(paper_tail(c, rr, l, b, hk, j, kv)[e]);
+  }
+  float x = paper_deq1(paper_stream(c, 1, l, b, hk), c.pm[1], j, kv, e);
+  for (int rr = 2; rr <= r; ++rr) {
+    const int t = c.slot[rr][(long long)b * c.S + j];
+    if (t < 0) break;
+    x = x + paper_deq1(paper_stream(c, rr, l, b, hk), c.pm[rr], t, kv, e);
+  }
+  return x;
+}
+// Entries of sequence b's loop-r stream that are quantized: positions [0, Sq)
+// at loop 1; at loop r the active rows below Sq (rows ascend).
+__device__ __forceinline__ int paper_body(const CacheGeo& c, int r, int b) {
+  if (r == 1) return c.Sq;
+  const int cnt = count_of(c, r, b);
+  const int32_t* rows = c.rows[r] + (long long)b * c.n[r];
+  int lo = 0, hi = cnt;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (rows[mid] < c.Sq) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// x_hat^(r) of dims [e0, e0 + 16) of K or V of token j (KV head hk): a tail
+// token reads the bf16 slot of the last loop <= r in which it is active; any
+// other token adds, in fp32 and loop order, the base and the residuals of
+// the loops in which it is active (sets are nested).
+__device__ __forceinline__ void paper_chain16(const CacheGeo& c, int r, int l, int b, int hk, int j, int kv, int e0,
+                                     float* x) {
+  if (j >= c.Sq) {
+    int rr = 1;
+    for (int q = 2; q <= r; ++q) {
+      if (c.slot[q][(long long)b * c.S + j] < 0) break;
+      rr = q;
+    }
+    const uint16_t* tv = paper_tail(c, rr, l, b, hk, j, kv) + e0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) x[e] = bf16_to_f32(tv[e]);
+    return;
+  }
+  paper_deq16(paper_stream(c, 1, l, b, hk), c.pm[1], j, kv, e0, x);
+  for (int rr = 2; rr <= r; ++rr) {
+    const int t = c.slot[rr][(long long)b * c.S + j];
+    if (t < 0) break;
+    float y[16];
+    paper_deq16(paper_stream(c, rr, l, b, hk), c.pm[rr], t, kv, e0, y);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) x[e] = x[e] + y[e];
   }
 }
 

@@ -11,6 +11,9 @@ namespace fl {
 hipError_t launch_quant_base(const CacheGeo& c, const void* k, const void* v, fl_dtype dt, uint8_t* base,
                              hipStream_t st);
 hipError_t launch_build_slot(const CacheGeo& c, int r, int32_t* slot, hipStream_t st);
+// The paper's format: the streams of loop r (base at r == 1) from k, v.
+hipError_t launch_paper_quant(const CacheGeo& c, int r, const void* k, const void* v, fl_dtype dt, uint8_t* out,
+                              hipStream_t st);
 // One new token at position pos, loop r, from k, v [L][B][Hkv][d]: r == 1 the
 // base records; r >= 2 row cnt[r][b] of every sequence, then the counts.
 hipError_t launch_append(const CacheGeo& c, int r, int pos, const void* k, const void* v, fl_dtype dt,
