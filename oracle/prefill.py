@@ -29,6 +29,7 @@ from __future__ import annotations
 
 import numpy as np
 
+from .paper_format import quantize_chain_paper
 from .quant import bf16_rne, quantize_chain
 
 ROW_BLOCK = 1024
@@ -225,18 +226,23 @@ def identity_chain(x: list, rows: list):
 
 
 def prefill_slice(rows, q, k, v, *, K_budget, bits, dtype, sel_force=None, stop_after=None,
-                  quantize=True, combine="mass"):
+                  quantize=True, combine="mass", fmt="workload"):
     """Run every loop of one (b, h) slice.
 
     rows[r-1], q[r-1], k[r-1], v[r-1]: loop-r active rows and compact inputs
     (loop 1 covers every row).  sel_force: optional {r: sel} that replaces the
     oracle's own selection at loop r (teacher forcing after near ties).
     combine: "mass" (the method's mass-rescaled update) or "mixed" (the exact
-    mixed-logit ablation).  Returns a dict of per-loop results (index r-1)."""
+    mixed-logit ablation).  fmt: "workload" (int8 base, 4/2-bit residuals,
+    32-dim groups) or "paper" (paper_format: INT4 g64, per-channel keys,
+    bf16 tail; `bits` unused).  Returns a dict of per-loop results (index r-1)."""
     R = len(q)
     S, d = k[0].shape
     tau = softmax_scale(d)
-    if quantize:
+    if quantize and fmt == "paper":
+        ks, krec = quantize_chain_paper(k, rows, "k")
+        vs, vrec = quantize_chain_paper(v, rows, "v")
+    elif quantize:
         ks, krec = quantize_chain(k, rows, bits)
         vs, vrec = quantize_chain(v, rows, bits)
     else:

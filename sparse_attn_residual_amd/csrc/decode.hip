@@ -76,7 +76,7 @@ constexpr int kDenseThreads = 512;  // one block per (layer, sequence, query-hea
 // so the accumulators are rescaled rarely.  Group states merge within each
 // wavefront by lane shuffles, then across wavefronts in LDS.  Every head's
 // arithmetic is the same whatever GQ is.
-template <typename T, int NT, int GQ>
+template <typename T, int NT, int GQ, bool PAPER>
 __global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
   constexpr int NG = NT / 8, NW = NT / kWave;
   static_assert(GQ * 128 <= NT, "one thread per output dim of every head");
@@ -109,6 +109,32 @@ __global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
   float* logit = a.logits + lbh0 * c.S;
   const uint16_t* scl = (const uint16_t*)(recs + 2 * d);
   for (int j = gid; j < c.T; j += NG) {
+    if (PAPER) {
+      // the paper's format: K and V of the token at loop 1, dequantized
+      float kx[16], vx[16], p[GQ];
+      paper_chain16(c, 1, l, b, kv_head(c, h0), j, 0, sub * 16, kx);
+      paper_chain16(c, 1, l, b, kv_head(c, h0), j, 1, sub * 16, vx);
+#pragma unroll
+      for (int u = 0; u < GQ; ++u) {
+        float part = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) part = __builtin_fmaf(q[u][e], kx[e], part);
+        const float s = tau * group8_sum_dpp(part);
+        if (sub == 0) logit[(long long)u * c.S + j] = s;
+        if (s > m[u] + kDecRescale) {
+          const float alpha = __expf(m[u] - s);
+          lsum[u] *= alpha;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[u][e] *= alpha;
+          m[u] = s;
+        }
+        p[u] = __expf(s - m[u]);
+        lsum[u] += p[u];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[u][e] = __builtin_fmaf(p[u], vx[e], acc[u][e]);
+      }
+      continue;
+    }
     const uint8_t* rec = recs + (long long)j * c.base_rb;
     const uint4 kw = *(const uint4*)(rec + sub * 16);
     const uint4 vw = *(const uint4*)(rec + d + sub * 16);
@@ -183,12 +209,15 @@ static void launch_dense(const DecodeArgs& a, float tau, hipStream_t st) {
   // query heads per block: the largest of 4, 2, 1 dividing the group size
   const int gq = a.c.G % 4 == 0 ? 4 : a.c.G % 2 == 0 ? 2 : 1;
   const unsigned nblk = (unsigned)((long long)a.c.L * a.c.B * (a.c.H / gq));
-  if (gq == 4)
-    hipLaunchKernelGGL((k_decode_dense<T, kDenseThreads, 4>), dim3(nblk), dim3(kDenseThreads), 0, st, a, tau);
+  if (a.c.fmt == kFmtPaper)  // one query head per block: the reads are reconstructions, not raw records
+    hipLaunchKernelGGL((k_decode_dense<T, kDenseThreads, 1, true>), dim3((unsigned)((long long)a.c.L * a.c.B * a.c.H)),
+                       dim3(kDenseThreads), 0, st, a, tau);
+  else if (gq == 4)
+    hipLaunchKernelGGL((k_decode_dense<T, kDenseThreads, 4, false>), dim3(nblk), dim3(kDenseThreads), 0, st, a, tau);
   else if (gq == 2)
-    hipLaunchKernelGGL((k_decode_dense<T, kDenseThreads, 2>), dim3(nblk), dim3(kDenseThreads), 0, st, a, tau);
+    hipLaunchKernelGGL((k_decode_dense<T, kDenseThreads, 2, false>), dim3(nblk), dim3(kDenseThreads), 0, st, a, tau);
   else
-    hipLaunchKernelGGL((k_decode_dense<T, kDenseThreads, 1>), dim3(nblk), dim3(kDenseThreads), 0, st, a, tau);
+    hipLaunchKernelGGL((k_decode_dense<T, kDenseThreads, 1, false>), dim3(nblk), dim3(kDenseThreads), 0, st, a, tau);
 }
 
 constexpr int kMaxFastLoops = 5;  // loops whose slot lookups are batched
@@ -362,7 +391,7 @@ __device__ inline void tok_accumulate(const float* q, const float* kx, const flo
 // Each wave walks chunks of 64 selected tokens: the index stage of the next
 // chunk (positions, slots, old logits; one token per lane) is in flight while
 // the current chunk's records are read, two tokens per 8-lane group at a time.
-template <typename T, bool PRUNED, int NR>
+template <typename T, bool PRUNED, int NR, bool PAPER>
 __global__ __launch_bounds__(kDecThreads) void k_decode_sparse(DecodeArgs a, float tau) {
   __shared__ GroupState gs;
   __shared__ float csum[PRUNED ? kDecGroups : 1][128];
@@ -445,12 +474,21 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_sparse(DecodeArgs a, flo
         }
       }
       TokLoads<NR> t2[2];
-      tok_load(c, l, b, h, j2[0], s2[0], sub, t2[0]);
-      tok_load(c, l, b, h, j2[1], s2[1], sub, t2[1]);
+      if (!PAPER) {
+        tok_load(c, l, b, h, j2[0], s2[0], sub, t2[0]);
+        tok_load(c, l, b, h, j2[1], s2[1], sub, t2[1]);
+      }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         float kx[16], vx[16], vp[16];
-        tok_decode<PRUNED>(c, r, l, b, h, j2[u], s2[u], sub, t2[u], kx, vx, vp);
+        if (PAPER) {
+          // the paper's format: K, V at loop r (and V at loop r-1) rebuilt here
+          paper_chain16(c, r, l, b, kv_head(c, h), j2[u], 0, sub * 16, kx);
+          paper_chain16(c, r, l, b, kv_head(c, h), j2[u], 1, sub * 16, vx);
+          if (PRUNED) paper_chain16(c, r - 1, l, b, kv_head(c, h), j2[u], 1, sub * 16, vp);
+        } else {
+          tok_decode<PRUNED>(c, r, l, b, h, j2[u], s2[u], sub, t2[u], kx, vx, vp);
+        }
         tok_accumulate<PRUNED>(q, kx, vx, vp, tau, o2[u], Mprev, lprev, v2[u], sub, logit + tt[u], m, lsum, acc,
                                C, P);
       }
@@ -518,11 +556,24 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
     e = launch_copy_sel(nullptr, (int)P, a.c.T, a.sel, st, a.c.S);
     if (e != hipSuccess) return e;
   }
+  if (a.c.fmt == kFmtPaper) {  // tokens rebuilt one at a time: no batched residual loads
+    switch (pruned * 2 + (bf ? 1 : 0)) {
+      case 0: hipLaunchKernelGGL((k_decode_sparse<float, false, 1, true>), dim3((unsigned)P), dim3(kDecThreads), 0,
+                                 st, a, tau); break;
+      case 1: hipLaunchKernelGGL((k_decode_sparse<uint16_t, false, 1, true>), dim3((unsigned)P), dim3(kDecThreads),
+                                 0, st, a, tau); break;
+      case 2: hipLaunchKernelGGL((k_decode_sparse<float, true, 1, true>), dim3((unsigned)P), dim3(kDecThreads), 0,
+                                 st, a, tau); break;
+      default: hipLaunchKernelGGL((k_decode_sparse<uint16_t, true, 1, true>), dim3((unsigned)P), dim3(kDecThreads),
+                                  0, st, a, tau); break;
+    }
+    return hipGetLastError();
+  }
   const int nr = (a.r < kMaxFastLoops ? a.r : kMaxFastLoops) - 1;
   switch (nr * 4 + pruned * 2 + (bf ? 1 : 0)) {
-#define FL_DEC_CASE(NR, PR, BF, T)                                                                          \
-  case NR * 4 + PR * 2 + BF:                                                                                \
-    hipLaunchKernelGGL((k_decode_sparse<T, PR, NR>), dim3((unsigned)P), dim3(kDecThreads), 0, st, a, tau); \
+#define FL_DEC_CASE(NR, PR, BF, T)                                                                                 \
+  case NR * 4 + PR * 2 + BF:                                                                                       \
+    hipLaunchKernelGGL((k_decode_sparse<T, PR, NR, false>), dim3((unsigned)P), dim3(kDecThreads), 0, st, a, tau); \
     break;
 #define FL_DEC_NR(NR)                 \
   FL_DEC_CASE(NR, 0, 0, float)        \

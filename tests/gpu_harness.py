@@ -42,7 +42,7 @@ def counts_list(cfg):
     return [np.array([cfg.counts(b)[r] for b in range(cfg.B)], np.int32) for r in range(cfg.R)]
 
 
-def run_prefill(cfg, rows, slices, *, mass_in=None, K_budget=None, mfma=None, mixed=False):
+def run_prefill(cfg, rows, slices, *, mass_in=None, K_budget=None, mfma=None, mixed=False, fmt=0):
     """All loops of one layer.  mass_in: optional {r: float32 [B][H][K_prev]}.
     K_budget: one budget for every loop, or a list (loop r uses K_budget[r-2]).
     mixed: the exact mixed-logit combine (the state carries lsel).
@@ -51,7 +51,7 @@ def run_prefill(cfg, rows, slices, *, mass_in=None, K_budget=None, mfma=None, mi
     K_budget = cfg.K if K_budget is None else K_budget
     R, B, H, S, d = cfg.R, cfg.B, cfg.H, cfg.S, cfg.d
     cache = fl.CacheBuffers(1, B, H, S, d, R, cfg.n, cfg.bits, rows_list(cfg, rows), Hkv=cfg.kv_heads,
-                            counts=counts_list(cfg))
+                            counts=counts_list(cfg), fmt=fmt)
     st = fl.PrefillState(B, H, S, d, mixed=mixed)
     dt = fl_dtype(cfg)
     qs = [upload(workloads.stack_loop(cfg, slices, r, "q"), cfg) for r in range(1, R + 1)]
@@ -100,12 +100,12 @@ def near_tie_ok(sel_gpu, sel_orc, mass_orc, cand, eps):
     return gap <= eps * float(np.max(mass_orc)), len(a - b)
 
 
-def build_decode_cache(cfg, rows, slices, L=None):
+def build_decode_cache(cfg, rows, slices, L=None, fmt=0):
     """Quantize layer 0 through fl_kv_resq, then copy it to every layer."""
     import sparse_attn_residual_amd as fl
     L = cfg.L if L is None else L
     cache = fl.CacheBuffers(L, cfg.B, cfg.H, cfg.S, cfg.d, cfg.R, cfg.n, cfg.bits, rows_list(cfg, rows),
-                            Hkv=cfg.kv_heads, counts=counts_list(cfg))
+                            Hkv=cfg.kv_heads, counts=counts_list(cfg), fmt=fmt)
     view = cache.layer_view(0)
     dt = fl_dtype(cfg)
     for r in range(1, cfg.R + 1):

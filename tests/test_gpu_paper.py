@@ -77,3 +77,82 @@ def test_paper_streams_bitexact(dtype, S, Hkv, ragged):
     rows, slices = workloads.gen_batch(cfg)
     cache = build_paper_cache(cfg, rows, slices)
     check_streams(cfg, cache, rows, slices)
+
+
+@pytest.mark.parametrize("dtype,d,Hkv", [("f32", 128, 2), ("bf16", 128, 4)])
+def test_paper_prefill(dtype, d, Hkv):
+    """All loops of one layer over paper-format streams (pruning budgets):
+    selections up to near ties, outputs within tolerance of the oracle run on
+    the oracle's own paper-format reconstructions."""
+    import tests.gpu_harness as gh
+    from oracle import prefill
+    import sparse_attn_residual_amd as fl
+    f32 = dtype == "f32"
+    cfg = workloads.custom(name="paper-prefill", dtype=dtype, B=2, H=4, d=d, S=1200, R=4, act=(1, 0.5, 0.3, 0.15),
+                           col="0.30", bits=(8, 4, 4, 4), lognormal=None if f32 else 0.5, seed=53, Hkv=Hkv)
+    _say("paper prefill", cfg)
+    rows, slices = workloads.gen_batch(cfg)
+    budgets = [360, 180, 90]
+    gpu = gh.run_prefill(cfg, rows, slices, K_budget=budgets, fmt=fl.FL_FMT_PAPER)
+    check_streams(cfg, gpu["cache"], rows, slices)
+    tol = 1e-5 if f32 else 2e-3
+    for b in range(cfg.B):
+        for h in (0, cfg.H - 1):
+            s = slices[(b, h)]
+            force = {r + 1: gpu["sel"][r][b, h] for r in range(1, cfg.R)}
+            o = prefill.prefill_slice(s.rows, s.q, s.k, s.v, K_budget=cfg.K, bits=cfg.bits, dtype=cfg.dtype,
+                                      sel_force=force, fmt="paper")
+            cand = np.arange(cfg.S)
+            for r in range(cfg.R):
+                if r >= 1:
+                    m = o["mass"][r]
+                    own = prefill.topk(m, cand, min(budgets[r - 1], len(cand)))
+                    ok, nd = gh.near_tie_ok(gpu["sel"][r][b, h], own, m, cand, 1e-5 if f32 else 2e-3)
+                    assert ok, (b, h, r + 1, nd)
+                    cand = gpu["sel"][r][b, h]
+                g, st = gpu["state"][r], o["state"][r]
+                O = g["O"][b, h]
+                if f32:
+                    assert np.max(np.abs(O - st.O)) <= tol, (b, h, r + 1, np.max(np.abs(O - st.O)))
+                else:
+                    err = np.linalg.norm(O - st.O) / np.linalg.norm(st.O)
+                    assert err <= tol, (b, h, r + 1, err)
+
+
+@pytest.mark.parametrize("dtype,Hkv", [("f32", 2), ("bf16", 4)])
+def test_paper_decode(dtype, Hkv):
+    """Decode over paper-format streams (tail tokens included), against the
+    oracle's decode step on the paper-format reconstructions."""
+    import tests.gpu_harness as gh
+    import sparse_attn_residual_amd as fl
+    from oracle import decode, prefill
+    cfg = workloads.custom(name="paper-decode", dtype=dtype, B=2, H=4, d=128, S=900, R=4, act=(1, 0.3, 0.15, 0.08),
+                           col="0.10", bits=(8, 4, 4, 4), gamma=0.5, lognormal=0.5, L=2, decode=True, seed=55,
+                           Hkv=Hkv)
+    _say("paper decode", cfg)
+    rows, slices = workloads.gen_batch(cfg)
+    cache = gh.build_decode_cache(cfg, rows, slices, fmt=fl.FL_FMT_PAPER)
+    qs = workloads.decode_queries(cfg)
+    gpu = gh.run_decode(cfg, cache, qs)
+    rel = dtype != "f32"
+    tol = 2e-3 if rel else 1e-5
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            s = slices[(b, h)]
+            _, krec = pf.quantize_chain_paper(s.k, s.rows, "k")
+            _, vrec = pf.quantize_chain_paper(s.v, s.rows, "v")
+            for l in range(cfg.L):
+                force = {r + 1: gpu[r]["sel"][l, b, h] for r in range(1, cfg.R)}
+                orc = decode.decode_slice(krec, vrec, [q[l, b, h] for q in qs], cfg.K, sel_force=force)
+                cand = np.arange(cfg.S)
+                for r in range(cfg.R):
+                    if r >= 1:
+                        key = orc[r - 1]["logits"]
+                        own = prefill.topk(key, cand, min(cfg.K, len(cand)))
+                        ok, nd = gh.near_tie_ok(gpu[r]["sel"][l, b, h], own, key - key.min(), cand,
+                                                2e-3 if rel else 1e-5)
+                        assert ok, (l, b, h, r + 1, nd)
+                        cand = gpu[r]["sel"][l, b, h]
+                    O, o = gpu[r]["O"][l, b, h], orc[r]["O"]
+                    err = np.linalg.norm(O - o) / np.linalg.norm(o) if rel else np.max(np.abs(O - o))
+                    assert err <= tol, (l, b, h, r + 1, err)
