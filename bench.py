@@ -84,7 +84,7 @@ class Timer:
         return {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in self.pairs.items()}
 
 
-def prefill_bench(args, torch, fl, workloads, acc, cfg=None, pruned=True):
+def prefill_bench(args, torch, fl, workloads, acc, cfg=None, pruned=True, fmt=0):
     cfg = workloads.CONFIGS[PREFILL_CFG] if cfg is None else cfg
     t0 = time.time()
     rows, slices = workloads.gen_batch(cfg)
@@ -98,7 +98,7 @@ def prefill_bench(args, torch, fl, workloads, acc, cfg=None, pruned=True):
     rows_l = [np.stack([np.concatenate([rows[b][r], np.full(cfg.n[r] - len(rows[b][r]), rows[b][r][-1], np.int32)])
                         for b in range(B)]) for r in range(R)]
     counts = [np.array([cfg.counts(b)[r] for b in range(B)], np.int32) for r in range(R)] if cfg.ragged else None
-    cache = fl.CacheBuffers(1, B, H, S, d, R, cfg.n, cfg.bits, rows_l, Hkv=cfg.kv_heads, counts=counts)
+    cache = fl.CacheBuffers(1, B, H, S, d, R, cfg.n, cfg.bits, rows_l, Hkv=cfg.kv_heads, counts=counts, fmt=fmt)
     st = fl.PrefillState(B, H, S, d)
     res = measure_prefill(args, torch, fl, acc, cfg, rows, q, k, v, cache, st, [cfg.K] * (R - 1))
     if pruned:
@@ -169,14 +169,14 @@ def measure_prefill(args, torch, fl, acc, cfg, rows, q, k, v, cache, st, budgets
                 total_tf=total_tf, Ks=Ks)
 
 
-def decode_bench(args, torch, fl, workloads, acc, cfg=None):
+def decode_bench(args, torch, fl, workloads, acc, cfg=None, fmt=0):
     cfg = workloads.CONFIGS[DECODE_CFG] if cfg is None else cfg
     L, B, H, S, d, R = cfg.L, cfg.B, cfg.H, cfg.S, cfg.d, cfg.R
     Hkv = cfg.kv_heads
     t0 = time.time()
     rows = {b: workloads.active_rows(cfg, b) for b in range(B)}
     rows_l = [np.stack([rows[b][r] for b in range(B)]) for r in range(R)]
-    cache = fl.CacheBuffers(L, B, H, S, d, R, cfg.n, cfg.bits, rows_l, Hkv=Hkv)
+    cache = fl.CacheBuffers(L, B, H, S, d, R, cfg.n, cfg.bits, rows_l, Hkv=Hkv, fmt=fmt)
     log(f"decode cache: {cache.nbytes() / 1e9:.1f} GB on device")
     for b in range(B):
         _, sl = workloads.gen_batch(cfg, batches=[b], with_q=False)
@@ -230,6 +230,7 @@ def decode_bench(args, torch, fl, workloads, acc, cfg=None):
     total = sum(loop_bytes)
     logits_overhead = float(L * B * H * S * 4 * 2)
     return dict(cfg=cfg, ms_step=ms_step, per=per, loop_bytes=loop_bytes, bytes=total,
+                cache_stream1_bytes=float(cache.base.numel()),
                 gbs=total / (ms_step * 1e-3) / 1e9, dense_gbs=loop_bytes[0] / (per["decode1"] * 1e-3) / 1e9,
                 logits_overhead=logits_overhead, cache_bytes=cache.nbytes())
 
@@ -371,6 +372,11 @@ def main():
     gqa_dec = None if args.no_decode else decode_bench(args, torch, fl, workloads, acc,
                                                        cfg=workloads.CONFIGS[DECODE_CFG].with_(Hkv=4))
     torch.cuda.empty_cache()
+    # the paper's own cache format (INT4 g64, per-channel keys, bf16 tail) on the same shapes
+    pap_pf = prefill_bench(args, torch, fl, workloads, acc, cfg=workloads.CONFIGS[PREFILL_CFG], pruned=False,
+                           fmt=fl.FL_FMT_PAPER)
+    pap_dec = None if args.no_decode else decode_bench(args, torch, fl, workloads, acc, fmt=fl.FL_FMT_PAPER)
+    torch.cuda.empty_cache()
     # a ragged batch: two 32K sequences, the second keeping half as many active rows
     rag_cfg = workloads.CONFIGS[PREFILL_CFG].with_(B=2, ragged=("1", "0.5"))
     rag_pf = prefill_bench(args, torch, fl, workloads, acc, cfg=rag_cfg, pruned=False)
@@ -477,6 +483,20 @@ def main():
             "decode_dense_unique_gbs": gqa_dec["dense_gbs"],
             "decode_dense_note": "loop 1 reads each KV head's records once for its 4 query heads; GB/s counts "
                                  "those unique bytes (the kernel is vector-ALU bound at this ratio)",
+        })
+    out["paper_format"] = {
+        "workload": "the 32K prefill and 48-layer decode workloads above with the paper's own cache format (INT4 "
+                    "asymmetric, group 64, keys per channel along tokens, values per token, 64-token bf16 tail)",
+        "prefill_ms_per_step": pap_pf["ms_step"],
+        "prefill_tokens_per_s": cfg.B * cfg.S / (pap_pf["ms_step"] * 1e-3),
+        "prefill_per_call_ms": {k: round(v, 4) for k, v in pap_pf["per"].items()},
+    }
+    if pap_dec is not None:
+        out["paper_format"].update({
+            "decode_ms_per_step": pap_dec["ms_step"],
+            "decode_per_loop_ms": {k: round(v, 4) for k, v in pap_dec["per"].items()},
+            "decode_cache_bytes": pap_dec["cache_bytes"],
+            "decode_dense_stream_gbs": pap_dec["cache_stream1_bytes"] / (pap_dec["per"]["decode1"] * 1e-3) / 1e9,
         })
     out["ragged"] = {
         "workload": f"{rag_cfg.name} with B = 2: active rows per loop {rag_cfg.counts(0)} and {rag_cfg.counts(1)}",
