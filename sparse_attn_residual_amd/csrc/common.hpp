@@ -202,20 +202,27 @@ __host__ __device__ __forceinline__ int paper_entries(const CacheGeo& c, int r) 
 
 // Dequantized dims [e0, e0 + 16) (e0 a multiple of 16) of K (kv = 0) or V of
 // entry t of a paper-format stream with m entries: fma(code, scale, zero).
+// Codes, key scales and zeros come in with 8- and 16-byte loads.
 __device__ __forceinline__ void paper_deq16(const uint8_t* st, int m, int t, int kv, int e0, float* x) {
   const uint8_t* rec = st + (long long)t * kPRec;
   const uint2 w = *(const uint2*)(rec + kv * 64 + e0 / 2);
   const uint32_t ws[2] = {w.x, w.y};
   if (kv == 0) {
-    const uint16_t* meta = (const uint16_t*)(st + (long long)m * kPRec + (long long)(t / kPGroup) * kPKMeta);
+    const uint8_t* meta = st + (long long)m * kPRec + (long long)(t / kPGroup) * kPKMeta;
+    const uint4 s0 = *(const uint4*)(meta + e0 * 2), s1 = *(const uint4*)(meta + e0 * 2 + 16);
+    const uint4 z0 = *(const uint4*)(meta + 256 + e0 * 2), z1 = *(const uint4*)(meta + 256 + e0 * 2 + 16);
+    const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    const uint32_t zw[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float code = (float)((ws[e >> 3] >> (4 * (e & 7))) & 15);
-      x[e] = __builtin_fmaf(code, h2f(meta[e0 + e]), h2f(meta[128 + e0 + e]));
+      const float s = h2f((uint16_t)(sw[e >> 1] >> (16 * (e & 1))));
+      const float z = h2f((uint16_t)(zw[e >> 1] >> (16 * (e & 1))));
+      x[e] = __builtin_fmaf(code, s, z);
     }
   } else {
-    const uint16_t* vm = (const uint16_t*)(rec + 128 + (e0 / 64) * 4);
-    const float s = h2f(vm[0]), z = h2f(vm[1]);
+    const uint32_t vm = *(const uint32_t*)(rec + 128 + (e0 / 64) * 4);
+    const float s = h2f((uint16_t)vm), z = h2f((uint16_t)(vm >> 16));
 #pragma unroll
     for (int e = 0; e < 16; ++e) x[e] = __builtin_fmaf((float)((ws[e >> 3] >> (4 * (e & 7))) & 15), s, z);
   }
@@ -281,9 +288,11 @@ __device__ __forceinline__ void paper_chain16(const CacheGeo& c, int r, int l, i
       if (c.slot[q][(long long)b * c.S + j] < 0) break;
       rr = q;
     }
-    const uint16_t* tv = paper_tail(c, rr, l, b, hk, j, kv) + e0;
+    const uint4* tv = (const uint4*)(paper_tail(c, rr, l, b, hk, j, kv) + e0);
+    const uint4 a0 = tv[0], a1 = tv[1];
+    const uint32_t aw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
-    for (int e = 0; e < 16; ++e) x[e] = bf16_to_f32(tv[e]);
+    for (int e = 0; e < 16; ++e) x[e] = __uint_as_float((e & 1) ? (aw[e >> 1] & 0xffff0000u) : (aw[e >> 1] << 16));
     return;
   }
   paper_deq16(paper_stream(c, 1, l, b, hk), c.pm[1], j, kv, e0, x);

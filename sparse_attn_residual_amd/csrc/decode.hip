@@ -108,10 +108,83 @@ __global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
   const uint8_t* recs = base_rec(c, l, b, kv_head(c, h0), 0);
   float* logit = a.logits + lbh0 * c.S;
   const uint16_t* scl = (const uint16_t*)(recs + 2 * d);
-  for (int j = gid; j < c.T; j += NG) {
-    if (PAPER) {
-      // the paper's format: K and V of the token at loop 1, dequantized
-      float kx[16], vx[16], p[GQ];
+  if (PAPER) {
+    // The paper's format.  Each 8-lane group takes 8 consecutive tokens of
+    // one 64-token key block, so the block's per-channel key scales and zeros
+    // are folded into the query once: q.k = sum (q s) c + sum q z.  A value
+    // group's zero is carried as one running sum per lane (its 16 dims share
+    // it) and added before the merge.  Tail tokens (bf16) come last.
+    const uint8_t* st = paper_stream(c, 1, l, b, kv_head(c, h0));
+    const int body = min(c.Sq, c.T);
+    const int nb = (body + kPGroup - 1) / kPGroup;
+    float zacc[GQ];
+#pragma unroll
+    for (int u = 0; u < GQ; ++u) zacc[u] = 0.0f;
+    for (int blk = gid / 8; blk < nb; blk += NG / 8) {
+      const uint8_t* meta = st + (long long)c.Sq * kPRec + (long long)blk * kPKMeta;
+      const uint4 s0 = *(const uint4*)(meta + sub * 32), s1 = *(const uint4*)(meta + sub * 32 + 16);
+      const uint4 z0 = *(const uint4*)(meta + 256 + sub * 32), z1 = *(const uint4*)(meta + 256 + sub * 32 + 16);
+      const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      const uint32_t zw[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+      float qs[GQ][16], qz[GQ];
+#pragma unroll
+      for (int u = 0; u < GQ; ++u) {
+        qz[u] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          qs[u][e] = q[u][e] * h2f((uint16_t)(sw[e >> 1] >> (16 * (e & 1))));
+          qz[u] = __builtin_fmaf(q[u][e], h2f((uint16_t)(zw[e >> 1] >> (16 * (e & 1)))), qz[u]);
+        }
+      }
+      const int t0 = blk * kPGroup + (gid & 7) * 8;
+      // the group's 8 records are all requested before the first is used
+      uint2 kwa[8], vwa[8];
+      uint32_t vma[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint8_t* rec = st + (long long)min(t0 + i, body - 1) * kPRec;
+        kwa[i] = *(const uint2*)(rec + sub * 8);
+        vwa[i] = *(const uint2*)(rec + 64 + sub * 8);
+        vma[i] = *(const uint32_t*)(rec + 128 + (sub >> 2) * 4);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = t0 + i;
+        if (j >= body) break;  // the same for the group's 8 lanes
+        const float vs = h2f((uint16_t)vma[i]), vz = h2f((uint16_t)(vma[i] >> 16));
+        const uint32_t kws[2] = {kwa[i].x, kwa[i].y}, vws[2] = {vwa[i].x, vwa[i].y};
+#pragma unroll
+        for (int u = 0; u < GQ; ++u) {
+          float part = qz[u];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) part = __builtin_fmaf(qs[u][e], (float)((kws[e >> 3] >> (4 * (e & 7))) & 15), part);
+          const float sc = tau * group8_sum_dpp(part);
+          if (sub == 0) logit[(long long)u * c.S + j] = sc;
+          if (sc > m[u] + kDecRescale) {
+            const float alpha = __expf(m[u] - sc);
+            lsum[u] *= alpha;
+            zacc[u] *= alpha;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[u][e] *= alpha;
+            m[u] = sc;
+          }
+          const float pr = __expf(sc - m[u]);
+          lsum[u] += pr;
+          const float pv = pr * vs;
+          zacc[u] = __builtin_fmaf(pr, vz, zacc[u]);
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            acc[u][e] = __builtin_fmaf(pv, (float)((vws[e >> 3] >> (4 * (e & 7))) & 15), acc[u][e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < GQ; ++u) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[u][e] += zacc[u];
+    }
+    for (int j = body + gid; j < c.T; j += NG) {  // the bf16 tail
+      float kx[16], vx[16];
       paper_chain16(c, 1, l, b, kv_head(c, h0), j, 0, sub * 16, kx);
       paper_chain16(c, 1, l, b, kv_head(c, h0), j, 1, sub * 16, vx);
 #pragma unroll
@@ -119,22 +192,23 @@ __global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
         float part = 0.0f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) part = __builtin_fmaf(q[u][e], kx[e], part);
-        const float s = tau * group8_sum_dpp(part);
-        if (sub == 0) logit[(long long)u * c.S + j] = s;
-        if (s > m[u] + kDecRescale) {
-          const float alpha = __expf(m[u] - s);
+        const float sc = tau * group8_sum_dpp(part);
+        if (sub == 0) logit[(long long)u * c.S + j] = sc;
+        if (sc > m[u] + kDecRescale) {
+          const float alpha = __expf(m[u] - sc);
           lsum[u] *= alpha;
 #pragma unroll
           for (int e = 0; e < 16; ++e) acc[u][e] *= alpha;
-          m[u] = s;
+          m[u] = sc;
         }
-        p[u] = __expf(s - m[u]);
-        lsum[u] += p[u];
+        const float pr = __expf(sc - m[u]);
+        lsum[u] += pr;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[u][e] = __builtin_fmaf(p[u], vx[e], acc[u][e]);
+        for (int e = 0; e < 16; ++e) acc[u][e] = __builtin_fmaf(pr, vx[e], acc[u][e]);
       }
-      continue;
     }
+  }
+  for (int j = gid; !PAPER && j < c.T; j += NG) {
     const uint8_t* rec = recs + (long long)j * c.base_rb;
     const uint4 kw = *(const uint4*)(rec + sub * 16);
     const uint4 vw = *(const uint4*)(rec + d + sub * 16);
