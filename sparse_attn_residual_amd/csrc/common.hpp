@@ -306,6 +306,70 @@ __device__ __forceinline__ void paper_chain16(const CacheGeo& c, int r, int l, i
   }
 }
 
+// K and V of token j at loop r, dims [e0, e0 + 16), in one pass over its
+// chain (each loop's slot and records read once), and, when PREV is set,
+// V at loop r-1: the values paper_chain16 gives for (r, K), (r, V), (r-1, V).
+template <bool PREV>
+__device__ __forceinline__ void paper_token16(const CacheGeo& c, int r, int l, int b, int hk, int j, int e0,
+                                              float* kx, float* vx, float* vprev) {
+  if (j >= c.Sq) {
+    int rr = 1;
+    for (int q = 2; q <= r; ++q) {
+      if (c.slot[q][(long long)b * c.S + j] < 0) break;
+      rr = q;
+    }
+    // the slot of loop r-1 when the token is active at loop r, else the same one
+    const int rp = rr == r && r >= 2 ? r - 1 : rr;
+    const uint4* tk = (const uint4*)(paper_tail(c, rr, l, b, hk, j, 0) + e0);
+    const uint4* tv = (const uint4*)(paper_tail(c, rr, l, b, hk, j, 1) + e0);
+    const uint4 k0 = tk[0], k1 = tk[1], v0 = tv[0], v1 = tv[1];
+    const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+    const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      kx[e] = __uint_as_float((e & 1) ? (kw[e >> 1] & 0xffff0000u) : (kw[e >> 1] << 16));
+      vx[e] = __uint_as_float((e & 1) ? (vw[e >> 1] & 0xffff0000u) : (vw[e >> 1] << 16));
+    }
+    if (PREV) {
+      if (rp == rr) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) vprev[e] = vx[e];
+      } else {
+        const uint4* tp = (const uint4*)(paper_tail(c, rp, l, b, hk, j, 1) + e0);
+        const uint4 p0 = tp[0], p1 = tp[1];
+        const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          vprev[e] = __uint_as_float((e & 1) ? (pw[e >> 1] & 0xffff0000u) : (pw[e >> 1] << 16));
+      }
+    }
+    return;
+  }
+  const uint8_t* st = paper_stream(c, 1, l, b, hk);
+  paper_deq16(st, c.pm[1], j, 0, e0, kx);
+  paper_deq16(st, c.pm[1], j, 1, e0, vx);
+  if (PREV) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) vprev[e] = vx[e];
+  }
+  for (int rr = 2; rr <= r; ++rr) {
+    const int t = c.slot[rr][(long long)b * c.S + j];
+    if (t < 0) break;
+    if (PREV && rr == r) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) vprev[e] = vx[e];
+    }
+    const uint8_t* sr = paper_stream(c, rr, l, b, hk);
+    float y[16];
+    paper_deq16(sr, c.pm[rr], t, 0, e0, y);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) kx[e] = kx[e] + y[e];
+    paper_deq16(sr, c.pm[rr], t, 1, e0, y);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) vx[e] = vx[e] + y[e];
+  }
+}
+
 // The 32 input elements [src, src + 32) of one group as floats, read with
 // 16-byte loads (src 16-byte aligned).
 template <typename T> __device__ inline void load_group16(const T* src, float* x);

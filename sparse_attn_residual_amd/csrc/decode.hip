@@ -557,9 +557,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_sparse(DecodeArgs a, flo
         float kx[16], vx[16], vp[16];
         if (PAPER) {
           // the paper's format: K, V at loop r (and V at loop r-1) rebuilt here
-          paper_chain16(c, r, l, b, kv_head(c, h), j2[u], 0, sub * 16, kx);
-          paper_chain16(c, r, l, b, kv_head(c, h), j2[u], 1, sub * 16, vx);
-          if (PRUNED) paper_chain16(c, r - 1, l, b, kv_head(c, h), j2[u], 1, sub * 16, vp);
+          paper_token16<PRUNED>(c, r, l, b, kv_head(c, h), j2[u], sub * 16, kx, vx, vp);
         } else {
           tok_decode<PRUNED>(c, r, l, b, h, j2[u], s2[u], sub, t2[u], kx, vx, vp);
         }
