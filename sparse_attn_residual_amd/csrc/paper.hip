@@ -35,10 +35,14 @@ __device__ __forceinline__ uint32_t code_q4(float x, const GroupQ& q) {
   return (uint32_t)c;
 }
 
-// Keys: one block per (l, b, hk, group of 64 entries); two threads per
-// channel, 32 entries each; codes staged in LDS, then packed per entry.
+// Keys: one block per (l, b, hk, group of 64 entries).  Each thread forms
+// 32 dims of one entry (the residual against the previous loop's values,
+// rebuilt with 16-byte loads) into an LDS block [64][128]; then two threads
+// per channel reduce its 64 entries, quantize, and the codes are packed per
+// entry from LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void k_pq_keys(CacheGeo c, int r, const T* __restrict__ k, uint8_t* __restrict__ out) {
+  __shared__ float xs[kPGroup][128 + 1];
   __shared__ float smin[2][128], smax[2][128];
   __shared__ uint8_t codes[kPGroup][128];
   const int m = paper_entries(c, r);
@@ -52,19 +56,37 @@ __global__ __launch_bounds__(256) void k_pq_keys(CacheGeo c, int r, const T* __r
   const int t1 = min(t0 + kPGroup, paper_body(c, r, b));
   if (t0 >= t1) return;  // the whole block: no quantized entry here
   const int stride = c.n[r];   // input rows per (l, b, hk) (n[1] == S)
+  {
+    const int e = threadIdx.x >> 2, qd = threadIdx.x & 3;   // entry, 32 dims
+    const int t = t0 + e;
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = 0.0f;
+    if (t < t1) {
+      load_group16<T>(k + (lbh * stride + t) * 128 + qd * 32, x);
+      if (r > 1) {
+        const int j = c.rows[r][(long long)b * c.n[r] + t];
+        float p[16];
+        paper_chain16(c, r - 1, l, b, hk, j, 0, qd * 32, p);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = x[i] - p[i];
+        paper_chain16(c, r - 1, l, b, hk, j, 0, qd * 32 + 16, p);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[16 + i] = x[16 + i] - p[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) xs[e][qd * 32 + i] = x[i];
+  }
+  __syncthreads();
   const int ch = threadIdx.x & 127, half = threadIdx.x >> 7;
-  float v[32];
   float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const int t = t0 + half * 32 + i;
-    v[i] = 0.0f;
-    if (t < t1) {
-      float x = load_elem<T>(k + (lbh * stride + t) * 128 + ch);
-      if (r > 1) x = x - paper_elem(c, r - 1, l, b, hk, c.rows[r][(long long)b * c.n[r] + t], 0, ch);
-      v[i] = x;
-      lo = fminf(lo, x);
-      hi = fmaxf(hi, x);
+    if (t0 + half * 32 + i < t1) {
+      const float v = xs[half * 32 + i][ch];
+      lo = fminf(lo, v);
+      hi = fmaxf(hi, v);
     }
   }
   smin[half][ch] = lo;
@@ -73,7 +95,7 @@ __global__ __launch_bounds__(256) void k_pq_keys(CacheGeo c, int r, const T* __r
   const GroupQ q = group_q4(fminf(smin[0][ch], smin[1][ch]), fmaxf(smax[0][ch], smax[1][ch]));
   uint8_t* st = out + lbh * c.pbytes[r];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) codes[half * 32 + i][ch] = (uint8_t)code_q4(v[i], q);
+  for (int i = 0; i < 32; ++i) codes[half * 32 + i][ch] = (uint8_t)code_q4(xs[half * 32 + i][ch], q);
   if (half == 0) {
     uint16_t* meta = (uint16_t*)(st + (long long)m * kPRec + (long long)blk * kPKMeta);
     meta[ch] = q.s16;
