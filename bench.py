@@ -340,6 +340,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--main-only", action="store_true",
+                    help="only the 32K prefill and 48-layer decode workloads (no gqa, paper_format, ragged sections)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only copy 1 GiB device to device three times (scales the HBM byte counters)")
     args = ap.parse_args()
@@ -366,20 +368,24 @@ def main():
     sel = select_bench(args, torch, fl, workloads, acc)
     dec = None if args.no_decode else decode_bench(args, torch, fl, workloads, acc)
     torch.cuda.empty_cache()
+    extra = not args.main_only
     # grouped-query attention (4 query heads per KV head) on the same shapes
-    gqa_pf = prefill_bench(args, torch, fl, workloads, acc, cfg=workloads.CONFIGS[PREFILL_CFG].with_(Hkv=4),
-                           pruned=False)
-    gqa_dec = None if args.no_decode else decode_bench(args, torch, fl, workloads, acc,
-                                                       cfg=workloads.CONFIGS[DECODE_CFG].with_(Hkv=4))
-    torch.cuda.empty_cache()
-    # the paper's own cache format (INT4 g64, per-channel keys, bf16 tail) on the same shapes
-    pap_pf = prefill_bench(args, torch, fl, workloads, acc, cfg=workloads.CONFIGS[PREFILL_CFG], pruned=False,
-                           fmt=fl.FL_FMT_PAPER)
-    pap_dec = None if args.no_decode else decode_bench(args, torch, fl, workloads, acc, fmt=fl.FL_FMT_PAPER)
-    torch.cuda.empty_cache()
+    gqa_pf = gqa_dec = pap_pf = pap_dec = rag_pf = None
+    if extra:
+        gqa_pf = prefill_bench(args, torch, fl, workloads, acc, cfg=workloads.CONFIGS[PREFILL_CFG].with_(Hkv=4),
+                               pruned=False)
+        gqa_dec = None if args.no_decode else decode_bench(args, torch, fl, workloads, acc,
+                                                           cfg=workloads.CONFIGS[DECODE_CFG].with_(Hkv=4))
+        torch.cuda.empty_cache()
+        # the paper's own cache format (INT4 g64, per-channel keys, bf16 tail) on the same shapes
+        pap_pf = prefill_bench(args, torch, fl, workloads, acc, cfg=workloads.CONFIGS[PREFILL_CFG], pruned=False,
+                               fmt=fl.FL_FMT_PAPER)
+        pap_dec = None if args.no_decode else decode_bench(args, torch, fl, workloads, acc, fmt=fl.FL_FMT_PAPER)
+        torch.cuda.empty_cache()
     # a ragged batch: two 32K sequences, the second keeping half as many active rows
     rag_cfg = workloads.CONFIGS[PREFILL_CFG].with_(B=2, ragged=("1", "0.5"))
-    rag_pf = prefill_bench(args, torch, fl, workloads, acc, cfg=rag_cfg, pruned=False)
+    if extra:
+        rag_pf = prefill_bench(args, torch, fl, workloads, acc, cfg=rag_cfg, pruned=False)
     cpu = None if args.no_cpu else cpu_baseline(workloads)
 
     cfg = pf["cfg"]
@@ -470,6 +476,15 @@ def main():
                 "step_frac": dec["gbs"] / acc.MI355X_HBM_GBS,
             },
         }
+    if extra:
+        _extras(out, cfg, gqa_pf, gqa_dec, pap_pf, pap_dec, rag_cfg, rag_pf)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    print(json.dumps(out), flush=True)
+
+
+def _extras(out, cfg, gqa_pf, gqa_dec, pap_pf, pap_dec, rag_cfg, rag_pf):
+    """The gqa, paper_format and ragged sections of the JSON line."""
     out["gqa"] = {
         "workload": f"the two workloads above with Hkv = 4 key/value heads for H = {cfg.H} query heads",
         "prefill_ms_per_step": gqa_pf["ms_step"],
@@ -504,9 +519,6 @@ def main():
         "prefill_tokens_per_s": rag_cfg.B * rag_cfg.S / (rag_pf["ms_step"] * 1e-3),
         "prefill_per_call_ms": {k: round(v, 4) for k, v in rag_pf["per"].items()},
     }
-    if cpu is not None:
-        out["cpu_baseline"] = cpu
-    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":
