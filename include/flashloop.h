@@ -55,6 +55,10 @@ extern "C" {
 
 #define FL_ABI_VERSION 1
 #define FL_MAX_LOOPS 16
+/* Longest sequence a cache may hold (2^21 tokens): the prefill kernels address
+ * one head's dequantized 64-column tiles (36 KB each) with 32-bit offsets.
+ * Larger S: FL_EUNSUPPORTED from every call that takes the cache. */
+#define FL_MAX_S (1 << 21)
 
 typedef enum fl_status {
   FL_OK = 0,

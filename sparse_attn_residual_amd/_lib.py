@@ -5,6 +5,7 @@ import ctypes
 import os
 
 FL_MAX_LOOPS = 16
+FL_MAX_S = 1 << 21
 FL_F32, FL_BF16 = 0, 1
 FL_WS_COLSEL, FL_WS_ATTN, FL_WS_DECODE = 1, 2, 3
 FL_FMT_WORKLOAD, FL_FMT_PAPER = 0, 1

@@ -61,6 +61,8 @@ fl_status check_cache(const char* fn, const fl_cache* c, int r, bool need_res_r,
   if (hkv < 1 || c->H % hkv != 0)
     return fail(FL_EINVAL, "%s: Hkv = %d must divide H = %d", fn, c->Hkv, c->H);
   if ((long long)c->L * c->B * c->H * c->S > (1LL << 40)) return fail(FL_EUNSUPPORTED, "%s: cache too large", fn);
+  // the tile images of one (b, h) are addressed with 32-bit byte offsets
+  if (c->S > FL_MAX_S) return fail(FL_EUNSUPPORTED, "%s: S = %d above FL_MAX_S = %d", fn, c->S, FL_MAX_S);
   FL_NEED_PTR(c->base, "cache->base");
   const int last = need_res_r ? r : r - 1;
   for (int rr = 2; rr <= c->R; ++rr) {

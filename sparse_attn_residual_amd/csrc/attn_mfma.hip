@@ -9,13 +9,13 @@
 // chosen key positions together with their share of the full distribution).
 //
 // Design (gfx950, wave64):
-//  * a 256-thread block owns BM = 4 waves x 32*RB query rows; a wave keeps
-//    its queries in registers as the B operand of S^T = K Q^T
+//  * a block of NW waves owns 32 * NW query rows (twelve waves, three per
+//    SIMD, when the launch is large; else four, two blocks per CU); a wave
+//    keeps its 32 rows' queries in registers as the B operand of S^T = K Q^T
 //    (v_mfma_f32_32x32x16_bf16), so each lane holds one query row's scores
 //    and the row softmax needs one cross-half exchange per tile;
 //  * key tiles of 64 columns: K stored row-major (bf16) and V transposed
-//    (fp16) in LDS, double buffered, the next tile's global loads in flight
-//    while the current one is multiplied;
+//    (fp16) in LDS; the K and V fragments are read a few MFMAs ahead of use;
 //  * P is rounded to fp16 (not bf16) for O^T += V^T P^T on
 //    v_mfma_f32_32x32x16_f16: P in [0, 1] needs significand, not range, and
 //    bf16 rounding alone would spend the whole error budget; the bf16 value
@@ -23,11 +23,11 @@
 //  * every record a loop attends is dequantized once per loop by
 //    k_build_tiles into 64-column tile images laid out exactly like the LDS
 //    tiles (p1 §4.4: the engine gathers the chosen tokens and keys into
-//    dense buffers); the attention kernel copies them into a three-deep LDS ring
-//    with direct global->LDS loads and overlaps the QK^T of the next tile
-//    with the softmax of the current one.  Dequantizing inside the
-//    attention kernel instead would repeat the work for every row block and
-//    the vector ALUs are already the busier unit on gfx950.
+//    dense buffers); the attention kernel copies them into a two-image LDS
+//    ring by direct buffer->LDS loads, the next tile's copy in flight while
+//    the current one is used.  Dequantizing inside the attention kernel
+//    instead would repeat the work for every row block and the vector ALUs
+//    are already the busier unit on gfx950.
 #include "launch.hpp"
 
 namespace fl {
@@ -66,7 +66,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 // Two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
@@ -164,17 +163,26 @@ struct MfmaArgs {
 };
 
 // Direct global->LDS copy of one image of CH 1 KB chunks, the chunks spread
-// over the block's NW waves (16 bytes per lane and chunk).
+// over the block's NW waves (16 bytes per lane and chunk).  The copies use the
+// buffer form (buffer_load_dwordx4 ... lds) on a resource that spans the
+// images one block reads: while a copy of the global-segment form is in
+// flight the compiler drains every LDS read (lgkmcnt(0)) before each use,
+// which serializes the matrix-operand reads; the buffer form counts on vmcnt
+// only, so the reads ahead of an MFMA overlap.  Offsets past the resource's
+// size read zeros.
+__device__ inline __amdgpu_buffer_rsrc_t img_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+}
 template <int NW, int CH>
-__device__ inline void dma_img(const uint8_t* img, uint8_t* lds) {
+__device__ inline void dma_img(__amdgpu_buffer_rsrc_t rs, int off, uint8_t* lds) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   for (int ch = wv; ch < CH; ch += NW)
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(img + ch * 1024 + lane * 16), (lds_void_t*)(lds + ch * 1024), 16,
-                                     0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds + ch * 1024), 16, off + ch * 1024 + lane * 16, 0,
+                                             0, 0);
 }
 template <int NW>
-__device__ inline void dma_tile(const uint8_t* img, uint8_t* lds) {
-  dma_img<NW, kImgChunks>(img, lds);
+__device__ inline void dma_tile(__amdgpu_buffer_rsrc_t rs, int off, uint8_t* lds) {
+  dma_img<NW, kImgChunks>(rs, off, lds);
 }
 
 // Workgroup barrier for the tile ring: the wave's LDS reads have returned
@@ -213,18 +221,41 @@ __device__ inline void wait_tiles_but(int keep) {
   wait_imgs_but<NW, kImgChunks>(keep);
 }
 
+// sched_group_barrier masks: MFMA and LDS-read instruction classes.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
 // S^T = K Q^T for one tile: the lane's row against the tile's 64 columns.
+// The K fragments of the next two k-steps are read while the current ones
+// are multiplied (the registers of the loop allow two steps ahead).
 __device__ inline void qk_tile(const uint8_t* T, const bf16x8_t* qf, int l32, int hf, f32x16_t& s0, f32x16_t& s1) {
+  constexpr int A = 2;
   const __bf16* kt = (const __bf16*)T;
   s0 = f32x16_t{};
   s1 = f32x16_t{};
+  bf16x8_t ka[A], kb[A];
+#pragma unroll
+  for (int i = 0; i < A; ++i) {
+    ka[i] = *(const bf16x8_t*)&kt[l32 * kKP + i * 16 + hf * 8];
+    kb[i] = *(const bf16x8_t*)&kt[(32 + l32) * kKP + i * 16 + hf * 8];
+  }
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    const bf16x8_t k0 = *(const bf16x8_t*)&kt[l32 * kKP + ks * 16 + hf * 8];
-    const bf16x8_t k1 = *(const bf16x8_t*)&kt[(32 + l32) * kKP + ks * 16 + hf * 8];
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % A], qf[ks], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[ks % A], qf[ks], s1, 0, 0, 0);
+    if (ks + A < 8) {
+      ka[ks % A] = *(const bf16x8_t*)&kt[l32 * kKP + (ks + A) * 16 + hf * 8];
+      kb[ks % A] = *(const bf16x8_t*)&kt[(32 + l32) * kKP + (ks + A) * 16 + hf * 8];
+    }
   }
+  // keep that order: the first 2A reads, then one MFMA per read, then the rest
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * A, 0);
+#pragma unroll
+  for (int i = 0; i < 16 - 2 * A; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * A, 0);
 }
 
 // Softmax of one tile for the lane's row, first part: the causal mask.
@@ -301,6 +332,15 @@ __device__ inline void pv_tile(const uint8_t* T, const f16x8_t* pf, int l32, int
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[k2], o[db], 0, 0, 0);
     }
   }
+  // eight V fragment reads in flight ahead of the MFMAs that use them
+  constexpr int A = 8;
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, A, 0);
+#pragma unroll
+  for (int i = 0; i < 16 - A; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, A, 0);
 }
 
 // Output of one row (64 of its 128 dims per lane): loop 1 writes O, U = 0,
@@ -499,7 +539,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_mfma(MfmaArgs
   const int nt = sh_ntiles;
 
   // ---- prologue: the first kAhead tiles into the ring
-  for (int k = 0; k < kAhead && k < nt; ++k) dma_tile<NW>(imgs + (long long)k * kImgBytes, lds + k * kImgBytes);
+  const __amdgpu_buffer_rsrc_t rs = img_rsrc(imgs, m.ntiles_total * kImgBytes);
+  for (int k = 0; k < kAhead && k < nt; ++k) dma_tile<NW>(rs, k * kImgBytes, lds + k * kImgBytes);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -507,7 +548,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_mfma(MfmaArgs
     const uint8_t* T = lds + (tt % kRing) * kImgBytes;
     // tile tt+kAhead goes into the slot tile tt-1 left (all waves passed it)
     if (tt + kAhead < nt)
-      dma_tile<NW>(imgs + (long long)(tt + kAhead) * kImgBytes, lds + ((tt + kAhead) % kRing) * kImgBytes);
+      dma_tile<NW>(rs, (tt + kAhead) * kImgBytes, lds + ((tt + kAhead) % kRing) * kImgBytes);
     f32x16_t s0, s1;
     qk_tile(T, qf, l32, hf, s0, s1);
     float x[32];
@@ -706,8 +747,8 @@ __global__ __launch_bounds__(64 * NW) void k_mass_mfma(MassArgs m) {
   const int jmax = sh_jmax;
   const uint8_t* rimg = m.rows + ((long long)bh * m.ntr + tile0) * kRowBytes;
 
-  for (int k = 0; k < kMassAhead && k < ntl; ++k)
-    dma_img<NW, kRowChunks>(rimg + (long long)k * kRowBytes, lds + k * kRowBytes);
+  const __amdgpu_buffer_rsrc_t rs = img_rsrc(rimg, ntl * kRowBytes);
+  for (int k = 0; k < kMassAhead && k < ntl; ++k) dma_img<NW, kRowChunks>(rs, k * kRowBytes, lds + k * kRowBytes);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -716,8 +757,7 @@ __global__ __launch_bounds__(64 * NW) void k_mass_mfma(MassArgs m) {
     const uint8_t* T = lds + (tt % kMassRing) * kRowBytes;
     // image tt+kMassAhead goes into the slot image tt-1 left (all waves passed it)
     if (tt + kMassAhead < ntl)
-      dma_img<NW, kRowChunks>(rimg + (long long)(tt + kMassAhead) * kRowBytes,
-                              lds + ((tt + kMassAhead) % kMassRing) * kRowBytes);
+      dma_img<NW, kRowChunks>(rs, (tt + kMassAhead) * kRowBytes, lds + ((tt + kMassAhead) % kMassRing) * kRowBytes);
     const __bf16* tq = (const __bf16*)T;
     const float* toff = (const float*)(T + kRowOffAt);
     const int* tpos = (const int*)(T + kRowPosAt);

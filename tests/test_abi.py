@@ -99,6 +99,11 @@ def test_validation_errors():
     # key/value heads must divide the query heads
     st, msg = _status("fl_kv_resq", ctypes.byref(_cache(Hkv=3)), 1, ok_ptr, ok_ptr, fl.FL_F32, None)
     assert st == EINVAL and "Hkv" in msg
+    # sequences longer than FL_MAX_S tokens are refused before any launch
+    long_c = _cache(S=fl.FL_MAX_S + 64)
+    long_c.n[1] = long_c.S
+    st, msg = _status("fl_kv_resq", ctypes.byref(long_c), 1, ok_ptr, ok_ptr, fl.FL_F32, None)
+    assert st == EUNSUP and "FL_MAX_S" in msg
     s = fl.FlState(ok_ptr, ok_ptr, ok_ptr, ok_ptr)
     st, msg = _status("fl_colsel", ctypes.byref(_cache()), 2, ok_ptr, fl.FL_F32, ctypes.byref(s), 64, None, 65,
                       None, None, ok_ptr, None, 0, None)
