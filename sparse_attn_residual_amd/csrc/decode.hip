@@ -341,21 +341,62 @@ __device__ inline void tok_load(const CacheGeo& c, int l, int b, int h, int j, c
   }
 }
 
-// K and V of the token reconstructed at loop r (and V at loop r-1 when PREV
-// is set) from its loads: base, plus the residuals of loops 2..r in which it
-// was active; loops beyond kMaxFastLoops are looked up here one at a time.
-template <bool PREV, int NR>
-__device__ inline void tok_decode(const CacheGeo& c, int r, int l, int b, int h, int j, const int* slot, int sub,
-                                  const TokLoads<NR>& t, float* kx, float* vx, float* vprev) {
+// The token's K and V reconstructed at loop r from its loads: base, plus the
+// residuals of loops 2..r in which it was active; loops beyond kMaxFastLoops
+// are looked up here one at a time.  K and V are rebuilt in two passes (K
+// before the score, V after it) so that only one 16-element array is live
+// next to the loads; every element sees the same operations in the same order
+// either way.
+template <int NR>
+__device__ __forceinline__ void tok_key(const CacheGeo& c, int r, int l, int b, int h, int j, const int* slot, int sub,
+                                        const TokLoads<NR>& t, float* kx) {
   constexpr int d = 128, G = 4;
   {
-    const float ks = h2f((uint16_t)t.sc), vs = h2f((uint16_t)(t.sc >> 16));
-    const uint32_t kws[4] = {t.kw.x, t.kw.y, t.kw.z, t.kw.w}, vws[4] = {t.vw.x, t.vw.y, t.vw.z, t.vw.w};
+    const float ks = h2f((uint16_t)t.sc);
+    const uint32_t kws[4] = {t.kw.x, t.kw.y, t.kw.z, t.kw.w};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) kx[e] = (float)(int8_t)(kws[e >> 2] >> (8 * (e & 3))) * ks;
+  }
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    if (slot[k] < 0) continue;
+    const int bits = c.bits[k + 2];
+    const float krs = h2f((uint16_t)t.meta[k][0]), krz = h2f((uint16_t)(t.meta[k][0] >> 16));
+    if (bits == 4) {
+      const uint32_t kq[2] = {t.kr[k].x, t.kr[k].y};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) kx[e] = kx[e] + __builtin_fmaf((float)((kq[e >> 3] >> (4 * (e & 7))) & 15), krs, krz);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) kx[e] = kx[e] + __builtin_fmaf((float)((t.kr[k].x >> (2 * e)) & 3), krs, krz);
+    }
+  }
+  for (int rr = kMaxFastLoops + 1; NR == kNF && rr <= r && slot[kNF - 1] >= 0; ++rr) {
+    const int ts = c.slot[rr][(long long)b * c.S + j];
+    if (ts < 0) break;
+    const int bits = c.bits[rr], g = sub >> 1;
+    const uint8_t* rrec = res_rec(c, rr, l, b, kv_head(c, h), ts);
+    const uint16_t* mt = (const uint16_t*)(rrec + 2 * (d * bits / 8));
+    const float krs = h2f(mt[g]), krz = h2f(mt[G + g]);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      kx[e] = (float)(int8_t)(kws[e >> 2] >> (8 * (e & 3))) * ks;
-      vx[e] = (float)(int8_t)(vws[e >> 2] >> (8 * (e & 3))) * vs;
+      const int kc = bits == 4 ? (rrec[sub * 8 + (e >> 1)] >> (4 * (e & 1))) & 15
+                               : (rrec[sub * 4 + (e >> 2)] >> (2 * (e & 3))) & 3;
+      kx[e] = kx[e] + __builtin_fmaf((float)kc, krs, krz);
     }
+  }
+}
+
+// V at loop r, and at loop r-1 when PREV is set.
+template <bool PREV, int NR>
+__device__ __forceinline__ void tok_value(const CacheGeo& c, int r, int l, int b, int h, int j, const int* slot,
+                                          int sub, const TokLoads<NR>& t, float* vx, float* vprev) {
+  constexpr int d = 128, G = 4;
+  {
+    const float vs = h2f((uint16_t)(t.sc >> 16));
+    const uint32_t vws[4] = {t.vw.x, t.vw.y, t.vw.z, t.vw.w};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) vx[e] = (float)(int8_t)(vws[e >> 2] >> (8 * (e & 3))) * vs;
   }
   if (PREV) {
 #pragma unroll
@@ -365,25 +406,18 @@ __device__ inline void tok_decode(const CacheGeo& c, int r, int l, int b, int h,
   for (int k = 0; k < NR; ++k) {
     if (slot[k] < 0) continue;
     const int bits = c.bits[k + 2];
-    const float krs = h2f((uint16_t)t.meta[k][0]), krz = h2f((uint16_t)(t.meta[k][0] >> 16));
     const float vrs = h2f((uint16_t)t.meta[k][1]), vrz = h2f((uint16_t)(t.meta[k][1] >> 16));
     if (PREV && k + 2 == r) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) vprev[e] = vx[e];
     }
     if (bits == 4) {
-      const uint32_t kq[2] = {t.kr[k].x, t.kr[k].y}, vq[2] = {t.vr[k].x, t.vr[k].y};
+      const uint32_t vq[2] = {t.vr[k].x, t.vr[k].y};
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        kx[e] = kx[e] + __builtin_fmaf((float)((kq[e >> 3] >> (4 * (e & 7))) & 15), krs, krz);
-        vx[e] = vx[e] + __builtin_fmaf((float)((vq[e >> 3] >> (4 * (e & 7))) & 15), vrs, vrz);
-      }
+      for (int e = 0; e < 16; ++e) vx[e] = vx[e] + __builtin_fmaf((float)((vq[e >> 3] >> (4 * (e & 7))) & 15), vrs, vrz);
     } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        kx[e] = kx[e] + __builtin_fmaf((float)((t.kr[k].x >> (2 * e)) & 3), krs, krz);
-        vx[e] = vx[e] + __builtin_fmaf((float)((t.vr[k].x >> (2 * e)) & 3), vrs, vrz);
-      }
+      for (int e = 0; e < 16; ++e) vx[e] = vx[e] + __builtin_fmaf((float)((t.vr[k].x >> (2 * e)) & 3), vrs, vrz);
     }
   }
   bool active_r = r >= 2 && r <= NR + 1 && slot[r - 2] >= 0;
@@ -398,14 +432,11 @@ __device__ inline void tok_decode(const CacheGeo& c, int r, int l, int b, int h,
     const int bits = c.bits[rr], C = d * bits / 8, g = sub >> 1;
     const uint8_t* rrec = res_rec(c, rr, l, b, kv_head(c, h), ts);
     const uint16_t* mt = (const uint16_t*)(rrec + 2 * C);
-    const float krs = h2f(mt[g]), krz = h2f(mt[G + g]), vrs = h2f(mt[2 * G + g]), vrz = h2f(mt[3 * G + g]);
+    const float vrs = h2f(mt[2 * G + g]), vrz = h2f(mt[3 * G + g]);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int kc = bits == 4 ? (rrec[sub * 8 + (e >> 1)] >> (4 * (e & 1))) & 15
-                               : (rrec[sub * 4 + (e >> 2)] >> (2 * (e & 3))) & 3;
       const int vc = bits == 4 ? (rrec[C + sub * 8 + (e >> 1)] >> (4 * (e & 1))) & 15
                                : (rrec[C + sub * 4 + (e >> 2)] >> (2 * (e & 3))) & 3;
-      kx[e] = kx[e] + __builtin_fmaf((float)kc, krs, krz);
       vx[e] = vx[e] + __builtin_fmaf((float)vc, vrs, vrz);
     }
   }
@@ -430,23 +461,24 @@ __device__ inline void chunk_index(const DecodeArgs& a, int b, int t0, int lane,
   for (int k = 0; k < NR; ++k) slot[k] = j >= 0 ? c.slot[k + 2][(long long)b * c.S + j] : -1;
 }
 
-// One token's contribution to the group's online softmax (and, pruned, to
-// the cached-mass sums C and P of the previous loop's weights).
+// One token's score and the group's online-softmax update up to its weight:
+// returns p = exp(s - m) for a valid token (the caller adds p * v) and, pruned,
+// pj = the previous loop's weight of the token (added to P here; the caller
+// adds pj * v^(r-1) to C).
 template <bool PRUNED>
-__device__ inline void tok_accumulate(const float* q, const float* kx, const float* vx, const float* vp, float tau,
-                                      float old, float Mprev, float lprev, bool valid, int sub, float* lg, float& m,
-                                      float& lsum, float* acc, float* C, float& P) {
+__device__ __forceinline__ float tok_weight(const float* q, const float* kx, float tau, float old, float Mprev,
+                                            float lprev, bool valid, int sub, float* lg, float& m, float& lsum,
+                                            float* acc, float& P, float& pj) {
   float part = 0.0f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) part = __builtin_fmaf(q[e], kx[e], part);
   const float s = tau * group8_sum_dpp(part);
-  if (!valid) return;
+  pj = 0.0f;
+  if (!valid) return 0.0f;
   if (sub == 0) *lg = s;
   if (PRUNED) {
-    const float pj = Mprev * __expf(old - lprev);
+    pj = Mprev * __expf(old - lprev);
     P += pj;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) C[e] = __builtin_fmaf(pj, vp[e], C[e]);
   }
   if (s > m + kDecRescale) {  // lazy rescale, as in the dense loop
     const float alpha = __expf(m - s);
@@ -457,6 +489,16 @@ __device__ inline void tok_accumulate(const float* q, const float* kx, const flo
   }
   const float p = __expf(s - m);
   lsum += p;
+  return p;
+}
+
+// The valid token's value terms: acc += p * v and, pruned, C += pj * v^(r-1).
+template <bool PRUNED>
+__device__ __forceinline__ void tok_add(float p, float pj, const float* vx, const float* vp, float* acc, float* C) {
+  if (PRUNED) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) C[e] = __builtin_fmaf(pj, vp[e], C[e]);
+  }
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = __builtin_fmaf(p, vx[e], acc[e]);
 }
@@ -465,8 +507,14 @@ __device__ inline void tok_accumulate(const float* q, const float* kx, const flo
 // Each wave walks chunks of 64 selected tokens: the index stage of the next
 // chunk (positions, slots, old logits; one token per lane) is in flight while
 // the current chunk's records are read, two tokens per 8-lane group at a time.
+// Blocks per CU the sparse kernel is built for: three (at most 168 VGPRs, a
+// third wave per SIMD for more loads in flight) where that fits without
+// spilling; otherwise what the code needs.
+constexpr int dec_sparse_blocks(bool pruned, int NR) { return (NR <= 2 || (NR == 3 && !pruned)) ? 3 : 1; }
+
 template <typename T, bool PRUNED, int NR, bool PAPER>
-__global__ __launch_bounds__(kDecThreads) void k_decode_sparse(DecodeArgs a, float tau) {
+__global__ __launch_bounds__(kDecThreads, dec_sparse_blocks(PRUNED, NR))
+void k_decode_sparse(DecodeArgs a, float tau) {
   __shared__ GroupState gs;
   __shared__ float csum[PRUNED ? kDecGroups : 1][128];
   __shared__ float psum[kDecGroups];
@@ -554,15 +602,26 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_sparse(DecodeArgs a, flo
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        float kx[16], vx[16], vp[16];
         if (PAPER) {
           // the paper's format: K, V at loop r (and V at loop r-1) rebuilt here
+          float kx[16], vx[16], vp[16], pj;
           paper_token16<PRUNED>(c, r, l, b, kv_head(c, h), j2[u], sub * 16, kx, vx, vp);
+          const float p = tok_weight<PRUNED>(q, kx, tau, o2[u], Mprev, lprev, v2[u], sub, logit + tt[u], m, lsum,
+                                             acc, P, pj);
+          if (v2[u]) tok_add<PRUNED>(p, pj, vx, vp, acc, C);
         } else {
-          tok_decode<PRUNED>(c, r, l, b, h, j2[u], s2[u], sub, t2[u], kx, vx, vp);
+          float p, pj;
+          {
+            float kx[16];
+            tok_key<NR>(c, r, l, b, h, j2[u], s2[u], sub, t2[u], kx);
+            p = tok_weight<PRUNED>(q, kx, tau, o2[u], Mprev, lprev, v2[u], sub, logit + tt[u], m, lsum, acc, P, pj);
+          }
+          if (v2[u]) {
+            float vx[16], vp[16];
+            tok_value<PRUNED, NR>(c, r, l, b, h, j2[u], s2[u], sub, t2[u], vx, vp);
+            tok_add<PRUNED>(p, pj, vx, vp, acc, C);
+          }
         }
-        tok_accumulate<PRUNED>(q, kx, vx, vp, tau, o2[u], Mprev, lprev, v2[u], sub, logit + tt[u], m, lsum, acc,
-                               C, P);
       }
     }
   }
