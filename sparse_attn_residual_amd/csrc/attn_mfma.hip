@@ -828,13 +828,10 @@ hipError_t launch_gather(const CacheGeo& c, int rc, const int32_t* sel, int K, u
 template <int NW, int MODE>
 static hipError_t launch_one(const MfmaArgs& m, hipStream_t st) {
   constexpr size_t lds = (size_t)kRing * kImgBytes;
-  static bool attr = false;  // the attribute is per kernel; setting it twice is harmless
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_attn_mfma<NW, MODE>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  // once per kernel and process (static initialisation is thread-safe)
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)k_attn_mfma<NW, MODE>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
   const int nunits = m.a.c.B * m.a.c.H * m.nblk;
   hipLaunchKernelGGL((k_attn_mfma<NW, MODE>), dim3(nunits), dim3(64 * NW), lds, st, m);
   return hipGetLastError();
@@ -890,13 +887,9 @@ hipError_t launch_um_mfma(const AttnArgs& a, uint8_t* ws, hipStream_t st) {
 template <bool BASE>
 static hipError_t launch_mass_one(const MassArgs& m, hipStream_t st) {
   constexpr size_t lds = (size_t)kMassRing * kRowBytes;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_mass_mfma<BASE, kMassNW>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static const hipError_t attr = hipFuncSetAttribute((const void*)k_mass_mfma<BASE, kMassNW>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
   const int nunits = m.a.c.B * m.a.c.H * m.ncb;
   hipLaunchKernelGGL((k_mass_mfma<BASE, kMassNW>), dim3(nunits), dim3(64 * kMassNW), lds, st, m);
   return hipGetLastError();

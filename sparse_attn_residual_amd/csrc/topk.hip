@@ -375,13 +375,9 @@ hipError_t launch_topk(const float* keys, long long key_stride, const int32_t* c
   do {                                                                                                          \
     if (cand) {                                                                                                 \
       const int lds = (IT) * kTopkThreads * (int)sizeof(int32_t);                                               \
-      static bool attr = false;                                                                                 \
-      if (!attr) {                                                                                              \
-        hipError_t e = hipFuncSetAttribute((const void*)k_topk<IT, true>,                                       \
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);                    \
-        if (e != hipSuccess) return e;                                                                          \
-        attr = true;                                                                                            \
-      }                                                                                                         \
+      static const hipError_t attr =                                                                            \
+          hipFuncSetAttribute((const void*)k_topk<IT, true>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);  \
+      if (attr != hipSuccess) return attr;                                                                      \
       hipLaunchKernelGGL((k_topk<IT, true>), grid, block, lds, st, keys, key_stride, cand, cand_stride, n, K,   \
                          sel_out, sel_stride, keys_out, keys_out_stride);                                       \
     } else {                                                                                                    \
