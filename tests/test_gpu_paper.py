@@ -79,25 +79,19 @@ def test_paper_streams_bitexact(dtype, S, Hkv, ragged):
     check_streams(cfg, cache, rows, slices)
 
 
-@pytest.mark.parametrize("dtype,d,Hkv", [("f32", 128, 2), ("bf16", 128, 4)])
-def test_paper_prefill(dtype, d, Hkv):
-    """All loops of one layer over paper-format streams (pruning budgets):
-    selections up to near ties, outputs within tolerance of the oracle run on
-    the oracle's own paper-format reconstructions."""
+def _paper_prefill_case(cfg, budgets, heads):
+    """All loops of one layer over paper-format streams on the GPU; the oracle
+    runs on the given heads with the GPU's selections forced (which must match
+    its own up to near ties) and its own paper-format reconstructions."""
     import tests.gpu_harness as gh
     from oracle import prefill
     import sparse_attn_residual_amd as fl
-    f32 = dtype == "f32"
-    cfg = workloads.custom(name="paper-prefill", dtype=dtype, B=2, H=4, d=d, S=1200, R=4, act=(1, 0.5, 0.3, 0.15),
-                           col="0.30", bits=(8, 4, 4, 4), lognormal=None if f32 else 0.5, seed=53, Hkv=Hkv)
-    _say("paper prefill", cfg)
+    f32 = cfg.dtype == "f32"
     rows, slices = workloads.gen_batch(cfg)
-    budgets = [360, 180, 90]
     gpu = gh.run_prefill(cfg, rows, slices, K_budget=budgets, fmt=fl.FL_FMT_PAPER)
-    check_streams(cfg, gpu["cache"], rows, slices)
     tol = 1e-5 if f32 else 2e-3
     for b in range(cfg.B):
-        for h in (0, cfg.H - 1):
+        for h in heads:
             s = slices[(b, h)]
             force = {r + 1: gpu["sel"][r][b, h] for r in range(1, cfg.R)}
             o = prefill.prefill_slice(s.rows, s.q, s.k, s.v, K_budget=cfg.K, bits=cfg.bits, dtype=cfg.dtype,
@@ -106,7 +100,8 @@ def test_paper_prefill(dtype, d, Hkv):
             for r in range(cfg.R):
                 if r >= 1:
                     m = o["mass"][r]
-                    own = prefill.topk(m, cand, min(budgets[r - 1], len(cand)))
+                    K = budgets[r - 1] if isinstance(budgets, list) else cfg.K
+                    own = prefill.topk(m, cand, min(K, len(cand)))
                     ok, nd = gh.near_tie_ok(gpu["sel"][r][b, h], own, m, cand, 1e-5 if f32 else 2e-3)
                     assert ok, (b, h, r + 1, nd)
                     cand = gpu["sel"][r][b, h]
@@ -117,24 +112,41 @@ def test_paper_prefill(dtype, d, Hkv):
                 else:
                     err = np.linalg.norm(O - st.O) / np.linalg.norm(st.O)
                     assert err <= tol, (b, h, r + 1, err)
+    return gpu, rows, slices
 
 
-@pytest.mark.parametrize("dtype,Hkv", [("f32", 2), ("bf16", 4)])
-def test_paper_decode(dtype, Hkv):
-    """Decode over paper-format streams (tail tokens included), against the
-    oracle's decode step on the paper-format reconstructions."""
+@pytest.mark.parametrize("dtype,d,Hkv", [("f32", 128, 2), ("bf16", 128, 4)])
+def test_paper_prefill(dtype, d, Hkv):
+    """All loops of one layer over paper-format streams (pruning budgets):
+    selections up to near ties, outputs within tolerance of the oracle run on
+    the oracle's own paper-format reconstructions; the streams bit-exact."""
+    f32 = dtype == "f32"
+    cfg = workloads.custom(name="paper-prefill", dtype=dtype, B=2, H=4, d=d, S=1200, R=4, act=(1, 0.5, 0.3, 0.15),
+                           col="0.30", bits=(8, 4, 4, 4), lognormal=None if f32 else 0.5, seed=53, Hkv=Hkv)
+    _say("paper prefill", cfg)
+    gpu, rows, slices = _paper_prefill_case(cfg, [360, 180, 90], heads=(0, cfg.H - 1))
+    check_streams(cfg, gpu["cache"], rows, slices)
+
+
+def test_paper_prefill_full_size():
+    """The 32K workload in the paper's cache format, in the launch
+    configuration the benchmark times; oracle on two heads."""
+    cfg = workloads.CONFIGS[2]
+    _say("paper prefill full size", cfg.name)
+    _paper_prefill_case(cfg, cfg.K, heads=(0, cfg.H - 1))
+
+
+def _paper_decode_case(cfg):
+    """Decode over paper-format streams (tail tokens included) against the
+    oracle's decode step on the paper-format reconstructions, every head."""
     import tests.gpu_harness as gh
     import sparse_attn_residual_amd as fl
     from oracle import decode, prefill
-    cfg = workloads.custom(name="paper-decode", dtype=dtype, B=2, H=4, d=128, S=900, R=4, act=(1, 0.3, 0.15, 0.08),
-                           col="0.10", bits=(8, 4, 4, 4), gamma=0.5, lognormal=0.5, L=2, decode=True, seed=55,
-                           Hkv=Hkv)
-    _say("paper decode", cfg)
     rows, slices = workloads.gen_batch(cfg)
     cache = gh.build_decode_cache(cfg, rows, slices, fmt=fl.FL_FMT_PAPER)
     qs = workloads.decode_queries(cfg)
     gpu = gh.run_decode(cfg, cache, qs)
-    rel = dtype != "f32"
+    rel = cfg.dtype != "f32"
     tol = 2e-3 if rel else 1e-5
     for b in range(cfg.B):
         for h in range(cfg.H):
@@ -156,3 +168,22 @@ def test_paper_decode(dtype, Hkv):
                     O, o = gpu[r]["O"][l, b, h], orc[r]["O"]
                     err = np.linalg.norm(O - o) / np.linalg.norm(o) if rel else np.max(np.abs(O - o))
                     assert err <= tol, (l, b, h, r + 1, err)
+
+
+@pytest.mark.parametrize("dtype,Hkv", [("f32", 2), ("bf16", 4)])
+def test_paper_decode(dtype, Hkv):
+    """Decode over paper-format streams with grouped KV heads, two layers."""
+    cfg = workloads.custom(name="paper-decode", dtype=dtype, B=2, H=4, d=128, S=900, R=4, act=(1, 0.3, 0.15, 0.08),
+                           col="0.10", bits=(8, 4, 4, 4), gamma=0.5, lognormal=0.5, L=2, decode=True, seed=55,
+                           Hkv=Hkv)
+    _say("paper decode", cfg)
+    _paper_decode_case(cfg)
+
+
+def test_paper_decode_full_shape():
+    """The 48-layer decode workload's per-head shape (T = 32768, K = 3276,
+    R = 4) in the paper's cache format, two heads of one layer and sequence."""
+    import dataclasses
+    cfg = dataclasses.replace(workloads.CONFIGS[3], name="paper-decode-full-shape", B=1, H=2, L=1)
+    _say("paper decode full shape", cfg)
+    _paper_decode_case(cfg)

@@ -336,6 +336,15 @@ def test_prefill_gqa(dtype, d, H, Hkv):
                rel=not f32)
 
 
+def test_prefill_gqa_full_size():
+    """The 32K workload with 4 KV heads for its 16 query heads, in the launch
+    configuration the benchmark times; oracle on one query head of each of two
+    KV groups."""
+    cfg = workloads.CONFIGS[2].with_(Hkv=4)
+    _say("prefill gqa full size", cfg.name, cfg.kv_heads)
+    _bf16_case(cfg, heads=[0, 7])
+
+
 @pytest.mark.parametrize("dtype,d,ragged", [("f32", 64, (1, 0.55, 0.3)), ("bf16", 128, (0.4, 1, 0.7))])
 def test_prefill_ragged_counts(dtype, d, ragged):
     """A batch whose sequences keep different numbers of active rows (a
