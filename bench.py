@@ -330,7 +330,27 @@ def cpu_baseline(workloads):
     value = cfg.S / (t * cfg.H)   # one head is 1/H of a step
     return dict(value=value, unit="tokens/s", cores=int(threads), kind="oracle",
                 sample=f"{cfg.name}: head 0 of {cfg.H}, all {cfg.R} loops in float64 ({t:.1f}s), "
-                       f"scaled to {cfg.H} heads")
+                       f"scaled to {cfg.H} heads", cpu_model=_cpu_model(), blas=_blas())
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas() -> str:
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{p.get('internal_api')} {p.get('version')}" for p in threadpool_info() if p.get("user_api") == "blas"]
+        return ", ".join(libs) or "unknown"
+    except Exception:
+        return "unknown"
 
 
 def main():
@@ -434,6 +454,19 @@ def main():
             "flops_per_launch": dense_flops,
             "avg_launch_ms": pf["per"]["attn1"],
         },
+    }
+    qb = [acc.resq_bytes(cfg.d, cfg.bits[:r], cfg.B * cfg.n[r - 1], cfg.kv_heads) for r in range(1, cfg.R + 1)]
+    qt = [pf["per"][f"resq{r}"] for r in range(1, cfg.R + 1)]
+    out["quantize"] = {
+        "kernel": "k_quant_base (r = 1), k_quant_res (r >= 2): fl_kv_resq of the prefill workload",
+        "algorithmic_bytes_per_loop": qb,
+        "ms_per_loop": [round(t, 4) for t in qt],
+        "gbs_per_loop": [b / (t * 1e6) for b, t in zip(qb, qt)],
+        "frac_per_loop": [b / (t * 1e6) / acc.MI355X_HBM_GBS for b, t in zip(qb, qt)],
+        "bound": "hbm",
+        "peak_gbs": acc.MI355X_HBM_GBS,
+        "bytes_note": "per active (row, KV head): K and V rows in, the records of the earlier loops the residual is "
+                      "taken against, one record out",
     }
     out["select"] = {
         "workload": f"{cfg.name}: next active sets of loops 2..{cfg.R}, hidden size {sel['D']}, bf16 "

@@ -53,6 +53,17 @@ def residual_record_bytes(d: int, bits: int) -> int:
     return 2 * (d * bits // 8) + 8 * (d // 32)
 
 
+def resq_bytes(d: int, bits, n_rows: int, kv_heads: int, elem_bytes: int = 2) -> int:
+    """Algorithmic HBM bytes of one fl_kv_resq call at loop r = len(bits): per
+    active (row, KV head) the loop's K and V rows are read, the records of
+    loops 1..r-1 the residual is taken against are read, and one record is
+    written.  bits = (bits_1, ..., bits_r)."""
+    r = len(bits)
+    chain = base_record_bytes(d) + sum(residual_record_bytes(d, b) for b in bits[1:r - 1]) if r > 1 else 0
+    write = base_record_bytes(d) if r == 1 else residual_record_bytes(d, bits[r - 1])
+    return n_rows * kv_heads * (2 * d * elem_bytes + chain + write)
+
+
 def prefill_work(cfg, rows_per_b, sels, masses_ran) -> dict:
     """Exact pair counts and FLOPs of one prefill step.
 

@@ -53,3 +53,14 @@ def test_record_bytes_match_layout():
         assert fl.fl_base_record_bytes(d) == (acc.base_record_bytes(d) + 15) // 16 * 16
         for b in (2, 4):
             assert fl.fl_residual_record_bytes(d, b) == (acc.residual_record_bytes(d, b) + 15) // 16 * 16
+
+
+def test_resq_bytes_hand_count():
+    """fl_kv_resq bytes at d = 128, bf16 inputs, per active (row, KV head):
+    K and V in (2 x 128 x 2 = 512 B), the earlier loops' records read (base
+    272 B, 4-bit residual 160 B), one record out (2-bit residual 96 B)."""
+    from sparse_attn_residual_amd import accounting as acc
+    assert acc.resq_bytes(128, (8,), 32768, 16) == 32768 * 16 * (512 + 272)
+    assert acc.resq_bytes(128, (8, 4), 9830, 16) == 9830 * 16 * (512 + 272 + 160)
+    assert acc.resq_bytes(128, (8, 4, 4), 4915, 16) == 4915 * 16 * (512 + 272 + 160 + 160)
+    assert acc.resq_bytes(128, (8, 4, 4, 2), 2621, 16) == 2621 * 16 * (512 + 272 + 160 + 160 + 96)
