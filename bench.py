@@ -333,6 +333,33 @@ def cpu_baseline(workloads):
                        f"scaled to {cfg.H} heads", cpu_model=_cpu_model(), blas=_blas())
 
 
+def cpu_decode_baseline(workloads, step_bytes):
+    """The oracle's decode step on a few (layer, sequence, head) slices of the
+    48-layer workload (all R loops each; the cache records are built first and
+    not timed), extrapolated to every slice of the step."""
+    import dataclasses
+    from oracle import decode, quant
+    cfg = workloads.CONFIGS[DECODE_CFG]
+    n = 4
+    small = dataclasses.replace(cfg, name=cfg.name + "-cpu-sample", B=1, H=n, L=1)
+    rows, sl = workloads.gen_batch(small)
+    qs = workloads.decode_queries(small)
+    t = 0.0
+    for h in range(n):
+        s = sl[(0, h)]
+        _, krec = quant.quantize_chain(s.k, s.rows, list(small.bits))
+        _, vrec = quant.quantize_chain(s.v, s.rows, list(small.bits))
+        t0 = time.perf_counter()
+        decode.decode_slice(krec, vrec, [q[0, 0, h] for q in qs], small.K)
+        t += time.perf_counter() - t0
+    slices = cfg.L * cfg.B * cfg.H
+    step_s = t / n * slices
+    return dict(value=step_bytes / step_s / 1e9, unit="GB/s", kind="oracle", extrapolated=True,
+                ms_per_step=step_s * 1e3,
+                sample=f"{n} of the step's {slices} (layer, sequence, head) slices, all {cfg.R} loops in float64 "
+                       f"({t:.2f}s), extrapolated to the whole step")
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -509,6 +536,8 @@ def main():
                 "step_frac": dec["gbs"] / acc.MI355X_HBM_GBS,
             },
         }
+        if not args.no_cpu:
+            out["decode"]["cpu_oracle"] = cpu_decode_baseline(workloads, dec["bytes"])
     if extra:
         _extras(out, cfg, gqa_pf, gqa_dec, pap_pf, pap_dec, rag_cfg, rag_pf)
     if cpu is not None:
