@@ -41,8 +41,13 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kD = 128;
 constexpr int kBN = 64;             // key columns per tile
 constexpr int kNoPos = 0x7fffffff;  // padding column: masked for every row
-constexpr float kRescale = 8.0f;    // lazy rescale threshold (log2 units): P <= 2^8
-constexpr float kRescaleP = 256.0f;  // 2^kRescale
+// Lazy rescale threshold (log2 units): a weight P = 2^(x*c2 - mref) may reach
+// 2^15 before the reference moves.  fp16 holds it (max 65504), rounds it with
+// the same relative error at any size, and keeps weights normal down to 2^-14,
+// i.e. scores up to 29 below the row maximum; a lower threshold would only
+// rescale more often.
+constexpr float kRescale = 15.0f;
+constexpr float kRescaleP = 32768.0f;  // 2^kRescale
 
 // Tile image: the exact LDS layout of one 64-column tile, built once per loop
 // in HBM and copied into LDS by direct global->LDS loads.
