@@ -247,6 +247,19 @@ def test_prefill_pruned_every_loop(dtype, d):
         _bf16_case(cfg, heads=[0, 1, 2], sel_eps=1e-5, budgets=[680, 350, 140], tol=1e-5, rel=False)
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 128)])
+def test_prefill_vector_path_other_dims(dtype, d):
+    """bf16 at head dim 64 and fp32 at head dim 128 take the vector-ALU
+    kernels (the matrix-core ones take bf16 at d = 128): every loop with
+    pruning budgets against the oracle."""
+    f32 = dtype == "f32"
+    cfg = workloads.custom(name="prefill-vector", dtype=dtype, B=2, H=2, d=d, S=1100, R=4, act=(1, 0.5, 0.3, 0.15),
+                           col="0.40", bits=(8, 4, 2, 4), lognormal=None if f32 else 0.5, seed=41)
+    _say("prefill vector path", dtype, d, cfg)
+    _bf16_case(cfg, heads=[0, 1], sel_eps=1e-5 if f32 else 2e-3, budgets=[440, 220, 90], tol=1e-5 if f32 else 2e-3,
+               rel=not f32)
+
+
 def test_prefill_pruned_full_size():
     """The 32K-token workload with a budget that shrinks every loop
     (3277 -> 2000 -> 1000 columns), all heads on the GPU, oracle on two."""
