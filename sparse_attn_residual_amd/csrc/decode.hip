@@ -76,16 +76,8 @@ constexpr int kDenseThreads = 512;  // one block per (layer, sequence, query-hea
 // so the accumulators are rescaled rarely.  Group states merge within each
 // wavefront by lane shuffles, then across wavefronts in LDS.  Every head's
 // arithmetic is the same whatever GQ is.
-// Waves per SIMD the dense kernel is built for: the paper format's
-// per-block key arithmetic needs ~138 VGPRs at its natural schedule, which
-// leaves one 512-thread block per CU; at 128 VGPRs two blocks fit and more
-// records are in flight.  Six values then live in scratch (a handful of
-// spill accesses per loop iteration); the loop is faster all the same.
-constexpr int dec_dense_waves(bool paper) { return paper ? 4 : 1; }
-
 template <typename T, int NT, int GQ, bool PAPER>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(dec_dense_waves(PAPER))))
-void k_decode_dense(DecodeArgs a, float tau) {
+__global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
   constexpr int NG = NT / 8, NW = NT / kWave;
   static_assert(GQ * 128 <= NT, "one thread per output dim of every head");
   __shared__ float wm[GQ][NW], wl[GQ][NW], wacc[GQ][NW][128];
