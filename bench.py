@@ -221,18 +221,32 @@ def decode_bench(args, torch, fl, workloads, acc, cfg=None, fmt=0):
     base_b = acc.base_record_bytes(d)
     res_b = [0] + [acc.residual_record_bytes(d, cfg.bits[r]) for r in range(1, R)]
     loop_bytes = [float(L * B * Hkv * S * base_b)]
-    sel = st.sel[..., :Ks[-1]].long()  # S_2 = S_3 = S_4 with a constant budget
-    cum = torch.full((B, S), float(base_b), dtype=torch.float64, device="cuda")
+    # S_2 = S_3 = S_4 with a constant budget: the last loop's selection,
+    # checked on the host before it indexes anything
+    sel = check_selection(st.sel[..., :Ks[-1]].cpu().numpy(), S, Ks[-1])
+    cum = np.full((B, S), float(base_b))
     for r in range(2, R + 1):
-        cum += (cache.slot[r - 1] >= 0).double() * res_b[r - 1]
-        per_j = torch.gather(cum.unsqueeze(0).unsqueeze(2).expand(L, B, H, S), 3, sel)
-        loop_bytes.append(float(per_j.sum().item()))
+        cum += (cache.slot[r - 1].cpu().numpy() >= 0) * float(res_b[r - 1])
+        loop_bytes.append(float(sum(np.take_along_axis(cum[b][None, None, :], sel[:, b], axis=2).sum()
+                                    for b in range(B))))
     total = sum(loop_bytes)
     logits_overhead = float(L * B * H * S * 4 * 2)
     return dict(cfg=cfg, ms_step=ms_step, per=per, loop_bytes=loop_bytes, bytes=total,
                 cache_stream1_bytes=float(cache.base.numel()),
                 gbs=total / (ms_step * 1e-3) / 1e9, dense_gbs=loop_bytes[0] / (per["decode1"] * 1e-3) / 1e9,
                 logits_overhead=logits_overhead, cache_bytes=cache.nbytes())
+
+
+def check_selection(sel, T, K):
+    """sel [..., K] int32 from the device: every row must hold K positions in
+    [0, T), strictly ascending.  Raises before the selection indexes anything."""
+    if sel.shape[-1] != K:
+        raise RuntimeError(f"decode selection has {sel.shape[-1]} entries per row, expected {K}")
+    if sel.size and (sel.min() < 0 or sel.max() >= T):
+        raise RuntimeError(f"decode selection holds positions outside [0, {T}): min {sel.min()}, max {sel.max()}")
+    if K > 1 and not np.all(np.diff(sel, axis=-1) > 0):
+        raise RuntimeError("decode selection is not strictly ascending")
+    return sel.astype(np.int64)
 
 
 def select_bench(args, torch, fl, workloads, acc):

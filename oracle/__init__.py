@@ -21,7 +21,8 @@ Modules
   brute      full-matrix bookkeeping form of the loop recurrences (tiny sizes)
   active     the next loop's active-token set (relative hidden-state change,
              top-k, nested)
-  accounting byte and FLOP accounting (cache sizes, decode bytes)
+  paper_format the paper's own cache format (INT4 asymmetric, group 64,
+             per-channel keys, per-token values, bf16 tail)
 
 Pins (see tests/test_oracle_*.py): brute-force code search, the half-step
 reconstruction bound, special groups, a hand-worked packing example, a library

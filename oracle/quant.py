@@ -107,18 +107,6 @@ def quant_residual(x: np.ndarray, prev: np.ndarray, bits: int):
     return c.reshape(delta.shape), s16, z16, recon
 
 
-def dequant_base(codes: np.ndarray, scale16: np.ndarray) -> np.ndarray:
-    c = _groups(codes.astype(np.float32))
-    return (c * scale16.astype(np.float32)[..., None]).reshape(codes.shape).astype(np.float32)
-
-
-def dequant_residual(codes: np.ndarray, scale16: np.ndarray, zero16: np.ndarray) -> np.ndarray:
-    c = _groups(codes.astype(np.float64))
-    s = scale16.astype(np.float64)[..., None]
-    z = zero16.astype(np.float64)[..., None]
-    return (c * s + z).astype(np.float32).reshape(codes.shape)
-
-
 def quantize_chain(k: list, rows: list, bits: list):
     """Quantize one (b, h) tensor chain of all loops.
 
@@ -142,7 +130,21 @@ def quantize_chain(k: list, rows: list, bits: list):
 
 
 def bf16_rne(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to bfloat16 (nearest even), returned as float32."""
-    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    """Round float32 values to bfloat16, round to nearest, ties to the even
+    significand (IEEE 754 roundTiesToEven), returned as float32.
+
+    bf16 keeps the upper 16 bits of a float32.  Adding 0x7FFF plus the lowest
+    kept bit before truncating moves every value above the halfway point up,
+    every value below it down, and a value exactly halfway to the neighbour
+    whose lowest kept bit is 0.  A carry out of the significand raises the
+    exponent, which is the right result, including overflow to infinity past
+    the largest bf16 value.  NaN stays NaN (the carry could otherwise turn a
+    NaN payload into infinity)."""
+    f = np.asarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
     u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    out = u.astype(np.uint32).view(np.float32)
+    nan = np.isnan(f)
+    if np.any(nan):
+        out = np.where(nan, np.float32(np.nan), out).astype(np.float32)
+    return out

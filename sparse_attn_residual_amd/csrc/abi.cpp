@@ -6,7 +6,10 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
+#include <vector>
 
 #include "launch.hpp"
 
@@ -125,6 +128,120 @@ fl_status check_state(const char* fn, const fl_state* s) {
 
 constexpr int kTopkMax = 32768;  // keys per selection problem (32 per thread)
 
+// ---------------------------------------------------------------- FL_CHECK
+// The synchronous validator of the device-side index data (the documented
+// preconditions nothing else checks): with FL_CHECK set to anything but "0"
+// or "", a call first drains its stream, copies the index arrays it will read
+// to the host and checks them; a violation returns FL_EINVAL before any
+// launch.  A debugging aid: it costs a synchronization and the copies.
+bool check_on() {
+  const char* e = std::getenv("FL_CHECK");
+  return e && e[0] && !(e[0] == '0' && e[1] == 0);
+}
+
+template <typename T>
+fl_status fetch(const char* fn, std::vector<T>& out, const void* dev, size_t n, hipStream_t st, const char* what) {
+  out.assign(n, T{});
+  if (n == 0) return FL_OK;
+  const hipError_t e = fl::copy_to_host(out.data(), dev, n * sizeof(T), st);
+  if (e != hipSuccess) return fail(FL_EHIP, "%s: FL_CHECK could not read %s: %s", fn, what, hipGetErrorString(e));
+  return FL_OK;
+}
+
+// Loops 2..last_rows: counts in [1, n[r]] and within loop r-1's count, rows
+// strictly ascending in [0, S) and a subset of loop r-1's active set (nested
+// sets; loop 1 holds every position).  Loops 2..last_slot: slot[r] is the
+// inverse of rows[r] (slot[r][b][rows[r][b][t]] = t) and -1 elsewhere.
+// active: if non-NULL, receives the [B][S] membership mask of A_last_rows.
+fl_status check_index_sets(const char* fn, const fl_cache* c, int last_rows, int last_slot, hipStream_t st,
+                           std::vector<uint8_t>* active = nullptr, std::vector<int32_t>* counts = nullptr,
+                           std::vector<int32_t>* rows_out = nullptr) {
+  const int B = c->B, S = c->S;
+  std::vector<int32_t> prev_cnt(B, S), cnt, rows, slot;
+  std::vector<uint8_t> prev_in((size_t)B * S, 1), in((size_t)B * S, 0);
+  fl_status s;
+  for (int r = 2; r <= last_rows; ++r) {
+    const int n = c->n[r];
+    char what[48];
+    if (c->cnt[r]) {
+      std::snprintf(what, sizeof what, "cache->cnt[%d]", r);
+      if ((s = fetch(fn, cnt, c->cnt[r], (size_t)B, st, what)) != FL_OK) return s;
+    } else {
+      cnt.assign(B, n);
+    }
+    std::snprintf(what, sizeof what, "cache->rows[%d]", r);
+    if ((s = fetch(fn, rows, c->rows[r], (size_t)B * n, st, what)) != FL_OK) return s;
+    if (r <= last_slot) {
+      std::snprintf(what, sizeof what, "cache->slot[%d]", r);
+      if ((s = fetch(fn, slot, c->slot[r], (size_t)B * S, st, what)) != FL_OK) return s;
+    }
+    std::fill(in.begin(), in.end(), (uint8_t)0);
+    for (int b = 0; b < B; ++b) {
+      const int t = cnt[b];
+      if (t < 1 || t > n)
+        return fail(FL_EINVAL, "%s: FL_CHECK: sequence %d has %d active rows at loop %d, outside [1, n[%d] = %d]", fn,
+                    b, t, r, r, n);
+      if (t > prev_cnt[b])
+        return fail(FL_EINVAL, "%s: FL_CHECK: sequence %d has %d active rows at loop %d, more than loop %d's %d "
+                    "(nested sets)", fn, b, t, r, r - 1, prev_cnt[b]);
+      const int32_t* rw = &rows[(size_t)b * n];
+      uint8_t* mine = &in[(size_t)b * S];
+      const uint8_t* theirs = &prev_in[(size_t)b * S];
+      for (int i = 0; i < t; ++i) {
+        const int j = rw[i];
+        if (j < 0 || j >= S)
+          return fail(FL_EINVAL, "%s: FL_CHECK: rows[%d][%d][%d] = %d outside [0, S = %d)", fn, r, b, i, j, S);
+        if (i > 0 && j <= rw[i - 1])
+          return fail(FL_EINVAL, "%s: FL_CHECK: rows[%d] of sequence %d not strictly ascending at entry %d (%d after %d)",
+                      fn, r, b, i, j, rw[i - 1]);
+        if (!theirs[j])
+          return fail(FL_EINVAL, "%s: FL_CHECK: rows[%d] of sequence %d holds position %d, not active at loop %d "
+                      "(nested sets)", fn, r, b, j, r - 1);
+        mine[j] = 1;
+      }
+      if (r <= last_slot) {
+        const int32_t* sl = &slot[(size_t)b * S];
+        for (int i = 0; i < t; ++i)
+          if (sl[rw[i]] != i)
+            return fail(FL_EINVAL, "%s: FL_CHECK: slot[%d][%d][%d] = %d, expected %d (rows[%d] entry)", fn, r, b, rw[i],
+                        sl[rw[i]], i, r);
+        for (int j = 0; j < S; ++j)
+          if (sl[j] != -1 && !mine[j])
+            return fail(FL_EINVAL, "%s: FL_CHECK: slot[%d][%d][%d] = %d for a position outside loop %d's rows", fn, r,
+                        b, j, sl[j], r);
+      }
+    }
+    prev_cnt.swap(cnt);
+    prev_in.swap(in);
+    if (rows_out && r == last_rows) *rows_out = rows;
+  }
+  if (active) *active = prev_in;
+  if (counts) *counts = prev_cnt;
+  return FL_OK;
+}
+
+// P rows of `len` int32 entries, `stride` entries apart: each strictly
+// ascending within [0, lim).
+fl_status check_sel(const char* fn, const int32_t* dev, long long P, int len, long long stride, int lim,
+                    hipStream_t st, const char* what) {
+  if (P <= 0 || len <= 0) return FL_OK;
+  std::vector<int32_t> h((size_t)P * len);
+  const hipError_t e = fl::copy_rows_to_host(h.data(), (size_t)len * 4, dev, (size_t)stride * 4, (size_t)len * 4,
+                                             (size_t)P, st);
+  if (e != hipSuccess) return fail(FL_EHIP, "%s: FL_CHECK could not read %s: %s", fn, what, hipGetErrorString(e));
+  for (long long p = 0; p < P; ++p) {
+    const int32_t* x = &h[(size_t)p * len];
+    for (int i = 0; i < len; ++i) {
+      if (x[i] < 0 || x[i] >= lim)
+        return fail(FL_EINVAL, "%s: FL_CHECK: %s row %lld entry %d = %d outside [0, %d)", fn, what, p, i, x[i], lim);
+      if (i > 0 && x[i] <= x[i - 1])
+        return fail(FL_EINVAL, "%s: FL_CHECK: %s row %lld not strictly ascending at entry %d (%d after %d)", fn, what,
+                    p, i, x[i], x[i - 1]);
+    }
+  }
+  return FL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -170,7 +287,10 @@ size_t mass_pass_bytes(const fl_cache* c, int r, bool base, int K_prev) {
 }  // namespace
 
 size_t fl_workspace_bytes(int which, const fl_cache* cache, int r, int K_prev, int K_r) {
-  if (!cache || K_prev < 0 || K_r < 0 || r < 1) return 0;
+  if (!cache || r < 1 || r > cache->R) return 0;
+  // loop 1's attention covers every position whatever the budgets say
+  if (which == FL_WS_ATTN && r == 1) return tiles_bytes(cache, cache->S);
+  if (K_prev < 0 || K_r < 0) return 0;
   if (which == FL_WS_COLSEL) {
     // masses, then (in turn) what the mass pass reads and the tiles of the
     // selected columns the cached-mass pass gathers
@@ -179,7 +299,7 @@ size_t fl_workspace_bytes(int which, const fl_cache* cache, int r, int K_prev, i
     return align256((size_t)cache->B * cache->H * (size_t)K_prev * sizeof(float)) +
            std::max(tiles_bytes(cache, K_r), mass_pass_bytes(cache, r, base, K_prev));
   }
-  if (which == FL_WS_ATTN) return tiles_bytes(cache, r == 1 ? cache->S : K_r);
+  if (which == FL_WS_ATTN) return tiles_bytes(cache, K_r);
   return 0;
 }
 
@@ -193,6 +313,8 @@ fl_status fl_kv_resq(const fl_cache* cache, int r, const void* k, const void* v,
   FL_NEED_PTR(k, "k");
   FL_NEED_PTR(v, "v");
   hipStream_t st = (hipStream_t)stream;
+  // loop r's rows are read here; slot[r] is written here
+  if (check_on() && r >= 2 && (s = check_index_sets(fn, cache, r, r - 1, st)) != FL_OK) return s;
   hipError_t e;
   if (r == 1) {
     e = geo.fmt == FL_FMT_PAPER ? fl::launch_paper_quant(geo, 1, k, v, dtype, cache->base, st)
@@ -223,6 +345,23 @@ fl_status fl_kv_append(const fl_cache* cache, int r, int pos, const void* k, con
     return fail(FL_EUNSUPPORTED, "%s: appending to the paper format (its key groups span 64 tokens)", fn);
   if (r >= 2 && !cache->cnt[r])
     return fail(FL_EINVAL, "%s: appending a row at loop %d needs the per-sequence counts cache->cnt[%d]", fn, r, r);
+  if (check_on() && r >= 2) {
+    // the sets as they stand, then: pos active at loop r-1 and after every
+    // row loop r holds in each sequence that still has room
+    std::vector<uint8_t> prev_in;
+    std::vector<int32_t> prev_cnt, cnt, rows;
+    if ((s = check_index_sets(fn, cache, r - 1, r - 1, (hipStream_t)stream, &prev_in, &prev_cnt)) != FL_OK) return s;
+    if ((s = check_index_sets(fn, cache, r, r, (hipStream_t)stream, nullptr, &cnt, &rows)) != FL_OK) return s;
+    for (int b = 0; b < cache->B; ++b) {
+      if (cnt[b] >= cache->n[r]) continue;
+      if (!prev_in[(size_t)b * cache->S + pos])
+        return fail(FL_EINVAL, "%s: FL_CHECK: position %d is not active at loop %d in sequence %d (nested sets)", fn,
+                    pos, r - 1, b);
+      if (rows[(size_t)b * cache->n[r] + cnt[b] - 1] >= pos)
+        return fail(FL_EINVAL, "%s: FL_CHECK: position %d does not follow the active rows of loop %d in sequence %d",
+                    fn, pos, r, b);
+    }
+  }
   hipError_t e = fl::launch_append(geo, r, pos, k, v, dtype, cache->base, cache->res[r],
                                    r >= 2 ? const_cast<int32_t*>(cache->rows[r]) : nullptr,
                                    r >= 2 ? cache->slot[r] : nullptr, r >= 2 ? cache->cnt[r] : nullptr,
@@ -274,6 +413,18 @@ fl_status fl_colsel(const fl_cache* cache, int r, const void* q_prev, fl_dtype d
   if (prune && K_prev > kTopkMax)
     return fail(FL_EUNSUPPORTED, "%s: %d candidates (at most %d)", fn, K_prev, kTopkMax);
   hipStream_t st = (hipStream_t)stream;
+  if (check_on()) {
+    // rows of loops <= r; the chains and queries of loop r-1
+    if ((s = check_index_sets(fn, cache, r, r - 1, st)) != FL_OK) return s;
+    if (cand && (s = check_sel(fn, cand, (long long)cache->B * cache->H, K_prev, K_prev, cache->S, st, "cand")) != FL_OK)
+      return s;
+    if (prune && mass_in) {
+      std::vector<float> m;
+      if ((s = fetch(fn, m, mass_in, (size_t)cache->B * cache->H * K_prev, st, "mass_in")) != FL_OK) return s;
+      for (size_t i = 0; i < m.size(); ++i)
+        if (std::isnan(m[i])) return fail(FL_EINVAL, "%s: FL_CHECK: mass_in[%zu] is NaN", fn, i);
+    }
+  }
   fl::AttnArgs a{};
   a.c = geo;
   a.r = r;
@@ -292,7 +443,7 @@ fl_status fl_colsel(const fl_cache* cache, int r, const void* q_prev, fl_dtype d
     if (e != hipSuccess) return hip_fail(e, fn);
     // same columns as loop r-1: their loop r-1 log-sum-exp is loop r-1's lse
     if (state->lsel) {
-      e = hipMemcpyAsync(state->lsel, state->lse, (size_t)P * cache->S * sizeof(float), hipMemcpyDeviceToDevice, st);
+      e = fl::copy_d2d_async(state->lsel, state->lse, (size_t)P * cache->S * sizeof(float), st);
       if (e != hipSuccess) return hip_fail(e, fn);
     }
     return FL_OK;
@@ -323,10 +474,17 @@ fl_status fl_loop_attn(const fl_cache* cache, int r, const void* q, fl_dtype dty
     if (K_r < 1 || K_r > cache->S) return fail(FL_EINVAL, "%s: K_r = %d outside [1, S]", fn, K_r);
   }
   {
-    const size_t need = dtype == FL_BF16 ? fl_workspace_bytes(FL_WS_ATTN, cache, r, K_r, K_r) : 0;
+    // the tile images of every attended column (K_r has been checked when r >= 2; loop 1 attends all S)
+    const size_t need = dtype == FL_BF16 ? tiles_bytes(cache, r == 1 ? cache->S : K_r) : 0;
     if (need > 0 && (!ws || ws_bytes < need))
       return fail(FL_EINVAL, "%s: workspace of %zu bytes needed (got %zu)", fn, need, ws ? ws_bytes : (size_t)0);
     if (need > 0 && !aligned16(ws)) return fail(FL_EINVAL, "%s: ws is not 16-byte aligned", fn);
+  }
+  if (check_on() && r >= 2) {
+    if ((s = check_index_sets(fn, cache, r, r, (hipStream_t)stream)) != FL_OK) return s;
+    if ((s = check_sel(fn, sel, (long long)cache->B * cache->H, K_r, K_r, cache->S, (hipStream_t)stream, "sel")) !=
+        FL_OK)
+      return s;
   }
   fl::AttnArgs a{};
   a.c = geo;
@@ -370,6 +528,13 @@ fl_status fl_loop_decode(const fl_cache* cache, int r, const void* q, fl_dtype d
     if (K_r < K_prev && K_prev > kTopkMax)
       return fail(FL_EUNSUPPORTED, "%s: %d candidates (at most %d)", fn, K_prev, kTopkMax);
   }
+  if (check_on() && r >= 2) {
+    if ((s = check_index_sets(fn, cache, r, r, (hipStream_t)stream)) != FL_OK) return s;
+    // loop r >= 3 ranks (or keeps) the previous loop's selection
+    if (r >= 3 && (s = check_sel(fn, state->sel, (long long)cache->L * cache->B * cache->H, K_prev, cache->S, geo.T,
+                                 (hipStream_t)stream, "state->sel")) != FL_OK)
+      return s;
+  }
   fl::DecodeArgs a{};
   a.c = geo;
   a.r = r;
@@ -404,6 +569,9 @@ fl_status fl_select_active(int B, int S, int D, const void* h_prev, const void* 
   if (k < n_prev && n_prev > kTopkMax)
     return fail(FL_EUNSUPPORTED, "%s: %d candidates (at most %d)", fn, n_prev, kTopkMax);
   if ((long long)B * S * D > (1LL << 40)) return fail(FL_EUNSUPPORTED, "%s: hidden states too large", fn);
+  if (check_on() && rows_prev &&
+      (s = check_sel(fn, rows_prev, B, n_prev, n_prev, S, (hipStream_t)stream, "rows_prev")) != FL_OK)
+    return s;
   hipError_t e = fl::launch_active(B, S, D, h_prev, h_cur, dtype, rows_prev, n_prev, k, rows_out, score_out,
                                    (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, fn);

@@ -607,9 +607,7 @@ constexpr int kMassNW = 8;      // waves per block: 256 columns
 constexpr int kMassRing = 3;    // row images resident in LDS (54 KB)
 constexpr int kMassAhead = kMassRing - 1;
 
-size_t row_img_bytes(int B, int H, int n) {
-  return (size_t)B * H * ((n + kMassRows - 1) / kMassRows) * kRowBytes;
-}
+static_assert(kRowBytes == kRowImgBytes && kMassRows == 64, "row image size (launch.hpp)");
 
 // One block of 256 threads per row image: four threads per row, 32 dims each.
 __global__ __launch_bounds__(256) void k_build_rows(AttnArgs a, int ntr, uint8_t* __restrict__ out) {
@@ -703,7 +701,7 @@ __global__ __launch_bounds__(64 * NW) void k_mass_mfma(MassArgs m) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float v = (float)(int8_t)(ws[e >> 2] >> (8 * (e & 3))) * s;
-          kf[ks][e] = __builtin_bit_cast(__bf16, f32_to_bf16(v));
+          kf[ks][e] = __builtin_bit_cast(__bf16, f32_to_bf16(v));  // v_cvt_pk_bf16_f32
         }
       }
     } else {
@@ -817,10 +815,7 @@ __global__ __launch_bounds__(64 * NW) void k_mass_mfma(MassArgs m) {
 }
 
 // ------------------------------------------------------------- host side
-size_t gather_bytes(const CacheGeo& c, int K) {
-  const int nt = (K + kBN - 1) / kBN;
-  return (size_t)c.B * c.H * nt * kImgBytes;
-}
+static_assert(kImgBytes == kTileImgBytes && kBN == 64, "tile image size (launch.hpp)");
 
 // Tile images of K columns (sel NULL: positions 0..K-1) at loop rc.
 hipError_t launch_gather(const CacheGeo& c, int rc, const int32_t* sel, int K, uint8_t* out, hipStream_t st) {

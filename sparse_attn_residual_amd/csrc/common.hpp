@@ -73,11 +73,13 @@ __device__ __forceinline__ const uint8_t* res_rec(const CacheGeo& c, int r, int 
 
 // ---------------------------------------------------------------- numbers
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-// Round-to-nearest-even float -> bf16 bits (finite inputs).
+// float -> bf16 bits, round to nearest even: gfx950's conversion
+// instruction (v_cvt_pk_bf16_f32), which rounds in the default mode.
+typedef __bf16 fl_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float fl_f32x2_t __attribute__((ext_vector_type(2)));
 __device__ inline uint16_t f32_to_bf16(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const fl_bf16x2_t v = __builtin_convertvector(fl_f32x2_t{x, 0.0f}, fl_bf16x2_t);
+  return (uint16_t)__builtin_bit_cast(uint32_t, v);
 }
 __device__ inline float round_bf16(float x) { return bf16_to_f32(f32_to_bf16(x)); }
 

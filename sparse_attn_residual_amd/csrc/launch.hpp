@@ -52,10 +52,16 @@ hipError_t launch_attn(const AttnArgs& a, uint8_t* ws, hipStream_t st);
 // Cached mass and reused part for loop r: reads loop r-1 state, q_prev and
 // chains to r-1; rows A_r; columns sel (S_r).  ws as for launch_attn.
 hipError_t launch_um(const AttnArgs& a, uint8_t* ws, hipStream_t st);
+// Bytes of one 64-column tile image and of one 64-row query image of the
+// matrix-core kernels (attn_mfma.hip lays them out).
+constexpr int kTileImgBytes = 36 * 1024;
+constexpr int kRowImgBytes = 18 * 1024;
 // Bytes of the gathered tiles of K selected columns (head dim 128).
-size_t gather_bytes(const CacheGeo& c, int K);
+inline size_t gather_bytes(const CacheGeo& c, int K) {
+  return (size_t)c.B * c.H * (size_t)((K + 63) / 64) * kTileImgBytes;
+}
 // Bytes of the 64-row images of n rows per (b, h) that the mass pass streams.
-size_t row_img_bytes(int B, int H, int n);
+inline size_t row_img_bytes(int B, int H, int n) { return (size_t)B * H * (size_t)((n + 63) / 64) * kRowImgBytes; }
 // Column mass of the candidates cand (NULL: all S) over rows A_r with loop
 // r-1's probabilities.  ws (head dim 128, bf16): gather_bytes(c, K_prev)
 // bytes when the candidates are gathered (cand != NULL or r > 2), then
@@ -69,6 +75,15 @@ hipError_t launch_mass(const AttnArgs& a, const int32_t* cand, int K_prev, float
 hipError_t launch_active(int B, int S, int D, const void* h_prev, const void* h_cur, fl_dtype dt,
                          const int32_t* rows_prev, int n_prev, int k, int32_t* rows_out, float* score,
                          hipStream_t st);
+
+// ---- memory operations of the ABI layer (no kernels)
+// Synchronous copies to host memory after the stream has drained (the
+// FL_CHECK validator): bytes contiguous, or `rows` rows of `width` bytes.
+hipError_t copy_to_host(void* dst, const void* src, size_t bytes, hipStream_t st);
+hipError_t copy_rows_to_host(void* dst, size_t dst_pitch, const void* src, size_t src_pitch, size_t width,
+                             size_t rows, hipStream_t st);
+// Device-to-device copy on the stream.
+hipError_t copy_d2d_async(void* dst, const void* src, size_t bytes, hipStream_t st);
 
 // ---- decode
 struct DecodeArgs {

@@ -87,9 +87,10 @@ def run_prefill(cfg, rows, slices, *, mass_in=None, K_budget=None, mfma=None, mi
     return out
 
 
-def near_tie_ok(sel_gpu, sel_orc, mass_orc, cand, eps):
-    """Selections may differ only between candidates whose masses are within
-    eps * max mass of each other."""
+def near_tie_ok(sel_gpu, sel_orc, mass_orc, cand, gap_max):
+    """Selections may differ only between candidates whose oracle keys lie
+    within gap_max of each other (an absolute gap in the key's units: callers
+    pass a fraction of the K-th candidate's mass, or a logit difference)."""
     a, b = set(sel_gpu.tolist()), set(sel_orc.tolist())
     if a == b:
         return True, 0
@@ -97,7 +98,19 @@ def near_tie_ok(sel_gpu, sel_orc, mass_orc, cand, eps):
     only_g = [mass_orc[pos[j]] for j in a - b]
     only_o = [mass_orc[pos[j]] for j in b - a]
     gap = max(only_o) - min(only_g)
-    return gap <= eps * float(np.max(mass_orc)), len(a - b)
+    return gap <= gap_max, len(a - b)
+
+
+def kth_key(keys, K):
+    """The K-th largest key (the selection threshold)."""
+    keys = np.asarray(keys, np.float64)
+    K = min(K, keys.shape[0])
+    return float(np.partition(keys, keys.shape[0] - K)[keys.shape[0] - K])
+
+
+# Selections ranked by logits (decode): a logit gap g is a relative mass gap
+# of e^g - 1 ~ g, so near ties are bounded in logit units.
+LOGIT_TIE = 1e-4
 
 
 def build_decode_cache(cfg, rows, slices, L=None, fmt=0):
@@ -140,5 +153,50 @@ def run_decode(cfg, cache, queries, K_budget=None, T=None):
         snap = dict(O=st.O.cpu().numpy(), U=st.U.cpu().numpy(), M=st.M.cpu().numpy(), lse=st.lse.cpu().numpy(),
                     logits=st.logits[..., :K].cpu().numpy(), sel=st.sel[..., :K].cpu().numpy() if r > 1 else None)
         out.append(snap)
+        K_prev = K
+    return out
+
+
+def build_decode_cache_per_sequence(cfg, fmt=0):
+    """The decode cache of every sequence of cfg (L layers), quantized one
+    sequence at a time (bounded host memory) into layer 0, then copied to
+    every layer."""
+    import sparse_attn_residual_amd as fl
+    rows = {b: workloads.active_rows(cfg, b) for b in range(cfg.B)}
+    cache = fl.CacheBuffers(cfg.L, cfg.B, cfg.H, cfg.S, cfg.d, cfg.R, cfg.n, cfg.bits, rows_list(cfg, rows),
+                            Hkv=cfg.kv_heads, counts=counts_list(cfg), fmt=fmt)
+    dt = fl_dtype(cfg)
+    for b in range(cfg.B):
+        _, sl = workloads.gen_batch(cfg, batches=[b], with_q=False)
+        view = cache.seq_view(0, b)
+        for r in range(1, cfg.R + 1):
+            k = upload(workloads.stack_loop(cfg, sl, r, "k", batches=[b]), cfg)
+            v = upload(workloads.stack_loop(cfg, sl, r, "v", batches=[b]), cfg)
+            fl.fl_kv_resq(view, r, k, v, dt)
+            torch.cuda.synchronize()
+            del k, v
+        del sl
+    if cfg.L > 1:
+        cache.replicate_layer0()
+    return cache
+
+
+def run_decode_device(cfg, cache, queries, K_budget=None):
+    """run_decode with the per-loop snapshots kept on the device (clones)."""
+    import sparse_attn_residual_amd as fl
+    K_budget = cfg.K if K_budget is None else K_budget
+    T = cfg.S
+    L = queries[0].shape[0]
+    st = fl.DecodeState(L, cfg.B, cfg.H, cfg.S, cfg.d)
+    dt = fl_dtype(cfg)
+    out = []
+    K_prev = T
+    for r in range(1, cfg.R + 1):
+        q = upload(queries[r - 1], cfg)
+        K = T if r == 1 else min(K_budget, K_prev)
+        fl.fl_loop_decode(cache.fl, r, q, dt, K_prev, K, st.fl)
+        torch.cuda.synchronize()
+        out.append(dict(O=st.O.clone(), U=st.U.clone(), M=st.M.clone(), lse=st.lse.clone(),
+                        logits=st.logits[..., :K].clone(), sel=st.sel[..., :K].clone() if r > 1 else None))
         K_prev = K
     return out

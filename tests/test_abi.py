@@ -121,6 +121,14 @@ def test_validation_errors():
     st, msg = _status("fl_loop_attn", ctypes.byref(_cache()), 2, ok_ptr, fl.FL_F32, 10, None, ctypes.byref(s),
                       None, 0, None)
     assert st == EINVAL and "sel" in msg
+    # loop 1 (bf16, head dim 128) needs the tile images of every position
+    # whatever K_r holds: a negative K_r must not shrink the requirement
+    c1 = _cache(d=128)
+    assert fl.fl_workspace_bytes(fl.FL_WS_ATTN, c1, 1, -1, -1) == 1 * 2 * 1 * 36864
+    for kr in (-1, 0, 5):
+        st, msg = _status("fl_loop_attn", ctypes.byref(c1), 1, ok_ptr, fl.FL_BF16, kr, None, ctypes.byref(s),
+                          None, 0, None)
+        assert st == EINVAL and "workspace" in msg, (kr, msg)
     ds = fl.FlDState(ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr, ok_ptr)
     st, msg = _status("fl_loop_decode", ctypes.byref(_cache()), 1, ok_ptr, fl.FL_F32, 64, 64, ctypes.byref(ds),
                       None, 0, None)
@@ -162,3 +170,26 @@ def test_binding_raises():
     with pytest.raises(fl.FlashLoopError) as ei:
         fl.fl_kv_resq(_cache(d=96), 1, 0x40000, 0x40000, fl.FL_F32, stream=0)
     assert ei.value.status == 2
+
+
+def test_validation_layer_under_address_sanitizer(tmp_path):
+    """abi.cpp's argument checks and the FL_CHECK index validator, built with
+    AddressSanitizer against a host stand-in of the launch layer
+    (tests/abi_host): every refused call launches nothing and returns
+    FL_EINVAL with an FL_CHECK message; valid index data passes; no memory
+    error is reported.  CPU only: host arrays play the device buffers."""
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "abi_host")
+    csrc = os.path.join(ROOT, "sparse_attn_residual_amd", "csrc")
+    exe = tmp_path / "abi_harness"
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    cmd = [hipcc, "-x", "hip", "--offload-host-only", "-std=c++17", "-O1", "-g",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+           "-I", os.path.join(ROOT, "include"), "-I", csrc,
+           os.path.join(csrc, "abi.cpp"), os.path.join(here, "stub_launch.cpp"), os.path.join(here, "harness.cpp"),
+           "-o", str(exe)]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0")
+    env.pop("FL_CHECK", None)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "PASS" in res.stdout and "AddressSanitizer" not in res.stderr, res.stdout + res.stderr

@@ -44,7 +44,7 @@ def _check(cfg, D, r, ks, all_first=False, tol=1e-5):
             s_or = active.change_scores(hs[b][0][cand[b]], hs[b][1][cand[b]])
             assert np.allclose(score[b], s_or, rtol=tol, atol=0), (rr, b, np.max(np.abs(score[b] - s_or)))
             want = active.select_active(hs[b][0], hs[b][1], cand[b], k)
-            ok, nd = gh.near_tie_ok(sel[b], want, s_or, cand[b], tol)
+            ok, nd = gh.near_tie_ok(sel[b], want, s_or, cand[b], tol * gh.kth_key(s_or, k))
             assert ok, (rr, b, nd)
             assert np.all(np.diff(sel[b]) > 0) and np.isin(sel[b], cand[b]).all()
             nxt.append(sel[b])

@@ -102,7 +102,8 @@ def _paper_prefill_case(cfg, budgets, heads):
                     m = o["mass"][r]
                     K = budgets[r - 1] if isinstance(budgets, list) else cfg.K
                     own = prefill.topk(m, cand, min(K, len(cand)))
-                    ok, nd = gh.near_tie_ok(gpu["sel"][r][b, h], own, m, cand, 1e-5 if f32 else 2e-3)
+                    ok, nd = gh.near_tie_ok(gpu["sel"][r][b, h], own, m, cand,
+                                            (1e-5 if f32 else 2e-3) * gh.kth_key(m, K))
                     assert ok, (b, h, r + 1, nd)
                     cand = gpu["sel"][r][b, h]
                 g, st = gpu["state"][r], o["state"][r]
@@ -161,8 +162,7 @@ def _paper_decode_case(cfg):
                     if r >= 1:
                         key = orc[r - 1]["logits"]
                         own = prefill.topk(key, cand, min(cfg.K, len(cand)))
-                        ok, nd = gh.near_tie_ok(gpu[r]["sel"][l, b, h], own, key - key.min(), cand,
-                                                2e-3 if rel else 1e-5)
+                        ok, nd = gh.near_tie_ok(gpu[r]["sel"][l, b, h], own, key, cand, gh.LOGIT_TIE)
                         assert ok, (l, b, h, r + 1, nd)
                         cand = gpu[r]["sel"][l, b, h]
                     O, o = gpu[r]["O"][l, b, h], orc[r]["O"]

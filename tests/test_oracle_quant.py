@@ -166,3 +166,59 @@ def test_record_roundtrip(d, bits):
     if d == 128:
         assert records.base_record_bytes(d) == 272
         assert records.residual_record_bytes(d, bits) == {4: 160, 2: 96}[bits]
+
+
+def _bf16_probe_values():
+    """float32 inputs for the bf16 rounding pins: random bit patterns of
+    every exponent, exact halfway cases with even and odd kept bits, values
+    next to halfway, the overflow edge, subnormals, signed zeros, infinities."""
+    rng = np.random.default_rng(17)
+    u = rng.integers(0, 1 << 32, 200000, dtype=np.uint64).astype(np.uint32)
+    kept = rng.integers(0, 1 << 16, 20000, dtype=np.uint64).astype(np.uint32) << 16
+    ties = kept | np.uint32(0x8000)
+    below = kept | np.uint32(0x7FFF)
+    above = kept | np.uint32(0x8001)
+    edge = np.array([0x7F7F0000, 0x7F7F7FFF, 0x7F7F8000, 0x7F7F8001, 0x7F7FFFFF, 0xFF7F8000, 0xFF7F7FFF,
+                     0x7F7E8000, 0x00008000, 0x00018000, 0x00007FFF, 0x0000FFFF, 0x80008000, 0x80018000,
+                     0x00000000, 0x80000000, 0x7F800000, 0xFF800000, 0x3F808000, 0x3F818000, 0x3F80FFFF],
+                    dtype=np.uint32)
+    allu = np.concatenate([u, ties, below, above, edge])
+    f = allu.view(np.float32)
+    return f[~np.isnan(f)]
+
+
+def test_bf16_rne_matches_torch_cast():
+    """The oracle's bf16 rounding equals torch's CPU float32 -> bfloat16 cast
+    (round to nearest, ties to even), bit for bit, on every probe value."""
+    import torch
+    x = _bf16_probe_values()
+    got = quant.bf16_rne(x)
+    want = torch.from_numpy(x.copy()).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # NaN stays NaN (of either sign and any payload)
+    nan = np.array([0x7FC00000, 0x7F800001, 0xFFFFFFFF, 0x7FFFFFFF], dtype=np.uint32).view(np.float32)
+    assert np.all(np.isnan(quant.bf16_rne(nan)))
+
+
+def test_bf16_rne_is_nearest_even_bruteforce():
+    """Independent of any library: the result is one of the two bf16 values
+    around x (the truncation and its successor away from zero); it is the
+    nearer one in exact float64 distance, and on an exact tie the one whose
+    lowest kept bit is 0.  Past the largest finite bf16 value, x rounds to
+    infinity when it lies at or beyond the halfway point to 2^128."""
+    x = _bf16_probe_values()
+    x = x[np.isfinite(x)]
+    got = quant.bf16_rne(x).astype(np.float64)
+    u = x.view(np.uint32)
+    lo_u = u & np.uint32(0xFFFF0000)
+    hi_u = lo_u + np.uint32(0x10000)           # next bf16 away from zero (may be infinity)
+    lo = lo_u.view(np.float32).astype(np.float64)
+    hi = hi_u.view(np.float32).astype(np.float64)
+    xf = x.astype(np.float64)
+    # distance to the successor: 2^128 stands in for infinity's position
+    sign = np.sign(xf)
+    hi_pos = np.where(np.isinf(hi), sign * 2.0 ** 128, hi)
+    dlo, dhi = np.abs(xf - lo), np.abs(hi_pos - xf)
+    lo_even = ((lo_u >> 16) & 1) == 0
+    want = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo_even, lo, hi)))
+    assert np.array_equal(got, want)
