@@ -32,16 +32,24 @@
  * Conventions for every call:
  *   - All array arguments are device pointers to caller-owned memory.  Index
  *     arrays (rows, slot, cand, sel), masses, M and lse must be 4-byte
- *     aligned; every other array 16-byte aligned.  The library allocates
- *     nothing and keeps no pointer after a call.
+ *     aligned; every other array 16-byte aligned.  No call allocates memory
+ *     or keeps a pointer after it returns (fl_loop_attn_noalloc's scratch is
+ *     a device array the library itself holds).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream) and do not synchronize.  They are reentrant and thread safe.
  *   - Every argument is validated before anything is launched; on error the
  *     call returns a nonzero fl_status, launches nothing and writes nothing;
  *     fl_last_error() then describes the error (per thread).  No C++ exception
  *     crosses this boundary.
- *   - Device-data preconditions are documented, not checked: rows ascending
- *     and nested, finite inputs, |x| < 8e6 (the fp16 scale range).
+ *   - Device-data preconditions are documented, and checked only on request:
+ *     rows strictly ascending and nested, counts within their bounds, slots
+ *     the inverse of the rows, selections strictly ascending, finite inputs,
+ *     |x| < 8e6 (the fp16 scale range; bf16 prefill also |v~| < 65504, the
+ *     fp16 range its matrix cores take V in).  With the environment variable
+ *     FL_CHECK set (to anything but "" or "0"), every call first drains its
+ *     stream, copies the index arrays it reads to the host and checks them;
+ *     a violation returns FL_EINVAL before anything is launched.  This costs
+ *     a synchronization and the copies: a debugging aid.
  */
 #ifndef FLASHLOOP_H
 #define FLASHLOOP_H
@@ -93,7 +101,7 @@ typedef void* fl_stream;
  *   cnt[r]             NULL, or [B] int32 device array: |A_r| of each sequence
  *                      (ragged batches, a serving variant).  Each count must
  *                      lie in [1, n[r]] and in [cnt[r+1][b], cnt[r-1][b]]
- *                      (nested sets; not checked: device memory); rows past a
+ *                      (nested sets; checked under FL_CHECK); rows past a
  *                      sequence's count are neither read nor written.
  *                      fl_kv_append writes them.
  *   T                  tokens a decode step attends, positions [0, T) (0: S);
@@ -311,6 +319,24 @@ fl_status fl_colsel(const fl_cache* cache, int r, const void* q_prev, fl_dtype d
 fl_status fl_loop_attn(const fl_cache* cache, int r, const void* q, fl_dtype dtype, int K_r,
                        const int32_t* sel, const fl_state* state, void* ws, size_t ws_bytes,
                        fl_stream stream);
+
+/*
+ * fl_loop_attn_noalloc — fl_loop_attn for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments and results as fl_loop_attn without the
+ * workspace: the tile images go to a device array of FL_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on until the process ends (its
+ * address is looked up on the first call on each device).  The call
+ * allocates nothing.  A call that would need more scratch than the array
+ * holds returns FL_EUNSUPPORTED (fl_workspace_bytes(FL_WS_ATTN, ...) gives the
+ * need; at most 64 MiB: e.g. the sparse loops of a 32K, 16-head layer, or a
+ * dense loop 1 of B * H * ceil(S / 64) <= 1820 tiles).  All calls on one GPU
+ * share the array: calls that overlap on one GPU (concurrent streams or
+ * threads) race and must be serialized by the caller.
+ */
+#define FL_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+fl_status fl_loop_attn_noalloc(const fl_cache* cache, int r, const void* q, fl_dtype dtype, int K_r,
+                               const int32_t* sel, const fl_state* state, fl_stream stream);
 
 /*
  * fl_loop_decode — loop r of one decode step for every (layer, sequence,

@@ -80,6 +80,8 @@ def _load():
     lib.fl_colsel.restype = I
     lib.fl_loop_attn.argtypes = [cp, I, P, I, I, P, ctypes.POINTER(FlState), P, S, P]
     lib.fl_loop_attn.restype = I
+    lib.fl_loop_attn_noalloc.argtypes = [cp, I, P, I, I, P, ctypes.POINTER(FlState), P]
+    lib.fl_loop_attn_noalloc.restype = I
     lib.fl_loop_decode.argtypes = [cp, I, P, I, I, I, ctypes.POINTER(FlDState), P, S, P]
     lib.fl_loop_decode.restype = I
     lib.fl_select_active.argtypes = [I, I, I, P, P, I, I, P, I, P, P, P]
@@ -155,6 +157,11 @@ def fl_loop_attn(cache: FlCache, r: int, q, dtype: int, K_r: int, sel, state: Fl
                  stream=None) -> None:
     _check("fl_loop_attn", _lib.fl_loop_attn(ctypes.byref(cache), r, _ptr(q), dtype, K_r, _ptr(sel),
                                              ctypes.byref(state), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def fl_loop_attn_noalloc(cache: FlCache, r: int, q, dtype: int, K_r: int, sel, state: FlState, stream=None) -> None:
+    _check("fl_loop_attn_noalloc", _lib.fl_loop_attn_noalloc(ctypes.byref(cache), r, _ptr(q), dtype, K_r, _ptr(sel),
+                                                             ctypes.byref(state), _stream(stream)))
 
 
 def fl_loop_decode(cache: FlCache, r: int, q, dtype: int, K_prev: int, K_r: int, state: FlDState, ws=None,

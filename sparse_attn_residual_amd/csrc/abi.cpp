@@ -579,3 +579,16 @@ fl_status fl_select_active(int B, int S, int D, const void* h_prev, const void* 
 }
 
 }  // extern "C"
+
+namespace fl {
+
+// Hooks of the allocation-free entry point (noalloc.hip): the workspace
+// fl_loop_attn checks for, and the per-thread error message.
+size_t attn_workspace_need(const fl_cache* cache, int r, int K_r, fl_dtype dtype) {
+  if (!cache || dtype != FL_BF16) return 0;
+  return tiles_bytes(cache, r == 1 ? cache->S : K_r);
+}
+
+fl_status report(fl_status s, const char* msg) { return fail(s, "%s", msg); }
+
+}  // namespace fl

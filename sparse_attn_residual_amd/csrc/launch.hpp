@@ -85,6 +85,12 @@ hipError_t copy_rows_to_host(void* dst, size_t dst_pitch, const void* src, size_
 // Device-to-device copy on the stream.
 hipError_t copy_d2d_async(void* dst, const void* src, size_t bytes, hipStream_t st);
 
+// ---- the allocation-free entry point (abi.cpp)
+// Workspace bytes fl_loop_attn requires for these arguments (0 when none).
+size_t attn_workspace_need(const fl_cache* cache, int r, int K_r, fl_dtype dtype);
+// Sets the calling thread's error message; returns s.
+fl_status report(fl_status s, const char* msg);
+
 // ---- decode
 struct DecodeArgs {
   CacheGeo c;

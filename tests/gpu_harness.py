@@ -42,10 +42,11 @@ def counts_list(cfg):
     return [np.array([cfg.counts(b)[r] for b in range(cfg.B)], np.int32) for r in range(cfg.R)]
 
 
-def run_prefill(cfg, rows, slices, *, mass_in=None, K_budget=None, mfma=None, mixed=False, fmt=0):
+def run_prefill(cfg, rows, slices, *, mass_in=None, K_budget=None, mfma=None, mixed=False, fmt=0, noalloc=False):
     """All loops of one layer.  mass_in: optional {r: float32 [B][H][K_prev]}.
     K_budget: one budget for every loop, or a list (loop r uses K_budget[r-2]).
     mixed: the exact mixed-logit combine (the state carries lsel).
+    noalloc: the attention of every loop through fl_loop_attn_noalloc.
     Returns dict with per-loop snapshots (index r-1), sel, mass and the cache."""
     import sparse_attn_residual_amd as fl
     K_budget = cfg.K if K_budget is None else K_budget
@@ -76,9 +77,12 @@ def run_prefill(cfg, rows, slices, *, mass_in=None, K_budget=None, mfma=None, mi
             fl.fl_colsel(cache.fl, r, qs[r - 2], dt, st.fl, K_prev, sel_prev, K, mi, mass, sel, ws, nws)
             out["sel"].append(sel.cpu().numpy())
             out["mass"].append(mass.cpu().numpy())
-        nws = fl.fl_workspace_bytes(fl.FL_WS_ATTN, cache.fl, r, K, K)
-        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=DEV)
-        fl.fl_loop_attn(cache.fl, r, qs[r - 1], dt, K, sel, st.fl, ws, nws)
+        if noalloc:
+            fl.fl_loop_attn_noalloc(cache.fl, r, qs[r - 1], dt, K, sel, st.fl)
+        else:
+            nws = fl.fl_workspace_bytes(fl.FL_WS_ATTN, cache.fl, r, K, K)
+            ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=DEV)
+            fl.fl_loop_attn(cache.fl, r, qs[r - 1], dt, K, sel, st.fl, ws, nws)
         torch.cuda.synchronize()
         out["state"].append({k2: v2.cpu().numpy() for k2, v2 in st.snapshot().items()})
         if r >= 2:

@@ -193,3 +193,15 @@ def test_validation_layer_under_address_sanitizer(tmp_path):
     res = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)
     assert res.returncode == 0, res.stdout + res.stderr
     assert "PASS" in res.stdout and "AddressSanitizer" not in res.stderr, res.stdout + res.stderr
+
+
+def test_noalloc_refuses_oversized_call_on_host():
+    """fl_loop_attn_noalloc checks its scratch need before touching a device:
+    a 32K, 16-head dense loop 1 (302 MB of tile images) is refused with
+    FL_EUNSUPPORTED, naming the array's size."""
+    import sparse_attn_residual_amd as fl
+    c = _cache(d=128, H=16, S=32768, R=1)
+    c.n[1] = 32768
+    s = fl.FlState(0x40000, 0x40000, 0x40000, 0x40000)
+    st, msg = _status("fl_loop_attn_noalloc", ctypes.byref(c), 1, 0x40000, fl.FL_BF16, 0, None, ctypes.byref(s), None)
+    assert st == 2 and "FL_NOALLOC_SCRATCH_BYTES" in msg, msg
