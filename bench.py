@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 
 PREFILL_CFG = 2
 DECODE_CFG = 3
+OTHER_PREFILL_CFGS = (1, 4)
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "bench_prefill_s32768_decode_t32768_l48_hbm_traffic.md")
 
 
@@ -125,7 +126,7 @@ def measure_prefill(args, torch, fl, acc, cfg, rows, q, k, v, cache, st, budgets
     tm = Timer(torch)
 
     def step(timed):
-        w = tm.wrap if timed else (lambda key, fn: fn())
+        w = timed if callable(timed) else (tm.wrap if timed else (lambda key, fn: fn()))
         for r in range(1, R + 1):
             w(f"resq{r}", lambda r=r: fl.fl_kv_resq(cache.fl, r, k[r - 1], v[r - 1], dt))
             if r >= 2:
@@ -155,6 +156,7 @@ def measure_prefill(args, torch, fl, acc, cfg, rows, q, k, v, cache, st, budgets
     per = tm.mean_ms()
     log(f"prefill K={Ks[1:]}: {ms_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}); per call (ms): "
         + ", ".join(f"{kk}={vv:.3f}" for kk, vv in per.items()))
+    kern = kernel_times(fl, torch, step, args.steps)
 
     # algorithmic work from the index lists of the run
     sels = [None] + [s.cpu().numpy() for s in sel[1:]]
@@ -165,8 +167,42 @@ def measure_prefill(args, torch, fl, acc, cfg, rows, q, k, v, cache, st, budgets
     sparse_t = sum(per[f"attn{r}"] for r in range(2, R + 1)) * 1e-3
     sparse_tf = work["sparse_flops"] / sparse_t / 1e12
     total_tf = work["flops"] / (ms_step * 1e-3) / 1e12
+    # the attention kernels alone (the tile builds excluded), from the kernel timer
+    k_dense = attn_kernel_ms(kern, "attn1")
+    k_sparse = sum(attn_kernel_ms(kern, f"attn{r}") for r in range(2, R + 1))
     return dict(cfg=cfg, ms_step=ms_step, per=per, work=work, dense_tf=dense_tf, sparse_tf=sparse_tf,
-                total_tf=total_tf, Ks=Ks)
+                total_tf=total_tf, Ks=Ks, kern=kern, dense_kernel_ms=k_dense,
+                dense_kernel_tf=work["dense_flops"] / (k_dense * 1e-3) / 1e12,
+                sparse_kernel_ms=k_sparse, sparse_kernel_tf=work["sparse_flops"] / (k_sparse * 1e-3) / 1e12)
+
+
+def kernel_times(fl, torch, step, steps):
+    """Per-kernel durations of each library call of a step: the library's
+    kernel timer brackets every launch with HIP events on its stream.  Runs
+    `steps` extra steps (the timed region above ran without the timer) and
+    returns {call: [(kernel, mean ms), ...]} in launch order."""
+    rec = {}
+    fl.fl_timing_enable(True)
+    try:
+        for _ in range(steps):
+            def wrap(key, fn):
+                fn()
+                rec.setdefault(key, []).append(fl.fl_timing_collect())
+            step(wrap)
+    finally:
+        fl.fl_timing_enable(False)
+        fl.fl_timing_collect()
+    out = {}
+    for key, runs in rec.items():
+        n = min(len(r) for r in runs)
+        out[key] = [(runs[0][i][0], float(np.mean([r[i][1] for r in runs]))) for i in range(n)]
+    return out
+
+
+def attn_kernel_ms(kern, key):
+    """Time of the attention kernel of one fl_loop_attn call (its k_attn
+    launches, without the tile build)."""
+    return sum(t for name, t in kern.get(key, []) if name.startswith("k_attn_"))
 
 
 def decode_bench(args, torch, fl, workloads, acc, cfg=None, fmt=0):
@@ -196,7 +232,7 @@ def decode_bench(args, torch, fl, workloads, acc, cfg=None, fmt=0):
     tm = Timer(torch)
 
     def step(timed):
-        w = tm.wrap if timed else (lambda key, fn: fn())
+        w = timed if callable(timed) else (tm.wrap if timed else (lambda key, fn: fn()))
         for r in range(1, R + 1):
             w(f"decode{r}", lambda r=r: fl.fl_loop_decode(cache.fl, r, qs[r - 1], fl.FL_BF16,
                                                           Ks[r - 2] if r >= 2 else S, Ks[r - 1], st.fl))
@@ -215,6 +251,7 @@ def decode_bench(args, torch, fl, workloads, acc, cfg=None, fmt=0):
     ms_step = e0.elapsed_time(e1) / steps
     per = tm.mean_ms()
     log(f"decode: {ms_step:.3f} ms/step; per loop (ms): " + ", ".join(f"{kk}={vv:.3f}" for kk, vv in per.items()))
+    kern = kernel_times(fl, torch, step, 1)
 
     # algorithmic packed bytes of the step, from the selections of the run
     # (the dense loop reads every record of every KV head once)
@@ -231,7 +268,9 @@ def decode_bench(args, torch, fl, workloads, acc, cfg=None, fmt=0):
                                     for b in range(B))))
     total = sum(loop_bytes)
     logits_overhead = float(L * B * H * S * 4 * 2)
-    return dict(cfg=cfg, ms_step=ms_step, per=per, loop_bytes=loop_bytes, bytes=total,
+    dense_kms = sum(t for n, t in kern.get("decode1", []) if n.startswith("k_decode_dense")) or per["decode1"]
+    return dict(cfg=cfg, ms_step=ms_step, per=per, kern=kern, dense_kernel_ms=dense_kms,
+                dense_kernel_gbs=loop_bytes[0] / (dense_kms * 1e-3) / 1e9, loop_bytes=loop_bytes, bytes=total,
                 cache_stream1_bytes=float(cache.base.numel()),
                 gbs=total / (ms_step * 1e-3) / 1e9, dense_gbs=loop_bytes[0] / (per["decode1"] * 1e-3) / 1e9,
                 logits_overhead=logits_overhead, cache_bytes=cache.nbytes())
@@ -327,24 +366,32 @@ def measured_peaks(torch):
     return dict(bf16_gemm_tflops=gemm, hbm_read_gbs=best)
 
 
-def cpu_baseline(workloads):
-    """The oracle as it stands, on one head of the prefill workload."""
+def cpu_baseline(workloads, cfg_id=PREFILL_CFG):
+    """The oracle as it stands on every head of one layer of a prefill
+    workload, all loops, the heads spread over a pool of worker threads (one
+    BLAS thread each; numpy releases the interpreter lock in its kernels)."""
+    from concurrent.futures import ThreadPoolExecutor
     from oracle import prefill
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
-    cfg = workloads.CONFIGS[PREFILL_CFG]
-    rows, sl = workloads.gen_batch(cfg, heads=[0])
-    s = sl[(0, 0)]
-    t0 = time.perf_counter()
-    prefill.prefill_slice(s.rows, s.q, s.k, s.v, K_budget=cfg.K, bits=cfg.bits, dtype=cfg.dtype)
-    t = time.perf_counter() - t0
-    value = cfg.S / (t * cfg.H)   # one head is 1/H of a step
-    return dict(value=value, unit="tokens/s", cores=int(threads), kind="oracle",
-                sample=f"{cfg.name}: head 0 of {cfg.H}, all {cfg.R} loops in float64 ({t:.1f}s), "
-                       f"scaled to {cfg.H} heads", cpu_model=_cpu_model(), blas=_blas())
+    from threadpoolctl import threadpool_limits
+    cfg = workloads.CONFIGS[cfg_id]
+    heads = list(range(cfg.H))
+    workers = max(1, min(len(heads), len(os.sched_getaffinity(0)), 16))
+    rows, sl = workloads.gen_batch(cfg, heads=heads)
+
+    def one(h):
+        s = sl[(0, h)]
+        prefill.prefill_slice(s.rows, s.q, s.k, s.v, K_budget=cfg.K, bits=cfg.bits, dtype=cfg.dtype)
+
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(one, heads))
+        t = time.perf_counter() - t0
+    value = cfg.B * cfg.S / t
+    log(f"cpu oracle {cfg.name}: {t:.1f}s for all {cfg.H} heads on {workers} threads")
+    return dict(value=value, unit="tokens/s", cores=int(workers), kind="oracle",
+                sample=f"{cfg.name}: all {cfg.H} heads of one layer, all {cfg.R} loops in float64 ({t:.1f}s), "
+                       f"{workers} worker threads with one BLAS thread each", cpu_model=_cpu_model(), blas=_blas())
 
 
 def cpu_decode_baseline(workloads, step_bytes):
@@ -426,6 +473,9 @@ def main():
 
     peaks = measured_peaks(torch)
     pf = prefill_bench(args, torch, fl, workloads, acc)
+    # the other prefill workloads: 8K (Ouro-1.4B shaped) and the deep 16K, R = 8 one
+    others = {cid: prefill_bench(args, torch, fl, workloads, acc, cfg=workloads.CONFIGS[cid], pruned=False)
+              for cid in OTHER_PREFILL_CFGS}
     sel = select_bench(args, torch, fl, workloads, acc)
     dec = None if args.no_decode else decode_bench(args, torch, fl, workloads, acc)
     torch.cuda.empty_cache()
@@ -448,6 +498,7 @@ def main():
     if extra:
         rag_pf = prefill_bench(args, torch, fl, workloads, acc, cfg=rag_cfg, pruned=False)
     cpu = None if args.no_cpu else cpu_baseline(workloads)
+    cpu_others = {} if args.no_cpu else {cid: cpu_baseline(workloads, cid) for cid in OTHER_PREFILL_CFGS}
 
     cfg = pf["cfg"]
     tokens_s = cfg.B * cfg.S / (pf["ms_step"] * 1e-3)
@@ -473,6 +524,9 @@ def main():
             "mfma_frac_whole_step": pf["total_tf"] / acc.MI355X_BF16_TFLOPS,
             "sparse_attn_tflops": pf["sparse_tf"],
             "sparse_attn_mfma_frac": pf["sparse_tf"] / acc.MI355X_BF16_TFLOPS,
+            "sparse_attn_kernel_ms": pf["sparse_kernel_ms"],
+            "sparse_attn_kernel_mfma_frac": pf["sparse_kernel_tf"] / acc.MI355X_BF16_TFLOPS,
+            "kernel_ms": {k: [[n, round(t, 4)] for n, t in v] for k, v in pf["kern"].items()},
             "pruned_schedule": {
                 "K": pf["pruned"]["Ks"][1:],
                 "ms_per_step": pf["pruned"]["ms_step"],
@@ -481,19 +535,22 @@ def main():
             },
         },
         "roofline": {
-            "kernel": "k_attn_mfma (fl_loop_attn r=1, dense causal over the int8 base)",
+            "kernel": "k_attn_mfma<12, 0> (the attention kernel of fl_loop_attn r=1: dense causal over the int8 base)",
             "bound": "mfma",
-            "achieved": pf["dense_tf"],
+            "achieved": pf["dense_kernel_tf"],
             "peak": acc.MI355X_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": pf["dense_tf"] / acc.MI355X_BF16_TFLOPS,
+            "frac": pf["dense_kernel_tf"] / acc.MI355X_BF16_TFLOPS,
             "measured_peak": peaks["bf16_gemm_tflops"],
             "measured_peak_kind": "hipBLASLt bf16 GEMM 16384^3 via torch.matmul, same run",
-            "frac_of_measured": pf["dense_tf"] / peaks["bf16_gemm_tflops"],
+            "frac_of_measured": pf["dense_kernel_tf"] / peaks["bf16_gemm_tflops"],
             "traffic": measured_traffic("attn1"),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "flops_per_launch": dense_flops,
-            "avg_launch_ms": pf["per"]["attn1"],
+            "avg_launch_ms": pf["dense_kernel_ms"],
+            "timing": "HIP events around the kernel's launch on its stream (the library's kernel timer)",
+            "call_ms": pf["per"]["attn1"],
+            "call_frac": pf["dense_tf"] / acc.MI355X_BF16_TFLOPS,
         },
     }
     qb = [acc.resq_bytes(cfg.d, cfg.bits[:r], cfg.B * cfg.n[r - 1], cfg.kv_heads) for r in range(1, cfg.R + 1)]
@@ -534,17 +591,19 @@ def main():
             "unit": "GB/s",
             "per_loop_ms": {k: round(v, 4) for k, v in dec["per"].items()},
             "loop_bytes": dec["loop_bytes"],
+            "kernel_ms": {k: [[n, round(t, 4)] for n, t in v] for k, v in dec["kern"].items()},
             "logits_overhead_bytes": dec["logits_overhead"],
             "roofline": {
                 "kernel": "k_decode_dense (fl_loop_decode r=1)",
                 "bound": "hbm",
-                "achieved": dec["dense_gbs"],
+                "achieved": dec["dense_kernel_gbs"],
                 "peak": acc.MI355X_HBM_GBS,
                 "unit": "GB/s",
-                "frac": dec["dense_gbs"] / acc.MI355X_HBM_GBS,
+                "frac": dec["dense_kernel_gbs"] / acc.MI355X_HBM_GBS,
+                "avg_launch_ms": dec["dense_kernel_ms"],
                 "measured_peak": peaks["hbm_read_gbs"],
                 "measured_peak_kind": "torch elementwise y = x + 1 over 4 GiB fp32 (read + written), same run",
-                "frac_of_measured": dec["dense_gbs"] / peaks["hbm_read_gbs"],
+                "frac_of_measured": dec["dense_kernel_gbs"] / peaks["hbm_read_gbs"],
                 "traffic": measured_traffic("decode1"),
                 "algorithmic_bytes": dec["loop_bytes"][0],
                 "step_frac": dec["gbs"] / acc.MI355X_HBM_GBS,
@@ -552,6 +611,29 @@ def main():
         }
         if not args.no_cpu:
             out["decode"]["cpu_oracle"] = cpu_decode_baseline(workloads, dec["bytes"])
+    out["workloads"] = {}
+    for cid, o in others.items():
+        c = o["cfg"]
+        out["workloads"][c.name] = {
+            "workload": f"{c.name}: one layer, B={c.B}, H={c.H}, d={c.d}, S={c.S}, R={c.R}, active rows {c.n}, "
+                        f"K={o['Ks'][1]}, bits {list(c.bits)}",
+            "metric": "prefill tokens/s",
+            "value": c.B * c.S / (o["ms_step"] * 1e-3),
+            "unit": "tokens/s",
+            "ms_per_step": o["ms_step"],
+            "per_call_ms": {k: round(v, 4) for k, v in o["per"].items()},
+            "prefill_flops": o["work"]["flops"],
+            "mfma_frac_whole_step": o["total_tf"] / acc.MI355X_BF16_TFLOPS,
+            "roofline": {
+                "kernel": "k_attn_mfma (dense loop 1)", "bound": "mfma", "achieved": o["dense_kernel_tf"],
+                "peak": acc.MI355X_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": o["dense_kernel_tf"] / acc.MI355X_BF16_TFLOPS, "avg_launch_ms": o["dense_kernel_ms"],
+            },
+            "sparse_attn_kernel_ms": o["sparse_kernel_ms"],
+            "sparse_attn_kernel_mfma_frac": o["sparse_kernel_tf"] / acc.MI355X_BF16_TFLOPS,
+            "sparse_attn_mfma_frac": o["sparse_tf"] / acc.MI355X_BF16_TFLOPS,
+            "cpu_baseline": cpu_others.get(cid),
+        }
     if extra:
         _extras(out, cfg, gqa_pf, gqa_dec, pap_pf, pap_dec, rag_cfg, rag_pf)
     if cpu is not None:

@@ -44,8 +44,8 @@
  *   - Device-data preconditions are documented, and checked only on request:
  *     rows strictly ascending and nested, counts within their bounds, slots
  *     the inverse of the rows, selections strictly ascending, finite inputs,
- *     |x| < 8e6 (the fp16 scale range; bf16 prefill also |v~| < 65504, the
- *     fp16 range its matrix cores take V in).  With the environment variable
+ *     |x| < 8e6 and |x^(r) - x_hat^(r-1)| < 65504 (the ranges of the fp16
+ *     scales and zeros).  With the environment variable
  *     FL_CHECK set (to anything but "" or "0"), every call first drains its
  *     stream, copies the index arrays it reads to the host and checks them;
  *     a violation returns FL_EINVAL before anything is launched.  This costs
@@ -382,6 +382,22 @@ fl_status fl_loop_decode(const fl_cache* cache, int r, const void* q, fl_dtype d
  */
 fl_status fl_select_active(int B, int S, int D, const void* h_prev, const void* h_cur, fl_dtype dtype, int n_prev,
                            const int32_t* rows_prev, int k, int32_t* rows_out, float* score_out, fl_stream stream);
+
+/*
+ * Kernel timing, a measurement aid outside the method: while a thread has it
+ * enabled (on != 0), every kernel that thread's library calls launch is
+ * bracketed by two HIP events recorded on the kernel's stream.
+ * fl_timing_collect waits for the recorded launches, writes up to max
+ * (kernel name, milliseconds) pairs in launch order into names / ms, clears
+ * the thread's list (records beyond max are dropped) and returns how many it
+ * wrote.  Names are the launch expression's text, truncated to
+ * FL_TIMING_NAME - 1 characters.  Off by default; when on it costs two event
+ * records per launch, and the events are created on first use and reused
+ * (so it is not for callers that must not create runtime objects).
+ */
+#define FL_TIMING_NAME 48
+void fl_timing_enable(int on);
+int fl_timing_collect(char (*names)[FL_TIMING_NAME], float* ms, int max);
 
 #ifdef __cplusplus
 }

@@ -84,6 +84,10 @@ def _load():
     lib.fl_loop_attn_noalloc.restype = I
     lib.fl_loop_decode.argtypes = [cp, I, P, I, I, I, ctypes.POINTER(FlDState), P, S, P]
     lib.fl_loop_decode.restype = I
+    lib.fl_timing_enable.argtypes = [I]
+    lib.fl_timing_enable.restype = None
+    lib.fl_timing_collect.argtypes = [P, P, I]
+    lib.fl_timing_collect.restype = I
     lib.fl_select_active.argtypes = [I, I, I, P, P, I, I, P, I, P, P, P]
     lib.fl_select_active.restype = I
     return lib
@@ -175,3 +179,19 @@ def fl_select_active(B: int, S: int, D: int, h_prev, h_cur, dtype: int, n_prev: 
     _check("fl_select_active", _lib.fl_select_active(B, S, D, _ptr(h_prev), _ptr(h_cur), dtype, n_prev,
                                                      _ptr(rows_prev), k, _ptr(rows_out), _ptr(score_out),
                                                      _stream(stream)))
+
+
+FL_TIMING_NAME = 48
+
+
+def fl_timing_enable(on: bool) -> None:
+    _lib.fl_timing_enable(1 if on else 0)
+
+
+def fl_timing_collect(max_records: int = 4096) -> list:
+    """[(kernel name, ms), ...] of the launches recorded since the last
+    collect on this thread, in launch order."""
+    names = (ctypes.c_char * FL_TIMING_NAME * max_records)()
+    ms = (ctypes.c_float * max_records)()
+    n = _lib.fl_timing_collect(ctypes.addressof(names), ctypes.addressof(ms), max_records)
+    return [(names[i].value.decode(), float(ms[i])) for i in range(n)]

@@ -66,10 +66,10 @@ hipError_t launch_active(int B, int S, int D, const void* h_prev, const void* h_
   const long long waves = (long long)B * n_prev;
   const dim3 grid((unsigned)((waves + kActThreads / kWave - 1) / (kActThreads / kWave)));
   if (dt == FL_BF16)
-    hipLaunchKernelGGL(k_active_score<uint16_t>, grid, dim3(kActThreads), 0, st, (const uint16_t*)h_prev,
+    FL_LAUNCH(k_active_score<uint16_t>, grid, dim3(kActThreads), 0, st, (const uint16_t*)h_prev,
                        (const uint16_t*)h_cur, S, D, B, rows_prev, n_prev, score);
   else
-    hipLaunchKernelGGL(k_active_score<float>, grid, dim3(kActThreads), 0, st, (const float*)h_prev,
+    FL_LAUNCH(k_active_score<float>, grid, dim3(kActThreads), 0, st, (const float*)h_prev,
                        (const float*)h_cur, S, D, B, rows_prev, n_prev, score);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

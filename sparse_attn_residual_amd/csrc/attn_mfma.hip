@@ -56,11 +56,16 @@ constexpr float kRescaleP = 32768.0f;  // 2^kRescale
 //                        columns, the 8 a lane multiplies are stored
 //                        contiguously: see vt_col)
 //   pos [64]       int32 (position of each column, kNoPos for padding)
+//   vsh            int32: the tile's V^T holds v~ * 2^-vsh, vsh >= 0 the
+//                  smallest shift that brings the tile's largest |v~| below
+//                  2^15 (fp16's range ends at 65504; bf16 values reach 3.4e38)
 constexpr int kKP = kD + 8;
 constexpr int kVP = kBN + 8;
 constexpr int kImgV = kBN * kKP * 2;          // 17408
 constexpr int kImgPos = kImgV + kD * kVP * 2;  // 35840
-constexpr int kImgBytes = 36 * 1024;           // 36864: 36 chunks of 1 KB (36096 used)
+constexpr int kImgShift = kImgPos + kBN * 4;   // 36096
+constexpr int kImgBytes = 36 * 1024;           // 36864: 36 chunks of 1 KB (36100 used)
+static_assert(kImgShift + 4 <= kImgBytes, "tile image layout");
 constexpr int kImgChunks = kImgBytes / 1024;
 // Tile ring of the attention kernel: two images resident, the next one
 // copied while this one is used (72 KB of LDS).
@@ -77,9 +82,6 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
   const bf16x2_t v = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
   return __builtin_bit_cast(uint32_t, v);
 }
-// v~ = bf16(x), stored as fp16 (exact for every bf16 value above 2^-17 in
-// magnitude; smaller ones round to the fp16 subnormal grid).
-__device__ inline _Float16 bf16_as_f16(float x) { return (_Float16)round_bf16(x); }
 
 // ------------------------------------------------------------- tile images
 // One block of 256 threads per tile: columns sel[tile*64 .. +64) (sel NULL:
@@ -131,7 +133,10 @@ __global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const i
       dst[i] = make_uint4(pack_bf16x2(x[8 * i], x[8 * i + 1]), pack_bf16x2(x[8 * i + 2], x[8 * i + 3]),
                           pack_bf16x2(x[8 * i + 4], x[8 * i + 5]), pack_bf16x2(x[8 * i + 6], x[8 * i + 7]));
   }
-  // V^T rows (bf16 value in fp16)
+  // V^T rows: v~ = bf16(x) scaled by the tile's power-of-two shift, in fp16
+  // (exact for magnitudes above 2^-14 after the shift; smaller ones round to
+  // fp16's subnormal grid, at most 2^-25 off, and the shift only appears for
+  // tiles whose largest magnitude is at least 2^15)
   if (j >= 0) {
     if (c.fmt == kFmtPaper) {
       paper_chain16(c, rc, 0, b, hk, j, 1, g * 32, x);
@@ -143,13 +148,30 @@ __global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const i
 #pragma unroll
     for (int e = 0; e < 32; ++e) x[e] = 0.0f;
   }
+  // the tile's largest |v~| decides its shift (almost always 0)
+  __shared__ float wmax[4];
+  {
+    float mx = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      x[e] = round_bf16(x[e]);
+      mx = fmaxf(mx, fabsf(x[e]));
+    }
+    mx = wave_max(mx);
+    if ((t & 63) == 0) wmax[t >> 6] = mx;
+  }
+  __syncthreads();
+  const float tmax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  // 2^e <= tmax < 2^(e+1); the shift brings tmax below 2^15
+  const int vsh = tmax >= 32768.0f ? ((__float_as_int(tmax) >> 23) & 255) - 127 - 14 : 0;
   {
     _Float16* vt = (_Float16*)(img + kImgV);
     const int vc = vt_col(col);
 #pragma unroll
-    for (int e = 0; e < 32; ++e) vt[(g * 32 + e) * kVP + vc] = bf16_as_f16(x[e]);
+    for (int e = 0; e < 32; ++e) vt[(g * 32 + e) * kVP + vc] = (_Float16)__builtin_ldexpf(x[e], -vsh);
   }
   if (g == 0) ((int*)(img + kImgPos))[col] = j >= 0 ? j : kNoPos;
+  if (t == 0) *(int*)(img + kImgShift) = vsh;
   __syncthreads();
   uint4* dst = (uint4*)(out + ((long long)bh * ntiles + tile) * kImgBytes);
   const uint4* src = (const uint4*)img;
@@ -352,14 +374,15 @@ __device__ inline void pv_tile(const uint8_t* T, const f16x8_t* pf, int l32, int
 // M = 1 and lse; a sparse loop patches O = U + M * acc / l and lse (or
 // lse = -inf when no column was left); the cached-mass pass writes
 // U = O - M_prev * acc and M = M_prev * l.
+// The accumulators hold 2^-osh times the products (V shifts); osc = 2^osh.
 template <int MODE>
 __device__ inline void write_row(const AttnArgs& a, int r, long long bhS, int i, int hf, float mref, float lt,
-                                 const f32x16_t* o) {
+                                 const f32x16_t* o, float osc) {
   if (i < 0) return;
   const long long rowp = (bhS + i) * kD;
   if (MODE == kModeAttn) {
     if (r == 1) {
-      const float inv = 1.0f / lt;
+      const float inv = (1.0f / lt) * osc;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -379,7 +402,7 @@ __device__ inline void write_row(const AttnArgs& a, int r, long long bhS, int i,
       const float b2 = (mref + __log2f(lt)) * 0.6931471805599453f;
       float cu, ca;
       mixed_coeffs(a.M[bhS + i], b2, a.lsel[bhS + i], cu, ca);
-      const float sc = ca / lt;
+      const float sc = (ca / lt) * osc;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -402,7 +425,7 @@ __device__ inline void write_row(const AttnArgs& a, int r, long long bhS, int i,
       }
     } else if (lt > 0.0f) {
       const float Mi = a.M[bhS + i];
-      const float sc = Mi / lt;
+      const float sc = (Mi / lt) * osc;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -422,6 +445,7 @@ __device__ inline void write_row(const AttnArgs& a, int r, long long bhS, int i,
   } else {
     const float Mp = a.M[bhS + i];
     const float Mu = Mp > 0.0f ? Mp : 0.0f;
+    const float Mo = Mu * osc;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -430,7 +454,7 @@ __device__ inline void write_row(const AttnArgs& a, int r, long long bhS, int i,
         const f32x4_t ov = *(const f32x4_t*)&a.O[rowp + dcol];
         f32x4_t uv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) uv[e] = ov[e] - Mu * o[db][qq * 4 + e];
+        for (int e = 0; e < 4; ++e) uv[e] = ov[e] - Mo * o[db][qq * 4 + e];
         *(f32x4_t*)&a.U[rowp + dcol] = uv;
       }
     }
@@ -549,6 +573,11 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_mfma(MfmaArgs
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
+  // V shift of the accumulators: o holds 2^-osh times the products, osh the
+  // largest tile shift seen so far (wave-uniform; 0 unless some |v~| >= 2^15).
+  // A tile of smaller shift d below osh enters with its weights scaled by
+  // 2^-d (folded into the exponent); the row sum always adds the unscaled ones.
+  int osh = 0;
   for (int tt = 0; tt < nt; ++tt) {
     const uint8_t* T = lds + (tt % kRing) * kImgBytes;
     // tile tt+kAhead goes into the slot tile tt-1 left (all waves passed it)
@@ -558,20 +587,28 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_mfma(MfmaArgs
     qk_tile(T, qf, l32, hf, s0, s1);
     float x[32];
     softmax_mask(T, s0, s1, ipos, blk_min, hf, x);
+    const int tsh = __builtin_amdgcn_readfirstlane(*(const int*)(T + kImgShift));
+    if (tsh > osh) {
+      const float f = __builtin_ldexpf(1.0f, osh - tsh);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= f;
+      osh = tsh;
+    }
+    const int dsh = osh - tsh;
     // Weights against the current reference (UM: the fixed loop r-1
     // statistics).  ATTN: only if a lane's sum exceeds 2^kRescale (so some
     // weight might) or a valid row has no reference yet is the tile max
     // taken, the lazy rescale applied and the weights formed again.
     f16x8_t pf[4];
-    float ls = softmax_probs(x, (MODE == kModeAttn && mref == -INFINITY) ? 0.0f : mref, m.c2, pf);
+    float ls = softmax_probs(x, ((MODE == kModeAttn && mref == -INFINITY) ? 0.0f : mref) + (float)dsh, m.c2, pf);
     if (MODE == kModeAttn) {
       const bool bad = (ipos >= 0 && mref == -INFINITY) || !(ls <= kRescaleP);
       if (__builtin_amdgcn_ballot_w64(bad)) {
         softmax_rescale(x, m.c2, mref, lsum, o);
-        ls = softmax_probs(x, mref == -INFINITY ? 0.0f : mref, m.c2, pf);
+        ls = softmax_probs(x, (mref == -INFINITY ? 0.0f : mref) + (float)dsh, m.c2, pf);
       }
     }
-    lsum += ls;
+    lsum += dsh == 0 ? ls : __builtin_ldexpf(ls, dsh);
     pv_tile(T, pf, l32, hf, o);
     // tile tt+1 must be in LDS for every wave
     wait_tiles_but<NW>(min(tt + kAhead, nt - 1) - (tt + 1));
@@ -580,7 +617,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_mfma(MfmaArgs
 
   // ---- epilogue: each lane writes 64 of its row's 128 dims
   const float lt = lsum + __shfl_xor(lsum, 32, 64);
-  write_row<MODE>(a, r, bhS, ipos, hf, mref, lt, o);
+  write_row<MODE>(a, r, bhS, ipos, hf, mref, lt, o, __builtin_ldexpf(1.0f, osh));
 }
 
 // ------------------------------------------------------------- column mass
@@ -701,7 +738,7 @@ __global__ __launch_bounds__(64 * NW) void k_mass_mfma(MassArgs m) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float v = (float)(int8_t)(ws[e >> 2] >> (8 * (e & 3))) * s;
-          kf[ks][e] = __builtin_bit_cast(__bf16, f32_to_bf16(v));  // v_cvt_pk_bf16_f32
+          kf[ks][e] = __builtin_bit_cast(__bf16, f32_to_bf16(v));
         }
       }
     } else {
@@ -821,7 +858,7 @@ static_assert(kImgBytes == kTileImgBytes && kBN == 64, "tile image size (launch.
 hipError_t launch_gather(const CacheGeo& c, int rc, const int32_t* sel, int K, uint8_t* out, hipStream_t st) {
   const int nt = (K + kBN - 1) / kBN;
   const int nh = sel ? c.H : c.Hkv;
-  hipLaunchKernelGGL(k_build_tiles, dim3((unsigned)(c.B * nh * nt)), dim3(256), 0, st, c, rc, sel, K, nt, out);
+  FL_LAUNCH(k_build_tiles, dim3((unsigned)(c.B * nh * nt)), dim3(256), 0, st, c, rc, sel, K, nt, out);
   return hipGetLastError();
 }
 
@@ -833,7 +870,7 @@ static hipError_t launch_one(const MfmaArgs& m, hipStream_t st) {
       hipFuncSetAttribute((const void*)k_attn_mfma<NW, MODE>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
   const int nunits = m.a.c.B * m.a.c.H * m.nblk;
-  hipLaunchKernelGGL((k_attn_mfma<NW, MODE>), dim3(nunits), dim3(64 * NW), lds, st, m);
+  FL_LAUNCH((k_attn_mfma<NW, MODE>), dim3(nunits), dim3(64 * NW), lds, st, m);
   return hipGetLastError();
 }
 
@@ -891,7 +928,7 @@ static hipError_t launch_mass_one(const MassArgs& m, hipStream_t st) {
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
   const int nunits = m.a.c.B * m.a.c.H * m.ncb;
-  hipLaunchKernelGGL((k_mass_mfma<BASE, kMassNW>), dim3(nunits), dim3(64 * kMassNW), lds, st, m);
+  FL_LAUNCH((k_mass_mfma<BASE, kMassNW>), dim3(nunits), dim3(64 * kMassNW), lds, st, m);
   return hipGetLastError();
 }
 
@@ -917,7 +954,7 @@ hipError_t launch_mass_mfma(const AttnArgs& a, const int32_t* cand, int K_prev, 
   m.ntr = (a.c.n[a.r] + kMassRows - 1) / kMassRows;
   m.rows = rows;
   if (m.ntr > 0) {
-    hipLaunchKernelGGL(k_build_rows, dim3((unsigned)(a.c.B * a.c.H * m.ntr)), dim3(256), 0, st, a, m.ntr, rows);
+    FL_LAUNCH(k_build_rows, dim3((unsigned)(a.c.B * a.c.H * m.ntr)), dim3(256), 0, st, a, m.ntr, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

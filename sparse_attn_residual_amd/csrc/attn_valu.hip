@@ -224,11 +224,11 @@ static float softmax_scale(int d) { return (float)(1.0 / __builtin_sqrt((double)
   do {                                                                                          \
     const bool bf = a.dt == FL_BF16;                                                            \
     if (a.c.d == 64) {                                                                          \
-      if (bf) hipLaunchKernelGGL((KERNEL<uint16_t, 1>), GRID, dim3(256), 0, st, __VA_ARGS__);   \
-      else hipLaunchKernelGGL((KERNEL<float, 1>), GRID, dim3(256), 0, st, __VA_ARGS__);         \
+      if (bf) FL_LAUNCH((KERNEL<uint16_t, 1>), GRID, dim3(256), 0, st, __VA_ARGS__);   \
+      else FL_LAUNCH((KERNEL<float, 1>), GRID, dim3(256), 0, st, __VA_ARGS__);         \
     } else {                                                                                    \
-      if (bf) hipLaunchKernelGGL((KERNEL<uint16_t, 2>), GRID, dim3(256), 0, st, __VA_ARGS__);   \
-      else hipLaunchKernelGGL((KERNEL<float, 2>), GRID, dim3(256), 0, st, __VA_ARGS__);         \
+      if (bf) FL_LAUNCH((KERNEL<uint16_t, 2>), GRID, dim3(256), 0, st, __VA_ARGS__);   \
+      else FL_LAUNCH((KERNEL<float, 2>), GRID, dim3(256), 0, st, __VA_ARGS__);         \
     }                                                                                           \
   } while (0)
 

@@ -287,12 +287,12 @@ static void launch_dense(const DecodeArgs& a, float tau, hipStream_t st) {
   const int gq = a.c.G % 2 == 0 ? 2 : 1;
   const unsigned nblk = (unsigned)((long long)a.c.L * a.c.B * (a.c.H / gq));
   if (a.c.fmt == kFmtPaper)  // one query head per block: the reads are reconstructions, not raw records
-    hipLaunchKernelGGL((k_decode_dense<T, kDenseThreads, 1, true>), dim3((unsigned)((long long)a.c.L * a.c.B * a.c.H)),
+    FL_LAUNCH((k_decode_dense<T, kDenseThreads, 1, true>), dim3((unsigned)((long long)a.c.L * a.c.B * a.c.H)),
                        dim3(kDenseThreads), 0, st, a, tau);
   else if (gq == 2)
-    hipLaunchKernelGGL((k_decode_dense<T, kDenseThreads, 2, false>), dim3(nblk), dim3(kDenseThreads), 0, st, a, tau);
+    FL_LAUNCH((k_decode_dense<T, kDenseThreads, 2, false>), dim3(nblk), dim3(kDenseThreads), 0, st, a, tau);
   else
-    hipLaunchKernelGGL((k_decode_dense<T, kDenseThreads, 1, false>), dim3(nblk), dim3(kDenseThreads), 0, st, a, tau);
+    FL_LAUNCH((k_decode_dense<T, kDenseThreads, 1, false>), dim3(nblk), dim3(kDenseThreads), 0, st, a, tau);
 }
 
 constexpr int kMaxFastLoops = 5;  // loops whose slot lookups are batched
@@ -690,13 +690,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   }
   if (a.c.fmt == kFmtPaper) {  // tokens rebuilt one at a time: no batched residual loads
     switch (pruned * 2 + (bf ? 1 : 0)) {
-      case 0: hipLaunchKernelGGL((k_decode_sparse<float, false, 1, true>), dim3((unsigned)P), dim3(kDecThreads), 0,
+      case 0: FL_LAUNCH((k_decode_sparse<float, false, 1, true>), dim3((unsigned)P), dim3(kDecThreads), 0,
                                  st, a, tau); break;
-      case 1: hipLaunchKernelGGL((k_decode_sparse<uint16_t, false, 1, true>), dim3((unsigned)P), dim3(kDecThreads),
+      case 1: FL_LAUNCH((k_decode_sparse<uint16_t, false, 1, true>), dim3((unsigned)P), dim3(kDecThreads),
                                  0, st, a, tau); break;
-      case 2: hipLaunchKernelGGL((k_decode_sparse<float, true, 1, true>), dim3((unsigned)P), dim3(kDecThreads), 0,
+      case 2: FL_LAUNCH((k_decode_sparse<float, true, 1, true>), dim3((unsigned)P), dim3(kDecThreads), 0,
                                  st, a, tau); break;
-      default: hipLaunchKernelGGL((k_decode_sparse<uint16_t, true, 1, true>), dim3((unsigned)P), dim3(kDecThreads),
+      default: FL_LAUNCH((k_decode_sparse<uint16_t, true, 1, true>), dim3((unsigned)P), dim3(kDecThreads),
                                   0, st, a, tau); break;
     }
     return hipGetLastError();
@@ -705,7 +705,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   switch (nr * 4 + pruned * 2 + (bf ? 1 : 0)) {
 #define FL_DEC_CASE(NR, PR, BF, T)                                                                                 \
   case NR * 4 + PR * 2 + BF:                                                                                       \
-    hipLaunchKernelGGL((k_decode_sparse<T, PR, NR, false>), dim3((unsigned)P), dim3(kDecThreads), 0, st, a, tau); \
+    FL_LAUNCH((k_decode_sparse<T, PR, NR, false>), dim3((unsigned)P), dim3(kDecThreads), 0, st, a, tau); \
     break;
 #define FL_DEC_NR(NR)                 \
   FL_DEC_CASE(NR, 0, 0, float)        \

@@ -7,6 +7,21 @@
 
 namespace fl {
 
+// ---- opt-in kernel timing (fl_timing_enable): while the calling thread has
+// it on, a launch through FL_LAUNCH records an event on its stream before and
+// after the kernel and files the pair under the kernel's name.
+struct TimedLaunch {
+  TimedLaunch(const char* name, hipStream_t st);
+  ~TimedLaunch();
+  hipStream_t st;
+  int slot;
+};
+#define FL_LAUNCH(kernel, grid, block, lds, st, ...)                 \
+  do {                                                               \
+    fl::TimedLaunch fl_timed_(#kernel, st);                          \
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, __VA_ARGS__);   \
+  } while (0)
+
 // ---- fl_kv_resq
 hipError_t launch_quant_base(const CacheGeo& c, const void* k, const void* v, fl_dtype dt, uint8_t* base,
                              hipStream_t st);

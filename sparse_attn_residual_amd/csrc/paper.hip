@@ -216,19 +216,19 @@ hipError_t launch_paper_quant(const CacheGeo& c, int r, const void* k, const voi
     const unsigned nk = (unsigned)(lbh * ((m + kPGroup - 1) / kPGroup));
     const unsigned nv = (unsigned)((lbh * m * 2 + 255) / 256);
     if (bf) {
-      hipLaunchKernelGGL(k_pq_keys<uint16_t>, dim3(nk), dim3(256), 0, st, c, r, (const uint16_t*)k, out);
-      hipLaunchKernelGGL(k_pq_values<uint16_t>, dim3(nv), dim3(256), 0, st, c, r, (const uint16_t*)v, out);
+      FL_LAUNCH(k_pq_keys<uint16_t>, dim3(nk), dim3(256), 0, st, c, r, (const uint16_t*)k, out);
+      FL_LAUNCH(k_pq_values<uint16_t>, dim3(nv), dim3(256), 0, st, c, r, (const uint16_t*)v, out);
     } else {
-      hipLaunchKernelGGL(k_pq_keys<float>, dim3(nk), dim3(256), 0, st, c, r, (const float*)k, out);
-      hipLaunchKernelGGL(k_pq_values<float>, dim3(nv), dim3(256), 0, st, c, r, (const float*)v, out);
+      FL_LAUNCH(k_pq_keys<float>, dim3(nk), dim3(256), 0, st, c, r, (const float*)k, out);
+      FL_LAUNCH(k_pq_values<float>, dim3(nv), dim3(256), 0, st, c, r, (const float*)v, out);
     }
   }
   const unsigned nt = (unsigned)((lbh * kPTailN * 16 + 255) / 256);
   if (bf)
-    hipLaunchKernelGGL(k_pq_tail<uint16_t>, dim3(nt), dim3(256), 0, st, c, r, (const uint16_t*)k, (const uint16_t*)v,
+    FL_LAUNCH(k_pq_tail<uint16_t>, dim3(nt), dim3(256), 0, st, c, r, (const uint16_t*)k, (const uint16_t*)v,
                        out);
   else
-    hipLaunchKernelGGL(k_pq_tail<float>, dim3(nt), dim3(256), 0, st, c, r, (const float*)k, (const float*)v, out);
+    FL_LAUNCH(k_pq_tail<float>, dim3(nt), dim3(256), 0, st, c, r, (const float*)k, (const float*)v, out);
   return hipGetLastError();
 }
 

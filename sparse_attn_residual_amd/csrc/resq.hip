@@ -222,17 +222,17 @@ hipError_t launch_quant_base(const CacheGeo& c, const void* k, const void* v, fl
   long long threads = ntok * 2 * (c.d / kGroup);
   dim3 grid((unsigned)((threads + 255) / 256));
   if (dt == FL_BF16)
-    hipLaunchKernelGGL(k_quant_base<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)k, (const uint16_t*)v,
+    FL_LAUNCH(k_quant_base<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)k, (const uint16_t*)v,
                        base, ntok, c.d, c.base_rb);
   else
-    hipLaunchKernelGGL(k_quant_base<float>, grid, dim3(256), 0, st, (const float*)k, (const float*)v, base, ntok,
+    FL_LAUNCH(k_quant_base<float>, grid, dim3(256), 0, st, (const float*)k, (const float*)v, base, ntok,
                        c.d, c.base_rb);
   return hipGetLastError();
 }
 
 hipError_t launch_build_slot(const CacheGeo& c, int r, int32_t* slot, hipStream_t st) {
   long long n = (long long)c.B * c.S;
-  hipLaunchKernelGGL(k_build_slot, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, c.rows[r], c.n[r], c.cnt[r],
+  FL_LAUNCH(k_build_slot, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, c.rows[r], c.n[r], c.cnt[r],
                      c.S, c.B, slot);
   return hipGetLastError();
 }
@@ -244,22 +244,22 @@ hipError_t launch_append(const CacheGeo& c, int r, int pos, const void* k, const
   const bool bf = dt == FL_BF16;
   if (r == 1) {
     if (bf)
-      hipLaunchKernelGGL(k_append_base<uint16_t>, grid, dim3(256), 0, st, c, pos, (const uint16_t*)k,
+      FL_LAUNCH(k_append_base<uint16_t>, grid, dim3(256), 0, st, c, pos, (const uint16_t*)k,
                          (const uint16_t*)v, base);
     else
-      hipLaunchKernelGGL(k_append_base<float>, grid, dim3(256), 0, st, c, pos, (const float*)k, (const float*)v,
+      FL_LAUNCH(k_append_base<float>, grid, dim3(256), 0, st, c, pos, (const float*)k, (const float*)v,
                          base);
     return hipGetLastError();
   }
   if (bf)
-    hipLaunchKernelGGL(k_append_res<uint16_t>, grid, dim3(256), 0, st, c, r, pos, (const uint16_t*)k,
+    FL_LAUNCH(k_append_res<uint16_t>, grid, dim3(256), 0, st, c, r, pos, (const uint16_t*)k,
                        (const uint16_t*)v, res, rows, slot);
   else
-    hipLaunchKernelGGL(k_append_res<float>, grid, dim3(256), 0, st, c, r, pos, (const float*)k, (const float*)v, res,
+    FL_LAUNCH(k_append_res<float>, grid, dim3(256), 0, st, c, r, pos, (const float*)k, (const float*)v, res,
                        rows, slot);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_count_up, dim3((unsigned)((c.B + 255) / 256)), dim3(256), 0, st, cnt, c.n[r], c.B);
+  FL_LAUNCH(k_count_up, dim3((unsigned)((c.B + 255) / 256)), dim3(256), 0, st, cnt, c.n[r], c.B);
   return hipGetLastError();
 }
 
@@ -269,10 +269,10 @@ hipError_t launch_quant_res(const CacheGeo& c, int r, const void* k, const void*
   long long threads = rowsn * 2 * (c.d / kGroup);
   dim3 grid((unsigned)((threads + 255) / 256));
   if (dt == FL_BF16)
-    hipLaunchKernelGGL(k_quant_res<uint16_t>, grid, dim3(256), 0, st, c, r, (const uint16_t*)k, (const uint16_t*)v,
+    FL_LAUNCH(k_quant_res<uint16_t>, grid, dim3(256), 0, st, c, r, (const uint16_t*)k, (const uint16_t*)v,
                        res);
   else
-    hipLaunchKernelGGL(k_quant_res<float>, grid, dim3(256), 0, st, c, r, (const float*)k, (const float*)v, res);
+    FL_LAUNCH(k_quant_res<float>, grid, dim3(256), 0, st, c, r, (const float*)k, (const float*)v, res);
   return hipGetLastError();
 }
 

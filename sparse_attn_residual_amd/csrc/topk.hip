@@ -360,7 +360,7 @@ __global__ void k_copy_sel(const int32_t* __restrict__ cand, int P, int K, int32
 
 hipError_t launch_copy_sel(const int32_t* cand, int P, int K, int32_t* sel, hipStream_t st, long long sel_stride) {
   long long n = (long long)P * K;
-  hipLaunchKernelGGL(k_copy_sel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, cand, P, K, sel,
+  FL_LAUNCH(k_copy_sel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, cand, P, K, sel,
                      sel_stride > 0 ? sel_stride : K);
   return hipGetLastError();
 }
@@ -378,10 +378,10 @@ hipError_t launch_topk(const float* keys, long long key_stride, const int32_t* c
       static const hipError_t attr =                                                                            \
           hipFuncSetAttribute((const void*)k_topk<IT, true>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);  \
       if (attr != hipSuccess) return attr;                                                                      \
-      hipLaunchKernelGGL((k_topk<IT, true>), grid, block, lds, st, keys, key_stride, cand, cand_stride, n, K,   \
+      FL_LAUNCH((k_topk<IT, true>), grid, block, lds, st, keys, key_stride, cand, cand_stride, n, K,   \
                          sel_out, sel_stride, keys_out, keys_out_stride);                                       \
     } else {                                                                                                    \
-      hipLaunchKernelGGL((k_topk<IT, false>), grid, block, 0, st, keys, key_stride, cand, cand_stride, n, K,    \
+      FL_LAUNCH((k_topk<IT, false>), grid, block, 0, st, keys, key_stride, cand, cand_stride, n, K,    \
                          sel_out, sel_stride, keys_out, keys_out_stride);                                       \
     }                                                                                                           \
   } while (0)

@@ -508,3 +508,72 @@ def test_fl_check_validator(monkeypatch):
     attn4()
     torch.cuda.synchronize()
     assert torch.equal(st.O, torch.from_numpy(b["state"][3]["O"]).cuda())
+
+
+def test_prefill_bf16_values_beyond_fp16():
+    """Values whose bf16 reconstructions exceed fp16's range (|v~| up to
+    ~6e5, inside the int8 base's fp16-scale range) take the matrix-core
+    path's per-tile V shift.  Head 0 has every value's loop-1 part scaled by
+    2^17, head 1 only the positions below 300, so tiles with and without a
+    shift meet in one row; the loop-to-loop changes keep their size (a
+    residual's fp16 zero bounds them by 65504).  Outputs are finite and
+    within the bf16 bar of the oracle."""
+    import tests.gpu_harness as gh
+    cfg = workloads.custom(name="bf16-large-v", dtype="bf16", B=1, H=2, d=128, S=900, R=4, act=(1, 0.4, 0.2, 0.1),
+                           col="0.20", bits=(8, 4, 4, 2), lognormal=0.5, seed=29)
+    _say("prefill bf16 large values", cfg)
+    rows, slices = workloads.gen_batch(cfg)
+    big = np.float32(2.0 ** 17)
+    for (b, h), s in slices.items():
+        v1 = s.v[0].copy()
+        for r in range(cfg.R):
+            pos = s.rows[r]
+            sel = np.ones(pos.shape[0], bool) if h == 0 else pos < 300
+            # loop r's value plus (2^17 - 1) times its loop-1 value, rounded to bf16
+            s.v[r][sel] = workloads.cast(s.v[r][sel] + (big - 1) * v1[pos[sel]], "bf16")
+    assert max(np.max(np.abs(s.v[0])) for s in slices.values()) > 65504
+    gpu = gh.run_prefill(cfg, rows, slices)
+    heads = [0, 1]
+    orc = _oracle_slices(cfg, rows, slices, gpu, heads)
+    _check_records(cfg, gpu, orc, heads)
+    for r in range(cfg.R):
+        assert np.all(np.isfinite(gpu["state"][r]["O"])), r + 1
+    for h in heads:
+        cand = np.arange(cfg.S)
+        for r in range(1, cfg.R):
+            m = orc[(0, h)]["mass"][r]
+            own = prefill.topk(m, cand, min(cfg.K, len(cand)))
+            ok, nd = gh_near_tie(gpu["sel"][r][0, h], own, m, cand, 2e-3 * _kth_mass(m, cfg.K))
+            assert ok, (h, r + 1, nd)
+            cand = gpu["sel"][r][0, h]
+    _check_outputs(cfg, gpu, orc, heads, 2e-3, rel=True)
+
+
+def gh_near_tie(*a):
+    import tests.gpu_harness as gh
+    return gh.near_tie_ok(*a)
+
+
+def test_kernel_timer_records_launches():
+    """The library's kernel timer: with it on, every launch of a prefill
+    step is recorded (name and a positive duration) in launch order; off, no
+    record is kept."""
+    import sparse_attn_residual_amd as fl
+    import tests.gpu_harness as gh
+    cfg = workloads.custom(name="timer", dtype="bf16", B=1, H=2, d=128, S=640, R=2, act=(1, 0.3), col="0.10",
+                           bits=(8, 4), lognormal=0.5, seed=2)
+    rows, slices = workloads.gen_batch(cfg)
+    fl.fl_timing_collect()
+    fl.fl_timing_enable(True)
+    try:
+        gh.run_prefill(cfg, rows, slices)
+        recs = fl.fl_timing_collect()
+    finally:
+        fl.fl_timing_enable(False)
+    names = [n for n, _ in recs]
+    _say("kernel timer", names)
+    assert names[0].startswith("k_quant_base") and any(n.startswith("k_attn_mfma") for n in names), names
+    assert any(n.startswith("k_mass_mfma") for n in names) and any(n.startswith("k_topk") for n in names), names
+    assert all(t > 0 for _, t in recs), recs
+    gh.run_prefill(cfg, rows, slices)
+    assert fl.fl_timing_collect() == []
