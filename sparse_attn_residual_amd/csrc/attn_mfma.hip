@@ -69,8 +69,6 @@ static_assert(kImgShift + 4 <= kImgBytes, "tile image layout");
 constexpr int kImgChunks = kImgBytes / 1024;
 // Tile ring of the attention kernel: two images resident, the next one
 // copied while this one is used (72 KB of LDS).
-constexpr int kRing = 2;
-constexpr int kAhead = kRing - 1;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -99,6 +97,9 @@ __host__ __device__ constexpr int vt_col(int x) {
 static_assert(vt_col(0) == 0 && vt_col(4) == 8 && vt_col(8) == 4 && vt_col(12) == 12 && vt_col(21) == 25,
               "V^T column slots");
 
+// NR >= 0: the workload format with a chain of exactly NR residual loops
+// (rc = NR + 1), its loads batched (chain_group_n); NR < 0: any chain.
+template <int NR>
 __global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const int32_t* __restrict__ sel, int K,
                                                      int ntiles, uint8_t* __restrict__ out) {
   __shared__ __align__(16) uint8_t img[kImgBytes];
@@ -119,6 +120,8 @@ __global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const i
     if (c.fmt == kFmtPaper) {
       paper_chain16(c, rc, 0, b, hk, j, 0, g * 32, x);
       paper_chain16(c, rc, 0, b, hk, j, 0, g * 32 + 16, x + 16);
+    } else if (NR >= 0) {
+      chain_group_n<NR < 0 ? 0 : NR>(c, 0, b, hk, j, 0, g, x);
     } else {
       chain_group(c, rc, 0, b, hk, j, 0, g, x);
     }
@@ -141,6 +144,8 @@ __global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const i
     if (c.fmt == kFmtPaper) {
       paper_chain16(c, rc, 0, b, hk, j, 1, g * 32, x);
       paper_chain16(c, rc, 0, b, hk, j, 1, g * 32 + 16, x + 16);
+    } else if (NR >= 0) {
+      chain_group_n<NR < 0 ? 0 : NR>(c, 0, b, hk, j, 1, g, x);
     } else {
       chain_group(c, rc, 0, b, hk, j, 1, g, x);
     }
@@ -472,10 +477,14 @@ __device__ inline void write_row(const AttnArgs& a, int r, long long bhS, int i,
 // two blocks of four) let one wave's vector work run under another's matrix
 // work.  Tile images arrive by direct global->LDS loads issued one tile
 // ahead into a two-image ring, so the loop itself writes no LDS.
-template <int NW, int MODE>
-__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_mfma(MfmaArgs m) {
+// RING: tile images resident in LDS.  Two: the next tile is copied while this
+// one is used; one: the copy waits for the block's waves to finish the tile
+// (three blocks per CU then cover each other's copies).
+template <int NW, int MODE, int RING>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? (RING == 1 ? 3 : 2) : 1) void k_attn_mfma(MfmaArgs m) {
   constexpr int BM = 32 * NW;
-  extern __shared__ __align__(16) uint8_t lds[];   // kRing tile images
+  constexpr int AHEAD = RING - 1;
+  extern __shared__ __align__(16) uint8_t lds[];   // RING tile images
   __shared__ int sh_ntiles;
   const AttnArgs& a = m.a;
   const CacheGeo& c = a.c;
@@ -567,9 +576,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_mfma(MfmaArgs
   __syncthreads();
   const int nt = sh_ntiles;
 
-  // ---- prologue: the first kAhead tiles into the ring
+  // ---- prologue: the first max(AHEAD, 1) tiles into the ring
   const __amdgpu_buffer_rsrc_t rs = img_rsrc(imgs, m.ntiles_total * kImgBytes);
-  for (int k = 0; k < kAhead && k < nt; ++k) dma_tile<NW>(rs, k * kImgBytes, lds + k * kImgBytes);
+  for (int k = 0; k < (AHEAD > 0 ? AHEAD : 1) && k < nt; ++k) dma_tile<NW>(rs, k * kImgBytes, lds + k * kImgBytes);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -579,10 +588,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_mfma(MfmaArgs
   // 2^-d (folded into the exponent); the row sum always adds the unscaled ones.
   int osh = 0;
   for (int tt = 0; tt < nt; ++tt) {
-    const uint8_t* T = lds + (tt % kRing) * kImgBytes;
-    // tile tt+kAhead goes into the slot tile tt-1 left (all waves passed it)
-    if (tt + kAhead < nt)
-      dma_tile<NW>(rs, (tt + kAhead) * kImgBytes, lds + ((tt + kAhead) % kRing) * kImgBytes);
+    const uint8_t* T = lds + (tt % RING) * kImgBytes;
+    // tile tt+AHEAD goes into the slot tile tt-1 left (all waves passed it)
+    if (AHEAD > 0 && tt + AHEAD < nt)
+      dma_tile<NW>(rs, (tt + AHEAD) * kImgBytes, lds + ((tt + AHEAD) % RING) * kImgBytes);
     f32x16_t s0, s1;
     qk_tile(T, qf, l32, hf, s0, s1);
     float x[32];
@@ -610,8 +619,17 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_attn_mfma(MfmaArgs
     }
     lsum += dsh == 0 ? ls : __builtin_ldexpf(ls, dsh);
     pv_tile(T, pf, l32, hf, o);
-    // tile tt+1 must be in LDS for every wave
-    wait_tiles_but<NW>(min(tt + kAhead, nt - 1) - (tt + 1));
+    if (AHEAD == 0) {
+      // every wave is done with the slot: copy the next tile into it
+      if (tt + 1 < nt) {
+        lds_barrier();
+        dma_tile<NW>(rs, (tt + 1) * kImgBytes, lds);
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+    } else {
+      // tile tt+1 must be in LDS for every wave
+      wait_tiles_but<NW>(min(tt + AHEAD, nt - 1) - (tt + 1));
+    }
     lds_barrier();
   }
 
@@ -858,19 +876,30 @@ static_assert(kImgBytes == kTileImgBytes && kBN == 64, "tile image size (launch.
 hipError_t launch_gather(const CacheGeo& c, int rc, const int32_t* sel, int K, uint8_t* out, hipStream_t st) {
   const int nt = (K + kBN - 1) / kBN;
   const int nh = sel ? c.H : c.Hkv;
-  FL_LAUNCH(k_build_tiles, dim3((unsigned)(c.B * nh * nt)), dim3(256), 0, st, c, rc, sel, K, nt, out);
+  const dim3 grid((unsigned)(c.B * nh * nt));
+  switch (c.fmt == kFmtPaper ? -1 : rc - 1) {
+    case 0: FL_LAUNCH(k_build_tiles<0>, grid, dim3(256), 0, st, c, rc, sel, K, nt, out); break;
+    case 1: FL_LAUNCH(k_build_tiles<1>, grid, dim3(256), 0, st, c, rc, sel, K, nt, out); break;
+    case 2: FL_LAUNCH(k_build_tiles<2>, grid, dim3(256), 0, st, c, rc, sel, K, nt, out); break;
+    case 3: FL_LAUNCH(k_build_tiles<3>, grid, dim3(256), 0, st, c, rc, sel, K, nt, out); break;
+    case 4: FL_LAUNCH(k_build_tiles<4>, grid, dim3(256), 0, st, c, rc, sel, K, nt, out); break;
+    case 5: FL_LAUNCH(k_build_tiles<5>, grid, dim3(256), 0, st, c, rc, sel, K, nt, out); break;
+    case 6: FL_LAUNCH(k_build_tiles<6>, grid, dim3(256), 0, st, c, rc, sel, K, nt, out); break;
+    case 7: FL_LAUNCH(k_build_tiles<7>, grid, dim3(256), 0, st, c, rc, sel, K, nt, out); break;
+    default: FL_LAUNCH(k_build_tiles<-1>, grid, dim3(256), 0, st, c, rc, sel, K, nt, out); break;
+  }
   return hipGetLastError();
 }
 
-template <int NW, int MODE>
+template <int NW, int MODE, int RING>
 static hipError_t launch_one(const MfmaArgs& m, hipStream_t st) {
-  constexpr size_t lds = (size_t)kRing * kImgBytes;
+  constexpr size_t lds = (size_t)RING * kImgBytes;
   // once per kernel and process (static initialisation is thread-safe)
   static const hipError_t attr =
-      hipFuncSetAttribute((const void*)k_attn_mfma<NW, MODE>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      hipFuncSetAttribute((const void*)k_attn_mfma<NW, MODE, RING>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
   const int nunits = m.a.c.B * m.a.c.H * m.nblk;
-  FL_LAUNCH((k_attn_mfma<NW, MODE>), dim3(nunits), dim3(64 * NW), lds, st, m);
+  FL_LAUNCH((k_attn_mfma<NW, MODE, RING>), dim3(nunits), dim3(64 * NW), lds, st, m);
   return hipGetLastError();
 }
 
@@ -880,15 +909,19 @@ static float c2_of(int d) { return (float)(1.4426950408889634 / __builtin_sqrt((
 
 // 384-row blocks of twelve waves (three per SIMD, one block per CU) when
 // 256-row blocks would fill the chip four times over; otherwise 128-row
-// blocks of four waves, two blocks per CU.
+// blocks of four waves: a dense loop 1 with a two-image ring (two blocks per
+// CU), the sparse loops and the cached-mass pass with one image (three
+// blocks per CU: measured faster there, slower for the dense loop; six-wave
+// blocks, two per CU, were slower everywhere).
 template <int MODE>
 static hipError_t launch_rows(MfmaArgs& m, int n, hipStream_t st) {
   if ((long long)m.a.c.B * m.a.c.H * ((n + 255) / 256) >= kWideBlocks) {
     m.nblk = (n + 383) / 384;
-    return launch_one<12, MODE>(m, st);
+    return launch_one<12, MODE, 2>(m, st);
   }
   m.nblk = (n + 127) / 128;
-  return launch_one<4, MODE>(m, st);
+  if (MODE == kModeAttn && m.a.r == 1) return launch_one<4, MODE, 2>(m, st);
+  return launch_one<4, MODE, 1>(m, st);
 }
 
 // Loop-r attention: r == 1 dense over every position, r >= 2 over S_r.

@@ -182,6 +182,63 @@ __device__ __forceinline__ void chain_group(const CacheGeo& c, int r, int l, int
   }
 }
 
+// chain_group for a chain of exactly NR residual loops (r = NR + 1): every
+// slot lookup is issued first, then every record of a loop where j is
+// active, so the loads of one token are two round trips rather than two per
+// loop.  The sets nest, so "active at loop rr" (slot >= 0) holds for a
+// prefix of the loops, and the sum runs over the same terms in the same
+// order as chain_group's: the values are the same.
+template <int NR>
+__device__ __forceinline__ void chain_group_n(const CacheGeo& c, int l, int b, int hk, int j, int kv, int g, float* x) {
+  const int d = c.d, G = d / kGroup;
+  int t[NR > 0 ? NR : 1];
+#pragma unroll
+  for (int k = 0; k < NR; ++k) t[k] = c.slot[k + 2][(long long)b * c.S + j];
+  const uint8_t* rec = base_rec(c, l, b, hk, j);
+  const uint4 w0 = *(const uint4*)(rec + kv * d + g * kGroup);
+  const uint4 w1 = *(const uint4*)(rec + kv * d + g * kGroup + 16);
+  const float s = h2f(((const uint16_t*)(rec + 2 * d))[kv * G + g]);
+  uint4 cw[NR > 0 ? NR : 1];
+  uint32_t sz[NR > 0 ? NR : 1];  // scale | zero << 16
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    cw[k] = make_uint4(0, 0, 0, 0);
+    sz[k] = 0;
+    if (t[k] >= 0) {
+      const uint8_t* q = res_rec(c, k + 2, l, b, hk, t[k]);
+      const int C = d * c.bits[k + 2] / 8;
+      const uint16_t* meta = (const uint16_t*)(q + 2 * C);
+      if (c.bits[k + 2] == 4) {
+        cw[k] = *(const uint4*)(q + kv * C + g * 16);
+      } else {
+        const uint2 pw = *(const uint2*)(q + kv * C + g * 8);
+        cw[k].x = pw.x;
+        cw[k].y = pw.y;
+      }
+      sz[k] = (uint32_t)meta[(2 * kv) * G + g] | ((uint32_t)meta[(2 * kv + 1) * G + g] << 16);
+    }
+  }
+  const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+  for (int e = 0; e < kGroup; ++e) x[e] = (float)(int8_t)(w[e >> 2] >> (8 * (e & 3))) * s;
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    if (t[k] < 0) break;
+    const float rs = h2f((uint16_t)sz[k]), rz = h2f((uint16_t)(sz[k] >> 16));
+    if (c.bits[k + 2] == 4) {
+      const uint32_t ws[4] = {cw[k].x, cw[k].y, cw[k].z, cw[k].w};
+#pragma unroll
+      for (int e = 0; e < kGroup; ++e)
+        x[e] = x[e] + __builtin_fmaf((float)((ws[e >> 3] >> (4 * (e & 7))) & 15), rs, rz);
+    } else {
+      const uint32_t ws[2] = {cw[k].x, cw[k].y};
+#pragma unroll
+      for (int e = 0; e < kGroup; ++e)
+        x[e] = x[e] + __builtin_fmaf((float)((ws[e >> 4] >> (2 * (e & 15))) & 3), rs, rz);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- the paper's format
 // (FL_FMT_PAPER, head dim 128).  Every (layer, sequence, KV head) owns one
 // stream per loop: m entries (loop 1: the positions [0, Sq); loop r: the
