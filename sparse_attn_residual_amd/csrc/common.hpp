@@ -83,6 +83,19 @@ __device__ inline uint16_t f32_to_bf16(float x) {
 }
 __device__ inline float round_bf16(float x) { return bf16_to_f32(f32_to_bf16(x)); }
 
+// Order-preserving uint32 key of a float (larger float, larger key; -0 ranks
+// as +0; no float maps to 0).
+__device__ inline uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// Histogram of a decode head's loop-1 logits by the top kHistBits bits of
+// their order keys: loop 1 leaves it in the first kHistBins entries of the
+// head's selection row, loop 2's selection starts from it.
+constexpr int kHistBits = 11;
+constexpr int kHistBins = 1 << kHistBits;
+
 __device__ inline float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 __device__ inline uint16_t f2h_rn(float x) { return __half_as_ushort(__float2half_rn(x)); }
 

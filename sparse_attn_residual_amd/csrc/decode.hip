@@ -81,6 +81,7 @@ __global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
   constexpr int NG = NT / 8, NW = NT / kWave;
   static_assert(GQ * 128 <= NT, "one thread per output dim of every head");
   __shared__ float wm[GQ][NW], wl[GQ][NW], wacc[GQ][NW][128];
+  __shared__ uint32_t hist[GQ][kHistBins];  // each head's logits by key (loop 2's selection)
   const CacheGeo& c = a.c;
   const int HB = c.H / GQ;                 // query-head groups per sequence
   const long long blk = blockIdx.x;        // over [L][B][HB]
@@ -96,6 +97,8 @@ __global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
   const int grp = lane >> 3;       // token within the wave's step
   const int gid = wv * 8 + grp;    // group id in the block
   const int g = sub >> 1;          // quantization group of the slice
+  for (int i = threadIdx.x; i < GQ * kHistBins; i += NT) (&hist[0][0])[i] = 0u;
+  __syncthreads();
   float q[GQ][16], m[GQ], lsum[GQ], acc[GQ][16];
 #pragma unroll
   for (int u = 0; u < GQ; ++u) {
@@ -159,7 +162,10 @@ __global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) part = __builtin_fmaf(qs[u][e], (float)((kws[e >> 3] >> (4 * (e & 7))) & 15), part);
           const float sc = tau * group8_sum_dpp(part);
-          if (sub == 0) logit[(long long)u * c.S + j] = sc;
+          if (sub == 0) {
+            logit[(long long)u * c.S + j] = sc;
+            atomicAdd(&hist[u][order_key(sc) >> (32 - kHistBits)], 1u);
+          }
           if (sc > m[u] + kDecRescale) {
             const float alpha = __expf(m[u] - sc);
             lsum[u] *= alpha;
@@ -193,7 +199,10 @@ __global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) part = __builtin_fmaf(q[u][e], kx[e], part);
         const float sc = tau * group8_sum_dpp(part);
-        if (sub == 0) logit[(long long)u * c.S + j] = sc;
+        if (sub == 0) {
+          logit[(long long)u * c.S + j] = sc;
+          atomicAdd(&hist[u][order_key(sc) >> (32 - kHistBits)], 1u);
+        }
         if (sc > m[u] + kDecRescale) {
           const float alpha = __expf(m[u] - sc);
           lsum[u] *= alpha;
@@ -224,7 +233,10 @@ __global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) part = __builtin_fmaf(q[u][e], cv[e], part);
       const float s = tau * group8_sum_dpp(part * ks);
-      if (sub == 0) logit[(long long)u * c.S + j] = s;
+      if (sub == 0) {
+        logit[(long long)u * c.S + j] = s;
+        atomicAdd(&hist[u][order_key(s) >> (32 - kHistBits)], 1u);
+      }
       if (s > m[u] + kDecRescale) {
         const float alpha = __expf(m[u] - s);  // 0 on the group's first token
         lsum[u] *= alpha;
@@ -274,6 +286,14 @@ __global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
     if (t == 0) {
       a.lse[lbh] = mx + __logf(L);
       a.M[lbh] = 1.0f;
+    }
+  }
+  // the histograms go to the front of each head's selection row (which loop
+  // 1 does not otherwise use) when the row holds them
+  if (c.S >= kHistBins) {
+    for (int i = threadIdx.x; i < GQ * kHistBins; i += NT) {
+      const int u = i / kHistBins, bin = i - u * kHistBins;
+      a.sel[(lbh0 + u) * c.S + bin] = (int32_t)hist[u][bin];
     }
   }
 }
@@ -680,7 +700,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   hipError_t e;
   if (pruned) {
     const int32_t* cand = (a.r == 2 && a.K_prev == a.c.T) ? nullptr : a.sel;
-    e = launch_topk(a.logits, a.c.S, cand, a.c.S, (int)P, a.K_prev, a.K, a.sel, a.c.S, a.logits, a.c.S, st);
+    // loop 1 left each head's logit histogram at the front of its selection row
+    const bool given = !cand && a.c.S >= kHistBins;
+    e = launch_topk(a.logits, a.c.S, cand, a.c.S, (int)P, a.K_prev, a.K, a.sel, a.c.S, a.logits, a.c.S, st, given);
     if (e != hipSuccess) return e;
   } else if (a.r == 2) {
     // every position stays selected: sel = 0..T-1 (rows of stride S); the

@@ -41,9 +41,12 @@ hipError_t launch_quant_res(const CacheGeo& c, int r, const void* k, const void*
 // writes sel_out [P][sel_stride] ascending and, if keys_out is set, the keys
 // of the selected entries in the same order.  In place (keys_out == keys,
 // sel_out == cand) is allowed: every block reads its inputs before writing.
+// given_hist: sel_out's rows hold, in their first 2048 entries, each
+// problem's histogram of keys by the top 11 bits of their order keys (cand
+// NULL, n <= 32768, sel_stride >= 2048); the search starts from it.
 hipError_t launch_topk(const float* keys, long long key_stride, const int32_t* cand, long long cand_stride,
                        int P, int n, int K, int32_t* sel_out, long long sel_stride, float* keys_out,
-                       long long keys_out_stride, hipStream_t st);
+                       long long keys_out_stride, hipStream_t st, bool given_hist = false);
 // sel[p][t] = cand ? cand[p][t] : t for t < K
 hipError_t launch_copy_sel(const int32_t* cand, int P, int K, int32_t* sel, hipStream_t st, long long sel_stride = 0);
 

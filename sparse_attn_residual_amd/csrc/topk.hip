@@ -18,11 +18,6 @@ namespace fl {
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 
-__device__ inline uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;  // -0 ranks as +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 __device__ inline float key_value(uint32_t u) {
   uint32_t b = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
   return __uint_as_float(b);
@@ -204,11 +199,16 @@ __device__ inline int level_bin(uint32_t u, uint32_t lo, bool by_value, float fl
 // a range of one value is T itself.  The output stage takes every key above
 // T and the first keys equal to T in candidate order, ranked with wave
 // ballots: ascending, unique.  Keys must not be NaN.
-template <int ITEMS, bool CAND>
+// HIST: the first level is given, not computed: the first kBins entries of
+// each problem's output row hold the histogram of its keys by the top 11
+// bits of their order keys (every key counted once; loop 1 of a decode step
+// leaves it there), so the range search starts at that level.
+template <int ITEMS, bool CAND, bool HIST>
 __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__ keys, long long key_stride,
                                                        const int32_t* cand, long long cand_stride, int n, int K,
                                                        int32_t* sel_out, long long sel_stride, float* keys_out,
                                                        long long keys_out_stride) {
+  static_assert(kBins == kHistBins, "the given histogram is the first level");
   static_assert(ITEMS <= 32, "at most 32768 keys per problem");
   __shared__ TopkShared sh;
   const int p = blockIdx.x;
@@ -238,14 +238,24 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
   }
   __syncthreads();  // every read of keys/cand precedes any write (in-place use)
 
-  // ---- range of the keys
+  // ---- range of the keys (HIST: every key; the bins of the full range are
+  // the top 11 bits, which is what the given histogram counts)
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  uint32_t given = 0;  // this thread's two bins of the given histogram
+  if (HIST) {
+    lo = 0u;
+    hi = 0xFFFFFFFFu;
+    const int32_t* hrow = sel_out + (long long)p * sel_stride;
+    given = (uint32_t)hrow[tid] | ((uint32_t)hrow[tid + kTopkThreads] << 16);  // counts < 2^16: n <= 32768
+  } else {
 #pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    lo = min(lo, u[i] ? u[i] : 0xFFFFFFFFu);
-    hi = max(hi, u[i]);
+    for (int i = 0; i < ITEMS; ++i) {
+      lo = min(lo, u[i] ? u[i] : 0xFFFFFFFFu);
+      hi = max(hi, u[i]);
+    }
+    block_minmax(lo, hi, sh);
   }
-  block_minmax(lo, hi, sh);
+  __syncthreads();  // (HIST) the histogram is read before any output is written
 
   uint32_t T = lo;
   int rem = K;       // rank sought among the keys in [lo, hi]
@@ -254,18 +264,28 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
       T = lo;
       break;
     }
+    const bool given_level = HIST && level == 0;
     const float flo = key_value(lo), fhi = key_value(hi);
     const float fscale = (float)kBins / (fhi - flo);
-    const bool by_value = level == 0 && fscale < INFINITY && fscale > 0.0f;
+    const bool by_value = !given_level && level == 0 && fscale < INFINITY && fscale > 0.0f;
+    // (HIST, level 0: hi - lo = 2^32 - 1, so the shift is 21: the top 11 bits)
     const int shift = max(0, 32 - __clz((int)(hi - lo)) - 11);
-    for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
     if (tid == 0) sh.ncand = 0;
-    __syncthreads();
-    const uint32_t span = hi - lo;  // keys in range: u - lo <= span (lo >= 1 excludes u = 0)
+    // keys in range: u - lo <= span (lo >= 1 excludes u = 0; with the given
+    // level, lo = 0 and the items past n, u = 0, are excluded by hand)
+    const uint32_t span = hi - lo;
+    if (given_level) {
+      sh.hist[tid] = given & 0xFFFFu;
+      sh.hist[tid + kTopkThreads] = given >> 16;
+      __syncthreads();
+    } else {
+      for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
+      __syncthreads();
 #pragma unroll
-    for (int i = 0; i < ITEMS; ++i)
-      if (u[i] - lo <= span) atomicAdd(&sh.hist[level_bin(u[i], lo, by_value, flo, fscale, shift)], 1u);
-    __syncthreads();
+      for (int i = 0; i < ITEMS; ++i)
+        if (u[i] - lo <= span) atomicAdd(&sh.hist[level_bin(u[i], lo, by_value, flo, fscale, shift)], 1u);
+      __syncthreads();
+    }
     // bins from the top: thread t covers bins kBins-1-2t and kBins-2-2t
     const int b0 = kBins - 1 - 2 * tid, b1 = b0 - 1;
     const int c0 = (int)sh.hist[b0], c1 = (int)sh.hist[b1];
@@ -292,7 +312,8 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
       // ---- the bin's keys into LDS, exact select among them
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i)
-        if (u[i] - lo2 <= span && level_bin(u[i], lo2, by_value, flo2, fscale2, shift) == bs)
+        if (u[i] - lo2 <= span && (!given_level || u[i] != 0u) &&
+            level_bin(u[i], lo2, by_value, flo2, fscale2, shift) == bs)
           sh.cu[atomicAdd(&sh.ncand, 1)] = u[i];
       __syncthreads();
       const int nc = sh.ncand;
@@ -307,7 +328,8 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
     uint32_t nlo = 0xFFFFFFFFu, nhi = 0u;
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
-      if (u[i] - lo2 <= span && level_bin(u[i], lo2, by_value, flo2, fscale2, shift) == bs) {
+      if (u[i] - lo2 <= span && (!given_level || u[i] != 0u) &&
+          level_bin(u[i], lo2, by_value, flo2, fscale2, shift) == bs) {
         nlo = min(nlo, u[i]);
         nhi = max(nhi, u[i]);
       }
@@ -367,22 +389,28 @@ hipError_t launch_copy_sel(const int32_t* cand, int P, int K, int32_t* sel, hipS
 
 hipError_t launch_topk(const float* keys, long long key_stride, const int32_t* cand, long long cand_stride, int P,
                        int n, int K, int32_t* sel_out, long long sel_stride, float* keys_out,
-                       long long keys_out_stride, hipStream_t st) {
+                       long long keys_out_stride, hipStream_t st, bool given_hist) {
   if (n < 1 || K < 1 || K > n) return hipErrorInvalidValue;
+  if (given_hist && (cand || n > 32768 || sel_stride < kHistBins)) return hipErrorInvalidValue;
   const int items = (n + kTopkThreads - 1) / kTopkThreads;
   dim3 grid(P), block(kTopkThreads);
+  if (given_hist) {
+    FL_LAUNCH((k_topk<32, false, true>), grid, block, 0, st, keys, key_stride, cand, cand_stride, n, K, sel_out,
+              sel_stride, keys_out, keys_out_stride);
+    return hipGetLastError();
+  }
 #define FL_TOPK(IT)                                                                                             \
   do {                                                                                                          \
     if (cand) {                                                                                                 \
       const int lds = (IT) * kTopkThreads * (int)sizeof(int32_t);                                               \
-      static const hipError_t attr =                                                                            \
-          hipFuncSetAttribute((const void*)k_topk<IT, true>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);  \
+      static const hipError_t attr = hipFuncSetAttribute((const void*)k_topk<IT, true, false>,                  \
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);      \
       if (attr != hipSuccess) return attr;                                                                      \
-      FL_LAUNCH((k_topk<IT, true>), grid, block, lds, st, keys, key_stride, cand, cand_stride, n, K,   \
-                         sel_out, sel_stride, keys_out, keys_out_stride);                                       \
+      FL_LAUNCH((k_topk<IT, true, false>), grid, block, lds, st, keys, key_stride, cand, cand_stride, n, K,     \
+                sel_out, sel_stride, keys_out, keys_out_stride);                                                \
     } else {                                                                                                    \
-      FL_LAUNCH((k_topk<IT, false>), grid, block, 0, st, keys, key_stride, cand, cand_stride, n, K,    \
-                         sel_out, sel_stride, keys_out, keys_out_stride);                                       \
+      FL_LAUNCH((k_topk<IT, false, false>), grid, block, 0, st, keys, key_stride, cand, cand_stride, n, K,      \
+                sel_out, sel_stride, keys_out, keys_out_stride);                                                \
     }                                                                                                           \
   } while (0)
   if (items <= 1) FL_TOPK(1);

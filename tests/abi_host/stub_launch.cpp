@@ -30,7 +30,7 @@ hipError_t launch_quant_res(const CacheGeo&, int, const void*, const void*, fl_d
   return counted();
 }
 hipError_t launch_topk(const float*, long long, const int32_t*, long long, int, int, int, int32_t*, long long, float*,
-                       long long, hipStream_t) {
+                       long long, hipStream_t, bool) {
   return counted();
 }
 hipError_t launch_copy_sel(const int32_t*, int, int, int32_t*, hipStream_t, long long) { return counted(); }

@@ -187,7 +187,8 @@ def test_validation_layer_under_address_sanitizer(tmp_path):
            "-I", os.path.join(ROOT, "include"), "-I", csrc,
            os.path.join(csrc, "abi.cpp"), os.path.join(here, "stub_launch.cpp"), os.path.join(here, "harness.cpp"),
            "-o", str(exe)]
-    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    build = subprocess.run(cmd, capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr[-4000:]
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0")
     env.pop("FL_CHECK", None)
     res = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)

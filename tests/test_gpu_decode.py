@@ -27,6 +27,9 @@ def _decode_case(cfg, tol, rel):
                 force = {r + 1: gpu[r]["sel"][l, b, h] for r in range(1, cfg.R)}
                 orc = decode.decode_slice(krec, vrec, [q[l, b, h] for q in qs], cfg.K, sel_force=force)
                 cand = np.arange(cfg.S)
+                # loop 2's selection from the GPU's own loop-1 logits: bit-exact
+                exact = prefill.topk(gpu[0]["logits"][l, b, h].astype(np.float64), cand, min(cfg.K, cfg.S))
+                assert np.array_equal(gpu[1]["sel"][l, b, h], exact), (l, b, h, "loop-2 selection from its logits")
                 for r in range(cfg.R):
                     g = {k: gpu[r][k][l, b, h] for k in ("O", "U", "M", "lse")}
                     o = orc[r]
@@ -294,6 +297,8 @@ def test_decode_full_launch_sampled():
             force = {r + 1: snaps[r]["sel"][l, b, h] for r in range(1, cfg.R)}
             orc = decode.decode_slice(krec, vrec, [q[l, b, h] for q in qs], cfg.K, sel_force=force)
             cand = np.arange(cfg.S)
+            exact = prefill.topk(snaps[0]["logits"][l, b, h].astype(np.float64), cand, cfg.K)
+            assert np.array_equal(snaps[1]["sel"][l, b, h], exact), (l, b, h, "loop-2 selection from its logits")
             for r in range(cfg.R):
                 if r >= 1:
                     key = orc[r - 1]["logits"]
@@ -313,3 +318,39 @@ def test_decode_full_launch_sampled():
                 assert np.max(np.abs(lg - orc[r]["logits"])) <= 1e-4 * max(1.0, np.max(np.abs(orc[r]["logits"])))
     del cache, runs
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype,T,ties", [("f32", 2500, False), ("bf16", 4096, True), ("f32", 2048, True)])
+def test_decode_selection_from_loop1_histogram(dtype, T, ties):
+    """Loop 2's selection starts from the histogram the dense loop leaves in
+    the selection rows (caches of at least 2048 positions): over a partial
+    context (T < S) and with logits made to tie (every loop-1 key repeated
+    over four consecutive positions, so equal records give equal logits), it
+    equals the oracle's top-K of the GPU's own loop-1 logits exactly (ties
+    to the lower position), and the outputs match the oracle."""
+    import torch
+    import sparse_attn_residual_amd as fl
+    import tests.gpu_harness as gh
+    cfg = workloads.custom(name="decode-hist", dtype=dtype, B=2, H=2, d=128, S=4096, R=3, act=(1, 0.4, 0.2),
+                           col="0.10", bits=(8, 4, 2), gamma=0.5, lognormal=0.5, L=2, decode=True, seed=17)
+    _say("decode selection from the loop-1 histogram", dtype, T, ties)
+    rows, slices = workloads.gen_batch(cfg)
+    if ties:
+        for s in slices.values():
+            s.k[0] = s.k[0][(np.arange(cfg.S) // 4) * 4].copy()
+    cache = gh.build_decode_cache(cfg, rows, slices)
+    qs = workloads.decode_queries(cfg)
+    gpu = gh.run_decode(cfg, cache, qs, T=T)
+    K = min(cfg.K, T)
+    n_ties = 0
+    for l in range(cfg.L):
+        for b in range(cfg.B):
+            for h in range(cfg.H):
+                lg = gpu[0]["logits"][l, b, h][:T].astype(np.float64)
+                exact = prefill.topk(lg, np.arange(T), K)
+                assert np.array_equal(gpu[1]["sel"][l, b, h], exact), (l, b, h)
+                kth = np.sort(lg)[::-1][K - 1]
+                n_ties += int(np.sum(lg == kth) > 1)
+    if ties:
+        assert n_ties > 0, "the tie case produced no tie at the threshold"
+    _check_decode(cfg, gpu, slices, qs, T, 1e-5 if dtype == "f32" else 2e-3, rel=dtype != "f32")
