@@ -28,6 +28,9 @@
 //    the current one is used.  Dequantizing inside the attention kernel
 //    instead would repeat the work for every row block and the vector ALUs
 //    are already the busier unit on gfx950.
+#include <cstdlib>
+#include <cstring>
+
 #include "launch.hpp"
 
 namespace fl {
@@ -82,11 +85,6 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 }
 
 // ------------------------------------------------------------- tile images
-// One block of 256 threads per tile: columns sel[tile*64 .. +64) (sel NULL:
-// positions tile*64 ..), reconstructed at loop rc, staged in LDS in the image
-// layout and written out with 16-byte stores.  Every packed record a loop
-// attends is dequantized exactly once here (p1 §4.4: chosen keys gathered into
-// dense buffers; p1 App. G: attention works from the packed streams).
 // Column slot of tile column x in the V^T image.  In the S^T = K Q^T
 // accumulator a lane of half hf holds, per 16 columns, columns 4hf..4hf+3
 // and 8+4hf..8+4hf+3; storing those eight next to each other lets the PV
@@ -97,23 +95,19 @@ __host__ __device__ constexpr int vt_col(int x) {
 static_assert(vt_col(0) == 0 && vt_col(4) == 8 && vt_col(8) == 4 && vt_col(12) == 12 && vt_col(21) == 25,
               "V^T column slots");
 
-// NR >= 0: the workload format with a chain of exactly NR residual loops
-// (rc = NR + 1), its loads batched (chain_group_n); NR < 0: any chain.
+// One tile image in LDS (img, kImgBytes) from 256 threads of a block: the
+// columns tile*64 .. +64 of a selection row (sel NULL: those positions
+// themselves; past K: padding), reconstructed at loop rc for KV head hk of
+// sequence b.  NR >= 0: the workload format with a chain of exactly NR
+// residual loops (rc = NR + 1), its loads batched (chain_group_n); NR < 0:
+// any chain.  Ends with a block barrier: the image is complete.
 template <int NR>
-__global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const int32_t* __restrict__ sel, int K,
-                                                     int ntiles, uint8_t* __restrict__ out) {
-  __shared__ __align__(16) uint8_t img[kImgBytes];
-  // sel NULL: the tiles of positions 0..K-1 are the same for every query
-  // head of a KV head, so they are built once per (b, KV head)
-  const int bh = blockIdx.x / ntiles;
-  const int tile = blockIdx.x - bh * ntiles;
-  const int nh = sel ? c.H : c.Hkv;
-  const int b = bh / nh;
-  const int hk = sel ? kv_head(c, bh - b * nh) : bh - b * nh;
+__device__ inline void build_tile(uint8_t* img, float* wmax, const CacheGeo& c, int rc, const int32_t* selrow, int K,
+                                  int tile, int b, int hk) {
   const int t = threadIdx.x;
   const int col = t >> 2, g = t & 3;
   const int idx = tile * kBN + col;
-  const int j = idx < K ? (sel ? sel[(long long)bh * K + idx] : idx) : -1;
+  const int j = idx < K ? (selrow ? selrow[idx] : idx) : -1;
   float x[32];
   // K rows (bf16)
   if (j >= 0) {
@@ -154,7 +148,6 @@ __global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const i
     for (int e = 0; e < 32; ++e) x[e] = 0.0f;
   }
   // the tile's largest |v~| decides its shift (almost always 0)
-  __shared__ float wmax[4];
   {
     float mx = 0.0f;
 #pragma unroll
@@ -178,9 +171,28 @@ __global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const i
   if (g == 0) ((int*)(img + kImgPos))[col] = j >= 0 ? j : kNoPos;
   if (t == 0) *(int*)(img + kImgShift) = vsh;
   __syncthreads();
+}
+
+// One block of 256 threads per tile: the image built in LDS (build_tile),
+// then written out with 16-byte stores.  Every packed record a loop attends
+// is dequantized exactly once here (p1 §4.4: chosen keys gathered into dense
+// buffers; p1 App. G: attention works from the packed streams).
+template <int NR>
+__global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const int32_t* __restrict__ sel, int K,
+                                                     int ntiles, uint8_t* __restrict__ out) {
+  __shared__ __align__(16) uint8_t img[kImgBytes];
+  __shared__ float wmax[4];
+  // sel NULL: the tiles of positions 0..K-1 are the same for every query
+  // head of a KV head, so they are built once per (b, KV head)
+  const int bh = blockIdx.x / ntiles;
+  const int tile = blockIdx.x - bh * ntiles;
+  const int nh = sel ? c.H : c.Hkv;
+  const int b = bh / nh;
+  const int hk = sel ? kv_head(c, bh - b * nh) : bh - b * nh;
+  build_tile<NR>(img, wmax, c, rc, sel ? sel + (long long)bh * K : nullptr, K, tile, b, hk);
   uint4* dst = (uint4*)(out + ((long long)bh * ntiles + tile) * kImgBytes);
   const uint4* src = (const uint4*)img;
-  for (int i = t; i < kImgBytes / 16; i += 256) dst[i] = src[i];
+  for (int i = threadIdx.x; i < kImgBytes / 16; i += 256) dst[i] = src[i];
 }
 
 // ------------------------------------------------------------- main kernel
@@ -188,9 +200,10 @@ enum { kModeAttn = 0, kModeUM = 1 };
 
 struct MfmaArgs {
   AttnArgs a;
-  const uint8_t* tiles;   // tile images [B][H][ntiles_total]
+  const uint8_t* tiles;   // tile images [B][H][ntiles_total] (not read when the block builds its own)
   int ntiles_total;       // tiles per (b, h)
   int nblk;               // row blocks per (b, h)
+  int rc;                 // loop whose reconstructions the tiles hold
   float c2;               // tau * log2(e)
 };
 
@@ -480,12 +493,20 @@ __device__ inline void write_row(const AttnArgs& a, int r, long long bhS, int i,
 // RING: tile images resident in LDS.  Two: the next tile is copied while this
 // one is used; one: the copy waits for the block's waves to finish the tile
 // (three blocks per CU then cover each other's copies).
-template <int NW, int MODE, int RING>
-__global__ __launch_bounds__(64 * NW, NW == 4 ? (RING == 1 ? 3 : 2) : 1) void k_attn_mfma(MfmaArgs m) {
+// SRC 0: the tiles are images built beforehand (k_build_tiles) and copied
+// in; SRC 1 (four waves, one-image ring, the sparse loops' attention): the
+// block's 256 threads build each tile from the packed records in LDS
+// themselves (build_tile) - no image round trip and no extra launch, but
+// every row block of a head repeats the dequantization, and the builder's
+// registers next to the attention state leave two blocks per CU.
+template <int NW, int MODE, int RING, int SRC>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? (SRC == 0 && RING == 1 ? 3 : 2) : 1) void k_attn_mfma(MfmaArgs m) {
+  static_assert(SRC == 0 || (NW == 4 && RING == 1), "blocks build their tiles with 256 threads into one image");
   constexpr int BM = 32 * NW;
   constexpr int AHEAD = RING - 1;
   extern __shared__ __align__(16) uint8_t lds[];   // RING tile images
   __shared__ int sh_ntiles;
+  __shared__ float sh_wmax[4];
   const AttnArgs& a = m.a;
   const CacheGeo& c = a.c;
   const int lane = threadIdx.x & 63;
@@ -509,7 +530,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (RING == 1 ? 3 : 2) : 1) void k_
   const long long bhS = (long long)bh * c.S;
   // loop 1 reads the tiles of its KV head (built once per KV head)
   const long long tbh = dense ? (long long)b * c.Hkv + kv_head(c, bh - b * c.H) : bh;
-  const uint8_t* imgs = m.tiles + tbh * m.ntiles_total * kImgBytes;
+  const uint8_t* imgs = SRC ? nullptr : m.tiles + tbh * m.ntiles_total * kImgBytes;
+  const int32_t* selrow = SRC ? a.sel + (long long)bh * a.K : nullptr;
 
   // ---- the lane's row and its queries (B operand of S^T = K Q^T)
   int ipos = -1;
@@ -553,7 +575,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (RING == 1 ? 3 : 2) : 1) void k_
     int lo = 0, hi = m.ntiles_total;  // first tile whose first column lies beyond blk_max
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      const int p0 = *(const int*)(imgs + (long long)mid * kImgBytes + kImgPos);
+      const int p0 = SRC ? selrow[mid * kBN] : *(const int*)(imgs + (long long)mid * kImgBytes + kImgPos);
       if (p0 <= blk_max) lo = mid + 1; else hi = mid;
     }
     sh_ntiles = lo;
@@ -577,10 +599,15 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (RING == 1 ? 3 : 2) : 1) void k_
   const int nt = sh_ntiles;
 
   // ---- prologue: the first max(AHEAD, 1) tiles into the ring
-  const __amdgpu_buffer_rsrc_t rs = img_rsrc(imgs, m.ntiles_total * kImgBytes);
-  for (int k = 0; k < (AHEAD > 0 ? AHEAD : 1) && k < nt; ++k) dma_tile<NW>(rs, k * kImgBytes, lds + k * kImgBytes);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  const int hk = kv_head(c, bh - b * c.H);
+  const __amdgpu_buffer_rsrc_t rs = img_rsrc(imgs, SRC ? 0 : m.ntiles_total * kImgBytes);
+  if (SRC) {
+    if (nt > 0) build_tile<-1>(lds, sh_wmax, c, m.rc, selrow, a.K, 0, b, hk);
+  } else {
+    for (int k = 0; k < (AHEAD > 0 ? AHEAD : 1) && k < nt; ++k) dma_tile<NW>(rs, k * kImgBytes, lds + k * kImgBytes);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
 
   // V shift of the accumulators: o holds 2^-osh times the products, osh the
   // largest tile shift seen so far (wave-uniform; 0 unless some |v~| >= 2^15).
@@ -619,6 +646,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (RING == 1 ? 3 : 2) : 1) void k_
     }
     lsum += dsh == 0 ? ls : __builtin_ldexpf(ls, dsh);
     pv_tile(T, pf, l32, hf, o);
+    if (SRC) {
+      // every wave is done with the slot: build the next tile in it
+      if (tt + 1 < nt) {
+        lds_barrier();
+        build_tile<-1>(lds, sh_wmax, c, m.rc, selrow, a.K, tt + 1, b, hk);
+      }
+      continue;
+    }
     if (AHEAD == 0) {
       // every wave is done with the slot: copy the next tile into it
       if (tt + 1 < nt) {
@@ -891,15 +926,16 @@ hipError_t launch_gather(const CacheGeo& c, int rc, const int32_t* sel, int K, u
   return hipGetLastError();
 }
 
-template <int NW, int MODE, int RING>
+template <int NW, int MODE, int RING, int SRC = 0>
 static hipError_t launch_one(const MfmaArgs& m, hipStream_t st) {
   constexpr size_t lds = (size_t)RING * kImgBytes;
   // once per kernel and process (static initialisation is thread-safe)
   static const hipError_t attr =
-      hipFuncSetAttribute((const void*)k_attn_mfma<NW, MODE, RING>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      hipFuncSetAttribute((const void*)k_attn_mfma<NW, MODE, RING, SRC>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)lds);
   if (attr != hipSuccess) return attr;
   const int nunits = m.a.c.B * m.a.c.H * m.nblk;
-  FL_LAUNCH((k_attn_mfma<NW, MODE, RING>), dim3(nunits), dim3(64 * NW), lds, st, m);
+  FL_LAUNCH((k_attn_mfma<NW, MODE, RING, SRC>), dim3(nunits), dim3(64 * NW), lds, st, m);
   return hipGetLastError();
 }
 
@@ -914,7 +950,13 @@ static float c2_of(int d) { return (float)(1.4426950408889634 / __builtin_sqrt((
 // blocks per CU: measured faster there, slower for the dense loop; six-wave
 // blocks, two per CU, were slower everywhere).
 template <int MODE>
-static hipError_t launch_rows(MfmaArgs& m, int n, hipStream_t st) {
+static hipError_t launch_rows(MfmaArgs& m, int n, hipStream_t st, bool own_tiles = false) {
+  if constexpr (MODE == kModeAttn) {
+    if (own_tiles) {
+      m.nblk = (n + 127) / 128;
+      return launch_one<4, MODE, 1, 1>(m, st);
+    }
+  }
   if ((long long)m.a.c.B * m.a.c.H * ((n + 255) / 256) >= kWideBlocks) {
     m.nblk = (n + 383) / 384;
     return launch_one<12, MODE, 2>(m, st);
@@ -924,17 +966,31 @@ static hipError_t launch_rows(MfmaArgs& m, int n, hipStream_t st) {
   return launch_one<4, MODE, 1>(m, st);
 }
 
+// Whether a sparse loop's row blocks build their tiles in LDS themselves
+// (FL_TILES=lds, a measurement aid) instead of reading the images built once
+// per loop (the default).  Measured slower at every size: 7.6 vs 6.2 ms for
+// the 32K step, and even for heads of one or two row blocks (loops 7 and 8
+// of the deep 16K workload, 0.17 vs 0.05 ms), where a few dozen blocks each
+// build all their tiles in turn while the image builder spreads the same
+// work over hundreds of blocks.
+static bool own_tiles(int) {
+  const char* e = std::getenv("FL_TILES");
+  return e && std::strcmp(e, "lds") == 0;
+}
+
 // Loop-r attention: r == 1 dense over every position, r >= 2 over S_r.
 // ws: gather_bytes(c, K) bytes (K = S at r == 1).
 hipError_t launch_attn_mfma(const AttnArgs& a, uint8_t* ws, hipStream_t st) {
   MfmaArgs m{};
   m.a = a;
   m.c2 = c2_of(a.c.d);
+  m.rc = a.r;
   const int K = a.r == 1 ? a.c.S : a.K;
+  m.ntiles_total = (K + kBN - 1) / kBN;
+  if (a.r >= 2 && own_tiles(a.c.n[a.r])) return launch_rows<kModeAttn>(m, a.c.n[a.r], st, true);
   hipError_t e = launch_gather(a.c, a.r, a.r == 1 ? nullptr : a.sel, K, ws, st);
   if (e != hipSuccess) return e;
   m.tiles = ws;
-  m.ntiles_total = (K + kBN - 1) / kBN;
   return launch_rows<kModeAttn>(m, a.r == 1 ? a.c.S : a.c.n[a.r], st);
 }
 
@@ -943,10 +999,11 @@ hipError_t launch_um_mfma(const AttnArgs& a, uint8_t* ws, hipStream_t st) {
   MfmaArgs m{};
   m.a = a;
   m.c2 = c2_of(a.c.d);
+  m.rc = a.r - 1;
+  m.ntiles_total = (a.K + kBN - 1) / kBN;
   hipError_t e = launch_gather(a.c, a.r - 1, a.sel, a.K, ws, st);
   if (e != hipSuccess) return e;
   m.tiles = ws;
-  m.ntiles_total = (a.K + kBN - 1) / kBN;
   return launch_rows<kModeUM>(m, a.c.n[a.r], st);
 }
 

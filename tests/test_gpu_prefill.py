@@ -577,3 +577,32 @@ def test_kernel_timer_records_launches():
     assert all(t > 0 for _, t in recs), recs
     gh.run_prefill(cfg, rows, slices)
     assert fl.fl_timing_collect() == []
+
+
+@pytest.mark.parametrize("cfgid", [None, 4])
+def test_prefill_tile_sources_agree(monkeypatch, cfgid):
+    """The sparse loops' attention from tile images built once per loop (the
+    default) and from tiles each row block builds in LDS (FL_TILES=lds, the
+    measured alternative) gives the same states bit for bit, both matching
+    the oracle; a small case and the deep 16K R = 8 workload."""
+    import tests.gpu_harness as gh
+    if cfgid is None:
+        cfg = workloads.custom(name="tile-src", dtype="bf16", B=2, H=2, d=128, S=1300, R=4, act=(1, 0.3, 0.15, 0.08),
+                               col="0.15", bits=(8, 4, 2, 4), lognormal=0.5, seed=33)
+        heads = [0, 1]
+    else:
+        cfg = workloads.CONFIGS[cfgid]
+        heads = [5]
+    _say("tile sources", cfg.name)
+    rows, slices = workloads.gen_batch(cfg, heads=None)
+    runs = {}
+    for src in ("images", "lds"):
+        monkeypatch.setenv("FL_TILES", src)
+        runs[src] = gh.run_prefill(cfg, rows, slices)
+    monkeypatch.delenv("FL_TILES")
+    a, b = runs["images"], runs["lds"]
+    for r in range(cfg.R):
+        for k in ("O", "U", "M", "lse"):
+            assert np.array_equal(a["state"][r][k], b["state"][r][k]), (r + 1, k)
+    orc = _oracle_slices(cfg, rows, slices, b, heads)
+    _check_outputs(cfg, b, orc, heads, 2e-3, rel=True)
