@@ -50,6 +50,10 @@
  *     stream, copies the index arrays it reads to the host and checks them;
  *     a violation returns FL_EINVAL before anything is launched.  This costs
  *     a synchronization and the copies: a debugging aid.
+ *   - FL_TILES=lds (environment, a measurement aid) makes the sparse loops'
+ *     attention build its tiles from the packed records in LDS in every row
+ *     block instead of reading the tile images built once per loop (the
+ *     default; same results bit for bit, measured slower).
  */
 #ifndef FLASHLOOP_H
 #define FLASHLOOP_H
