@@ -499,12 +499,20 @@ __device__ inline void write_row(const AttnArgs& a, int r, long long bhS, int i,
 // themselves (build_tile) - no image round trip and no extra launch, but
 // every row block of a head repeats the dequantization, and the builder's
 // registers next to the attention state leave two blocks per CU.
-template <int NW, int MODE, int RING, int SRC>
+// SPLIT > 1 (one-image ring of prebuilt tiles): the waves form NW / SPLIT
+// row groups of 32 rows times SPLIT column splits.  Each step copies SPLIT
+// consecutive tiles and split s takes the s-th of them; at the end splits
+// 1.. hand their (reference, sum, accumulators) to split 0 through LDS, which
+// merges them in split order (fixed: deterministic).  Fewer rows per block
+// and a shorter tile chain per wave: for launches too small to fill the chip.
+template <int NW, int MODE, int RING, int SRC, int SPLIT = 1>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? (SRC == 0 && RING == 1 ? 3 : 2) : 1) void k_attn_mfma(MfmaArgs m) {
   static_assert(SRC == 0 || (NW == 4 && RING == 1), "blocks build their tiles with 256 threads into one image");
-  constexpr int BM = 32 * NW;
+  static_assert(SPLIT == 1 || (SRC == 0 && RING == 1 && NW % SPLIT == 0), "column splits: prebuilt tiles, one step");
+  constexpr int G = NW / SPLIT;   // row groups
+  constexpr int BM = 32 * G;
   constexpr int AHEAD = RING - 1;
-  extern __shared__ __align__(16) uint8_t lds[];   // RING tile images
+  extern __shared__ __align__(16) uint8_t lds[];   // RING steps of SPLIT tile images
   __shared__ int sh_ntiles;
   __shared__ float sh_wmax[4];
   const AttnArgs& a = m.a;
@@ -513,6 +521,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (SRC == 0 && RING == 1 ? 3 : 2) 
   const int wv = threadIdx.x >> 6;
   const int hf = lane >> 5;       // half of the wave
   const int l32 = lane & 31;
+  const int rg = SPLIT == 1 ? wv : wv % G;  // row group
+  const int sp = SPLIT == 1 ? 0 : wv / G;   // column split
 
   // block -> (b, h, row block); every XCD gets whole heads, heavy blocks first
   const int nunits = c.B * c.H * m.nblk;
@@ -532,12 +542,17 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (SRC == 0 && RING == 1 ? 3 : 2) 
   const long long tbh = dense ? (long long)b * c.Hkv + kv_head(c, bh - b * c.H) : bh;
   const uint8_t* imgs = SRC ? nullptr : m.tiles + tbh * m.ntiles_total * kImgBytes;
   const int32_t* selrow = SRC ? a.sel + (long long)bh * a.K : nullptr;
+  const int hk = kv_head(c, bh - b * c.H);
+  const __amdgpu_buffer_rsrc_t rs = img_rsrc(imgs, SRC ? 0 : m.ntiles_total * kImgBytes);
+  // Tile 0 is needed by every block that has a column at all: its copy is
+  // issued first, under the query loads and the tile count below.
+  if (!SRC && m.ntiles_total > 0) dma_img<NW, kImgChunks * SPLIT>(rs, 0, lds);
 
   // ---- the lane's row and its queries (B operand of S^T = K Q^T)
   int ipos = -1;
   bf16x8_t qf[8];
   {
-    const int t = row0 + wv * 32 + l32;
+    const int t = row0 + rg * 32 + l32;
     long long qrow = 0;
     if (t < nrows) {
       if (dense) {
@@ -571,14 +586,33 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (SRC == 0 && RING == 1 ? 3 : 2) 
       blk_max = c.rows[r][(long long)b * c.n[r] + t1];
     }
   }
-  if (threadIdx.x == 0) {
-    int lo = 0, hi = m.ntiles_total;  // first tile whose first column lies beyond blk_max
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      const int p0 = SRC ? selrow[mid * kBN] : *(const int*)(imgs + (long long)mid * kImgBytes + kImgPos);
-      if (p0 <= blk_max) lo = mid + 1; else hi = mid;
+  // Tiles the block reads: those whose first column is <= blk_max (first
+  // columns ascend).  Loop 1's tiles are the positions in order; otherwise
+  // wave 0 probes up to 64 tiles at once and keeps the segment the answer
+  // lies in (one round up to 64 tiles, two up to 4096).
+  if (wv == 0) {
+    int base = 0;
+    if (dense) {
+      base = min(m.ntiles_total, blk_max / kBN + 1);
+    } else {
+      int end = m.ntiles_total;  // answer in [base, end]; tiles [base, end) unprobed
+      while (end > base) {
+        const int len = end - base;
+        const int step = (len + 63) >> 6;
+        bool le = false;
+        if (lane * step < len) {
+          const int t = base + lane * step;
+          const int p0 = SRC ? selrow[t * kBN] : *(const int*)(imgs + (long long)t * kImgBytes + kImgPos);
+          le = p0 <= blk_max;
+        }
+        const int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(le));
+        if (cnt == 0) break;
+        const int nb = base + (cnt - 1) * step + 1;
+        end = min(base + cnt * step, end);
+        base = nb;
+      }
     }
-    sh_ntiles = lo;
+    if (lane == 0) sh_ntiles = base;
   }
 
   // row state: mref = reference max (log2 units), lsum = partial row sum
@@ -598,13 +632,11 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (SRC == 0 && RING == 1 ? 3 : 2) 
   __syncthreads();
   const int nt = sh_ntiles;
 
-  // ---- prologue: the first max(AHEAD, 1) tiles into the ring
-  const int hk = kv_head(c, bh - b * c.H);
-  const __amdgpu_buffer_rsrc_t rs = img_rsrc(imgs, SRC ? 0 : m.ntiles_total * kImgBytes);
+  // ---- prologue: the first max(AHEAD, 1) tiles into the ring (tile 0 issued above)
   if (SRC) {
     if (nt > 0) build_tile<-1>(lds, sh_wmax, c, m.rc, selrow, a.K, 0, b, hk);
   } else {
-    for (int k = 0; k < (AHEAD > 0 ? AHEAD : 1) && k < nt; ++k) dma_tile<NW>(rs, k * kImgBytes, lds + k * kImgBytes);
+    for (int k = 1; k < AHEAD && k < nt; ++k) dma_tile<NW>(rs, k * kImgBytes, lds + k * kImgBytes);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
@@ -614,38 +646,42 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (SRC == 0 && RING == 1 ? 3 : 2) 
   // A tile of smaller shift d below osh enters with its weights scaled by
   // 2^-d (folded into the exponent); the row sum always adds the unscaled ones.
   int osh = 0;
-  for (int tt = 0; tt < nt; ++tt) {
-    const uint8_t* T = lds + (tt % RING) * kImgBytes;
+  const int nsteps = SPLIT == 1 ? nt : (nt + SPLIT - 1) / SPLIT;
+  for (int ks = 0; ks < nsteps; ++ks) {
+    const int tt = ks * SPLIT + sp;  // this wave's tile
+    const uint8_t* T = lds + (SPLIT == 1 ? tt % RING : sp) * kImgBytes;
     // tile tt+AHEAD goes into the slot tile tt-1 left (all waves passed it)
     if (AHEAD > 0 && tt + AHEAD < nt)
       dma_tile<NW>(rs, (tt + AHEAD) * kImgBytes, lds + ((tt + AHEAD) % RING) * kImgBytes);
-    f32x16_t s0, s1;
-    qk_tile(T, qf, l32, hf, s0, s1);
-    float x[32];
-    softmax_mask(T, s0, s1, ipos, blk_min, hf, x);
-    const int tsh = __builtin_amdgcn_readfirstlane(*(const int*)(T + kImgShift));
-    if (tsh > osh) {
-      const float f = __builtin_ldexpf(1.0f, osh - tsh);
+    if (SPLIT == 1 || tt < nt) {
+      f32x16_t s0, s1;
+      qk_tile(T, qf, l32, hf, s0, s1);
+      float x[32];
+      softmax_mask(T, s0, s1, ipos, blk_min, hf, x);
+      const int tsh = __builtin_amdgcn_readfirstlane(*(const int*)(T + kImgShift));
+      if (tsh > osh) {
+        const float f = __builtin_ldexpf(1.0f, osh - tsh);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= f;
-      osh = tsh;
-    }
-    const int dsh = osh - tsh;
-    // Weights against the current reference (UM: the fixed loop r-1
-    // statistics).  ATTN: only if a lane's sum exceeds 2^kRescale (so some
-    // weight might) or a valid row has no reference yet is the tile max
-    // taken, the lazy rescale applied and the weights formed again.
-    f16x8_t pf[4];
-    float ls = softmax_probs(x, ((MODE == kModeAttn && mref == -INFINITY) ? 0.0f : mref) + (float)dsh, m.c2, pf);
-    if (MODE == kModeAttn) {
-      const bool bad = (ipos >= 0 && mref == -INFINITY) || !(ls <= kRescaleP);
-      if (__builtin_amdgcn_ballot_w64(bad)) {
-        softmax_rescale(x, m.c2, mref, lsum, o);
-        ls = softmax_probs(x, (mref == -INFINITY ? 0.0f : mref) + (float)dsh, m.c2, pf);
+        for (int db = 0; db < 4; ++db) o[db] *= f;
+        osh = tsh;
       }
+      const int dsh = osh - tsh;
+      // Weights against the current reference (UM: the fixed loop r-1
+      // statistics).  ATTN: only if a lane's sum exceeds 2^kRescale (so some
+      // weight might) or a valid row has no reference yet is the tile max
+      // taken, the lazy rescale applied and the weights formed again.
+      f16x8_t pf[4];
+      float ls = softmax_probs(x, ((MODE == kModeAttn && mref == -INFINITY) ? 0.0f : mref) + (float)dsh, m.c2, pf);
+      if (MODE == kModeAttn) {
+        const bool bad = (ipos >= 0 && mref == -INFINITY) || !(ls <= kRescaleP);
+        if (__builtin_amdgcn_ballot_w64(bad)) {
+          softmax_rescale(x, m.c2, mref, lsum, o);
+          ls = softmax_probs(x, (mref == -INFINITY ? 0.0f : mref) + (float)dsh, m.c2, pf);
+        }
+      }
+      lsum += dsh == 0 ? ls : __builtin_ldexpf(ls, dsh);
+      pv_tile(T, pf, l32, hf, o);
     }
-    lsum += dsh == 0 ? ls : __builtin_ldexpf(ls, dsh);
-    pv_tile(T, pf, l32, hf, o);
     if (SRC) {
       // every wave is done with the slot: build the next tile in it
       if (tt + 1 < nt) {
@@ -655,10 +691,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (SRC == 0 && RING == 1 ? 3 : 2) 
       continue;
     }
     if (AHEAD == 0) {
-      // every wave is done with the slot: copy the next tile into it
-      if (tt + 1 < nt) {
+      // every wave is done with the slot: copy the next step's tiles into it
+      if (ks + 1 < nsteps) {
         lds_barrier();
-        dma_tile<NW>(rs, (tt + 1) * kImgBytes, lds);
+        dma_img<NW, kImgChunks * SPLIT>(rs, (ks + 1) * SPLIT * kImgBytes, lds);
         __builtin_amdgcn_s_waitcnt(0);
       }
     } else {
@@ -669,7 +705,72 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (SRC == 0 && RING == 1 ? 3 : 2) 
   }
 
   // ---- epilogue: each lane writes 64 of its row's 128 dims
-  const float lt = lsum + __shfl_xor(lsum, 32, 64);
+  float lt = lsum + __shfl_xor(lsum, 32, 64);
+  if constexpr (SPLIT > 1) {
+    // Splits 1.. leave their state in LDS (the images are no longer read:
+    // every wave passed the loop's last barrier), lane-major 16-byte slots.
+    constexpr int kPart = 17 * 1024;
+    static_assert((SPLIT - 1) * G * kPart <= SPLIT * kImgBytes, "merge buffers fit the images");
+    if (sp > 0) {
+      f32x4_t* po = (f32x4_t*)(lds + ((sp - 1) * G + rg) * kPart);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          po[(db * 4 + qq) * 64 + lane] = f32x4_t{o[db][qq * 4], o[db][qq * 4 + 1], o[db][qq * 4 + 2], o[db][qq * 4 + 3]};
+      po[16 * 64 + lane] = f32x4_t{mref, lt, (float)osh, 0.0f};
+    }
+    lds_barrier();
+    if (sp > 0) return;
+    // Split 0 merges in split order: the common reference M = max of the
+    // references (UM: all equal, the fixed loop r-1 statistics) and shift
+    // OSH = max of the shifts; split s enters with weight 2^(mref_s - M)
+    // (0 for a split that saw no column of the row) and its accumulators
+    // with 2^(osh_s - OSH) more.
+    float ms[SPLIT], ls[SPLIT];
+    int os[SPLIT];
+    ms[0] = mref;
+    ls[0] = lt;
+    os[0] = osh;
+#pragma unroll
+    for (int s = 1; s < SPLIT; ++s) {
+      const f32x4_t st4 = ((const f32x4_t*)(lds + ((s - 1) * G + rg) * kPart))[16 * 64 + lane];
+      ms[s] = st4[0];
+      ls[s] = st4[1];
+      os[s] = (int)st4[2];
+    }
+    float M = ms[0];
+    int OSH = os[0];
+#pragma unroll
+    for (int s = 1; s < SPLIT; ++s) {
+      M = fmaxf(M, ms[s]);
+      OSH = max(OSH, os[s]);
+    }
+    float f[SPLIT];
+    lt = 0.0f;
+#pragma unroll
+    for (int s = 0; s < SPLIT; ++s) {
+      const float w = MODE == kModeAttn ? (ms[s] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms[s] - M)) : 1.0f;
+      lt += w * ls[s];
+      f[s] = w * __builtin_ldexpf(1.0f, os[s] - OSH);
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] *= f[0];
+#pragma unroll
+    for (int s = 1; s < SPLIT; ++s) {
+      const f32x4_t* po = (const f32x4_t*)(lds + ((s - 1) * G + rg) * kPart);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const f32x4_t v = po[(db * 4 + qq) * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[db][qq * 4 + e] = __builtin_fmaf(f[s], v[e], o[db][qq * 4 + e]);
+        }
+    }
+    mref = M;
+    osh = OSH;
+  }
   write_row<MODE>(a, r, bhS, ipos, hf, mref, lt, o, __builtin_ldexpf(1.0f, osh));
 }
 
@@ -926,20 +1027,27 @@ hipError_t launch_gather(const CacheGeo& c, int rc, const int32_t* sel, int K, u
   return hipGetLastError();
 }
 
-template <int NW, int MODE, int RING, int SRC = 0>
+template <int NW, int MODE, int RING, int SRC = 0, int SPLIT = 1>
 static hipError_t launch_one(const MfmaArgs& m, hipStream_t st) {
-  constexpr size_t lds = (size_t)RING * kImgBytes;
+  constexpr size_t lds = (size_t)RING * SPLIT * kImgBytes;
   // once per kernel and process (static initialisation is thread-safe)
   static const hipError_t attr =
-      hipFuncSetAttribute((const void*)k_attn_mfma<NW, MODE, RING, SRC>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds);
+      hipFuncSetAttribute((const void*)k_attn_mfma<NW, MODE, RING, SRC, SPLIT>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
   const int nunits = m.a.c.B * m.a.c.H * m.nblk;
-  FL_LAUNCH((k_attn_mfma<NW, MODE, RING, SRC>), dim3(nunits), dim3(64 * NW), lds, st, m);
+  FL_LAUNCH((k_attn_mfma<NW, MODE, RING, SRC, SPLIT>), dim3(nunits), dim3(64 * NW), lds, st, m);
   return hipGetLastError();
 }
 
 constexpr int kWideBlocks = 1024;
+// Sparse launches take the most column splits whose blocks all fit on the
+// chip at once: four splits (32-row blocks, four images: one block per CU),
+// else two (64-row blocks, two per CU), else none (128-row blocks, three per
+// CU).  Measured on the deep 16K R = 8 workload, loops 4-8: 39/36/35/34/34 us
+// unsplit, 37/31/26/25/23 us split; a split launch that needs a second round
+// of blocks is slower than the unsplit one (8K workload, loop 2: 45 vs 58 us).
+constexpr int kCUs = 256;
 
 static float c2_of(int d) { return (float)(1.4426950408889634 / __builtin_sqrt((double)d)); }
 
@@ -963,6 +1071,15 @@ static hipError_t launch_rows(MfmaArgs& m, int n, hipStream_t st, bool own_tiles
   }
   m.nblk = (n + 127) / 128;
   if (MODE == kModeAttn && m.a.r == 1) return launch_one<4, MODE, 2>(m, st);
+  const long long bh = (long long)m.a.c.B * m.a.c.H;
+  if (bh * ((n + 31) / 32) <= kCUs) {
+    m.nblk = (n + 31) / 32;
+    return launch_one<4, MODE, 1, 0, 4>(m, st);
+  }
+  if (bh * ((n + 63) / 64) <= 2 * kCUs) {
+    m.nblk = (n + 63) / 64;
+    return launch_one<4, MODE, 1, 0, 2>(m, st);
+  }
   return launch_one<4, MODE, 1>(m, st);
 }
 

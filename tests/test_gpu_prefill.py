@@ -583,8 +583,10 @@ def test_kernel_timer_records_launches():
 def test_prefill_tile_sources_agree(monkeypatch, cfgid):
     """The sparse loops' attention from tile images built once per loop (the
     default) and from tiles each row block builds in LDS (FL_TILES=lds, the
-    measured alternative) gives the same states bit for bit, both matching
-    the oracle; a small case and the deep 16K R = 8 workload."""
+    measured alternative) both match the oracle; a small case and the deep
+    16K R = 8 workload.  Loop 1 and the selections do not depend on the
+    source and agree bit for bit (the image path splits small launches'
+    columns across waves, so its sparse-loop sums are ordered differently)."""
     import tests.gpu_harness as gh
     if cfgid is None:
         cfg = workloads.custom(name="tile-src", dtype="bf16", B=2, H=2, d=128, S=1300, R=4, act=(1, 0.3, 0.15, 0.08),
@@ -601,8 +603,10 @@ def test_prefill_tile_sources_agree(monkeypatch, cfgid):
         runs[src] = gh.run_prefill(cfg, rows, slices)
     monkeypatch.delenv("FL_TILES")
     a, b = runs["images"], runs["lds"]
-    for r in range(cfg.R):
-        for k in ("O", "U", "M", "lse"):
-            assert np.array_equal(a["state"][r][k], b["state"][r][k]), (r + 1, k)
-    orc = _oracle_slices(cfg, rows, slices, b, heads)
-    _check_outputs(cfg, b, orc, heads, 2e-3, rel=True)
+    for k in ("O", "U", "M", "lse"):
+        assert np.array_equal(a["state"][0][k], b["state"][0][k]), (1, k)
+    for r in range(1, cfg.R):
+        assert np.array_equal(a["sel"][r], b["sel"][r]), r + 1
+    for run in (a, b):
+        orc = _oracle_slices(cfg, rows, slices, run, heads)
+        _check_outputs(cfg, run, orc, heads, 2e-3, rel=True)
