@@ -28,8 +28,11 @@ __device__ inline float key_value(uint32_t u) {
 // rowoff[i] with the flagged count of the rows before i.  The rank of a
 // flagged candidate in candidate order is then
 //   rowoff[i] + wtab[w][i] + popcount(ballot_i & lanes below).
+// Both prefix sums are parallel: thread (i, w) scans row i over the waves in
+// a group of kTopkWaves lanes, then one wave scans the row totals.
 template <int ITEMS>
 __device__ inline void row_counts(uint64_t bits, int (*wtab)[64], int* rowoff) {
+  static_assert(ITEMS * kTopkWaves <= kTopkThreads && kTopkWaves == 16 && ITEMS <= kWave, "scan shape");
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
@@ -37,24 +40,29 @@ __device__ inline void row_counts(uint64_t bits, int (*wtab)[64], int* rowoff) {
     if (lane == 0) wtab[wv][i] = __popcll(m);
   }
   __syncthreads();
-  if (threadIdx.x < ITEMS) {
-    const int i = threadIdx.x;
-    int acc = 0;
-    for (int w = 0; w < kTopkWaves; ++w) {
-      const int t = wtab[w][i];
-      wtab[w][i] = acc;
-      acc += t;
+  const int t = threadIdx.x;
+  if (t < ITEMS * kTopkWaves) {
+    const int i = t / kTopkWaves, w = t % kTopkWaves;
+    const int c = wtab[w][i];
+    int x = c;
+#pragma unroll
+    for (int o = 1; o < kTopkWaves; o <<= 1) {
+      const int y = __shfl_up(x, o, kTopkWaves);
+      if (w >= o) x += y;
     }
-    rowoff[i] = acc;
+    wtab[w][i] = x - c;
+    if (w == kTopkWaves - 1) rowoff[i] = x;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int i = 0; i < ITEMS; ++i) {
-      const int t = rowoff[i];
-      rowoff[i] = acc;
-      acc += t;
+  if (t < kWave) {
+    const int c = t < ITEMS ? rowoff[t] : 0;
+    int x = c;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(x, o, kWave);
+      if (t >= o) x += y;
     }
+    if (t < ITEMS) rowoff[t] = x - c;
   }
   __syncthreads();
 }
@@ -70,7 +78,7 @@ struct TopkShared {
   int wsum[kTopkWaves];
   uint32_t wmin[kTopkWaves], wmax[kTopkWaves];
   uint32_t digit;
-  int rem, bstar, cnt, ncand, bad;
+  int rem, bstar, cnt, ncand, bad, eqc;
 };
 
 // Block-wide inclusive prefix sum of one value per thread.
@@ -89,16 +97,20 @@ __device__ inline int block_incl_scan(int x, int* wsum) {
 }
 
 // Radix select over NI keys per thread (bit i of vmask: key i valid): the
-// K-th largest key T and how many keys equal to T are among the K largest.
-// Four 8-bit passes with an LDS digit histogram and a parallel digit search.
+// K-th largest key T, how many keys equal to T are among the K largest (rem)
+// and how many keys equal T (eqc).  8-bit passes with an LDS digit histogram
+// and a parallel digit search; the first p0 digits are known to be those of
+// prefix0 (shared by every key), so the passes start at digit p0.
 template <int NI>
-__device__ inline void radix_find(const uint32_t* v, uint64_t vmask, int K, TopkShared& sh, uint32_t& T, int& rem) {
+__device__ inline void radix_find(const uint32_t* v, uint64_t vmask, int K, int p0, uint32_t prefix0,
+                                  TopkShared& sh, uint32_t& T, int& rem, int& eqc) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
-  uint32_t prefix = 0, mask = 0;
+  uint32_t mask = p0 > 0 ? 0xFFFFFFFFu << (32 - 8 * p0) : 0u;
+  uint32_t prefix = prefix0 & mask;
   rem = K;
-  for (int pass = 0; pass < 4; ++pass) {
+  for (int pass = p0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     if (tid < 256) sh.hist[tid] = 0;
     __syncthreads();
@@ -106,7 +118,7 @@ __device__ inline void radix_find(const uint32_t* v, uint64_t vmask, int K, Topk
     for (int i = 0; i < NI; ++i) {
       bool part = ((vmask >> i) & 1) && (v[i] & mask) == prefix;
       const uint32_t dg = (v[i] >> shift) & 255u;
-      if (pass == 0) {
+      if (pass == p0) {
         // keys of one problem share their leading digit: aggregate per wave
         for (int it = 0; it < 4; ++it) {
           const uint64_t pm = __ballot(part);
@@ -141,12 +153,14 @@ __device__ inline void radix_find(const uint32_t* v, uint64_t vmask, int K, Topk
       if (excl < rem && x >= rem) {
         sh.digit = (uint32_t)(255 - tid);
         sh.rem = rem - excl;
+        sh.eqc = c;
       }
     }
     __syncthreads();
     prefix |= sh.digit << shift;
     mask |= 255u << shift;
     rem = sh.rem;
+    eqc = sh.eqc;
     __syncthreads();
   }
   T = prefix;
@@ -199,16 +213,11 @@ __device__ inline int level_bin(uint32_t u, uint32_t lo, bool by_value, float fl
 // a range of one value is T itself.  The output stage takes every key above
 // T and the first keys equal to T in candidate order, ranked with wave
 // ballots: ascending, unique.  Keys must not be NaN.
-// HIST: the first level is given, not computed: the first kBins entries of
-// each problem's output row hold the histogram of its keys by the top 11
-// bits of their order keys (every key counted once; loop 1 of a decode step
-// leaves it there), so the range search starts at that level.
-template <int ITEMS, bool CAND, bool HIST>
+template <int ITEMS, bool CAND>
 __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__ keys, long long key_stride,
                                                        const int32_t* cand, long long cand_stride, int n, int K,
                                                        int32_t* sel_out, long long sel_stride, float* keys_out,
                                                        long long keys_out_stride) {
-  static_assert(kBins == kHistBins, "the given histogram is the first level");
   static_assert(ITEMS <= 32, "at most 32768 keys per problem");
   __shared__ TopkShared sh;
   const int p = blockIdx.x;
@@ -238,54 +247,38 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
   }
   __syncthreads();  // every read of keys/cand precedes any write (in-place use)
 
-  // ---- range of the keys (HIST: every key; the bins of the full range are
-  // the top 11 bits, which is what the given histogram counts)
+  // ---- range of the keys
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  uint32_t given = 0;  // this thread's two bins of the given histogram
-  if (HIST) {
-    lo = 0u;
-    hi = 0xFFFFFFFFu;
-    const int32_t* hrow = sel_out + (long long)p * sel_stride;
-    given = (uint32_t)hrow[tid] | ((uint32_t)hrow[tid + kTopkThreads] << 16);  // counts < 2^16: n <= 32768
-  } else {
 #pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      lo = min(lo, u[i] ? u[i] : 0xFFFFFFFFu);
-      hi = max(hi, u[i]);
-    }
-    block_minmax(lo, hi, sh);
+  for (int i = 0; i < ITEMS; ++i) {
+    lo = min(lo, u[i] ? u[i] : 0xFFFFFFFFu);
+    hi = max(hi, u[i]);
   }
-  __syncthreads();  // (HIST) the histogram is read before any output is written
+  block_minmax(lo, hi, sh);
 
   uint32_t T = lo;
   int rem = K;       // rank sought among the keys in [lo, hi]
+  int eqc = -1;      // keys equal to T once known (-1: rank them)
+  int nrange = n;    // keys in [lo, hi]
   for (int level = 0; level < 5; ++level) {
     if (lo == hi) {  // every key left is T
       T = lo;
+      eqc = nrange;
       break;
     }
-    const bool given_level = HIST && level == 0;
     const float flo = key_value(lo), fhi = key_value(hi);
     const float fscale = (float)kBins / (fhi - flo);
-    const bool by_value = !given_level && level == 0 && fscale < INFINITY && fscale > 0.0f;
-    // (HIST, level 0: hi - lo = 2^32 - 1, so the shift is 21: the top 11 bits)
+    const bool by_value = level == 0 && fscale < INFINITY && fscale > 0.0f;
     const int shift = max(0, 32 - __clz((int)(hi - lo)) - 11);
     if (tid == 0) sh.ncand = 0;
-    // keys in range: u - lo <= span (lo >= 1 excludes u = 0; with the given
-    // level, lo = 0 and the items past n, u = 0, are excluded by hand)
+    // keys in range: u - lo <= span (lo >= 1 excludes u = 0)
     const uint32_t span = hi - lo;
-    if (given_level) {
-      sh.hist[tid] = given & 0xFFFFu;
-      sh.hist[tid + kTopkThreads] = given >> 16;
-      __syncthreads();
-    } else {
-      for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
-      __syncthreads();
+    for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
+    __syncthreads();
 #pragma unroll
-      for (int i = 0; i < ITEMS; ++i)
-        if (u[i] - lo <= span) atomicAdd(&sh.hist[level_bin(u[i], lo, by_value, flo, fscale, shift)], 1u);
-      __syncthreads();
-    }
+    for (int i = 0; i < ITEMS; ++i)
+      if (u[i] - lo <= span) atomicAdd(&sh.hist[level_bin(u[i], lo, by_value, flo, fscale, shift)], 1u);
+    __syncthreads();
     // bins from the top: thread t covers bins kBins-1-2t and kBins-2-2t
     const int b0 = kBins - 1 - 2 * tid, b1 = b0 - 1;
     const int c0 = (int)sh.hist[b0], c1 = (int)sh.hist[b1];
@@ -312,8 +305,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
       // ---- the bin's keys into LDS, exact select among them
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i)
-        if (u[i] - lo2 <= span && (!given_level || u[i] != 0u) &&
-            level_bin(u[i], lo2, by_value, flo2, fscale2, shift) == bs)
+        if (u[i] - lo2 <= span && level_bin(u[i], lo2, by_value, flo2, fscale2, shift) == bs)
           sh.cu[atomicAdd(&sh.ncand, 1)] = u[i];
       __syncthreads();
       const int nc = sh.ncand;
@@ -321,15 +313,15 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
       const uint64_t cm = (tid < nc ? 1ull : 0ull) | (tid + kTopkThreads < nc ? 2ull : 0ull);
       const int rb = rem;
       __syncthreads();
-      radix_find<2>(cv, cm, rb, sh, T, rem);
+      radix_find<2>(cv, cm, rb, 0, 0u, sh, T, rem, eqc);
       break;
     }
+    nrange = cnt;
     // ---- narrow the range to the bin's keys
     uint32_t nlo = 0xFFFFFFFFu, nhi = 0u;
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
-      if (u[i] - lo2 <= span && (!given_level || u[i] != 0u) &&
-          level_bin(u[i], lo2, by_value, flo2, fscale2, shift) == bs) {
+      if (u[i] - lo2 <= span && level_bin(u[i], lo2, by_value, flo2, fscale2, shift) == bs) {
         nlo = min(nlo, u[i]);
         nhi = max(nhi, u[i]);
       }
@@ -346,14 +338,18 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
     if (u[i] == T) eq |= 1ull << i;
     if (u[i] > T) take |= 1ull << i;
   }
-  row_counts<ITEMS>(eq, sh.wtab, sh.rowoff);
+  if (eqc == rem) {
+    take |= eq;  // every key equal to T is taken: no ranking among them
+  } else {
+    row_counts<ITEMS>(eq, sh.wtab, sh.rowoff);
 #pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const uint64_t m = __ballot((eq >> i) & 1);
-    const int rk = sh.rowoff[i] + sh.wtab[wv][i] + __popcll(m & below);
-    if (((eq >> i) & 1) && rk < rem) take |= 1ull << i;
+    for (int i = 0; i < ITEMS; ++i) {
+      const uint64_t m = __ballot((eq >> i) & 1);
+      const int rk = sh.rowoff[i] + sh.wtab[wv][i] + __popcll(m & below);
+      if (((eq >> i) & 1) && rk < rem) take |= 1ull << i;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   row_counts<ITEMS>(take, sh.wtab, sh.rowoff);
   int32_t* so = sel_out + (long long)p * sel_stride;
   float* ko = keys_out ? keys_out + (long long)p * keys_out_stride : nullptr;
@@ -370,6 +366,158 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
       if (ko) ko[rk] = key_value(u[i]);
     }
   }
+}
+
+// Top-K given the first histogram level (a decode step's loop 2: loop 1
+// leaves each head's histogram of its logits by the top 11 order-key bits in
+// the first kBins entries of the head's selection row).  Thread t holds the
+// keys of positions 32t .. 32t+31, so positions ascend with (thread, item)
+// and every rank in position order is one block-wide prefix sum plus a
+// popcount inside the thread.  The histogram gives the threshold bin b*;
+// keys above it are taken, and the keys in it (their number is the bin's
+// count, at most kCandCap here) are compacted into LDS in position order,
+// where a radix select over their low 21 bits finds T and how many keys equal
+// to T are needed; equal keys are taken in position order.  A bin of more than
+// kCandCap keys takes a radix select over all the keys instead.  Output:
+// the selected positions ascending and, if keys_out is set, their keys in the
+// same order (keys and keys_out, histogram and sel_out may be the same rows:
+// every read precedes the first barrier, every write follows it).
+__global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, long long key_stride, int n, int K,
+                                                          int32_t* sel_out, long long sel_stride, float* keys_out,
+                                                          long long keys_out_stride) {
+  constexpr int NI = 32;
+  static_assert(kBins == kHistBins && NI * kTopkThreads == 32768, "one problem of at most 32768 keys");
+  __shared__ TopkShared sh;
+  __shared__ uint8_t ctake[kCandCap];
+  const int p = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* kp = keys + (long long)p * key_stride;
+  const int32_t* hrow = sel_out + (long long)p * sel_stride;
+  const int pos0 = tid * NI;
+  if (tid == 0) {  // (a histogram without the K-th key leaves these: every key is then a candidate)
+    sh.bstar = 0;
+    sh.rem = K;
+    sh.cnt = n;
+  }
+  // the given bins, from the top: thread t has kBins-1-2t and kBins-2-2t
+  const int c0 = hrow[kBins - 1 - 2 * tid], c1 = hrow[kBins - 2 - 2 * tid];
+  uint32_t u[NI];  // order keys; 0 past n (no key maps to 0)
+  if (((key_stride & 3) == 0) && ((reinterpret_cast<uintptr_t>(keys) & 15) == 0) && pos0 + NI <= n) {
+    const float4* k4 = (const float4*)(kp + pos0);
+#pragma unroll
+    for (int k = 0; k < NI / 4; ++k) {
+      const float4 v = k4[k];
+      u[4 * k] = order_key(v.x);
+      u[4 * k + 1] = order_key(v.y);
+      u[4 * k + 2] = order_key(v.z);
+      u[4 * k + 3] = order_key(v.w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const float v = kp[min(pos0 + i, n - 1)];
+      u[i] = pos0 + i < n ? order_key(v) : 0u;
+    }
+  }
+  // threshold bin: the scan's first barrier follows every read of the rows
+  const int incl = block_incl_scan(c0 + c1, sh.wsum);
+  const int excl = incl - c0 - c1;
+  if (excl < K && excl + c0 >= K) {
+    sh.bstar = kBins - 1 - 2 * tid;
+    sh.rem = K - excl;
+    sh.cnt = c0;
+  } else if (excl + c0 < K && incl >= K) {
+    sh.bstar = kBins - 2 - 2 * tid;
+    sh.rem = K - excl - c0;
+    sh.cnt = c1;
+  }
+  __syncthreads();
+  const uint32_t bs = (uint32_t)sh.bstar;
+  int rem = sh.rem;
+  uint32_t above = 0, cand = 0;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const uint32_t bn = u[i] >> (32 - kHistBits);
+    if (u[i] != 0u && bn > bs) above |= 1u << i;
+    if (u[i] != 0u && bn == bs) cand |= 1u << i;
+  }
+  const int nct = __popc(cand);
+  const int cincl = block_incl_scan(nct, sh.wsum);
+  if (tid == kTopkThreads - 1) sh.ncand = cincl;
+  __syncthreads();
+  const int ncand = sh.ncand;
+  uint32_t T;
+  int eqc;
+  uint32_t take = above;
+  if (ncand <= kCandCap) {
+    // ---- the bin's keys into LDS in position order, exact select among them
+    int slot = cincl - nct;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      if ((cand >> i) & 1) sh.cu[slot++] = u[i];
+    __syncthreads();
+    const uint32_t cv[2] = {tid < ncand ? sh.cu[tid] : 0u, tid + kTopkThreads < ncand ? sh.cu[tid + kTopkThreads] : 0u};
+    const uint64_t cm = (tid < ncand ? 1ull : 0ull) | (tid + kTopkThreads < ncand ? 2ull : 0ull);
+    const int rb = rem;
+    // the bin's keys share their top kHistBits bits: the passes start at the second digit
+    radix_find<2>(cv, cm, rb, 1, bs << (32 - kHistBits), sh, T, rem, eqc);
+    // which slots are taken: keys above T, and the first rem keys equal to T
+    const int s0 = 2 * tid, s1 = 2 * tid + 1;
+    const uint32_t k0 = s0 < ncand ? sh.cu[s0] : 0u, k1 = s1 < ncand ? sh.cu[s1] : 0u;
+    const int e0 = k0 == T, e1 = k1 == T;   // k = 0 (no slot) never equals T >= 1
+    int ee = 0;
+    if (eqc != rem) ee = block_incl_scan(e0 + e1, sh.wsum) - e0 - e1;
+    if (s0 < ncand) ctake[s0] = k0 > T || (e0 && (eqc == rem || ee < rem));
+    if (s1 < ncand) ctake[s1] = k1 > T || (e1 && (eqc == rem || ee + e0 < rem));
+    __syncthreads();
+    slot = cincl - nct;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      if ((cand >> i) & 1) {
+        if (ctake[slot]) take |= 1u << i;
+        ++slot;
+      }
+  } else {
+    // ---- a crowded bin: radix select over every key
+    uint64_t vm = 0;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      if (u[i] != 0u) vm |= 1ull << i;
+    radix_find<NI>(u, vm, K, 0, 0u, sh, T, rem, eqc);
+    uint32_t eq = 0;
+    take = 0;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (u[i] > T) take |= 1u << i;
+      if (u[i] == T) eq |= 1u << i;
+    }
+    if (eqc == rem) {
+      take |= eq;
+    } else {
+      const int ne = __popc(eq);
+      int rk = block_incl_scan(ne, sh.wsum) - ne;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        if ((eq >> i) & 1) {
+          if (rk < rem) take |= 1u << i;
+          ++rk;
+        }
+    }
+  }
+  // ---- output in position order
+  const int ntk = __popc(take);
+  int rk = block_incl_scan(ntk, sh.wsum) - ntk;
+  int32_t* so = sel_out + (long long)p * sel_stride;
+  float* ko = keys_out ? keys_out + (long long)p * keys_out_stride : nullptr;
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    if ((take >> i) & 1) {
+      if (rk < K) {
+        so[rk] = pos0 + i;
+        if (ko) ko[rk] = key_value(u[i]);
+      }
+      ++rk;
+    }
 }
 
 __global__ void k_copy_sel(const int32_t* __restrict__ cand, int P, int K, int32_t* __restrict__ sel,
@@ -395,21 +543,21 @@ hipError_t launch_topk(const float* keys, long long key_stride, const int32_t* c
   const int items = (n + kTopkThreads - 1) / kTopkThreads;
   dim3 grid(P), block(kTopkThreads);
   if (given_hist) {
-    FL_LAUNCH((k_topk<32, false, true>), grid, block, 0, st, keys, key_stride, cand, cand_stride, n, K, sel_out,
-              sel_stride, keys_out, keys_out_stride);
+    FL_LAUNCH(k_topk_hist, grid, block, 0, st, keys, key_stride, n, K, sel_out, sel_stride, keys_out,
+              keys_out_stride);
     return hipGetLastError();
   }
 #define FL_TOPK(IT)                                                                                             \
   do {                                                                                                          \
     if (cand) {                                                                                                 \
       const int lds = (IT) * kTopkThreads * (int)sizeof(int32_t);                                               \
-      static const hipError_t attr = hipFuncSetAttribute((const void*)k_topk<IT, true, false>,                  \
+      static const hipError_t attr = hipFuncSetAttribute((const void*)k_topk<IT, true>,                  \
                                                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);      \
       if (attr != hipSuccess) return attr;                                                                      \
-      FL_LAUNCH((k_topk<IT, true, false>), grid, block, lds, st, keys, key_stride, cand, cand_stride, n, K,     \
+      FL_LAUNCH((k_topk<IT, true>), grid, block, lds, st, keys, key_stride, cand, cand_stride, n, K,     \
                 sel_out, sel_stride, keys_out, keys_out_stride);                                                \
     } else {                                                                                                    \
-      FL_LAUNCH((k_topk<IT, false, false>), grid, block, 0, st, keys, key_stride, cand, cand_stride, n, K,      \
+      FL_LAUNCH((k_topk<IT, false>), grid, block, 0, st, keys, key_stride, cand, cand_stride, n, K,      \
                 sel_out, sel_stride, keys_out, keys_out_stride);                                                \
     }                                                                                                           \
   } while (0)
