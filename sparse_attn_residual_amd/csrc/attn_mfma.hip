@@ -230,13 +230,6 @@ __device__ inline void dma_tile(__amdgpu_buffer_rsrc_t rs, int off, uint8_t* lds
   dma_img<NW, kImgChunks>(rs, off, lds);
 }
 
-// Workgroup barrier for the tile ring: the wave's LDS reads have returned
-// (lgkmcnt 0) and the compiler may not move memory operations across it, but
-// unlike __syncthreads it does not drain the wave's in-flight tile copies.
-__device__ inline void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt unconstrained
-  asm volatile("s_barrier" ::: "memory");
-}
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // the wave are outstanding (expcnt and lgkmcnt left unconstrained).

@@ -83,6 +83,15 @@ __device__ inline uint16_t f32_to_bf16(float x) {
 }
 __device__ inline float round_bf16(float x) { return bf16_to_f32(f32_to_bf16(x)); }
 
+// Workgroup barrier for data exchanged through LDS only: the wave's LDS
+// operations have completed (lgkmcnt 0) and the compiler may not move memory
+// operations across it, but unlike __syncthreads (whose release fence waits
+// for every outstanding memory operation) it leaves the wave's global loads
+// and global->LDS copies in flight.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+  asm volatile("s_barrier" ::: "memory");
+}
 // Order-preserving uint32 key of a float (larger float, larger key; -0 ranks
 // as +0; no float maps to 0).
 __device__ inline uint32_t order_key(float f) {

@@ -90,9 +90,9 @@ __device__ inline int block_incl_scan(int x, int* wsum) {
     if (lane >= o) x += y;
   }
   if (lane == kWave - 1) wsum[wv] = x;
-  __syncthreads();
+  lds_barrier();
   for (int w = 0; w < wv; ++w) x += wsum[w];
-  __syncthreads();
+  lds_barrier();
   return x;
 }
 
@@ -373,121 +373,139 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
 // the first kBins entries of the head's selection row).  Thread t holds the
 // keys of positions 32t .. 32t+31, so positions ascend with (thread, item)
 // and every rank in position order is one block-wide prefix sum plus a
-// popcount inside the thread.  The histogram gives the threshold bin b*;
-// keys above it are taken, and the keys in it (their number is the bin's
-// count, at most kCandCap here) are compacted into LDS in position order,
-// where a radix select over their low 21 bits finds T and how many keys equal
-// to T are needed; equal keys are taken in position order.  A bin of more than
-// kCandCap keys takes a radix select over all the keys instead.  Output:
-// the selected positions ascending and, if keys_out is set, their keys in the
-// same order (keys and keys_out, histogram and sel_out may be the same rows:
-// every read precedes the first barrier, every write follows it).
-__global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, long long key_stride, int n, int K,
-                                                          int32_t* sel_out, long long sel_stride, float* keys_out,
-                                                          long long keys_out_stride) {
-  constexpr int NI = 32;
-  static_assert(kBins == kHistBins && NI * kTopkThreads == 32768, "one problem of at most 32768 keys");
+// popcount inside the thread.  The histogram gives the bin of the K-th
+// largest key and its rank there; two more histogram levels over the next 11
+// and 10 bits of the keys still in the bin (LDS atomics of those keys only)
+// give the K-th largest key T itself and how many keys equal to T are needed.
+// Every key above T is taken, and the keys equal to T in position order.
+// Output: the selected positions ascending and, if keys_out is set, their
+// keys in the same order (keys and keys_out, histogram and sel_out may be the
+// same rows: a problem's reads all precede the barrier after which its
+// writes begin).
+// Persistent: one block per CU walks problems blockIdx.x, + gridDim.x, ...;
+// the next problem's keys are copied into LDS (direct global->LDS loads,
+// 64 keys per load instruction, a padding word after every 64 so that the
+// 32-key runs of the threads fall on distinct banks) while this one is
+// worked on from registers (from after this problem's histogram levels on).
+// Barriers inside a problem exchange LDS data only and leave that copy in
+// flight; the wait for it comes at the top of the next problem.
+constexpr int kTkRun = 32;                       // keys per thread
+constexpr int kTkKeys = kTkRun * kTopkThreads;   // 32768
+constexpr int kTkStage = kTkKeys / 64 * 65;      // staged words (padded)
+constexpr int kTopkHistBlocks = 256;             // MI355X: one per CU
+
+__global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, long long key_stride, int P, int n,
+                                                          int K, int32_t* sel_out, long long sel_stride,
+                                                          float* keys_out, long long keys_out_stride) {
+  constexpr int NI = kTkRun;
+  static_assert(kBins == kHistBins, "the given histogram is the first level");
   __shared__ TopkShared sh;
-  __shared__ uint8_t ctake[kCandCap];
-  const int p = blockIdx.x;
+  __shared__ float stage[kTkStage];
   const int tid = threadIdx.x;
-  const float* kp = keys + (long long)p * key_stride;
-  const int32_t* hrow = sel_out + (long long)p * sel_stride;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
   const int pos0 = tid * NI;
-  if (tid == 0) {  // (a histogram without the K-th key leaves these: every key is then a candidate)
-    sh.bstar = 0;
-    sh.rem = K;
-    sh.cnt = n;
+
+  // copy of problem q's keys into the stage: wave w moves the 64-key chunks
+  // w, w + 16, ...; keys past n read as 0 (the resource ends at n)
+  auto stage_keys = [&](int q) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(keys + (long long)q * key_stride), (short)0, n * 4, 0x00020000);
+    for (int ch = wv; ch < kTkKeys / 64; ch += kTopkWaves)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + ch * 65), 4,
+                                               ch * 256 + lane * 4, 0, 0, 0);
+  };
+  int p = blockIdx.x;
+  if (p >= P) return;
+  stage_keys(p);
+  int c0, c1;  // the given bins, from the top: thread t has kBins-1-2t and kBins-2-2t
+  {
+    const int32_t* hrow = sel_out + (long long)p * sel_stride;
+    c0 = hrow[kBins - 1 - 2 * tid];
+    c1 = hrow[kBins - 2 - 2 * tid];
   }
-  // the given bins, from the top: thread t has kBins-1-2t and kBins-2-2t
-  const int c0 = hrow[kBins - 1 - 2 * tid], c1 = hrow[kBins - 2 - 2 * tid];
-  uint32_t u[NI];  // order keys; 0 past n (no key maps to 0)
-  if (((key_stride & 3) == 0) && ((reinterpret_cast<uintptr_t>(keys) & 15) == 0) && pos0 + NI <= n) {
-    const float4* k4 = (const float4*)(kp + pos0);
-#pragma unroll
-    for (int k = 0; k < NI / 4; ++k) {
-      const float4 v = k4[k];
-      u[4 * k] = order_key(v.x);
-      u[4 * k + 1] = order_key(v.y);
-      u[4 * k + 2] = order_key(v.z);
-      u[4 * k + 3] = order_key(v.w);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const float v = kp[min(pos0 + i, n - 1)];
-      u[i] = pos0 + i < n ? order_key(v) : 0u;
-    }
-  }
-  // threshold bin: the scan's first barrier follows every read of the rows
-  const int incl = block_incl_scan(c0 + c1, sh.wsum);
-  const int excl = incl - c0 - c1;
-  if (excl < K && excl + c0 >= K) {
-    sh.bstar = kBins - 1 - 2 * tid;
-    sh.rem = K - excl;
-    sh.cnt = c0;
-  } else if (excl + c0 < K && incl >= K) {
-    sh.bstar = kBins - 2 - 2 * tid;
-    sh.rem = K - excl - c0;
-    sh.cnt = c1;
-  }
-  __syncthreads();
-  const uint32_t bs = (uint32_t)sh.bstar;
-  int rem = sh.rem;
-  uint32_t above = 0, cand = 0;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const uint32_t bn = u[i] >> (32 - kHistBits);
-    if (u[i] != 0u && bn > bs) above |= 1u << i;
-    if (u[i] != 0u && bn == bs) cand |= 1u << i;
-  }
-  const int nct = __popc(cand);
-  const int cincl = block_incl_scan(nct, sh.wsum);
-  if (tid == kTopkThreads - 1) sh.ncand = cincl;
-  __syncthreads();
-  const int ncand = sh.ncand;
-  uint32_t T;
-  int eqc;
-  uint32_t take = above;
-  if (ncand <= kCandCap) {
-    // ---- the bin's keys into LDS in position order, exact select among them
-    int slot = cincl - nct;
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      if ((cand >> i) & 1) sh.cu[slot++] = u[i];
+  for (; p < P; p += gridDim.x) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies and loads have landed
     __syncthreads();
-    const uint32_t cv[2] = {tid < ncand ? sh.cu[tid] : 0u, tid + kTopkThreads < ncand ? sh.cu[tid + kTopkThreads] : 0u};
-    const uint64_t cm = (tid < ncand ? 1ull : 0ull) | (tid + kTopkThreads < ncand ? 2ull : 0ull);
-    const int rb = rem;
-    // the bin's keys share their top kHistBits bits: the passes start at the second digit
-    radix_find<2>(cv, cm, rb, 1, bs << (32 - kHistBits), sh, T, rem, eqc);
-    // which slots are taken: keys above T, and the first rem keys equal to T
-    const int s0 = 2 * tid, s1 = 2 * tid + 1;
-    const uint32_t k0 = s0 < ncand ? sh.cu[s0] : 0u, k1 = s1 < ncand ? sh.cu[s1] : 0u;
-    const int e0 = k0 == T, e1 = k1 == T;   // k = 0 (no slot) never equals T >= 1
-    int ee = 0;
-    if (eqc != rem) ee = block_incl_scan(e0 + e1, sh.wsum) - e0 - e1;
-    if (s0 < ncand) ctake[s0] = k0 > T || (e0 && (eqc == rem || ee < rem));
-    if (s1 < ncand) ctake[s1] = k1 > T || (e1 && (eqc == rem || ee + e0 < rem));
-    __syncthreads();
-    slot = cincl - nct;
+    uint32_t u[NI];  // order keys; 0 past n (no key maps to 0)
+    {
+      const float* run = stage + (pos0 >> 6) * 65 + (pos0 & 63);
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      if ((cand >> i) & 1) {
-        if (ctake[slot]) take |= 1u << i;
-        ++slot;
+      for (int i = 0; i < NI; ++i) u[i] = pos0 + i < n ? order_key(run[i]) : 0u;
+    }
+    if (tid == 0) {  // (a histogram without the K-th key leaves these: every key is then in the bin)
+      sh.bstar = 0;
+      sh.rem = K;
+      sh.cnt = n;
+    }
+    // threshold bin (the scan's barriers also end every read of the stage)
+    {
+      const int incl = block_incl_scan(c0 + c1, sh.wsum);
+      const int excl = incl - c0 - c1;
+      if (excl < K && excl + c0 >= K) {
+        sh.bstar = kBins - 1 - 2 * tid;
+        sh.rem = K - excl;
+        sh.cnt = c0;
+      } else if (excl + c0 < K && incl >= K) {
+        sh.bstar = kBins - 2 - 2 * tid;
+        sh.rem = K - excl - c0;
+        sh.cnt = c1;
       }
-  } else {
-    // ---- a crowded bin: radix select over every key
-    uint64_t vm = 0;
+      lds_barrier();
+    }
+    // the threshold's leading bits: the keys with u >> shift == prefix hold it
+    uint32_t prefix = (uint32_t)sh.bstar;
+    int shift = 32 - kHistBits;
+    int rem = sh.rem, cnt = sh.cnt;
+    // The bin is split by the next 11, then 10 bits of its keys, counted
+    // from the registers (LDS atomics of the keys still in the bin only),
+    // down to one value: the threshold T, with cnt keys equal to it.
+    while (shift > 0) {
+      const int nb = shift > 11 ? 11 : shift;
+      for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
+      lds_barrier();
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      if (u[i] != 0u) vm |= 1ull << i;
-    radix_find<NI>(u, vm, K, 0, 0u, sh, T, rem, eqc);
-    uint32_t eq = 0;
-    take = 0;
+      for (int i = 0; i < NI; ++i)
+        if (u[i] != 0u && (u[i] >> shift) == prefix)
+          atomicAdd(&sh.hist[(u[i] >> (shift - nb)) & ((1u << nb) - 1u)], 1u);
+      lds_barrier();
+      const int b0 = kBins - 1 - 2 * tid, b1 = b0 - 1;
+      const int h0 = (int)sh.hist[b0], h1 = (int)sh.hist[b1];
+      const int incl = block_incl_scan(h0 + h1, sh.wsum);
+      const int excl = incl - h0 - h1;
+      if (excl < rem && excl + h0 >= rem) {
+        sh.bstar = b0;
+        sh.rem = rem - excl;
+        sh.cnt = h0;
+      } else if (excl + h0 < rem && incl >= rem) {
+        sh.bstar = b1;
+        sh.rem = rem - excl - h0;
+        sh.cnt = h1;
+      }
+      lds_barrier();
+      prefix = (prefix << nb) | (uint32_t)sh.bstar;
+      shift -= nb;
+      rem = sh.rem;
+      cnt = sh.cnt;
+      lds_barrier();
+    }
+    const uint32_t T = prefix;
+    const int eqc = cnt;
+    // The next problem's keys into the stage and its bins into registers.
+    // Issued after the histogram levels: the compiler cannot tell their LDS
+    // atomics from the copy's destination and would wait for the copy before
+    // each of them.
+    const int pn = p + gridDim.x;
+    if (pn < P) {
+      stage_keys(pn);
+      const int32_t* hrow = sel_out + (long long)pn * sel_stride;
+      c0 = hrow[kBins - 1 - 2 * tid];
+      c1 = hrow[kBins - 2 - 2 * tid];
+    }
+    // take every key above T and the first rem keys equal to T
+    uint32_t take = 0, eq = 0;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
+    for (int i = 0; i < NI; ++i) {  // T >= 1: items past n never match
       if (u[i] > T) take |= 1u << i;
       if (u[i] == T) eq |= 1u << i;
     }
@@ -503,21 +521,21 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, l
           ++rk;
         }
     }
-  }
-  // ---- output in position order
-  const int ntk = __popc(take);
-  int rk = block_incl_scan(ntk, sh.wsum) - ntk;
-  int32_t* so = sel_out + (long long)p * sel_stride;
-  float* ko = keys_out ? keys_out + (long long)p * keys_out_stride : nullptr;
+    // ---- output in position order
+    const int ntk = __popc(take);
+    int rk = block_incl_scan(ntk, sh.wsum) - ntk;
+    int32_t* so = sel_out + (long long)p * sel_stride;
+    float* ko = keys_out ? keys_out + (long long)p * keys_out_stride : nullptr;
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
-    if ((take >> i) & 1) {
-      if (rk < K) {
-        so[rk] = pos0 + i;
-        if (ko) ko[rk] = key_value(u[i]);
+    for (int i = 0; i < NI; ++i)
+      if ((take >> i) & 1) {
+        if (rk < K) {
+          so[rk] = pos0 + i;
+          if (ko) ko[rk] = key_value(u[i]);
+        }
+        ++rk;
       }
-      ++rk;
-    }
+  }
 }
 
 __global__ void k_copy_sel(const int32_t* __restrict__ cand, int P, int K, int32_t* __restrict__ sel,
@@ -543,7 +561,9 @@ hipError_t launch_topk(const float* keys, long long key_stride, const int32_t* c
   const int items = (n + kTopkThreads - 1) / kTopkThreads;
   dim3 grid(P), block(kTopkThreads);
   if (given_hist) {
-    FL_LAUNCH(k_topk_hist, grid, block, 0, st, keys, key_stride, n, K, sel_out, sel_stride, keys_out,
+    // persistent blocks, one per CU (the key stage takes most of the LDS)
+    const int nb = P < kTopkHistBlocks ? P : kTopkHistBlocks;
+    FL_LAUNCH(k_topk_hist, dim3(nb), block, 0, st, keys, key_stride, P, n, K, sel_out, sel_stride, keys_out,
               keys_out_stride);
     return hipGetLastError();
   }
