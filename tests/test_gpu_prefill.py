@@ -386,16 +386,29 @@ def test_prefill_mixed_combine(dtype, d, budgets):
                         e = np.linalg.norm((g[key][b, h] - ref) / w[:, None])
                         assert e <= tol * np.linalg.norm(st.O), (b, h, r + 1, key, e / np.linalg.norm(st.O))
                     assert np.max(np.abs(g["M"][b, h] - st.M) / w) <= 4 * tol, (b, h, r + 1, "M")
+                    # Rows whose combine never divided by D < 1 carry no
+                    # amplification: there the plain bar holds, over the rows
+                    # and per row (floored at the median row norm).
+                    good = rr[w[rr] == 1.0]
+                    if good.size:
+                        Og, Oo = g["O"][b, h][good], st.O[good]
+                        frob = np.linalg.norm(Og - Oo) / np.linalg.norm(Oo)
+                        en, on = _row_errors(Og, Oo)
+                        row = en / np.maximum(on, np.median(on))
+                        print(f"[parity] mixed b={b} h={h} loop={r + 1} unamplified rows={good.size}/{rr.size} "
+                              f"O_frob={frob:.2e} O_row_max={row.max():.2e}", flush=True)
+                        assert frob <= tol and row.max() <= tol, (b, h, r + 1, "O unamplified", frob, row.max())
                     fin = np.isfinite(st.lse)
                     assert np.array_equal(fin, np.isfinite(g["lse"][b, h]))
-                    assert np.max(np.abs(g["lse"][b, h][fin] - st.lse[fin])) <= \
-                        8 * tol * max(1, np.max(np.abs(st.lse[fin])))
+                    # lse is loop r's log-sum-exp over the selection: no division by D
+                    assert np.max(np.abs(g["lse"][b, h][fin] - st.lse[fin])) <= tol, (b, h, r + 1, "lse")
                 want, got = o["lsel"][r], g["lsel"][b, h][rr]
                 fin = np.isfinite(want)
                 assert np.array_equal(fin, np.isfinite(got)), (b, h, r + 1)
                 err = np.max(np.abs(got[fin] - want[fin])) if fin.any() else 0.0
-                assert err <= (tol if f32 else 8 * tol) * max(1.0, np.max(np.abs(want[fin]), initial=0.0)), \
-                    (b, h, r + 1, "lsel", err)
+                # (fp32: relative to the log-sum-exp's size, the precision a float keeps)
+                lim = tol * max(1.0, np.max(np.abs(want[fin]), initial=0.0)) if f32 else tol
+                assert err <= lim, (b, h, r + 1, "lsel", err)
 
 
 @pytest.mark.parametrize("dtype,d,H,Hkv", [("f32", 64, 4, 2), ("bf16", 128, 6, 2), ("bf16", 128, 4, 1)])
