@@ -248,6 +248,19 @@ def test_prefill_bf16_full_size(cfgid, heads):
     _bf16_case(cfg, heads=heads)
 
 
+@pytest.mark.parametrize("act", [(1, 0.5, 0.1253, 0.125), (1, 0.50025, 0.2505, 0.12525)])
+def test_prefill_split_boundaries(act):
+    """Sparse launches on both sides of the column-split thresholds (16 heads,
+    S = 4096): loops of 2048, 513 and 512 active rows (two splits exactly at
+    their limit, two splits, four exactly at theirs) and of 2049, 1026 and 513
+    (no split one row past the limit, two, two); with a pruning schedule the
+    cached-mass passes take the same launch rule."""
+    cfg = workloads.custom(name="split-bounds", dtype="bf16", B=1, H=16, d=128, S=4096, R=4, act=act, col="0.10",
+                           bits=(8, 4, 4, 2), lognormal=0.5, seed=51)
+    _say("prefill split boundaries", cfg.n, cfg)
+    _bf16_case(cfg, heads=[0, 15], budgets=[409, 300, 200])
+
+
 def test_prefill_bf16_mfma_wide():
     """Enough heads that the twelve-wave (384-row block) kernel runs in the
     dense loop and in loop 2, with ragged row blocks; loops 3 and 4 take the
