@@ -395,30 +395,48 @@ def cpu_baseline(workloads, cfg_id=PREFILL_CFG):
 
 
 def cpu_decode_baseline(workloads, step_bytes):
-    """The oracle's decode step on a few (layer, sequence, head) slices of the
-    48-layer workload (all R loops each; the cache records are built first and
-    not timed), extrapolated to every slice of the step."""
+    """The oracle's decode step (all R loops) on 64 (sequence, head) queries of
+    the 48-layer workload over the cache records of four of its slices (the
+    records are built first and not timed), the problems spread over a pool of
+    worker threads (one BLAS thread each), extrapolated to every slice of the
+    step."""
     import dataclasses
+    from concurrent.futures import ThreadPoolExecutor
     from oracle import decode, quant
+    from threadpoolctl import threadpool_limits
     cfg = workloads.CONFIGS[DECODE_CFG]
-    n = 4
-    small = dataclasses.replace(cfg, name=cfg.name + "-cpu-sample", B=1, H=n, L=1)
+    nrec = 4
+    small = dataclasses.replace(cfg, name=cfg.name + "-cpu-sample", B=1, H=nrec, L=1)
     rows, sl = workloads.gen_batch(small)
-    qs = workloads.decode_queries(small)
-    t = 0.0
-    for h in range(n):
+    recs = []
+    for h in range(nrec):
         s = sl[(0, h)]
-        _, krec = quant.quantize_chain(s.k, s.rows, list(small.bits))
-        _, vrec = quant.quantize_chain(s.v, s.rows, list(small.bits))
+        recs.append((quant.quantize_chain(s.k, s.rows, list(small.bits))[1],
+                     quant.quantize_chain(s.v, s.rows, list(small.bits))[1]))
+    qcfg = dataclasses.replace(cfg, name=cfg.name + "-cpu-queries", B=4, H=16, L=1)
+    qs = workloads.decode_queries(qcfg)
+    probs = [(b, h) for b in range(qcfg.B) for h in range(qcfg.H)]
+    workers = max(1, min(len(probs), len(os.sched_getaffinity(0)), 16))
+
+    def one(bh):
+        b, h = bh
+        krec, vrec = recs[(b * qcfg.H + h) % nrec]
+        decode.decode_slice(krec, vrec, [q[0, b, h] for q in qs], cfg.K)
+
+    with threadpool_limits(1):
         t0 = time.perf_counter()
-        decode.decode_slice(krec, vrec, [q[0, 0, h] for q in qs], small.K)
-        t += time.perf_counter() - t0
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(one, probs))
+        t = time.perf_counter() - t0
     slices = cfg.L * cfg.B * cfg.H
-    step_s = t / n * slices
-    return dict(value=step_bytes / step_s / 1e9, unit="GB/s", kind="oracle", extrapolated=True,
+    step_s = t / len(probs) * slices
+    log(f"cpu oracle decode: {len(probs)} problems in {t:.2f}s on {workers} threads")
+    return dict(value=step_bytes / step_s / 1e9, unit="GB/s", kind="oracle", extrapolated=True, cores=int(workers),
                 ms_per_step=step_s * 1e3,
-                sample=f"{n} of the step's {slices} (layer, sequence, head) slices, all {cfg.R} loops in float64 "
-                       f"({t:.2f}s), extrapolated to the whole step")
+                sample=f"{len(probs)} (sequence, head) decode queries over the cache records of {nrec} of the "
+                       f"step's {slices} (layer, sequence, head) slices, all {cfg.R} loops in float64 ({t:.2f}s on "
+                       f"{workers} worker threads with one BLAS thread each), extrapolated to the whole step",
+                cpu_model=_cpu_model(), blas=_blas())
 
 
 def _cpu_model() -> str:
