@@ -284,6 +284,12 @@ size_t mass_pass_bytes(const fl_cache* c, int r, bool base, int K_prev) {
   if (c->d != 128) return 0;
   return (base ? 0 : tiles_bytes(c, K_prev)) + fl::row_img_bytes(c->B, c->H, c->n[r]);
 }
+// The first-level histogram of the masses the column-mass pass counts for
+// the top-K (head dim 128, where that pass is the MFMA one).
+size_t hist_bytes(const fl_cache* c) {
+  if (c->d != 128) return 0;
+  return align256((size_t)c->B * c->H * fl::kHistBins * sizeof(uint32_t));
+}
 }  // namespace
 
 size_t fl_workspace_bytes(int which, const fl_cache* cache, int r, int K_prev, int K_r) {
@@ -292,11 +298,12 @@ size_t fl_workspace_bytes(int which, const fl_cache* cache, int r, int K_prev, i
   if (which == FL_WS_ATTN && r == 1) return tiles_bytes(cache, cache->S);
   if (K_prev < 0 || K_r < 0) return 0;
   if (which == FL_WS_COLSEL) {
-    // masses, then (in turn) what the mass pass reads and the tiles of the
-    // selected columns the cached-mass pass gathers
+    // masses, their first-level histogram, then (in turn) what the mass
+    // pass reads and the tiles of the selected columns the cached-mass pass
+    // gathers
     if (r > cache->R || r < 2) return 0;
     const bool base = r == 2 && K_prev == cache->S && cache->fmt == FL_FMT_WORKLOAD;
-    return align256((size_t)cache->B * cache->H * (size_t)K_prev * sizeof(float)) +
+    return align256((size_t)cache->B * cache->H * (size_t)K_prev * sizeof(float)) + hist_bytes(cache) +
            std::max(tiles_bytes(cache, K_r), mass_pass_bytes(cache, r, base, K_prev));
   }
   if (which == FL_WS_ATTN) return tiles_bytes(cache, K_r);
@@ -394,12 +401,15 @@ fl_status fl_colsel(const fl_cache* cache, int r, const void* q_prev, fl_dtype d
   const bool need_mass = (prune && !mass_in) || mass_out;
   float* mass = mass_out;
   const size_t mass_ws = align256((size_t)cache->B * cache->H * (size_t)K_prev * sizeof(float));
+  const size_t hist_ws = hist_bytes(cache);
   // what the mass pass reads, then (reusing the space) the tiles of the
   // selected columns the cached-mass pass gathers
   const size_t pass_ws = std::max(prune ? tiles_bytes(cache, K_r) : 0,
                                   need_mass ? mass_pass_bytes(cache, r, r == 2 && !cand && geo.fmt == FL_FMT_WORKLOAD,
                                                               K_prev) : 0);
-  const size_t need = (need_mass && !mass_out ? mass_ws : 0) + pass_ws;
+  // the masses' first-level histogram, when the top-K can start from it
+  const bool use_hist = prune && !mass_in && !cand && hist_ws > 0;
+  const size_t need = (need_mass && !mass_out ? mass_ws : 0) + (use_hist ? hist_ws : 0) + pass_ws;
   if (need > 0) {
     if (!ws || ws_bytes < need)
       return fail(FL_EINVAL, "%s: workspace of %zu bytes needed (got %zu)", fn, need, ws ? ws_bytes : (size_t)0);
@@ -408,7 +418,12 @@ fl_status fl_colsel(const fl_cache* cache, int r, const void* q_prev, fl_dtype d
   uint8_t* tiles_ws = (uint8_t*)ws;
   if (need_mass && !mass_out) {
     mass = (float*)ws;
-    tiles_ws = (uint8_t*)ws + mass_ws;
+    tiles_ws += mass_ws;
+  }
+  uint32_t* hist = nullptr;
+  if (use_hist) {
+    hist = (uint32_t*)tiles_ws;
+    tiles_ws += hist_ws;
   }
   if (prune && K_prev > kTopkMax)
     return fail(FL_EUNSUPPORTED, "%s: %d candidates (at most %d)", fn, K_prev, kTopkMax);
@@ -433,8 +448,9 @@ fl_status fl_colsel(const fl_cache* cache, int r, const void* q_prev, fl_dtype d
   a.O = state->O; a.U = state->U; a.M = state->M; a.lse = state->lse;
   a.lsel = state->lsel;
   hipError_t e;
+  bool hist_built = false;
   if (need_mass) {
-    e = fl::launch_mass(a, cand, K_prev, mass, tiles_ws, st);
+    e = fl::launch_mass(a, cand, K_prev, mass, tiles_ws, st, hist, &hist_built);
     if (e != hipSuccess) return hip_fail(e, fn);
   }
   const int P = cache->B * cache->H;
@@ -449,7 +465,8 @@ fl_status fl_colsel(const fl_cache* cache, int r, const void* q_prev, fl_dtype d
     return FL_OK;
   }
   const float* keys = mass_in ? mass_in : mass;
-  e = fl::launch_topk(keys, K_prev, cand, K_prev, P, K_prev, K_r, sel_out, K_r, nullptr, 0, st);
+  e = fl::launch_topk(keys, K_prev, cand, K_prev, P, K_prev, K_r, sel_out, K_r, nullptr, 0, st,
+                      hist_built ? (const int32_t*)hist : nullptr, fl::kHistBins);
   if (e != hipSuccess) return hip_fail(e, fn);
   a.K = K_r;
   a.sel = sel_out;

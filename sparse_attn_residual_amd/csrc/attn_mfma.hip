@@ -794,8 +794,11 @@ constexpr int kMassAhead = kMassRing - 1;
 static_assert(kRowBytes == kRowImgBytes && kMassRows == 64, "row image size (launch.hpp)");
 
 // One block of 256 threads per row image: four threads per row, 32 dims each.
-__global__ __launch_bounds__(256) void k_build_rows(AttnArgs a, int ntr, uint8_t* __restrict__ out) {
+__global__ __launch_bounds__(256) void k_build_rows(AttnArgs a, int ntr, uint8_t* __restrict__ out,
+                                                   uint32_t* __restrict__ hist, int nhist) {
   const CacheGeo& c = a.c;
+  // the mass histogram the column-mass pass fills starts at zero
+  for (int i = blockIdx.x * 256 + threadIdx.x; hist && i < nhist; i += gridDim.x * 256) hist[i] = 0u;
   const int bh = blockIdx.x / ntr;
   const int tile = blockIdx.x - bh * ntr;
   const int b = bh / c.H;
@@ -846,6 +849,7 @@ struct MassArgs {
   int ntr;
   int ncb;                // column blocks per (b, h)
   float c2;
+  uint32_t* hist;         // [B*H][kHistBins] counts of the masses by order-key bin, or NULL
 };
 
 template <bool BASE, int NW>
@@ -995,7 +999,23 @@ __global__ __launch_bounds__(64 * NW) void k_mass_mfma(MassArgs m) {
     lds_barrier();
   }
   acc += __shfl_xor(acc, 32, 64);
-  if (hf == 0 && jpos != kNoPos) m.mass[(long long)bh * m.K_prev + cidx] = acc;
+  const bool mine = hf == 0 && jpos != kNoPos;
+  if (mine) m.mass[(long long)bh * m.K_prev + cidx] = acc;
+  if (m.hist) {
+    // each column's mass counted once into its head's histogram by the top
+    // kHistBits bits of its order key (the first level of the selection);
+    // lanes with the same bin add together
+    const uint32_t bin = order_key(acc) >> (32 - kHistBits);
+    bool part = mine;
+    while (__builtin_amdgcn_ballot_w64(part)) {
+      const uint64_t pm = __builtin_amdgcn_ballot_w64(part);
+      const int leader = __ffsll((long long)pm) - 1;
+      const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
+      const uint64_t same = __builtin_amdgcn_ballot_w64(part && bin == lb);
+      if (lane == leader) atomicAdd(&m.hist[(long long)bh * kHistBins + lb], (uint32_t)__popcll(same));
+      if (bin == lb) part = false;
+    }
+  }
 }
 
 // ------------------------------------------------------------- host side
@@ -1133,7 +1153,7 @@ static hipError_t launch_mass_one(const MassArgs& m, hipStream_t st) {
 }
 
 hipError_t launch_mass_mfma(const AttnArgs& a, const int32_t* cand, int K_prev, float* mass, uint8_t* ws,
-                            hipStream_t st) {
+                            hipStream_t st, uint32_t* hist, bool* hist_built) {
   MassArgs m{};
   m.a = a;
   m.K_prev = K_prev;
@@ -1153,8 +1173,13 @@ hipError_t launch_mass_mfma(const AttnArgs& a, const int32_t* cand, int K_prev, 
   }
   m.ntr = (a.c.n[a.r] + kMassRows - 1) / kMassRows;
   m.rows = rows;
+  // the histogram is zeroed by the row-image builder, so it is built only
+  // when that runs (no active rows: every mass is 0, nothing to rank by it)
+  m.hist = m.ntr > 0 ? hist : nullptr;
+  if (hist_built) *hist_built = m.hist != nullptr;
   if (m.ntr > 0) {
-    FL_LAUNCH(k_build_rows, dim3((unsigned)(a.c.B * a.c.H * m.ntr)), dim3(256), 0, st, a, m.ntr, rows);
+    FL_LAUNCH(k_build_rows, dim3((unsigned)(a.c.B * a.c.H * m.ntr)), dim3(256), 0, st, a, m.ntr, rows, m.hist,
+              a.c.B * a.c.H * kHistBins);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -702,7 +702,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
     const int32_t* cand = (a.r == 2 && a.K_prev == a.c.T) ? nullptr : a.sel;
     // loop 1 left each head's logit histogram at the front of its selection row
     const bool given = !cand && a.c.S >= kHistBins;
-    e = launch_topk(a.logits, a.c.S, cand, a.c.S, (int)P, a.K_prev, a.K, a.sel, a.c.S, a.logits, a.c.S, st, given);
+    e = launch_topk(a.logits, a.c.S, cand, a.c.S, (int)P, a.K_prev, a.K, a.sel, a.c.S, a.logits, a.c.S, st,
+                    given ? a.sel : nullptr, a.c.S);
     if (e != hipSuccess) return e;
   } else if (a.r == 2) {
     // every position stays selected: sel = 0..T-1 (rows of stride S); the

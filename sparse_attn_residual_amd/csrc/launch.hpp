@@ -41,12 +41,14 @@ hipError_t launch_quant_res(const CacheGeo& c, int r, const void* k, const void*
 // writes sel_out [P][sel_stride] ascending and, if keys_out is set, the keys
 // of the selected entries in the same order.  In place (keys_out == keys,
 // sel_out == cand) is allowed: every block reads its inputs before writing.
-// given_hist: sel_out's rows hold, in their first 2048 entries, each
-// problem's histogram of keys by the top 11 bits of their order keys (cand
-// NULL, n <= 32768, sel_stride >= 2048); the search starts from it.
+// given_hist: rows of hist_stride entries, one per problem, whose first
+// kHistBins entries hold the problem's histogram of keys by the top 11 bits
+// of their order keys (cand NULL, n <= 32768); the search starts from it.
+// It may be sel_out itself (every row read before any is written).
 hipError_t launch_topk(const float* keys, long long key_stride, const int32_t* cand, long long cand_stride,
                        int P, int n, int K, int32_t* sel_out, long long sel_stride, float* keys_out,
-                       long long keys_out_stride, hipStream_t st, bool given_hist = false);
+                       long long keys_out_stride, hipStream_t st, const int32_t* given_hist = nullptr,
+                       long long hist_stride = 0);
 // sel[p][t] = cand ? cand[p][t] : t for t < K
 hipError_t launch_copy_sel(const int32_t* cand, int P, int K, int32_t* sel, hipStream_t st, long long sel_stride = 0);
 
@@ -84,8 +86,10 @@ inline size_t row_img_bytes(int B, int H, int n) { return (size_t)B * H * (size_
 // r-1's probabilities.  ws (head dim 128, bf16): gather_bytes(c, K_prev)
 // bytes when the candidates are gathered (cand != NULL or r > 2), then
 // row_img_bytes(B, H, n_r).
+// hist (or NULL): [B*H][kHistBins] space for the masses' first-level
+// histogram; *hist_built says whether it was filled.
 hipError_t launch_mass(const AttnArgs& a, const int32_t* cand, int K_prev, float* mass, uint8_t* ws,
-                       hipStream_t st);
+                       hipStream_t st, uint32_t* hist = nullptr, bool* hist_built = nullptr);
 
 // ---- next active set: scores [B][n_prev] (relative hidden-state change of
 // the candidates rows_prev, NULL: positions 0..n_prev-1), then the top k of

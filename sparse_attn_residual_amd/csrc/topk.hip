@@ -368,9 +368,10 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
   }
 }
 
-// Top-K given the first histogram level (a decode step's loop 2: loop 1
-// leaves each head's histogram of its logits by the top 11 order-key bits in
-// the first kBins entries of the head's selection row).  Thread t holds the
+// Top-K given the first histogram level: each problem's histogram of its
+// keys by the top 11 order-key bits (a decode step's loop 2: loop 1 leaves it
+// in the first kBins entries of the head's selection row; a prefill
+// selection: the column-mass pass counts each mass it writes).  Thread t holds the
 // keys of positions 32t .. 32t+31, so positions ascend with (thread, item)
 // and every rank in position order is one block-wide prefix sum plus a
 // popcount inside the thread.  The histogram gives the bin of the K-th
@@ -395,8 +396,9 @@ constexpr int kTkStage = kTkKeys / 64 * 65;      // staged words (padded)
 constexpr int kTopkHistBlocks = 256;             // MI355X: one per CU
 
 __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, long long key_stride, int P, int n,
-                                                          int K, int32_t* sel_out, long long sel_stride,
-                                                          float* keys_out, long long keys_out_stride) {
+                                                          int K, const int32_t* hist, long long hist_stride,
+                                                          int32_t* sel_out, long long sel_stride, float* keys_out,
+                                                          long long keys_out_stride) {
   constexpr int NI = kTkRun;
   static_assert(kBins == kHistBins, "the given histogram is the first level");
   __shared__ TopkShared sh;
@@ -420,7 +422,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, l
   stage_keys(p);
   int c0, c1;  // the given bins, from the top: thread t has kBins-1-2t and kBins-2-2t
   {
-    const int32_t* hrow = sel_out + (long long)p * sel_stride;
+    const int32_t* hrow = hist + (long long)p * hist_stride;
     c0 = hrow[kBins - 1 - 2 * tid];
     c1 = hrow[kBins - 2 - 2 * tid];
   }
@@ -498,7 +500,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, l
     const int pn = p + gridDim.x;
     if (pn < P) {
       stage_keys(pn);
-      const int32_t* hrow = sel_out + (long long)pn * sel_stride;
+      const int32_t* hrow = hist + (long long)pn * hist_stride;
       c0 = hrow[kBins - 1 - 2 * tid];
       c1 = hrow[kBins - 2 - 2 * tid];
     }
@@ -555,16 +557,17 @@ hipError_t launch_copy_sel(const int32_t* cand, int P, int K, int32_t* sel, hipS
 
 hipError_t launch_topk(const float* keys, long long key_stride, const int32_t* cand, long long cand_stride, int P,
                        int n, int K, int32_t* sel_out, long long sel_stride, float* keys_out,
-                       long long keys_out_stride, hipStream_t st, bool given_hist) {
+                       long long keys_out_stride, hipStream_t st, const int32_t* given_hist,
+                       long long hist_stride) {
   if (n < 1 || K < 1 || K > n) return hipErrorInvalidValue;
-  if (given_hist && (cand || n > 32768 || sel_stride < kHistBins)) return hipErrorInvalidValue;
+  if (given_hist && (cand || n > 32768 || hist_stride < kHistBins)) return hipErrorInvalidValue;
   const int items = (n + kTopkThreads - 1) / kTopkThreads;
   dim3 grid(P), block(kTopkThreads);
   if (given_hist) {
     // persistent blocks, one per CU (the key stage takes most of the LDS)
     const int nb = P < kTopkHistBlocks ? P : kTopkHistBlocks;
-    FL_LAUNCH(k_topk_hist, dim3(nb), block, 0, st, keys, key_stride, P, n, K, sel_out, sel_stride, keys_out,
-              keys_out_stride);
+    FL_LAUNCH(k_topk_hist, dim3(nb), block, 0, st, keys, key_stride, P, n, K, given_hist, hist_stride, sel_out,
+              sel_stride, keys_out, keys_out_stride);
     return hipGetLastError();
   }
 #define FL_TOPK(IT)                                                                                             \

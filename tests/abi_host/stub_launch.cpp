@@ -30,13 +30,16 @@ hipError_t launch_quant_res(const CacheGeo&, int, const void*, const void*, fl_d
   return counted();
 }
 hipError_t launch_topk(const float*, long long, const int32_t*, long long, int, int, int, int32_t*, long long, float*,
-                       long long, hipStream_t, bool) {
+                       long long, hipStream_t, const int32_t*, long long) {
   return counted();
 }
 hipError_t launch_copy_sel(const int32_t*, int, int, int32_t*, hipStream_t, long long) { return counted(); }
 hipError_t launch_attn(const AttnArgs&, uint8_t*, hipStream_t) { return counted(); }
 hipError_t launch_um(const AttnArgs&, uint8_t*, hipStream_t) { return counted(); }
-hipError_t launch_mass(const AttnArgs&, const int32_t*, int, float*, uint8_t*, hipStream_t) { return counted(); }
+hipError_t launch_mass(const AttnArgs&, const int32_t*, int, float*, uint8_t*, hipStream_t, uint32_t*, bool* built) {
+  if (built) *built = false;
+  return counted();
+}
 hipError_t launch_active(int, int, int, const void*, const void*, fl_dtype, const int32_t*, int, int, int32_t*, float*,
                          hipStream_t) {
   return counted();

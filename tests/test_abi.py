@@ -138,12 +138,13 @@ def test_validation_errors():
                       None, 0, None)
     assert st == EINVAL and "K_prev" in msg
     assert fl.fl_workspace_bytes(fl.FL_WS_COLSEL, _cache(), 2, 64, 10) == 1 * 2 * 64 * 4
-    # head dim 128: masses, then the larger of the mass pass's 64-row images
-    # (18 KiB each) and the cached-mass pass's 64-column tiles (36 KiB each)
-    assert fl.fl_workspace_bytes(fl.FL_WS_COLSEL, c128, 2, 64, 10) == 512 + 2 * 36864
+    # head dim 128: masses, the masses' 2048-bin histogram per head, then the
+    # larger of the mass pass's 64-row images (18 KiB each) and the
+    # cached-mass pass's 64-column tiles (36 KiB each)
+    assert fl.fl_workspace_bytes(fl.FL_WS_COLSEL, c128, 2, 64, 10) == 512 + 2 * 2048 * 4 + 2 * 36864
     c128.n[2] = 64 * 5
     c128.S = c128.n[1] = 64 * 5
-    assert fl.fl_workspace_bytes(fl.FL_WS_COLSEL, c128, 2, 320, 10) == 2 * 320 * 4 + 2 * 5 * 18432
+    assert fl.fl_workspace_bytes(fl.FL_WS_COLSEL, c128, 2, 320, 10) == 2 * 320 * 4 + 2 * 2048 * 4 + 2 * 5 * 18432
     # a pruning selection takes at most 32768 candidates
     big = _cache(S=40000)
     big.n[1], big.n[2] = 40000, 20000
