@@ -140,19 +140,24 @@ def measure_prefill(args, torch, fl, acc, cfg, rows, q, k, v, cache, st, budgets
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
-    # timed region: barrier + synchronize on both sides (one process)
+    # timed region: barrier + synchronize on both sides (one process); the
+    # steps run with no events between their calls
     torch.cuda.synchronize()
-    tm.reset()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     e0.record()
     for _ in range(args.steps):
-        step(True)
+        step(False)
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = e0.elapsed_time(e1) / args.steps
+    # per-call times: as many more steps with events around every call
+    tm.reset()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
     per = tm.mean_ms()
     log(f"prefill K={Ks[1:]}: {ms_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}); per call (ms): "
         + ", ".join(f"{kk}={vv:.3f}" for kk, vv in per.items()))
@@ -245,10 +250,14 @@ def decode_bench(args, torch, fl, workloads, acc, cfg=None, fmt=0):
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        step(True)
+        step(False)
     e1.record()
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / steps
+    # per-loop times: as many more steps with events around every call
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
     per = tm.mean_ms()
     log(f"decode: {ms_step:.3f} ms/step; per loop (ms): " + ", ".join(f"{kk}={vv:.3f}" for kk, vv in per.items()))
     kern = kernel_times(fl, torch, step, 1)
