@@ -395,6 +395,7 @@ constexpr int kTkKeys = kTkRun * kTopkThreads;   // 32768
 constexpr int kTkStage = kTkKeys / 64 * 65;      // staged words (padded)
 constexpr int kTopkHistBlocks = 256;             // MI355X: one per CU
 
+template <bool FULL>
 __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, long long key_stride, int P, int n,
                                                           int K, const int32_t* hist, long long hist_stride,
                                                           int32_t* sel_out, long long sel_stride, float* keys_out,
@@ -429,11 +430,16 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, l
   for (; p < P; p += gridDim.x) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies and loads have landed
     __syncthreads();
+    // the thread's keys in the stage (32 consecutive positions inside one
+    // 65-word chunk) and which of them lie inside the problem
+    const float* run = stage + (pos0 >> 6) * 65 + (pos0 & 63);
+    const int lim = n - pos0;
+    const uint32_t valid = FULL || lim >= NI ? 0xffffffffu : (lim <= 0 ? 0u : (1u << lim) - 1u);
     uint32_t u[NI];  // order keys; 0 past n (no key maps to 0)
-    {
-      const float* run = stage + (pos0 >> 6) * 65 + (pos0 & 63);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) u[i] = pos0 + i < n ? order_key(run[i]) : 0u;
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t k = order_key(run[i]);  // the stage holds 0.0f past n: read, then dropped
+      u[i] = FULL || ((valid >> i) & 1u) ? k : 0u;
     }
     if (tid == 0) {  // (a histogram without the K-th key leaves these: every key is then in the bin)
       sh.bstar = 0;
@@ -465,11 +471,21 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, l
     while (shift > 0) {
       const int nb = shift > 11 ? 11 : shift;
       for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
-      lds_barrier();
+      // the thread's keys still in the bin (few: most threads have none),
+      // marked without branches, then counted one set bit at a time with the
+      // key read again from the stage (it holds this problem's keys until
+      // the levels are done)
+      uint32_t mm = 0;
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
-        if (u[i] != 0u && (u[i] >> shift) == prefix)
-          atomicAdd(&sh.hist[(u[i] >> (shift - nb)) & ((1u << nb) - 1u)], 1u);
+      for (int i = 0; i < NI; ++i) mm |= (u[i] >> shift) == prefix ? 1u << i : 0u;
+      if (!FULL) mm &= valid;
+      lds_barrier();
+      while (mm) {
+        const int i = __builtin_ctz(mm);
+        mm &= mm - 1u;
+        const uint32_t k = order_key(run[i]);
+        atomicAdd(&sh.hist[(k >> (shift - nb)) & ((1u << nb) - 1u)], 1u);
+      }
       lds_barrier();
       const int b0 = kBins - 1 - 2 * tid, b1 = b0 - 1;
       const int h0 = (int)sh.hist[b0], h1 = (int)sh.hist[b1];
@@ -528,15 +544,38 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, l
     int rk = block_incl_scan(ntk, sh.wsum) - ntk;
     int32_t* so = sel_out + (long long)p * sel_stride;
     float* ko = keys_out ? keys_out + (long long)p * keys_out_stride : nullptr;
+    if (__builtin_amdgcn_ballot_w64(rk + ntk > K)) {
+      // never more than K outputs (only a histogram that disagreed with the
+      // keys could ask for more)
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      if ((take >> i) & 1) {
-        if (rk < K) {
-          so[rk] = pos0 + i;
-          if (ko) ko[rk] = key_value(u[i]);
+      for (int i = 0; i < NI; ++i)
+        if ((take >> i) & 1) {
+          if (rk < K) {
+            so[rk] = pos0 + i;
+            if (ko) ko[rk] = key_value(u[i]);
+          }
+          ++rk;
         }
-        ++rk;
+    } else if (ko) {
+      unsigned ro = (unsigned)rk;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const unsigned t = (take >> i) & 1u;
+        if (t) {
+          so[ro] = pos0 + i;
+          ko[ro] = key_value(u[i]);
+        }
+        ro += t;
       }
+    } else {
+      unsigned ro = (unsigned)rk;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const unsigned t = (take >> i) & 1u;
+        if (t) so[ro] = pos0 + i;
+        ro += t;
+      }
+    }
   }
 }
 
@@ -566,8 +605,13 @@ hipError_t launch_topk(const float* keys, long long key_stride, const int32_t* c
   if (given_hist) {
     // persistent blocks, one per CU (the key stage takes most of the LDS)
     const int nb = P < kTopkHistBlocks ? P : kTopkHistBlocks;
-    FL_LAUNCH(k_topk_hist, dim3(nb), block, 0, st, keys, key_stride, P, n, K, given_hist, hist_stride, sel_out,
-              sel_stride, keys_out, keys_out_stride);
+    // every thread's 32 positions inside the problem: no per-key range masks
+    if (n == kTkKeys)
+      FL_LAUNCH(k_topk_hist<true>, dim3(nb), block, 0, st, keys, key_stride, P, n, K, given_hist, hist_stride,
+                sel_out, sel_stride, keys_out, keys_out_stride);
+    else
+      FL_LAUNCH(k_topk_hist<false>, dim3(nb), block, 0, st, keys, key_stride, P, n, K, given_hist, hist_stride,
+                sel_out, sel_stride, keys_out, keys_out_stride);
     return hipGetLastError();
   }
 #define FL_TOPK(IT)                                                                                             \
