@@ -371,13 +371,15 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
 // Top-K given the first histogram level: each problem's histogram of its
 // keys by the top 11 order-key bits (a decode step's loop 2: loop 1 leaves it
 // in the first kBins entries of the head's selection row; a prefill
-// selection: the column-mass pass counts each mass it writes).  Thread t holds the
-// keys of positions 32t .. 32t+31, so positions ascend with (thread, item)
-// and every rank in position order is one block-wide prefix sum plus a
-// popcount inside the thread.  The histogram gives the bin of the K-th
-// largest key and its rank there; two more histogram levels over the next 11
-// and 10 bits of the keys still in the bin (LDS atomics of those keys only)
-// give the K-th largest key T itself and how many keys equal to T are needed.
+// selection: the column-mass pass counts each mass it writes).  Thread t
+// holds the keys of positions 32t .. 32t+31, so positions ascend with
+// (thread, item) and every rank in position order is one block-wide prefix
+// sum plus a popcount inside the thread.  The histogram gives the bin of the
+// K-th largest key and its rank there; two more histogram levels over the
+// next 11 and 10 bits of the keys still in the bin (LDS atomics of those keys
+// only, re-read from the stage) give the K-th largest key T itself and how
+// many keys equal to T are needed.  FULL: n == 32768, every thread's 32
+// positions lie inside the problem (no per-key range masks).
 // Every key above T is taken, and the keys equal to T in position order.
 // Output: the selected positions ascending and, if keys_out is set, their
 // keys in the same order (keys and keys_out, histogram and sel_out may be the
