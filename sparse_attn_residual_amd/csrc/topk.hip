@@ -81,18 +81,31 @@ struct TopkShared {
   int rem, bstar, cnt, ncand, bad, eqc;
 };
 
-// Block-wide inclusive prefix sum of one value per thread.
+// Inclusive prefix sum over a wavefront by DPP moves (no LDS round trips):
+// shifts by 1, 2, 4 and 8 lanes inside each 16-lane row, then the last lane
+// of rows 0 and 2 added into rows 1 and 3, and the last lane of row 1 into
+// rows 2 and 3.  Every lane of the wave must be active.
+__device__ inline int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2 and 3
+  return x;
+}
+
+// Block-wide inclusive prefix sum of one value per thread.  CLOSE = false
+// leaves out the closing barrier: the caller has another barrier between
+// this scan's reads of wsum and the next scan's write.
+template <bool CLOSE = true>
 __device__ inline int block_incl_scan(int x, int* wsum) {
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
+  x = wave_incl_scan(x);
   if (lane == kWave - 1) wsum[wv] = x;
   lds_barrier();
   for (int w = 0; w < wv; ++w) x += wsum[w];
-  lds_barrier();
+  if (CLOSE) lds_barrier();
   return x;
 }
 
@@ -448,9 +461,10 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, l
       sh.rem = K;
       sh.cnt = n;
     }
-    // threshold bin (the scan's barriers also end every read of the stage)
+    // threshold bin (the scan's barrier also ends every read of the stage;
+    // the barrier below closes the scan)
     {
-      const int incl = block_incl_scan(c0 + c1, sh.wsum);
+      const int incl = block_incl_scan<false>(c0 + c1, sh.wsum);
       const int excl = incl - c0 - c1;
       if (excl < K && excl + c0 >= K) {
         sh.bstar = kBins - 1 - 2 * tid;
@@ -491,7 +505,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, l
       lds_barrier();
       const int b0 = kBins - 1 - 2 * tid, b1 = b0 - 1;
       const int h0 = (int)sh.hist[b0], h1 = (int)sh.hist[b1];
-      const int incl = block_incl_scan(h0 + h1, sh.wsum);
+      const int incl = block_incl_scan<false>(h0 + h1, sh.wsum);  // closed by the barrier below
       const int excl = incl - h0 - h1;
       if (excl < rem && excl + h0 >= rem) {
         sh.bstar = b0;
@@ -503,11 +517,11 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, l
         sh.cnt = h1;
       }
       lds_barrier();
+      // (the next writes of these come after the next level's barriers)
       prefix = (prefix << nb) | (uint32_t)sh.bstar;
       shift -= nb;
       rem = sh.rem;
       cnt = sh.cnt;
-      lds_barrier();
     }
     const uint32_t T = prefix;
     const int eqc = cnt;
@@ -543,16 +557,17 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, l
     }
     // ---- output in position order
     const int ntk = __popc(take);
-    int rk = block_incl_scan(ntk, sh.wsum) - ntk;
+    // (closed by the barrier at the top of the next problem)
+    int rk = block_incl_scan<false>(ntk, sh.wsum) - ntk;
     int32_t* so = sel_out + (long long)p * sel_stride;
     float* ko = keys_out ? keys_out + (long long)p * keys_out_stride : nullptr;
-    if (__builtin_amdgcn_ballot_w64(rk + ntk > K)) {
-      // never more than K outputs (only a histogram that disagreed with the
-      // keys could ask for more)
+    if (__builtin_amdgcn_ballot_w64(rk < 0 || rk + ntk > K)) {
+      // outputs only at ranks 0 .. K-1 (only a histogram that disagreed with
+      // the keys could ask for more)
 #pragma unroll
       for (int i = 0; i < NI; ++i)
         if ((take >> i) & 1) {
-          if (rk < K) {
+          if (rk >= 0 && rk < K) {
             so[rk] = pos0 + i;
             if (ko) ko[rk] = key_value(u[i]);
           }
