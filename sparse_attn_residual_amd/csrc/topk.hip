@@ -23,13 +23,34 @@ __device__ inline float key_value(uint32_t u) {
   return __uint_as_float(b);
 }
 
+// Inclusive prefix sum inside each 16-lane row of a wavefront by DPP moves:
+// shifts by 1, 2, 4 and 8 lanes.  Every lane of the row must be active.
+__device__ inline int row_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  return x;
+}
+
+// Inclusive prefix sum over a wavefront by DPP moves (no LDS round trips):
+// shifts by 1, 2, 4 and 8 lanes inside each 16-lane row, then the last lane
+// of rows 0 and 2 added into rows 1 and 3, and the last lane of row 1 into
+// rows 2 and 3.  Every lane of the wave must be active.
+__device__ inline int wave_incl_scan(int x) {
+  x = row_incl_scan(x);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2 and 3
+  return x;
+}
+
 // Per-row counts of a flag bitmask (bit i = candidate i*1024 + tid): fills
 // wtab[w][i] with the flagged count of the waves before w in row i and
 // rowoff[i] with the flagged count of the rows before i.  The rank of a
 // flagged candidate in candidate order is then
 //   rowoff[i] + wtab[w][i] + popcount(ballot_i & lanes below).
 // Both prefix sums are parallel: thread (i, w) scans row i over the waves in
-// a group of kTopkWaves lanes, then one wave scans the row totals.
+// one 16-lane row of a wavefront, then one wave scans the row totals.
 template <int ITEMS>
 __device__ inline void row_counts(uint64_t bits, int (*wtab)[64], int* rowoff) {
   static_assert(ITEMS * kTopkWaves <= kTopkThreads && kTopkWaves == 16 && ITEMS <= kWave, "scan shape");
@@ -44,24 +65,14 @@ __device__ inline void row_counts(uint64_t bits, int (*wtab)[64], int* rowoff) {
   if (t < ITEMS * kTopkWaves) {
     const int i = t / kTopkWaves, w = t % kTopkWaves;
     const int c = wtab[w][i];
-    int x = c;
-#pragma unroll
-    for (int o = 1; o < kTopkWaves; o <<= 1) {
-      const int y = __shfl_up(x, o, kTopkWaves);
-      if (w >= o) x += y;
-    }
+    const int x = row_incl_scan(c);  // the 16 waves' counts of item i: one 16-lane row
     wtab[w][i] = x - c;
     if (w == kTopkWaves - 1) rowoff[i] = x;
   }
   __syncthreads();
   if (t < kWave) {
     const int c = t < ITEMS ? rowoff[t] : 0;
-    int x = c;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int y = __shfl_up(x, o, kWave);
-      if (t >= o) x += y;
-    }
+    const int x = wave_incl_scan(c);
     if (t < ITEMS) rowoff[t] = x - c;
   }
   __syncthreads();
@@ -80,20 +91,6 @@ struct TopkShared {
   uint32_t digit;
   int rem, bstar, cnt, ncand, bad, eqc;
 };
-
-// Inclusive prefix sum over a wavefront by DPP moves (no LDS round trips):
-// shifts by 1, 2, 4 and 8 lanes inside each 16-lane row, then the last lane
-// of rows 0 and 2 added into rows 1 and 3, and the last lane of row 1 into
-// rows 2 and 3.  Every lane of the wave must be active.
-__device__ inline int wave_incl_scan(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1 and 3
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2 and 3
-  return x;
-}
 
 // Block-wide inclusive prefix sum of one value per thread.  CLOSE = false
 // leaves out the closing barrier: the caller has another barrier between
@@ -151,12 +148,7 @@ __device__ inline void radix_find(const uint32_t* v, uint64_t vmask, int K, int 
     int c = 0, x = 0;
     if (tid < 256) {
       c = (int)sh.hist[255 - tid];
-      x = c;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(x, o, kWave);
-        if (lane >= o) x += y;
-      }
+      x = wave_incl_scan(c);
       if (lane == kWave - 1) sh.wsum[wv] = x;
     }
     __syncthreads();
@@ -374,7 +366,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
   for (int i = 0; i < ITEMS; ++i) {
     const uint64_t m = __ballot((take >> i) & 1);
     const int rk = sh.rowoff[i] + sh.wtab[wv][i] + __popcll(m & below);
-    if (((take >> i) & 1) && rk < K) {
+    if (((take >> i) & 1) && rk >= 0 && rk < K) {
       so[rk] = CAND ? sh_idx[i * kTopkThreads + tid2] : i * kTopkThreads + tid2;
       if (ko) ko[rk] = key_value(u[i]);
     }
