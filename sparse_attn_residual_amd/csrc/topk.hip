@@ -391,15 +391,21 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
 // same rows: a problem's reads all precede the barrier after which its
 // writes begin).
 // Persistent: one block per CU walks problems blockIdx.x, + gridDim.x, ...;
-// the next problem's keys are copied into LDS (direct global->LDS loads,
-// 64 keys per load instruction, a padding word after every 64 so that the
-// 32-key runs of the threads fall on distinct banks) while this one is
-// worked on from registers (from after this problem's histogram levels on).
+// the next problem's keys are copied into LDS (direct global->LDS loads, 256
+// keys per load instruction: the fewer copy instructions, the sooner the
+// output stores behind them leave) while this one is worked on from
+// registers (from after this problem's histogram levels on).  Each thread
+// reads its 32-key run in 16-byte groups starting at group t mod 8, so the
+// eight runs of a 1 KB chunk are read from distinct banks (and, with 16
+// bytes of padding after every chunk, those of two neighbouring chunks); its
+// registers keep that order and masks rotate between register and position
+// order.
 // Barriers inside a problem exchange LDS data only and leave that copy in
 // flight; the wait for it comes at the top of the next problem.
 constexpr int kTkRun = 32;                       // keys per thread
 constexpr int kTkKeys = kTkRun * kTopkThreads;   // 32768
-constexpr int kTkStage = kTkKeys / 64 * 65;      // staged words (padded)
+constexpr int kTkChunk = 256 + 4;                // staged words per 256 keys (16 bytes of padding)
+constexpr int kTkStage = kTkKeys / 256 * kTkChunk;  // staged words
 constexpr int kTopkHistBlocks = 256;             // MI355X: one per CU
 
 template <bool FULL>
@@ -410,21 +416,40 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, l
   constexpr int NI = kTkRun;
   static_assert(kBins == kHistBins, "the given histogram is the first level");
   __shared__ TopkShared sh;
-  __shared__ float stage[kTkStage];
+  __shared__ __align__(16) float stage[kTkStage];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
   const int pos0 = tid * NI;
 
-  // copy of problem q's keys into the stage: wave w moves the 64-key chunks
-  // w, w + 16, ...; keys past n read as 0 (the resource ends at n)
+  // copy of problem q's keys into the stage (positions in order): FULL, 16
+  // bytes per lane, wave w moving the 256-key chunks w, w + 16, ...;
+  // otherwise 4 bytes per lane (64-key chunks), so that every key past n
+  // reads as 0 (the resource ends at n)
   auto stage_keys = [&](int q) {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(keys + (long long)q * key_stride), (short)0, n * 4, 0x00020000);
-    for (int ch = wv; ch < kTkKeys / 64; ch += kTopkWaves)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + ch * 65), 4,
-                                               ch * 256 + lane * 4, 0, 0, 0);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // offsets made here, not kept across problems
+    if (FULL) {
+      for (int ch = wv; ch < kTkKeys / 256; ch += kTopkWaves)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(stage + ch * kTkChunk), 16, ch * 1024 + ln * 16, 0, 0, 0);
+    } else {
+      for (int ch = wv; ch < kTkKeys / 64; ch += kTopkWaves)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(stage + (ch >> 2) * kTkChunk + (ch & 3) * 64), 4,
+            ch * 256 + ln * 4, 0, 0, 0);
+    }
   };
+  // Thread t reads its 32 keys as eight 16-byte groups starting at group
+  // t mod 8 (so the eight threads of one 1 KB chunk hit distinct banks) and
+  // keeps them in that order: register j holds position pos0 + nat(j), with
+  // nat(j) = (j + 4 (t mod 8)) mod 32.  Bit j of a register-order mask is
+  // bit nat(j) of the position-order mask: rotl by rot, and back by rotr.
+  const int rot = 4 * (tid & 7);
+  auto to_pos = [&](uint32_t m) { return rot ? (m << rot) | (m >> (32 - rot)) : m; };
+  auto to_reg = [&](uint32_t m) { return rot ? (m >> rot) | (m << (32 - rot)) : m; };
   int p = blockIdx.x;
   if (p >= P) return;
   stage_keys(p);
@@ -437,16 +462,22 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, l
   for (; p < P; p += gridDim.x) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies and loads have landed
     __syncthreads();
-    // the thread's keys in the stage (32 consecutive positions inside one
-    // 65-word chunk) and which of them lie inside the problem
-    const float* run = stage + (pos0 >> 6) * 65 + (pos0 & 63);
+    // the thread's keys (register order) and which of them lie inside the
+    // problem
+    const float* run = stage + (pos0 >> 8) * kTkChunk + (pos0 & 255);
     const int lim = n - pos0;
-    const uint32_t valid = FULL || lim >= NI ? 0xffffffffu : (lim <= 0 ? 0u : (1u << lim) - 1u);
+    const uint32_t valid =
+        FULL || lim >= NI ? 0xffffffffu : to_reg(lim <= 0 ? 0u : (1u << lim) - 1u);
     uint32_t u[NI];  // order keys; 0 past n (no key maps to 0)
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const uint32_t k = order_key(run[i]);  // the stage holds 0.0f past n: read, then dropped
-      u[i] = FULL || ((valid >> i) & 1u) ? k : 0u;
+    for (int i = 0; i < NI / 4; ++i) {
+      const float4 kv = *(const float4*)(run + ((4 * i + rot) & (NI - 1)));
+      const float kk[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t k = order_key(kk[e]);  // the stage holds 0.0f past n: read, then dropped
+        u[4 * i + e] = FULL || ((valid >> (4 * i + e)) & 1u) ? k : 0u;
+      }
     }
     if (tid == 0) {  // (a histogram without the K-th key leaves these: every key is then in the bin)
       sh.bstar = 0;
@@ -482,7 +513,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, l
       // the thread's keys still in the bin (few: most threads have none),
       // marked without branches, then counted one set bit at a time with the
       // key read again from the stage (it holds this problem's keys until
-      // the levels are done)
+      // the levels are done; register j is position nat(j))
       uint32_t mm = 0;
 #pragma unroll
       for (int i = 0; i < NI; ++i) mm |= (u[i] >> shift) == prefix ? 1u << i : 0u;
@@ -491,7 +522,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, l
       while (mm) {
         const int i = __builtin_ctz(mm);
         mm &= mm - 1u;
-        const uint32_t k = order_key(run[i]);
+        const uint32_t k = order_key(run[(i + rot) & (NI - 1)]);
         atomicAdd(&sh.hist[(k >> (shift - nb)) & ((1u << nb) - 1u)], 1u);
       }
       lds_barrier();
@@ -521,12 +552,14 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, l
     // Issued after the histogram levels: the compiler cannot tell their LDS
     // atomics from the copy's destination and would wait for the copy before
     // each of them.
+    // (the bins first: loads complete in order, so a wait for them does not
+    // wait for the copy)
     const int pn = p + gridDim.x;
     if (pn < P) {
-      stage_keys(pn);
       const int32_t* hrow = hist + (long long)pn * hist_stride;
       c0 = hrow[kBins - 1 - 2 * tid];
       c1 = hrow[kBins - 2 - 2 * tid];
+      stage_keys(pn);
     }
     // take every key above T and the first rem keys equal to T
     uint32_t take = 0, eq = 0;
@@ -538,50 +571,52 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, l
     if (eqc == rem) {
       take |= eq;
     } else {
+      // the first rem keys equal to T in position order (ranks as in the
+      // output below)
       const int ne = __popc(eq);
-      int rk = block_incl_scan(ne, sh.wsum) - ne;
+      const int rk = block_incl_scan(ne, sh.wsum) - ne;
+      const uint32_t eqp = to_pos(eq);
+      int rotq = rot;
+      asm volatile("" : "+v"(rotq));  // rank masks made here, not kept across problems
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
-        if ((eq >> i) & 1) {
-          if (rk < rem) take |= 1u << i;
-          ++rk;
+      for (int g = 0; g < NI / 4; ++g) {
+        const int np0 = (4 * g + rotq) & (NI - 1);
+        int re = rk + __popc(eqp & ((1u << np0) - 1u));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g + e;
+          const int t = (eq >> i) & 1;
+          if (t && re < rem) take |= 1u << i;
+          re += t;
         }
+      }
     }
-    // ---- output in position order
+    // ---- output in position order: register j goes to rank rk plus the
+    // taken keys at positions before nat(j); the 4-key groups of registers
+    // are consecutive positions, so the rank steps by one inside a group
     const int ntk = __popc(take);
     // (closed by the barrier at the top of the next problem)
-    int rk = block_incl_scan<false>(ntk, sh.wsum) - ntk;
+    const int rk = block_incl_scan<false>(ntk, sh.wsum) - ntk;
+    const uint32_t takep = to_pos(take);
     int32_t* so = sel_out + (long long)p * sel_stride;
     float* ko = keys_out ? keys_out + (long long)p * keys_out_stride : nullptr;
-    if (__builtin_amdgcn_ballot_w64(rk < 0 || rk + ntk > K)) {
-      // outputs only at ranks 0 .. K-1 (only a histogram that disagreed with
-      // the keys could ask for more)
+    const bool safe = !__builtin_amdgcn_ballot_w64(rk < 0 || rk + ntk > K);
+    int roto = rot;
+    asm volatile("" : "+v"(roto));  // rank masks made here, not kept across problems
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
-        if ((take >> i) & 1) {
-          if (rk >= 0 && rk < K) {
-            so[rk] = pos0 + i;
-            if (ko) ko[rk] = key_value(u[i]);
-          }
-          ++rk;
-        }
-    } else if (ko) {
-      unsigned ro = (unsigned)rk;
+    for (int g = 0; g < NI / 4; ++g) {
+      const int np0 = (4 * g + roto) & (NI - 1);  // position of register 4g
+      unsigned ro = (unsigned)(rk + __popc(takep & ((1u << np0) - 1u)));
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * g + e;
         const unsigned t = (take >> i) & 1u;
-        if (t) {
-          so[ro] = pos0 + i;
-          ko[ro] = key_value(u[i]);
+        // outputs only at ranks 0 .. K-1 (only a histogram that disagreed
+        // with the keys could ask for more)
+        if (t && (safe || ro < (unsigned)K)) {
+          so[ro] = pos0 + np0 + e;
+          if (ko) ko[ro] = key_value(u[i]);
         }
-        ro += t;
-      }
-    } else {
-      unsigned ro = (unsigned)rk;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const unsigned t = (take >> i) & 1u;
-        if (t) so[ro] = pos0 + i;
         ro += t;
       }
     }
