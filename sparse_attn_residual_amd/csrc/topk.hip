@@ -506,14 +506,16 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, l
     int rem = sh.rem, cnt = sh.cnt;
     // The bin is split by the next 11, then 10 bits of its keys, counted
     // from the registers (LDS atomics of the keys still in the bin only),
-    // down to one value: the threshold T, with cnt keys equal to it.
-    while (shift > 0) {
-      const int nb = shift > 11 ? 11 : shift;
+    // down to one value: the threshold T, with cnt keys equal to it.  A
+    // sub-bin left with a single key ends the search there.
+    auto level = [&](const int nb) {
       for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
       // the thread's keys still in the bin (few: most threads have none),
       // marked without branches, then counted one set bit at a time with the
       // key read again from the stage (it holds this problem's keys until
-      // the levels are done; register j is position nat(j))
+      // the levels are done; register j is position nat(j)); each key is
+      // also left in its sub-bin's slot of cu, which keeps the key itself
+      // when the sub-bin has only that one
       uint32_t mm = 0;
 #pragma unroll
       for (int i = 0; i < NI; ++i) mm |= (u[i] >> shift) == prefix ? 1u << i : 0u;
@@ -523,7 +525,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, l
         const int i = __builtin_ctz(mm);
         mm &= mm - 1u;
         const uint32_t k = order_key(run[(i + rot) & (NI - 1)]);
-        atomicAdd(&sh.hist[(k >> (shift - nb)) & ((1u << nb) - 1u)], 1u);
+        const uint32_t sb = (k >> (shift - nb)) & ((1u << nb) - 1u);
+        atomicAdd(&sh.hist[sb], 1u);
+        sh.cu[sb] = k;
       }
       lds_barrier();
       const int b0 = kBins - 1 - 2 * tid, b1 = b0 - 1;
@@ -545,6 +549,14 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, l
       shift -= nb;
       rem = sh.rem;
       cnt = sh.cnt;
+    };
+    level(11);
+    if (cnt == 1) {
+      // one key left with these leading bits: it is the threshold
+      prefix = sh.cu[sh.bstar];
+      shift = 0;
+    } else {
+      level(10);
     }
     const uint32_t T = prefix;
     const int eqc = cnt;
