@@ -354,3 +354,34 @@ def test_decode_selection_from_loop1_histogram(dtype, T, ties):
     if ties:
         assert n_ties > 0, "the tie case produced no tie at the threshold"
     _check_decode(cfg, gpu, slices, qs, T, 1e-5 if dtype == "f32" else 2e-3, rel=dtype != "f32")
+
+
+@pytest.mark.parametrize("pattern", ["plain", "groups", "equal"])
+def test_decode_selection_full_problem(pattern):
+    """Loop 2's selection on problems of exactly 32768 keys (the top-K kernel
+    variant without per-key range masks): plain logits, logits tied in
+    groups of four consecutive positions, and every logit equal (the whole
+    problem in one bin down to the last level, the first K positions taken).
+    The selection equals the oracle's top-K of the GPU's own loop-1 logits,
+    ties to the lower position, and the outputs match the oracle."""
+    import tests.gpu_harness as gh
+    cfg = workloads.custom(name="decode-full-problem", dtype="bf16", B=1, H=2, d=128, S=32768, R=2, act=(1, 0.3),
+                           col="0.10", bits=(8, 4), gamma=0.5, lognormal=0.5, L=1, decode=True, seed=29)
+    _say("decode selection on 32768-key problems", pattern)
+    rows, slices = workloads.gen_batch(cfg)
+    for sl in slices.values():
+        if pattern == "groups":
+            sl.k[0] = sl.k[0][(np.arange(cfg.S) // 4) * 4].copy()
+        elif pattern == "equal":
+            sl.k[0] = np.repeat(sl.k[0][:1], cfg.S, axis=0)
+    cache = gh.build_decode_cache(cfg, rows, slices)
+    qs = workloads.decode_queries(cfg)
+    gpu = gh.run_decode(cfg, cache, qs)
+    for h in range(cfg.H):
+        lg = gpu[0]["logits"][0, 0, h].astype(np.float64)
+        exact = prefill.topk(lg, np.arange(cfg.S), cfg.K)
+        assert np.array_equal(gpu[1]["sel"][0, 0, h], exact), (pattern, h)
+        if pattern == "equal":
+            assert np.all(lg == lg[0]) and np.array_equal(exact, np.arange(cfg.K))
+    _check_decode(cfg, gpu, slices, qs, cfg.S, 2e-3, rel=True)
+
