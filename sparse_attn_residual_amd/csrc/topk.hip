@@ -382,9 +382,10 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
 // sum plus a popcount inside the thread.  The histogram gives the bin of the
 // K-th largest key and its rank there; two more histogram levels over the
 // next 11 and 10 bits of the keys still in the bin (LDS atomics of those keys
-// only, re-read from the stage) give the K-th largest key T itself and how
-// many keys equal to T are needed.  FULL: n == 32768, every thread's 32
-// positions lie inside the problem (no per-key range masks).
+// only, re-read from the stage; the second level is skipped when the first
+// leaves a single key) give the K-th largest key T itself and how many keys
+// equal to T are needed.  FULL: n == 32768, every thread's 32 positions lie
+// inside the problem (no per-key range masks).
 // Every key above T is taken, and the keys equal to T in position order.
 // Output: the selected positions ascending and, if keys_out is set, their
 // keys in the same order (keys and keys_out, histogram and sel_out may be the
