@@ -505,10 +505,10 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_hist(const float* keys, l
     uint32_t prefix = (uint32_t)sh.bstar;
     int shift = 32 - kHistBits;
     int rem = sh.rem, cnt = sh.cnt;
-    // The bin is split by the next 11, then 10 bits of its keys, counted
-    // from the registers (LDS atomics of the keys still in the bin only),
-    // down to one value: the threshold T, with cnt keys equal to it.  A
-    // sub-bin left with a single key ends the search there.
+    // The bin is split by the next 11, then 10 bits of its keys (marked in
+    // the registers, counted by LDS atomics of the keys still in the bin
+    // only), down to one value: the threshold T, with cnt keys equal to it.
+    // A sub-bin left with a single key ends the search there.
     auto level = [&](const int nb) {
       for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
       // the thread's keys still in the bin (few: most threads have none),
