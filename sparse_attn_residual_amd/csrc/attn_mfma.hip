@@ -44,13 +44,16 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kD = 128;
 constexpr int kBN = 64;             // key columns per tile
 constexpr int kNoPos = 0x7fffffff;  // padding column: masked for every row
-// Lazy rescale threshold (log2 units): a weight P = 2^(x*c2 - mref) may reach
-// 2^15 before the reference moves.  fp16 holds it (max 65504), rounds it with
-// the same relative error at any size, and keeps weights normal down to 2^-14,
-// i.e. scores up to 29 below the row maximum; a lower threshold would only
-// rescale more often.
+// Lazy rescale: the weights P = 2^(x*c2 - mref) of a tile are formed against
+// the current reference mref (log2 units) and used as they are while every one
+// of them fits fp16 (up to 65504; fp16 rounds them with the same relative
+// error at any size and keeps them normal down to 2^-14, i.e. scores up to ~30
+// below the largest weight).  Only when one does not (a lane's fp32 sum of its
+// 32 rounded weights is then not finite, above 32 * 65504) does the reference
+// move: to the tile maximum, for the rows whose maximum exceeds it by more
+// than kRescale.
 constexpr float kRescale = 15.0f;
-constexpr float kRescaleP = 32768.0f;  // 2^kRescale
+constexpr float kRescaleP = 32.0f * 65504.0f;  // largest sum of 32 finite fp16 weights
 
 // Tile image: the exact LDS layout of one 64-column tile, built once per loop
 // in HBM and copied into LDS by direct global->LDS loads.
@@ -317,8 +320,7 @@ __device__ inline void softmax_mask(const uint8_t* T, f32x16_t s0, f32x16_t s1, 
 
 // Lazy rescale: the reference max mref (log2 units) moves to the row max of
 // the tile only when that max exceeds it by more than kRescale (or it is
-// unset); the row sum and accumulators are rescaled then.  Otherwise every
-// weight 2^(x*c2 - mref) stays below 2^kRescale and fp16 holds it.
+// unset); the row sum and accumulators are rescaled then.
 __device__ inline void softmax_rescale(const float* x, float c2, float& mref, float& lsum, f32x16_t* o) {
   float mt = x[0];
 #pragma unroll
@@ -660,8 +662,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (SRC == 0 && RING == 1 ? 3 : 2) 
       }
       const int dsh = osh - tsh;
       // Weights against the current reference (UM: the fixed loop r-1
-      // statistics).  ATTN: only if a lane's sum exceeds 2^kRescale (so some
-      // weight might) or a valid row has no reference yet is the tile max
+      // statistics).  ATTN: only if a lane's weights overflowed fp16 (its sum
+      // is not finite) or a valid row has no reference yet is the tile max
       // taken, the lazy rescale applied and the weights formed again.
       f16x8_t pf[4];
       float ls = softmax_probs(x, ((MODE == kModeAttn && mref == -INFINITY) ? 0.0f : mref) + (float)dsh, m.c2, pf);
