@@ -97,6 +97,15 @@ __host__ __device__ constexpr int vt_col(int x) {
 }
 static_assert(vt_col(0) == 0 && vt_col(4) == 8 && vt_col(8) == 4 && vt_col(12) == 12 && vt_col(21) == 25,
               "V^T column slots");
+// The same for the 16x16x32 products of the 48-row dense kernel: there a lane
+// of group g (lane / 16) holds, per 32 columns, columns 4g..4g+3 and
+// 16+4g..16+4g+3 of its row, stored as slots 8g..8g+7.
+__host__ __device__ constexpr int vt_col16(int x) {
+  return (x & ~31) + ((x >> 2) & 3) * 8 + ((x >> 4) & 1) * 4 + (x & 3);
+}
+static_assert(vt_col16(0) == 0 && vt_col16(4) == 8 && vt_col16(16) == 4 && vt_col16(21) == 13 &&
+                  vt_col16(31) == 31 && vt_col16(44) == 56,
+              "V^T column slots (16x16 products)");
 
 // One tile image in LDS (img, kImgBytes) from 256 threads of a block: the
 // columns tile*64 .. +64 of a selection row (sel NULL: those positions
@@ -104,7 +113,8 @@ static_assert(vt_col(0) == 0 && vt_col(4) == 8 && vt_col(8) == 4 && vt_col(12) =
 // sequence b.  NR >= 0: the workload format with a chain of exactly NR
 // residual loops (rc = NR + 1), its loads batched (chain_group_n); NR < 0:
 // any chain.  Ends with a block barrier: the image is complete.
-template <int NR>
+// V16: V^T columns in the slots of the 16x16x32 products (vt_col16).
+template <int NR, bool V16 = false>
 __device__ inline void build_tile(uint8_t* img, float* wmax, const CacheGeo& c, int rc, const int32_t* selrow, int K,
                                   int tile, int b, int hk) {
   const int t = threadIdx.x;
@@ -167,7 +177,7 @@ __device__ inline void build_tile(uint8_t* img, float* wmax, const CacheGeo& c, 
   const int vsh = tmax >= 32768.0f ? ((__float_as_int(tmax) >> 23) & 255) - 127 - 14 : 0;
   {
     _Float16* vt = (_Float16*)(img + kImgV);
-    const int vc = vt_col(col);
+    const int vc = V16 ? vt_col16(col) : vt_col(col);
 #pragma unroll
     for (int e = 0; e < 32; ++e) vt[(g * 32 + e) * kVP + vc] = (_Float16)__builtin_ldexpf(x[e], -vsh);
   }
@@ -180,7 +190,7 @@ __device__ inline void build_tile(uint8_t* img, float* wmax, const CacheGeo& c, 
 // then written out with 16-byte stores.  Every packed record a loop attends
 // is dequantized exactly once here (p1 §4.4: chosen keys gathered into dense
 // buffers; p1 App. G: attention works from the packed streams).
-template <int NR>
+template <int NR, bool V16 = false>
 __global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const int32_t* __restrict__ sel, int K,
                                                      int ntiles, uint8_t* __restrict__ out) {
   __shared__ __align__(16) uint8_t img[kImgBytes];
@@ -192,7 +202,7 @@ __global__ __launch_bounds__(256) void k_build_tiles(CacheGeo c, int rc, const i
   const int nh = sel ? c.H : c.Hkv;
   const int b = bh / nh;
   const int hk = sel ? kv_head(c, bh - b * nh) : bh - b * nh;
-  build_tile<NR>(img, wmax, c, rc, sel ? sel + (long long)bh * K : nullptr, K, tile, b, hk);
+  build_tile<NR, V16>(img, wmax, c, rc, sel ? sel + (long long)bh * K : nullptr, K, tile, b, hk);
   uint4* dst = (uint4*)(out + ((long long)bh * ntiles + tile) * kImgBytes);
   const uint4* src = (const uint4*)img;
   for (int i = threadIdx.x; i < kImgBytes / 16; i += 256) dst[i] = src[i];
@@ -769,6 +779,269 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (SRC == 0 && RING == 1 ? 3 : 2) 
   write_row<MODE>(a, r, bhS, ipos, hf, mref, lt, o, __builtin_ldexpf(1.0f, osh));
 }
 
+// ------------------------------------------------------------- dense loop 1, 48 rows per wave
+// Loop-1 attention over every position on 16x16x32 products: each wave owns
+// 48 query rows as three 16-row blocks, so every K or V^T fragment a lane
+// reads from LDS feeds three products (1.5x the matrix work per LDS byte of
+// the 32-row kernel), at two waves per SIMD.  In S^T = K Q^T a lane of group
+// g = lane / 16 holds, for row l16 = lane % 16 of each row block, columns
+// 16kb + 4g .. +3 of the tile (kb = 0..3): a row's 64 columns lie in four
+// lanes, which reduce a row's maximum or sum with two exchanges.  The
+// weights of columns 32j + {4g..4g+3, 16+4g..16+4g+3} form the lane's B
+// fragment of O^T += V^T P^T for k-step j, matched by the tile image's V^T
+// column slots (vt_col16).  Lazy rescale, V shifts and outputs as in the
+// 32-row kernel.
+constexpr int kR48 = 48;
+
+__device__ inline void qk_tile48(const uint8_t* T, const bf16x8_t (*qf)[4], int l16, int g, f32x4_t (*s)[3]) {
+  constexpr int A = 3;
+  const __bf16* kt = (const __bf16*)T;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int rb = 0; rb < 3; ++rb) s[kb][rb] = f32x4_t{};
+  // fragment f = ks * 4 + kb: key row 16kb + l16, dims 32ks + 8g .. +7
+  bf16x8_t kf[A];
+#pragma unroll
+  for (int f = 0; f < A; ++f) kf[f] = *(const bf16x8_t*)&kt[((f & 3) * 16 + l16) * kKP + (f >> 2) * 32 + g * 8];
+#pragma unroll
+  for (int f = 0; f < 16; ++f) {
+    const int kb = f & 3, ks = f >> 2;
+#pragma unroll
+    for (int rb = 0; rb < 3; ++rb) s[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[f % A], qf[rb][ks], s[kb][rb], 0, 0, 0);
+    if (f + A < 16) {
+      const int fn = f + A;
+      kf[f % A] = *(const bf16x8_t*)&kt[((fn & 3) * 16 + l16) * kKP + (fn >> 2) * 32 + g * 8];
+    }
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, A, 0);
+#pragma unroll
+  for (int i = 0; i < 16 - A; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 3 * A, 0);
+}
+
+__device__ inline void pv_tile48(const uint8_t* T, const f16x8_t (*pf)[2], int l16, int g, f32x4_t (*o)[3]) {
+  constexpr int A = 3;
+  const _Float16* vt = (const _Float16*)(T + kImgV);
+  // fragment f = j * 8 + db: V^T rows 16db + l16, column slots 32j + 8g .. +7
+  f16x8_t vf[A];
+#pragma unroll
+  for (int f = 0; f < A; ++f) vf[f] = *(const f16x8_t*)&vt[((f & 7) * 16 + l16) * kVP + (f >> 3) * 32 + g * 8];
+#pragma unroll
+  for (int f = 0; f < 16; ++f) {
+    const int db = f & 7, j = f >> 3;
+#pragma unroll
+    for (int rb = 0; rb < 3; ++rb) o[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[f % A], pf[rb][j], o[db][rb], 0, 0, 0);
+    if (f + A < 16) {
+      const int fn = f + A;
+      vf[f % A] = *(const f16x8_t*)&vt[((fn & 7) * 16 + l16) * kVP + (fn >> 3) * 32 + g * 8];
+    }
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, A, 0);
+#pragma unroll
+  for (int i = 0; i < 16 - A; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 3 * A, 0);
+}
+
+// Weights of one row block: P = 2^(x*c2 - base) in fp16 for the lane's 16
+// columns (x[8j + e]: k-step j, slot e); returns the lane's sum of exactly
+// those fp16 weights.
+__device__ inline float probs48(const float* x, float base, float c2, f16x8_t* pf) {
+  const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+  float ls0 = 0.0f, ls1 = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[8 * j + e], c2, -base));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[8 * j + e + 1], c2, -base));
+      const f16x2_t h = {(_Float16)p0, (_Float16)p1};
+      pf[j][e] = h[0];
+      pf[j][e + 1] = h[1];
+      if (e & 2)
+        ls1 = __builtin_amdgcn_fdot2(h, one2, ls1, false);
+      else
+        ls0 = __builtin_amdgcn_fdot2(h, one2, ls0, false);
+    }
+  }
+  return ls0 + ls1;
+}
+
+// Rescale of one row block: the row's tile maximum over its four lanes.
+__device__ inline void rescale48(const float* x, float c2, float& mref, float& lsum, f32x4_t (*o)[3], int rb) {
+  float mt = x[0];
+#pragma unroll
+  for (int v = 1; v < 16; ++v) mt = fmaxf(mt, x[v]);
+  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * c2;
+  const bool need = mt > mref + kRescale;
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    const float mn = need ? mt : mref;
+    const float alpha = need ? __builtin_amdgcn_exp2f(mref - mn) : 1.0f;
+    mref = mn;
+    lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[db][rb] *= alpha;
+  }
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_attn_dense48(MfmaArgs m) {
+  constexpr int BM = kR48 * NW;
+  constexpr int RING = 2;
+  extern __shared__ __align__(16) uint8_t lds[];   // two tile images
+  const AttnArgs& a = m.a;
+  const CacheGeo& c = a.c;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int g = lane >> 4;
+  const int l16 = lane & 15;
+
+  // block -> (b, h, row block); every XCD gets whole heads, heavy blocks first
+  const int nunits = c.B * c.H * m.nblk;
+  int u = blockIdx.x;
+  if ((nunits & 7) == 0) u = (u & 7) * (nunits >> 3) + (u >> 3);
+  const int bh = u / m.nblk;
+  const int blk = m.nblk - 1 - (u - bh * m.nblk);
+  const int b = bh / c.H;
+  const int nrows = c.S;
+  const int row0 = blk * BM;
+  if (row0 >= nrows) return;
+  const long long bhS = (long long)bh * c.S;
+  const long long tbh = (long long)b * c.Hkv + kv_head(c, bh - b * c.H);
+  const uint8_t* imgs = m.tiles + tbh * m.ntiles_total * kImgBytes;
+  const __amdgpu_buffer_rsrc_t rs = img_rsrc(imgs, m.ntiles_total * kImgBytes);
+  if (m.ntiles_total > 0) dma_img<NW, kImgChunks>(rs, 0, lds);
+
+  // the lane's rows (one per row block) and their queries
+  const int w0 = row0 + wv * kR48;
+  int ipos[3];
+  bf16x8_t qf[3][4];
+#pragma unroll
+  for (int rb = 0; rb < 3; ++rb) {
+    const int t = w0 + rb * 16 + l16;
+    ipos[rb] = t < nrows ? t : -1;
+    const bf16x8_t* qp = (const bf16x8_t*)((const uint16_t*)a.q + (bhS + (t < nrows ? t : 0)) * kD);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[rb][ks] = ipos[rb] >= 0 ? qp[ks * 4 + g] : bf16x8_t{};
+  }
+  // tiles of the block: up to its last row; the wave computes those up to
+  // its own last row (none if it has no row)
+  const int nt = min(m.ntiles_total, (min(row0 + BM, nrows) - 1) / kBN + 1);
+  const int wmax = w0 < nrows ? min(w0 + kR48, nrows) - 1 : -1;
+
+  float mref[3], lsum[3];
+  f32x4_t o[8][3];
+#pragma unroll
+  for (int rb = 0; rb < 3; ++rb) {
+    mref[rb] = -INFINITY;
+    lsum[rb] = 0.0f;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[db][rb] = f32x4_t{};
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // V shift of the accumulators (as in the 32-row kernel)
+  int osh = 0;
+  f32x4_t s[4][3];
+  f16x8_t pf[3][2];
+  // The weights pf of tile t from its scores s: mask, V shift, lazy rescale.
+  auto weights = [&](int t) {
+    const uint8_t* T = lds + (t % RING) * kImgBytes;
+    // x[rb][8j + e]: column 32j + 16(e / 4) + 4g + e % 4
+    float x[3][16];
+#pragma unroll
+    for (int rb = 0; rb < 3; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[rb][kb * 4 + i] = s[kb][rb][i];
+    // causal mask (positions are the columns themselves; padding columns
+    // lie past every row)
+    if (t * kBN + kBN - 1 > w0) {
+#pragma unroll
+      for (int rb = 0; rb < 3; ++rb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int col = t * kBN + (v >> 2) * 16 + 4 * g + (v & 3);
+          if (col > ipos[rb]) x[rb][v] = -INFINITY;
+        }
+    }
+    const int tsh = __builtin_amdgcn_readfirstlane(*(const int*)(T + kImgShift));
+    if (tsh > osh) {
+      const float f = __builtin_ldexpf(1.0f, osh - tsh);
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int rb = 0; rb < 3; ++rb) o[db][rb] *= f;
+      osh = tsh;
+    }
+    const int dsh = osh - tsh;
+    // lazy rescale as in the 32-row kernel; a lane holds 16 weights of each
+    // of its rows, so a sum above 16 * 65504 means one overflowed fp16
+    float ls[3];
+    bool bad = false;
+#pragma unroll
+    for (int rb = 0; rb < 3; ++rb) {
+      ls[rb] = probs48(x[rb], (mref[rb] == -INFINITY ? 0.0f : mref[rb]) + (float)dsh, m.c2, pf[rb]);
+      bad |= (ipos[rb] >= 0 && mref[rb] == -INFINITY) || !(ls[rb] <= 16.0f * 65504.0f);
+    }
+    if (__builtin_amdgcn_ballot_w64(bad)) {
+#pragma unroll
+      for (int rb = 0; rb < 3; ++rb) {
+        rescale48(x[rb], m.c2, mref[rb], lsum[rb], o, rb);
+        ls[rb] = probs48(x[rb], (mref[rb] == -INFINITY ? 0.0f : mref[rb]) + (float)dsh, m.c2, pf[rb]);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < 3; ++rb) lsum[rb] += dsh == 0 ? ls[rb] : __builtin_ldexpf(ls[rb], dsh);
+  };
+  for (int tt = 0; tt < nt; ++tt) {
+    const uint8_t* T = lds + (tt % RING) * kImgBytes;
+    // tile tt+1 goes into the slot tile tt-1 left (all waves passed it)
+    if (tt + 1 < nt) dma_tile<NW>(rs, (tt + 1) * kImgBytes, lds + ((tt + 1) % RING) * kImgBytes);
+    if (tt * kBN <= wmax) {
+      qk_tile48(T, qf, l16, g, s);
+      weights(tt);
+      pv_tile48(T, pf, l16, g, o);
+    }
+    // tile tt+1 must be in LDS for every wave
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+  }
+
+  // ---- epilogue: a lane writes dims 16db + 4g .. +3 of each of its rows
+  const float osc = __builtin_ldexpf(1.0f, osh);
+#pragma unroll
+  for (int rb = 0; rb < 3; ++rb) {
+    float lt = lsum[rb];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    const int i = ipos[rb];
+    if (i < 0) continue;
+    const long long rowp = (bhS + i) * kD;
+    const float inv = (1.0f / lt) * osc;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int dcol = db * 16 + 4 * g;
+      f32x4_t ov = o[db][rb] * inv;
+      *(f32x4_t*)&a.O[rowp + dcol] = ov;
+      *(f32x4_t*)&a.U[rowp + dcol] = f32x4_t{};
+    }
+    if (g == 0) {
+      a.lse[bhS + i] = (mref[rb] + __log2f(lt)) * 0.6931471805599453f;
+      a.M[bhS + i] = 1.0f;
+    }
+  }
+}
+
 // ------------------------------------------------------------- column mass
 // c_j = sum_{i in A_r, i >= j} P^(r-1)_ij for the candidate columns (p1 §4.2
 // and §D.2: columns ranked by the preceding loop's attention statistics over
@@ -1024,10 +1297,19 @@ __global__ __launch_bounds__(64 * NW) void k_mass_mfma(MassArgs m) {
 static_assert(kImgBytes == kTileImgBytes && kBN == 64, "tile image size (launch.hpp)");
 
 // Tile images of K columns (sel NULL: positions 0..K-1) at loop rc.
-hipError_t launch_gather(const CacheGeo& c, int rc, const int32_t* sel, int K, uint8_t* out, hipStream_t st) {
+// V16: V^T in the column slots of the 48-row dense kernel.
+static hipError_t launch_gather(const CacheGeo& c, int rc, const int32_t* sel, int K, uint8_t* out, hipStream_t st,
+                                bool v16 = false) {
   const int nt = (K + kBN - 1) / kBN;
   const int nh = sel ? c.H : c.Hkv;
   const dim3 grid((unsigned)(c.B * nh * nt));
+  if (v16) {
+    if (c.fmt != kFmtPaper && rc == 1)
+      FL_LAUNCH((k_build_tiles<0, true>), grid, dim3(256), 0, st, c, rc, sel, K, nt, out);
+    else
+      FL_LAUNCH((k_build_tiles<-1, true>), grid, dim3(256), 0, st, c, rc, sel, K, nt, out);
+    return hipGetLastError();
+  }
   switch (c.fmt == kFmtPaper ? -1 : rc - 1) {
     case 0: FL_LAUNCH(k_build_tiles<0>, grid, dim3(256), 0, st, c, rc, sel, K, nt, out); break;
     case 1: FL_LAUNCH(k_build_tiles<1>, grid, dim3(256), 0, st, c, rc, sel, K, nt, out); break;
@@ -1110,6 +1392,25 @@ static bool own_tiles(int) {
   return e && std::strcmp(e, "lds") == 0;
 }
 
+// Dense loop 1 on the 48-row kernel (384-row blocks of eight waves, two per
+// SIMD, one block per CU) when 256-row blocks would fill the chip four times
+// over; smaller launches keep the 32-row kernel's 128-row blocks (two per
+// CU), which measured 3 % faster there than 192-row blocks of the 48-row one
+// (8K workload, loop 1: 0.32 vs 0.33 ms).
+static bool dense48(const CacheGeo& c) {
+  return (long long)c.B * c.H * ((c.S + 255) / 256) >= kWideBlocks;
+}
+template <int NW>
+static hipError_t launch_dense48(MfmaArgs& m, hipStream_t st) {
+  constexpr size_t lds = 2 * (size_t)kImgBytes;
+  static const hipError_t attr = hipFuncSetAttribute((const void*)k_attn_dense48<NW>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  m.nblk = (m.a.c.S + kR48 * NW - 1) / (kR48 * NW);
+  FL_LAUNCH(k_attn_dense48<NW>, dim3((unsigned)(m.a.c.B * m.a.c.H * m.nblk)), dim3(64 * NW), lds, st, m);
+  return hipGetLastError();
+}
+
 // Loop-r attention: r == 1 dense over every position, r >= 2 over S_r.
 // ws: gather_bytes(c, K) bytes (K = S at r == 1).
 hipError_t launch_attn_mfma(const AttnArgs& a, uint8_t* ws, hipStream_t st) {
@@ -1120,9 +1421,11 @@ hipError_t launch_attn_mfma(const AttnArgs& a, uint8_t* ws, hipStream_t st) {
   const int K = a.r == 1 ? a.c.S : a.K;
   m.ntiles_total = (K + kBN - 1) / kBN;
   if (a.r >= 2 && own_tiles(a.c.n[a.r])) return launch_rows<kModeAttn>(m, a.c.n[a.r], st, true);
-  hipError_t e = launch_gather(a.c, a.r, a.r == 1 ? nullptr : a.sel, K, ws, st);
+  const bool d48 = a.r == 1 && dense48(a.c);
+  hipError_t e = launch_gather(a.c, a.r, a.r == 1 ? nullptr : a.sel, K, ws, st, d48);
   if (e != hipSuccess) return e;
   m.tiles = ws;
+  if (d48) return launch_dense48<8>(m, st);
   return launch_rows<kModeAttn>(m, a.r == 1 ? a.c.S : a.c.n[a.r], st);
 }
 

@@ -262,9 +262,9 @@ def test_prefill_split_boundaries(act):
 
 
 def test_prefill_bf16_mfma_wide():
-    """Enough heads that the twelve-wave (384-row block) kernel runs in the
-    dense loop and in loop 2, with ragged row blocks; loops 3 and 4 take the
-    four-wave kernel."""
+    """Enough heads that the 384-row block kernels run: the 48-row one in
+    the dense loop and the twelve-wave one in loop 2, with ragged row blocks
+    and a ragged last tile; loops 3 and 4 take the four-wave kernel."""
     cfg = workloads.custom(name="bf16-wide", dtype="bf16", B=4, H=64, d=128, S=1000, R=4, act=(1, 0.9, 0.6, 0.3),
                            col="0.25", bits=(8, 4, 2, 4), lognormal=0.5, seed=7)
     _say("prefill bf16 wide", cfg)
@@ -536,16 +536,18 @@ def test_fl_check_validator(monkeypatch):
     assert torch.equal(st.O, torch.from_numpy(b["state"][3]["O"]).cuda())
 
 
-def test_prefill_bf16_values_beyond_fp16():
+@pytest.mark.parametrize("B,H", [(1, 2), (2, 128)])
+def test_prefill_bf16_values_beyond_fp16(B, H):
     """Values whose bf16 reconstructions exceed fp16's range (|v~| up to
     ~6e5, inside the int8 base's fp16-scale range) take the matrix-core
     path's per-tile V shift.  Head 0 has every value's loop-1 part scaled by
-    2^17, head 1 only the positions below 300, so tiles with and without a
-    shift meet in one row; the loop-to-loop changes keep their size (a
-    residual's fp16 zero bounds them by 65504).  Outputs are finite and
-    within the bf16 bar of the oracle."""
+    2^17, the other heads only the positions below 300, so tiles with and
+    without a shift meet in one row; the loop-to-loop changes keep their size
+    (a residual's fp16 zero bounds them by 65504).  Outputs are finite and
+    within the bf16 bar of the oracle.  With 2 x 128 heads the dense loop runs
+    on the 48-row kernel."""
     import tests.gpu_harness as gh
-    cfg = workloads.custom(name="bf16-large-v", dtype="bf16", B=1, H=2, d=128, S=900, R=4, act=(1, 0.4, 0.2, 0.1),
+    cfg = workloads.custom(name="bf16-large-v", dtype="bf16", B=B, H=H, d=128, S=900, R=4, act=(1, 0.4, 0.2, 0.1),
                            col="0.20", bits=(8, 4, 4, 2), lognormal=0.5, seed=29)
     _say("prefill bf16 large values", cfg)
     rows, slices = workloads.gen_batch(cfg)
