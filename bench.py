@@ -562,7 +562,7 @@ def main():
             },
         },
         "roofline": {
-            "kernel": "k_attn_mfma<12, 0> (the attention kernel of fl_loop_attn r=1: dense causal over the int8 base)",
+            "kernel": "k_attn_dense48<8> (the attention kernel of fl_loop_attn r=1: dense causal over the int8 base)",
             "bound": "mfma",
             "achieved": pf["dense_kernel_tf"],
             "peak": acc.MI355X_BF16_TFLOPS,
@@ -652,7 +652,7 @@ def main():
             "prefill_flops": o["work"]["flops"],
             "mfma_frac_whole_step": o["total_tf"] / acc.MI355X_BF16_TFLOPS,
             "roofline": {
-                "kernel": "k_attn_mfma (dense loop 1)", "bound": "mfma", "achieved": o["dense_kernel_tf"],
+                "kernel": "dense loop-1 attention kernel", "bound": "mfma", "achieved": o["dense_kernel_tf"],
                 "peak": acc.MI355X_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": o["dense_kernel_tf"] / acc.MI355X_BF16_TFLOPS, "avg_launch_ms": o["dense_kernel_ms"],
             },

@@ -964,7 +964,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_dense48(MfmaArgs m) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[rb][kb * 4 + i] = s[kb][rb][i];
     // causal mask (positions are the columns themselves; padding columns
-    // lie past every row)
+    // lie past every row), only on tiles that reach past the wave's first row
     if (t * kBN + kBN - 1 > w0) {
 #pragma unroll
       for (int rb = 0; rb < 3; ++rb)
