@@ -791,15 +791,15 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (SRC == 0 && RING == 1 ? 3 : 2) 
 // fragment of O^T += V^T P^T for k-step j, matched by the tile image's V^T
 // column slots (vt_col16).  Lazy rescale, V shifts and outputs as in the
 // 32-row kernel.
-constexpr int kR48 = 48;
 
-__device__ inline void qk_tile48(const uint8_t* T, const bf16x8_t (*qf)[4], int l16, int g, f32x4_t (*s)[3]) {
-  constexpr int A = 3;
+template <int RB>
+__device__ inline void qk_tile48(const uint8_t* T, const bf16x8_t (*qf)[4], int l16, int g, f32x4_t (*s)[RB]) {
+  constexpr int A = RB == 3 ? 3 : 2;  // fragments read ahead
   const __bf16* kt = (const __bf16*)T;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int rb = 0; rb < 3; ++rb) s[kb][rb] = f32x4_t{};
+    for (int rb = 0; rb < RB; ++rb) s[kb][rb] = f32x4_t{};
   // fragment f = ks * 4 + kb: key row 16kb + l16, dims 32ks + 8g .. +7
   bf16x8_t kf[A];
 #pragma unroll
@@ -808,7 +808,7 @@ __device__ inline void qk_tile48(const uint8_t* T, const bf16x8_t (*qf)[4], int 
   for (int f = 0; f < 16; ++f) {
     const int kb = f & 3, ks = f >> 2;
 #pragma unroll
-    for (int rb = 0; rb < 3; ++rb) s[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[f % A], qf[rb][ks], s[kb][rb], 0, 0, 0);
+    for (int rb = 0; rb < RB; ++rb) s[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[f % A], qf[rb][ks], s[kb][rb], 0, 0, 0);
     if (f + A < 16) {
       const int fn = f + A;
       kf[f % A] = *(const bf16x8_t*)&kt[((fn & 3) * 16 + l16) * kKP + (fn >> 2) * 32 + g * 8];
@@ -817,14 +817,15 @@ __device__ inline void qk_tile48(const uint8_t* T, const bf16x8_t (*qf)[4], int 
   __builtin_amdgcn_sched_group_barrier(kSchedDsRead, A, 0);
 #pragma unroll
   for (int i = 0; i < 16 - A; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, RB, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 3 * A, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, RB * A, 0);
 }
 
-__device__ inline void pv_tile48(const uint8_t* T, const f16x8_t (*pf)[2], int l16, int g, f32x4_t (*o)[3]) {
-  constexpr int A = 3;
+template <int RB>
+__device__ inline void pv_tile48(const uint8_t* T, const f16x8_t (*pf)[2], int l16, int g, f32x4_t (*o)[RB]) {
+  constexpr int A = RB == 3 ? 3 : 2;  // fragments read ahead
   const _Float16* vt = (const _Float16*)(T + kImgV);
   // fragment f = j * 8 + db: V^T rows 16db + l16, column slots 32j + 8g .. +7
   f16x8_t vf[A];
@@ -834,7 +835,7 @@ __device__ inline void pv_tile48(const uint8_t* T, const f16x8_t (*pf)[2], int l
   for (int f = 0; f < 16; ++f) {
     const int db = f & 7, j = f >> 3;
 #pragma unroll
-    for (int rb = 0; rb < 3; ++rb) o[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[f % A], pf[rb][j], o[db][rb], 0, 0, 0);
+    for (int rb = 0; rb < RB; ++rb) o[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[f % A], pf[rb][j], o[db][rb], 0, 0, 0);
     if (f + A < 16) {
       const int fn = f + A;
       vf[f % A] = *(const f16x8_t*)&vt[((fn & 7) * 16 + l16) * kVP + (fn >> 3) * 32 + g * 8];
@@ -843,10 +844,10 @@ __device__ inline void pv_tile48(const uint8_t* T, const f16x8_t (*pf)[2], int l
   __builtin_amdgcn_sched_group_barrier(kSchedDsRead, A, 0);
 #pragma unroll
   for (int i = 0; i < 16 - A; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, RB, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, 3 * A, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, RB * A, 0);
 }
 
 // Weights of one row block: P = 2^(x*c2 - base) in fp16 for the lane's 16
@@ -874,7 +875,8 @@ __device__ inline float probs48(const float* x, float base, float c2, f16x8_t* p
 }
 
 // Rescale of one row block: the row's tile maximum over its four lanes.
-__device__ inline void rescale48(const float* x, float c2, float& mref, float& lsum, f32x4_t (*o)[3], int rb) {
+template <int RB>
+__device__ inline void rescale48(const float* x, float c2, float& mref, float& lsum, f32x4_t (*o)[RB], int rb) {
   float mt = x[0];
 #pragma unroll
   for (int v = 1; v < 16; ++v) mt = fmaxf(mt, x[v]);
@@ -891,9 +893,10 @@ __device__ inline void rescale48(const float* x, float c2, float& mref, float& l
   }
 }
 
-template <int NW>
+template <int NW, int RB>
 __global__ __launch_bounds__(64 * NW, 1) void k_attn_dense48(MfmaArgs m) {
-  constexpr int BM = kR48 * NW;
+  constexpr int WR = 16 * RB;  // rows per wave
+  constexpr int BM = WR * NW;
   constexpr int RING = 2;
   extern __shared__ __align__(16) uint8_t lds[];   // two tile images
   const AttnArgs& a = m.a;
@@ -920,11 +923,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_dense48(MfmaArgs m) {
   if (m.ntiles_total > 0) dma_img<NW, kImgChunks>(rs, 0, lds);
 
   // the lane's rows (one per row block) and their queries
-  const int w0 = row0 + wv * kR48;
-  int ipos[3];
-  bf16x8_t qf[3][4];
+  const int w0 = row0 + wv * WR;
+  int ipos[RB];
+  bf16x8_t qf[RB][4];
 #pragma unroll
-  for (int rb = 0; rb < 3; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     const int t = w0 + rb * 16 + l16;
     ipos[rb] = t < nrows ? t : -1;
     const bf16x8_t* qp = (const bf16x8_t*)((const uint16_t*)a.q + (bhS + (t < nrows ? t : 0)) * kD);
@@ -934,12 +937,12 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_dense48(MfmaArgs m) {
   // tiles of the block: up to its last row; the wave computes those up to
   // its own last row (none if it has no row)
   const int nt = min(m.ntiles_total, (min(row0 + BM, nrows) - 1) / kBN + 1);
-  const int wmax = w0 < nrows ? min(w0 + kR48, nrows) - 1 : -1;
+  const int wmax = w0 < nrows ? min(w0 + WR, nrows) - 1 : -1;
 
-  float mref[3], lsum[3];
-  f32x4_t o[8][3];
+  float mref[RB], lsum[RB];
+  f32x4_t o[8][RB];
 #pragma unroll
-  for (int rb = 0; rb < 3; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     mref[rb] = -INFINITY;
     lsum[rb] = 0.0f;
 #pragma unroll
@@ -950,15 +953,15 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_dense48(MfmaArgs m) {
 
   // V shift of the accumulators (as in the 32-row kernel)
   int osh = 0;
-  f32x4_t s[4][3];
-  f16x8_t pf[3][2];
+  f32x4_t s[4][RB];
+  f16x8_t pf[RB][2];
   // The weights pf of tile t from its scores s: mask, V shift, lazy rescale.
   auto weights = [&](int t) {
     const uint8_t* T = lds + (t % RING) * kImgBytes;
     // x[rb][8j + e]: column 32j + 16(e / 4) + 4g + e % 4
-    float x[3][16];
+    float x[RB][16];
 #pragma unroll
-    for (int rb = 0; rb < 3; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -967,7 +970,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_dense48(MfmaArgs m) {
     // lie past every row), only on tiles that reach past the wave's first row
     if (t * kBN + kBN - 1 > w0) {
 #pragma unroll
-      for (int rb = 0; rb < 3; ++rb)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int col = t * kBN + (v >> 2) * 16 + 4 * g + (v & 3);
@@ -980,37 +983,37 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_dense48(MfmaArgs m) {
 #pragma unroll
       for (int db = 0; db < 8; ++db)
 #pragma unroll
-        for (int rb = 0; rb < 3; ++rb) o[db][rb] *= f;
+        for (int rb = 0; rb < RB; ++rb) o[db][rb] *= f;
       osh = tsh;
     }
     const int dsh = osh - tsh;
     // lazy rescale as in the 32-row kernel; a lane holds 16 weights of each
     // of its rows, so a sum above 16 * 65504 means one overflowed fp16
-    float ls[3];
+    float ls[RB];
     bool bad = false;
 #pragma unroll
-    for (int rb = 0; rb < 3; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
       ls[rb] = probs48(x[rb], (mref[rb] == -INFINITY ? 0.0f : mref[rb]) + (float)dsh, m.c2, pf[rb]);
       bad |= (ipos[rb] >= 0 && mref[rb] == -INFINITY) || !(ls[rb] <= 16.0f * 65504.0f);
     }
     if (__builtin_amdgcn_ballot_w64(bad)) {
 #pragma unroll
-      for (int rb = 0; rb < 3; ++rb) {
-        rescale48(x[rb], m.c2, mref[rb], lsum[rb], o, rb);
+      for (int rb = 0; rb < RB; ++rb) {
+        rescale48<RB>(x[rb], m.c2, mref[rb], lsum[rb], o, rb);
         ls[rb] = probs48(x[rb], (mref[rb] == -INFINITY ? 0.0f : mref[rb]) + (float)dsh, m.c2, pf[rb]);
       }
     }
 #pragma unroll
-    for (int rb = 0; rb < 3; ++rb) lsum[rb] += dsh == 0 ? ls[rb] : __builtin_ldexpf(ls[rb], dsh);
+    for (int rb = 0; rb < RB; ++rb) lsum[rb] += dsh == 0 ? ls[rb] : __builtin_ldexpf(ls[rb], dsh);
   };
   for (int tt = 0; tt < nt; ++tt) {
     const uint8_t* T = lds + (tt % RING) * kImgBytes;
     // tile tt+1 goes into the slot tile tt-1 left (all waves passed it)
     if (tt + 1 < nt) dma_tile<NW>(rs, (tt + 1) * kImgBytes, lds + ((tt + 1) % RING) * kImgBytes);
     if (tt * kBN <= wmax) {
-      qk_tile48(T, qf, l16, g, s);
+      qk_tile48<RB>(T, qf, l16, g, s);
       weights(tt);
-      pv_tile48(T, pf, l16, g, o);
+      pv_tile48<RB>(T, pf, l16, g, o);
     }
     // tile tt+1 must be in LDS for every wave
     __builtin_amdgcn_s_waitcnt(0);
@@ -1020,7 +1023,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn_dense48(MfmaArgs m) {
   // ---- epilogue: a lane writes dims 16db + 4g .. +3 of each of its rows
   const float osc = __builtin_ldexpf(1.0f, osh);
 #pragma unroll
-  for (int rb = 0; rb < 3; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     float lt = lsum[rb];
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
@@ -1400,14 +1403,15 @@ static bool own_tiles(int) {
 static bool dense48(const CacheGeo& c) {
   return (long long)c.B * c.H * ((c.S + 255) / 256) >= kWideBlocks;
 }
-template <int NW>
+template <int NW, int RB>
 static hipError_t launch_dense48(MfmaArgs& m, hipStream_t st) {
   constexpr size_t lds = 2 * (size_t)kImgBytes;
-  static const hipError_t attr = hipFuncSetAttribute((const void*)k_attn_dense48<NW>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)k_attn_dense48<NW, RB>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  m.nblk = (m.a.c.S + kR48 * NW - 1) / (kR48 * NW);
-  FL_LAUNCH(k_attn_dense48<NW>, dim3((unsigned)(m.a.c.B * m.a.c.H * m.nblk)), dim3(64 * NW), lds, st, m);
+  constexpr int BM = 16 * RB * NW;
+  m.nblk = (m.a.c.S + BM - 1) / BM;
+  FL_LAUNCH((k_attn_dense48<NW, RB>), dim3((unsigned)(m.a.c.B * m.a.c.H * m.nblk)), dim3(64 * NW), lds, st, m);
   return hipGetLastError();
 }
 
@@ -1425,7 +1429,7 @@ hipError_t launch_attn_mfma(const AttnArgs& a, uint8_t* ws, hipStream_t st) {
   hipError_t e = launch_gather(a.c, a.r, a.r == 1 ? nullptr : a.sel, K, ws, st, d48);
   if (e != hipSuccess) return e;
   m.tiles = ws;
-  if (d48) return launch_dense48<8>(m, st);
+  if (d48) return launch_dense48<8, 3>(m, st);
   return launch_rows<kModeAttn>(m, a.r == 1 ? a.c.S : a.c.n[a.r], st);
 }
 
