@@ -781,9 +781,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (SRC == 0 && RING == 1 ? 3 : 2) 
 
 // ------------------------------------------------------------- dense loop 1, 48 rows per wave
 // Loop-1 attention over every position on 16x16x32 products: each wave owns
-// 48 query rows as three 16-row blocks, so every K or V^T fragment a lane
-// reads from LDS feeds three products (1.5x the matrix work per LDS byte of
-// the 32-row kernel), at two waves per SIMD.  In S^T = K Q^T a lane of group
+// RB 16-row blocks of queries (RB = 3: 48 rows, two waves per SIMD), so every
+// K or V^T fragment a lane reads from LDS feeds RB products (three: 1.5x the
+// matrix work per LDS byte of the 32-row kernel).  In S^T = K Q^T a lane of group
 // g = lane / 16 holds, for row l16 = lane % 16 of each row block, columns
 // 16kb + 4g .. +3 of the tile (kb = 0..3): a row's 64 columns lie in four
 // lanes, which reduce a row's maximum or sum with two exchanges.  The
