@@ -562,7 +562,7 @@ def main():
             },
         },
         "roofline": {
-            "kernel": "k_attn_dense48<8> (the attention kernel of fl_loop_attn r=1: dense causal over the int8 base)",
+            "kernel": "k_attn_dense48<8, 3> (the attention kernel of fl_loop_attn r=1: dense causal over the int8 base)",
             "bound": "mfma",
             "achieved": pf["dense_kernel_tf"],
             "peak": acc.MI355X_BF16_TFLOPS,
