@@ -400,7 +400,7 @@ __device__ inline void pv_tile(const uint8_t* T, const f16x8_t* pf, int l32, int
 // The accumulators hold 2^-osh times the products (V shifts); osc = 2^osh.
 template <int MODE>
 __device__ inline void write_row(const AttnArgs& a, int r, long long bhS, int i, int hf, float mref, float lt,
-                                 const f32x16_t* o, float osc) {
+                                 const f32x16_t* o, float osc, float um_off = 0.0f) {
   if (i < 0) return;
   const long long rowp = (bhS + i) * kD;
   if (MODE == kModeAttn) {
@@ -466,8 +466,11 @@ __device__ inline void write_row(const AttnArgs& a, int r, long long bhS, int i,
       a.lse[bhS + i] = -INFINITY;
     }
   } else {
-    const float Mp = a.M[bhS + i];
-    const float Mu = Mp > 0.0f ? Mp : 0.0f;
+    // The sums are against the reference mref; the loop r-1 probabilities
+    // are P = 2^(x - um_off) with um_off = lse_prev log2 e - log2 M_prev (+inf
+    // when M_prev = 0), so both take Mu = 2^(mref - um_off) (none if the row
+    // saw no selected column: lt = 0).
+    const float Mu = (lt > 0.0f && um_off != INFINITY) ? __builtin_amdgcn_exp2f(mref - um_off) : 0.0f;
     const float Mo = Mu * osc;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -625,14 +628,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (SRC == 0 && RING == 1 ? 3 : 2) 
   f32x16_t o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16_t{};
-  if (MODE == kModeUM) {
-    // loop r-1 statistics of the row: P = M * 2^(x - lse*log2e)
-    float Mp = 0.0f, lp = 0.0f;
-    if (ipos >= 0) {
-      Mp = a.M[bhS + ipos];
-      lp = a.lse[bhS + ipos];
-    }
-    mref = (Mp > 0.0f) ? lp * 1.4426950408889634f : INFINITY;
+  // cached-mass pass: the row's loop r-1 statistics as one exponent offset,
+  // P = M 2^(x - lse log2 e) = 2^(x - um_off)
+  float um_off = INFINITY;
+  if (MODE == kModeUM && ipos >= 0) {
+    const float Mp = a.M[bhS + ipos];
+    if (Mp > 0.0f) um_off = a.lse[bhS + ipos] * 1.4426950408889634f - __log2f(Mp);
   }
   __syncthreads();
   const int nt = sh_ntiles;
@@ -671,13 +672,17 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (SRC == 0 && RING == 1 ? 3 : 2) 
         osh = tsh;
       }
       const int dsh = osh - tsh;
-      // Weights against the current reference (UM: the fixed loop r-1
-      // statistics).  ATTN: only if a lane's weights overflowed fp16 (its sum
-      // is not finite) or a valid row has no reference yet is the tile max
-      // taken, the lazy rescale applied and the weights formed again.
+      // Weights against the current reference: only if a lane's weights
+      // overflowed fp16 (its sum is not finite) or a valid row has no
+      // reference yet is the tile max taken, the lazy rescale applied and the
+      // weights formed again.  The cached-mass pass does the same and brings
+      // its sums to the loop r-1 statistics at the end (write_row): weights
+      // formed against the loop r-1 log-sum-exp itself would fall into fp16's
+      // subnormal range for a row whose selected columns carry little of its
+      // mass, and lose their relative precision there.
       f16x8_t pf[4];
-      float ls = softmax_probs(x, ((MODE == kModeAttn && mref == -INFINITY) ? 0.0f : mref) + (float)dsh, m.c2, pf);
-      if (MODE == kModeAttn) {
+      float ls = softmax_probs(x, (mref == -INFINITY ? 0.0f : mref) + (float)dsh, m.c2, pf);
+      {
         const bool bad = (ipos >= 0 && mref == -INFINITY) || !(ls <= kRescaleP);
         if (__builtin_amdgcn_ballot_w64(bad)) {
           softmax_rescale(x, m.c2, mref, lsum, o);
@@ -728,8 +733,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (SRC == 0 && RING == 1 ? 3 : 2) 
     lds_barrier();
     if (sp > 0) return;
     // Split 0 merges in split order: the common reference M = max of the
-    // references (UM: all equal, the fixed loop r-1 statistics) and shift
-    // OSH = max of the shifts; split s enters with weight 2^(mref_s - M)
+    // references and shift OSH = max of the shifts; split s enters with
+    // weight 2^(mref_s - M)
     // (0 for a split that saw no column of the row) and its accumulators
     // with 2^(osh_s - OSH) more.
     float ms[SPLIT], ls[SPLIT];
@@ -755,7 +760,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (SRC == 0 && RING == 1 ? 3 : 2) 
     lt = 0.0f;
 #pragma unroll
     for (int s = 0; s < SPLIT; ++s) {
-      const float w = MODE == kModeAttn ? (ms[s] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms[s] - M)) : 1.0f;
+      const float w = ms[s] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms[s] - M);
       lt += w * ls[s];
       f[s] = w * __builtin_ldexpf(1.0f, os[s] - OSH);
     }
@@ -776,7 +781,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? (SRC == 0 && RING == 1 ? 3 : 2) 
     mref = M;
     osh = OSH;
   }
-  write_row<MODE>(a, r, bhS, ipos, hf, mref, lt, o, __builtin_ldexpf(1.0f, osh));
+  write_row<MODE>(a, r, bhS, ipos, hf, mref, lt, o, __builtin_ldexpf(1.0f, osh), um_off);
 }
 
 // ------------------------------------------------------------- dense loop 1, 48 rows per wave

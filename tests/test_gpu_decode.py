@@ -59,6 +59,25 @@ def test_decode_small(dtype):
     _decode_case(cfg, 1e-5, rel=False)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("S,act,col", [
+    (64, (1, "0.02", "0.02", "0.02"), "0.02"),   # one tile of context, one residual row, one selected column
+    (65, (1, "0.5", "0.25", "0.02"), "0.02"),    # a tile and one position of context, one selected column
+    (130, (1, 1, 1, 1), "1"),                    # every position selected at every loop
+])
+def test_decode_degenerate(dtype, S, act, col):
+    """Degenerate decode problems: a context of one tile or one tile and one
+    position, a selection of one column (K_r = 1), residual chains of a single
+    token, and loops that keep every position."""
+    cfg = workloads.custom(name="decode-degenerate", dtype=dtype, B=2, H=2, d=128, S=S, R=4, act=act, col=col,
+                           bits=(8, 4, 4, 2), gamma=0.5, lognormal=0.5, L=2, decode=True, seed=42)
+    _say("decode degenerate", dtype, S, cfg.n, cfg.K)
+    if dtype == "f32":
+        _decode_case(cfg, 1e-5, rel=False)
+    else:
+        _decode_case(cfg, 2e-3, rel=True)
+
+
 def test_decode_pruned_every_loop():
     """Budgets that shrink every loop exercise the reuse update at r >= 3."""
     import tests.gpu_harness as gh

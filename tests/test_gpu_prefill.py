@@ -112,7 +112,12 @@ def _check_outputs(cfg, gpu, orc, heads, tol, rel, budgets=None):
                     m_g = gpu["mass"][r][b, h]
                     K = (budgets[r - 1] if budgets else cfg.K)
                     thr = _kth_mass(m_or, K)
-                    em = np.max(np.abs(m_g - m_or) / np.maximum(np.abs(m_or), thr))
+                    # relative to max(c_j, c_K); where both are zero (a row set
+                    # that sees none of the candidates) only an exact zero agrees
+                    den = np.maximum(np.abs(m_or), thr)
+                    dif = np.abs(m_g - m_or)
+                    em = float(np.max(np.where(den > 0, dif / np.where(den > 0, den, 1.0),
+                                               np.where(dif > 0, np.inf, 0.0)), initial=0.0))
                     print(f"[parity] b={b} h={h} loop={r + 1} mass_err/max(c,c_K)={em:.2e} c_K={thr:.3e}", flush=True)
                     assert em <= tol, (b, h, r + 1, "mass", em)
 
@@ -334,6 +339,25 @@ def test_prefill_vector_path_other_dims(dtype, d):
     _say("prefill vector path", dtype, d, cfg)
     _bf16_case(cfg, heads=[0, 1], sel_eps=1e-5 if f32 else 2e-3, budgets=[440, 220, 90], tol=1e-5 if f32 else 2e-3,
                rel=not f32)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("S,act,col", [
+    (64, (1, "0.02", "0.02", "0.02"), "0.02"),   # one tile; one active row and one selected column per loop
+    (65, (1, "0.5", "0.25", "0.02"), "0.02"),    # a tile and one position; one selected column
+    (130, (1, 1, 1, 1), "1"),                    # every row and every column at every loop
+])
+def test_prefill_degenerate(dtype, d, S, act, col):
+    """Degenerate sizes of the method: a single active row (n_r = 1), a
+    single selected column (K_r = 1, so most rows have no selected column at
+    or before them and keep loop r-1's state), a sequence of one tile or one
+    tile and one position, and loops that keep every row and column (the
+    cached mass is one and the reused part zero)."""
+    f32 = dtype == "f32"
+    cfg = workloads.custom(name="degenerate", dtype=dtype, B=2, H=2, d=d, S=S, R=4, act=act, col=col,
+                           bits=(8, 4, 4, 2), lognormal=0.5, seed=41)
+    _say("prefill degenerate", cfg.name, dtype, d, S, cfg.n, cfg.K)
+    _bf16_case(cfg, heads=[0, 1], sel_eps=1e-5 if f32 else 2e-3, tol=1e-5 if f32 else 2e-3, rel=not f32)
 
 
 def test_prefill_pruned_full_size():
