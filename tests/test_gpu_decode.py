@@ -64,11 +64,12 @@ def test_decode_small(dtype):
     (64, (1, "0.02", "0.02", "0.02"), "0.02"),   # one tile of context, one residual row, one selected column
     (65, (1, "0.5", "0.25", "0.02"), "0.02"),    # a tile and one position of context, one selected column
     (130, (1, 1, 1, 1), "1"),                    # every position selected at every loop
+    (1, (1, 1, 1, 1), "1"),                      # a single token
 ])
 def test_decode_degenerate(dtype, S, act, col):
-    """Degenerate decode problems: a context of one tile or one tile and one
-    position, a selection of one column (K_r = 1), residual chains of a single
-    token, and loops that keep every position."""
+    """Degenerate decode problems: a context of one token, one tile or one
+    tile and one position, a selection of one column (K_r = 1), residual
+    chains of a single token, and loops that keep every position."""
     cfg = workloads.custom(name="decode-degenerate", dtype=dtype, B=2, H=2, d=128, S=S, R=4, act=act, col=col,
                            bits=(8, 4, 4, 2), gamma=0.5, lognormal=0.5, L=2, decode=True, seed=42)
     _say("decode degenerate", dtype, S, cfg.n, cfg.K)

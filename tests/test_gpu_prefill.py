@@ -346,13 +346,14 @@ def test_prefill_vector_path_other_dims(dtype, d):
     (64, (1, "0.02", "0.02", "0.02"), "0.02"),   # one tile; one active row and one selected column per loop
     (65, (1, "0.5", "0.25", "0.02"), "0.02"),    # a tile and one position; one selected column
     (130, (1, 1, 1, 1), "1"),                    # every row and every column at every loop
+    (1, (1, 1, 1, 1), "1"),                      # a single token
 ])
 def test_prefill_degenerate(dtype, d, S, act, col):
     """Degenerate sizes of the method: a single active row (n_r = 1), a
     single selected column (K_r = 1, so most rows have no selected column at
-    or before them and keep loop r-1's state), a sequence of one tile or one
-    tile and one position, and loops that keep every row and column (the
-    cached mass is one and the reused part zero)."""
+    or before them and keep loop r-1's state), a sequence of one token, one
+    tile or one tile and one position, and loops that keep every row and
+    column (the cached mass is one and the reused part zero)."""
     f32 = dtype == "f32"
     cfg = workloads.custom(name="degenerate", dtype=dtype, B=2, H=2, d=d, S=S, R=4, act=act, col=col,
                            bits=(8, 4, 4, 2), lognormal=0.5, seed=41)
