@@ -82,6 +82,7 @@ __global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
   static_assert(GQ * 128 <= NT, "one thread per output dim of every head");
   __shared__ float wm[GQ][NW], wl[GQ][NW], wacc[GQ][NW][128];
   __shared__ uint32_t hist[GQ][kHistBins];  // each head's logits by key (loop 2's selection)
+  __shared__ float lgs[GQ][NW][64];          // a wave's logits of a step, stored as whole lines
   const CacheGeo& c = a.c;
   const int HB = c.H / GQ;                 // query-head groups per sequence
   const long long blk = blockIdx.x;        // over [L][B][HB]
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
           for (int e = 0; e < 16; ++e) part = __builtin_fmaf(qs[u][e], (float)((kws[e >> 3] >> (4 * (e & 7))) & 15), part);
           const float sc = tau * group8_sum_dpp(part);
           if (sub == 0) {
-            logit[(long long)u * c.S + j] = sc;
+            lgs[u][wv][(gid & 7) * 8 + i] = sc;
             atomicAdd(&hist[u][order_key(sc) >> (32 - kHistBits)], 1u);
           }
           if (sc > m[u] + kDecRescale) {
@@ -183,6 +184,16 @@ __global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
             acc[u][e] = __builtin_fmaf(pv, (float)((vws[e >> 3] >> (4 * (e & 7))) & 15), acc[u][e]);
         }
       }
+      // the key block's 64 logits (the wave's eight groups), two whole lines
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
+      if (blk * kPGroup + lane < body) {
+#pragma unroll
+        for (int u = 0; u < GQ; ++u) logit[(long long)u * c.S + blk * kPGroup + lane] = lgs[u][wv][lane];
+      }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
     }
 #pragma unroll
     for (int u = 0; u < GQ; ++u) {
@@ -217,42 +228,68 @@ __global__ __launch_bounds__(NT) void k_decode_dense(DecodeArgs a, float tau) {
       }
     }
   }
-  for (int j = gid; !PAPER && j < c.T; j += NG) {
-    const uint8_t* rec = recs + (long long)j * c.base_rb;
-    const uint4 kw = *(const uint4*)(rec + sub * 16);
-    const uint4 vw = *(const uint4*)(rec + d + sub * 16);
-    const uint16_t* sc = (const uint16_t*)((const uint8_t*)scl + (long long)j * c.base_rb);
-    const float ks = h2f(sc[g]);
-    const float vs = h2f(sc[4 + g]);
-    float cv[16];
-    unpack_i8x16(kw, cv);
-    float p[GQ];
+  // The block takes 256 positions per step, each wave 32 consecutive ones in
+  // four rounds of 8 (one per 8-lane group): its 32 logits then fill one
+  // 128-byte line, staged in LDS and stored by one instruction.  Stored by
+  // each token's group as it went (32 bytes per wave and round: partial lines
+  // among the record reads), they made the 48-layer loop at 32K positions
+  // ~2 ms slower (21.3 against 19.3 ms), and slower still in some physical
+  // placements of the cache.
+  // round it: step it / 4, round it % 4; position w0 + 8 (it % 4) + grp
+  for (int it = 0; !PAPER && (it >> 2) * (32 * NW) < c.T; ++it) {
+    const int w0 = (it >> 2) * (32 * NW) + wv * 32;
+    const int j = w0 + (it & 3) * 8 + grp;
+    if (j < c.T) {  // the same for the group's 8 lanes
+      const uint8_t* rec = recs + (long long)j * c.base_rb;
+      const uint4 kw = *(const uint4*)(rec + sub * 16);
+      const uint4 vw = *(const uint4*)(rec + d + sub * 16);
+      const uint16_t* sc = (const uint16_t*)((const uint8_t*)scl + (long long)j * c.base_rb);
+      const float ks = h2f(sc[g]);
+      const float vs = h2f(sc[4 + g]);
+      float cv[16];
+      unpack_i8x16(kw, cv);
+      float p[GQ];
 #pragma unroll
-    for (int u = 0; u < GQ; ++u) {
-      float part = 0.0f;
+      for (int u = 0; u < GQ; ++u) {
+        float part = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) part = __builtin_fmaf(q[u][e], cv[e], part);
-      const float s = tau * group8_sum_dpp(part * ks);
-      if (sub == 0) {
-        logit[(long long)u * c.S + j] = s;
-        atomicAdd(&hist[u][order_key(s) >> (32 - kHistBits)], 1u);
+        for (int e = 0; e < 16; ++e) part = __builtin_fmaf(q[u][e], cv[e], part);
+        const float s = tau * group8_sum_dpp(part * ks);
+        if (sub == 0) {
+          lgs[u][wv][(it & 3) * 8 + grp] = s;
+          atomicAdd(&hist[u][order_key(s) >> (32 - kHistBits)], 1u);
+        }
+        if (s > m[u] + kDecRescale) {
+          const float alpha = __expf(m[u] - s);  // 0 on the group's first token
+          lsum[u] *= alpha;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[u][e] *= alpha;
+          m[u] = s;
+        }
+        p[u] = __expf(s - m[u]);
+        lsum[u] += p[u];
       }
-      if (s > m[u] + kDecRescale) {
-        const float alpha = __expf(m[u] - s);  // 0 on the group's first token
-        lsum[u] *= alpha;
+      unpack_i8x16(vw, cv);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[u][e] *= alpha;
-        m[u] = s;
+      for (int u = 0; u < GQ; ++u) {
+        const float pv = p[u] * vs;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[u][e] = __builtin_fmaf(pv, cv[e], acc[u][e]);
       }
-      p[u] = __expf(s - m[u]);
-      lsum[u] += p[u];
     }
-    unpack_i8x16(vw, cv);
+    // after the fourth round, the wave's logits of this step (LDS operations of
+    // one wave complete in order: its stores are visible to its reads once
+    // they have completed)
+    if ((it & 3) == 3) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
+      if (lane < 32 && w0 + lane < c.T) {
 #pragma unroll
-    for (int u = 0; u < GQ; ++u) {
-      const float pv = p[u] * vs;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[u][e] = __builtin_fmaf(pv, cv[e], acc[u][e]);
+        for (int u = 0; u < GQ; ++u) logit[(long long)u * c.S + w0 + lane] = lgs[u][wv][lane];
+      }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
     }
   }
 #pragma unroll
@@ -539,6 +576,9 @@ void k_decode_sparse(DecodeArgs a, float tau) {
   __shared__ GroupState gs;
   __shared__ float csum[PRUNED ? kDecGroups : 1][128];
   __shared__ float psum[kDecGroups];
+  // a chunk's 64 logits, stored in two whole lines at the end of the chunk
+  // (stored token by token they are partial-line writes among the gathers)
+  __shared__ float lgst[kDecThreads / kWave][64];
   const CacheGeo& c = a.c;
   const long long lbh = blockIdx.x;
   const int h = (int)(lbh % c.H);
@@ -627,15 +667,16 @@ void k_decode_sparse(DecodeArgs a, float tau) {
           // the paper's format: K, V at loop r (and V at loop r-1) rebuilt here
           float kx[16], vx[16], vp[16], pj;
           paper_token16<PRUNED>(c, r, l, b, kv_head(c, h), j2[u], sub * 16, kx, vx, vp);
-          const float p = tok_weight<PRUNED>(q, kx, tau, o2[u], Mprev, lprev, v2[u], sub, logit + tt[u], m, lsum,
-                                             acc, P, pj);
+          const float p = tok_weight<PRUNED>(q, kx, tau, o2[u], Mprev, lprev, v2[u], sub, &lgst[wv][tt[u] - t0], m,
+                                             lsum, acc, P, pj);
           if (v2[u]) tok_add<PRUNED>(p, pj, vx, vp, acc, C);
         } else {
           float p, pj;
           {
             float kx[16];
             tok_key<NR>(c, r, l, b, h, j2[u], s2[u], sub, t2[u], kx);
-            p = tok_weight<PRUNED>(q, kx, tau, o2[u], Mprev, lprev, v2[u], sub, logit + tt[u], m, lsum, acc, P, pj);
+            p = tok_weight<PRUNED>(q, kx, tau, o2[u], Mprev, lprev, v2[u], sub, &lgst[wv][tt[u] - t0], m, lsum, acc,
+                                   P, pj);
           }
           if (v2[u]) {
             float vx[16], vp[16];
@@ -645,6 +686,14 @@ void k_decode_sparse(DecodeArgs a, float tau) {
         }
       }
     }
+    // the chunk's logits (each valid token's, written above by its group;
+    // LDS operations of one wave complete in order)
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    if (lane < nv) logit[t0 + lane] = lgst[wv][lane];
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
   }
   if (sub == 0) {
     gs.m[gid] = m;
